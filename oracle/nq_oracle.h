@@ -1,0 +1,79 @@
+/*
+ * nq_oracle -- plain, slow, single-threaded CPU decoder for packed
+ * block-quantized weights.  TEST INFRASTRUCTURE ONLY: the product library
+ * never links, loads or calls it; only the tests, the smoke check and the
+ * CPU-baseline leg of the benchmark do.
+ *
+ * What it computes is defined by two pages:
+ *   - ONNX "DequantizePacked decoding specification" (opset 29): the
+ *     signature and storage rules, the format identifier table, the packed
+ *     layout table, the binary32 rounding rules and the "Mathematical
+ *     decoding rules" (conventional, K-quant, IQ and ternary/block-floating
+ *     subsections), the IQ codebooks;
+ *   - NInfer "tensor-formats" maintainer page, section 3.3 (nvfp4 with an
+ *     FP32 weight divisor), 3.1 (bf16 words), 3.2 (fp32 words).
+ *
+ * Every floating-point operation is one IEEE binary32 operation rounded to
+ * nearest-even with gradual underflow (built with -ffp-contract=off and no
+ * fast-math); nothing is fused or reassociated.
+ */
+#ifndef NQ_ORACLE_H
+#define NQ_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes of the oracle's own length rule. */
+enum {
+    NQO_OK = 0,
+    NQO_ERR_FORMAT = 1,   /* index out of range */
+    NQO_ERR_RANK = 2,     /* rank < 1 */
+    NQO_ERR_DIM = 3,      /* a negative dimension */
+    NQO_ERR_ALIGN = 4,    /* shape[-1] % B != 0 */
+    NQO_ERR_OVERFLOW = 5, /* a byte or element count beyond INT64_MAX */
+    NQO_ERR_LENGTH = 6,   /* nbytes differs from the length rule */
+    NQO_ERR_DTYPE = 7     /* unknown output dtype */
+};
+
+/* Output dtypes: 0 binary32, 1 binary16, 2 bfloat16, 3 binary64. */
+enum { NQO_F32 = 0, NQO_F16 = 1, NQO_BF16 = 2, NQO_F64 = 3 };
+
+/* Format table: index -> (name, B values per block, S bytes per block,
+ * trailer bytes after the blocks).  28 entries: the 27 "gguf:" profiles of
+ * the identifier table and "nvfp4" (block bytes as gguf:nvfp4 plus a
+ * trailing little-endian binary32 divisor). */
+int nqo_format_count(void);
+int nqo_format_info(int fmt, const char **name, int *B, int *S, int *trailer);
+int nqo_format_find(const char *name); /* exact, case-sensitive; -1 if absent */
+
+/* Length rule: nbytes = prod(shape[:-1]) * (shape[-1] / B) * S (+ trailer). */
+int nqo_sizes(int fmt, const int64_t *shape, int rank, uint64_t *nbytes, uint64_t *nelems);
+
+/* Decode a whole payload.  out holds prod(shape) values of `dtype`. */
+int nqo_decode(int fmt, const uint8_t *payload, uint64_t nbytes, const int64_t *shape,
+               int rank, int dtype, void *out);
+
+/* Decode `nblocks` back-to-back blocks to binary32 (no trailer; `d_w` is the
+ * divisor used by "nvfp4" and ignored by every other format). */
+int nqo_decode_blocks_f32(int fmt, const uint8_t *blocks, uint64_t nblocks, float d_w, float *y);
+
+/* Scalar word conversions, each written from its IEEE / page definition. */
+float nqo_f16_to_f32(uint16_t h);
+uint16_t nqo_f32_to_bf16(float x);
+uint16_t nqo_f32_to_f16(float x);
+float nqo_e4m3fn_to_f32(uint8_t w);
+void nqo_convert(const float *x, uint64_t n, int dtype, void *out);
+
+/* Expanded IQ codebooks: book 0..5 = iq2xxs, iq2xs, iq2s, iq3xxs, iq3s, iq1s. */
+int nqo_grid_rows(int book);
+int nqo_grid_width(int book);
+int nqo_grid_value(int book, int row, int j);
+int nqo_grid_bad_fields(void); /* packed fields that index past the value list */
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,468 @@
+"""Pins of the oracle against what the pages and mathematics fix (CPU only).
+
+Each test names the passage it pins.  None of them recomputes the oracle's
+own formula: they compare with library routines (numpy, PyTorch), closed
+forms, tables printed elsewhere on the pages, hand-derived blocks
+(tests/golden/one_block.json), the page's second notation, and a structural
+bit-flip map written separately from the layout table (tests/layout_map.py).
+"""
+import json
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import layout_map
+import page_notation
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GGUF = [f for f in oracle.format_names() if f.startswith("gguf:")]
+ALL = oracle.format_names()
+RECIPE = synth.binade(-12, -6, True)
+
+# --------------------------------------------------------------------------
+# Registry: DequantizePacked page, "Quantization formats" (B, S) versus the
+# field list of "Packed layouts and decoding" and the NInfer page's GGUF
+# bits/weight column.
+# --------------------------------------------------------------------------
+LAYOUT_FIELDS = {
+    "q4_0": "h d; u8 q[16]", "q4_1": "h d,m; u8 q[16]", "q5_0": "h d; u8 high[4],q[16]",
+    "q5_1": "h d,m; u8 high[4],q[16]", "q8_0": "h d; i8 q[32]", "q8_1": "h d,s; i8 q[32]",
+    "q2_k": "u8 scales[16],q[64]; h d,dmin", "q3_k": "u8 mask[32],q[64],scales[12]; h d",
+    "q4_k": "h d,dmin; u8 scales[12],q[128]", "q5_k": "h d,dmin; u8 scales[12],high[32],q[128]",
+    "q6_k": "u8 low[128],high[64]; i8 scales[16]; h d", "q8_k": "f d; i8 q[256]; i16 sums[16]",
+    "iq2_xxs": "h d; u16 q[32]", "iq2_xs": "h d; u16 q[32]; u8 scales[8]",
+    "iq2_s": "h d; u8 q[64],high[8],scales[8]", "iq3_xxs": "h d; u8 q[96]",
+    "iq3_s": "h d; u8 q[64],high[8],signs[32],scales[4]", "iq1_s": "h d; u8 q[32]; u16 high[8]",
+    "iq1_m": "u8 q[32],high[16],scales[8]", "iq4_nl": "h d; u8 q[16]",
+    "iq4_xs": "h d; u16 high; u8 scales[4],q[128]", "tq1_0": "u8 q[48],high[4]; h d",
+    "tq2_0": "u8 q[64]; h d", "mxfp4": "u8 exponent,q[16]", "nvfp4": "u8 scales[4],q[32]",
+    "q1_0": "h d; u8 q[16]", "q2_0": "h d; u8 q[16]",
+}
+TYPE_BYTES = {"h": 2, "f": 4, "u8": 1, "i8": 1, "u16": 2, "i16": 2}
+
+# NInfer tensor-formats page, GGUF block format table: name -> (B, S, bits/weight)
+NINFER_GGUF = {
+    "q8_0": (32, 34, 8.50), "q4_0": (32, 18, 4.50), "q5_0": (32, 22, 5.50), "q2_0": (64, 18, 2.25),
+    "q2_k": (256, 84, 2.625), "q3_k": (256, 110, 3.4375), "q4_k": (256, 144, 4.50),
+    "q5_k": (256, 176, 5.50), "q6_k": (256, 210, 6.5625), "iq2_xxs": (256, 66, 2.0625),
+    "iq2_xs": (256, 74, 2.3125), "iq3_xxs": (256, 98, 3.0625), "iq1_s": (256, 50, 1.5625),
+    "iq4_nl": (32, 18, 4.50), "iq3_s": (256, 110, 3.4375), "iq2_s": (256, 82, 2.5625),
+    "iq4_xs": (256, 136, 4.25), "iq1_m": (256, 56, 1.75),
+}
+
+
+def _field_bytes(desc):
+    total = 0
+    for group in desc.split(";"):
+        typ, rest = group.strip().split(" ", 1)
+        for name in rest.split(","):
+            m = re.match(r"\s*\w+(?:\[(\d+)\])?\s*$", name)
+            total += TYPE_BYTES[typ] * (int(m.group(1)) if m.group(1) else 1)
+    return total
+
+
+def test_registry_has_27_profiles_plus_nvfp4():
+    assert len(GGUF) == 27
+    assert set(ALL) == set(GGUF) | {"nvfp4"}
+
+
+@pytest.mark.parametrize("fmt", GGUF)
+def test_block_bytes_equal_layout_field_sum(fmt):
+    _, B, S, T = oracle.info(fmt)
+    assert S == _field_bytes(LAYOUT_FIELDS[fmt[5:]])
+    assert T == 0
+
+
+@pytest.mark.parametrize("name", sorted(NINFER_GGUF))
+def test_block_geometry_matches_ninfer_table(name):
+    _, B, S, _ = oracle.info("gguf:" + name)
+    b_ref, s_ref, bpw = NINFER_GGUF[name]
+    assert (B, S) == (b_ref, s_ref)
+    assert 8 * S / B == bpw
+
+
+def test_nvfp4_divisor_variant_geometry():
+    # gguf:nvfp4 block bytes (64 values, 36 bytes) plus one 4-byte divisor
+    assert oracle.info("nvfp4")[1:] == (64, 36, 4)
+    assert oracle.info("gguf:nvfp4")[1:] == (64, 36, 0)
+
+
+# --------------------------------------------------------------------------
+# Length rule: "Format identifiers" (closed form) and the Kiln quantization
+# page's scale-count formula ceil(shape[axis]/group) * prod(other dims).
+# --------------------------------------------------------------------------
+def _kiln_count(shape, group):
+    others = 1  # the product of no dimensions is 1
+    for d in shape[:-1]:
+        others *= d
+    return -(-shape[-1] // group) * others
+
+
+@pytest.mark.parametrize("fmt", ALL)
+@pytest.mark.parametrize("shape", [[32 * 256], [3, 512], [2, 3, 1024], [7, 256]])
+def test_length_rule_closed_form(fmt, shape):
+    _, B, S, T = oracle.info(fmt)
+    st, nb, ne = oracle.sizes(fmt, shape)
+    assert st == oracle.OK
+    assert ne == int(np.prod(shape))
+    assert nb == _kiln_count(shape, B) * S + T
+
+
+def test_kiln_examples():
+    # a rank-1 tensor of 32 elements with group 32 needs one scale: one MXFP4 block
+    st, nb, ne = oracle.sizes("gguf:mxfp4", [32])
+    assert (st, nb, ne) == (oracle.OK, 17, 32)
+    assert _kiln_count([32], 32) == 1
+
+
+@pytest.mark.parametrize("shape,status", [
+    ([], oracle.ERR_RANK), ([-1, 32], oracle.ERR_DIM), ([4, 31], oracle.ERR_ALIGN),
+    ([0, 33], oracle.ERR_ALIGN), ([2 ** 40, 2 ** 40, 32], oracle.ERR_OVERFLOW),
+])
+def test_length_rule_rejections(shape, status):
+    assert oracle.sizes("gguf:q4_0", shape)[0] == status
+
+
+def test_empty_tensors():
+    assert oracle.sizes("gguf:q4_k", [0, 256]) == (oracle.OK, 0, 0)
+    assert oracle.sizes("gguf:q4_k", [5, 0]) == (oracle.OK, 0, 0)
+    assert oracle.sizes("nvfp4", [0, 64]) == (oracle.OK, 4, 0)
+    # a zero anywhere makes the count exactly zero, however large the rest
+    assert oracle.sizes("gguf:q4_0", [2 ** 62, 0, 32])[0] == oracle.OK
+
+
+@pytest.mark.parametrize("delta", [-36, -1, 1, 36])
+def test_wrong_length_rejected(delta):
+    p = synth.payload("gguf:q8_1", 8, 1, RECIPE)
+    bad = np.zeros(p.size + delta, dtype=np.uint8) if delta > 0 else p[:delta]
+    assert oracle.decode_status("gguf:q8_1", bad, [8 * 32]) == oracle.ERR_LENGTH
+
+
+# --------------------------------------------------------------------------
+# Word conversions versus library routines.
+# --------------------------------------------------------------------------
+def test_binary16_all_words_match_numpy():
+    words = np.arange(65536, dtype=np.uint16)
+    ref = words.view(np.float16).astype(np.float32)
+    got = np.array([oracle.f16_to_f32(int(w)) for w in words], dtype=np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def _structured_f32_sample():
+    """Every high half (sign, exponent, top mantissa bits) with low halves at
+    and around the rounding points of both bf16 and f16, plus random words."""
+    hi = np.arange(65536, dtype=np.uint32) << 16
+    lows = np.array([0x0000, 0x0001, 0x0FFF, 0x1000, 0x1001, 0x1FFF, 0x2000, 0x2001, 0x3000,
+                     0x7FFF, 0x8000, 0x8001, 0xBFFF, 0xC000, 0xFFFF], dtype=np.uint32)
+    words = (hi[:, None] | lows[None, :]).ravel()
+    rng = np.random.default_rng(2024)
+    rand = rng.integers(0, 2 ** 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)
+    return np.concatenate([words, rand]).view(np.float32)
+
+
+def test_bf16_rne_matches_torch():
+    x = _structured_f32_sample()
+    got = oracle.convert(x, "bf16")
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    nan = np.isnan(x)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # NaN stays NaN with its sign
+    assert np.all((got[nan] & 0x7F80) == 0x7F80) and np.all((got[nan] & 0x7F) != 0)
+    assert np.array_equal(got[nan] >> 15, (x[nan].view(np.uint32) >> 31).astype(np.uint16))
+
+
+def test_f16_rne_matches_numpy():
+    x = _structured_f32_sample()
+    got = oracle.convert(x, "f16")
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    nan = np.isnan(x)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.all((got[nan] & 0x7C00) == 0x7C00) and np.all((got[nan] & 0x3FF) != 0)
+
+
+def test_f16_rne_overflow_and_subnormal_edges():
+    cases = {65504.0: 0x7BFF, 65519.99: 0x7BFF, 65520.0: 0x7C00, 2.0 ** -24: 0x0001,
+             2.0 ** -25: 0x0000, 1.5 * 2.0 ** -25: 0x0001, 3 * 2.0 ** -25: 0x0002,
+             2.0 ** -14: 0x0400, -0.0: 0x8000}
+    for v, bits in cases.items():
+        assert int(oracle.convert(np.array([v], np.float32), "f16")[0]) == bits, v
+
+
+def test_e4m3fn_all_words_match_torch():
+    words = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = words.view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    got = np.array([oracle.e4m3fn_to_f32(w) for w in range(256)], dtype=np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and set(np.nonzero(nan)[0]) == {0x7F, 0xFF}
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_float_output_types_match_libraries():
+    for fmt in ("gguf:q4_k", "gguf:iq2_xxs", "gguf:mxfp4", "nvfp4", "gguf:q8_k"):
+        _, B, S, T = oracle.info(fmt)
+        p = synth.payload(fmt, 64, 11, synth.raw() if fmt != "nvfp4" else RECIPE)
+        shape = [64 * B]
+        f32 = oracle.decode(fmt, p, shape, "f32")
+        nan = np.isnan(f32)
+        bf = oracle.decode(fmt, p, shape, "bf16")
+        ref_bf = torch.from_numpy(f32.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(bf[~nan], ref_bf[~nan])
+        with np.errstate(over="ignore"):
+            ref_h = f32.astype(np.float16).view(np.uint16)
+        assert np.array_equal(oracle.decode(fmt, p, shape, "f16")[~nan], ref_h[~nan])
+        f64 = oracle.decode(fmt, p, shape, "f64")
+        assert np.array_equal(f64[~nan], f32[~nan].astype(np.float64))
+        assert np.array_equal(np.isnan(f64), nan)
+
+
+# --------------------------------------------------------------------------
+# Scale decodes: closed forms and library routines.
+# --------------------------------------------------------------------------
+E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]  # NInfer page 3.3, positive code words
+
+
+def test_mxfp4_every_exponent_byte_and_code():
+    """Half scale x doubled E2M1 equals the OCP MX value 2^(e-127) * E2M1(code);
+    both zeros are +0; e = 255 keeps the page's 2^127 half scale."""
+    blocks = []
+    for e in range(256):
+        blocks.append(bytes([e]) + bytes([c | (c << 4) for c in range(16)]))
+    y = oracle.decode_blocks_f32("gguf:mxfp4", np.frombuffer(b"".join(blocks), np.uint8))
+    y = y.reshape(256, 32)
+    for e in range(256):
+        for code in range(16):
+            mag = E2M1[code & 7]
+            sign = -1.0 if (code & 8) and mag != 0 else 1.0
+            with np.errstate(over="ignore"):
+                ref = np.float32(sign * math.ldexp(mag, e - 127)) if e < 255 else \
+                    np.float32(sign * mag * 2.0 * 2.0 ** 127)
+            for j in (code, 16 + code):
+                assert y[e, j].view(np.uint32) == np.array(ref).view(np.uint32), (e, code)
+    # e = 127: the plain E2M1 values (scale 1.0)
+    assert list(y[127, :8]) == E2M1
+
+
+def test_gguf_nvfp4_every_scale_byte_and_code():
+    """Half scale = unsigned E4M3 value / 2 with bit 7 ignored, computed with
+    PyTorch's float8_e4m3fn on the low 7 bits; the whole byte 127 gives 0 and
+    0xFF (E=15, m=7 once bit 7 is dropped) gives 240."""
+    low7 = torch.arange(128, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    ue4m3 = low7.to(torch.float32).numpy()
+    blocks = []
+    for e in range(256):
+        blocks.append(bytes([e, 0x38, 0x38, 0x38]) + bytes([c | (c << 4) for c in range(8)] +
+                                                           [(c + 8) | ((c + 8) << 4) for c in range(8)]) +
+                      bytes(16))
+    y = oracle.decode_blocks_f32("gguf:nvfp4", np.frombuffer(b"".join(blocks), np.uint8)).reshape(256, 64)
+    V = [0, 1, 2, 3, 4, 6, 8, 12, 0, -1, -2, -3, -4, -6, -8, -12]
+    for e in range(256):
+        if e == 127:
+            half = 0.0
+        elif (e & 0x7F) == 0x7F:
+            half = 240.0
+        else:
+            half = float(ue4m3[e & 0x7F]) / 2
+        for j in range(8):
+            assert y[e, j] == np.float32(half * V[j]), (e, j)
+            assert y[e, 8 + j] == np.float32(half * V[j]), (e, j)
+    # spot values of the scale byte
+    assert y[0x38, 1] == 0.5 and y[0x7E, 2] == 448.0 and y[0x01, 2] == 2.0 ** -9
+    assert y[0x80, 2] == 0.0 and y[0xFF, 2] == 480.0
+
+
+# --------------------------------------------------------------------------
+# Q8 family: y = d*q in binary32 (numpy's IEEE multiply); cached fields ignored.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("fmt,doff,qoff,n,dbytes", [
+    ("gguf:q8_0", 0, 2, 32, 2), ("gguf:q8_1", 0, 4, 32, 2), ("gguf:q8_k", 0, 4, 256, 4)])
+def test_q8_is_d_times_q(fmt, doff, qoff, n, dbytes):
+    _, B, S, _ = oracle.info(fmt)
+    p = synth.payload(fmt, 200, 5, synth.raw())
+    y = oracle.decode(fmt, p, [200 * B]).reshape(200, B)
+    blk = p.reshape(200, S)
+    dt = np.float16 if dbytes == 2 else np.float32
+    d = blk[:, doff:doff + dbytes].copy().view(dt).astype(np.float32)
+    q = blk[:, qoff:qoff + n].view(np.int8).astype(np.float32)
+    ref = d * q
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(y), nan)
+    assert np.array_equal(y[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt,start,stop", [("gguf:q8_1", 2, 4), ("gguf:q8_k", 260, 292)])
+def test_q8_cached_sums_ignored(fmt, start, stop):
+    _, B, S, _ = oracle.info(fmt)
+    p = synth.payload(fmt, 16, 9, RECIPE)
+    y0 = oracle.decode(fmt, p, [16 * B])
+    rng = np.random.default_rng(0)
+    for t in range(start, stop):
+        q = p.copy()
+        q.reshape(16, S)[:, t] ^= rng.integers(1, 256, size=16).astype(np.uint8)
+        assert np.array_equal(oracle.decode(fmt, q, [16 * B]).view(np.uint32), y0.view(np.uint32))
+
+
+def test_q1_0_is_plus_minus_d():
+    p = synth.payload("gguf:q1_0", 50, 3, synth.raw())
+    y = oracle.decode("gguf:q1_0", p, [50 * 128]).reshape(50, 128)
+    blk = p.reshape(50, 18)
+    d = blk[:, 0:2].copy().view(np.float16).astype(np.float32)[:, 0]
+    bits = np.unpackbits(blk[:, 2:], axis=1, bitorder="little")
+    ref = np.where(bits == 1, d[:, None], -d[:, None])
+    nan = np.isnan(ref)
+    assert np.array_equal(y[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+# --------------------------------------------------------------------------
+# nvfp4 with divisor (NInfer page 3.3): the exact product e2m1 * e4m3fn is
+# divided once; numpy computes the quotient in binary64 and rounds to
+# binary32 (double rounding is innocuous for division at 53 >= 2*24+2 bits).
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("d_w", [1.0, 3.0, 448.0, 7.1234567, 1e-30, 3.4e38])
+def test_nvfp4_divisor_against_binary64(d_w):
+    scales = list(range(0x00, 0x7F))  # every valid (sign-zero, finite) scale word
+    e4 = torch.tensor(scales, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    e4 = e4.to(torch.float64).numpy()
+    blocks = b""
+    for s in scales:
+        blocks += bytes([s, s, s, s]) + bytes([c | ((c ^ 8) << 4) for c in range(8)] * 4)
+    n = len(scales)
+    payload = np.frombuffer(blocks + np.array([d_w], "<f4").tobytes(), np.uint8)
+    y = oracle.decode("nvfp4", payload, [n * 64]).reshape(n, 64)
+    dw = float(np.float32(d_w))
+    for bi in range(n):
+        for j in range(16):
+            code = j if j < 8 else (j - 8) ^ 8
+            mag = E2M1[code & 7]
+            e2 = -mag if code & 8 else mag
+            ref = np.float32(np.float64(e2) * e4[bi] / np.float64(dw))
+            assert y[bi, j].view(np.uint32) == np.array(ref).view(np.uint32), (bi, j)
+
+
+# --------------------------------------------------------------------------
+# Codebooks: "IQ codebooks" row counts, value ranges, distinct rows.
+# --------------------------------------------------------------------------
+ROWS = {"iq2xxs_grid": (256, 8), "iq2xs_grid": (512, 8), "iq2s_grid": (1024, 8),
+        "iq3xxs_grid": (256, 4), "iq3s_grid": (512, 4), "iq1s_grid": (2048, 8)}
+VALUES = {"iq2xxs_grid": {8, 25, 43}, "iq2xs_grid": {8, 25, 43}, "iq2s_grid": {8, 25, 43},
+          "iq3xxs_grid": {4, 12, 20, 28, 36, 44, 52, 62}, "iq3s_grid": {1, 3, 5, 7, 9, 11, 13, 15},
+          "iq1s_grid": {-1, 0, 1}}
+
+
+@pytest.mark.parametrize("book", sorted(ROWS))
+def test_codebook_shape_and_distinct_rows(book):
+    g = oracle.grid(book)
+    assert g.shape == ROWS[book]
+    assert set(np.unique(g)) <= VALUES[book]
+    assert len({tuple(r) for r in g}) == g.shape[0]
+
+
+def test_codebook_fields_in_range_and_spot_rows():
+    assert oracle.grid_bad_fields() == 0
+    assert list(oracle.grid("iq2xxs_grid")[0]) == [8] * 8
+    assert list(oracle.grid("iq1s_grid")[0]) == [-1] * 8
+    assert list(oracle.grid("iq1s_grid")[2047]) == [1] * 8
+    assert list(oracle.grid("iq3s_grid")[0]) == [1] * 4
+    assert list(oracle.grid("iq3xxs_grid")[0]) == [4] * 4
+
+
+# --------------------------------------------------------------------------
+# Hand-derived one-block examples (tests/golden/one_block.json).
+# --------------------------------------------------------------------------
+def _golden():
+    with open(os.path.join(HERE, "golden", "one_block.json")) as f:
+        return json.load(f)["examples"]
+
+
+def _expand(runs, n, bits32=True):
+    out = np.zeros(n, dtype=np.uint32 if bits32 else np.uint16)
+    seen = np.zeros(n, dtype=bool)
+    for lo, hi, v in runs:
+        if isinstance(v, str):
+            w = int(v, 16)
+        else:
+            w = int(np.array([v], np.float32).view(np.uint32)[0])
+        out[lo:hi + 1] = w
+        seen[lo:hi + 1] = True
+    assert seen.all()
+    return out
+
+
+@pytest.mark.parametrize("ex", _golden(), ids=lambda e: e["id"])
+def test_golden_one_block(ex):
+    fmt = ex["format"]
+    _, B, S, T = oracle.info(fmt)
+    p = np.frombuffer(bytes.fromhex(ex["payload"]), np.uint8)
+    y = oracle.decode(fmt, p, [B], "f32")
+    assert np.array_equal(y.view(np.uint32), _expand(ex["expect"], B))
+    if "expect_bf16" in ex:
+        yb = oracle.decode(fmt, p, [B], "bf16")
+        assert np.array_equal(yb, _expand(ex["expect_bf16"], B, bits32=False))
+
+
+# --------------------------------------------------------------------------
+# Second reading: the page's own Python notation, on random corpora.
+# --------------------------------------------------------------------------
+NOTATION = page_notation.load()
+
+
+@pytest.mark.skipif(NOTATION is None, reason="page text not mounted")
+@pytest.mark.parametrize("fmt", GGUF)
+@pytest.mark.parametrize("recipe", [synth.raw(), RECIPE], ids=repr)
+def test_oracle_matches_page_python_notation(fmt, recipe):
+    _, B, S, _ = oracle.info(fmt)
+    nb = 24
+    p = synth.payload(fmt, nb, 77, recipe)
+    y = oracle.decode(fmt, p, [nb * B])
+    ref = []
+    for i in range(nb):
+        ref += NOTATION["decode_block"](list(bytes(p[i * S:(i + 1) * S])), page_notation.kind_of(fmt))
+    ref = np.array(ref, dtype=np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(y), nan)
+    assert np.array_equal(y[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+@pytest.mark.skipif(NOTATION is None, reason="page text not mounted")
+def test_oracle_codebooks_match_page_python_notation():
+    for book in ROWS:
+        g = oracle.grid(book)
+        for r in range(g.shape[0]):
+            assert list(g[r]) == NOTATION["grid"](book, r)
+
+
+# --------------------------------------------------------------------------
+# Structure: flipping one payload bit changes only the outputs the layout
+# table and the element-order rules say it can reach.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("fmt", ALL)
+def test_bit_flip_structure(fmt):
+    _, B, S, T = oracle.info(fmt)
+    m = layout_map.build(fmt)
+    trials = 6
+    base = synth.payload(fmt, trials, 1234, RECIPE)
+    d_w = 3.0
+    blocks = base[:trials * S]
+    y0 = oracle.decode_blocks_f32(fmt, blocks, d_w).reshape(trials, B).view(np.uint32)
+    for key, (kind, outs) in m.m.items():
+        byte, bit = divmod(key, 8)
+        flipped = blocks.copy().reshape(trials, S)
+        flipped[:, byte] ^= np.uint8(1 << bit)
+        y1 = oracle.decode_blocks_f32(fmt, flipped.ravel(), d_w).reshape(trials, B).view(np.uint32)
+        union = set()
+        for t in range(trials):
+            changed = set(np.nonzero(y0[t] != y1[t])[0].tolist())
+            assert changed <= outs, (fmt, byte, bit, sorted(changed - outs)[:8])
+            union |= changed
+        if kind == "exact":
+            assert union == set(outs), (fmt, byte, bit, sorted(set(outs) - union)[:8])
+        elif kind == "some":
+            assert union, (fmt, byte, bit)
