@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Decode throughput of packed block-quantized weights on one MI355X.
+
+A step decodes the whole Llama-3-8B-shaped weight set (226 tensors; formats
+q4_k, q6_k, q8_0, nvfp4, tq2_0 in rotation) to bf16, back to back on one
+stream, with every payload already resident in HBM.  The JSON line reports:
+
+  value          (payload + output bytes of the step) / (seconds per step)
+  roofline       the dominant kernel (most total time) against MI355X HBM
+                 peak: its algorithmic bytes per launch over its mean launch
+                 duration, timed with HIP events on the launch stream
+  cpu_baseline   the oracle, single-threaded on the host, on a bounded sample
+                 (the first eighth of each tensor's blocks)
+  per_format     every format of the step, plus the remaining workloads
+                 (q4_k/q6_k [4096,4096], mxfp4/nvfp4 [14336,4096], the IQ set
+                 [4096,14336] to f32 and bf16), each timed over rotating
+                 replicas so no launch reads a payload out of a warm cache
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+METRIC = "decode GB/s (payload+output) per format & % of HBM peak, 1×MI355X"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+OUT_CODES = {"f32": 0, "f16": 1, "bf16": 2, "f64": 3}
+OUT_SIZE = {"f32": 4, "f16": 2, "bf16": 2, "f64": 8}
+
+
+def log(msg):
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+class Tensor:
+    """One resident payload and its output buffer."""
+
+    def __init__(self, name, fmt, shape, recipe, seed, dtype, staging, torch, nq, synth):
+        info = nq.format_query(fmt)
+        self.name, self.fmt, self.shape, self.dtype = name, fmt, list(shape), dtype
+        self.fid = info.id
+        nel = 1
+        for d in shape:
+            nel *= d
+        self.nelems = nel
+        self.nblocks = nel // info.block_values
+        self.nbytes = self.nblocks * info.block_bytes + info.trailer_bytes
+        host = staging[: self.nbytes]
+        if self.nblocks:
+            synth.fill_into(fmt, self.nblocks, seed, recipe, host.data_ptr())
+        if info.trailer_bytes:
+            bits = synth.divisor_bits(seed)
+            host[self.nblocks * info.block_bytes:] = torch.tensor(
+                [(bits >> (8 * i)) & 0xFF for i in range(4)], dtype=torch.uint8)
+        self.payload = torch.empty(self.nbytes, dtype=torch.uint8, device="cuda:0")
+        self.payload.copy_(host, non_blocking=False)
+        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "f64": torch.float64}[dtype]
+        self.out = torch.empty(nel, dtype=tdt, device="cuda:0")
+        self.algo_bytes = self.nbytes + nel * OUT_SIZE[dtype]
+        self.seed, self.recipe = seed, recipe
+
+    def launch(self, nq, stream_handle):
+        st = nq.dequantize_packed_raw(self.fid, self.payload.data_ptr(), self.nbytes, self.shape,
+                                      OUT_CODES[self.dtype], self.out.data_ptr(), stream_handle)
+        if st != 0:
+            raise nq.NqError(st, self.name)
+
+
+def staging_buffer(torch, tensors, nq):
+    need = 0
+    for _, fmt, shape, _, _ in tensors:
+        info = nq.format_query(fmt)
+        nel = math.prod(shape)
+        need = max(need, nel // info.block_values * info.block_bytes + info.trailer_bytes)
+    return torch.empty(need, dtype=torch.uint8, pin_memory=True)
+
+
+def time_step_set(torch, nq, items, steps, warmup, per_launch_events=True):
+    """Warm up, then time `steps` passes over items; returns wall ms/step and per-item ms lists."""
+    stream = torch.cuda.current_stream()
+    handle = stream.cuda_stream
+    for _ in range(warmup):
+        for it in items:
+            it.launch(nq, handle)
+    torch.cuda.synchronize()
+    evs = []
+    if per_launch_events:
+        evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in items] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for s in range(steps):
+        for i, it in enumerate(items):
+            if per_launch_events:
+                evs[s][i][0].record(stream)
+            it.launch(nq, handle)
+            if per_launch_events:
+                evs[s][i][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    event_ms = start.elapsed_time(end) / steps
+    per_item = [[evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(steps)] for i in range(len(items))] \
+        if per_launch_events else None
+    return wall_ms, event_ms, per_item
+
+
+def per_format_breakdown(items, per_item):
+    agg = {}
+    for it, ms in zip(items, per_item):
+        a = agg.setdefault(it.fmt, {"launches": 0, "ms": 0.0, "bytes": 0})
+        a["launches"] += len(ms)
+        a["ms"] += sum(ms)
+        a["bytes"] += it.algo_bytes * len(ms)
+    out = {}
+    for fmt, a in agg.items():
+        gbps = a["bytes"] / (a["ms"] * 1e-3) / 1e9
+        out[fmt] = {"gbps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                    "launches": a["launches"], "mean_launch_us": round(a["ms"] * 1e3 / a["launches"], 2),
+                    "total_ms": a["ms"], "bytes_per_launch": a["bytes"] / a["launches"]}
+    return out
+
+
+def rotating_measurement(torch, nq, synth, name, fmt, shape, recipe, seed, dtype, staging, launches=60,
+                         footprint=1 << 30):
+    """Mean launch time of one workload over replicas whose total footprint defeats the caches."""
+    first = Tensor(name, fmt, shape, recipe, seed, dtype, staging, torch, nq, synth)
+    reps = max(1, math.ceil(footprint / first.algo_bytes))
+    items = [first]
+    for r in range(1, reps):
+        t = Tensor(name, fmt, shape, recipe, seed, dtype, staging, torch, nq, synth)
+        items.append(t)
+    order = [items[i % reps] for i in range(launches)]
+    _, _, per_item = time_step_set(torch, nq, order, 1, 1, per_launch_events=True)
+    ms = [x[0] for x in per_item]
+    mean_ms = sum(ms) / len(ms)
+    gbps = first.algo_bytes / (mean_ms * 1e-3) / 1e9
+    res = {"shape": shape, "out": dtype, "gbps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+           "mean_launch_us": round(mean_ms * 1e3, 2), "replicas": reps,
+           "elements_per_s": round(first.nelems / (mean_ms * 1e-3), 1), "bytes_per_launch": first.algo_bytes}
+    del items, order, first
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(nq, synth, tensors, fraction=8):
+    """The oracle on the first 1/fraction of every tensor's blocks, one thread."""
+    import numpy as np
+    import oracle
+    total_bytes = 0
+    total_elems = 0
+    secs = 0.0
+    for name, fmt, shape, recipe, seed in tensors:
+        _, B, S, T = oracle.info(fmt)
+        nb = math.prod(shape) // B
+        ns = max(1, nb // fraction)
+        p = synth.payload(fmt, ns, seed, recipe)
+        if T:
+            p[-4:] = np.array([synth.divisor_bits(seed)], "<u4").view(np.uint8)
+        t0 = time.perf_counter()
+        oracle.decode(fmt, p, [ns * B], "bf16")
+        secs += time.perf_counter() - t0
+        total_bytes += p.size + ns * B * 2
+        total_elems += ns * B
+    return {"value": round(total_bytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first 1/{fraction} of the blocks of each of the {len(tensors)} tensors "
+                      f"({total_elems / 1e9:.3f} G values to bf16, {secs:.1f} s on one host core)",
+            "elements_per_s": round(total_elems / secs, 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-per-format", action="store_true", help="skip the rotating per-workload timings")
+    ap.add_argument("--no-launch-events", action="store_true", help="time the step without per-launch events")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
+                    help="first run a plain device copy of this many MiB (for counter calibration)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the decode needs no collective and this build runs on a single "
+              "MI355X; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_quantized_weight_nq_amd as nq
+    import synth
+    from synth import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    nq.library()  # fails loudly if libnq.so is missing
+    log(f"device {torch.cuda.get_device_name(0)}")
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 x {args.calibrate_copy} MiB device copies done")
+        del a, b
+
+    tensors, _ = workloads.config5()
+    staging = staging_buffer(torch, tensors, nq)
+    t0 = time.perf_counter()
+    items = [Tensor(n, f, s, r, sd, "bf16", staging, torch, nq, synth) for n, f, s, r, sd in tensors]
+    torch.cuda.synchronize()
+    log(f"generated and uploaded {len(items)} payloads in {time.perf_counter() - t0:.1f} s")
+    step_bytes = sum(it.algo_bytes for it in items)
+    payload_bytes = sum(it.nbytes for it in items)
+    elems = sum(it.nelems for it in items)
+
+    wall_ms, event_ms, per_item = time_step_set(torch, nq, items, args.steps, args.warmup,
+                                                per_launch_events=not args.no_launch_events)
+    log(f"step: wall {wall_ms:.3f} ms, events {event_ms:.3f} ms")
+    value = step_bytes / (wall_ms * 1e-3) / 1e9
+
+    roofline = None
+    formats = {}
+    if per_item is not None:
+        formats = per_format_breakdown(items, per_item)
+        dom = max(formats, key=lambda f: formats[f]["total_ms"])
+        d = formats[dom]
+        achieved = d["bytes_per_launch"] / (d["mean_launch_us"] * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": dom,
+                    "bytes_per_launch": round(d["bytes_per_launch"]), "mean_launch_us": d["mean_launch_us"]}
+        for f in formats.values():
+            del f["total_ms"]
+    del items
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if not args.no_per_format:
+        for cfg in (2, 3, 4):
+            ts, dtypes = workloads.CONFIGS[cfg]()
+            st2 = staging_buffer(torch, ts, nq)
+            for name, fmt, shape, recipe, seed in ts:
+                for dt in dtypes:
+                    key = f"{name}->{dt}"
+                    extra[key] = rotating_measurement(torch, nq, synth, name, fmt, shape, recipe, seed, dt, st2)
+                    log(f"{key}: {extra[key]['gbps']} GB/s ({100 * extra[key]['frac_hbm_peak']:.1f}% of peak)")
+            del st2
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(nq, synth, tensors)
+        log(f"cpu baseline: {cpu['value']} GB/s ({cpu['sample']})")
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "llama3-8b weight set: 226 tensors, q4_k/q6_k/q8_0/nvfp4/tq2_0 rotation -> bf16",
+                   "tensors": len(tensors), "elements": elems, "payload_bytes": payload_bytes,
+                   "output_bytes": step_bytes - payload_bytes, "event_ms_per_step": round(event_ms, 4),
+                   "frac_hbm_peak": round(value / HBM_PEAK_GBPS, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_format": {"step": formats, "workloads": extra},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,162 @@
+"""Python binding of libnq.so, the MI355X (gfx950) packed-weight decoder.
+
+Argument marshalling only: every step of a decode runs in the library's HIP
+kernels behind the C ABI of include/nq.h.  PyTorch supplies device memory
+and streams.  There is no fallback: if libnq.so is missing, every call raises.
+
+    import torch, block_quantized_weight_nq_amd as nq
+    y = nq.dequantize_packed("gguf:q4_k", payload_u8_cuda, [4096, 4096], torch.bfloat16)
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnq.so")
+
+NQ_OK = 0
+STATUS_NAMES = {0: "NQ_OK", 1: "NQ_ERR_NULL_ARG", 2: "NQ_ERR_UNKNOWN_FORMAT", 3: "NQ_ERR_BAD_RANK",
+                4: "NQ_ERR_BAD_DIM", 5: "NQ_ERR_NOT_BLOCK_ALIGNED", 6: "NQ_ERR_LENGTH_MISMATCH",
+                7: "NQ_ERR_OVERFLOW", 8: "NQ_ERR_BAD_DTYPE", 9: "NQ_ERR_HIP"}
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "f64": 3}
+FAMILIES = {0: "simple", 1: "kquant", 2: "iq", 3: "fp4", 4: "ternary"}
+EXPORTS = ["nq_format_count", "nq_format_by_id", "nq_format_query", "nq_validate",
+           "nq_dequantize_packed", "nq_status_string"]
+
+
+class NqError(RuntimeError):
+    def __init__(self, status, what=""):
+        self.status = status
+        msg = _lib().nq_status_string(status).decode()
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}{(' (' + what + ')') if what else ''}")
+
+
+class FormatInfo(ctypes.Structure):
+    _fields_ = [("id", ctypes.c_int32), ("name", ctypes.c_char_p), ("block_values", ctypes.c_int32),
+                ("block_bytes", ctypes.c_int32), ("trailer_bytes", ctypes.c_int32),
+                ("family", ctypes.c_int32)]
+
+    def __repr__(self):
+        return (f"FormatInfo(id={self.id}, name={self.name.decode()!r}, B={self.block_values}, "
+                f"S={self.block_bytes}, trailer={self.trailer_bytes}, family={FAMILIES[self.family]})")
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                              "python block_quantized_weight_nq_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        c = ctypes
+        L.nq_format_count.restype = c.c_int
+        L.nq_format_by_id.argtypes = [c.c_int32, c.POINTER(FormatInfo)]
+        L.nq_format_query.argtypes = [c.c_char_p, c.POINTER(FormatInfo)]
+        L.nq_validate.argtypes = [c.c_int32, c.c_uint64, c.POINTER(c.c_int64), c.c_int32, c.c_int32,
+                                  c.POINTER(c.c_uint64), c.POINTER(c.c_uint64)]
+        L.nq_dequantize_packed.argtypes = [c.c_int32, c.c_void_p, c.c_uint64, c.POINTER(c.c_int64),
+                                           c.c_int32, c.c_int32, c.c_void_p, c.c_void_p]
+        L.nq_status_string.argtypes = [c.c_int]
+        L.nq_status_string.restype = c.c_char_p
+        _LIB = L
+    return _LIB
+
+
+def library():
+    """The loaded ctypes library (raises if not built)."""
+    return _lib()
+
+
+def format_count():
+    return _lib().nq_format_count()
+
+
+def format_by_id(i):
+    info = FormatInfo()
+    st = _lib().nq_format_by_id(i, ctypes.byref(info))
+    if st != NQ_OK:
+        raise NqError(st, f"id {i}")
+    return info
+
+
+def format_query(name):
+    info = FormatInfo()
+    st = _lib().nq_format_query(name.encode(), ctypes.byref(info))
+    if st != NQ_OK:
+        raise NqError(st, repr(name))
+    return info
+
+
+def format_names():
+    return [format_by_id(i).name.decode() for i in range(format_count())]
+
+
+def _shape(shape):
+    shape = [int(d) for d in shape]
+    return (ctypes.c_int64 * max(1, len(shape)))(*shape), len(shape)
+
+
+def _dtype_code(dtype):
+    if isinstance(dtype, str):
+        return DTYPE_CODES[dtype]
+    import torch
+    return {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.float64: 3}[dtype]
+
+
+def validate_status(fmt, nbytes, shape, out_dtype="f32"):
+    """Raw status of nq_validate plus (elems, out_bytes)."""
+    fid = fmt if isinstance(fmt, int) else format_query(fmt).id
+    arr, rank = _shape(shape)
+    ne, nb = ctypes.c_uint64(), ctypes.c_uint64()
+    code = out_dtype if isinstance(out_dtype, int) else _dtype_code(out_dtype)
+    st = _lib().nq_validate(fid, nbytes, arr, rank, code, ctypes.byref(ne), ctypes.byref(nb))
+    return st, ne.value, nb.value
+
+
+def validate(fmt, nbytes, shape, out_dtype="f32"):
+    st, ne, nb = validate_status(fmt, nbytes, shape, out_dtype)
+    if st != NQ_OK:
+        raise NqError(st)
+    return ne, nb
+
+
+def dequantize_packed_raw(fmt_id, payload_ptr, nbytes, shape, out_dtype_code, out_ptr, stream_handle):
+    """Direct call of the C entry point with integer addresses; returns the status."""
+    arr, rank = _shape(shape)
+    return _lib().nq_dequantize_packed(fmt_id, ctypes.c_void_p(payload_ptr), nbytes, arr, rank,
+                                       out_dtype_code, ctypes.c_void_p(out_ptr),
+                                       ctypes.c_void_p(stream_handle))
+
+
+def dequantize_packed(fmt, payload, shape, out_dtype=None, out=None, stream=None):
+    """Decode a rank-1 uint8 CUDA tensor into a new (or the given) tensor of `shape`.
+
+    out_dtype: torch.float32 (default), torch.float16, torch.bfloat16 or torch.float64.
+    The decode is enqueued on `stream` (default: the current stream).
+    """
+    import torch
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.float32
+    code = _dtype_code(out_dtype)
+    fid = fmt if isinstance(fmt, int) else format_query(fmt).id
+    if payload.dtype != torch.uint8 or payload.dim() != 1 or not payload.is_cuda:
+        raise ValueError("payload must be a rank-1 torch.uint8 CUDA tensor")
+    if not payload.is_contiguous():
+        raise ValueError("payload must be contiguous")
+    n = 1
+    for d in shape:
+        n *= int(d)
+    if out is None:
+        out = torch.empty([int(d) for d in shape], dtype=out_dtype, device=payload.device)
+    elif (out.dtype != out_dtype or not out.is_contiguous() or out.numel() != n or
+          (n and out.device != payload.device)):
+        raise ValueError("out must be a contiguous tensor of the requested dtype, size and device")
+    if stream is None:
+        stream = torch.cuda.current_stream(payload.device)
+    st = dequantize_packed_raw(fid, payload.data_ptr(), payload.numel(), shape, code,
+                               out.data_ptr(), stream.cuda_stream)
+    if st != NQ_OK:
+        raise NqError(st, f"{fmt} {list(shape)}")
+    return out

@@ -1,0 +1,72 @@
+"""Build libnq.so (gfx950) in-tree with hipcc.
+
+Each kernel family compiles as its own translation unit (in parallel), then
+everything links into one shared library exporting the C ABI of
+include/nq.h.  Flags that matter for exactness:
+
+* ``-ffp-contract=off``: no fused multiply-add; every page operation is its
+  own binary32 rounding;
+* fp32 / fp16 denormals stay enabled (HIP's default; the kernel descriptors
+  carry denorm mode 3);
+* ``-fhip-fp32-correctly-rounded-divide-sqrt``: the "nvfp4" quotient is a
+  correctly rounded division;
+* ``-Xclang -target-feature -Xclang -packed-fp32-ops`` is passed as given (the
+  build never emits packed-fp32 VALU instructions).
+"""
+import concurrent.futures
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libnq.so")
+ARCH = os.environ.get("NQ_OFFLOAD_ARCH", "gfx950")
+
+KERNEL_SOURCES = ["k_simple.hip", "k_kquant.hip", "k_iq.hip", "k_fp4.hip", "k_ternary.hip"]
+HOST_SOURCES = ["nq_abi.cpp"]
+
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-ffp-contract=off",
+          "-fno-fast-math", "-Wall", "-Wno-unused-function"]
+DEVICE = [f"--offload-arch={ARCH}", "-fhip-fp32-correctly-rounded-divide-sqrt",
+          "-fno-gpu-flush-denormals-to-zero",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _hipcc():
+    for c in ("/opt/rocm/bin/hipcc", "hipcc"):
+        if os.path.exists(c) or c == "hipcc":
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def _compile(src, is_kernel):
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [_hipcc(), *COMMON, *DEVICE, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build(jobs=None, verbose=False):
+    """Compile every source and link libnq.so; returns the library path."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = jobs or min(8, os.cpu_count() or 4)
+    work = [(s, True) for s in KERNEL_SOURCES + HOST_SOURCES]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda a: _compile(*a), work))
+    tmp = LIB + ".tmp"
+    cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}", file=sys.stderr)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

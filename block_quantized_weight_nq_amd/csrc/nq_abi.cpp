@@ -1,0 +1,171 @@
+// nq_abi.cpp -- the C ABI: closed format registry, the length rule, launch.
+//
+// Registry and rule: ONNX "DequantizePacked decoding specification",
+// sections "Format identifiers" (27 case-sensitive identifiers, no
+// parameters, unknown spellings are errors; the length rule) and
+// "Quantization formats" (B, S); "nvfp4" is section 3.3 of the NInfer
+// "tensor-formats" page carried as gguf:nvfp4 blocks plus a 4-byte binary32
+// divisor.
+#include <atomic>
+#include <string.h>
+
+#include "../../include/nq.h"
+#include "nq_launch.h"
+
+#define NQ_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+struct Entry {
+    const char *name;
+    int family;
+};
+
+// Index = nq::Fmt id.
+const Entry REGISTRY[nq::NUM_FORMATS] = {
+    {"gguf:q4_0", NQ_FAMILY_SIMPLE},    {"gguf:q4_1", NQ_FAMILY_SIMPLE},
+    {"gguf:q5_0", NQ_FAMILY_SIMPLE},    {"gguf:q5_1", NQ_FAMILY_SIMPLE},
+    {"gguf:q8_0", NQ_FAMILY_SIMPLE},    {"gguf:q8_1", NQ_FAMILY_SIMPLE},
+    {"gguf:q2_k", NQ_FAMILY_KQUANT},    {"gguf:q3_k", NQ_FAMILY_KQUANT},
+    {"gguf:q4_k", NQ_FAMILY_KQUANT},    {"gguf:q5_k", NQ_FAMILY_KQUANT},
+    {"gguf:q6_k", NQ_FAMILY_KQUANT},    {"gguf:q8_k", NQ_FAMILY_KQUANT},
+    {"gguf:iq2_xxs", NQ_FAMILY_IQ},     {"gguf:iq2_xs", NQ_FAMILY_IQ},
+    {"gguf:iq3_xxs", NQ_FAMILY_IQ},     {"gguf:iq1_s", NQ_FAMILY_IQ},
+    {"gguf:iq4_nl", NQ_FAMILY_SIMPLE},  {"gguf:iq3_s", NQ_FAMILY_IQ},
+    {"gguf:iq2_s", NQ_FAMILY_IQ},       {"gguf:iq4_xs", NQ_FAMILY_KQUANT},
+    {"gguf:iq1_m", NQ_FAMILY_IQ},       {"gguf:tq1_0", NQ_FAMILY_TERNARY},
+    {"gguf:tq2_0", NQ_FAMILY_TERNARY},  {"gguf:mxfp4", NQ_FAMILY_FP4},
+    {"gguf:nvfp4", NQ_FAMILY_FP4},      {"gguf:q1_0", NQ_FAMILY_SIMPLE},
+    {"gguf:q2_0", NQ_FAMILY_SIMPLE},    {"nvfp4", NQ_FAMILY_FP4},
+};
+
+constexpr int B_OF(int f) { return nq::block_values(f); }
+constexpr int S_OF(int f) { return nq::block_bytes(f); }
+constexpr int TRAILER_OF(int f) { return f == nq::NVFP4_DIV ? 4 : 0; }
+constexpr uint64_t OUT_SIZE[4] = {4, 2, 2, 8};
+constexpr uint64_t I64MAX = 0x7FFFFFFFFFFFFFFFull;
+
+// a * b if it stays <= INT64_MAX.
+bool mul_checked(uint64_t a, uint64_t b, uint64_t *r) {
+    if (a != 0 && b > I64MAX / a) return false;
+    *r = a * b;
+    return true;
+}
+
+void fill_info(int id, nq_format_info *out) {
+    out->id = id;
+    out->name = REGISTRY[id].name;
+    out->block_values = B_OF(id);
+    out->block_bytes = S_OF(id);
+    out->trailer_bytes = TRAILER_OF(id);
+    out->family = REGISTRY[id].family;
+}
+
+// Compute units per device, looked up once per device.
+constexpr int MAX_DEVICES = 64;
+std::atomic<int> g_cu_count[MAX_DEVICES];
+
+uint32_t max_workgroups() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return 2048;
+    int cu = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cu <= 0) {
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
+            cu = 256;
+        g_cu_count[dev].store(cu, std::memory_order_relaxed);
+    }
+    return (uint32_t)cu * 8u;  // 8 workgroups of 256 threads = 32 waves per CU
+}
+
+}  // namespace
+
+NQ_API int nq_format_count(void) { return nq::NUM_FORMATS; }
+
+NQ_API int nq_format_by_id(int32_t id, nq_format_info *out) {
+    if (!out) return NQ_ERR_NULL_ARG;
+    if (id < 0 || id >= nq::NUM_FORMATS) return NQ_ERR_UNKNOWN_FORMAT;
+    fill_info(id, out);
+    return NQ_OK;
+}
+
+NQ_API int nq_format_query(const char *name, nq_format_info *out) {
+    if (!name || !out) return NQ_ERR_NULL_ARG;
+    for (int id = 0; id < nq::NUM_FORMATS; id++) {
+        if (strcmp(REGISTRY[id].name, name) == 0) {
+            fill_info(id, out);
+            return NQ_OK;
+        }
+    }
+    return NQ_ERR_UNKNOWN_FORMAT;
+}
+
+NQ_API int nq_validate(int32_t format, uint64_t nbytes, const int64_t *shape, int32_t rank,
+                       int32_t out_dtype, uint64_t *out_elems, uint64_t *out_bytes) {
+    if (format < 0 || format >= nq::NUM_FORMATS) return NQ_ERR_UNKNOWN_FORMAT;
+    if (out_dtype < NQ_F32 || out_dtype > NQ_F64) return NQ_ERR_BAD_DTYPE;
+    if (rank < 1) return NQ_ERR_BAD_RANK;
+    if (!shape) return NQ_ERR_NULL_ARG;
+    bool empty = false;
+    for (int32_t i = 0; i < rank; i++) {
+        if (shape[i] < 0) return NQ_ERR_BAD_DIM;
+        if (shape[i] == 0) empty = true;
+    }
+    const uint64_t B = (uint64_t)B_OF(format), S = (uint64_t)S_OF(format);
+    const uint64_t K = (uint64_t)shape[rank - 1];
+    if (K % B != 0) return NQ_ERR_NOT_BLOCK_ALIGNED;
+    uint64_t elems = 0, bytes = 0;
+    if (!empty) {
+        uint64_t rows = 1, blocks = 0, wide = 0;
+        for (int32_t i = 0; i + 1 < rank; i++)
+            if (!mul_checked(rows, (uint64_t)shape[i], &rows)) return NQ_ERR_OVERFLOW;
+        if (!mul_checked(rows, K / B, &blocks) || !mul_checked(blocks, S, &bytes) ||
+            !mul_checked(rows, K, &elems) || !mul_checked(elems, 8, &wide))
+            return NQ_ERR_OVERFLOW;
+    }
+    bytes += (uint64_t)TRAILER_OF(format);
+    if (bytes > I64MAX) return NQ_ERR_OVERFLOW;
+    if (nbytes != bytes) return NQ_ERR_LENGTH_MISMATCH;
+    if (out_elems) *out_elems = elems;
+    if (out_bytes) *out_bytes = elems * OUT_SIZE[out_dtype];
+    return NQ_OK;
+}
+
+NQ_API int nq_dequantize_packed(int32_t format, const void *payload, uint64_t nbytes, const int64_t *shape,
+                                int32_t rank, int32_t out_dtype, void *out, hipStream_t stream) {
+    uint64_t elems = 0;
+    const int st = nq_validate(format, nbytes, shape, rank, out_dtype, &elems, nullptr);
+    if (st != NQ_OK) return st;
+    if (nbytes > 0 && !payload) return NQ_ERR_NULL_ARG;
+    if (elems == 0) return NQ_OK;
+    if (!out) return NQ_ERR_NULL_ARG;
+    if (((uintptr_t)out % OUT_SIZE[out_dtype]) != 0) return NQ_ERR_NULL_ARG;
+    nq::LaunchArgs L;
+    L.payload = (const uint8_t *)payload;
+    L.nbytes = nbytes;
+    L.nblocks = elems / (uint64_t)B_OF(format);
+    L.out = out;
+    L.max_wgs = max_workgroups();
+    switch (REGISTRY[format].family) {
+    case NQ_FAMILY_SIMPLE: return nq::launch_simple(format, out_dtype, L, stream);
+    case NQ_FAMILY_KQUANT: return nq::launch_kquant(format, out_dtype, L, stream);
+    case NQ_FAMILY_IQ: return nq::launch_iq(format, out_dtype, L, stream);
+    case NQ_FAMILY_FP4: return nq::launch_fp4(format, out_dtype, L, stream);
+    default: return nq::launch_ternary(format, out_dtype, L, stream);
+    }
+}
+
+NQ_API const char *nq_status_string(int status) {
+    switch (status) {
+    case NQ_OK: return "ok";
+    case NQ_ERR_NULL_ARG: return "a required pointer is NULL or misaligned";
+    case NQ_ERR_UNKNOWN_FORMAT: return "unknown format identifier";
+    case NQ_ERR_BAD_RANK: return "shape rank must be at least 1";
+    case NQ_ERR_BAD_DIM: return "shape has a negative dimension";
+    case NQ_ERR_NOT_BLOCK_ALIGNED: return "last dimension is not a multiple of the block size";
+    case NQ_ERR_LENGTH_MISMATCH: return "payload length differs from the length rule";
+    case NQ_ERR_OVERFLOW: return "byte or element count overflows";
+    case NQ_ERR_BAD_DTYPE: return "unknown output dtype";
+    case NQ_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}

@@ -1,0 +1,335 @@
+// nq_kernel.h -- the decode kernel template and its launcher.
+//
+// Streaming layout: thread t of workgroup w handles units (8 outputs each)
+// u = base + k*256 + t for k < UPT, with base stepping over the grid, so a
+// wave's 64 lanes write 64 consecutive units: one contiguous 1 KiB (bf16/f16)
+// or 2 KiB (f32) run per store instruction.  Each lane reads only the payload
+// dwords its unit needs; lanes of a block share them through the vector L1.
+// IQ formats stage their codebook in LDS once per workgroup; "nvfp4" stages a
+// 256 x 16 table of its correctly rounded quotients.
+#pragma once
+
+#include "iq_grids.h"
+#include "nq_decode.h"
+
+namespace nq {
+
+typedef uint32_t u32x2a4 __attribute__((ext_vector_type(2), aligned(4)));
+typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+
+// Payload source: dword loads from a 4-byte-aligned base; `last` is the index
+// of the last dword that holds payload bytes (loads never go past it).
+struct DevSrc {
+    const uint32_t *base;
+    uint32_t last;
+    template <int N>
+    NQ_HD void load(uint32_t i, uint32_t (&r)[N]) const {
+        const uint32_t *p = base + i;
+        if constexpr (N == 1) {
+            r[0] = p[0];
+        } else if constexpr (N == 2) {
+            const u32x2a4 v = *(const u32x2a4 *)p;
+            r[0] = v.x;
+            r[1] = v.y;
+        } else if constexpr (N == 3) {
+            const u32x2a4 v = *(const u32x2a4 *)p;
+            r[0] = v.x;
+            r[1] = v.y;
+            r[2] = p[2];
+        } else {
+            const u32x4a4 v = *(const u32x4a4 *)p;
+            r[0] = v.x;
+            r[1] = v.y;
+            r[2] = v.z;
+            r[3] = v.w;
+        }
+    }
+    NQ_HD uint32_t dw(uint32_t i) const { return base[i]; }
+};
+
+// Two-pass source pair.  No payload address depends on loaded data, so a
+// decoder's loads form a fixed sequence.  Pass 1 runs the decoder over a
+// Recorder, which issues the loads and keeps the raw dwords (the arithmetic
+// of that pass is dead and compiled away); pass 2 runs it over a Player,
+// which hands the same dwords back in the same order.  Every unit of a
+// thread thus has its loads in flight before any of them is consumed.
+constexpr int RAW_CAP = 16;  // dwords one unit may load
+
+template <class Base>
+struct Recorder {
+    Base src;
+    uint32_t *buf;
+    mutable int n;
+    uint32_t last;
+    template <int N>
+    NQ_HD void load(uint32_t i, uint32_t (&r)[N]) const {
+        src.template load<N>(i, r);
+#pragma unroll
+        for (int k = 0; k < N; k++) buf[n++] = r[k];
+    }
+    NQ_HD uint32_t dw(uint32_t i) const {
+        const uint32_t v = src.dw(i);
+        buf[n++] = v;
+        return v;
+    }
+};
+
+struct Player {
+    const uint32_t *buf;
+    mutable int n;
+    uint32_t last;
+    template <int N>
+    NQ_HD void load(uint32_t, uint32_t (&r)[N]) const {
+#pragma unroll
+        for (int k = 0; k < N; k++) r[k] = buf[n++];
+    }
+    NQ_HD uint32_t dw(uint32_t) const { return buf[n++]; }
+};
+
+// Lookup tables (LDS in the kernels, host arrays in the emulator).
+struct Tab {
+    const uint64_t *t8;
+    const uint32_t *t4;
+    const float *nvq;
+    NQ_HD uint64_t iq2xxs(uint32_t r) const { return t8[r]; }
+    NQ_HD uint64_t iq2xs(uint32_t r) const { return t8[r]; }
+    NQ_HD uint64_t iq2s(uint32_t r) const { return t8[r]; }
+    NQ_HD uint64_t iq1s(uint32_t r) const { return t8[r]; }
+    NQ_HD uint32_t iq3xxs(uint32_t r) const { return t4[r]; }
+    NQ_HD uint32_t iq3s(uint32_t r) const { return t4[r]; }
+    NQ_HD float nv(uint32_t k) const { return nvq[k]; }
+};
+
+// Table sizes per format.
+template <int F>
+struct TabSpec {
+    static constexpr int n8 = F == IQ2_XXS ? 256 : F == IQ2_XS ? 512 : F == IQ2_S ? 1024
+                            : (F == IQ1_S || F == IQ1_M) ? 2048 : 0;
+    static constexpr int n4 = F == IQ3_XXS ? 256 : F == IQ3_S ? 512 : 0;
+    static constexpr int nf = F == NVFP4_DIV ? 4096 : 0;
+    NQ_HD static const uint64_t *src8() {
+        return F == IQ2_XXS ? NQ_GRID_IQ2XXS : F == IQ2_XS ? NQ_GRID_IQ2XS : F == IQ2_S ? NQ_GRID_IQ2S
+                                                                                     : NQ_GRID_IQ1S;
+    }
+    NQ_HD static const uint32_t *src4() { return F == IQ3_XXS ? NQ_GRID_IQ3XXS : NQ_GRID_IQ3S; }
+};
+
+// Kernel arguments for one launch (one chunk of whole blocks).
+struct KArgs {
+    const uint32_t *base;     // payload of this chunk, aligned down to 4 bytes
+    const uint32_t *tr_base;  // "nvfp4" divisor, aligned down to 4 bytes
+    void *out;                // output element 0 of this chunk
+    uint32_t mis;             // payload start - base (0..3)
+    uint32_t last;            // last payload dword of this chunk, from base
+    uint32_t tr_mis;          // divisor address - tr_base (0..3)
+    uint32_t nunits;          // units in this chunk
+};
+
+// Output conversion and store of one unit (8 values) at element 8u.
+// Conversion happens once, from the binary32 value, with round-to-nearest-
+// even (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32 under the default round mode).
+template <int OT, bool VEC>
+NQ_HD void store8(void *out, uint32_t u, const float (&y)[8]) {
+    const uint64_t e = 8ull * u;
+    if constexpr (OT == 0) {
+        float *o = (float *)out + e;
+        if constexpr (VEC) {
+            u32x4 a, b;
+            a.x = __builtin_bit_cast(uint32_t, y[0]); a.y = __builtin_bit_cast(uint32_t, y[1]);
+            a.z = __builtin_bit_cast(uint32_t, y[2]); a.w = __builtin_bit_cast(uint32_t, y[3]);
+            b.x = __builtin_bit_cast(uint32_t, y[4]); b.y = __builtin_bit_cast(uint32_t, y[5]);
+            b.z = __builtin_bit_cast(uint32_t, y[6]); b.w = __builtin_bit_cast(uint32_t, y[7]);
+            *(u32x4 *)o = a;
+            *(u32x4 *)(o + 4) = b;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; k++) o[k] = y[k];
+        }
+    } else if constexpr (OT == 1 || OT == 2) {
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            f32x2 v;
+            v.x = y[2 * k];
+            v.y = y[2 * k + 1];
+            if constexpr (OT == 2)
+                w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+            else
+                w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+        }
+        uint16_t *o = (uint16_t *)out + e;
+        if constexpr (VEC) {
+            u32x4 a;
+            a.x = w[0]; a.y = w[1]; a.z = w[2]; a.w = w[3];
+            *(u32x4 *)o = a;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; k++) o[k] = (uint16_t)(w[k >> 1] >> (16 * (k & 1)));
+        }
+    } else {
+        double *o = (double *)out + e;
+        if constexpr (VEC) {
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                f64x2 v;
+                v.x = (double)y[2 * k];
+                v.y = (double)y[2 * k + 1];
+                *(f64x2 *)(o + 2 * k) = v;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; k++) o[k] = (double)y[k];
+        }
+    }
+}
+
+constexpr int WG = 256;  // threads per workgroup (4 wave64)
+
+// One thread's share of a launch: the grid-stride loop over units.
+template <int F, int OT, int UPT, bool VEC, class Src, class T>
+NQ_HD void process(const Src &src, const T &tab, const KArgs &a, uint32_t bid, uint32_t nwg, uint32_t tid) {
+    constexpr uint32_t UPB = block_values(F) / 8;
+    constexpr uint32_t S = block_bytes(F);
+    const uint32_t step = nwg * (uint32_t)(WG * UPT);
+    for (uint32_t u0 = bid * (uint32_t)(WG * UPT); u0 < a.nunits; u0 += step) {
+        if (u0 + (uint32_t)(WG * UPT) <= a.nunits) {
+            uint32_t raw[UPT][RAW_CAP];
+            float y[UPT][8];
+#pragma unroll
+            for (int k = 0; k < UPT; k++) {  // pass 1: every load of every unit
+                const uint32_t u = u0 + (uint32_t)(k * WG) + tid;
+                const Recorder<Src> rec{src, raw[k], 0, src.last};
+                float dead[8];
+                decode_unit<F>(rec, a.mis + (u / UPB) * S, u % UPB, tab, dead);
+            }
+#pragma unroll
+            for (int k = 0; k < UPT; k++) {  // pass 2: the arithmetic
+                const uint32_t u = u0 + (uint32_t)(k * WG) + tid;
+                const Player pl{raw[k], 0, src.last};
+                decode_unit<F>(pl, a.mis + (u / UPB) * S, u % UPB, tab, y[k]);
+            }
+#pragma unroll
+            for (int k = 0; k < UPT; k++) store8<OT, VEC>(a.out, u0 + (uint32_t)(k * WG) + tid, y[k]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < UPT; k++) {
+                const uint32_t u = u0 + (uint32_t)(k * WG) + tid;
+                if (u < a.nunits) {
+                    float y[8];
+                    decode_unit<F>(src, a.mis + (u / UPB) * S, u % UPB, tab, y);
+                    store8<OT, VEC>(a.out, u, y);
+                }
+            }
+        }
+    }
+}
+
+// Table setup, strided over `nthreads` cooperating threads.
+template <int F, class TrSrc>
+NQ_HD void fill_tables(uint64_t *t8, uint32_t *t4, float *nvq, const TrSrc &tr, uint32_t tr_mis,
+                       uint32_t tid, uint32_t nthreads) {
+    using TS = TabSpec<F>;
+    if constexpr (TS::n8 > 0) {
+        const uint64_t *g = TS::src8();
+        for (uint32_t r = tid; r < (uint32_t)TS::n8; r += nthreads) t8[r] = g[r];
+    }
+    if constexpr (TS::n4 > 0) {
+        const uint32_t *g = TS::src4();
+        for (uint32_t r = tid; r < (uint32_t)TS::n4; r += nthreads) t4[r] = g[r];
+    }
+    if constexpr (TS::nf > 0) {
+        uint32_t dww[1];
+        window<1>(tr, tr_mis, dww);
+        const float dw = bits_f32(dww[0]);
+        for (uint32_t k = tid; k < (uint32_t)TS::nf; k += nthreads) nvq[k] = e2m1_e4m3_div(k >> 4, k & 15u, dw);
+    }
+}
+
+template <int F, int OT, int UPT, bool VEC>
+__global__ __launch_bounds__(WG) void k_decode(KArgs a) {
+    using TS = TabSpec<F>;
+    __shared__ uint64_t t8[TS::n8 > 0 ? TS::n8 : 1];
+    __shared__ uint32_t t4[TS::n4 > 0 ? TS::n4 : 1];
+    __shared__ float nvq[TS::nf > 0 ? TS::nf : 1];
+    const uint32_t tid = threadIdx.x;
+    if constexpr (TS::n8 + TS::n4 + TS::nf > 0) {
+        fill_tables<F>(t8, t4, nvq, DevSrc{a.tr_base, (a.tr_mis + 3u) >> 2}, a.tr_mis, tid, WG);
+        __syncthreads();
+    }
+    const Tab tab{t8, t4, nvq};
+    process<F, OT, UPT, VEC>(DevSrc{a.base, a.last}, tab, a, blockIdx.x, gridDim.x, tid);
+}
+
+// Host launch description for one call.
+struct LaunchArgs {
+    const uint8_t *payload;  // device
+    uint64_t nbytes;
+    uint64_t nblocks;
+    void *out;               // device
+    uint32_t max_wgs;        // persistent-grid cap for the device
+};
+
+constexpr int UPT_DEFAULT = 2;
+
+// Blocks per launch chunk: unit indices stay below 2^30 and payload byte
+// offsets below 2^32.
+template <int F>
+constexpr uint64_t chunk_blocks() {
+    constexpr uint64_t a = (1ull << 30) / (block_values(F) / 8), b = 0xFFFFFFF0ull / block_bytes(F);
+    return a < b ? a : b;
+}
+
+// Kernel arguments and grid size of the chunk starting at block b0.
+template <int F, int OT, int UPT>
+NQ_HD KArgs chunk_args(const LaunchArgs &L, uint64_t b0, uint64_t nb, uint32_t *grid) {
+    constexpr uint64_t S = block_bytes(F);
+    constexpr uint64_t OSZ = OT == 0 ? 4 : OT == 3 ? 8 : 2;
+    const uint8_t *p = L.payload + b0 * S;
+    const uint8_t *tr = L.payload + L.nbytes - (F == NVFP4_DIV ? 4 : 0);
+    KArgs a;
+    a.base = (const uint32_t *)((uintptr_t)p & ~(uintptr_t)3);
+    a.mis = (uint32_t)((uintptr_t)p & 3);
+    a.last = (uint32_t)((a.mis + nb * S - 1) >> 2);
+    a.tr_base = (const uint32_t *)((uintptr_t)tr & ~(uintptr_t)3);
+    a.tr_mis = (uint32_t)((uintptr_t)tr & 3);
+    a.nunits = (uint32_t)(nb * (block_values(F) / 8));
+    a.out = (uint8_t *)L.out + b0 * (uint64_t)block_values(F) * OSZ;
+    const uint64_t per_wg = (uint64_t)WG * UPT;
+    uint64_t g = (a.nunits + per_wg - 1) / per_wg;
+    *grid = (uint32_t)(g > L.max_wgs ? L.max_wgs : g);
+    return a;
+}
+
+template <int F, int OT>
+int launch(const LaunchArgs &L, hipStream_t stream) {
+    constexpr int UPT = UPT_DEFAULT;
+    constexpr uint64_t CB = chunk_blocks<F>();
+    for (uint64_t b0 = 0; b0 < L.nblocks; b0 += CB) {
+        const uint64_t nb = (L.nblocks - b0 < CB) ? L.nblocks - b0 : CB;
+        uint32_t grid;
+        const KArgs a = chunk_args<F, OT, UPT>(L, b0, nb, &grid);
+        if (((uintptr_t)a.out & 15) == 0)
+            hipLaunchKernelGGL((k_decode<F, OT, UPT, true>), dim3(grid), dim3(WG), 0, stream, a);
+        else
+            hipLaunchKernelGGL((k_decode<F, OT, UPT, false>), dim3(grid), dim3(WG), 0, stream, a);
+        if (hipGetLastError() != hipSuccess) return 9;  // NQ_ERR_HIP
+    }
+    return 0;
+}
+
+template <int F>
+int launch_any(int ot, const LaunchArgs &L, hipStream_t stream) {
+    switch (ot) {
+    case 0: return launch<F, 0>(L, stream);
+    case 1: return launch<F, 1>(L, stream);
+    case 2: return launch<F, 2>(L, stream);
+    default: return launch<F, 3>(L, stream);
+    }
+}
+
+}  // namespace nq

@@ -1,0 +1,120 @@
+/*
+ * nq.h -- C ABI of the MI355X (gfx950) packed-weight decoder.
+ *
+ * The operation is DequantizePacked as defined by the ONNX page
+ * "DequantizePacked decoding specification" (opset 29), section "Signature and
+ * storage": a rank-one payload of packed bytes, a format identifier and a
+ * logical shape decode, block by block in input order, to binary32 values
+ * that are reshaped to `shape` (row-major) and converted once to the output
+ * type, with round-to-nearest-even for FLOAT16 and BFLOAT16.  The formats
+ * are the 27 "gguf:" profiles of that page's identifier table and "nvfp4",
+ * the FP32-divisor format of section 3.3 of the NInfer "tensor-formats" page
+ * (stored as gguf:nvfp4 blocks followed by one little-endian binary32
+ * divisor; see nq_dequantize_packed).
+ *
+ * Every entry point is reentrant and keeps no mutable global state beyond a
+ * per-device cache of the compute-unit count.  No entry point allocates,
+ * frees or retains caller memory.
+ */
+#ifndef NQ_H
+#define NQ_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  Every metadata error is detected on the host before any
+ * launch, so a failed call has written nothing. */
+typedef enum {
+    NQ_OK = 0,
+    NQ_ERR_NULL_ARG = 1,          /* a required pointer is NULL */
+    NQ_ERR_UNKNOWN_FORMAT = 2,    /* name or id outside the closed registry */
+    NQ_ERR_BAD_RANK = 3,          /* rank < 1 */
+    NQ_ERR_BAD_DIM = 4,           /* a negative dimension */
+    NQ_ERR_NOT_BLOCK_ALIGNED = 5, /* shape[rank-1] % B != 0 (also for empty tensors) */
+    NQ_ERR_LENGTH_MISMATCH = 6,   /* nbytes differs from the length rule */
+    NQ_ERR_OVERFLOW = 7,          /* byte count, or element count * 8, beyond INT64_MAX */
+    NQ_ERR_BAD_DTYPE = 8,         /* out_dtype not one of nq_dtype */
+    NQ_ERR_HIP = 9                /* the HIP runtime reported an error at launch */
+} nq_status;
+
+/* Output types: the page's FLOAT, FLOAT16, BFLOAT16 and DOUBLE. */
+typedef enum { NQ_F32 = 0, NQ_F16 = 1, NQ_BF16 = 2, NQ_F64 = 3 } nq_dtype;
+
+/* Kernel family a format decodes in. */
+typedef enum {
+    NQ_FAMILY_SIMPLE = 0,  /* 32/64/128-value blocks: q4_0..q8_1, iq4_nl, q1_0, q2_0 */
+    NQ_FAMILY_KQUANT = 1,  /* 256-value super-blocks: q2_k..q8_k, iq4_xs */
+    NQ_FAMILY_IQ = 2,      /* codebook formats: iq2_xxs, iq2_xs, iq2_s, iq3_xxs, iq3_s, iq1_s, iq1_m */
+    NQ_FAMILY_FP4 = 3,     /* gguf:mxfp4, gguf:nvfp4, nvfp4 */
+    NQ_FAMILY_TERNARY = 4  /* tq1_0, tq2_0 */
+} nq_family;
+
+typedef struct {
+    int32_t id;            /* 0 .. nq_format_count()-1 */
+    const char *name;      /* static string, e.g. "gguf:q4_k" */
+    int32_t block_values;  /* B */
+    int32_t block_bytes;   /* S */
+    int32_t trailer_bytes; /* bytes after the last block: 4 for "nvfp4", else 0 */
+    int32_t family;        /* nq_family */
+} nq_format_info;
+
+/* Number of registered formats (28). */
+int nq_format_count(void);
+
+/* Registry entry by id.  NQ_ERR_NULL_ARG if out is NULL,
+ * NQ_ERR_UNKNOWN_FORMAT if id is out of range. */
+int nq_format_by_id(int32_t id, nq_format_info *out);
+
+/* Registry entry by identifier: exact, case-sensitive match of one of the
+ * page's identifiers ("gguf:q4_0" ... "gguf:q2_0") or "nvfp4".  Other
+ * spellings, including parameterized ones, are NQ_ERR_UNKNOWN_FORMAT
+ * (DequantizePacked page, "Format identifiers"). */
+int nq_format_query(const char *name, nq_format_info *out);
+
+/* Host-only metadata check (no device access).  Applies the length rule of
+ * the DequantizePacked page, "Format identifiers": rank >= 1, every dimension
+ * >= 0, shape[rank-1] % B == 0 (also when another dimension is zero), and
+ * nbytes == prod(shape[:-1]) * (shape[-1] / B) * S, plus 4 trailer bytes for
+ * "nvfp4" (present even for an empty tensor).  On success stores the element
+ * count and the output byte count for out_dtype (either pointer may be
+ * NULL).  shape may be NULL only when rank < 1 (then NQ_ERR_BAD_RANK). */
+int nq_validate(int32_t format, uint64_t nbytes, const int64_t *shape, int32_t rank,
+                int32_t out_dtype, uint64_t *out_elems, uint64_t *out_bytes);
+
+/* Decode a payload into `out`, asynchronously on `stream`.
+ *
+ *   format    registry id (nq_format_query)
+ *   payload   device pointer to nbytes packed bytes, any alignment; block i
+ *             occupies bytes [i*S, (i+1)*S).  For "nvfp4" the last 4 bytes are
+ *             the binary32 divisor d_w.  May be NULL only if nbytes == 0.
+ *   shape     host array of `rank` int64 dimensions (ONNX order, last
+ *             dimension contiguous)
+ *   out_dtype nq_dtype
+ *   out       device pointer to prod(shape) elements of out_dtype, aligned to
+ *             the element size; 16-byte alignment takes the vector-store path.
+ *             May be NULL only if prod(shape) == 0.  Must not overlap payload.
+ *   stream    HIP stream (0 for the null stream)
+ *
+ * Element j of block i is out[i*B + j]: y = DequantizePacked(x) in the flat
+ * row-major order of `shape`.  Ownership stays with the caller; nothing is
+ * retained after return.  The call validates as nq_validate, returns NQ_OK
+ * without launching for an empty tensor, and otherwise enqueues the decode
+ * and returns NQ_OK, or NQ_ERR_HIP if the launch failed.  Payload bytes are
+ * never inspected on the host: every byte pattern of the "gguf:" formats
+ * decodes; for "nvfp4" only sign-zero finite E4M3FN scales and a finite
+ * positive divisor are valid words (NInfer page, section 3.3), and other
+ * words decode deterministically by the same formula. */
+int nq_dequantize_packed(int32_t format, const void *payload, uint64_t nbytes, const int64_t *shape,
+                         int32_t rank, int32_t out_dtype, void *out, hipStream_t stream);
+
+/* Static description of a status code. */
+const char *nq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,111 @@
+// nq_emu.hip -- host emulator of the decode kernels (test infrastructure).
+//
+// Runs the kernels' own per-thread code (process<> from nq_kernel.h) for
+// every workgroup and thread of every launch chunk, sequentially on the CPU,
+// with the launcher's own chunk and grid arithmetic (chunk_args<>).  The
+// payload source checks that every dword read overlaps the payload bytes of
+// its chunk; the caller checks the output guards.  Built host-only.
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "../../block_quantized_weight_nq_amd/csrc/nq_kernel.h"
+
+namespace {
+
+struct Check {
+    uintptr_t lo, hi;  // valid payload byte range [lo, hi)
+    long errors;
+    char msg[256];
+};
+
+struct HostSrc {
+    const uint32_t *base;
+    uint32_t last;
+    Check *chk;
+    template <int N>
+    void load(uint32_t i, uint32_t (&r)[N]) const {
+        for (int k = 0; k < N; k++) r[k] = dw(i + (uint32_t)k);
+    }
+    uint32_t dw(uint32_t i) const {
+        const uintptr_t a = (uintptr_t)(base + i);
+        if (i > last || a + 4 <= chk->lo || a >= chk->hi) {
+            if (chk->errors++ == 0)
+                snprintf(chk->msg, sizeof chk->msg, "dword %u (last %u) at %#lx outside payload [%#lx, %#lx)",
+                         i, last, (unsigned long)a, (unsigned long)chk->lo, (unsigned long)chk->hi);
+        }
+        return base[i];
+    }
+};
+
+template <int F, int OT>
+long run(const uint8_t *payload, uint64_t nbytes, uint64_t nblocks, void *out, uint32_t max_wgs,
+         uint64_t chunk, char *err, int errlen) {
+    using namespace nq;
+    constexpr int UPT = UPT_DEFAULT;
+    constexpr uint64_t S = block_bytes(F);
+    using TS = TabSpec<F>;
+    LaunchArgs L{payload, nbytes, nblocks, out, max_wgs};
+    const uint64_t CB = chunk ? chunk : chunk_blocks<F>();
+    std::vector<uint64_t> t8(TS::n8 > 0 ? TS::n8 : 1);
+    std::vector<uint32_t> t4(TS::n4 > 0 ? TS::n4 : 1);
+    std::vector<float> nvq(TS::nf > 0 ? TS::nf : 1);
+    long errors = 0;
+    for (uint64_t b0 = 0; b0 < nblocks; b0 += CB) {
+        const uint64_t nb = (nblocks - b0 < CB) ? nblocks - b0 : CB;
+        uint32_t grid;
+        const KArgs a = chunk_args<F, OT, UPT>(L, b0, nb, &grid);
+        Check chk{(uintptr_t)(payload + b0 * S), (uintptr_t)(payload + (b0 + nb) * S), 0, {0}};
+        Check chk_tr{(uintptr_t)(payload + nbytes - 4), (uintptr_t)(payload + nbytes), 0, {0}};
+        if (TS::n8 + TS::n4 + TS::nf > 0)
+            for (uint32_t tid = 0; tid < (uint32_t)WG; tid++)
+                fill_tables<F>(t8.data(), t4.data(), nvq.data(), HostSrc{a.tr_base, (a.tr_mis + 3u) >> 2, &chk_tr},
+                               a.tr_mis, tid, WG);
+        const Tab tab{t8.data(), t4.data(), nvq.data()};
+        const HostSrc src{a.base, a.last, &chk};
+        const bool vec = ((uintptr_t)a.out & 15) == 0;
+        for (uint32_t bid = 0; bid < grid; bid++)
+            for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) {
+                if (vec)
+                    process<F, OT, UPT, true>(src, tab, a, bid, grid, tid);
+                else
+                    process<F, OT, UPT, false>(src, tab, a, bid, grid, tid);
+            }
+        for (Check *c : {&chk, &chk_tr})
+            if (c->errors) {
+                if (errors == 0) snprintf(err, errlen, "%s", c->msg);
+                errors += c->errors;
+            }
+    }
+    return errors;
+}
+
+template <int F>
+long run_ot(int ot, const uint8_t *p, uint64_t nbytes, uint64_t nblocks, void *out, uint32_t mw, uint64_t ch,
+            char *err, int errlen) {
+    switch (ot) {
+    case 0: return run<F, 0>(p, nbytes, nblocks, out, mw, ch, err, errlen);
+    case 1: return run<F, 1>(p, nbytes, nblocks, out, mw, ch, err, errlen);
+    case 2: return run<F, 2>(p, nbytes, nblocks, out, mw, ch, err, errlen);
+    default: return run<F, 3>(p, nbytes, nblocks, out, mw, ch, err, errlen);
+    }
+}
+
+}  // namespace
+
+// Returns the number of out-of-payload reads (0 on success), or -1 for a bad format.
+extern "C" __attribute__((visibility("default"))) long nq_emu_decode(int fmt, int ot, const uint8_t *payload,
+                                                                    uint64_t nbytes, uint64_t nblocks, void *out,
+                                                                    uint32_t max_wgs, uint64_t chunk_blocks,
+                                                                    char *err, int errlen) {
+    using namespace nq;
+    switch (fmt) {
+#define C(X) \
+    case X: return run_ot<X>(ot, payload, nbytes, nblocks, out, max_wgs, chunk_blocks, err, errlen);
+        C(Q4_0) C(Q4_1) C(Q5_0) C(Q5_1) C(Q8_0) C(Q8_1) C(Q2_K) C(Q3_K) C(Q4_K) C(Q5_K) C(Q6_K) C(Q8_K)
+        C(IQ2_XXS) C(IQ2_XS) C(IQ3_XXS) C(IQ1_S) C(IQ4_NL) C(IQ3_S) C(IQ2_S) C(IQ4_XS) C(IQ1_M)
+        C(TQ1_0) C(TQ2_0) C(MXFP4) C(NVFP4_GGUF) C(Q1_0) C(Q2_0) C(NVFP4_DIV)
+#undef C
+    default: return -1;
+    }
+}

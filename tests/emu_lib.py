@@ -1,0 +1,69 @@
+"""Build and call the host emulator of the decode kernels (tests/emu/nq_emu.hip)."""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "emu", "nq_emu.hip")
+LIB = os.path.join(HERE, "emu", "libnq_emu.so")
+CSRC = os.path.join(os.path.dirname(HERE), "block_quantized_weight_nq_amd", "csrc")
+OSIZE = {"f32": 4, "f16": 2, "bf16": 2, "f64": 8}
+NPT = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "f64": np.float64}
+_lib = None
+
+
+def build():
+    cmd = ["hipcc", "-x", "hip", "--offload-host-only", "-O1", "-std=c++17", "-fPIC", "-shared",
+           "-ffp-contract=off", "-fvisibility=hidden", SRC, "-o", LIB]
+    subprocess.run(cmd, check=True, capture_output=True)
+
+
+def _stale():
+    if not os.path.exists(LIB):
+        return True
+    t = os.path.getmtime(LIB)
+    deps = [SRC] + [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if _stale():
+            build()
+        L = ctypes.CDLL(LIB)
+        L.nq_emu_decode.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64,
+                                    ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64,
+                                    ctypes.c_char_p, ctypes.c_int]
+        L.nq_emu_decode.restype = ctypes.c_long
+        _lib = L
+    return _lib
+
+
+def _placed(nbytes, align, mis, slack=64):
+    """A uint8 buffer and an offset whose address is `mis` mod `align`."""
+    buf = np.zeros(nbytes + 2 * slack + align, dtype=np.uint8)
+    base = buf.ctypes.data
+    off = slack + ((mis - (base + slack)) % align)
+    return buf, off
+
+
+def decode(fmt_id, payload, nblocks, B, dtype, mis=0, out_mis=0, max_wgs=2048, chunk=0):
+    """Run the emulator; returns (values, out-of-payload reads, message, guards_ok)."""
+    payload = np.ascontiguousarray(payload, dtype=np.uint8)
+    pbuf, poff = _placed(payload.size, 4, mis)
+    pbuf[:] = 0xEE
+    pbuf[poff:poff + payload.size] = payload
+    n = nblocks * B
+    osz = OSIZE[dtype]
+    obuf, ooff = _placed(n * osz, 16, out_mis)
+    obuf[:] = 0xA5
+    err = ctypes.create_string_buffer(256)
+    rc = lib().nq_emu_decode(fmt_id, {"f32": 0, "f16": 1, "bf16": 2, "f64": 3}[dtype],
+                             pbuf.ctypes.data + poff, payload.size, nblocks,
+                             obuf.ctypes.data + ooff, max_wgs, chunk, err, 256)
+    guards = bool(np.all(obuf[:ooff] == 0xA5) and np.all(obuf[ooff + n * osz:] == 0xA5))
+    vals = obuf[ooff:ooff + n * osz].copy().view(NPT[dtype])
+    return vals, rc, err.value.decode(), guards

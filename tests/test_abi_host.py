@@ -1,0 +1,109 @@
+"""The C ABI on the host: exports, registry, length rule, error paths (no GPU).
+
+Only entry points that return before touching the device are called here:
+registry queries, nq_validate, and nq_dequantize_packed calls that fail
+validation or have no elements.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_quantized_weight_nq_amd as nq
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nq.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(nq_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    declared = _declared()
+    assert set(declared) == set(nq.EXPORTS)
+    lib = nq.library()
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_registry_matches_oracle_geometry():
+    assert nq.format_count() == 28
+    assert nq.format_names() == oracle.format_names()
+    for i in range(nq.format_count()):
+        info = nq.format_by_id(i)
+        _, B, S, T = oracle.info(info.name.decode())
+        assert (info.block_values, info.block_bytes, info.trailer_bytes) == (B, S, T)
+        assert nq.format_query(info.name.decode()).id == i
+
+
+@pytest.mark.parametrize("bad", ["GGUF:q4_0", "gguf:Q4_0", "q4_0", "gguf:q4_0(32)", "gguf:q4_0 ", "nvfp4:1",
+                                 "gguf:", "", "gguf:nvfp4x", "NVFP4"])
+def test_unknown_spellings_rejected(bad):
+    info = nq.FormatInfo()
+    assert nq.library().nq_format_query(bad.encode(), ctypes.byref(info)) == 2
+
+
+def test_null_arguments():
+    L = nq.library()
+    assert L.nq_format_query(None, ctypes.byref(nq.FormatInfo())) == 1
+    assert L.nq_format_query(b"gguf:q4_0", None) == 1
+    assert L.nq_format_by_id(0, None) == 1
+    assert L.nq_format_by_id(28, ctypes.byref(nq.FormatInfo())) == 2
+    assert L.nq_format_by_id(-1, ctypes.byref(nq.FormatInfo())) == 2
+
+
+SHAPES = [[256], [3, 512], [2, 3, 1024], [0, 256], [5, 0], [0], [4096, 14336], [7, 1, 256],
+          [4, 31], [31], [0, 33], [-1, 256], [], [2 ** 40, 2 ** 40, 256], [2 ** 62, 0, 256], [1, 2 ** 61]]
+
+
+@pytest.mark.parametrize("fmt", oracle.format_names())
+def test_length_rule_agrees_with_oracle(fmt):
+    ostatus = {oracle.OK: 0, oracle.ERR_RANK: 3, oracle.ERR_DIM: 4, oracle.ERR_ALIGN: 5, oracle.ERR_OVERFLOW: 7}
+    for shape in SHAPES:
+        st, nbytes, nelems = oracle.sizes(fmt, shape)
+        want = ostatus[st]
+        got, ne, _ = nq.validate_status(fmt, nbytes if st == oracle.OK else 0, shape, "f32")
+        assert got == want, (fmt, shape, got, want)
+        if st == oracle.OK:
+            assert ne == nelems
+            for delta in (-1, 1):
+                if nbytes + delta >= 0:
+                    assert nq.validate_status(fmt, nbytes + delta, shape)[0] == 6
+
+
+def test_validate_reports_output_bytes():
+    for code, size in (("f32", 4), ("f16", 2), ("bf16", 2), ("f64", 8)):
+        ne, nb = nq.validate("gguf:q4_k", 144 * 6, [3, 512], code)
+        assert (ne, nb) == (1536, 1536 * size)
+    assert nq.validate_status("gguf:q4_k", 144 * 6, [3, 512], 4)[0] == 8
+    assert nq.validate_status("gguf:q4_k", 144 * 6, [3, 512], -1)[0] == 8
+
+
+def test_dequantize_rejects_bad_metadata_without_device():
+    fid = nq.format_query("gguf:q8_0").id
+    buf = np.zeros(64, dtype=np.uint8)
+    p = buf.ctypes.data
+    assert nq.dequantize_packed_raw(fid, p, 33, [32], 0, p, 0) == 6
+    assert nq.dequantize_packed_raw(fid, p, 34, [31], 0, p, 0) == 5
+    assert nq.dequantize_packed_raw(fid, p, 34, [32], 7, p, 0) == 8
+    assert nq.dequantize_packed_raw(fid, 0, 34, [32], 0, p, 0) == 1
+    assert nq.dequantize_packed_raw(fid, p, 34, [32], 0, 0, 0) == 1
+    assert nq.dequantize_packed_raw(99, p, 34, [32], 0, p, 0) == 2
+    # an element-misaligned output is refused before launch
+    assert nq.dequantize_packed_raw(fid, p, 34, [32], 0, p + 2, 0) == 1
+    # empty tensors succeed without launching (null pointers allowed)
+    assert nq.dequantize_packed_raw(fid, 0, 0, [0, 32], 0, 0, 0) == 0
+    nv = nq.format_query("nvfp4").id
+    assert nq.dequantize_packed_raw(nv, p, 4, [0, 64], 2, 0, 0) == 0
+    assert nq.dequantize_packed_raw(nv, p, 0, [0, 64], 2, 0, 0) == 6
+
+
+def test_status_strings():
+    for st in range(10):
+        assert nq.library().nq_status_string(st)
+    assert nq.library().nq_status_string(12345) == b"unknown status"

@@ -1,0 +1,80 @@
+"""The kernels' own per-thread code, run on the CPU, against the oracle.
+
+The host emulator (tests/emu) executes process<> of nq_kernel.h for every
+workgroup and thread, with the launcher's chunk and grid arithmetic, reading
+the payload through a source that flags any dword outside the payload.  This
+checks indexing, bounds and the decode arithmetic before any GPU run; the
+output conversions here are the compiler's software ones, so the GPU tests
+remain the authority for the bf16/f16 epilogue.
+"""
+import numpy as np
+import pytest
+
+import block_quantized_weight_nq_amd as nq
+import compare
+import emu_lib
+import oracle
+import synth
+
+FORMATS = oracle.format_names()
+RAW = synth.raw()
+RECIPE = synth.binade(-12, -6, True)
+
+
+def _oracle(fmt, payload, nblocks, B, dtype):
+    return oracle.decode(fmt, payload, [nblocks * B], dtype)
+
+
+def _same(got, ref, dtype):
+    return compare.same(got, ref, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "f64"])
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_emulated_kernel_matches_oracle(fmt, dtype):
+    info = nq.format_query(fmt)
+    B = info.block_values
+    nblocks = 37
+    recipe = RECIPE if fmt == "nvfp4" else RAW
+    p = synth.payload(fmt, nblocks, 1000 + info.id, recipe)
+    got, bad, msg, guards = emu_lib.decode(info.id, p, nblocks, B, dtype)
+    assert bad == 0, msg
+    assert guards
+    assert _same(got, _oracle(fmt, p, nblocks, B, dtype), dtype)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("mis,out_mis", [(1, 0), (2, 4), (3, 8), (1, 2)])
+def test_emulated_misaligned_payload_and_output(fmt, mis, out_mis):
+    info = nq.format_query(fmt)
+    B = info.block_values
+    nblocks = 11
+    p = synth.payload(fmt, nblocks, 77, RECIPE)
+    dtype = "bf16" if out_mis % 4 else "f32"
+    got, bad, msg, guards = emu_lib.decode(info.id, p, nblocks, B, dtype, mis=mis, out_mis=out_mis)
+    assert bad == 0, msg
+    assert guards
+    assert _same(got, _oracle(fmt, p, nblocks, B, dtype), dtype)
+
+
+@pytest.mark.parametrize("fmt", ["gguf:q4_k", "gguf:q8_0", "gguf:mxfp4", "nvfp4", "gguf:iq2_s", "gguf:tq1_0"])
+@pytest.mark.parametrize("chunk,max_wgs", [(5, 1), (3, 2), (64, 3)])
+def test_emulated_chunks_and_grid_stride(fmt, chunk, max_wgs):
+    info = nq.format_query(fmt)
+    B = info.block_values
+    nblocks = 300
+    p = synth.payload(fmt, nblocks, 5, RECIPE)
+    got, bad, msg, guards = emu_lib.decode(info.id, p, nblocks, B, "bf16", mis=3, chunk=chunk,
+                                           max_wgs=max_wgs)
+    assert bad == 0, msg
+    assert guards
+    assert _same(got, _oracle(fmt, p, nblocks, B, "bf16"), "bf16")
+
+
+@pytest.mark.parametrize("d_w", [1.0, 3.0, 448.0, 1e-30, 3e38])
+def test_emulated_nvfp4_divisor(d_w):
+    info = nq.format_query("nvfp4")
+    p = synth.payload("nvfp4", 40, 3, RECIPE, divisor=d_w)
+    got, bad, msg, guards = emu_lib.decode(info.id, p, 40, 64, "f32", mis=2)
+    assert bad == 0 and guards, msg
+    assert _same(got, _oracle("nvfp4", p, 40, 64, "f32"), "f32")

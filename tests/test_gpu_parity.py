@@ -1,0 +1,205 @@
+"""GPU (gfx950) decode through the C ABI against the oracle, bit for bit.
+
+Every comparison is exact except NaN payloads, which the DequantizePacked page
+leaves unspecified (compared by class).  Inputs come from the seeded
+generator; sizes span many workgroups with a ragged tail, and the full-size
+workloads are checked on sampled blocks in the same launch configuration the
+benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_weight_nq_amd as nq
+import compare
+import oracle
+import synth
+from synth import workloads
+from gpu_util import TORCH_DT, announce, decode, oracle_blocks, to_numpy, upload
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = oracle.format_names()
+RAW = synth.raw()
+RECIPE = synth.binade(-12, -6, True)
+
+
+def _check(fmt, payload, shape, dtype, **kw):
+    got, _, _ = decode(fmt, payload, shape, dtype, **kw)
+    ref = oracle.decode(fmt, payload, shape, dtype)
+    assert compare.same(got, ref, dtype), f"{fmt} {shape} {dtype} {kw}: {compare.describe(got, ref, dtype)}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "f64"])
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_every_format_and_output_type(fmt, dtype):
+    info = nq.format_query(fmt)
+    nblocks = 2053  # several waves of workgroups and a ragged last iteration
+    for r, recipe in enumerate([RAW if fmt != "nvfp4" else RECIPE, RECIPE]):
+        announce(f"every_format {fmt} {dtype} recipe={recipe} blocks={nblocks}")
+        p = synth.payload(fmt, nblocks, 500 + 7 * info.id + r, recipe)
+        _check(fmt, p, [nblocks * info.block_values], dtype)
+
+
+@pytest.mark.parametrize("fmt", ["gguf:q4_0", "gguf:mxfp4", "gguf:q6_k", "gguf:iq2_xs", "nvfp4", "gguf:tq1_0",
+                                 "gguf:q3_k", "gguf:iq1_m"])
+def test_payload_offsets_0_to_15(fmt):
+    info = nq.format_query(fmt)
+    nblocks = 301
+    p = synth.payload(fmt, nblocks, 9, RECIPE)
+    for off in range(16):
+        announce(f"payload_offset {fmt} off={off}")
+        _check(fmt, p, [nblocks * info.block_values], "bf16", pay_off=off)
+
+
+@pytest.mark.parametrize("dtype,out_off", [("f32", 1), ("f32", 3), ("bf16", 1), ("bf16", 5), ("f16", 7),
+                                           ("f64", 1)])
+def test_unaligned_output_takes_scalar_stores(dtype, out_off):
+    for fmt in ("gguf:q8_0", "gguf:q4_k", "gguf:iq3_s", "gguf:nvfp4"):
+        info = nq.format_query(fmt)
+        p = synth.payload(fmt, 129, 21, RECIPE)
+        announce(f"unaligned_output {fmt} {dtype} out_off={out_off}")
+        got, obuf, _ = decode(fmt, p, [129 * info.block_values], dtype, out_off=out_off)
+        ref = oracle.decode(fmt, p, [129 * info.block_values], dtype)
+        assert compare.same(got, ref, dtype), compare.describe(got, ref, dtype)
+        head = to_numpy(obuf[:out_off], dtype)
+        tail = to_numpy(obuf[out_off + got.size:], dtype)
+        assert np.all(compare.nan_mask(head, dtype)) and np.all(compare.nan_mask(tail, dtype))
+
+
+@pytest.mark.parametrize("shape", [[3, 2, 512], [1, 256], [256], [7, 1, 256]])
+def test_shapes_are_flat_row_major(shape):
+    for fmt in ("gguf:q2_k", "gguf:iq4_xs"):
+        info = nq.format_query(fmt)
+        nb = int(np.prod(shape)) // info.block_values
+        p = synth.payload(fmt, nb, 3, RECIPE)
+        announce(f"shape {fmt} {shape}")
+        _check(fmt, p, shape, "f32")
+
+
+def test_empty_tensors_launch_nothing():
+    for fmt, shape in [("gguf:q4_k", [0, 256]), ("gguf:q8_0", [5, 0]), ("nvfp4", [0, 64]), ("gguf:mxfp4", [0])]:
+        info = nq.format_query(fmt)
+        p = synth.payload(fmt, 0, 1, RECIPE)
+        announce(f"empty {fmt} {shape}")
+        payload, _ = upload(p)
+        sentinel = torch.full((8,), 7.0, device="cuda:0")
+        out = torch.empty(0, device="cuda:0")
+        y = nq.dequantize_packed(fmt, payload, shape, torch.float32, out=out)
+        torch.cuda.synchronize()
+        assert y.numel() == 0 and torch.all(sentinel == 7.0)
+
+
+def test_metadata_errors_return_before_launch():
+    fid = nq.format_query("gguf:q4_0").id
+    p = synth.payload("gguf:q4_0", 4, 1, RECIPE)
+    payload, _ = upload(p)
+    out = torch.full((128,), 3.0, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    announce("metadata errors q4_0")
+    cases = [([128], p.size - 1, 0, 6), ([4, 31], p.size, 0, 5), ([-1, 32], p.size, 0, 4), ([], p.size, 0, 3),
+             ([128], p.size, 9, 8), ([128], p.size + 18, 0, 6)]
+    for shape, nbytes, dt, want in cases:
+        st = nq.dequantize_packed_raw(fid, payload.data_ptr(), nbytes, shape, dt, out.data_ptr(), stream)
+        assert st == want, (shape, nbytes, dt, st)
+    assert nq.dequantize_packed_raw(99, payload.data_ptr(), p.size, [128], 0, out.data_ptr(), stream) == 2
+    assert nq.dequantize_packed_raw(fid, 0, p.size, [128], 0, out.data_ptr(), stream) == 1
+    assert nq.dequantize_packed_raw(fid, payload.data_ptr(), p.size, [128], 0, 0, stream) == 1
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0)
+
+
+def test_mxfp4_every_exponent_byte_and_code():
+    blocks = b"".join(bytes([e]) + bytes([c | ((15 - c) << 4) for c in range(16)]) for e in range(256))
+    p = np.frombuffer(blocks, np.uint8)
+    for dtype in ("f32", "bf16", "f16"):
+        announce(f"mxfp4 exhaustive {dtype}")
+        _check("gguf:mxfp4", p, [256 * 32], dtype)
+
+
+def test_nvfp4_every_scale_byte_and_code():
+    rows = []
+    for e in range(256):
+        rows.append(bytes([e, (e + 1) & 255, (e + 2) & 255, (e + 3) & 255]) +
+                    bytes([c | ((15 - c) << 4) for c in range(8)] * 4))
+    p = np.frombuffer(b"".join(rows), np.uint8)
+    for dtype in ("f32", "bf16", "f16"):
+        announce(f"gguf:nvfp4 exhaustive {dtype}")
+        _check("gguf:nvfp4", p, [256 * 64], dtype)
+        for d_w in (1.0, 3.0, 7.1234567, 448.0, 1e-30, 3e38):
+            announce(f"nvfp4 exhaustive {dtype} d_w={d_w}")
+            q = np.concatenate([p, np.array([d_w], "<f4").view(np.uint8)])
+            _check("nvfp4", q, [256 * 64], dtype)
+
+
+def test_output_conversion_edges_through_q8_k():
+    """y = d * q with binary32 d covering every high half-word and the low
+    half-words around both rounding points: exercises the hardware bf16/f16
+    conversions on ties, subnormals, overflow and NaN."""
+    hi = np.arange(65536, dtype=np.uint32) << 16
+    lows = np.array([0x0000, 0x0FFF, 0x1000, 0x1001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint32)
+    d = (hi[:, None] | lows[None, :]).ravel()
+    n = d.size
+    blk = np.zeros((n, 292), dtype=np.uint8)
+    blk[:, 0:4] = d.view(np.uint8).reshape(n, 4)
+    q = np.array([1, -1, 2, 3, -128, 127, 0, 5] * 32, dtype=np.int8)
+    blk[:, 4:260] = q.view(np.uint8)
+    p = blk.ravel()
+    for dtype in ("bf16", "f16", "f32"):
+        announce(f"q8_k conversion edges {dtype} blocks={n}")
+        _check("gguf:q8_k", p, [n * 256], dtype)
+
+
+def test_side_stream_is_ordered():
+    fmt = "gguf:q4_k"
+    p = synth.payload(fmt, 4096, 8, RECIPE)
+    payload, _ = upload(p)
+    s = torch.cuda.Stream()
+    announce("side stream q4_k")
+    with torch.cuda.stream(s):
+        out = torch.empty(4096 * 256, dtype=torch.bfloat16, device="cuda:0")
+        nq.dequantize_packed(fmt, payload, [4096, 256], torch.bfloat16, out=out, stream=s)
+    s.synchronize()
+    ref = oracle.decode(fmt, p, [4096 * 256], "bf16")
+    assert compare.same(to_numpy(out, "bf16"), ref, "bf16")
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, sampled blocks.
+# ---------------------------------------------------------------------------
+def _full_size_sampled(name, fmt, shape, recipe, seed, dtype, nsample=2048):
+    info = nq.format_query(fmt)
+    B = info.block_values
+    nel = int(np.prod(shape))
+    nb = nel // B
+    announce(f"full-size {name} {fmt} {shape} {dtype} seed={seed:#x}")
+    p = synth.payload(fmt, nb, seed, recipe)
+    payload, _ = upload(p)
+    out = nq.dequantize_packed(fmt, payload, shape, TORCH_DT[dtype])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed & 0xFFFFFFFF)
+    ids = np.unique(np.concatenate([[0, nb - 1], rng.integers(0, nb, size=nsample)]))
+    got = to_numpy(out.reshape(nb, B)[torch.from_numpy(ids).to("cuda:0")], dtype).ravel()
+    ref = oracle_blocks(fmt, p, ids, dtype)
+    assert compare.same(got, ref, dtype), f"{name}: {compare.describe(got, ref, dtype)}"
+    del out, payload
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("config", [1, 2, 3, 4])
+def test_full_size_configs_sampled(config):
+    tensors, dtypes = workloads.CONFIGS[config]()
+    for name, fmt, shape, recipe, seed in tensors:
+        for dtype in dtypes:
+            _full_size_sampled(name, fmt, shape, recipe, seed, dtype)
+
+
+def test_full_size_llama3_8b_set_sampled():
+    tensors, dtypes = workloads.config5()
+    seen = set()
+    for t, (name, fmt, shape, recipe, seed) in enumerate(tensors):
+        key = (fmt, tuple(shape))
+        if key in seen and t != len(tensors) - 1:
+            continue
+        seen.add(key)
+        _full_size_sampled(name, fmt, shape, recipe, seed, "bf16", nsample=1024)
