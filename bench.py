@@ -79,51 +79,65 @@ def staging_buffer(torch, tensors, nq):
     return torch.empty(need, dtype=torch.uint8, pin_memory=True)
 
 
-def time_step_set(torch, nq, items, steps, warmup, per_launch_events=True):
-    """Warm up, then time `steps` passes over items; returns wall ms/step and per-item ms lists."""
+def capture(torch, nq, items):
+    """A HIP graph holding one launch per item, in order, on torch's capture stream."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        h = torch.cuda.current_stream().cuda_stream
+        for it in items:
+            it.launch(nq, h)
+    return g
+
+
+def time_graph(torch, g, reps, warmup=1):
+    """Mean milliseconds per replay, timed with events on the replay stream."""
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(reps):
+        g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / reps
+    return start.elapsed_time(end) / reps, wall
+
+
+def time_eager(torch, nq, items, steps, warmup):
+    """Wall and event milliseconds per pass of eager launches (no per-launch events)."""
     stream = torch.cuda.current_stream()
     handle = stream.cuda_stream
     for _ in range(warmup):
         for it in items:
             it.launch(nq, handle)
     torch.cuda.synchronize()
-    evs = []
-    if per_launch_events:
-        evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in items] for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
-    for s in range(steps):
-        for i, it in enumerate(items):
-            if per_launch_events:
-                evs[s][i][0].record(stream)
+    for _ in range(steps):
+        for it in items:
             it.launch(nq, handle)
-            if per_launch_events:
-                evs[s][i][1].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    event_ms = start.elapsed_time(end) / steps
-    per_item = [[evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(steps)] for i in range(len(items))] \
-        if per_launch_events else None
-    return wall_ms, event_ms, per_item
+    return (time.perf_counter() - t0) * 1e3 / steps, start.elapsed_time(end) / steps
 
 
-def per_format_breakdown(items, per_item):
-    agg = {}
-    for it, ms in zip(items, per_item):
-        a = agg.setdefault(it.fmt, {"launches": 0, "ms": 0.0, "bytes": 0})
-        a["launches"] += len(ms)
-        a["ms"] += sum(ms)
-        a["bytes"] += it.algo_bytes * len(ms)
+def per_format_times(torch, nq, items, reps):
+    """Per format: one graph of all its launches in the step, timed by events."""
     out = {}
-    for fmt, a in agg.items():
-        gbps = a["bytes"] / (a["ms"] * 1e-3) / 1e9
+    for fmt in dict.fromkeys(it.fmt for it in items):
+        sel = [it for it in items if it.fmt == fmt]
+        g = capture(torch, nq, sel)
+        ms, _ = time_graph(torch, g, reps)
+        nbytes = sum(it.algo_bytes for it in sel)
+        gbps = nbytes / (ms * 1e-3) / 1e9
         out[fmt] = {"gbps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
-                    "launches": a["launches"], "mean_launch_us": round(a["ms"] * 1e3 / a["launches"], 2),
-                    "total_ms": a["ms"], "bytes_per_launch": a["bytes"] / a["launches"]}
+                    "launches": len(sel), "mean_launch_us": round(ms * 1e3 / len(sel), 3),
+                    "bytes_per_launch": round(nbytes / len(sel)), "total_ms": ms}
+        del g
     return out
 
 
@@ -134,17 +148,16 @@ def rotating_measurement(torch, nq, synth, name, fmt, shape, recipe, seed, dtype
     reps = max(1, math.ceil(footprint / first.algo_bytes))
     items = [first]
     for r in range(1, reps):
-        t = Tensor(name, fmt, shape, recipe, seed, dtype, staging, torch, nq, synth)
-        items.append(t)
+        items.append(Tensor(name, fmt, shape, recipe, seed, dtype, staging, torch, nq, synth))
     order = [items[i % reps] for i in range(launches)]
-    _, _, per_item = time_step_set(torch, nq, order, 1, 1, per_launch_events=True)
-    ms = [x[0] for x in per_item]
-    mean_ms = sum(ms) / len(ms)
+    g = capture(torch, nq, order)
+    ms, _ = time_graph(torch, g, 3)
+    mean_ms = ms / launches
     gbps = first.algo_bytes / (mean_ms * 1e-3) / 1e9
     res = {"shape": shape, "out": dtype, "gbps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
-           "mean_launch_us": round(mean_ms * 1e3, 2), "replicas": reps,
+           "mean_launch_us": round(mean_ms * 1e3, 3), "replicas": reps,
            "elements_per_s": round(first.nelems / (mean_ms * 1e-3), 1), "bytes_per_launch": first.algo_bytes}
-    del items, order, first
+    del g, items, order, first
     torch.cuda.empty_cache()
     return res
 
@@ -181,7 +194,6 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-per-format", action="store_true", help="skip the rotating per-workload timings")
-    ap.add_argument("--no-launch-events", action="store_true", help="time the step without per-launch events")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
                     help="first run a plain device copy of this many MiB (for counter calibration)")
     args = ap.parse_args()
@@ -222,23 +234,24 @@ def main():
     payload_bytes = sum(it.nbytes for it in items)
     elems = sum(it.nelems for it in items)
 
-    wall_ms, event_ms, per_item = time_step_set(torch, nq, items, args.steps, args.warmup,
-                                                per_launch_events=not args.no_launch_events)
-    log(f"step: wall {wall_ms:.3f} ms, events {event_ms:.3f} ms")
-    value = step_bytes / (wall_ms * 1e-3) / 1e9
+    eager_wall_ms, eager_event_ms = time_eager(torch, nq, items, args.steps, args.warmup)
+    log(f"eager step: wall {eager_wall_ms:.3f} ms, events {eager_event_ms:.3f} ms")
+    step_graph = capture(torch, nq, items)
+    graph_ms, graph_wall_ms = time_graph(torch, step_graph, args.steps, warmup=args.warmup)
+    log(f"graph step: events {graph_ms:.3f} ms, wall {graph_wall_ms:.3f} ms")
+    del step_graph
+    ms_per_step = graph_wall_ms
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
-    roofline = None
-    formats = {}
-    if per_item is not None:
-        formats = per_format_breakdown(items, per_item)
-        dom = max(formats, key=lambda f: formats[f]["total_ms"])
-        d = formats[dom]
-        achieved = d["bytes_per_launch"] / (d["mean_launch_us"] * 1e-6) / 1e9
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": dom,
-                    "bytes_per_launch": round(d["bytes_per_launch"]), "mean_launch_us": d["mean_launch_us"]}
-        for f in formats.values():
-            del f["total_ms"]
+    formats = per_format_times(torch, nq, items, reps=max(2, args.steps // 2))
+    dom = max(formats, key=lambda f: formats[f]["total_ms"])
+    d = formats[dom]
+    achieved = d["bytes_per_launch"] / (d["mean_launch_us"] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": f"k_decode {dom} -> bf16",
+                "bytes_per_launch": d["bytes_per_launch"], "mean_launch_us": d["mean_launch_us"]}
+    for f in formats.values():
+        del f["total_ms"]
     del items
     torch.cuda.empty_cache()
 
@@ -261,11 +274,12 @@ def main():
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(wall_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "llama3-8b weight set: 226 tensors, q4_k/q6_k/q8_0/nvfp4/tq2_0 rotation -> bf16",
                    "tensors": len(tensors), "elements": elems, "payload_bytes": payload_bytes,
-                   "output_bytes": step_bytes - payload_bytes, "event_ms_per_step": round(event_ms, 4),
+                   "output_bytes": step_bytes - payload_bytes, "graph_event_ms_per_step": round(graph_ms, 4),
+                   "eager_wall_ms_per_step": round(eager_wall_ms, 4), "eager_event_ms_per_step": round(eager_event_ms, 4),
                    "frac_hbm_peak": round(value / HBM_PEAK_GBPS, 4)},
         "roofline": roofline,
         "cpu_baseline": cpu,

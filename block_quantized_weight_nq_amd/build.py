@@ -41,31 +41,37 @@ def _hipcc():
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src, is_kernel):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *COMMON, *DEVICE, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src, is_kernel, build_dir=BUILD, defines=()):
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [_hipcc(), *COMMON, *DEVICE, *[f"-D{d}" for d in defines], "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(jobs=None, verbose=False):
-    """Compile every source and link libnq.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs=None, verbose=False, out=LIB, defines=()):
+    """Compile every source and link the library (default: libnq.so in-tree).
+
+    `defines` are extra -D macros (the tuning knobs NQ_UPT, NQ_WG_PER_CU,
+    NQ_NT_STORE of csrc/nq_kernel.h); a non-default `out` builds elsewhere.
+    """
+    build_dir = BUILD if out == LIB else out + ".build"
+    os.makedirs(build_dir, exist_ok=True)
     jobs = jobs or min(8, os.cpu_count() or 4)
-    work = [(s, True) for s in KERNEL_SOURCES + HOST_SOURCES]
+    work = [(s, True, build_dir, tuple(defines)) for s in KERNEL_SOURCES + HOST_SOURCES]
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda a: _compile(*a), work))
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}", file=sys.stderr)
-    return LIB
+        print(f"built {out}", file=sys.stderr)
+    return out
 
 
 if __name__ == "__main__":

@@ -74,7 +74,7 @@ uint32_t max_workgroups() {
             cu = 256;
         g_cu_count[dev].store(cu, std::memory_order_relaxed);
     }
-    return (uint32_t)cu * 8u;  // 8 workgroups of 256 threads = 32 waves per CU
+    return (uint32_t)cu * NQ_WG_PER_CU;  // persistent grid: workgroups per CU
 }
 
 }  // namespace

@@ -443,9 +443,12 @@ NQ_HD void unit_nvfp4_gguf(const Src &src, uint32_t bo, uint32_t s, float (&y)[8
 }
 
 // nvfp4 (NInfer 3.3): y = RN32(e2m1(c) * e4m3fn(s) / d_w).  The product is
-// exact in binary32, so the value is one correctly rounded division; the
-// kernels read it from a per-workgroup table of all 256 x 16 (s, c) quotients
-// computed with that same division (e2m1_e4m3_div).
+// exact in binary32, so the value is one correctly rounded division.  IEEE
+// products and quotients take the XOR of their operands' signs (zeros
+// included) and round symmetrically, so y is the quotient of the magnitudes
+// with sign bit (c bit 3) ^ (s bit 7).  The kernels read that magnitude from
+// a per-workgroup table of all 128 x 8 (s & 0x7F, c & 7) quotients computed
+// with the same division (e2m1_e4m3_div).
 NQ_HD float e4m3fn(uint32_t w) {
     const uint32_t sign = (w >> 7) & 1u, E = (w >> 3) & 15u, m = w & 7u;
     float mag;
@@ -464,7 +467,6 @@ NQ_HD float e2m1(uint32_t c) {
 }
 NQ_HD float e2m1_e4m3_div(uint32_t sw, uint32_t c, float dw) { return M(e2m1(c), e4m3fn(sw)) / dw; }
 
-// The unit reads its 8 quotients from tab[16 * scale + code].
 template <class Src, class Tab>
 NQ_HD void unit_nvfp4_div(const Src &src, uint32_t bo, uint32_t s, const Tab &tab, float (&y)[8]) {
     const uint32_t g = s >> 1;
@@ -473,8 +475,13 @@ NQ_HD void unit_nvfp4_div(const Src &src, uint32_t bo, uint32_t s, const Tab &ta
     window<2>(src, bo + 4 + 8u * g, q);
     uint32_t c[2];
     nibbles(q, s & 1u, c);
+    const uint32_t row = 8u * (sw & 0x7Fu);
 #pragma unroll
-    for (int j = 0; j < 8; j++) y[j] = tab.nv(16u * sw + code_at(c, j));
+    for (int j = 0; j < 8; j++) {
+        const uint32_t code = code_at(c, j);
+        const uint32_t neg = ((code >> 3) ^ (sw >> 7)) & 1u;
+        y[j] = bits_f32(__builtin_bit_cast(uint32_t, tab.nv(row + (code & 7u))) ^ (neg << 31));
+    }
 }
 
 // --- IQ2 / IQ3 / IQ1: unit = lane i = 4g + l --------------------------------

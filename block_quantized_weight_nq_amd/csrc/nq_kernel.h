@@ -12,6 +12,25 @@
 #include "iq_grids.h"
 #include "nq_decode.h"
 
+// Tuning knobs (compile-time; the defaults are the measured best on MI355X):
+//   NQ_LDS        1: stage each tile's payload in LDS (0: per-unit global loads)
+//   NQ_NTL        1: staging loads are non-temporal (each payload byte is read once)
+//   NQ_UPT        units (8 outputs) per thread per tile
+//   NQ_WG_PER_CU  persistent-grid workgroups per compute unit
+//   NQ_NT_STORE   non-temporal output stores: 0 never, 1 always, 2 16-bit outputs only
+#ifndef NQ_LDS
+#define NQ_LDS 1
+#endif
+#ifndef NQ_NTL
+#define NQ_NTL 1
+#endif
+#ifndef NQ_UPT
+#define NQ_UPT 4
+#endif
+#ifndef NQ_WG_PER_CU
+#define NQ_WG_PER_CU 8
+#endif
+
 namespace nq {
 
 typedef uint32_t u32x2a4 __attribute__((ext_vector_type(2), aligned(4)));
@@ -50,6 +69,18 @@ struct DevSrc {
         }
     }
     NQ_HD uint32_t dw(uint32_t i) const { return base[i]; }
+    // 16 bytes that are read once (non-temporal when NQ_NTL).
+    NQ_HD void load_stream4(uint32_t i, uint32_t (&r)[4]) const {
+#if NQ_NTL && defined(__HIP_DEVICE_COMPILE__)
+        const u32x4a4 v = __builtin_nontemporal_load((const u32x4a4 *)(base + i));
+#else
+        const u32x4a4 v = *(const u32x4a4 *)(base + i);
+#endif
+        r[0] = v.x;
+        r[1] = v.y;
+        r[2] = v.z;
+        r[3] = v.w;
+    }
 };
 
 // Two-pass source pair.  No payload address depends on loaded data, so a
@@ -111,7 +142,7 @@ struct TabSpec {
     static constexpr int n8 = F == IQ2_XXS ? 256 : F == IQ2_XS ? 512 : F == IQ2_S ? 1024
                             : (F == IQ1_S || F == IQ1_M) ? 2048 : 0;
     static constexpr int n4 = F == IQ3_XXS ? 256 : F == IQ3_S ? 512 : 0;
-    static constexpr int nf = F == NVFP4_DIV ? 4096 : 0;
+    static constexpr int nf = F == NVFP4_DIV ? 1024 : 0;
     NQ_HD static const uint64_t *src8() {
         return F == IQ2_XXS ? NQ_GRID_IQ2XXS : F == IQ2_XS ? NQ_GRID_IQ2XS : F == IQ2_S ? NQ_GRID_IQ2S
                                                                                      : NQ_GRID_IQ1S;
@@ -130,6 +161,26 @@ struct KArgs {
     uint32_t nunits;          // units in this chunk
 };
 
+// Non-temporal 16-byte stores (streamed past the caches) pay off when each
+// store instruction of a wave covers whole cache lines: the 16-bit outputs,
+// where 64 lanes write one contiguous 1 KiB run.  The 32/64-bit outputs write
+// each line from two instructions and keep ordinary stores.  NQ_NT_STORE
+// overrides: 0 never, 1 always, 2 (default) 16-bit outputs only.
+#ifndef NQ_NT_STORE
+#define NQ_NT_STORE 2
+#endif
+template <int OT>
+NQ_HD void vstore(void *p, u32x4 v) {
+    constexpr bool nt = NQ_NT_STORE == 1 || (NQ_NT_STORE == 2 && (OT == 1 || OT == 2));
+#if defined(__HIP_DEVICE_COMPILE__)
+    if constexpr (nt) {
+        __builtin_nontemporal_store(v, (u32x4 *)p);
+        return;
+    }
+#endif
+    *(u32x4 *)p = v;
+}
+
 // Output conversion and store of one unit (8 values) at element 8u.
 // Conversion happens once, from the binary32 value, with round-to-nearest-
 // even (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32 under the default round mode).
@@ -144,8 +195,8 @@ NQ_HD void store8(void *out, uint32_t u, const float (&y)[8]) {
             a.z = __builtin_bit_cast(uint32_t, y[2]); a.w = __builtin_bit_cast(uint32_t, y[3]);
             b.x = __builtin_bit_cast(uint32_t, y[4]); b.y = __builtin_bit_cast(uint32_t, y[5]);
             b.z = __builtin_bit_cast(uint32_t, y[6]); b.w = __builtin_bit_cast(uint32_t, y[7]);
-            *(u32x4 *)o = a;
-            *(u32x4 *)(o + 4) = b;
+            vstore<OT>(o, a);
+            vstore<OT>(o + 4, b);
         } else {
 #pragma unroll
             for (int k = 0; k < 8; k++) o[k] = y[k];
@@ -166,7 +217,7 @@ NQ_HD void store8(void *out, uint32_t u, const float (&y)[8]) {
         if constexpr (VEC) {
             u32x4 a;
             a.x = w[0]; a.y = w[1]; a.z = w[2]; a.w = w[3];
-            *(u32x4 *)o = a;
+            vstore<OT>(o, a);
         } else {
 #pragma unroll
             for (int k = 0; k < 8; k++) o[k] = (uint16_t)(w[k >> 1] >> (16 * (k & 1)));
@@ -179,7 +230,7 @@ NQ_HD void store8(void *out, uint32_t u, const float (&y)[8]) {
                 f64x2 v;
                 v.x = (double)y[2 * k];
                 v.y = (double)y[2 * k + 1];
-                *(f64x2 *)(o + 2 * k) = v;
+                vstore<OT>(o + 2 * k, __builtin_bit_cast(u32x4, v));
             }
         } else {
 #pragma unroll
@@ -190,43 +241,200 @@ NQ_HD void store8(void *out, uint32_t u, const float (&y)[8]) {
 
 constexpr int WG = 256;  // threads per workgroup (4 wave64)
 
-// One thread's share of a launch: the grid-stride loop over units.
+// One thread's share of a launch.  Units are grouped in tiles of WG * UPT;
+// workgroup `bid` takes tiles bid, bid + nwg, ...  Full tiles run software-
+// pipelined: the loads of a thread's next tile are issued before the current
+// tile is computed and stored, so the wait for a tile's loads never waits on
+// the previous tile's stores (loads and stores share one counter).  The last,
+// partial tile takes a guarded path.
+template <int F, int UPT, class Src, class T>
+NQ_HD void fetch_tile(const Src &src, const T &tab, const KArgs &a, uint32_t tile, uint32_t tid,
+                      uint32_t (&raw)[UPT][RAW_CAP]) {
+    constexpr uint32_t UPB = block_values(F) / 8;
+    constexpr uint32_t S = block_bytes(F);
+#pragma unroll
+    for (int k = 0; k < UPT; k++) {
+        const uint32_t u = tile * (uint32_t)(WG * UPT) + (uint32_t)(k * WG) + tid;
+        const Recorder<Src> rec{src, raw[k], 0, src.last};
+        float dead[8];
+        decode_unit<F>(rec, a.mis + (u / UPB) * S, u % UPB, tab, dead);
+    }
+}
+
 template <int F, int OT, int UPT, bool VEC, class Src, class T>
 NQ_HD void process(const Src &src, const T &tab, const KArgs &a, uint32_t bid, uint32_t nwg, uint32_t tid) {
     constexpr uint32_t UPB = block_values(F) / 8;
     constexpr uint32_t S = block_bytes(F);
-    const uint32_t step = nwg * (uint32_t)(WG * UPT);
-    for (uint32_t u0 = bid * (uint32_t)(WG * UPT); u0 < a.nunits; u0 += step) {
-        if (u0 + (uint32_t)(WG * UPT) <= a.nunits) {
-            uint32_t raw[UPT][RAW_CAP];
+    constexpr uint32_t PER = (uint32_t)(WG * UPT);
+    const uint32_t full = a.nunits / PER;
+    uint32_t t = bid;
+    if (t < full) {
+        uint32_t raw[UPT][RAW_CAP];
+        fetch_tile<F, UPT>(src, tab, a, t, tid, raw);
+        for (; t < full; t += nwg) {
+            uint32_t cur[UPT][RAW_CAP];
+#pragma unroll
+            for (int k = 0; k < UPT; k++)
+#pragma unroll
+                for (int i = 0; i < RAW_CAP; i++) cur[k][i] = raw[k][i];
+            // next tile's loads (the current tile again on the last pass: always in bounds)
+            const uint32_t tn = (t + nwg < full) ? t + nwg : t;
+            fetch_tile<F, UPT>(src, tab, a, tn, tid, raw);
             float y[UPT][8];
 #pragma unroll
-            for (int k = 0; k < UPT; k++) {  // pass 1: every load of every unit
-                const uint32_t u = u0 + (uint32_t)(k * WG) + tid;
-                const Recorder<Src> rec{src, raw[k], 0, src.last};
-                float dead[8];
-                decode_unit<F>(rec, a.mis + (u / UPB) * S, u % UPB, tab, dead);
-            }
-#pragma unroll
-            for (int k = 0; k < UPT; k++) {  // pass 2: the arithmetic
-                const uint32_t u = u0 + (uint32_t)(k * WG) + tid;
-                const Player pl{raw[k], 0, src.last};
+            for (int k = 0; k < UPT; k++) {
+                const uint32_t u = t * PER + (uint32_t)(k * WG) + tid;
+                const Player pl{cur[k], 0, src.last};
                 decode_unit<F>(pl, a.mis + (u / UPB) * S, u % UPB, tab, y[k]);
             }
 #pragma unroll
-            for (int k = 0; k < UPT; k++) store8<OT, VEC>(a.out, u0 + (uint32_t)(k * WG) + tid, y[k]);
-        } else {
+            for (int k = 0; k < UPT; k++) store8<OT, VEC>(a.out, t * PER + (uint32_t)(k * WG) + tid, y[k]);
+        }
+    }
+    if (t == full) {  // the partial tile, if any, falls to exactly one workgroup
 #pragma unroll
-            for (int k = 0; k < UPT; k++) {
-                const uint32_t u = u0 + (uint32_t)(k * WG) + tid;
-                if (u < a.nunits) {
-                    float y[8];
-                    decode_unit<F>(src, a.mis + (u / UPB) * S, u % UPB, tab, y);
-                    store8<OT, VEC>(a.out, u, y);
-                }
+        for (int k = 0; k < UPT; k++) {
+            const uint32_t u = full * PER + (uint32_t)(k * WG) + tid;
+            if (u < a.nunits) {
+                float y[8];
+                decode_unit<F>(src, a.mis + (u / UPB) * S, u % UPB, tab, y);
+                store8<OT, VEC>(a.out, u, y);
             }
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// LDS-staged decode.  A workgroup copies each full tile's payload bytes into
+// LDS with coalesced 16-byte loads (one to three per thread), loads of the
+// next tile in flight while the current one decodes from LDS; the unit
+// decoders are unchanged and read through LdsSrc.  Every global dword index
+// is clamped to the last payload dword, so staging never leaves the payload.
+// The phases (stage_load, stage_store, decode_staged) are host-compilable so
+// the emulator can run them in barrier order.
+// ---------------------------------------------------------------------------
+
+struct LdsSrc {
+    const uint32_t *base;  // the staged tile: LDS dword 0 = payload dword a0
+    uint32_t last;         // last staged dword holding this tile's bytes
+    template <int N>
+    NQ_HD void load(uint32_t i, uint32_t (&r)[N]) const {
+#pragma unroll
+        for (int k = 0; k < N; k++) r[k] = base[i + (uint32_t)k];
+    }
+    NQ_HD uint32_t dw(uint32_t i) const { return base[i]; }
+};
+
+template <int F, int UPT>
+struct Stage {
+    static constexpr uint32_t UPB = block_values(F) / 8;
+    static constexpr uint32_t PER = (uint32_t)(WG * UPT);      // units per tile
+    static constexpr uint32_t BPT = PER / UPB;                  // blocks per tile
+    static constexpr uint32_t TB = BPT * block_bytes(F);        // payload bytes per tile
+    static constexpr uint32_t NDW = (TB + 3) / 4 + 1;           // dwords spanned, any start offset
+    static constexpr uint32_t NCH = (NDW + 3) / 4;              // 16-byte chunks
+    static constexpr uint32_t NK = (NCH + WG - 1) / WG;         // chunks per thread
+    static constexpr uint32_t SLOT_DW = NK * WG * 4;            // LDS dwords per slot
+};
+
+// Global loads of tile t's chunks for this thread (into registers).
+template <int F, int UPT, class Src>
+NQ_HD void stage_load(const Src &src, const KArgs &a, uint32_t t, uint32_t tid, uint32_t (&r)[Stage<F, UPT>::NK][4]) {
+    using ST = Stage<F, UPT>;
+    const uint32_t p = a.mis + t * ST::TB;
+    const uint32_t a0 = p >> 2, a_end = (p + ST::TB - 1) >> 2;
+#pragma unroll
+    for (uint32_t k = 0; k < ST::NK; k++) {
+        const uint32_t c = k * WG + tid;
+        const uint32_t d0 = a0 + 4 * c;
+        if (d0 <= a_end) {
+            if (d0 + 3 <= src.last) {
+                src.load_stream4(d0, r[k]);
+            } else {
+#pragma unroll
+                for (uint32_t j = 0; j < 4; j++) r[k][j] = src.dw(d0 + j <= src.last ? d0 + j : src.last);
+            }
+        }
+    }
+}
+
+template <int F, int UPT>
+NQ_HD void stage_store(uint32_t *slot, const KArgs &a, uint32_t t, uint32_t tid,
+                       const uint32_t (&r)[Stage<F, UPT>::NK][4]) {
+    using ST = Stage<F, UPT>;
+    const uint32_t p = a.mis + t * ST::TB;
+    const uint32_t a0 = p >> 2, a_end = (p + ST::TB - 1) >> 2;
+#pragma unroll
+    for (uint32_t k = 0; k < ST::NK; k++) {
+        const uint32_t c = k * WG + tid;
+        if (a0 + 4 * c <= a_end) {
+            u32x4 v;
+            v.x = r[k][0]; v.y = r[k][1]; v.z = r[k][2]; v.w = r[k][3];
+            *(u32x4 *)(slot + 4 * c) = v;
+        }
+    }
+}
+
+// Decode this thread's units of tile t from its staged copy in `buf`.
+template <int F, int OT, int UPT, bool VEC, class T>
+NQ_HD void decode_staged(const T &tab, const KArgs &a, uint32_t t, uint32_t tid, const uint32_t *buf) {
+    using ST = Stage<F, UPT>;
+    constexpr uint32_t UPB = ST::UPB;
+    constexpr uint32_t S = block_bytes(F);
+    const uint32_t p = a.mis + t * ST::TB;
+    const uint32_t a0 = p >> 2;
+    const LdsSrc src{buf, ((p + ST::TB - 1) >> 2) - a0};
+    float y[UPT][8];
+#pragma unroll
+    for (int k = 0; k < UPT; k++) {
+        const uint32_t u = t * ST::PER + (uint32_t)(k * WG) + tid;
+        const uint32_t bo = (p & 3u) + (u / UPB - t * ST::BPT) * S;
+        decode_unit<F>(src, bo, u % UPB, tab, y[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < UPT; k++) store8<OT, VEC>(a.out, t * ST::PER + (uint32_t)(k * WG) + tid, y[k]);
+}
+
+// The partial last tile (if any), straight from global memory, decoded by
+// the workgroup whose turn it is: tile `full` falls to bid == full % nwg.
+template <int F, int OT, int UPT, bool VEC, class Src, class T>
+NQ_HD void decode_tail(const Src &src, const T &tab, const KArgs &a, uint32_t bid, uint32_t nwg, uint32_t tid) {
+    using ST = Stage<F, UPT>;
+    const uint32_t full = a.nunits / ST::PER;
+    if (full * ST::PER == a.nunits || full % nwg != bid) return;
+#pragma unroll
+    for (int k = 0; k < UPT; k++) {
+        const uint32_t u = full * ST::PER + (uint32_t)(k * WG) + tid;
+        if (u < a.nunits) {
+            float y[8];
+            decode_unit<F>(src, a.mis + (u / ST::UPB) * block_bytes(F), u % ST::UPB, tab, y);
+            store8<OT, VEC>(a.out, u, y);
+        }
+    }
+}
+
+// Workgroup `bid` decodes full tiles bid, bid + nwg, ... (then the tail).
+template <int F, int OT, int UPT, bool VEC, class T>
+__device__ __forceinline__ void process_lds(const T &tab, const KArgs &a, uint32_t bid, uint32_t nwg, uint32_t tid,
+                                            uint32_t *lds) {
+    using ST = Stage<F, UPT>;
+    const uint32_t full = a.nunits / ST::PER;
+    const DevSrc src{a.base, a.last};
+    uint32_t t = bid;
+    if (t < full) {
+        uint32_t r[ST::NK][4];
+        stage_load<F, UPT>(src, a, t, tid, r);
+        uint32_t slot = 0;
+        for (; t < full; t += nwg) {
+            uint32_t *buf = lds + slot * ST::SLOT_DW;
+            stage_store<F, UPT>(buf, a, t, tid, r);
+            __syncthreads();
+            if (t + nwg < full) stage_load<F, UPT>(src, a, t + nwg, tid, r);
+            decode_staged<F, OT, UPT, VEC>(tab, a, t, tid, buf);
+            slot ^= 1u;
+        }
+    }
+    decode_tail<F, OT, UPT, VEC>(src, tab, a, bid, nwg, tid);
 }
 
 // Table setup, strided over `nthreads` cooperating threads.
@@ -246,7 +454,7 @@ NQ_HD void fill_tables(uint64_t *t8, uint32_t *t4, float *nvq, const TrSrc &tr, 
         uint32_t dww[1];
         window<1>(tr, tr_mis, dww);
         const float dw = bits_f32(dww[0]);
-        for (uint32_t k = tid; k < (uint32_t)TS::nf; k += nthreads) nvq[k] = e2m1_e4m3_div(k >> 4, k & 15u, dw);
+        for (uint32_t k = tid; k < (uint32_t)TS::nf; k += nthreads) nvq[k] = e2m1_e4m3_div(k >> 3, k & 7u, dw);
     }
 }
 
@@ -262,7 +470,12 @@ __global__ __launch_bounds__(WG) void k_decode(KArgs a) {
         __syncthreads();
     }
     const Tab tab{t8, t4, nvq};
+#if NQ_LDS
+    __shared__ __attribute__((aligned(16))) uint32_t stage[2 * Stage<F, UPT>::SLOT_DW];
+    process_lds<F, OT, UPT, VEC>(tab, a, blockIdx.x, gridDim.x, tid, stage);
+#else
     process<F, OT, UPT, VEC>(DevSrc{a.base, a.last}, tab, a, blockIdx.x, gridDim.x, tid);
+#endif
 }
 
 // Host launch description for one call.
@@ -274,7 +487,7 @@ struct LaunchArgs {
     uint32_t max_wgs;        // persistent-grid cap for the device
 };
 
-constexpr int UPT_DEFAULT = 2;
+constexpr int UPT_DEFAULT = NQ_UPT;  // units per thread per tile
 
 // Blocks per launch chunk: unit indices stay below 2^30 and payload byte
 // offsets below 2^32.

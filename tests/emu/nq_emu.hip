@@ -6,6 +6,7 @@
 // payload source checks that every dword read overlaps the payload bytes of
 // its chunk; the caller checks the output guards.  Built host-only.
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <vector>
 
@@ -27,6 +28,7 @@ struct HostSrc {
     void load(uint32_t i, uint32_t (&r)[N]) const {
         for (int k = 0; k < N; k++) r[k] = dw(i + (uint32_t)k);
     }
+    void load_stream4(uint32_t i, uint32_t (&r)[4]) const { load<4>(i, r); }
     uint32_t dw(uint32_t i) const {
         const uintptr_t a = (uintptr_t)(base + i);
         if (i > last || a + 4 <= chk->lo || a >= chk->hi) {
@@ -64,6 +66,35 @@ long run(const uint8_t *payload, uint64_t nbytes, uint64_t nblocks, void *out, u
         const Tab tab{t8.data(), t4.data(), nvq.data()};
         const HostSrc src{a.base, a.last, &chk};
         const bool vec = ((uintptr_t)a.out & 15) == 0;
+#if NQ_LDS
+        // the staged path, phase by phase: every thread stages a tile, then
+        // every thread decodes it (the kernel's barrier), then the tail tile
+        using ST = Stage<F, UPT>;
+        std::vector<uint32_t> slot(ST::SLOT_DW);
+        const uint32_t full = a.nunits / ST::PER;
+        for (uint32_t bid = 0; bid < grid; bid++) {
+            for (uint32_t t = bid; t < full; t += grid) {
+                std::fill(slot.begin(), slot.end(), 0xA5A5A5A5u);  // stale words poison the result
+                for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) {
+                    uint32_t r[ST::NK][4];
+                    stage_load<F, UPT>(src, a, t, tid, r);
+                    stage_store<F, UPT>(slot.data(), a, t, tid, r);
+                }
+                for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) {
+                    if (vec)
+                        decode_staged<F, OT, UPT, true>(tab, a, t, tid, slot.data());
+                    else
+                        decode_staged<F, OT, UPT, false>(tab, a, t, tid, slot.data());
+                }
+            }
+            for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) {
+                if (vec)
+                    decode_tail<F, OT, UPT, true>(src, tab, a, bid, grid, tid);
+                else
+                    decode_tail<F, OT, UPT, false>(src, tab, a, bid, grid, tid);
+            }
+        }
+#else
         for (uint32_t bid = 0; bid < grid; bid++)
             for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) {
                 if (vec)
@@ -71,6 +102,7 @@ long run(const uint8_t *payload, uint64_t nbytes, uint64_t nblocks, void *out, u
                 else
                     process<F, OT, UPT, false>(src, tab, a, bid, grid, tid);
             }
+#endif
         for (Check *c : {&chk, &chk_tr})
             if (c->errors) {
                 if (errors == 0) snprintf(err, errlen, "%s", c->msg);

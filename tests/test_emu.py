@@ -35,8 +35,7 @@ def test_emulated_kernel_matches_oracle(fmt, dtype):
     info = nq.format_query(fmt)
     B = info.block_values
     nblocks = 37
-    recipe = RECIPE if fmt == "nvfp4" else RAW
-    p = synth.payload(fmt, nblocks, 1000 + info.id, recipe)
+    p = synth.payload(fmt, nblocks, 1000 + info.id, RAW)
     got, bad, msg, guards = emu_lib.decode(info.id, p, nblocks, B, dtype)
     assert bad == 0, msg
     assert guards
@@ -58,11 +57,13 @@ def test_emulated_misaligned_payload_and_output(fmt, mis, out_mis):
 
 
 @pytest.mark.parametrize("fmt", ["gguf:q4_k", "gguf:q8_0", "gguf:mxfp4", "nvfp4", "gguf:iq2_s", "gguf:tq1_0"])
-@pytest.mark.parametrize("chunk,max_wgs", [(5, 1), (3, 2), (64, 3)])
+@pytest.mark.parametrize("chunk,max_wgs", [(5, 1), (3, 2), (64, 3), (700, 3), (2900, 2)])
 def test_emulated_chunks_and_grid_stride(fmt, chunk, max_wgs):
+    """Several launch chunks, each with several full staged tiles and a tail,
+    walked by small grids (the grid-stride loop turns many times)."""
     info = nq.format_query(fmt)
     B = info.block_values
-    nblocks = 300
+    nblocks = 300 if chunk < 100 else 5000
     p = synth.payload(fmt, nblocks, 5, RECIPE)
     got, bad, msg, guards = emu_lib.decode(info.id, p, nblocks, B, "bf16", mis=3, chunk=chunk,
                                            max_wgs=max_wgs)

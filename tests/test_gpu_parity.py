@@ -203,3 +203,41 @@ def test_full_size_llama3_8b_set_sampled():
             continue
         seen.add(key)
         _full_size_sampled(name, fmt, shape, recipe, seed, "bf16", nsample=1024)
+
+
+def test_graph_replays_match_eager():
+    """Decodes captured in a HIP graph give the eager result on every replay,
+    with eager work, output clearing and synchronization between replays."""
+    cases = [("gguf:q4_k", 512), ("nvfp4", 777), ("gguf:iq2_xxs", 300), ("gguf:q6_k", 129)]
+    items = []
+    for fmt, nb in cases:
+        info = nq.format_query(fmt)
+        p = synth.payload(fmt, nb, 31, RECIPE)
+        payload, keep = upload(p)
+        n = nb * info.block_values
+        ref = nq.dequantize_packed(fmt, payload, [n], torch.bfloat16)
+        out = torch.zeros(n, dtype=torch.bfloat16, device="cuda:0")
+        items.append((fmt, payload, keep, n, ref, out, p))
+    torch.cuda.synchronize()
+    for fmt, _, _, n, ref, _, p in items:
+        assert compare.same(to_numpy(ref, "bf16"), oracle.decode(fmt, p, [n], "bf16"), "bf16")
+    announce("graph capture of 4 decodes")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        h = torch.cuda.current_stream().cuda_stream
+        for fmt, payload, _, n, _, out, _ in items:
+            st = nq.dequantize_packed_raw(nq.format_query(fmt).id, payload.data_ptr(), payload.numel(), [n], 2,
+                                          out.data_ptr(), h)
+            assert st == 0
+    other = synth.payload("gguf:q8_0", 1000, 5, RECIPE)
+    other_dev, _ = upload(other)
+    for r in range(4):
+        announce(f"graph replay {r}")
+        for *_, out, _ in items:
+            out.zero_()
+        nq.dequantize_packed("gguf:q8_0", other_dev, [32000], torch.float32)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for fmt, _, _, n, ref, out, _ in items:
+            assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), (fmt, r)
