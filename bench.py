@@ -31,6 +31,42 @@ OUT_CODES = {"f32": 0, "f16": 1, "bf16": 2, "f64": 3}
 OUT_SIZE = {"f32": 4, "f16": 2, "bf16": 2, "f64": 8}
 
 
+def sources_sha256():
+    """Hash of the kernel sources without comments (the build the counter profile was taken on)."""
+    import glob
+    import re
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    csrc = os.path.join(here, "block_quantized_weight_nq_amd", "csrc")
+    files = sorted(glob.glob(os.path.join(csrc, "*.h")) + glob.glob(os.path.join(csrc, "*.hip")) +
+                   glob.glob(os.path.join(csrc, "*.cpp")))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f) as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        # comments and blank lines do not change the kernels
+        code = [ln.split("//", 1)[0].rstrip() for ln in text.splitlines()]
+        h.update("\n".join(ln for ln in code if ln).encode())
+    return h.hexdigest()
+
+
+def profiled_traffic(kernel_fmt):
+    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE profile (copy-calibrated),
+    or None when that profile was taken on other kernel sources."""
+    import glob
+    here = os.path.dirname(os.path.abspath(__file__))
+    for path in sorted(glob.glob(os.path.join(here, "profiles", "traffic_*.md"))):
+        with open(path) as f:
+            for line in f:
+                line = line.strip()
+                if line.startswith("TRAFFIC "):
+                    rec = json.loads(line[len("TRAFFIC "):])
+                    if rec.get("sources_sha256") == sources_sha256() and kernel_fmt in rec.get("kernels", {}):
+                        return rec["kernels"][kernel_fmt]["traffic_bytes"]
+    return None
+
+
 def log(msg):
     sys.stderr.write(f"[bench] {msg}\n")
     sys.stderr.flush()
@@ -248,7 +284,8 @@ def main():
     d = formats[dom]
     achieved = d["bytes_per_launch"] / (d["mean_launch_us"] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": f"k_decode {dom} -> bf16",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": profiled_traffic(dom),
+                "kernel": f"k_decode {dom} -> bf16",
                 "bytes_per_launch": d["bytes_per_launch"], "mean_launch_us": d["mean_launch_us"]}
     for f in formats.values():
         del f["total_ms"]

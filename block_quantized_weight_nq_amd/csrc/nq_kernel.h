@@ -1,31 +1,30 @@
 // nq_kernel.h -- the decode kernel template and its launcher.
 //
-// Streaming layout: thread t of workgroup w handles units (8 outputs each)
-// u = base + k*256 + t for k < UPT, with base stepping over the grid, so a
-// wave's 64 lanes write 64 consecutive units: one contiguous 1 KiB (bf16/f16)
-// or 2 KiB (f32) run per store instruction.  Each lane reads only the payload
-// dwords its unit needs; lanes of a block share them through the vector L1.
-// IQ formats stage their codebook in LDS once per workgroup; "nvfp4" stages a
-// 256 x 16 table of its correctly rounded quotients.
+// One persistent kernel per (format, output type, vector store).  The output
+// is cut into tiles of 256*UPT units (a unit is 8 consecutive outputs of one
+// block); workgroup w takes tiles w, w + grid, ...  For each tile the
+// workgroup copies the tile's payload bytes into one of two LDS slots with
+// coalesced 16-byte loads, keeps the next tile's loads in flight while it
+// decodes the current one from LDS, and writes its units so that a wave's 64
+// lanes cover 64 consecutive units: one contiguous 1 KiB (bf16/f16) or 2 KiB
+// (f32) run per store instruction.  A partial last tile is decoded straight
+// from global memory.  IQ formats copy their codebook to LDS once per
+// workgroup; "nvfp4" fills a 1024-entry table of its correctly rounded
+// quotients (128 scale magnitudes x 8 code magnitudes; signs are applied as
+// bit flips).
 #pragma once
 
 #include "iq_grids.h"
 #include "nq_decode.h"
 
 // Tuning knobs (compile-time; the defaults are the measured best on MI355X):
-//   NQ_LDS        1: stage each tile's payload in LDS (0: per-unit global loads)
 //   NQ_NTL        1: staging loads are non-temporal (each payload byte is read once)
-//   NQ_UPT        units (8 outputs) per thread per tile
+//   NQ_UPT        units (8 outputs) per thread per tile for every format
+//                 (default: the per-format table in upt_for)
 //   NQ_WG_PER_CU  persistent-grid workgroups per compute unit
 //   NQ_NT_STORE   non-temporal output stores: 0 never, 1 always, 2 16-bit outputs only
-#ifndef NQ_LDS
-#define NQ_LDS 1
-#endif
 #ifndef NQ_NTL
 #define NQ_NTL 1
-#endif
-#ifndef NQ_UPT
-#define NQ_UPT 4
 #endif
 #ifndef NQ_WG_PER_CU
 #define NQ_WG_PER_CU 8
@@ -81,45 +80,6 @@ struct DevSrc {
         r[2] = v.z;
         r[3] = v.w;
     }
-};
-
-// Two-pass source pair.  No payload address depends on loaded data, so a
-// decoder's loads form a fixed sequence.  Pass 1 runs the decoder over a
-// Recorder, which issues the loads and keeps the raw dwords (the arithmetic
-// of that pass is dead and compiled away); pass 2 runs it over a Player,
-// which hands the same dwords back in the same order.  Every unit of a
-// thread thus has its loads in flight before any of them is consumed.
-constexpr int RAW_CAP = 16;  // dwords one unit may load
-
-template <class Base>
-struct Recorder {
-    Base src;
-    uint32_t *buf;
-    mutable int n;
-    uint32_t last;
-    template <int N>
-    NQ_HD void load(uint32_t i, uint32_t (&r)[N]) const {
-        src.template load<N>(i, r);
-#pragma unroll
-        for (int k = 0; k < N; k++) buf[n++] = r[k];
-    }
-    NQ_HD uint32_t dw(uint32_t i) const {
-        const uint32_t v = src.dw(i);
-        buf[n++] = v;
-        return v;
-    }
-};
-
-struct Player {
-    const uint32_t *buf;
-    mutable int n;
-    uint32_t last;
-    template <int N>
-    NQ_HD void load(uint32_t, uint32_t (&r)[N]) const {
-#pragma unroll
-        for (int k = 0; k < N; k++) r[k] = buf[n++];
-    }
-    NQ_HD uint32_t dw(uint32_t) const { return buf[n++]; }
 };
 
 // Lookup tables (LDS in the kernels, host arrays in the emulator).
@@ -241,69 +201,6 @@ NQ_HD void store8(void *out, uint32_t u, const float (&y)[8]) {
 
 constexpr int WG = 256;  // threads per workgroup (4 wave64)
 
-// One thread's share of a launch.  Units are grouped in tiles of WG * UPT;
-// workgroup `bid` takes tiles bid, bid + nwg, ...  Full tiles run software-
-// pipelined: the loads of a thread's next tile are issued before the current
-// tile is computed and stored, so the wait for a tile's loads never waits on
-// the previous tile's stores (loads and stores share one counter).  The last,
-// partial tile takes a guarded path.
-template <int F, int UPT, class Src, class T>
-NQ_HD void fetch_tile(const Src &src, const T &tab, const KArgs &a, uint32_t tile, uint32_t tid,
-                      uint32_t (&raw)[UPT][RAW_CAP]) {
-    constexpr uint32_t UPB = block_values(F) / 8;
-    constexpr uint32_t S = block_bytes(F);
-#pragma unroll
-    for (int k = 0; k < UPT; k++) {
-        const uint32_t u = tile * (uint32_t)(WG * UPT) + (uint32_t)(k * WG) + tid;
-        const Recorder<Src> rec{src, raw[k], 0, src.last};
-        float dead[8];
-        decode_unit<F>(rec, a.mis + (u / UPB) * S, u % UPB, tab, dead);
-    }
-}
-
-template <int F, int OT, int UPT, bool VEC, class Src, class T>
-NQ_HD void process(const Src &src, const T &tab, const KArgs &a, uint32_t bid, uint32_t nwg, uint32_t tid) {
-    constexpr uint32_t UPB = block_values(F) / 8;
-    constexpr uint32_t S = block_bytes(F);
-    constexpr uint32_t PER = (uint32_t)(WG * UPT);
-    const uint32_t full = a.nunits / PER;
-    uint32_t t = bid;
-    if (t < full) {
-        uint32_t raw[UPT][RAW_CAP];
-        fetch_tile<F, UPT>(src, tab, a, t, tid, raw);
-        for (; t < full; t += nwg) {
-            uint32_t cur[UPT][RAW_CAP];
-#pragma unroll
-            for (int k = 0; k < UPT; k++)
-#pragma unroll
-                for (int i = 0; i < RAW_CAP; i++) cur[k][i] = raw[k][i];
-            // next tile's loads (the current tile again on the last pass: always in bounds)
-            const uint32_t tn = (t + nwg < full) ? t + nwg : t;
-            fetch_tile<F, UPT>(src, tab, a, tn, tid, raw);
-            float y[UPT][8];
-#pragma unroll
-            for (int k = 0; k < UPT; k++) {
-                const uint32_t u = t * PER + (uint32_t)(k * WG) + tid;
-                const Player pl{cur[k], 0, src.last};
-                decode_unit<F>(pl, a.mis + (u / UPB) * S, u % UPB, tab, y[k]);
-            }
-#pragma unroll
-            for (int k = 0; k < UPT; k++) store8<OT, VEC>(a.out, t * PER + (uint32_t)(k * WG) + tid, y[k]);
-        }
-    }
-    if (t == full) {  // the partial tile, if any, falls to exactly one workgroup
-#pragma unroll
-        for (int k = 0; k < UPT; k++) {
-            const uint32_t u = full * PER + (uint32_t)(k * WG) + tid;
-            if (u < a.nunits) {
-                float y[8];
-                decode_unit<F>(src, a.mis + (u / UPB) * S, u % UPB, tab, y);
-                store8<OT, VEC>(a.out, u, y);
-            }
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
 // LDS-staged decode.  A workgroup copies each full tile's payload bytes into
 // LDS with coalesced 16-byte loads (one to three per thread), loads of the
@@ -334,7 +231,7 @@ struct Stage {
     static constexpr uint32_t NDW = (TB + 3) / 4 + 1;           // dwords spanned, any start offset
     static constexpr uint32_t NCH = (NDW + 3) / 4;              // 16-byte chunks
     static constexpr uint32_t NK = (NCH + WG - 1) / WG;         // chunks per thread
-    static constexpr uint32_t SLOT_DW = NK * WG * 4;            // LDS dwords per slot
+    static constexpr uint32_t SLOT_DW = NCH * 4;                // LDS dwords per slot (chunks written)
 };
 
 // Global loads of tile t's chunks for this thread (into registers).
@@ -458,8 +355,17 @@ NQ_HD void fill_tables(uint64_t *t8, uint32_t *t4, float *nvq, const TrSrc &tr, 
     }
 }
 
+#ifndef NQ_WAVES_PER_EU
+#define NQ_WAVES_PER_EU 0  // >0: ask the compiler for this many waves per SIMD (caps VGPRs)
+#endif
+#if NQ_WAVES_PER_EU > 0
+#define NQ_OCCUPANCY __attribute__((amdgpu_waves_per_eu(NQ_WAVES_PER_EU)))
+#else
+#define NQ_OCCUPANCY
+#endif
+
 template <int F, int OT, int UPT, bool VEC>
-__global__ __launch_bounds__(WG) void k_decode(KArgs a) {
+__global__ __launch_bounds__(WG) NQ_OCCUPANCY void k_decode(KArgs a) {
     using TS = TabSpec<F>;
     __shared__ uint64_t t8[TS::n8 > 0 ? TS::n8 : 1];
     __shared__ uint32_t t4[TS::n4 > 0 ? TS::n4 : 1];
@@ -470,12 +376,8 @@ __global__ __launch_bounds__(WG) void k_decode(KArgs a) {
         __syncthreads();
     }
     const Tab tab{t8, t4, nvq};
-#if NQ_LDS
     __shared__ __attribute__((aligned(16))) uint32_t stage[2 * Stage<F, UPT>::SLOT_DW];
     process_lds<F, OT, UPT, VEC>(tab, a, blockIdx.x, gridDim.x, tid, stage);
-#else
-    process<F, OT, UPT, VEC>(DevSrc{a.base, a.last}, tab, a, blockIdx.x, gridDim.x, tid);
-#endif
 }
 
 // Host launch description for one call.
@@ -487,7 +389,6 @@ struct LaunchArgs {
     uint32_t max_wgs;        // persistent-grid cap for the device
 };
 
-constexpr int UPT_DEFAULT = NQ_UPT;  // units per thread per tile
 
 // Blocks per launch chunk: unit indices stay below 2^30 and payload byte
 // offsets below 2^32.
@@ -518,19 +419,41 @@ NQ_HD KArgs chunk_args(const LaunchArgs &L, uint64_t b0, uint64_t nb, uint32_t *
     return a;
 }
 
+// Units per thread per tile for format F.  Measured on MI355X at a 16 GiB
+// footprint and on the Llama-3-8B-shaped step: 8 for the formats with the
+// least payload per output (ternary, IQ, FP4: their tiles stay small in LDS)
+// and for nvfp4 (fewer workgroups build its quotient table), 4 for the rest.
+// NQ_UPT overrides every format when defined.
+template <int F>
+constexpr int upt_for() {
+#ifdef NQ_UPT
+    return NQ_UPT;
+#else
+    return (F == TQ1_0 || F == TQ2_0 || F == MXFP4 || F == NVFP4_GGUF || F == NVFP4_DIV || F == IQ4_XS ||
+            is_iq(F))
+               ? 8
+               : 4;
+#endif
+}
+
+template <int F, int OT, int UPT>
+int launch_chunk(const LaunchArgs &L, uint64_t b0, uint64_t nb, hipStream_t stream) {
+    uint32_t grid;
+    const KArgs a = chunk_args<F, OT, UPT>(L, b0, nb, &grid);
+    if (((uintptr_t)a.out & 15) == 0)
+        hipLaunchKernelGGL((k_decode<F, OT, UPT, true>), dim3(grid), dim3(WG), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_decode<F, OT, UPT, false>), dim3(grid), dim3(WG), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? 0 : 9;  // NQ_ERR_HIP
+}
+
 template <int F, int OT>
 int launch(const LaunchArgs &L, hipStream_t stream) {
-    constexpr int UPT = UPT_DEFAULT;
     constexpr uint64_t CB = chunk_blocks<F>();
     for (uint64_t b0 = 0; b0 < L.nblocks; b0 += CB) {
         const uint64_t nb = (L.nblocks - b0 < CB) ? L.nblocks - b0 : CB;
-        uint32_t grid;
-        const KArgs a = chunk_args<F, OT, UPT>(L, b0, nb, &grid);
-        if (((uintptr_t)a.out & 15) == 0)
-            hipLaunchKernelGGL((k_decode<F, OT, UPT, true>), dim3(grid), dim3(WG), 0, stream, a);
-        else
-            hipLaunchKernelGGL((k_decode<F, OT, UPT, false>), dim3(grid), dim3(WG), 0, stream, a);
-        if (hipGetLastError() != hipSuccess) return 9;  // NQ_ERR_HIP
+        const int st = launch_chunk<F, OT, upt_for<F>()>(L, b0, nb, stream);
+        if (st != 0) return st;
     }
     return 0;
 }

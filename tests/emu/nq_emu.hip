@@ -40,74 +40,75 @@ struct HostSrc {
     }
 };
 
+// One launch chunk with UPT units per thread, as the kernel runs it: every
+// thread stages a tile, then every thread decodes it (the barrier), then
+// the tail tile.
+template <int F, int OT, int UPT>
+long run_chunk(const nq::LaunchArgs &L, uint64_t b0, uint64_t nb, const uint8_t *payload, uint64_t nbytes,
+               char *err, int errlen) {
+    using namespace nq;
+    constexpr uint64_t S = block_bytes(F);
+    using TS = TabSpec<F>;
+    using ST = Stage<F, UPT>;
+    std::vector<uint64_t> t8(TS::n8 > 0 ? TS::n8 : 1);
+    std::vector<uint32_t> t4(TS::n4 > 0 ? TS::n4 : 1);
+    std::vector<float> nvq(TS::nf > 0 ? TS::nf : 1);
+    uint32_t grid;
+    const KArgs a = chunk_args<F, OT, UPT>(L, b0, nb, &grid);
+    Check chk{(uintptr_t)(payload + b0 * S), (uintptr_t)(payload + (b0 + nb) * S), 0, {0}};
+    Check chk_tr{(uintptr_t)(payload + nbytes - 4), (uintptr_t)(payload + nbytes), 0, {0}};
+    if (TS::n8 + TS::n4 + TS::nf > 0)
+        for (uint32_t tid = 0; tid < (uint32_t)WG; tid++)
+            fill_tables<F>(t8.data(), t4.data(), nvq.data(), HostSrc{a.tr_base, (a.tr_mis + 3u) >> 2, &chk_tr},
+                           a.tr_mis, tid, WG);
+    const Tab tab{t8.data(), t4.data(), nvq.data()};
+    const HostSrc src{a.base, a.last, &chk};
+    const bool vec = ((uintptr_t)a.out & 15) == 0;
+    std::vector<uint32_t> slot(ST::SLOT_DW);
+    const uint32_t full = a.nunits / ST::PER;
+    for (uint32_t bid = 0; bid < grid; bid++) {
+        for (uint32_t t = bid; t < full; t += grid) {
+            std::fill(slot.begin(), slot.end(), 0xA5A5A5A5u);  // stale words poison the result
+            for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) {
+                uint32_t r[ST::NK][4];
+                stage_load<F, UPT>(src, a, t, tid, r);
+                stage_store<F, UPT>(slot.data(), a, t, tid, r);
+            }
+            for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) {
+                if (vec)
+                    decode_staged<F, OT, UPT, true>(tab, a, t, tid, slot.data());
+                else
+                    decode_staged<F, OT, UPT, false>(tab, a, t, tid, slot.data());
+            }
+        }
+        for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) {
+            if (vec)
+                decode_tail<F, OT, UPT, true>(src, tab, a, bid, grid, tid);
+            else
+                decode_tail<F, OT, UPT, false>(src, tab, a, bid, grid, tid);
+        }
+    }
+    long errors = 0;
+    for (Check *c : {&chk, &chk_tr})
+        if (c->errors) {
+            if (errors == 0) snprintf(err, errlen, "%s", c->msg);
+            errors += c->errors;
+        }
+    return errors;
+}
+
+// The launcher's chunk loop and per-chunk choice of units per thread.
 template <int F, int OT>
 long run(const uint8_t *payload, uint64_t nbytes, uint64_t nblocks, void *out, uint32_t max_wgs,
          uint64_t chunk, char *err, int errlen) {
     using namespace nq;
-    constexpr int UPT = UPT_DEFAULT;
-    constexpr uint64_t S = block_bytes(F);
-    using TS = TabSpec<F>;
     LaunchArgs L{payload, nbytes, nblocks, out, max_wgs};
     const uint64_t CB = chunk ? chunk : chunk_blocks<F>();
-    std::vector<uint64_t> t8(TS::n8 > 0 ? TS::n8 : 1);
-    std::vector<uint32_t> t4(TS::n4 > 0 ? TS::n4 : 1);
-    std::vector<float> nvq(TS::nf > 0 ? TS::nf : 1);
     long errors = 0;
     for (uint64_t b0 = 0; b0 < nblocks; b0 += CB) {
         const uint64_t nb = (nblocks - b0 < CB) ? nblocks - b0 : CB;
-        uint32_t grid;
-        const KArgs a = chunk_args<F, OT, UPT>(L, b0, nb, &grid);
-        Check chk{(uintptr_t)(payload + b0 * S), (uintptr_t)(payload + (b0 + nb) * S), 0, {0}};
-        Check chk_tr{(uintptr_t)(payload + nbytes - 4), (uintptr_t)(payload + nbytes), 0, {0}};
-        if (TS::n8 + TS::n4 + TS::nf > 0)
-            for (uint32_t tid = 0; tid < (uint32_t)WG; tid++)
-                fill_tables<F>(t8.data(), t4.data(), nvq.data(), HostSrc{a.tr_base, (a.tr_mis + 3u) >> 2, &chk_tr},
-                               a.tr_mis, tid, WG);
-        const Tab tab{t8.data(), t4.data(), nvq.data()};
-        const HostSrc src{a.base, a.last, &chk};
-        const bool vec = ((uintptr_t)a.out & 15) == 0;
-#if NQ_LDS
-        // the staged path, phase by phase: every thread stages a tile, then
-        // every thread decodes it (the kernel's barrier), then the tail tile
-        using ST = Stage<F, UPT>;
-        std::vector<uint32_t> slot(ST::SLOT_DW);
-        const uint32_t full = a.nunits / ST::PER;
-        for (uint32_t bid = 0; bid < grid; bid++) {
-            for (uint32_t t = bid; t < full; t += grid) {
-                std::fill(slot.begin(), slot.end(), 0xA5A5A5A5u);  // stale words poison the result
-                for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) {
-                    uint32_t r[ST::NK][4];
-                    stage_load<F, UPT>(src, a, t, tid, r);
-                    stage_store<F, UPT>(slot.data(), a, t, tid, r);
-                }
-                for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) {
-                    if (vec)
-                        decode_staged<F, OT, UPT, true>(tab, a, t, tid, slot.data());
-                    else
-                        decode_staged<F, OT, UPT, false>(tab, a, t, tid, slot.data());
-                }
-            }
-            for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) {
-                if (vec)
-                    decode_tail<F, OT, UPT, true>(src, tab, a, bid, grid, tid);
-                else
-                    decode_tail<F, OT, UPT, false>(src, tab, a, bid, grid, tid);
-            }
-        }
-#else
-        for (uint32_t bid = 0; bid < grid; bid++)
-            for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) {
-                if (vec)
-                    process<F, OT, UPT, true>(src, tab, a, bid, grid, tid);
-                else
-                    process<F, OT, UPT, false>(src, tab, a, bid, grid, tid);
-            }
-#endif
-        for (Check *c : {&chk, &chk_tr})
-            if (c->errors) {
-                if (errors == 0) snprintf(err, errlen, "%s", c->msg);
-                errors += c->errors;
-            }
+        const long e = run_chunk<F, OT, upt_for<F>()>(L, b0, nb, payload, nbytes, err, errlen);
+        errors += e;
     }
     return errors;
 }

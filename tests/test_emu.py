@@ -57,7 +57,7 @@ def test_emulated_misaligned_payload_and_output(fmt, mis, out_mis):
 
 
 @pytest.mark.parametrize("fmt", ["gguf:q4_k", "gguf:q8_0", "gguf:mxfp4", "nvfp4", "gguf:iq2_s", "gguf:tq1_0"])
-@pytest.mark.parametrize("chunk,max_wgs", [(5, 1), (3, 2), (64, 3), (700, 3), (2900, 2)])
+@pytest.mark.parametrize("chunk,max_wgs", [(5, 1), (3, 2), (64, 3), (700, 3), (2900, 2), (700, 16), (2900, 8)])
 def test_emulated_chunks_and_grid_stride(fmt, chunk, max_wgs):
     """Several launch chunks, each with several full staged tiles and a tail,
     walked by small grids (the grid-stride loop turns many times)."""
