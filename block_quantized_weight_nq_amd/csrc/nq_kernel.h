@@ -234,24 +234,42 @@ struct Stage {
     static constexpr uint32_t SLOT_DW = NCH * 4;                // LDS dwords per slot (chunks written)
 };
 
+// Chunk c of tile t covers payload dwords a0 + 4c .. a0 + 4c + 3, where a0 is
+// the tile's first dword; chunks 0..cmax hold the tile's bytes.  Threads
+// whose chunk index passes cmax take chunk cmax again (same address within
+// the wave, so no extra traffic, and the same value written to the same LDS
+// dwords), which keeps the staging code free of branches.
+template <int F, int UPT>
+NQ_HD uint32_t stage_first(const KArgs &a, uint32_t t, uint32_t *cmax) {
+    using ST = Stage<F, UPT>;
+    const uint32_t p = a.mis + t * ST::TB;
+    *cmax = (((p + ST::TB - 1) >> 2) - (p >> 2)) >> 2;
+    return p >> 2;
+}
+
+// Tiles staged through LDS: the full tiles whose chunks all end at or before
+// the last payload dword.  Only the last full tile can fail that (when no
+// partial tile follows it); it then joins the tail.
+template <int F, int UPT>
+NQ_HD uint32_t staged_tiles(const KArgs &a) {
+    using ST = Stage<F, UPT>;
+    const uint32_t full = a.nunits / ST::PER;
+    if (full == 0) return 0;
+    uint32_t cmax;
+    const uint32_t a0 = stage_first<F, UPT>(a, full - 1, &cmax);
+    return a0 + 4u * cmax + 3u <= a.last ? full : full - 1;
+}
+
 // Global loads of tile t's chunks for this thread (into registers).
 template <int F, int UPT, class Src>
 NQ_HD void stage_load(const Src &src, const KArgs &a, uint32_t t, uint32_t tid, uint32_t (&r)[Stage<F, UPT>::NK][4]) {
     using ST = Stage<F, UPT>;
-    const uint32_t p = a.mis + t * ST::TB;
-    const uint32_t a0 = p >> 2, a_end = (p + ST::TB - 1) >> 2;
+    uint32_t cmax;
+    const uint32_t a0 = stage_first<F, UPT>(a, t, &cmax);
 #pragma unroll
     for (uint32_t k = 0; k < ST::NK; k++) {
-        const uint32_t c = k * WG + tid;
-        const uint32_t d0 = a0 + 4 * c;
-        if (d0 <= a_end) {
-            if (d0 + 3 <= src.last) {
-                src.load_stream4(d0, r[k]);
-            } else {
-#pragma unroll
-                for (uint32_t j = 0; j < 4; j++) r[k][j] = src.dw(d0 + j <= src.last ? d0 + j : src.last);
-            }
-        }
+        const uint32_t c0 = k * WG + tid;
+        src.load_stream4(a0 + 4u * (c0 < cmax ? c0 : cmax), r[k]);
     }
 }
 
@@ -259,16 +277,14 @@ template <int F, int UPT>
 NQ_HD void stage_store(uint32_t *slot, const KArgs &a, uint32_t t, uint32_t tid,
                        const uint32_t (&r)[Stage<F, UPT>::NK][4]) {
     using ST = Stage<F, UPT>;
-    const uint32_t p = a.mis + t * ST::TB;
-    const uint32_t a0 = p >> 2, a_end = (p + ST::TB - 1) >> 2;
+    uint32_t cmax;
+    stage_first<F, UPT>(a, t, &cmax);
 #pragma unroll
     for (uint32_t k = 0; k < ST::NK; k++) {
-        const uint32_t c = k * WG + tid;
-        if (a0 + 4 * c <= a_end) {
-            u32x4 v;
-            v.x = r[k][0]; v.y = r[k][1]; v.z = r[k][2]; v.w = r[k][3];
-            *(u32x4 *)(slot + 4 * c) = v;
-        }
+        const uint32_t c0 = k * WG + tid;
+        u32x4 v;
+        v.x = r[k][0]; v.y = r[k][1]; v.z = r[k][2]; v.w = r[k][3];
+        *(u32x4 *)(slot + 4u * (c0 < cmax ? c0 : cmax)) = v;
     }
 }
 
@@ -292,43 +308,53 @@ NQ_HD void decode_staged(const T &tab, const KArgs &a, uint32_t t, uint32_t tid,
     for (int k = 0; k < UPT; k++) store8<OT, VEC>(a.out, t * ST::PER + (uint32_t)(k * WG) + tid, y[k]);
 }
 
-// The partial last tile (if any), straight from global memory, decoded by
-// the workgroup whose turn it is: tile `full` falls to bid == full % nwg.
+// The tiles after the staged ones (a partial last tile, and the last full
+// tile when its chunks would pass the payload's end), straight from global
+// memory; tile tt falls to the workgroup bid == tt % nwg.
 template <int F, int OT, int UPT, bool VEC, class Src, class T>
 NQ_HD void decode_tail(const Src &src, const T &tab, const KArgs &a, uint32_t bid, uint32_t nwg, uint32_t tid) {
     using ST = Stage<F, UPT>;
-    const uint32_t full = a.nunits / ST::PER;
-    if (full * ST::PER == a.nunits || full % nwg != bid) return;
+    const uint32_t ntiles = (a.nunits + ST::PER - 1) / ST::PER;
+    for (uint32_t tt = staged_tiles<F, UPT>(a); tt < ntiles; tt++) {
+        if (tt % nwg != bid) continue;
 #pragma unroll
-    for (int k = 0; k < UPT; k++) {
-        const uint32_t u = full * ST::PER + (uint32_t)(k * WG) + tid;
-        if (u < a.nunits) {
-            float y[8];
-            decode_unit<F>(src, a.mis + (u / ST::UPB) * block_bytes(F), u % ST::UPB, tab, y);
-            store8<OT, VEC>(a.out, u, y);
+        for (int k = 0; k < UPT; k++) {
+            const uint32_t u = tt * ST::PER + (uint32_t)(k * WG) + tid;
+            if (u < a.nunits) {
+                float y[8];
+                decode_unit<F>(src, a.mis + (u / ST::UPB) * block_bytes(F), u % ST::UPB, tab, y);
+                store8<OT, VEC>(a.out, u, y);
+            }
         }
     }
 }
 
-// Workgroup `bid` decodes full tiles bid, bid + nwg, ... (then the tail).
+// Workgroup `bid` decodes staged tiles bid, bid + nwg, ... (then the tail).
 template <int F, int OT, int UPT, bool VEC, class T>
 __device__ __forceinline__ void process_lds(const T &tab, const KArgs &a, uint32_t bid, uint32_t nwg, uint32_t tid,
                                             uint32_t *lds) {
     using ST = Stage<F, UPT>;
-    const uint32_t full = a.nunits / ST::PER;
+    const uint32_t nst = staged_tiles<F, UPT>(a);
     const DevSrc src{a.base, a.last};
     uint32_t t = bid;
-    if (t < full) {
+    if (t < nst) {
+        // The next tile's loads are issued before this tile's output stores
+        // and copied to LDS after them, so the wait for the loads does not
+        // wait for the stores (one counter covers both, in issue order).
         uint32_t r[ST::NK][4];
         stage_load<F, UPT>(src, a, t, tid, r);
         uint32_t slot = 0;
-        for (; t < full; t += nwg) {
-            uint32_t *buf = lds + slot * ST::SLOT_DW;
-            stage_store<F, UPT>(buf, a, t, tid, r);
-            __syncthreads();
-            if (t + nwg < full) stage_load<F, UPT>(src, a, t + nwg, tid, r);
-            decode_staged<F, OT, UPT, VEC>(tab, a, t, tid, buf);
+        stage_store<F, UPT>(lds, a, t, tid, r);
+        __syncthreads();
+        for (;;) {
+            const bool more = t + nwg < nst;
+            if (more) stage_load<F, UPT>(src, a, t + nwg, tid, r);
+            decode_staged<F, OT, UPT, VEC>(tab, a, t, tid, lds + slot * ST::SLOT_DW);
+            if (!more) break;
+            t += nwg;
             slot ^= 1u;
+            stage_store<F, UPT>(lds + slot * ST::SLOT_DW, a, t, tid, r);
+            __syncthreads();
         }
     }
     decode_tail<F, OT, UPT, VEC>(src, tab, a, bid, nwg, tid);

@@ -64,16 +64,23 @@ long run_chunk(const nq::LaunchArgs &L, uint64_t b0, uint64_t nb, const uint8_t 
     const Tab tab{t8.data(), t4.data(), nvq.data()};
     const HostSrc src{a.base, a.last, &chk};
     const bool vec = ((uintptr_t)a.out & 15) == 0;
-    std::vector<uint32_t> slot(ST::SLOT_DW);
-    const uint32_t full = a.nunits / ST::PER;
+    // the LDS slot plus guard words that staging must leave alone
+    constexpr uint32_t GUARD = 64, GUARD_WORD = 0x5A5A5A5Au;
+    std::vector<uint32_t> slot(ST::SLOT_DW + GUARD);
+    long lds_errors = 0;
+    const uint32_t nst = staged_tiles<F, UPT>(a);
     for (uint32_t bid = 0; bid < grid; bid++) {
-        for (uint32_t t = bid; t < full; t += grid) {
-            std::fill(slot.begin(), slot.end(), 0xA5A5A5A5u);  // stale words poison the result
+        for (uint32_t t = bid; t < nst; t += grid) {
+            std::fill(slot.begin(), slot.begin() + ST::SLOT_DW, 0xA5A5A5A5u);  // stale words poison the result
+            std::fill(slot.begin() + ST::SLOT_DW, slot.end(), GUARD_WORD);
             for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) {
                 uint32_t r[ST::NK][4];
                 stage_load<F, UPT>(src, a, t, tid, r);
                 stage_store<F, UPT>(slot.data(), a, t, tid, r);
             }
+            for (uint32_t i = ST::SLOT_DW; i < ST::SLOT_DW + GUARD; i++)
+                if (slot[i] != GUARD_WORD && lds_errors++ == 0)
+                    snprintf(chk.msg, sizeof chk.msg, "staging wrote past the LDS slot (tile %u)", t);
             for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) {
                 if (vec)
                     decode_staged<F, OT, UPT, true>(tab, a, t, tid, slot.data());
@@ -89,6 +96,7 @@ long run_chunk(const nq::LaunchArgs &L, uint64_t b0, uint64_t nb, const uint8_t 
         }
     }
     long errors = 0;
+    chk.errors += lds_errors;
     for (Check *c : {&chk, &chk_tr})
         if (c->errors) {
             if (errors == 0) snprintf(err, errlen, "%s", c->msg);
@@ -135,6 +143,21 @@ extern "C" __attribute__((visibility("default"))) long nq_emu_decode(int fmt, in
     switch (fmt) {
 #define C(X) \
     case X: return run_ot<X>(ot, payload, nbytes, nblocks, out, max_wgs, chunk_blocks, err, errlen);
+        C(Q4_0) C(Q4_1) C(Q5_0) C(Q5_1) C(Q8_0) C(Q8_1) C(Q2_K) C(Q3_K) C(Q4_K) C(Q5_K) C(Q6_K) C(Q8_K)
+        C(IQ2_XXS) C(IQ2_XS) C(IQ3_XXS) C(IQ1_S) C(IQ4_NL) C(IQ3_S) C(IQ2_S) C(IQ4_XS) C(IQ1_M)
+        C(TQ1_0) C(TQ2_0) C(MXFP4) C(NVFP4_GGUF) C(Q1_0) C(Q2_0) C(NVFP4_DIV)
+#undef C
+    default: return -1;
+    }
+}
+
+// Whole blocks per staged tile of format fmt (the launcher's choice of units
+// per thread), for tests that place tile boundaries.
+extern "C" __attribute__((visibility("default"))) long nq_emu_tile_blocks(int fmt) {
+    using namespace nq;
+    switch (fmt) {
+#define C(X) \
+    case X: return (long)Stage<X, upt_for<X>()>::BPT;
         C(Q4_0) C(Q4_1) C(Q5_0) C(Q5_1) C(Q8_0) C(Q8_1) C(Q2_K) C(Q3_K) C(Q4_K) C(Q5_K) C(Q6_K) C(Q8_K)
         C(IQ2_XXS) C(IQ2_XS) C(IQ3_XXS) C(IQ1_S) C(IQ4_NL) C(IQ3_S) C(IQ2_S) C(IQ4_XS) C(IQ1_M)
         C(TQ1_0) C(TQ2_0) C(MXFP4) C(NVFP4_GGUF) C(Q1_0) C(Q2_0) C(NVFP4_DIV)

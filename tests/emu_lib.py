@@ -38,6 +38,8 @@ def lib():
                                     ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64,
                                     ctypes.c_char_p, ctypes.c_int]
         L.nq_emu_decode.restype = ctypes.c_long
+        L.nq_emu_tile_blocks.argtypes = [ctypes.c_int]
+        L.nq_emu_tile_blocks.restype = ctypes.c_long
         _lib = L
     return _lib
 
@@ -67,3 +69,8 @@ def decode(fmt_id, payload, nblocks, B, dtype, mis=0, out_mis=0, max_wgs=2048, c
     guards = bool(np.all(obuf[:ooff] == 0xA5) and np.all(obuf[ooff + n * osz:] == 0xA5))
     vals = obuf[ooff:ooff + n * osz].copy().view(NPT[dtype])
     return vals, rc, err.value.decode(), guards
+
+
+def tile_blocks(fmt_id):
+    """Whole blocks per staged tile of the format's kernel."""
+    return lib().nq_emu_tile_blocks(fmt_id)

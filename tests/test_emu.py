@@ -72,6 +72,25 @@ def test_emulated_chunks_and_grid_stride(fmt, chunk, max_wgs):
     assert _same(got, _oracle(fmt, p, nblocks, B, "bf16"), "bf16")
 
 
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_emulated_exact_tile_multiples(fmt):
+    """Payloads that end exactly at a tile boundary, at every payload
+    alignment: the last full tile's 16-byte staging chunks may pass the
+    payload's end, so that tile must be decoded without staging."""
+    info = nq.format_query(fmt)
+    B = info.block_values
+    bpt = emu_lib.tile_blocks(info.id)
+    assert bpt > 0
+    for nblocks, max_wgs in ((bpt, 1), (2 * bpt, 1), (3 * bpt, 2), (bpt + 1, 1), (2 * bpt - 1, 2)):
+        p = synth.payload(fmt, nblocks, 11 + nblocks, RECIPE)
+        ref = _oracle(fmt, p, nblocks, B, "bf16")
+        for mis in range(4):
+            got, bad, msg, guards = emu_lib.decode(info.id, p, nblocks, B, "bf16", mis=mis, max_wgs=max_wgs)
+            assert bad == 0, (nblocks, mis, msg)
+            assert guards
+            assert _same(got, ref, "bf16"), (nblocks, mis)
+
+
 @pytest.mark.parametrize("d_w", [1.0, 3.0, 448.0, 1e-30, 3e38])
 def test_emulated_nvfp4_divisor(d_w):
     info = nq.format_query("nvfp4")
