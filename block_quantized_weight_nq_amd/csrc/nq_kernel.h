@@ -19,8 +19,8 @@
 
 // Tuning knobs (compile-time; the defaults are the measured best on MI355X):
 //   NQ_NTL        1: staging loads are non-temporal (each payload byte is read once)
-//   NQ_UPT        units (8 outputs) per thread per tile for every format
-//                 (default: the per-format table in upt_for)
+//   NQ_UPT        units (8 outputs) per thread per tile for every launch
+//                 (default: chosen per launch from its size, see choose_upt)
 //   NQ_WG_PER_CU  persistent-grid workgroups per compute unit
 //   NQ_NT_STORE   non-temporal output stores: 0 never, 1 always, 2 16-bit outputs only
 #ifndef NQ_NTL
@@ -260,16 +260,22 @@ NQ_HD uint32_t staged_tiles(const KArgs &a) {
     return a0 + 4u * cmax + 3u <= a.last ? full : full - 1;
 }
 
-// Global loads of tile t's chunks for this thread (into registers).
+// Global loads of tile t's chunks for this thread (into registers).  The
+// dword index is also clamped to end at the last payload dword, which changes
+// nothing for a staged tile and keeps a load of any other tile (issued only
+// to keep the code free of branches; its values are not used) in bounds:
+// every nonempty payload spans at least 4 dwords.
 template <int F, int UPT, class Src>
 NQ_HD void stage_load(const Src &src, const KArgs &a, uint32_t t, uint32_t tid, uint32_t (&r)[Stage<F, UPT>::NK][4]) {
     using ST = Stage<F, UPT>;
     uint32_t cmax;
     const uint32_t a0 = stage_first<F, UPT>(a, t, &cmax);
+    const uint32_t lim = a.last - 3u;
 #pragma unroll
     for (uint32_t k = 0; k < ST::NK; k++) {
         const uint32_t c0 = k * WG + tid;
-        src.load_stream4(a0 + 4u * (c0 < cmax ? c0 : cmax), r[k]);
+        const uint32_t d0 = a0 + 4u * (c0 < cmax ? c0 : cmax);
+        src.load_stream4(d0 < lim ? d0 : lim, r[k]);
     }
 }
 
@@ -329,37 +335,6 @@ NQ_HD void decode_tail(const Src &src, const T &tab, const KArgs &a, uint32_t bi
     }
 }
 
-// Workgroup `bid` decodes staged tiles bid, bid + nwg, ... (then the tail).
-template <int F, int OT, int UPT, bool VEC, class T>
-__device__ __forceinline__ void process_lds(const T &tab, const KArgs &a, uint32_t bid, uint32_t nwg, uint32_t tid,
-                                            uint32_t *lds) {
-    using ST = Stage<F, UPT>;
-    const uint32_t nst = staged_tiles<F, UPT>(a);
-    const DevSrc src{a.base, a.last};
-    uint32_t t = bid;
-    if (t < nst) {
-        // The next tile's loads are issued before this tile's output stores
-        // and copied to LDS after them, so the wait for the loads does not
-        // wait for the stores (one counter covers both, in issue order).
-        uint32_t r[ST::NK][4];
-        stage_load<F, UPT>(src, a, t, tid, r);
-        uint32_t slot = 0;
-        stage_store<F, UPT>(lds, a, t, tid, r);
-        __syncthreads();
-        for (;;) {
-            const bool more = t + nwg < nst;
-            if (more) stage_load<F, UPT>(src, a, t + nwg, tid, r);
-            decode_staged<F, OT, UPT, VEC>(tab, a, t, tid, lds + slot * ST::SLOT_DW);
-            if (!more) break;
-            t += nwg;
-            slot ^= 1u;
-            stage_store<F, UPT>(lds + slot * ST::SLOT_DW, a, t, tid, r);
-            __syncthreads();
-        }
-    }
-    decode_tail<F, OT, UPT, VEC>(src, tab, a, bid, nwg, tid);
-}
-
 // Table setup, strided over `nthreads` cooperating threads.
 template <int F, class TrSrc>
 NQ_HD void fill_tables(uint64_t *t8, uint32_t *t4, float *nvq, const TrSrc &tr, uint32_t tr_mis,
@@ -390,20 +365,45 @@ NQ_HD void fill_tables(uint64_t *t8, uint32_t *t4, float *nvq, const TrSrc &tr, 
 #define NQ_OCCUPANCY
 #endif
 
+// Workgroup w decodes staged tiles w, w + grid, ... and then its share of
+// the tail.  The first tile's loads are issued before the lookup tables are
+// filled, so the two latencies overlap; one barrier publishes both.
 template <int F, int OT, int UPT, bool VEC>
 __global__ __launch_bounds__(WG) NQ_OCCUPANCY void k_decode(KArgs a) {
     using TS = TabSpec<F>;
+    using ST = Stage<F, UPT>;
     __shared__ uint64_t t8[TS::n8 > 0 ? TS::n8 : 1];
     __shared__ uint32_t t4[TS::n4 > 0 ? TS::n4 : 1];
     __shared__ float nvq[TS::nf > 0 ? TS::nf : 1];
-    const uint32_t tid = threadIdx.x;
-    if constexpr (TS::n8 + TS::n4 + TS::nf > 0) {
-        fill_tables<F>(t8, t4, nvq, DevSrc{a.tr_base, (a.tr_mis + 3u) >> 2}, a.tr_mis, tid, WG);
-        __syncthreads();
-    }
+    __shared__ __attribute__((aligned(16))) uint32_t lds[2 * ST::SLOT_DW];
+    const uint32_t tid = threadIdx.x, bid = blockIdx.x, nwg = gridDim.x;
+    const uint32_t nst = staged_tiles<F, UPT>(a);
+    const DevSrc src{a.base, a.last};
     const Tab tab{t8, t4, nvq};
-    __shared__ __attribute__((aligned(16))) uint32_t stage[2 * Stage<F, UPT>::SLOT_DW];
-    process_lds<F, OT, UPT, VEC>(tab, a, blockIdx.x, gridDim.x, tid, stage);
+    uint32_t t = bid;
+    uint32_t r[ST::NK][4];
+    stage_load<F, UPT>(src, a, t < nst ? t : 0u, tid, r);
+    if constexpr (TS::n8 + TS::n4 + TS::nf > 0)
+        fill_tables<F>(t8, t4, nvq, DevSrc{a.tr_base, (a.tr_mis + 3u) >> 2}, a.tr_mis, tid, WG);
+    if (t < nst) stage_store<F, UPT>(lds, a, t, tid, r);
+    __syncthreads();
+    if (t < nst) {
+        // The next tile's loads are issued before this tile's output stores
+        // and copied to LDS after them, so the wait for the loads does not
+        // wait for the stores (one counter covers both, in issue order).
+        uint32_t slot = 0;
+        for (;;) {
+            const bool more = t + nwg < nst;
+            if (more) stage_load<F, UPT>(src, a, t + nwg, tid, r);
+            decode_staged<F, OT, UPT, VEC>(tab, a, t, tid, lds + slot * ST::SLOT_DW);
+            if (!more) break;
+            t += nwg;
+            slot ^= 1u;
+            stage_store<F, UPT>(lds + slot * ST::SLOT_DW, a, t, tid, r);
+            __syncthreads();
+        }
+    }
+    decode_tail<F, OT, UPT, VEC>(src, tab, a, bid, nwg, tid);
 }
 
 // Host launch description for one call.
@@ -445,40 +445,64 @@ NQ_HD KArgs chunk_args(const LaunchArgs &L, uint64_t b0, uint64_t nb, uint32_t *
     return a;
 }
 
-// Units per thread per tile for format F.  Measured on MI355X at a 16 GiB
-// footprint and on the Llama-3-8B-shaped step: 8 for the formats with the
-// least payload per output (ternary, IQ, FP4: their tiles stay small in LDS)
-// and for nvfp4 (fewer workgroups build its quotient table), 4 for the rest.
-// NQ_UPT overrides every format when defined.
-template <int F>
-constexpr int upt_for() {
+// Units per thread per tile.  A launch whose units are few next to the
+// persistent grid gets smaller tiles, so more workgroups share it and each
+// one's single tile is short; large launches take 8 units per thread, which
+// amortises the per-tile barrier.  The size classes come from measurements
+// on MI355X over 0.6-180 MB tensors of seven formats (grid = 2048):
+//   units per grid workgroup  < 128 -> 1,  < 1024 -> 2,  < 2048 -> 4,  else 8.
+// Outputs that are not 16-byte aligned, and f64 outputs, always take 8.
+// NQ_UPT, when defined, fixes the tile size of every launch.
+constexpr int UPT_MAX = 8;
+NQ_HD inline int choose_upt(uint64_t nunits, uint32_t max_wgs) {
 #ifdef NQ_UPT
+    (void)nunits;
+    (void)max_wgs;
     return NQ_UPT;
 #else
-    return (F == TQ1_0 || F == TQ2_0 || F == MXFP4 || F == NVFP4_GGUF || F == NVFP4_DIV || F == IQ4_XS ||
-            is_iq(F))
-               ? 8
-               : 4;
+    const uint64_t q = nunits / (max_wgs ? max_wgs : 1u);
+    return q < 128 ? 1 : q < 1024 ? 2 : q < 2048 ? 4 : UPT_MAX;
 #endif
 }
 
-template <int F, int OT, int UPT>
+#ifdef NQ_UPT
+constexpr int UPT_FIXED = NQ_UPT;
+#else
+constexpr int UPT_FIXED = UPT_MAX;
+#endif
+
+template <int F, int OT, int UPT, bool VEC>
 int launch_chunk(const LaunchArgs &L, uint64_t b0, uint64_t nb, hipStream_t stream) {
     uint32_t grid;
     const KArgs a = chunk_args<F, OT, UPT>(L, b0, nb, &grid);
-    if (((uintptr_t)a.out & 15) == 0)
-        hipLaunchKernelGGL((k_decode<F, OT, UPT, true>), dim3(grid), dim3(WG), 0, stream, a);
-    else
-        hipLaunchKernelGGL((k_decode<F, OT, UPT, false>), dim3(grid), dim3(WG), 0, stream, a);
+    hipLaunchKernelGGL((k_decode<F, OT, UPT, VEC>), dim3(grid), dim3(WG), 0, stream, a);
     return hipGetLastError() == hipSuccess ? 0 : 9;  // NQ_ERR_HIP
 }
 
 template <int F, int OT>
 int launch(const LaunchArgs &L, hipStream_t stream) {
     constexpr uint64_t CB = chunk_blocks<F>();
+    constexpr uint64_t OSZ = OT == 0 ? 4 : OT == 3 ? 8 : 2;
     for (uint64_t b0 = 0; b0 < L.nblocks; b0 += CB) {
         const uint64_t nb = (L.nblocks - b0 < CB) ? L.nblocks - b0 : CB;
-        const int st = launch_chunk<F, OT, upt_for<F>()>(L, b0, nb, stream);
+        const uintptr_t out = (uintptr_t)L.out + b0 * (uint64_t)block_values(F) * OSZ;
+        int st;
+        if ((out & 15) != 0) {
+            st = launch_chunk<F, OT, UPT_FIXED, false>(L, b0, nb, stream);
+        } else if constexpr (OT == 3) {
+            st = launch_chunk<F, OT, UPT_FIXED, true>(L, b0, nb, stream);
+        } else {
+#ifdef NQ_UPT
+            st = launch_chunk<F, OT, UPT_FIXED, true>(L, b0, nb, stream);
+#else
+            switch (choose_upt(nb * (block_values(F) / 8), L.max_wgs)) {
+            case 1: st = launch_chunk<F, OT, 1, true>(L, b0, nb, stream); break;
+            case 2: st = launch_chunk<F, OT, 2, true>(L, b0, nb, stream); break;
+            case 4: st = launch_chunk<F, OT, 4, true>(L, b0, nb, stream); break;
+            default: st = launch_chunk<F, OT, UPT_MAX, true>(L, b0, nb, stream); break;
+            }
+#endif
+        }
         if (st != 0) return st;
     }
     return 0;

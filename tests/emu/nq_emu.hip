@@ -70,6 +70,11 @@ long run_chunk(const nq::LaunchArgs &L, uint64_t b0, uint64_t nb, const uint8_t 
     long lds_errors = 0;
     const uint32_t nst = staged_tiles<F, UPT>(a);
     for (uint32_t bid = 0; bid < grid; bid++) {
+        if (bid >= nst)  // the kernel's branch-free first load, of tile 0, whose values go unused
+            for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) {
+                uint32_t r[ST::NK][4];
+                stage_load<F, UPT>(src, a, 0u, tid, r);
+            }
         for (uint32_t t = bid; t < nst; t += grid) {
             std::fill(slot.begin(), slot.begin() + ST::SLOT_DW, 0xA5A5A5A5u);  // stale words poison the result
             std::fill(slot.begin() + ST::SLOT_DW, slot.end(), GUARD_WORD);
@@ -105,17 +110,28 @@ long run_chunk(const nq::LaunchArgs &L, uint64_t b0, uint64_t nb, const uint8_t 
     return errors;
 }
 
-// The launcher's chunk loop and per-chunk choice of units per thread.
+// The launcher's chunk loop and per-chunk choice of units per thread
+// (force_upt > 0 overrides the choice for aligned outputs).
 template <int F, int OT>
 long run(const uint8_t *payload, uint64_t nbytes, uint64_t nblocks, void *out, uint32_t max_wgs,
-         uint64_t chunk, char *err, int errlen) {
+         uint64_t chunk, int force_upt, char *err, int errlen) {
     using namespace nq;
     LaunchArgs L{payload, nbytes, nblocks, out, max_wgs};
     const uint64_t CB = chunk ? chunk : chunk_blocks<F>();
+    constexpr uint64_t OSZ = OT == 0 ? 4 : OT == 3 ? 8 : 2;
     long errors = 0;
     for (uint64_t b0 = 0; b0 < nblocks; b0 += CB) {
         const uint64_t nb = (nblocks - b0 < CB) ? nblocks - b0 : CB;
-        const long e = run_chunk<F, OT, upt_for<F>()>(L, b0, nb, payload, nbytes, err, errlen);
+        const uintptr_t o = (uintptr_t)out + b0 * (uint64_t)block_values(F) * OSZ;
+        int upt = UPT_FIXED;
+        if ((o & 15) == 0 && OT != 3) upt = force_upt > 0 ? force_upt : choose_upt(nb * (block_values(F) / 8), max_wgs);
+        long e;
+        switch (upt) {
+        case 1: e = run_chunk<F, OT, 1>(L, b0, nb, payload, nbytes, err, errlen); break;
+        case 2: e = run_chunk<F, OT, 2>(L, b0, nb, payload, nbytes, err, errlen); break;
+        case 4: e = run_chunk<F, OT, 4>(L, b0, nb, payload, nbytes, err, errlen); break;
+        default: e = run_chunk<F, OT, UPT_MAX>(L, b0, nb, payload, nbytes, err, errlen); break;
+        }
         errors += e;
     }
     return errors;
@@ -123,12 +139,23 @@ long run(const uint8_t *payload, uint64_t nbytes, uint64_t nblocks, void *out, u
 
 template <int F>
 long run_ot(int ot, const uint8_t *p, uint64_t nbytes, uint64_t nblocks, void *out, uint32_t mw, uint64_t ch,
-            char *err, int errlen) {
+            int fu, char *err, int errlen) {
     switch (ot) {
-    case 0: return run<F, 0>(p, nbytes, nblocks, out, mw, ch, err, errlen);
-    case 1: return run<F, 1>(p, nbytes, nblocks, out, mw, ch, err, errlen);
-    case 2: return run<F, 2>(p, nbytes, nblocks, out, mw, ch, err, errlen);
-    default: return run<F, 3>(p, nbytes, nblocks, out, mw, ch, err, errlen);
+    case 0: return run<F, 0>(p, nbytes, nblocks, out, mw, ch, fu, err, errlen);
+    case 1: return run<F, 1>(p, nbytes, nblocks, out, mw, ch, fu, err, errlen);
+    case 2: return run<F, 2>(p, nbytes, nblocks, out, mw, ch, fu, err, errlen);
+    default: return run<F, 3>(p, nbytes, nblocks, out, mw, ch, fu, err, errlen);
+    }
+}
+
+template <int F>
+long tile_blocks(int upt) {
+    using namespace nq;
+    switch (upt) {
+    case 1: return (long)Stage<F, 1>::BPT;
+    case 2: return (long)Stage<F, 2>::BPT;
+    case 4: return (long)Stage<F, 4>::BPT;
+    default: return (long)Stage<F, UPT_MAX>::BPT;
     }
 }
 
@@ -138,11 +165,11 @@ long run_ot(int ot, const uint8_t *p, uint64_t nbytes, uint64_t nblocks, void *o
 extern "C" __attribute__((visibility("default"))) long nq_emu_decode(int fmt, int ot, const uint8_t *payload,
                                                                     uint64_t nbytes, uint64_t nblocks, void *out,
                                                                     uint32_t max_wgs, uint64_t chunk_blocks,
-                                                                    char *err, int errlen) {
+                                                                    int force_upt, char *err, int errlen) {
     using namespace nq;
     switch (fmt) {
 #define C(X) \
-    case X: return run_ot<X>(ot, payload, nbytes, nblocks, out, max_wgs, chunk_blocks, err, errlen);
+    case X: return run_ot<X>(ot, payload, nbytes, nblocks, out, max_wgs, chunk_blocks, force_upt, err, errlen);
         C(Q4_0) C(Q4_1) C(Q5_0) C(Q5_1) C(Q8_0) C(Q8_1) C(Q2_K) C(Q3_K) C(Q4_K) C(Q5_K) C(Q6_K) C(Q8_K)
         C(IQ2_XXS) C(IQ2_XS) C(IQ3_XXS) C(IQ1_S) C(IQ4_NL) C(IQ3_S) C(IQ2_S) C(IQ4_XS) C(IQ1_M)
         C(TQ1_0) C(TQ2_0) C(MXFP4) C(NVFP4_GGUF) C(Q1_0) C(Q2_0) C(NVFP4_DIV)
@@ -151,17 +178,22 @@ extern "C" __attribute__((visibility("default"))) long nq_emu_decode(int fmt, in
     }
 }
 
-// Whole blocks per staged tile of format fmt (the launcher's choice of units
-// per thread), for tests that place tile boundaries.
-extern "C" __attribute__((visibility("default"))) long nq_emu_tile_blocks(int fmt) {
+// Whole blocks per staged tile of format fmt at `upt` units per thread, for
+// tests that place tile boundaries.
+extern "C" __attribute__((visibility("default"))) long nq_emu_tile_blocks(int fmt, int upt) {
     using namespace nq;
     switch (fmt) {
 #define C(X) \
-    case X: return (long)Stage<X, upt_for<X>()>::BPT;
+    case X: return tile_blocks<X>(upt);
         C(Q4_0) C(Q4_1) C(Q5_0) C(Q5_1) C(Q8_0) C(Q8_1) C(Q2_K) C(Q3_K) C(Q4_K) C(Q5_K) C(Q6_K) C(Q8_K)
         C(IQ2_XXS) C(IQ2_XS) C(IQ3_XXS) C(IQ1_S) C(IQ4_NL) C(IQ3_S) C(IQ2_S) C(IQ4_XS) C(IQ1_M)
         C(TQ1_0) C(TQ2_0) C(MXFP4) C(NVFP4_GGUF) C(Q1_0) C(Q2_0) C(NVFP4_DIV)
 #undef C
     default: return -1;
     }
+}
+
+// The launcher's choice of units per thread for a launch of `nunits` units.
+extern "C" __attribute__((visibility("default"))) int nq_emu_choose_upt(uint64_t nunits, uint32_t max_wgs) {
+    return nq::choose_upt(nunits, max_wgs);
 }

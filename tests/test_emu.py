@@ -72,23 +72,51 @@ def test_emulated_chunks_and_grid_stride(fmt, chunk, max_wgs):
     assert _same(got, _oracle(fmt, p, nblocks, B, "bf16"), "bf16")
 
 
+@pytest.mark.parametrize("upt", [1, 2, 4, 8])
 @pytest.mark.parametrize("fmt", FORMATS)
-def test_emulated_exact_tile_multiples(fmt):
+def test_emulated_exact_tile_multiples(fmt, upt):
     """Payloads that end exactly at a tile boundary, at every payload
     alignment: the last full tile's 16-byte staging chunks may pass the
     payload's end, so that tile must be decoded without staging."""
     info = nq.format_query(fmt)
     B = info.block_values
-    bpt = emu_lib.tile_blocks(info.id)
+    bpt = emu_lib.tile_blocks(info.id, upt)
     assert bpt > 0
     for nblocks, max_wgs in ((bpt, 1), (2 * bpt, 1), (3 * bpt, 2), (bpt + 1, 1), (2 * bpt - 1, 2)):
         p = synth.payload(fmt, nblocks, 11 + nblocks, RECIPE)
         ref = _oracle(fmt, p, nblocks, B, "bf16")
         for mis in range(4):
-            got, bad, msg, guards = emu_lib.decode(info.id, p, nblocks, B, "bf16", mis=mis, max_wgs=max_wgs)
+            got, bad, msg, guards = emu_lib.decode(info.id, p, nblocks, B, "bf16", mis=mis, max_wgs=max_wgs,
+                                                   upt=upt)
             assert bad == 0, (nblocks, mis, msg)
             assert guards
             assert _same(got, ref, "bf16"), (nblocks, mis)
+
+
+@pytest.mark.parametrize("upt", [1, 2, 4, 8])
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_emulated_tile_sizes_grid_stride(fmt, upt):
+    """Every tile size the launcher can pick, over several tiles per
+    workgroup plus a partial tile, to f32 and bf16."""
+    info = nq.format_query(fmt)
+    B = info.block_values
+    nblocks = 5 * emu_lib.tile_blocks(info.id, upt) + 3
+    p = synth.payload(fmt, nblocks, 21 + upt, RECIPE)
+    for dtype in ("f32", "bf16"):
+        got, bad, msg, guards = emu_lib.decode(info.id, p, nblocks, B, dtype, mis=1, max_wgs=2, upt=upt)
+        assert bad == 0, msg
+        assert guards
+        assert _same(got, _oracle(fmt, p, nblocks, B, dtype), dtype)
+
+
+def test_tile_size_classes():
+    """The launcher's size classes: units per grid workgroup below 128, 1024
+    and 2048 take 1, 2 and 4 units per thread, larger launches 8."""
+    g = 2048
+    for q, want in ((0, 1), (1, 1), (127, 1), (128, 2), (1023, 2), (1024, 4), (2047, 4), (2048, 8), (1 << 20, 8)):
+        assert emu_lib.choose_upt(q * g, g) == want, q
+        assert emu_lib.choose_upt(q * g + g - 1, g) == want, q
+    assert emu_lib.choose_upt(100, 0) == 1
 
 
 @pytest.mark.parametrize("d_w", [1.0, 3.0, 448.0, 1e-30, 3e38])
