@@ -65,7 +65,9 @@ void fill_info(int id, nq_format_info *out) {
 constexpr int MAX_DEVICES = 64;
 std::atomic<int> g_cu_count[MAX_DEVICES];
 
-uint32_t max_workgroups() {
+// Workgroups the current device holds at once (the scale of the tile-size
+// choice).
+uint32_t resident_workgroups() {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return 2048;
     int cu = g_cu_count[dev].load(std::memory_order_relaxed);
@@ -74,7 +76,7 @@ uint32_t max_workgroups() {
             cu = 256;
         g_cu_count[dev].store(cu, std::memory_order_relaxed);
     }
-    return (uint32_t)cu * NQ_WG_PER_CU;  // persistent grid: workgroups per CU
+    return (uint32_t)cu * NQ_RESIDENT_PER_CU;
 }
 
 }  // namespace
@@ -144,7 +146,7 @@ NQ_API int nq_dequantize_packed(int32_t format, const void *payload, uint64_t nb
     L.nbytes = nbytes;
     L.nblocks = elems / (uint64_t)B_OF(format);
     L.out = out;
-    L.max_wgs = max_workgroups();
+    L.resident = resident_workgroups();
     switch (REGISTRY[format].family) {
     case NQ_FAMILY_SIMPLE: return nq::launch_simple(format, out_dtype, L, stream);
     case NQ_FAMILY_KQUANT: return nq::launch_kquant(format, out_dtype, L, stream);

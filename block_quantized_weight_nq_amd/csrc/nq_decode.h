@@ -125,18 +125,18 @@ constexpr uint32_t FP4T2 = pack4(0, -1, -2, -3), FP4T3 = pack4(-4, -6, -8, -12);
 // ---------------------------------------------------------------------------
 // Payload windows.  `off` is a byte offset from the source's 4-byte-aligned
 // base (32-bit: a launch covers less than 4 GiB of payload).  A window of ND
-// dwords reads dwords a..a+ND-1 plus one more for the byte shift; that extra
-// index is clamped to the source's last dword, so no access leaves the dwords
-// that hold payload bytes (when the clamp bites, the shift is 0 and the extra
-// dword is not used).
+// dwords reads dwords a..a+ND-1 plus one more for the byte shift, through the
+// source's dwx(): a global-memory source clamps that index to its last dword,
+// so no access leaves the dwords that hold payload bytes, and an LDS source
+// reads its padding.  Where that dword lies past the payload the shift is 0
+// and the extra dword is not used.
 template <int ND, class Src>
 NQ_HD void window(const Src &src, uint32_t off, uint32_t (&w)[ND]) {
     const uint32_t a = off >> 2;
     const uint32_t sh = off & 3u;
     uint32_t r[ND];
     src.template load<ND>(a, r);
-    const uint32_t xa = a + ND;
-    const uint32_t extra = src.dw(xa < src.last ? xa : src.last);
+    const uint32_t extra = src.dwx(a + ND);
 #pragma unroll
     for (int k = 0; k < ND; k++) w[k] = alignbyte(k + 1 < ND ? r[k + 1] : extra, r[k], sh);
 }
@@ -146,7 +146,7 @@ NQ_HD uint32_t u16_at(const Src &src, uint32_t off) {
     const uint32_t a = off >> 2;
     const uint32_t sh = off & 3u;
     const uint32_t r0 = src.dw(a);
-    const uint32_t r1 = src.dw(a + 1 < src.last ? a + 1 : src.last);
+    const uint32_t r1 = src.dwx(a + 1);
     return alignbyte(r1, r0, sh) & 0xFFFFu;
 }
 
@@ -155,15 +155,25 @@ NQ_HD uint32_t u8_at(const Src &src, uint32_t off) {
     return (src.dw(off >> 2) >> (8u * (off & 3u))) & 0xFFu;
 }
 
+// A value the compiler may not look through: code words built by a shift and
+// a byte mask are then converted byte by byte (v_cvt_f32_ubyte0..3) instead of
+// one bit-field extract per code.
+NQ_HD uint32_t opaque(uint32_t x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm("" : "+v"(x));
+#endif
+    return x;
+}
+
 // 8 nibbles (plane `hi` of the 8 bytes in w[0], w[1]) as two words of 4 codes.
 NQ_HD void nibbles(const uint32_t (&w)[2], uint32_t hi, uint32_t (&c)[2]) {
-    c[0] = (w[0] >> (4u * hi)) & 0x0F0F0F0Fu;
-    c[1] = (w[1] >> (4u * hi)) & 0x0F0F0F0Fu;
+    c[0] = opaque((w[0] >> (4u * hi)) & 0x0F0F0F0Fu);
+    c[1] = opaque((w[1] >> (4u * hi)) & 0x0F0F0F0Fu);
 }
 // 2-bit fields of plane p of the 8 bytes in w[0], w[1], one per byte.
 NQ_HD void crumbs(const uint32_t (&w)[2], uint32_t p, uint32_t (&c)[2]) {
-    c[0] = (w[0] >> (2u * p)) & 0x03030303u;
-    c[1] = (w[1] >> (2u * p)) & 0x03030303u;
+    c[0] = opaque((w[0] >> (2u * p)) & 0x03030303u);
+    c[1] = opaque((w[1] >> (2u * p)) & 0x03030303u);
 }
 NQ_HD uint32_t code_at(const uint32_t (&c)[2], int k) { return bytek(c[k >> 2], (uint32_t)(k & 3)); }
 

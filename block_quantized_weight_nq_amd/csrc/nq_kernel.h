@@ -1,17 +1,15 @@
 // nq_kernel.h -- the decode kernel template and its launcher.
 //
-// One persistent kernel per (format, output type, vector store).  The output
+// One kernel per (format, output type, tile size, vector store).  The output
 // is cut into tiles of 256*UPT units (a unit is 8 consecutive outputs of one
-// block); workgroup w takes tiles w, w + grid, ...  For each tile the
-// workgroup copies the tile's payload bytes into one of two LDS slots with
-// coalesced 16-byte loads, keeps the next tile's loads in flight while it
-// decodes the current one from LDS, and writes its units so that a wave's 64
-// lanes cover 64 consecutive units: one contiguous 1 KiB (bf16/f16) or 2 KiB
-// (f32) run per store instruction.  A partial last tile is decoded straight
-// from global memory.  IQ formats copy their codebook to LDS once per
-// workgroup; "nvfp4" fills a 1024-entry table of its correctly rounded
-// quotients (128 scale magnitudes x 8 code magnitudes; signs are applied as
-// bit flips).
+// block), and each tile is one workgroup: it copies the tile's payload bytes
+// into LDS with coalesced 16-byte loads, then decodes its units so that a
+// wave's 64 lanes cover 64 consecutive units: one contiguous 1 KiB
+// (bf16/f16) or 2 KiB (f32) run per store instruction.  A tile whose staging
+// would pass the payload's end is decoded straight from global memory.  IQ
+// formats copy their codebook to LDS in every workgroup; "nvfp4" fills a
+// 1024-entry table of its correctly rounded quotients (128 scale magnitudes x
+// 8 code magnitudes; signs are applied as bit flips).
 #pragma once
 
 #include "iq_grids.h"
@@ -21,13 +19,14 @@
 //   NQ_NTL        1: staging loads are non-temporal (each payload byte is read once)
 //   NQ_UPT        units (8 outputs) per thread per tile for every launch
 //                 (default: chosen per launch from its size, see choose_upt)
-//   NQ_WG_PER_CU  persistent-grid workgroups per compute unit
+//   NQ_RESIDENT_PER_CU  workgroups a compute unit holds at once, the scale of
+//                 the per-launch tile-size choice
 //   NQ_NT_STORE   non-temporal output stores: 0 never, 1 always, 2 16-bit outputs only
 #ifndef NQ_NTL
 #define NQ_NTL 1
 #endif
-#ifndef NQ_WG_PER_CU
-#define NQ_WG_PER_CU 8
+#ifndef NQ_RESIDENT_PER_CU
+#define NQ_RESIDENT_PER_CU 8
 #endif
 
 namespace nq {
@@ -68,6 +67,8 @@ struct DevSrc {
         }
     }
     NQ_HD uint32_t dw(uint32_t i) const { return base[i]; }
+    // the extra dword of a window, clamped to the last payload dword
+    NQ_HD uint32_t dwx(uint32_t i) const { return base[i < last ? i : last]; }
     // 16 bytes that are read once (non-temporal when NQ_NTL).
     NQ_HD void load_stream4(uint32_t i, uint32_t (&r)[4]) const {
 #if NQ_NTL && defined(__HIP_DEVICE_COMPILE__)
@@ -220,6 +221,14 @@ struct LdsSrc {
         for (int k = 0; k < N; k++) r[k] = base[i + (uint32_t)k];
     }
     NQ_HD uint32_t dw(uint32_t i) const { return base[i]; }
+    // the extra dword of a window: at most one past `last`, inside the slot's
+    // padding, and unused there (no clamp needed)
+    NQ_HD uint32_t dwx(uint32_t i) const {
+#if !defined(__HIP_DEVICE_COMPILE__)
+        if (i > last + 1) __builtin_trap();
+#endif
+        return base[i];
+    }
 };
 
 template <int F, int UPT>
@@ -231,7 +240,7 @@ struct Stage {
     static constexpr uint32_t NDW = (TB + 3) / 4 + 1;           // dwords spanned, any start offset
     static constexpr uint32_t NCH = (NDW + 3) / 4;              // 16-byte chunks
     static constexpr uint32_t NK = (NCH + WG - 1) / WG;         // chunks per thread
-    static constexpr uint32_t SLOT_DW = NCH * 4;                // LDS dwords per slot (chunks written)
+    static constexpr uint32_t SLOT_DW = NCH * 4 + 4;            // LDS dwords per slot: chunks + padding
 };
 
 // Chunk c of tile t covers payload dwords a0 + 4c .. a0 + 4c + 3, where a0 is
@@ -260,22 +269,17 @@ NQ_HD uint32_t staged_tiles(const KArgs &a) {
     return a0 + 4u * cmax + 3u <= a.last ? full : full - 1;
 }
 
-// Global loads of tile t's chunks for this thread (into registers).  The
-// dword index is also clamped to end at the last payload dword, which changes
-// nothing for a staged tile and keeps a load of any other tile (issued only
-// to keep the code free of branches; its values are not used) in bounds:
-// every nonempty payload spans at least 4 dwords.
+// Global loads of tile t's chunks for this thread (into registers); t is a
+// staged tile, so every chunk lies inside the payload.
 template <int F, int UPT, class Src>
 NQ_HD void stage_load(const Src &src, const KArgs &a, uint32_t t, uint32_t tid, uint32_t (&r)[Stage<F, UPT>::NK][4]) {
     using ST = Stage<F, UPT>;
     uint32_t cmax;
     const uint32_t a0 = stage_first<F, UPT>(a, t, &cmax);
-    const uint32_t lim = a.last - 3u;
 #pragma unroll
     for (uint32_t k = 0; k < ST::NK; k++) {
         const uint32_t c0 = k * WG + tid;
-        const uint32_t d0 = a0 + 4u * (c0 < cmax ? c0 : cmax);
-        src.load_stream4(d0 < lim ? d0 : lim, r[k]);
+        src.load_stream4(a0 + 4u * (c0 < cmax ? c0 : cmax), r[k]);
     }
 }
 
@@ -294,43 +298,41 @@ NQ_HD void stage_store(uint32_t *slot, const KArgs &a, uint32_t t, uint32_t tid,
     }
 }
 
-// Decode this thread's units of tile t from its staged copy in `buf`.
+// Decode this thread's units of tile t from its staged copy in `buf`.  A
+// block's units are consecutive and a tile row of 256 units holds whole
+// blocks, so unit k*256 + tid of a tile lies in the tile's block
+// k*(256/UPB) + tid/UPB, at unit tid % UPB of that block.
 template <int F, int OT, int UPT, bool VEC, class T>
 NQ_HD void decode_staged(const T &tab, const KArgs &a, uint32_t t, uint32_t tid, const uint32_t *buf) {
     using ST = Stage<F, UPT>;
     constexpr uint32_t UPB = ST::UPB;
     constexpr uint32_t S = block_bytes(F);
+    static_assert(WG % UPB == 0, "a tile row holds whole blocks");
     const uint32_t p = a.mis + t * ST::TB;
     const uint32_t a0 = p >> 2;
     const LdsSrc src{buf, ((p + ST::TB - 1) >> 2) - a0};
+    const uint32_t s = tid % UPB;
+    const uint32_t bo0 = (p & 3u) + (tid / UPB) * S;
     float y[UPT][8];
 #pragma unroll
-    for (int k = 0; k < UPT; k++) {
-        const uint32_t u = t * ST::PER + (uint32_t)(k * WG) + tid;
-        const uint32_t bo = (p & 3u) + (u / UPB - t * ST::BPT) * S;
-        decode_unit<F>(src, bo, u % UPB, tab, y[k]);
-    }
+    for (int k = 0; k < UPT; k++) decode_unit<F>(src, bo0 + (uint32_t)k * (WG / UPB) * S, s, tab, y[k]);
 #pragma unroll
     for (int k = 0; k < UPT; k++) store8<OT, VEC>(a.out, t * ST::PER + (uint32_t)(k * WG) + tid, y[k]);
 }
 
-// The tiles after the staged ones (a partial last tile, and the last full
-// tile when its chunks would pass the payload's end), straight from global
-// memory; tile tt falls to the workgroup bid == tt % nwg.
+// A tile that is not staged (a partial last tile, or the last full tile when
+// its chunks would pass the payload's end), decoded straight from global
+// memory.
 template <int F, int OT, int UPT, bool VEC, class Src, class T>
-NQ_HD void decode_tail(const Src &src, const T &tab, const KArgs &a, uint32_t bid, uint32_t nwg, uint32_t tid) {
+NQ_HD void decode_direct(const Src &src, const T &tab, const KArgs &a, uint32_t t, uint32_t tid) {
     using ST = Stage<F, UPT>;
-    const uint32_t ntiles = (a.nunits + ST::PER - 1) / ST::PER;
-    for (uint32_t tt = staged_tiles<F, UPT>(a); tt < ntiles; tt++) {
-        if (tt % nwg != bid) continue;
 #pragma unroll
-        for (int k = 0; k < UPT; k++) {
-            const uint32_t u = tt * ST::PER + (uint32_t)(k * WG) + tid;
-            if (u < a.nunits) {
-                float y[8];
-                decode_unit<F>(src, a.mis + (u / ST::UPB) * block_bytes(F), u % ST::UPB, tab, y);
-                store8<OT, VEC>(a.out, u, y);
-            }
+    for (int k = 0; k < UPT; k++) {
+        const uint32_t u = t * ST::PER + (uint32_t)(k * WG) + tid;
+        if (u < a.nunits) {
+            float y[8];
+            decode_unit<F>(src, a.mis + (u / ST::UPB) * block_bytes(F), u % ST::UPB, tab, y);
+            store8<OT, VEC>(a.out, u, y);
         }
     }
 }
@@ -356,54 +358,37 @@ NQ_HD void fill_tables(uint64_t *t8, uint32_t *t4, float *nvq, const TrSrc &tr, 
     }
 }
 
-#ifndef NQ_WAVES_PER_EU
-#define NQ_WAVES_PER_EU 0  // >0: ask the compiler for this many waves per SIMD (caps VGPRs)
-#endif
-#if NQ_WAVES_PER_EU > 0
-#define NQ_OCCUPANCY __attribute__((amdgpu_waves_per_eu(NQ_WAVES_PER_EU)))
-#else
-#define NQ_OCCUPANCY
-#endif
-
-// Workgroup w decodes staged tiles w, w + grid, ... and then its share of
-// the tail.  The first tile's loads are issued before the lookup tables are
-// filled, so the two latencies overlap; one barrier publishes both.
+// One workgroup per tile: workgroup t stages tile t in LDS and decodes it
+// (or decodes it from global memory when it is not staged); the hardware
+// keeps as many workgroups in flight as LDS and registers allow.  The tile's
+// loads are issued before the lookup tables are filled, so the two
+// latencies overlap, and one barrier publishes both.
 template <int F, int OT, int UPT, bool VEC>
-__global__ __launch_bounds__(WG) NQ_OCCUPANCY void k_decode(KArgs a) {
+__global__ __launch_bounds__(WG) void k_decode(KArgs a) {
     using TS = TabSpec<F>;
     using ST = Stage<F, UPT>;
     __shared__ uint64_t t8[TS::n8 > 0 ? TS::n8 : 1];
     __shared__ uint32_t t4[TS::n4 > 0 ? TS::n4 : 1];
     __shared__ float nvq[TS::nf > 0 ? TS::nf : 1];
-    __shared__ __attribute__((aligned(16))) uint32_t lds[2 * ST::SLOT_DW];
-    const uint32_t tid = threadIdx.x, bid = blockIdx.x, nwg = gridDim.x;
-    const uint32_t nst = staged_tiles<F, UPT>(a);
+    __shared__ __attribute__((aligned(16))) uint32_t lds[ST::SLOT_DW];
+    const uint32_t tid = threadIdx.x, t = blockIdx.x;
     const DevSrc src{a.base, a.last};
     const Tab tab{t8, t4, nvq};
-    uint32_t t = bid;
-    uint32_t r[ST::NK][4];
-    stage_load<F, UPT>(src, a, t < nst ? t : 0u, tid, r);
-    if constexpr (TS::n8 + TS::n4 + TS::nf > 0)
-        fill_tables<F>(t8, t4, nvq, DevSrc{a.tr_base, (a.tr_mis + 3u) >> 2}, a.tr_mis, tid, WG);
-    if (t < nst) stage_store<F, UPT>(lds, a, t, tid, r);
-    __syncthreads();
-    if (t < nst) {
-        // The next tile's loads are issued before this tile's output stores
-        // and copied to LDS after them, so the wait for the loads does not
-        // wait for the stores (one counter covers both, in issue order).
-        uint32_t slot = 0;
-        for (;;) {
-            const bool more = t + nwg < nst;
-            if (more) stage_load<F, UPT>(src, a, t + nwg, tid, r);
-            decode_staged<F, OT, UPT, VEC>(tab, a, t, tid, lds + slot * ST::SLOT_DW);
-            if (!more) break;
-            t += nwg;
-            slot ^= 1u;
-            stage_store<F, UPT>(lds + slot * ST::SLOT_DW, a, t, tid, r);
+    if (t < staged_tiles<F, UPT>(a)) {
+        uint32_t r[ST::NK][4];
+        stage_load<F, UPT>(src, a, t, tid, r);
+        if constexpr (TS::n8 + TS::n4 + TS::nf > 0)
+            fill_tables<F>(t8, t4, nvq, DevSrc{a.tr_base, (a.tr_mis + 3u) >> 2}, a.tr_mis, tid, WG);
+        stage_store<F, UPT>(lds, a, t, tid, r);
+        __syncthreads();
+        decode_staged<F, OT, UPT, VEC>(tab, a, t, tid, lds);
+    } else {
+        if constexpr (TS::n8 + TS::n4 + TS::nf > 0) {
+            fill_tables<F>(t8, t4, nvq, DevSrc{a.tr_base, (a.tr_mis + 3u) >> 2}, a.tr_mis, tid, WG);
             __syncthreads();
         }
+        decode_direct<F, OT, UPT, VEC>(src, tab, a, t, tid);
     }
-    decode_tail<F, OT, UPT, VEC>(src, tab, a, bid, nwg, tid);
 }
 
 // Host launch description for one call.
@@ -412,7 +397,7 @@ struct LaunchArgs {
     uint64_t nbytes;
     uint64_t nblocks;
     void *out;               // device
-    uint32_t max_wgs;        // persistent-grid cap for the device
+    uint32_t resident;       // workgroups the device holds at once (the tile-size scale)
 };
 
 
@@ -440,35 +425,46 @@ NQ_HD KArgs chunk_args(const LaunchArgs &L, uint64_t b0, uint64_t nb, uint32_t *
     a.nunits = (uint32_t)(nb * (block_values(F) / 8));
     a.out = (uint8_t *)L.out + b0 * (uint64_t)block_values(F) * OSZ;
     const uint64_t per_wg = (uint64_t)WG * UPT;
-    uint64_t g = (a.nunits + per_wg - 1) / per_wg;
-    *grid = (uint32_t)(g > L.max_wgs ? L.max_wgs : g);
+    *grid = (uint32_t)((a.nunits + per_wg - 1) / per_wg);  // one workgroup per tile
     return a;
 }
 
-// Units per thread per tile.  A launch whose units are few next to the
-// persistent grid gets smaller tiles, so more workgroups share it and each
-// one's single tile is short; large launches take 8 units per thread, which
-// amortises the per-tile barrier.  The size classes come from measurements
-// on MI355X over 0.6-180 MB tensors of seven formats (grid = 2048):
-//   units per grid workgroup  < 128 -> 1,  < 1024 -> 2,  < 2048 -> 4,  else 8.
+// Units per thread per tile, from the launch's units per resident workgroup
+// q (the device holds `resident` workgroups at once; 2048 on MI355X).  Few
+// units per resident workgroup call for small tiles, so that every compute
+// unit gets work; large launches take larger tiles, which spend less on
+// per-workgroup setup.  Formats whose codebook fills 8 KiB or more of LDS
+// (IQ2_S, IQ1_S, IQ1_M) copy it once per workgroup and so take larger tiles
+// sooner.  The classes come from measurements on MI355X over 0.6-180 MB
+// tensors of nine formats:
+//   q < 128 -> 1,  < 1024 -> 2,  < 2048 -> 4,  else 8;
+//   large codebooks: q < 128 -> 1, < 256 -> 2, < 512 -> 4, < 1024 -> 8, else 16.
 // Outputs that are not 16-byte aligned, and f64 outputs, always take 8.
 // NQ_UPT, when defined, fixes the tile size of every launch.
-constexpr int UPT_MAX = 8;
-NQ_HD inline int choose_upt(uint64_t nunits, uint32_t max_wgs) {
+template <int F>
+constexpr bool big_codebook() {
+    return TabSpec<F>::n8 >= 1024;
+}
+
+template <int F>
+NQ_HD int choose_upt(uint64_t nunits, uint32_t resident) {
 #ifdef NQ_UPT
     (void)nunits;
-    (void)max_wgs;
+    (void)resident;
     return NQ_UPT;
 #else
-    const uint64_t q = nunits / (max_wgs ? max_wgs : 1u);
-    return q < 128 ? 1 : q < 1024 ? 2 : q < 2048 ? 4 : UPT_MAX;
+    const uint64_t q = nunits / (resident ? resident : 1u);
+    if constexpr (big_codebook<F>())
+        return q < 128 ? 1 : q < 256 ? 2 : q < 512 ? 4 : q < 1024 ? 8 : 16;
+    else
+        return q < 128 ? 1 : q < 1024 ? 2 : q < 2048 ? 4 : 8;
 #endif
 }
 
 #ifdef NQ_UPT
 constexpr int UPT_FIXED = NQ_UPT;
 #else
-constexpr int UPT_FIXED = UPT_MAX;
+constexpr int UPT_FIXED = 8;
 #endif
 
 template <int F, int OT, int UPT, bool VEC>
@@ -495,11 +491,17 @@ int launch(const LaunchArgs &L, hipStream_t stream) {
 #ifdef NQ_UPT
             st = launch_chunk<F, OT, UPT_FIXED, true>(L, b0, nb, stream);
 #else
-            switch (choose_upt(nb * (block_values(F) / 8), L.max_wgs)) {
+            switch (choose_upt<F>(nb * (block_values(F) / 8), L.resident)) {
             case 1: st = launch_chunk<F, OT, 1, true>(L, b0, nb, stream); break;
             case 2: st = launch_chunk<F, OT, 2, true>(L, b0, nb, stream); break;
             case 4: st = launch_chunk<F, OT, 4, true>(L, b0, nb, stream); break;
-            default: st = launch_chunk<F, OT, UPT_MAX, true>(L, b0, nb, stream); break;
+            case 8: st = launch_chunk<F, OT, 8, true>(L, b0, nb, stream); break;
+            default:
+                if constexpr (big_codebook<F>())
+                    st = launch_chunk<F, OT, 16, true>(L, b0, nb, stream);
+                else
+                    st = 9;  // unreachable: other formats top out at 8
+                break;
             }
 #endif
         }

@@ -29,6 +29,7 @@ struct HostSrc {
         for (int k = 0; k < N; k++) r[k] = dw(i + (uint32_t)k);
     }
     void load_stream4(uint32_t i, uint32_t (&r)[4]) const { load<4>(i, r); }
+    uint32_t dwx(uint32_t i) const { return dw(i < last ? i : last); }
     uint32_t dw(uint32_t i) const {
         const uintptr_t a = (uintptr_t)(base + i);
         if (i > last || a + 4 <= chk->lo || a >= chk->hi) {
@@ -40,9 +41,10 @@ struct HostSrc {
     }
 };
 
-// One launch chunk with UPT units per thread, as the kernel runs it: every
-// thread stages a tile, then every thread decodes it (the barrier), then
-// the tail tile.
+// One launch chunk with UPT units per thread, as the kernel runs it: one
+// workgroup per tile; a staged tile is copied into the LDS slot by every
+// thread, then decoded by every thread (the barrier); other tiles are
+// decoded from the payload directly.
 template <int F, int OT, int UPT>
 long run_chunk(const nq::LaunchArgs &L, uint64_t b0, uint64_t nb, const uint8_t *payload, uint64_t nbytes,
                char *err, int errlen) {
@@ -69,13 +71,12 @@ long run_chunk(const nq::LaunchArgs &L, uint64_t b0, uint64_t nb, const uint8_t 
     std::vector<uint32_t> slot(ST::SLOT_DW + GUARD);
     long lds_errors = 0;
     const uint32_t nst = staged_tiles<F, UPT>(a);
-    for (uint32_t bid = 0; bid < grid; bid++) {
-        if (bid >= nst)  // the kernel's branch-free first load, of tile 0, whose values go unused
-            for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) {
-                uint32_t r[ST::NK][4];
-                stage_load<F, UPT>(src, a, 0u, tid, r);
-            }
-        for (uint32_t t = bid; t < nst; t += grid) {
+    if (grid != (a.nunits + ST::PER - 1) / ST::PER) {
+        snprintf(err, errlen, "grid %u is not one workgroup per tile", grid);
+        return 1;
+    }
+    for (uint32_t t = 0; t < grid; t++) {
+        if (t < nst) {
             std::fill(slot.begin(), slot.begin() + ST::SLOT_DW, 0xA5A5A5A5u);  // stale words poison the result
             std::fill(slot.begin() + ST::SLOT_DW, slot.end(), GUARD_WORD);
             for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) {
@@ -92,12 +93,13 @@ long run_chunk(const nq::LaunchArgs &L, uint64_t b0, uint64_t nb, const uint8_t 
                 else
                     decode_staged<F, OT, UPT, false>(tab, a, t, tid, slot.data());
             }
-        }
-        for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) {
-            if (vec)
-                decode_tail<F, OT, UPT, true>(src, tab, a, bid, grid, tid);
-            else
-                decode_tail<F, OT, UPT, false>(src, tab, a, bid, grid, tid);
+        } else {
+            for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) {
+                if (vec)
+                    decode_direct<F, OT, UPT, true>(src, tab, a, t, tid);
+                else
+                    decode_direct<F, OT, UPT, false>(src, tab, a, t, tid);
+            }
         }
     }
     long errors = 0;
@@ -123,14 +125,17 @@ long run(const uint8_t *payload, uint64_t nbytes, uint64_t nblocks, void *out, u
     for (uint64_t b0 = 0; b0 < nblocks; b0 += CB) {
         const uint64_t nb = (nblocks - b0 < CB) ? nblocks - b0 : CB;
         const uintptr_t o = (uintptr_t)out + b0 * (uint64_t)block_values(F) * OSZ;
-        int upt = UPT_FIXED;
-        if ((o & 15) == 0 && OT != 3) upt = force_upt > 0 ? force_upt : choose_upt(nb * (block_values(F) / 8), max_wgs);
+        int upt = UPT_FIXED;  // misaligned and f64 outputs
+        if ((o & 15) == 0 && OT != 3)
+            upt = force_upt > 0 ? force_upt : choose_upt<F>(nb * (block_values(F) / 8), max_wgs);
         long e;
         switch (upt) {
         case 1: e = run_chunk<F, OT, 1>(L, b0, nb, payload, nbytes, err, errlen); break;
         case 2: e = run_chunk<F, OT, 2>(L, b0, nb, payload, nbytes, err, errlen); break;
         case 4: e = run_chunk<F, OT, 4>(L, b0, nb, payload, nbytes, err, errlen); break;
-        default: e = run_chunk<F, OT, UPT_MAX>(L, b0, nb, payload, nbytes, err, errlen); break;
+        case 8: e = run_chunk<F, OT, 8>(L, b0, nb, payload, nbytes, err, errlen); break;
+        case 16: e = run_chunk<F, OT, 16>(L, b0, nb, payload, nbytes, err, errlen); break;
+        default: snprintf(err, errlen, "no tile size %d", upt); return 1;
         }
         errors += e;
     }
@@ -155,7 +160,9 @@ long tile_blocks(int upt) {
     case 1: return (long)Stage<F, 1>::BPT;
     case 2: return (long)Stage<F, 2>::BPT;
     case 4: return (long)Stage<F, 4>::BPT;
-    default: return (long)Stage<F, UPT_MAX>::BPT;
+    case 8: return (long)Stage<F, 8>::BPT;
+    case 16: return (long)Stage<F, 16>::BPT;
+    default: return -1;
     }
 }
 
@@ -193,7 +200,17 @@ extern "C" __attribute__((visibility("default"))) long nq_emu_tile_blocks(int fm
     }
 }
 
-// The launcher's choice of units per thread for a launch of `nunits` units.
-extern "C" __attribute__((visibility("default"))) int nq_emu_choose_upt(uint64_t nunits, uint32_t max_wgs) {
-    return nq::choose_upt(nunits, max_wgs);
+// The launcher's choice of units per thread for a launch of `nunits` units
+// of format fmt.
+extern "C" __attribute__((visibility("default"))) int nq_emu_choose_upt(int fmt, uint64_t nunits, uint32_t resident) {
+    using namespace nq;
+    switch (fmt) {
+#define C(X) \
+    case X: return choose_upt<X>(nunits, resident);
+        C(Q4_0) C(Q4_1) C(Q5_0) C(Q5_1) C(Q8_0) C(Q8_1) C(Q2_K) C(Q3_K) C(Q4_K) C(Q5_K) C(Q6_K) C(Q8_K)
+        C(IQ2_XXS) C(IQ2_XS) C(IQ3_XXS) C(IQ1_S) C(IQ4_NL) C(IQ3_S) C(IQ2_S) C(IQ4_XS) C(IQ1_M)
+        C(TQ1_0) C(TQ2_0) C(MXFP4) C(NVFP4_GGUF) C(Q1_0) C(Q2_0) C(NVFP4_DIV)
+#undef C
+    default: return -1;
+    }
 }

@@ -39,7 +39,7 @@ def lib():
                                     ctypes.c_int, ctypes.c_char_p, ctypes.c_int]
         L.nq_emu_decode.restype = ctypes.c_long
         L.nq_emu_tile_blocks.argtypes = [ctypes.c_int, ctypes.c_int]
-        L.nq_emu_choose_upt.argtypes = [ctypes.c_uint64, ctypes.c_uint32]
+        L.nq_emu_choose_upt.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint32]
         L.nq_emu_choose_upt.restype = ctypes.c_int
         L.nq_emu_tile_blocks.restype = ctypes.c_long
         _lib = L
@@ -78,6 +78,6 @@ def tile_blocks(fmt_id, upt):
     return lib().nq_emu_tile_blocks(fmt_id, upt)
 
 
-def choose_upt(nunits, max_wgs):
-    """The launcher's units per thread for a launch of `nunits` units."""
-    return lib().nq_emu_choose_upt(nunits, max_wgs)
+def choose_upt(fmt_id, nunits, resident):
+    """The launcher's units per thread for a launch of `nunits` units of a format."""
+    return lib().nq_emu_choose_upt(fmt_id, nunits, resident)

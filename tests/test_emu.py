@@ -58,9 +58,9 @@ def test_emulated_misaligned_payload_and_output(fmt, mis, out_mis):
 
 @pytest.mark.parametrize("fmt", ["gguf:q4_k", "gguf:q8_0", "gguf:mxfp4", "nvfp4", "gguf:iq2_s", "gguf:tq1_0"])
 @pytest.mark.parametrize("chunk,max_wgs", [(5, 1), (3, 2), (64, 3), (700, 3), (2900, 2), (700, 16), (2900, 8)])
-def test_emulated_chunks_and_grid_stride(fmt, chunk, max_wgs):
-    """Several launch chunks, each with several full staged tiles and a tail,
-    walked by small grids (the grid-stride loop turns many times)."""
+def test_emulated_chunks(fmt, chunk, max_wgs):
+    """Several launch chunks, each with several staged tiles and a partial
+    one; small resident-workgroup counts make the launcher pick large tiles."""
     info = nq.format_query(fmt)
     B = info.block_values
     nblocks = 300 if chunk < 100 else 5000
@@ -72,7 +72,7 @@ def test_emulated_chunks_and_grid_stride(fmt, chunk, max_wgs):
     assert _same(got, _oracle(fmt, p, nblocks, B, "bf16"), "bf16")
 
 
-@pytest.mark.parametrize("upt", [1, 2, 4, 8])
+@pytest.mark.parametrize("upt", [1, 2, 4, 8, 16])
 @pytest.mark.parametrize("fmt", FORMATS)
 def test_emulated_exact_tile_multiples(fmt, upt):
     """Payloads that end exactly at a tile boundary, at every payload
@@ -93,11 +93,11 @@ def test_emulated_exact_tile_multiples(fmt, upt):
             assert _same(got, ref, "bf16"), (nblocks, mis)
 
 
-@pytest.mark.parametrize("upt", [1, 2, 4, 8])
+@pytest.mark.parametrize("upt", [1, 2, 4, 8, 16])
 @pytest.mark.parametrize("fmt", FORMATS)
-def test_emulated_tile_sizes_grid_stride(fmt, upt):
-    """Every tile size the launcher can pick, over several tiles per
-    workgroup plus a partial tile, to f32 and bf16."""
+def test_emulated_tile_sizes(fmt, upt):
+    """Every tile size, over several tiles plus a partial one, to f32 and
+    bf16."""
     info = nq.format_query(fmt)
     B = info.block_values
     nblocks = 5 * emu_lib.tile_blocks(info.id, upt) + 3
@@ -110,13 +110,20 @@ def test_emulated_tile_sizes_grid_stride(fmt, upt):
 
 
 def test_tile_size_classes():
-    """The launcher's size classes: units per grid workgroup below 128, 1024
-    and 2048 take 1, 2 and 4 units per thread, larger launches 8."""
+    """The launcher's size classes by units per resident workgroup q: below
+    128, 1024 and 2048 take 1, 2 and 4 units per thread, larger launches 8;
+    formats with codebooks of 8 KiB or more step up at 128, 256, 512 and 1024
+    to 2, 4, 8 and 16."""
     g = 2048
-    for q, want in ((0, 1), (1, 1), (127, 1), (128, 2), (1023, 2), (1024, 4), (2047, 4), (2048, 8), (1 << 20, 8)):
-        assert emu_lib.choose_upt(q * g, g) == want, q
-        assert emu_lib.choose_upt(q * g + g - 1, g) == want, q
-    assert emu_lib.choose_upt(100, 0) == 1
+    plain = [(0, 1), (1, 1), (127, 1), (128, 2), (1023, 2), (1024, 4), (2047, 4), (2048, 8), (1 << 20, 8)]
+    big = [(0, 1), (127, 1), (128, 2), (255, 2), (256, 4), (511, 4), (512, 8), (1023, 8), (1024, 16), (1 << 20, 16)]
+    for fmt in FORMATS:
+        fid = nq.format_query(fmt).id
+        table = big if fmt in ("gguf:iq2_s", "gguf:iq1_s", "gguf:iq1_m") else plain
+        for q, want in table:
+            assert emu_lib.choose_upt(fid, q * g, g) == want, (fmt, q)
+            assert emu_lib.choose_upt(fid, q * g + g - 1, g) == want, (fmt, q)
+        assert emu_lib.choose_upt(fid, 100, 0) == 1
 
 
 @pytest.mark.parametrize("d_w", [1.0, 3.0, 448.0, 1e-30, 3e38])
