@@ -22,7 +22,7 @@ CFLAGS = ["-O1", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-s
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "f64": 3}
 _NP_OUT = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "f64": np.float64}
 
-OK, ERR_FORMAT, ERR_RANK, ERR_DIM, ERR_ALIGN, ERR_OVERFLOW, ERR_LENGTH, ERR_DTYPE = range(8)
+OK, ERR_FORMAT, ERR_RANK, ERR_DIM, ERR_ALIGN, ERR_OVERFLOW, ERR_LENGTH, ERR_DTYPE, ERR_DIVISORS = range(9)
 
 _lib = None
 
@@ -48,6 +48,10 @@ def lib():
         L.nqo_decode.argtypes = [c.c_int, c.c_void_p, c.c_uint64, c.POINTER(c.c_int64), c.c_int,
                                  c.c_int, c.c_void_p]
         L.nqo_decode_blocks_f32.argtypes = [c.c_int, c.c_void_p, c.c_uint64, c.c_float, c.c_void_p]
+        L.nqo_sizes_nvfp4_stacked.argtypes = [c.POINTER(c.c_int64), c.c_int, c.c_int64, c.POINTER(c.c_uint64),
+                                              c.POINTER(c.c_uint64)]
+        L.nqo_decode_nvfp4_stacked.argtypes = [c.c_void_p, c.c_uint64, c.POINTER(c.c_int64), c.c_int, c.c_int64,
+                                               c.c_int, c.c_void_p]
         L.nqo_f16_to_f32.argtypes = [c.c_uint16]
         L.nqo_f16_to_f32.restype = c.c_float
         L.nqo_f32_to_bf16.argtypes = [c.c_float]
@@ -124,6 +128,29 @@ def decode_status(fmt, payload, shape, dtype="f32"):
     arr, rank = _shape_arg(shape)
     return lib().nqo_decode(idx, payload.ctypes.data, payload.size, arr, rank,
                             DTYPES.get(dtype, 99), out.ctypes.data)
+
+
+def sizes_nvfp4_stacked(shape, divisors):
+    """(status, nbytes, nelems) of the stacked-divisor nvfp4 length rule."""
+    arr, rank = _shape_arg(shape)
+    nb, ne = ctypes.c_uint64(), ctypes.c_uint64()
+    st = lib().nqo_sizes_nvfp4_stacked(arr, rank, divisors, ctypes.byref(nb), ctypes.byref(ne))
+    return st, nb.value, ne.value
+
+
+def decode_nvfp4_stacked(payload, shape, divisors, dtype="f32"):
+    """Decode an nvfp4 plane of `divisors` stacked sources (flat array, raw 16-bit words for f16/bf16)."""
+    payload = np.ascontiguousarray(payload, dtype=np.uint8)
+    st, nbytes, nelems = sizes_nvfp4_stacked(shape, divisors)
+    if st != OK:
+        raise ValueError(f"oracle length rule rejects nvfp4 {shape} divisors={divisors}: status {st}")
+    out = np.empty(nelems, dtype=_NP_OUT[dtype])
+    arr, rank = _shape_arg(shape)
+    st = lib().nqo_decode_nvfp4_stacked(payload.ctypes.data, payload.size, arr, rank, divisors, DTYPES[dtype],
+                                        out.ctypes.data)
+    if st != OK:
+        raise ValueError(f"oracle decode of nvfp4 {shape} divisors={divisors} failed: status {st}")
+    return out
 
 
 def decode_blocks_f32(fmt, blocks, d_w=0.0):

@@ -720,3 +720,51 @@ int nqo_decode(int fmt, const uint8_t *payload, uint64_t nbytes, const int64_t *
     }
     return NQO_OK;
 }
+
+/* Stacked nvfp4 (NInfer tensor-formats 3.3).  The rows of the plane are the  */
+/* N = prod(shape[:-1]) rows of the flat row-major layout; row n takes the   */
+/* divisor of its source, d_w[floor(n / (N / divisors))], and each of its    */
+/* blocks is decoded with that divisor.                                      */
+int nqo_sizes_nvfp4_stacked(const int64_t *shape, int rank, int64_t divisors, uint64_t *nbytes,
+                            uint64_t *nelems)
+{
+    uint64_t nb1 = 0, ne = 0;
+    const int st = nqo_sizes(F_NVFP4_DIV, shape, rank, &nb1, &ne);
+    if (st != NQO_OK) return st;
+    if (divisors < 1) return NQO_ERR_DIVISORS;
+    uint64_t rows = 1; /* N = prod(shape[:-1]), the product of no dimensions being 1 */
+    for (int i = 0; i + 1 < rank; i++)
+        if (!mul_ok(rows, (uint64_t)shape[i], &rows)) return NQO_ERR_OVERFLOW;
+    if (rows % (uint64_t)divisors != 0) return NQO_ERR_DIVISORS;
+    if ((uint64_t)divisors > (0x7FFFFFFFFFFFFFFFull - (nb1 - 4)) / 4) return NQO_ERR_OVERFLOW;
+    if (nbytes) *nbytes = nb1 - 4 + 4 * (uint64_t)divisors;
+    if (nelems) *nelems = ne;
+    return NQO_OK;
+}
+
+int nqo_decode_nvfp4_stacked(const uint8_t *payload, uint64_t nbytes, const int64_t *shape, int rank,
+                             int64_t divisors, int dtype, void *out)
+{
+    if (dtype < NQO_F32 || dtype > NQO_F64) return NQO_ERR_DTYPE;
+    uint64_t need = 0, nelems = 0;
+    const int st = nqo_sizes_nvfp4_stacked(shape, rank, divisors, &need, &nelems);
+    if (st != NQO_OK) return st;
+    if (need != nbytes) return NQO_ERR_LENGTH;
+    if (nelems == 0) return NQO_OK;
+    const uint64_t K = (uint64_t)shape[rank - 1];
+    const uint64_t N = nelems / K;
+    const uint64_t rows_per_source = N / (uint64_t)divisors;
+    const uint64_t blocks_per_row = K / 64;
+    const uint8_t *trailer = payload + N * blocks_per_row * 36;
+    static const int OSIZE[4] = {4, 2, 2, 8};
+    float y[64];
+    for (uint64_t n = 0; n < N; n++) {
+        const float d_w = R32((uint32_t)U(trailer + 4 * (n / rows_per_source), 4));
+        for (uint64_t b = 0; b < blocks_per_row; b++) {
+            const uint64_t i = n * blocks_per_row + b;
+            dec_nvfp4_div(payload + i * 36, d_w, y);
+            nqo_convert(y, 64, dtype, (uint8_t *)out + i * 64 * (uint64_t)OSIZE[dtype]);
+        }
+    }
+    return NQO_OK;
+}

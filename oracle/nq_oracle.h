@@ -35,7 +35,8 @@ enum {
     NQO_ERR_ALIGN = 4,    /* shape[-1] % B != 0 */
     NQO_ERR_OVERFLOW = 5, /* a byte or element count beyond INT64_MAX */
     NQO_ERR_LENGTH = 6,   /* nbytes differs from the length rule */
-    NQO_ERR_DTYPE = 7     /* unknown output dtype */
+    NQO_ERR_DTYPE = 7,    /* unknown output dtype */
+    NQO_ERR_DIVISORS = 8  /* divisors < 1, or the row count is not a multiple of it */
 };
 
 /* Output dtypes: 0 binary32, 1 binary16, 2 bfloat16, 3 binary64. */
@@ -55,6 +56,18 @@ int nqo_sizes(int fmt, const int64_t *shape, int rank, uint64_t *nbytes, uint64_
 /* Decode a whole payload.  out holds prod(shape) values of `dtype`. */
 int nqo_decode(int fmt, const uint8_t *payload, uint64_t nbytes, const int64_t *shape,
                int rank, int dtype, void *out);
+
+/* "nvfp4" with stacked divisors (NInfer tensor-formats section 3.3): a plane
+ * of N = prod(shape[:-1]) rows assembled from `divisors` source matrices
+ * holds one binary32 weight divisor per source; source j covers the N /
+ * divisors consecutive rows starting at row j * (N / divisors), and row n
+ * is divided by d_w[floor(n / (N / divisors))].  Bytes: the gguf:nvfp4
+ * blocks of all rows, then the `divisors` little-endian binary32 words in
+ * stacking order.  divisors == 1 is the plain "nvfp4" format. */
+int nqo_sizes_nvfp4_stacked(const int64_t *shape, int rank, int64_t divisors, uint64_t *nbytes,
+                            uint64_t *nelems);
+int nqo_decode_nvfp4_stacked(const uint8_t *payload, uint64_t nbytes, const int64_t *shape, int rank,
+                             int64_t divisors, int dtype, void *out);
 
 /* Decode `nblocks` back-to-back blocks to binary32 (no trailer; `d_w` is the
  * divisor used by "nvfp4" and ignored by every other format). */

@@ -97,21 +97,26 @@ def fill_into(fmt, nblocks, seed, recipe, buf_ptr):
         raise ValueError(f"synth_fill failed for {fmt}")
 
 
-def payload(fmt, nblocks, seed, recipe, divisor=None):
+def payload(fmt, nblocks, seed, recipe, divisor=None, divisors=1):
     """Return a uint8 array: nblocks blocks, then the trailer if the format has one.
 
-    The trailer of ``nvfp4`` is a little-endian binary32 divisor: ``divisor``
-    (a float) if given, else bits uniform in [bits(1.0), bits(448.0)].
+    The trailer of ``nvfp4`` is ``divisors`` little-endian binary32 divisors
+    (one per stacked source): ``divisor`` (a float, or a sequence of
+    ``divisors`` floats) if given, else bits uniform in [bits(1.0),
+    bits(448.0)], the j-th drawn from seed + j.
     """
     S = block_bytes(fmt)
     T = trailer_bytes(fmt)
-    out = np.empty(nblocks * S + T, dtype=np.uint8)
+    nd = divisors if T == 4 else 0
+    out = np.empty(nblocks * S + 4 * nd, dtype=np.uint8)
     if nblocks:
         fill_into(fmt, nblocks, seed, recipe, out.ctypes.data)
-    if T == 4:
+    if nd:
         if divisor is None:
-            bits = divisor_bits(seed)
+            bits = [divisor_bits(seed + j) for j in range(nd)]
         else:
-            bits = int(np.array([divisor], dtype=np.float32).view(np.uint32)[0])
-        out[nblocks * S:] = np.array([bits], dtype="<u4").view(np.uint8)
+            vals = list(divisor) if hasattr(divisor, "__len__") else [divisor] * nd
+            assert len(vals) == nd
+            bits = [int(v) for v in np.array(vals, dtype=np.float32).view(np.uint32)]
+        out[nblocks * S:] = np.array(bits, dtype="<u4").view(np.uint8)
     return out

@@ -466,3 +466,73 @@ def test_bit_flip_structure(fmt):
             assert union == set(outs), (fmt, byte, bit, sorted(set(outs) - union)[:8])
         elif kind == "some":
             assert union, (fmt, byte, bit)
+
+
+# ---------------------------------------------------------------------------
+# nvfp4 with stacked divisors (NInfer tensor-formats, section 3.3: one weight
+# divisor per source matrix stacked into the plane, covering N / divisors
+# consecutive rows in stacking order).
+# ---------------------------------------------------------------------------
+def _stacked(shape, divisors, seed, d_ws=None):
+    K = shape[-1]
+    N = int(np.prod(shape[:-1])) if len(shape) > 1 else 1
+    nb = N * K // 64
+    return synth.payload("nvfp4", nb, seed, synth.binade(-12, -6, True), divisor=d_ws, divisors=divisors), N, K
+
+
+@pytest.mark.parametrize("shape,divisors", [([12, 128], 1), ([12, 128], 2), ([12, 128], 3), ([12, 128], 4),
+                                            ([12, 128], 12), ([2, 6, 64], 3), ([8, 256], 2)])
+def test_nvfp4_stacked_equals_each_source_decoded_alone(shape, divisors):
+    """A stacked plane decodes as its sources would one by one: source j is the
+    rows [j N/D, (j+1) N/D) with the j-th trailer word as its only divisor."""
+    p, N, K = _stacked(shape, divisors, 101 + divisors)
+    got = oracle.decode_nvfp4_stacked(p, shape, divisors, "f32").view(np.uint32)
+    rows = N // divisors
+    src_bytes = rows * (K // 64) * 36
+    trailer = p[N * (K // 64) * 36:]
+    for j in range(divisors):
+        alone = np.concatenate([p[j * src_bytes:(j + 1) * src_bytes], trailer[4 * j:4 * j + 4]])
+        ref = oracle.decode("nvfp4", alone, [rows, K], "f32").view(np.uint32)
+        assert np.array_equal(got[j * rows * K:(j + 1) * rows * K], ref), j
+
+
+def test_nvfp4_stacked_power_of_two_divisors_scale_exactly():
+    """Every source holds the same blocks and d_w[j] = 2^j, so source j is
+    source 0 divided by 2^j exactly (all values stay normal binary32)."""
+    K, rows, D = 128, 3, 4
+    one = synth.payload("nvfp4", rows * K // 64, 7, synth.binade(-12, -6, True), divisor=1.0)[:-4]
+    p = np.concatenate([np.tile(one, D), np.array([2.0 ** j for j in range(D)], dtype="<f4").view(np.uint8)])
+    y = oracle.decode_nvfp4_stacked(p, [D * rows, K], D, "f64").reshape(D, rows * K)
+    assert np.any(y[0] != 0)
+    for j in range(D):
+        assert np.array_equal(y[j], y[0] / 2.0 ** j)
+    # the trailer length tells the stacking apart: one divisor means 12 bytes fewer
+    assert oracle.sizes_nvfp4_stacked([D * rows, K], 1)[1] == p.size - 12
+
+
+def test_nvfp4_stacked_single_divisor_is_plain_nvfp4():
+    p, N, K = _stacked([5, 192], 1, 33)
+    for dtype in ("f32", "bf16", "f16", "f64"):
+        assert np.array_equal(oracle.decode_nvfp4_stacked(p, [5, 192], 1, dtype),
+                              oracle.decode("nvfp4", p, [5, 192], dtype))
+
+
+@pytest.mark.parametrize("shape,divisors,want", [
+    ([12, 128], 0, "ERR_DIVISORS"), ([12, 128], -3, "ERR_DIVISORS"), ([12, 128], 5, "ERR_DIVISORS"),
+    ([12, 128], 6, "OK"), ([6, 0], 4, "ERR_DIVISORS"), ([6, 0], 3, "OK"), ([0, 128], 7, "OK"),
+    ([128], 1, "OK"), ([128], 2, "ERR_DIVISORS"), ([12, 100], 2, "ERR_ALIGN"), ([3, 4, 64], 4, "OK"),
+    ([3, 4, 64], 8, "ERR_DIVISORS"), ([2 ** 40, 2 ** 40, 0], 1, "ERR_OVERFLOW")])
+def test_nvfp4_stacked_length_rule(shape, divisors, want):
+    """nbytes = prod(shape[:-1]) (shape[-1]/64) 36 + 4 divisors, with
+    N = prod(shape[:-1]) a multiple of divisors (the product of no dimensions
+    is 1)."""
+    st, nbytes, nelems = oracle.sizes_nvfp4_stacked(shape, divisors)
+    assert st == getattr(oracle, want), (st, want)
+    if st == oracle.OK:
+        N = math.prod(shape[:-1])
+        assert nbytes == N * (shape[-1] // 64) * 36 + 4 * divisors
+        assert nelems == N * shape[-1]
+        p = np.zeros(nbytes, dtype=np.uint8)
+        assert len(oracle.decode_nvfp4_stacked(p, shape, divisors)) == nelems
+        with pytest.raises(ValueError):
+            oracle.decode_nvfp4_stacked(np.zeros(nbytes + 1, dtype=np.uint8), shape, divisors)
