@@ -75,7 +75,7 @@ def log(msg):
 class Tensor:
     """One resident payload and its output buffer."""
 
-    def __init__(self, name, fmt, shape, recipe, seed, dtype, staging, torch, nq, synth):
+    def __init__(self, name, fmt, shape, recipe, seed, dtype, staging, torch, nq, synth, divisors=1):
         info = nq.format_query(fmt)
         self.name, self.fmt, self.shape, self.dtype = name, fmt, list(shape), dtype
         self.fid = info.id
@@ -84,14 +84,15 @@ class Tensor:
             nel *= d
         self.nelems = nel
         self.nblocks = nel // info.block_values
-        self.nbytes = self.nblocks * info.block_bytes + info.trailer_bytes
+        self.divisors = divisors if info.trailer_bytes else 0
+        self.nbytes = self.nblocks * info.block_bytes + 4 * self.divisors
         host = staging[: self.nbytes]
         if self.nblocks:
             synth.fill_into(fmt, self.nblocks, seed, recipe, host.data_ptr())
-        if info.trailer_bytes:
-            bits = synth.divisor_bits(seed)
-            host[self.nblocks * info.block_bytes:] = torch.tensor(
-                [(bits >> (8 * i)) & 0xFF for i in range(4)], dtype=torch.uint8)
+        for j in range(self.divisors):  # one binary32 divisor per stacked source
+            bits = synth.divisor_bits(seed + j)
+            o = self.nblocks * info.block_bytes + 4 * j
+            host[o:o + 4] = torch.tensor([(bits >> (8 * i)) & 0xFF for i in range(4)], dtype=torch.uint8)
         self.payload = torch.empty(self.nbytes, dtype=torch.uint8, device="cuda:0")
         self.payload.copy_(host, non_blocking=False)
         tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "f64": torch.float64}[dtype]
@@ -100,8 +101,12 @@ class Tensor:
         self.seed, self.recipe = seed, recipe
 
     def launch(self, nq, stream_handle):
-        st = nq.dequantize_packed_raw(self.fid, self.payload.data_ptr(), self.nbytes, self.shape,
-                                      OUT_CODES[self.dtype], self.out.data_ptr(), stream_handle)
+        if self.divisors > 1:
+            st = nq.dequantize_nvfp4_stacked_raw(self.payload.data_ptr(), self.nbytes, self.shape, self.divisors,
+                                                 OUT_CODES[self.dtype], self.out.data_ptr(), stream_handle)
+        else:
+            st = nq.dequantize_packed_raw(self.fid, self.payload.data_ptr(), self.nbytes, self.shape,
+                                          OUT_CODES[self.dtype], self.out.data_ptr(), stream_handle)
         if st != 0:
             raise nq.NqError(st, self.name)
 
@@ -178,13 +183,13 @@ def per_format_times(torch, nq, items, reps):
 
 
 def rotating_measurement(torch, nq, synth, name, fmt, shape, recipe, seed, dtype, staging, launches=60,
-                         footprint=1 << 30):
+                         footprint=1 << 30, divisors=1):
     """Mean launch time of one workload over replicas whose total footprint defeats the caches."""
-    first = Tensor(name, fmt, shape, recipe, seed, dtype, staging, torch, nq, synth)
+    first = Tensor(name, fmt, shape, recipe, seed, dtype, staging, torch, nq, synth, divisors)
     reps = max(1, math.ceil(footprint / first.algo_bytes))
     items = [first]
     for r in range(1, reps):
-        items.append(Tensor(name, fmt, shape, recipe, seed, dtype, staging, torch, nq, synth))
+        items.append(Tensor(name, fmt, shape, recipe, seed, dtype, staging, torch, nq, synth, divisors))
     order = [items[i % reps] for i in range(launches)]
     g = capture(torch, nq, order)
     ms, _ = time_graph(torch, g, 3)
@@ -302,6 +307,14 @@ def main():
                     key = f"{name}->{dt}"
                     extra[key] = rotating_measurement(torch, nq, synth, name, fmt, shape, recipe, seed, dt, st2)
                     log(f"{key}: {extra[key]['gbps']} GB/s ({100 * extra[key]['frac_hbm_peak']:.1f}% of peak)")
+            del st2
+        # nvfp4 planes stacked from two and eight sources (a gate/up pair, eight experts' slices)
+        for shape, nd in (([2 * 14336, 4096], 2), ([8 * 1024, 4096], 8)):
+            key = f"nvfp4x{nd}{shape}->bf16"
+            st2 = torch.empty(math.prod(shape) // 64 * 36 + 4 * nd, dtype=torch.uint8, pin_memory=True)
+            extra[key] = rotating_measurement(torch, nq, synth, key, "nvfp4", shape, workloads.recipe_for("nvfp4"),
+                                              0x6E710000 + 77 * nd, "bf16", st2, divisors=nd)
+            log(f"{key}: {extra[key]['gbps']} GB/s ({100 * extra[key]['frac_hbm_peak']:.1f}% of peak)")
             del st2
 
     cpu = None

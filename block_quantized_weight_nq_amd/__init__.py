@@ -16,11 +16,12 @@ LIB_PATH = os.path.join(_HERE, "libnq.so")
 NQ_OK = 0
 STATUS_NAMES = {0: "NQ_OK", 1: "NQ_ERR_NULL_ARG", 2: "NQ_ERR_UNKNOWN_FORMAT", 3: "NQ_ERR_BAD_RANK",
                 4: "NQ_ERR_BAD_DIM", 5: "NQ_ERR_NOT_BLOCK_ALIGNED", 6: "NQ_ERR_LENGTH_MISMATCH",
-                7: "NQ_ERR_OVERFLOW", 8: "NQ_ERR_BAD_DTYPE", 9: "NQ_ERR_HIP"}
+                7: "NQ_ERR_OVERFLOW", 8: "NQ_ERR_BAD_DTYPE", 9: "NQ_ERR_HIP", 10: "NQ_ERR_BAD_DIVISORS"}
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "f64": 3}
 FAMILIES = {0: "simple", 1: "kquant", 2: "iq", 3: "fp4", 4: "ternary"}
 EXPORTS = ["nq_format_count", "nq_format_by_id", "nq_format_query", "nq_validate",
-           "nq_dequantize_packed", "nq_status_string"]
+           "nq_dequantize_packed", "nq_validate_nvfp4_stacked", "nq_dequantize_nvfp4_stacked",
+           "nq_status_string"]
 
 
 class NqError(RuntimeError):
@@ -58,6 +59,10 @@ def _lib():
                                   c.POINTER(c.c_uint64), c.POINTER(c.c_uint64)]
         L.nq_dequantize_packed.argtypes = [c.c_int32, c.c_void_p, c.c_uint64, c.POINTER(c.c_int64),
                                            c.c_int32, c.c_int32, c.c_void_p, c.c_void_p]
+        L.nq_validate_nvfp4_stacked.argtypes = [c.c_uint64, c.POINTER(c.c_int64), c.c_int32, c.c_int64,
+                                                c.c_int32, c.POINTER(c.c_uint64), c.POINTER(c.c_uint64)]
+        L.nq_dequantize_nvfp4_stacked.argtypes = [c.c_void_p, c.c_uint64, c.POINTER(c.c_int64), c.c_int32,
+                                                  c.c_int64, c.c_int32, c.c_void_p, c.c_void_p]
         L.nq_status_string.argtypes = [c.c_int]
         L.nq_status_string.restype = c.c_char_p
         _LIB = L
@@ -130,17 +135,29 @@ def dequantize_packed_raw(fmt_id, payload_ptr, nbytes, shape, out_dtype_code, ou
                                        ctypes.c_void_p(stream_handle))
 
 
-def dequantize_packed(fmt, payload, shape, out_dtype=None, out=None, stream=None):
-    """Decode a rank-1 uint8 CUDA tensor into a new (or the given) tensor of `shape`.
+def validate_nvfp4_stacked_status(nbytes, shape, divisors, out_dtype="f32"):
+    """Raw status of nq_validate_nvfp4_stacked plus (elems, out_bytes)."""
+    arr, rank = _shape(shape)
+    ne, nb = ctypes.c_uint64(), ctypes.c_uint64()
+    code = out_dtype if isinstance(out_dtype, int) else _dtype_code(out_dtype)
+    st = _lib().nq_validate_nvfp4_stacked(nbytes, arr, rank, int(divisors), code, ctypes.byref(ne),
+                                          ctypes.byref(nb))
+    return st, ne.value, nb.value
 
-    out_dtype: torch.float32 (default), torch.float16, torch.bfloat16 or torch.float64.
-    The decode is enqueued on `stream` (default: the current stream).
-    """
+
+def dequantize_nvfp4_stacked_raw(payload_ptr, nbytes, shape, divisors, out_dtype_code, out_ptr, stream_handle):
+    """Direct call of nq_dequantize_nvfp4_stacked with integer addresses; returns the status."""
+    arr, rank = _shape(shape)
+    return _lib().nq_dequantize_nvfp4_stacked(ctypes.c_void_p(payload_ptr), nbytes, arr, rank, int(divisors),
+                                              out_dtype_code, ctypes.c_void_p(out_ptr),
+                                              ctypes.c_void_p(stream_handle))
+
+
+def _prepare(payload, shape, out_dtype, out, stream):
     import torch
     if out_dtype is None:
         out_dtype = out.dtype if out is not None else torch.float32
     code = _dtype_code(out_dtype)
-    fid = fmt if isinstance(fmt, int) else format_query(fmt).id
     if payload.dtype != torch.uint8 or payload.dim() != 1 or not payload.is_cuda:
         raise ValueError("payload must be a rank-1 torch.uint8 CUDA tensor")
     if not payload.is_contiguous():
@@ -155,6 +172,28 @@ def dequantize_packed(fmt, payload, shape, out_dtype=None, out=None, stream=None
         raise ValueError("out must be a contiguous tensor of the requested dtype, size and device")
     if stream is None:
         stream = torch.cuda.current_stream(payload.device)
+    return code, out, stream
+
+
+def dequantize_nvfp4_stacked(payload, shape, divisors, out_dtype=None, out=None, stream=None):
+    """Decode an "nvfp4" plane stacked from `divisors` sources (one binary32
+    divisor per source after the blocks) into a new (or the given) tensor."""
+    code, out, stream = _prepare(payload, shape, out_dtype, out, stream)
+    st = dequantize_nvfp4_stacked_raw(payload.data_ptr(), payload.numel(), shape, divisors, code,
+                                      out.data_ptr(), stream.cuda_stream)
+    if st != NQ_OK:
+        raise NqError(st, f"nvfp4 {list(shape)} divisors={divisors}")
+    return out
+
+
+def dequantize_packed(fmt, payload, shape, out_dtype=None, out=None, stream=None):
+    """Decode a rank-1 uint8 CUDA tensor into a new (or the given) tensor of `shape`.
+
+    out_dtype: torch.float32 (default), torch.float16, torch.bfloat16 or torch.float64.
+    The decode is enqueued on `stream` (default: the current stream).
+    """
+    fid = fmt if isinstance(fmt, int) else format_query(fmt).id
+    code, out, stream = _prepare(payload, shape, out_dtype, out, stream)
     st = dequantize_packed_raw(fid, payload.data_ptr(), payload.numel(), shape, code,
                                out.data_ptr(), stream.cuda_stream)
     if st != NQ_OK:

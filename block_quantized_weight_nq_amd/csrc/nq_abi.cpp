@@ -132,11 +132,12 @@ NQ_API int nq_validate(int32_t format, uint64_t nbytes, const int64_t *shape, in
     return NQ_OK;
 }
 
-NQ_API int nq_dequantize_packed(int32_t format, const void *payload, uint64_t nbytes, const int64_t *shape,
-                                int32_t rank, int32_t out_dtype, void *out, hipStream_t stream) {
-    uint64_t elems = 0;
-    const int st = nq_validate(format, nbytes, shape, rank, out_dtype, &elems, nullptr);
-    if (st != NQ_OK) return st;
+namespace {
+
+// Pointer checks and the launch, after validation.  ndiv divisor words
+// close an "nvfp4" payload; each covers gu units (rows per source * K / 8).
+int launch_validated(int32_t format, const void *payload, uint64_t nbytes, uint64_t elems, int32_t out_dtype,
+                     void *out, uint32_t ndiv, uint64_t gu, hipStream_t stream) {
     if (nbytes > 0 && !payload) return NQ_ERR_NULL_ARG;
     if (elems == 0) return NQ_OK;
     if (!out) return NQ_ERR_NULL_ARG;
@@ -147,6 +148,8 @@ NQ_API int nq_dequantize_packed(int32_t format, const void *payload, uint64_t nb
     L.nblocks = elems / (uint64_t)B_OF(format);
     L.out = out;
     L.resident = resident_workgroups();
+    L.ndiv = ndiv;
+    L.gu = gu;
     switch (REGISTRY[format].family) {
     case NQ_FAMILY_SIMPLE: return nq::launch_simple(format, out_dtype, L, stream);
     case NQ_FAMILY_KQUANT: return nq::launch_kquant(format, out_dtype, L, stream);
@@ -154,6 +157,60 @@ NQ_API int nq_dequantize_packed(int32_t format, const void *payload, uint64_t nb
     case NQ_FAMILY_FP4: return nq::launch_fp4(format, out_dtype, L, stream);
     default: return nq::launch_ternary(format, out_dtype, L, stream);
     }
+}
+
+constexpr int64_t MAX_DIVISORS = (int64_t)1 << 30;
+
+}  // namespace
+
+NQ_API int nq_dequantize_packed(int32_t format, const void *payload, uint64_t nbytes, const int64_t *shape,
+                                int32_t rank, int32_t out_dtype, void *out, hipStream_t stream) {
+    uint64_t elems = 0;
+    const int st = nq_validate(format, nbytes, shape, rank, out_dtype, &elems, nullptr);
+    if (st != NQ_OK) return st;
+    // one divisor: its group is the whole tensor
+    return launch_validated(format, payload, nbytes, elems, out_dtype, out, 1u, elems / 8 ? elems / 8 : 1, stream);
+}
+
+NQ_API int nq_validate_nvfp4_stacked(uint64_t nbytes, const int64_t *shape, int32_t rank, int64_t divisors,
+                                     int32_t out_dtype, uint64_t *out_elems, uint64_t *out_bytes) {
+    if (out_dtype < NQ_F32 || out_dtype > NQ_F64) return NQ_ERR_BAD_DTYPE;
+    if (rank < 1) return NQ_ERR_BAD_RANK;
+    if (!shape) return NQ_ERR_NULL_ARG;
+    for (int32_t i = 0; i < rank; i++)
+        if (shape[i] < 0) return NQ_ERR_BAD_DIM;
+    if (shape[rank - 1] % 64 != 0) return NQ_ERR_NOT_BLOCK_ALIGNED;
+    if (divisors < 1 || divisors > MAX_DIVISORS) return NQ_ERR_BAD_DIVISORS;
+    // the single-divisor rule fixes every count except the trailer
+    uint64_t elems = 0, bytes1 = 0, rows = 1;
+    const int st = nq_validate(nq::NVFP4_DIV, 0, shape, rank, out_dtype, nullptr, nullptr);
+    if (st != NQ_OK && st != NQ_ERR_LENGTH_MISMATCH) return st;
+    for (int32_t i = 0; i + 1 < rank; i++)
+        if (!mul_checked(rows, (uint64_t)shape[i], &rows)) return NQ_ERR_OVERFLOW;
+    if (rows % (uint64_t)divisors != 0) return NQ_ERR_BAD_DIVISORS;
+    for (int32_t i = 0; i < rank; i++)
+        if (shape[i] == 0) rows = 0;
+    if (rows != 0) {
+        const uint64_t K = (uint64_t)shape[rank - 1];
+        elems = rows * K;                 // bounded by nq_validate
+        bytes1 = rows * (K / 64) * 36;
+    }
+    const uint64_t bytes = bytes1 + 4 * (uint64_t)divisors;
+    if (bytes > I64MAX) return NQ_ERR_OVERFLOW;
+    if (nbytes != bytes) return NQ_ERR_LENGTH_MISMATCH;
+    if (out_elems) *out_elems = elems;
+    if (out_bytes) *out_bytes = elems * OUT_SIZE[out_dtype];
+    return NQ_OK;
+}
+
+NQ_API int nq_dequantize_nvfp4_stacked(const void *payload, uint64_t nbytes, const int64_t *shape, int32_t rank,
+                                       int64_t divisors, int32_t out_dtype, void *out, hipStream_t stream) {
+    uint64_t elems = 0;
+    const int st = nq_validate_nvfp4_stacked(nbytes, shape, rank, divisors, out_dtype, &elems, nullptr);
+    if (st != NQ_OK) return st;
+    const uint64_t gu = elems / 8 / (uint64_t)divisors;  // units per source; 0 only when empty
+    return launch_validated(nq::NVFP4_DIV, payload, nbytes, elems, out_dtype, out, (uint32_t)divisors,
+                            gu ? gu : 1, stream);
 }
 
 NQ_API const char *nq_status_string(int status) {
@@ -168,6 +225,7 @@ NQ_API const char *nq_status_string(int status) {
     case NQ_ERR_OVERFLOW: return "byte or element count overflows";
     case NQ_ERR_BAD_DTYPE: return "unknown output dtype";
     case NQ_ERR_HIP: return "HIP launch failed";
+    case NQ_ERR_BAD_DIVISORS: return "divisors must be in [1, 2^30] and divide the row count";
     default: return "unknown status";
     }
 }

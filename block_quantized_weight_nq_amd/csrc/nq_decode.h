@@ -477,8 +477,10 @@ NQ_HD float e2m1(uint32_t c) {
 }
 NQ_HD float e2m1_e4m3_div(uint32_t sw, uint32_t c, float dw) { return M(e2m1(c), e4m3fn(sw)) / dw; }
 
-template <class Src, class Tab>
-NQ_HD void unit_nvfp4_div(const Src &src, uint32_t bo, uint32_t s, const Tab &tab, float (&y)[8]) {
+// DIRECT: divide by `dw` here instead of reading the table built for the
+// tile's first divisor group (same correctly rounded quotient).
+template <bool DIRECT, class Src, class Tab>
+NQ_HD void unit_nvfp4_div(const Src &src, uint32_t bo, uint32_t s, const Tab &tab, float dw, float (&y)[8]) {
     const uint32_t g = s >> 1;
     const uint32_t sw = u8_at(src, bo + g);
     uint32_t q[2];
@@ -490,7 +492,8 @@ NQ_HD void unit_nvfp4_div(const Src &src, uint32_t bo, uint32_t s, const Tab &ta
     for (int j = 0; j < 8; j++) {
         const uint32_t code = code_at(c, j);
         const uint32_t neg = ((code >> 3) ^ (sw >> 7)) & 1u;
-        y[j] = bits_f32(__builtin_bit_cast(uint32_t, tab.nv(row + (code & 7u))) ^ (neg << 31));
+        const float mag = DIRECT ? e2m1_e4m3_div(sw & 0x7Fu, code & 7u, dw) : tab.nv(row + (code & 7u));
+        y[j] = bits_f32(__builtin_bit_cast(uint32_t, mag) ^ (neg << 31));
     }
 }
 
@@ -632,7 +635,7 @@ NQ_HD void decode_unit(const Src &src, uint32_t bo, uint32_t s, const Tab &tab, 
     else if constexpr (F == NVFP4_GGUF)
         unit_nvfp4_gguf(src, bo, s, y);
     else if constexpr (F == NVFP4_DIV)
-        unit_nvfp4_div(src, bo, s, tab, y);
+        unit_nvfp4_div<false>(src, bo, s, tab, 0.0f, y);
     else
         unit_iq<F>(src, bo, s, tab, y);
 }

@@ -87,7 +87,10 @@ struct DevSrc {
 struct Tab {
     const uint64_t *t8;
     const uint32_t *t4;
-    const float *nvq;
+    const float *nvq;        // "nvfp4": quotients by the divisor of the tile's first unit
+    const float *nvd;        // "nvfp4": divisors of the groups the tile reaches, from that one on
+    uint32_t nv_bound;       // "nvfp4": first unit (chunk-relative) past that divisor's group
+    uint32_t nv_gu;          // "nvfp4": units per divisor group, capped at 2^31 - 1
     NQ_HD uint64_t iq2xxs(uint32_t r) const { return t8[r]; }
     NQ_HD uint64_t iq2xs(uint32_t r) const { return t8[r]; }
     NQ_HD uint64_t iq2s(uint32_t r) const { return t8[r]; }
@@ -104,6 +107,9 @@ struct TabSpec {
                             : (F == IQ1_S || F == IQ1_M) ? 2048 : 0;
     static constexpr int n4 = F == IQ3_XXS ? 256 : F == IQ3_S ? 512 : 0;
     static constexpr int nf = F == NVFP4_DIV ? 1024 : 0;
+    // divisors a tile can reach: a group is at least one row of 64 values
+    // (8 units), a tile at most 16 * 256 units
+    static constexpr int nd = F == NVFP4_DIV ? 1 + 16 * 256 / 8 : 0;
     NQ_HD static const uint64_t *src8() {
         return F == IQ2_XXS ? NQ_GRID_IQ2XXS : F == IQ2_XS ? NQ_GRID_IQ2XS : F == IQ2_S ? NQ_GRID_IQ2S
                                                                                      : NQ_GRID_IQ1S;
@@ -114,12 +120,16 @@ struct TabSpec {
 // Kernel arguments for one launch (one chunk of whole blocks).
 struct KArgs {
     const uint32_t *base;     // payload of this chunk, aligned down to 4 bytes
-    const uint32_t *tr_base;  // "nvfp4" divisor, aligned down to 4 bytes
+    const uint32_t *tr_base;  // "nvfp4" divisor words, aligned down to 4 bytes
     void *out;                // output element 0 of this chunk
     uint32_t mis;             // payload start - base (0..3)
     uint32_t last;            // last payload dword of this chunk, from base
-    uint32_t tr_mis;          // divisor address - tr_base (0..3)
+    uint32_t tr_mis;          // first divisor's address - tr_base (0..3)
+    uint32_t tr_last;         // last dword holding divisor bytes, from tr_base
     uint32_t nunits;          // units in this chunk
+    uint32_t ndiv;            // "nvfp4": number of divisors (stacked sources)
+    uint64_t u0;              // "nvfp4": tensor unit index of the chunk's first unit
+    uint64_t gu;              // "nvfp4": units per divisor group (rows per source * K / 8)
 };
 
 // Non-temporal 16-byte stores (streamed past the caches) pay off when each
@@ -298,6 +308,13 @@ NQ_HD void stage_store(uint32_t *slot, const KArgs &a, uint32_t t, uint32_t tid,
     }
 }
 
+// "nvfp4" units past the divisor group of the tile's first unit (u >=
+// tab.nv_bound) are decoded a second time, dividing by their own group's
+// divisor directly (the same correctly rounded quotient the table holds); the
+// first pass skips their stores.  This pass is a rolled loop so that its
+// divisions appear once in the code.
+NQ_HD inline bool nv_table_unit(const Tab &tab, uint32_t u) { return u < tab.nv_bound; }
+
 // Decode this thread's units of tile t from its staged copy in `buf`.  A
 // block's units are consecutive and a tile row of 256 units holds whole
 // blocks, so unit k*256 + tid of a tile lies in the tile's block
@@ -313,11 +330,26 @@ NQ_HD void decode_staged(const T &tab, const KArgs &a, uint32_t t, uint32_t tid,
     const LdsSrc src{buf, ((p + ST::TB - 1) >> 2) - a0};
     const uint32_t s = tid % UPB;
     const uint32_t bo0 = (p & 3u) + (tid / UPB) * S;
-    float y[UPT][8];
 #pragma unroll
-    for (int k = 0; k < UPT; k++) decode_unit<F>(src, bo0 + (uint32_t)k * (WG / UPB) * S, s, tab, y[k]);
-#pragma unroll
-    for (int k = 0; k < UPT; k++) store8<OT, VEC>(a.out, t * ST::PER + (uint32_t)(k * WG) + tid, y[k]);
+    for (int k = 0; k < UPT; k++) {
+        const uint32_t u = t * ST::PER + (uint32_t)(k * WG) + tid;
+        float y[8];
+        decode_unit<F>(src, bo0 + (uint32_t)k * (WG / UPB) * S, s, tab, y);
+        if (F != NVFP4_DIV || nv_table_unit(tab, u)) store8<OT, VEC>(a.out, u, y);
+    }
+    if constexpr (F == NVFP4_DIV) {
+        if (!nv_table_unit(tab, t * ST::PER + (uint32_t)((UPT - 1) * WG) + tid)) {
+#pragma unroll 1
+            for (int k = 0; k < UPT; k++) {
+                const uint32_t u = t * ST::PER + (uint32_t)(k * WG) + tid;
+                if (nv_table_unit(tab, u)) continue;
+                float y[8];
+                unit_nvfp4_div<true>(src, bo0 + (uint32_t)k * (WG / UPB) * S, s, tab,
+                                     tab.nvd[1u + (u - tab.nv_bound) / tab.nv_gu], y);
+                store8<OT, VEC>(a.out, u, y);
+            }
+        }
+    }
 }
 
 // A tile that is not staged (a partial last tile, or the last full tile when
@@ -332,15 +364,49 @@ NQ_HD void decode_direct(const Src &src, const T &tab, const KArgs &a, uint32_t 
         if (u < a.nunits) {
             float y[8];
             decode_unit<F>(src, a.mis + (u / ST::UPB) * block_bytes(F), u % ST::UPB, tab, y);
+            if (F != NVFP4_DIV || nv_table_unit(tab, u)) store8<OT, VEC>(a.out, u, y);
+        }
+    }
+    if constexpr (F == NVFP4_DIV) {
+#pragma unroll 1
+        for (int k = 0; k < UPT; k++) {
+            const uint32_t u = t * ST::PER + (uint32_t)(k * WG) + tid;
+            if (u >= a.nunits || nv_table_unit(tab, u)) continue;
+            float y[8];
+            unit_nvfp4_div<true>(src, a.mis + (u / ST::UPB) * block_bytes(F), u % ST::UPB, tab,
+                                 tab.nvd[1u + (u - tab.nv_bound) / tab.nv_gu], y);
             store8<OT, VEC>(a.out, u, y);
         }
     }
 }
 
-// Table setup, strided over `nthreads` cooperating threads.
+// "nvfp4" divisor g (little-endian binary32 word g of the divisor array).
+template <class TrSrc>
+NQ_HD float divisor_at(const TrSrc &tr, const KArgs &a, uint32_t g) {
+    uint32_t w[1];
+    window<1>(tr, a.tr_mis + 4u * g, w);
+    return bits_f32(w[0]);
+}
+
+// "nvfp4": the divisor group of tile t's first unit, and the chunk-relative
+// unit where that group ends (capped at 2^32 - 1).
+template <int UPT>
+NQ_HD uint32_t nv_first_group(const KArgs &a, uint32_t t, uint32_t *bound) {
+    if (a.ndiv == 1) {  // one divisor: skip the 64-bit division
+        *bound = 0xFFFFFFFFu;
+        return 0;
+    }
+    const uint64_t g0 = (a.u0 + (uint64_t)t * (uint32_t)(WG * UPT)) / a.gu;
+    const uint64_t end = (g0 + 1) * a.gu - a.u0;
+    *bound = end > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)end;
+    return (uint32_t)g0;
+}
+
+// Table setup for the tile whose first divisor group is g0, strided over
+// `nthreads` cooperating threads.
 template <int F, class TrSrc>
-NQ_HD void fill_tables(uint64_t *t8, uint32_t *t4, float *nvq, const TrSrc &tr, uint32_t tr_mis,
-                       uint32_t tid, uint32_t nthreads) {
+NQ_HD void fill_tables(uint64_t *t8, uint32_t *t4, float *nvq, float *nvd, const TrSrc &tr, const KArgs &a,
+                       uint32_t g0, uint32_t tid, uint32_t nthreads) {
     using TS = TabSpec<F>;
     if constexpr (TS::n8 > 0) {
         const uint64_t *g = TS::src8();
@@ -351,9 +417,9 @@ NQ_HD void fill_tables(uint64_t *t8, uint32_t *t4, float *nvq, const TrSrc &tr, 
         for (uint32_t r = tid; r < (uint32_t)TS::n4; r += nthreads) t4[r] = g[r];
     }
     if constexpr (TS::nf > 0) {
-        uint32_t dww[1];
-        window<1>(tr, tr_mis, dww);
-        const float dw = bits_f32(dww[0]);
+        const uint32_t nd = a.ndiv - g0 < (uint32_t)TS::nd ? a.ndiv - g0 : (uint32_t)TS::nd;
+        for (uint32_t k = tid; k < nd; k += nthreads) nvd[k] = divisor_at(tr, a, g0 + k);
+        const float dw = divisor_at(tr, a, g0);
         for (uint32_t k = tid; k < (uint32_t)TS::nf; k += nthreads) nvq[k] = e2m1_e4m3_div(k >> 3, k & 7u, dw);
     }
 }
@@ -370,21 +436,27 @@ __global__ __launch_bounds__(WG) void k_decode(KArgs a) {
     __shared__ uint64_t t8[TS::n8 > 0 ? TS::n8 : 1];
     __shared__ uint32_t t4[TS::n4 > 0 ? TS::n4 : 1];
     __shared__ float nvq[TS::nf > 0 ? TS::nf : 1];
+    __shared__ float nvd[TS::nd > 0 ? TS::nd : 1];
     __shared__ __attribute__((aligned(16))) uint32_t lds[ST::SLOT_DW];
     const uint32_t tid = threadIdx.x, t = blockIdx.x;
     const DevSrc src{a.base, a.last};
-    const Tab tab{t8, t4, nvq};
+    Tab tab{t8, t4, nvq, nvd, 0xFFFFFFFFu, 1u};
+    uint32_t g0 = 0;
+    if constexpr (F == NVFP4_DIV) {
+        g0 = nv_first_group<UPT>(a, t, &tab.nv_bound);
+        tab.nv_gu = a.gu < 0x7FFFFFFFull ? (uint32_t)a.gu : 0x7FFFFFFFu;
+    }
+    const DevSrc tr{a.tr_base, a.tr_last};
     if (t < staged_tiles<F, UPT>(a)) {
         uint32_t r[ST::NK][4];
         stage_load<F, UPT>(src, a, t, tid, r);
-        if constexpr (TS::n8 + TS::n4 + TS::nf > 0)
-            fill_tables<F>(t8, t4, nvq, DevSrc{a.tr_base, (a.tr_mis + 3u) >> 2}, a.tr_mis, tid, WG);
+        if constexpr (TS::n8 + TS::n4 + TS::nf > 0) fill_tables<F>(t8, t4, nvq, nvd, tr, a, g0, tid, WG);
         stage_store<F, UPT>(lds, a, t, tid, r);
         __syncthreads();
         decode_staged<F, OT, UPT, VEC>(tab, a, t, tid, lds);
     } else {
         if constexpr (TS::n8 + TS::n4 + TS::nf > 0) {
-            fill_tables<F>(t8, t4, nvq, DevSrc{a.tr_base, (a.tr_mis + 3u) >> 2}, a.tr_mis, tid, WG);
+            fill_tables<F>(t8, t4, nvq, nvd, tr, a, g0, tid, WG);
             __syncthreads();
         }
         decode_direct<F, OT, UPT, VEC>(src, tab, a, t, tid);
@@ -398,6 +470,8 @@ struct LaunchArgs {
     uint64_t nblocks;
     void *out;               // device
     uint32_t resident;       // workgroups the device holds at once (the tile-size scale)
+    uint32_t ndiv;           // "nvfp4": divisor words after the blocks (stacked sources)
+    uint64_t gu;             // "nvfp4": units per divisor group
 };
 
 
@@ -415,13 +489,17 @@ NQ_HD KArgs chunk_args(const LaunchArgs &L, uint64_t b0, uint64_t nb, uint32_t *
     constexpr uint64_t S = block_bytes(F);
     constexpr uint64_t OSZ = OT == 0 ? 4 : OT == 3 ? 8 : 2;
     const uint8_t *p = L.payload + b0 * S;
-    const uint8_t *tr = L.payload + L.nbytes - (F == NVFP4_DIV ? 4 : 0);
+    const uint8_t *tr = L.payload + L.nbytes - (F == NVFP4_DIV ? 4ull * L.ndiv : 0);
     KArgs a;
     a.base = (const uint32_t *)((uintptr_t)p & ~(uintptr_t)3);
     a.mis = (uint32_t)((uintptr_t)p & 3);
     a.last = (uint32_t)((a.mis + nb * S - 1) >> 2);
     a.tr_base = (const uint32_t *)((uintptr_t)tr & ~(uintptr_t)3);
     a.tr_mis = (uint32_t)((uintptr_t)tr & 3);
+    a.tr_last = F == NVFP4_DIV ? (uint32_t)((a.tr_mis + 4ull * L.ndiv - 1) >> 2) : 0u;
+    a.ndiv = F == NVFP4_DIV ? L.ndiv : 0u;
+    a.u0 = b0 * (block_values(F) / 8);
+    a.gu = F == NVFP4_DIV ? L.gu : 1u;
     a.nunits = (uint32_t)(nb * (block_values(F) / 8));
     a.out = (uint8_t *)L.out + b0 * (uint64_t)block_values(F) * OSZ;
     const uint64_t per_wg = (uint64_t)WG * UPT;

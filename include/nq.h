@@ -38,7 +38,8 @@ typedef enum {
     NQ_ERR_LENGTH_MISMATCH = 6,   /* nbytes differs from the length rule */
     NQ_ERR_OVERFLOW = 7,          /* byte count, or element count * 8, beyond INT64_MAX */
     NQ_ERR_BAD_DTYPE = 8,         /* out_dtype not one of nq_dtype */
-    NQ_ERR_HIP = 9                /* the HIP runtime reported an error at launch */
+    NQ_ERR_HIP = 9,               /* the HIP runtime reported an error at launch */
+    NQ_ERR_BAD_DIVISORS = 10      /* stacked nvfp4: divisors < 1, above 2^30, or not dividing the rows */
 } nq_status;
 
 /* Output types: the page's FLOAT, FLOAT16, BFLOAT16 and DOUBLE. */
@@ -110,6 +111,32 @@ int nq_validate(int32_t format, uint64_t nbytes, const int64_t *shape, int32_t r
  * words decode deterministically by the same formula. */
 int nq_dequantize_packed(int32_t format, const void *payload, uint64_t nbytes, const int64_t *shape,
                          int32_t rank, int32_t out_dtype, void *out, hipStream_t stream);
+
+/* "nvfp4" planes stacked from several source matrices (NInfer
+ * "tensor-formats" page, section 3.3): such a plane carries one binary32
+ * weight divisor per source.  With N = prod(shape[:-1]) rows, source j covers
+ * the N / divisors consecutive rows from row j * (N / divisors) on, and
+ * every value of row n is e2m1(c) * e4m3fn(s) / d_w[floor(n / (N / divisors))]
+ * (one correctly rounded binary32 division).
+ *
+ * Layout (the page leaves the placement of the divisors open): the
+ * gguf:nvfp4 blocks of all rows, then `divisors` little-endian binary32
+ * words in stacking order; divisors == 1 is exactly the "nvfp4" format.
+ * Length rule: nbytes == N * (shape[-1] / 64) * 36 + 4 * divisors.
+ *
+ * nq_validate_nvfp4_stacked checks, in this order: out_dtype, rank >= 1,
+ * shape != NULL, dimensions >= 0, shape[-1] % 64 == 0, 1 <= divisors <= 2^30
+ * (NQ_ERR_BAD_DIVISORS), the counts (NQ_ERR_OVERFLOW as nq_validate), N %
+ * divisors == 0 (NQ_ERR_BAD_DIVISORS; N may be 0), then nbytes; on success it
+ * stores the element and output byte counts (either pointer may be NULL).
+ * nq_dequantize_nvfp4_stacked validates the same way, then behaves as
+ * nq_dequantize_packed for "nvfp4": asynchronous on `stream`, nothing
+ * launched for an empty tensor, the same pointer and alignment rules, the
+ * same ownership (the caller's buffers are neither retained nor freed). */
+int nq_validate_nvfp4_stacked(uint64_t nbytes, const int64_t *shape, int32_t rank, int64_t divisors,
+                              int32_t out_dtype, uint64_t *out_elems, uint64_t *out_bytes);
+int nq_dequantize_nvfp4_stacked(const void *payload, uint64_t nbytes, const int64_t *shape, int32_t rank,
+                                int64_t divisors, int32_t out_dtype, void *out, hipStream_t stream);
 
 /* Static description of a status code. */
 const char *nq_status_string(int status);

@@ -55,15 +55,27 @@ long run_chunk(const nq::LaunchArgs &L, uint64_t b0, uint64_t nb, const uint8_t 
     std::vector<uint64_t> t8(TS::n8 > 0 ? TS::n8 : 1);
     std::vector<uint32_t> t4(TS::n4 > 0 ? TS::n4 : 1);
     std::vector<float> nvq(TS::nf > 0 ? TS::nf : 1);
+    std::vector<float> nvd(TS::nd > 0 ? TS::nd : 1);
     uint32_t grid;
     const KArgs a = chunk_args<F, OT, UPT>(L, b0, nb, &grid);
     Check chk{(uintptr_t)(payload + b0 * S), (uintptr_t)(payload + (b0 + nb) * S), 0, {0}};
-    Check chk_tr{(uintptr_t)(payload + nbytes - 4), (uintptr_t)(payload + nbytes), 0, {0}};
-    if (TS::n8 + TS::n4 + TS::nf > 0)
-        for (uint32_t tid = 0; tid < (uint32_t)WG; tid++)
-            fill_tables<F>(t8.data(), t4.data(), nvq.data(), HostSrc{a.tr_base, (a.tr_mis + 3u) >> 2, &chk_tr},
-                           a.tr_mis, tid, WG);
-    const Tab tab{t8.data(), t4.data(), nvq.data()};
+    Check chk_tr{(uintptr_t)(payload + nbytes - 4ull * L.ndiv), (uintptr_t)(payload + nbytes), 0, {0}};
+    const HostSrc tr{a.tr_base, a.tr_last, &chk_tr};
+    // per tile (the kernel's prologue): the divisor group of the tile's first
+    // unit, and the tables; stale divisor slots are poisoned
+    auto setup = [&](uint32_t t, Tab &tab) {
+        uint32_t g0 = 0;
+        tab = Tab{t8.data(), t4.data(), nvq.data(), nvd.data(), 0xFFFFFFFFu, 1u};
+        if constexpr (F == NVFP4_DIV) {
+            g0 = nv_first_group<UPT>(a, t, &tab.nv_bound);
+            tab.nv_gu = a.gu < 0x7FFFFFFFull ? (uint32_t)a.gu : 0x7FFFFFFFu;
+            std::fill(nvd.begin(), nvd.end(), bits_f32(0x7FA5A5A5u));
+        }
+        if (TS::n8 + TS::n4 + TS::nf > 0)
+            for (uint32_t tid = 0; tid < (uint32_t)WG; tid++)
+                fill_tables<F>(t8.data(), t4.data(), nvq.data(), nvd.data(), tr, a, g0, tid, WG);
+    };
+    Tab tab{};
     const HostSrc src{a.base, a.last, &chk};
     const bool vec = ((uintptr_t)a.out & 15) == 0;
     // the LDS slot plus guard words that staging must leave alone
@@ -76,6 +88,7 @@ long run_chunk(const nq::LaunchArgs &L, uint64_t b0, uint64_t nb, const uint8_t 
         return 1;
     }
     for (uint32_t t = 0; t < grid; t++) {
+        setup(t, tab);
         if (t < nst) {
             std::fill(slot.begin(), slot.begin() + ST::SLOT_DW, 0xA5A5A5A5u);  // stale words poison the result
             std::fill(slot.begin() + ST::SLOT_DW, slot.end(), GUARD_WORD);
@@ -116,9 +129,10 @@ long run_chunk(const nq::LaunchArgs &L, uint64_t b0, uint64_t nb, const uint8_t 
 // (force_upt > 0 overrides the choice for aligned outputs).
 template <int F, int OT>
 long run(const uint8_t *payload, uint64_t nbytes, uint64_t nblocks, void *out, uint32_t max_wgs,
-         uint64_t chunk, int force_upt, char *err, int errlen) {
+         uint64_t chunk, int force_upt, uint32_t ndiv, char *err, int errlen) {
     using namespace nq;
-    LaunchArgs L{payload, nbytes, nblocks, out, max_wgs};
+    const uint64_t units = nblocks * (block_values(F) / 8);
+    LaunchArgs L{payload, nbytes, nblocks, out, max_wgs, ndiv, units / ndiv ? units / ndiv : 1};
     const uint64_t CB = chunk ? chunk : chunk_blocks<F>();
     constexpr uint64_t OSZ = OT == 0 ? 4 : OT == 3 ? 8 : 2;
     long errors = 0;
@@ -144,12 +158,12 @@ long run(const uint8_t *payload, uint64_t nbytes, uint64_t nblocks, void *out, u
 
 template <int F>
 long run_ot(int ot, const uint8_t *p, uint64_t nbytes, uint64_t nblocks, void *out, uint32_t mw, uint64_t ch,
-            int fu, char *err, int errlen) {
+            int fu, uint32_t nd, char *err, int errlen) {
     switch (ot) {
-    case 0: return run<F, 0>(p, nbytes, nblocks, out, mw, ch, fu, err, errlen);
-    case 1: return run<F, 1>(p, nbytes, nblocks, out, mw, ch, fu, err, errlen);
-    case 2: return run<F, 2>(p, nbytes, nblocks, out, mw, ch, fu, err, errlen);
-    default: return run<F, 3>(p, nbytes, nblocks, out, mw, ch, fu, err, errlen);
+    case 0: return run<F, 0>(p, nbytes, nblocks, out, mw, ch, fu, nd, err, errlen);
+    case 1: return run<F, 1>(p, nbytes, nblocks, out, mw, ch, fu, nd, err, errlen);
+    case 2: return run<F, 2>(p, nbytes, nblocks, out, mw, ch, fu, nd, err, errlen);
+    default: return run<F, 3>(p, nbytes, nblocks, out, mw, ch, fu, nd, err, errlen);
     }
 }
 
@@ -169,14 +183,17 @@ long tile_blocks(int upt) {
 }  // namespace
 
 // Returns the number of out-of-payload reads (0 on success), or -1 for a bad format.
+// ndiv: "nvfp4" divisor words after the blocks (stacked sources), 1 otherwise.
 extern "C" __attribute__((visibility("default"))) long nq_emu_decode(int fmt, int ot, const uint8_t *payload,
                                                                     uint64_t nbytes, uint64_t nblocks, void *out,
                                                                     uint32_t max_wgs, uint64_t chunk_blocks,
-                                                                    int force_upt, char *err, int errlen) {
+                                                                    int force_upt, uint32_t ndiv, char *err,
+                                                                    int errlen) {
     using namespace nq;
+    if (ndiv < 1) ndiv = 1;
     switch (fmt) {
 #define C(X) \
-    case X: return run_ot<X>(ot, payload, nbytes, nblocks, out, max_wgs, chunk_blocks, force_upt, err, errlen);
+    case X: return run_ot<X>(ot, payload, nbytes, nblocks, out, max_wgs, chunk_blocks, force_upt, ndiv, err, errlen);
         C(Q4_0) C(Q4_1) C(Q5_0) C(Q5_1) C(Q8_0) C(Q8_1) C(Q2_K) C(Q3_K) C(Q4_K) C(Q5_K) C(Q6_K) C(Q8_K)
         C(IQ2_XXS) C(IQ2_XS) C(IQ3_XXS) C(IQ1_S) C(IQ4_NL) C(IQ3_S) C(IQ2_S) C(IQ4_XS) C(IQ1_M)
         C(TQ1_0) C(TQ2_0) C(MXFP4) C(NVFP4_GGUF) C(Q1_0) C(Q2_0) C(NVFP4_DIV)

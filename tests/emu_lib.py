@@ -36,7 +36,7 @@ def lib():
         L = ctypes.CDLL(LIB)
         L.nq_emu_decode.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64,
                                     ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64,
-                                    ctypes.c_int, ctypes.c_char_p, ctypes.c_int]
+                                    ctypes.c_int, ctypes.c_uint32, ctypes.c_char_p, ctypes.c_int]
         L.nq_emu_decode.restype = ctypes.c_long
         L.nq_emu_tile_blocks.argtypes = [ctypes.c_int, ctypes.c_int]
         L.nq_emu_choose_upt.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint32]
@@ -54,7 +54,7 @@ def _placed(nbytes, align, mis, slack=64):
     return buf, off
 
 
-def decode(fmt_id, payload, nblocks, B, dtype, mis=0, out_mis=0, max_wgs=2048, chunk=0, upt=0):
+def decode(fmt_id, payload, nblocks, B, dtype, mis=0, out_mis=0, max_wgs=2048, chunk=0, upt=0, ndiv=1):
     """Run the emulator; returns (values, out-of-payload reads, message, guards_ok)."""
     payload = np.ascontiguousarray(payload, dtype=np.uint8)
     pbuf, poff = _placed(payload.size, 4, mis)
@@ -67,7 +67,7 @@ def decode(fmt_id, payload, nblocks, B, dtype, mis=0, out_mis=0, max_wgs=2048, c
     err = ctypes.create_string_buffer(256)
     rc = lib().nq_emu_decode(fmt_id, {"f32": 0, "f16": 1, "bf16": 2, "f64": 3}[dtype],
                              pbuf.ctypes.data + poff, payload.size, nblocks,
-                             obuf.ctypes.data + ooff, max_wgs, chunk, upt, err, 256)
+                             obuf.ctypes.data + ooff, max_wgs, chunk, upt, ndiv, err, 256)
     guards = bool(np.all(obuf[:ooff] == 0xA5) and np.all(obuf[ooff + n * osz:] == 0xA5))
     vals = obuf[ooff:ooff + n * osz].copy().view(NPT[dtype])
     return vals, rc, err.value.decode(), guards

@@ -104,6 +104,50 @@ def test_dequantize_rejects_bad_metadata_without_device():
 
 
 def test_status_strings():
-    for st in range(10):
-        assert nq.library().nq_status_string(st)
+    for st in range(11):
+        assert nq.library().nq_status_string(st) != b"unknown status"
     assert nq.library().nq_status_string(12345) == b"unknown status"
+
+
+STACKED_CASES = [([12, 128], 1), ([12, 128], 2), ([12, 128], 3), ([12, 128], 4), ([12, 128], 5), ([12, 128], 12),
+                 ([12, 128], 0), ([12, 128], -2), ([6, 0], 3), ([6, 0], 4), ([0, 128], 7), ([128], 1), ([128], 2),
+                 ([12, 100], 2), ([3, 4, 64], 4), ([3, 4, 64], 8), ([12, 128], 1 << 30), ([12, 128], (1 << 30) + 1),
+                 ([2 ** 40, 2 ** 40, 0], 1), ([-1, 64], 1), ([], 1)]
+
+
+@pytest.mark.parametrize("shape,divisors", STACKED_CASES)
+def test_nvfp4_stacked_length_rule_agrees_with_oracle(shape, divisors):
+    ostatus = {oracle.OK: 0, oracle.ERR_RANK: 3, oracle.ERR_DIM: 4, oracle.ERR_ALIGN: 5, oracle.ERR_OVERFLOW: 7,
+               oracle.ERR_DIVISORS: 10}
+    st, nbytes, nelems = oracle.sizes_nvfp4_stacked(shape, divisors)
+    want = ostatus[st]
+    if want == 0 and divisors > (1 << 30):
+        want = 10  # the library's own limit on the number of divisors
+    got, ne, ob = nq.validate_nvfp4_stacked_status(nbytes if st == oracle.OK else 0, shape, divisors, "bf16")
+    assert got == want, (shape, divisors, got, want)
+    if got == 0:
+        assert ne == nelems and ob == 2 * nelems
+        for delta in (-4, -1, 1, 4):
+            if nbytes + delta >= 0:
+                assert nq.validate_nvfp4_stacked_status(nbytes + delta, shape, divisors)[0] == 6
+
+
+def test_nvfp4_stacked_one_divisor_matches_plain_nvfp4_rule():
+    for shape in ([12, 128], [0, 64], [3, 4, 64], [64]):
+        st, nbytes, ne = oracle.sizes("nvfp4", shape)
+        assert nq.validate_nvfp4_stacked_status(nbytes, shape, 1)[:2] == (0, ne)
+        assert nq.validate_status("nvfp4", nbytes, shape)[:2] == (0, ne)
+
+
+def test_nvfp4_stacked_rejects_before_device():
+    buf = np.zeros(1024, dtype=np.uint8)
+    p = buf.ctypes.data
+    assert nq.dequantize_nvfp4_stacked_raw(p, 12 * 2 * 36 + 8, [12, 128], 3, 2, p, 0) == 6
+    assert nq.dequantize_nvfp4_stacked_raw(p, 12 * 2 * 36 + 20, [12, 128], 5, 2, p, 0) == 10
+    assert nq.dequantize_nvfp4_stacked_raw(p, 12 * 2 * 36 + 8, [12, 128], 2, 7, p, 0) == 8
+    assert nq.dequantize_nvfp4_stacked_raw(0, 12 * 2 * 36 + 8, [12, 128], 2, 2, p, 0) == 1
+    assert nq.dequantize_nvfp4_stacked_raw(p, 12 * 2 * 36 + 8, [12, 128], 2, 2, 0, 0) == 1
+    assert nq.dequantize_nvfp4_stacked_raw(p, 12 * 2 * 36 + 8, [12, 128], 2, 2, p + 1, 0) == 1
+    # empty planes succeed without launching (null pointers allowed when nothing is read or written)
+    assert nq.dequantize_nvfp4_stacked_raw(p, 12, [6, 0], 3, 2, 0, 0) == 0
+    assert nq.dequantize_nvfp4_stacked_raw(0, 0, [6, 0], 3, 2, 0, 0) == 6

@@ -133,3 +133,21 @@ def test_emulated_nvfp4_divisor(d_w):
     got, bad, msg, guards = emu_lib.decode(info.id, p, 40, 64, "f32", mis=2)
     assert bad == 0 and guards, msg
     assert _same(got, _oracle("nvfp4", p, 40, 64, "f32"), "f32")
+
+
+@pytest.mark.parametrize("upt", [0, 1, 2, 8, 16])
+@pytest.mark.parametrize("rows,K,divisors", [(24, 128, 1), (24, 128, 2), (24, 128, 3), (24, 128, 24),
+                                             (40, 64, 40), (40, 64, 8), (6, 4096, 3), (96, 512, 4)])
+def test_emulated_nvfp4_stacked_divisors(rows, K, divisors, upt):
+    """Planes stacked from several sources: tiles that start in one divisor
+    group and reach others (down to one-row groups of 8 units), at every
+    payload alignment, against the oracle."""
+    nb = rows * K // 64
+    p = synth.payload("nvfp4", nb, 900 + divisors, RECIPE, divisors=divisors)
+    ref = oracle.decode_nvfp4_stacked(p, [rows, K], divisors, "f32")
+    fid = nq.format_query("nvfp4").id
+    for mis in range(4):
+        got, bad, msg, guards = emu_lib.decode(fid, p, nb, 64, "f32", mis=mis, upt=upt, ndiv=divisors)
+        assert bad == 0, (mis, msg)
+        assert guards
+        assert _same(got, ref, "f32"), (mis, divisors)

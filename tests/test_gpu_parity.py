@@ -261,3 +261,44 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         for fmt, _, _, n, ref, out, _ in items:
             assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), (fmt, r)
+
+
+# ---------------------------------------------------------------------------
+# nvfp4 planes stacked from several sources (one divisor per source).
+# ---------------------------------------------------------------------------
+def _stacked_check(shape, divisors, dtype, seed, pay_off=0, d_ws=None):
+    N = int(np.prod(shape[:-1])) if len(shape) > 1 else 1
+    nb = N * shape[-1] // 64
+    p = synth.payload("nvfp4", nb, seed, workloads.recipe_for("nvfp4"), divisor=d_ws, divisors=divisors)
+    payload, _keep = upload(p, pay_off)
+    out = nq.dequantize_nvfp4_stacked(payload, shape, divisors, TORCH_DT[dtype])
+    torch.cuda.synchronize()
+    got = to_numpy(out.reshape(-1), dtype)
+    ref = oracle.decode_nvfp4_stacked(p, shape, divisors, dtype)
+    assert compare.same(got, ref, dtype), f"{shape} D={divisors} {dtype} off={pay_off}: {compare.describe(got, ref, dtype)}"
+
+
+@pytest.mark.parametrize("shape,divisors", [([24, 128], 1), ([24, 128], 2), ([24, 128], 3), ([24, 128], 24),
+                                            ([40, 64], 40), ([40, 64], 8), ([6, 4096], 3), ([96, 512], 4),
+                                            ([3, 8, 1024], 6), ([4100, 64], 4100), ([2050, 128], 5)])
+def test_nvfp4_stacked_divisors(shape, divisors):
+    for dtype in ("f32", "bf16", "f16", "f64"):
+        for off in (0, 1, 2, 3):
+            announce(f"nvfp4_stacked {shape} D={divisors} {dtype} off={off}")
+            _stacked_check(shape, divisors, dtype, 70 + divisors, pay_off=off)
+
+
+def test_nvfp4_stacked_full_size_sources():
+    """Stacked gate/up and q/k/v-like planes at Llama-3-8B sizes, compared in full."""
+    for shape, divisors in (([2 * 14336, 4096], 2), ([3 * 4096, 4096], 3), ([8 * 1024, 4096], 8)):
+        announce(f"nvfp4_stacked full size {shape} D={divisors}")
+        _stacked_check(shape, divisors, "bf16", 5 + divisors)
+
+
+def test_nvfp4_stacked_one_divisor_is_plain_nvfp4():
+    p = synth.payload("nvfp4", 4000, 17, workloads.recipe_for("nvfp4"))
+    payload, _keep = upload(p)
+    a = nq.dequantize_nvfp4_stacked(payload, [1000, 256], 1, torch.bfloat16)
+    b = nq.dequantize_packed("nvfp4", payload, [1000, 256], torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
