@@ -48,6 +48,11 @@ def lib():
         L.nqo_decode.argtypes = [c.c_int, c.c_void_p, c.c_uint64, c.POINTER(c.c_int64), c.c_int,
                                  c.c_int, c.c_void_p]
         L.nqo_decode_blocks_f32.argtypes = [c.c_int, c.c_void_p, c.c_uint64, c.c_float, c.c_void_p]
+        L.nqo_sizes_fp8_row.argtypes = [c.POINTER(c.c_int64), c.c_int, c.POINTER(c.c_uint64), c.POINTER(c.c_uint64)]
+        L.nqo_decode_fp8_row.argtypes = [c.c_int, c.c_void_p, c.c_uint64, c.POINTER(c.c_int64), c.c_int, c.c_int,
+                                         c.c_void_p]
+        L.nqo_bf16_to_f32.argtypes = [c.c_uint16]
+        L.nqo_bf16_to_f32.restype = c.c_float
         L.nqo_sizes_nvfp4_stacked.argtypes = [c.POINTER(c.c_int64), c.c_int, c.c_int64, c.POINTER(c.c_uint64),
                                               c.POINTER(c.c_uint64)]
         L.nqo_decode_nvfp4_stacked.argtypes = [c.c_void_p, c.c_uint64, c.POINTER(c.c_int64), c.c_int, c.c_int64,
@@ -151,6 +156,36 @@ def decode_nvfp4_stacked(payload, shape, divisors, dtype="f32"):
     if st != OK:
         raise ValueError(f"oracle decode of nvfp4 {shape} divisors={divisors} failed: status {st}")
     return out
+
+
+FP8_ROW_KINDS = {"fp8_e4m3fn_row_bf16": 0, "fp8_e4m3fn_row_fp16": 1}
+
+
+def sizes_fp8_row(shape):
+    """(status, nbytes, nelems) of the row-scaled FP8 length rule."""
+    arr, rank = _shape_arg(shape)
+    nb, ne = ctypes.c_uint64(), ctypes.c_uint64()
+    st = lib().nqo_sizes_fp8_row(arr, rank, ctypes.byref(nb), ctypes.byref(ne))
+    return st, nb.value, ne.value
+
+
+def decode_fp8_row(fmt, payload, shape, dtype="f32"):
+    """Decode a row-scaled FP8 matrix (flat array, raw 16-bit words for f16/bf16)."""
+    payload = np.ascontiguousarray(payload, dtype=np.uint8)
+    st, nbytes, nelems = sizes_fp8_row(shape)
+    if st != OK:
+        raise ValueError(f"oracle length rule rejects {fmt} {shape}: status {st}")
+    out = np.empty(nelems, dtype=_NP_OUT[dtype])
+    arr, rank = _shape_arg(shape)
+    st = lib().nqo_decode_fp8_row(FP8_ROW_KINDS[fmt], payload.ctypes.data, payload.size, arr, rank, DTYPES[dtype],
+                                  out.ctypes.data)
+    if st != OK:
+        raise ValueError(f"oracle decode of {fmt} {shape} failed: status {st}")
+    return out
+
+
+def bf16_to_f32(w):
+    return lib().nqo_bf16_to_f32(w)
 
 
 def decode_blocks_f32(fmt, blocks, d_w=0.0):

@@ -193,6 +193,22 @@ float nqo_e4m3fn_to_f32(uint8_t w)
     return sign ? -mag : mag;
 }
 
+/* bfloat16 word -> binary32 from its value classes (NInfer tensor-formats  */
+/* 3.1): sign bit 15, 8-bit exponent (bias 127), 7-bit fraction; exponent 0  */
+/* holds zeros and subnormals f * 2^-133, exponent 255 infinities and NaNs.  */
+float nqo_bf16_to_f32(uint16_t w)
+{
+    const int sign = w >> 15, e = (w >> 7) & 255, f = w & 127;
+    float mag;
+    if (e == 0)
+        mag = ldexpf((float)f, -133);
+    else if (e == 255)
+        mag = f ? NAN : INFINITY;
+    else
+        mag = ldexpf(1.0f + (float)f / 128.0f, e - 127);
+    return sign ? -mag : mag;
+}
+
 void nqo_convert(const float *x, uint64_t n, int dtype, void *out)
 {
     for (uint64_t i = 0; i < n; i++) {
@@ -764,6 +780,47 @@ int nqo_decode_nvfp4_stacked(const uint8_t *payload, uint64_t nbytes, const int6
             const uint64_t i = n * blocks_per_row + b;
             dec_nvfp4_div(payload + i * 36, d_w, y);
             nqo_convert(y, 64, dtype, (uint8_t *)out + i * 64 * (uint64_t)OSIZE[dtype]);
+        }
+    }
+    return NQO_OK;
+}
+
+/* Row-scaled FP8 (NInfer tensor-formats 3.3): w_hat[n,k] = binary32(c32 *   */
+/* s32) with c32 the exact E4M3FN value of code c[n,k] and s32 the exact     */
+/* binary32 value of row n's bfloat16 (kind 0) or binary16 (kind 1) scale.   */
+int nqo_sizes_fp8_row(const int64_t *shape, int rank, uint64_t *nbytes, uint64_t *nelems)
+{
+    if (rank != 2 || !shape) return NQO_ERR_RANK;
+    if (shape[0] <= 0 || shape[1] <= 0) return NQO_ERR_DIM; /* positive dimensions */
+    uint64_t elems, out_bytes, scale_bytes, bytes;
+    if (!mul_ok((uint64_t)shape[0], (uint64_t)shape[1], &elems)) return NQO_ERR_OVERFLOW;
+    if (!mul_ok(elems, 8, &out_bytes)) return NQO_ERR_OVERFLOW;
+    if (!mul_ok((uint64_t)shape[0], 2, &scale_bytes)) return NQO_ERR_OVERFLOW;
+    bytes = elems + scale_bytes;
+    if (bytes < elems || bytes > (uint64_t)INT64_MAX) return NQO_ERR_OVERFLOW;
+    if (nbytes) *nbytes = bytes;
+    if (nelems) *nelems = elems;
+    return NQO_OK;
+}
+
+int nqo_decode_fp8_row(int scale_kind, const uint8_t *payload, uint64_t nbytes, const int64_t *shape,
+                       int rank, int dtype, void *out)
+{
+    if (scale_kind != 0 && scale_kind != 1) return NQO_ERR_FORMAT;
+    if (dtype < NQO_F32 || dtype > NQO_F64) return NQO_ERR_DTYPE;
+    uint64_t need = 0, nelems = 0;
+    const int st = nqo_sizes_fp8_row(shape, rank, &need, &nelems);
+    if (st != NQO_OK) return st;
+    if (need != nbytes) return NQO_ERR_LENGTH;
+    const uint64_t N = (uint64_t)shape[0], K = (uint64_t)shape[1];
+    const uint8_t *scales = payload + N * K;
+    static const int OSIZE[4] = {4, 2, 2, 8};
+    for (uint64_t n = 0; n < N; n++) {
+        const uint16_t sw = (uint16_t)U(scales + 2 * n, 2);
+        const float s32 = scale_kind == 0 ? nqo_bf16_to_f32(sw) : nqo_f16_to_f32(sw);
+        for (uint64_t k = 0; k < K; k++) {
+            const float w = M(nqo_e4m3fn_to_f32(payload[n * K + k]), s32);
+            nqo_convert(&w, 1, dtype, (uint8_t *)out + (n * K + k) * (uint64_t)OSIZE[dtype]);
         }
     }
     return NQO_OK;

@@ -69,6 +69,17 @@ int nqo_sizes_nvfp4_stacked(const int64_t *shape, int rank, int64_t divisors, ui
 int nqo_decode_nvfp4_stacked(const uint8_t *payload, uint64_t nbytes, const int64_t *shape, int rank,
                              int64_t divisors, int dtype, void *out);
 
+/* Row-scaled FP8 (NInfer tensor-formats section 3.3): fp8_e4m3fn_row_bf16
+ * (scale_kind 0) and fp8_e4m3fn_row_fp16 (scale_kind 1).  A rank-two [N, K]
+ * matrix with positive dimensions; every weight is one E4M3FN code word and
+ * every row one bfloat16 / binary16 multiplier; the value is the binary32
+ * product code * scale.  Bytes (the page leaves the layout to an undefined
+ * layout registry): the N*K codes row-major, then the N scale words,
+ * little-endian 16-bit, in row order.  nbytes = N*K + 2*N. */
+int nqo_sizes_fp8_row(const int64_t *shape, int rank, uint64_t *nbytes, uint64_t *nelems);
+int nqo_decode_fp8_row(int scale_kind, const uint8_t *payload, uint64_t nbytes, const int64_t *shape,
+                       int rank, int dtype, void *out);
+
 /* Decode `nblocks` back-to-back blocks to binary32 (no trailer; `d_w` is the
  * divisor used by "nvfp4" and ignored by every other format). */
 int nqo_decode_blocks_f32(int fmt, const uint8_t *blocks, uint64_t nblocks, float d_w, float *y);
@@ -78,6 +89,7 @@ float nqo_f16_to_f32(uint16_t h);
 uint16_t nqo_f32_to_bf16(float x);
 uint16_t nqo_f32_to_f16(float x);
 float nqo_e4m3fn_to_f32(uint8_t w);
+float nqo_bf16_to_f32(uint16_t w);
 void nqo_convert(const float *x, uint64_t n, int dtype, void *out);
 
 /* Expanded IQ codebooks: book 0..5 = iq2xxs, iq2xs, iq2s, iq3xxs, iq3s, iq1s. */

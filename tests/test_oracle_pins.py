@@ -536,3 +536,94 @@ def test_nvfp4_stacked_length_rule(shape, divisors, want):
         assert len(oracle.decode_nvfp4_stacked(p, shape, divisors)) == nelems
         with pytest.raises(ValueError):
             oracle.decode_nvfp4_stacked(np.zeros(nbytes + 1, dtype=np.uint8), shape, divisors)
+
+
+# ---------------------------------------------------------------------------
+# Row-scaled FP8 (NInfer tensor-formats, section 3.3): w_hat = binary32(c32 * s32).
+# ---------------------------------------------------------------------------
+def test_bf16_words_against_torch():
+    """Every bfloat16 word against torch's conversion (NaN by class)."""
+    w = np.arange(1 << 16, dtype=np.uint32)
+    ref = torch.from_numpy(w.astype(np.int32)).to(torch.int16).view(torch.bfloat16).to(torch.float32).numpy()
+    got = np.array([oracle.bf16_to_f32(int(x)) for x in w], dtype=np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    assert np.array_equal(np.signbit(got[nan]), np.signbit(ref[nan]))
+
+
+def _fp8_payload(codes, scale_words):
+    return np.concatenate([np.asarray(codes, np.uint8).ravel(), np.asarray(scale_words, "<u2").view(np.uint8)])
+
+
+@pytest.mark.parametrize("fmt", ["fp8_e4m3fn_row_bf16", "fp8_e4m3fn_row_fp16"])
+def test_fp8_row_every_code_against_binary64(fmt):
+    """All 256 codes times scale words of every class: each value is the
+    binary64 product (exact: at most 4 x 11 significant bits) rounded once to
+    binary32, as torch computes it from its own float8/bfloat16/float16."""
+    scales = ([0x3F80, 0x4000, 0x0001, 0x007F, 0x0080, 0x7F7F, 0x7F80, 0xFF80, 0x8000, 0x0000, 0x7FC1, 0xC2F7, 0x3E2B]
+              if fmt.endswith("bf16") else
+              [0x3C00, 0x4000, 0x0001, 0x03FF, 0x0400, 0x7BFF, 0x7C00, 0xFC00, 0x8000, 0x0000, 0x7E01, 0xC8F7, 0x3555])
+    N, K = len(scales), 256
+    codes = np.tile(np.arange(256, dtype=np.uint8), (N, 1))
+    y = oracle.decode_fp8_row(fmt, _fp8_payload(codes, scales), [N, K], "f32").reshape(N, K)
+    c64 = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    sdt = torch.bfloat16 if fmt.endswith("bf16") else torch.float16
+    s64 = torch.tensor(scales, dtype=torch.int32).to(torch.int16).view(sdt).to(torch.float64).numpy()
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref = (s64[:, None] * c64[None, :]).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(y), nan)
+    assert np.array_equal(y[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_fp8_row_golden_examples():
+    path = os.path.join(os.path.dirname(__file__), "golden", "fp8_row.json")
+    for ex in json.load(open(path))["examples"]:
+        p = np.frombuffer(bytes.fromhex(ex["payload"]), np.uint8)
+        y = oracle.decode_fp8_row(ex["format"], p, ex["shape"], "f32")
+        assert y.size == len(ex["expect"]), ex["id"]
+        for v, want in zip(y, ex["expect"]):
+            if want == "nan":
+                assert np.isnan(v), ex["id"]
+            elif isinstance(want, str):
+                assert int(np.array(v, np.float32).view(np.uint32)) == int(want, 16), (ex["id"], v, want)
+            else:
+                assert np.array(v, np.float32).view(np.uint32) == np.array(want, np.float32).view(np.uint32), \
+                    (ex["id"], v, want)
+
+
+def test_fp8_row_structure():
+    """A code word changes only its own output; a scale word only its row."""
+    N, K = 5, 37
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    codes[codes & 0x7F == 0x7F] = 0x11  # keep NaN words out
+    scales = np.array([0x3F80, 0x4040, 0x3E00, 0x4300, 0x3C23], np.uint16)
+    base = oracle.decode_fp8_row("fp8_e4m3fn_row_bf16", _fp8_payload(codes, scales), [N, K], "f32").reshape(N, K)
+    for (n, k) in [(0, 0), (2, 17), (4, 36)]:
+        c2 = codes.copy()
+        c2[n, k] ^= 0x41
+        y = oracle.decode_fp8_row("fp8_e4m3fn_row_bf16", _fp8_payload(c2, scales), [N, K], "f32").reshape(N, K)
+        diff = np.argwhere(y.view(np.uint32) != base.view(np.uint32))
+        assert [tuple(d) for d in diff] == [(n, k)]
+    for n in range(N):
+        s2 = scales.copy()
+        s2[n] ^= 0x0080
+        y = oracle.decode_fp8_row("fp8_e4m3fn_row_bf16", _fp8_payload(codes, s2), [N, K], "f32").reshape(N, K)
+        rows = set(np.argwhere(y.view(np.uint32) != base.view(np.uint32))[:, 0])
+        assert rows == {n}
+
+
+@pytest.mark.parametrize("shape,want", [([3, 5], "OK"), ([1, 1], "OK"), ([0, 5], "ERR_DIM"), ([3, 0], "ERR_DIM"),
+                                        ([-1, 5], "ERR_DIM"), ([15], "ERR_RANK"), ([1, 3, 5], "ERR_RANK"),
+                                        ([], "ERR_RANK"), ([2 ** 62, 4], "ERR_OVERFLOW"),
+                                        ([2 ** 31, 2 ** 31], "ERR_OVERFLOW")])
+def test_fp8_row_length_rule(shape, want):
+    """Rank two, positive dimensions, nbytes = N*K + 2N (and N*K*8 within INT64)."""
+    st, nbytes, nelems = oracle.sizes_fp8_row(shape)
+    assert st == getattr(oracle, want), st
+    if st == oracle.OK:
+        assert nbytes == shape[0] * shape[1] + 2 * shape[0] and nelems == shape[0] * shape[1]
+        with pytest.raises(ValueError):
+            oracle.decode_fp8_row("fp8_e4m3fn_row_bf16", np.zeros(nbytes - 1, np.uint8), shape)
