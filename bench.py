@@ -203,6 +203,43 @@ def rotating_measurement(torch, nq, synth, name, fmt, shape, recipe, seed, dtype
     return res
 
 
+def fp8_row_measurement(torch, nq, fmt, shape, dtype, launches=60, footprint=1 << 30, seed=0x6E7F8000):
+    """Row-scaled FP8 decode over rotating replicas: random code words with the
+    NaN words replaced, positive normal scale words ([2^-9, 2^-5) for bfloat16,
+    [2^-8, 2^-4) for binary16)."""
+    import numpy as np
+    N, K = shape
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, size=N * K, dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] ^= 0x01
+    lo, hi = (0x3B00, 0x3D00) if fmt.endswith("bf16") else (0x1C00, 0x2C00)
+    scales = rng.integers(lo, hi, size=N).astype("<u2")
+    host = torch.from_numpy(np.concatenate([codes, scales.view(np.uint8)]))
+    nbytes = host.numel()
+    out_bytes = N * K * OUT_SIZE[dtype]
+    reps = max(1, math.ceil(footprint / (nbytes + out_bytes)))
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "f64": torch.float64}[dtype]
+    items = [(host.to("cuda:0"), torch.empty(N * K, dtype=tdt, device="cuda:0")) for _ in range(reps)]
+    kind = nq.FP8_ROW_KINDS[fmt]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        h = torch.cuda.current_stream().cuda_stream
+        for i in range(launches):
+            p, o = items[i % reps]
+            st = nq.dequantize_fp8_row_raw(kind, p.data_ptr(), nbytes, shape, OUT_CODES[dtype], o.data_ptr(), h)
+            if st != 0:
+                raise nq.NqError(st, fmt)
+    ms, _ = time_graph(torch, g, 3)
+    mean_ms = ms / launches
+    gbps = (nbytes + out_bytes) / (mean_ms * 1e-3) / 1e9
+    res = {"shape": shape, "out": dtype, "gbps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+           "mean_launch_us": round(mean_ms * 1e3, 3), "replicas": reps,
+           "elements_per_s": round(N * K / (mean_ms * 1e-3), 1), "bytes_per_launch": nbytes + out_bytes}
+    del g, items
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(nq, synth, tensors, fraction=8):
     """The oracle on the first 1/fraction of every tensor's blocks, one thread."""
     import numpy as np
@@ -316,6 +353,10 @@ def main():
                                               0x6E710000 + 77 * nd, "bf16", st2, divisors=nd)
             log(f"{key}: {extra[key]['gbps']} GB/s ({100 * extra[key]['frac_hbm_peak']:.1f}% of peak)")
             del st2
+        for fmt in ("fp8_e4m3fn_row_bf16", "fp8_e4m3fn_row_fp16"):
+            key = f"{fmt}[14336, 4096]->bf16"
+            extra[key] = fp8_row_measurement(torch, nq, fmt, [14336, 4096], "bf16")
+            log(f"{key}: {extra[key]['gbps']} GB/s ({100 * extra[key]['frac_hbm_peak']:.1f}% of peak)")
 
     cpu = None
     if not args.no_cpu_baseline:

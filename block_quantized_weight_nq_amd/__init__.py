@@ -21,7 +21,8 @@ DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "f64": 3}
 FAMILIES = {0: "simple", 1: "kquant", 2: "iq", 3: "fp4", 4: "ternary"}
 EXPORTS = ["nq_format_count", "nq_format_by_id", "nq_format_query", "nq_validate",
            "nq_dequantize_packed", "nq_validate_nvfp4_stacked", "nq_dequantize_nvfp4_stacked",
-           "nq_status_string"]
+           "nq_validate_fp8_row", "nq_dequantize_fp8_row", "nq_status_string"]
+FP8_ROW_KINDS = {"fp8_e4m3fn_row_bf16": 0, "fp8_e4m3fn_row_fp16": 1}
 
 
 class NqError(RuntimeError):
@@ -63,6 +64,10 @@ def _lib():
                                                 c.c_int32, c.POINTER(c.c_uint64), c.POINTER(c.c_uint64)]
         L.nq_dequantize_nvfp4_stacked.argtypes = [c.c_void_p, c.c_uint64, c.POINTER(c.c_int64), c.c_int32,
                                                   c.c_int64, c.c_int32, c.c_void_p, c.c_void_p]
+        L.nq_validate_fp8_row.argtypes = [c.c_int32, c.c_uint64, c.POINTER(c.c_int64), c.c_int32, c.c_int32,
+                                          c.POINTER(c.c_uint64), c.POINTER(c.c_uint64)]
+        L.nq_dequantize_fp8_row.argtypes = [c.c_int32, c.c_void_p, c.c_uint64, c.POINTER(c.c_int64), c.c_int32,
+                                            c.c_int32, c.c_void_p, c.c_void_p]
         L.nq_status_string.argtypes = [c.c_int]
         L.nq_status_string.restype = c.c_char_p
         _LIB = L
@@ -183,6 +188,35 @@ def dequantize_nvfp4_stacked(payload, shape, divisors, out_dtype=None, out=None,
                                       out.data_ptr(), stream.cuda_stream)
     if st != NQ_OK:
         raise NqError(st, f"nvfp4 {list(shape)} divisors={divisors}")
+    return out
+
+
+def validate_fp8_row_status(fmt, nbytes, shape, out_dtype="f32"):
+    """Raw status of nq_validate_fp8_row plus (elems, out_bytes); fmt is the
+    format name or the scale kind (0 bf16 scales, 1 fp16 scales)."""
+    kind = FP8_ROW_KINDS[fmt] if isinstance(fmt, str) else int(fmt)
+    arr, rank = _shape(shape)
+    ne, nb = ctypes.c_uint64(), ctypes.c_uint64()
+    code = out_dtype if isinstance(out_dtype, int) else _dtype_code(out_dtype)
+    st = _lib().nq_validate_fp8_row(kind, nbytes, arr, rank, code, ctypes.byref(ne), ctypes.byref(nb))
+    return st, ne.value, nb.value
+
+
+def dequantize_fp8_row_raw(kind, payload_ptr, nbytes, shape, out_dtype_code, out_ptr, stream_handle):
+    """Direct call of nq_dequantize_fp8_row with integer addresses; returns the status."""
+    arr, rank = _shape(shape)
+    return _lib().nq_dequantize_fp8_row(int(kind), ctypes.c_void_p(payload_ptr), nbytes, arr, rank, out_dtype_code,
+                                        ctypes.c_void_p(out_ptr), ctypes.c_void_p(stream_handle))
+
+
+def dequantize_fp8_row(fmt, payload, shape, out_dtype=None, out=None, stream=None):
+    """Decode a row-scaled FP8 matrix ("fp8_e4m3fn_row_bf16" or "_fp16":
+    N*K codes, then N scale words) into a new (or the given) [N, K] tensor."""
+    code, out, stream = _prepare(payload, shape, out_dtype, out, stream)
+    st = dequantize_fp8_row_raw(FP8_ROW_KINDS[fmt], payload.data_ptr(), payload.numel(), shape, code,
+                                out.data_ptr(), stream.cuda_stream)
+    if st != NQ_OK:
+        raise NqError(st, f"{fmt} {list(shape)}")
     return out
 
 

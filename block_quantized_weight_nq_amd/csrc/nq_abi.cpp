@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include "../../include/nq.h"
+#include "nq_fp8row.h"
 #include "nq_launch.h"
 
 #define NQ_API extern "C" __attribute__((visibility("default")))
@@ -211,6 +212,38 @@ NQ_API int nq_dequantize_nvfp4_stacked(const void *payload, uint64_t nbytes, con
     const uint64_t gu = elems / 8 / (uint64_t)divisors;  // units per source; 0 only when empty
     return launch_validated(nq::NVFP4_DIV, payload, nbytes, elems, out_dtype, out, (uint32_t)divisors,
                             gu ? gu : 1, stream);
+}
+
+NQ_API int nq_validate_fp8_row(int32_t scale_kind, uint64_t nbytes, const int64_t *shape, int32_t rank,
+                               int32_t out_dtype, uint64_t *out_elems, uint64_t *out_bytes) {
+    if (scale_kind != NQ_FP8_ROW_BF16 && scale_kind != NQ_FP8_ROW_FP16) return NQ_ERR_UNKNOWN_FORMAT;
+    if (out_dtype < NQ_F32 || out_dtype > NQ_F64) return NQ_ERR_BAD_DTYPE;
+    if (rank != 2) return NQ_ERR_BAD_RANK;
+    if (!shape) return NQ_ERR_NULL_ARG;
+    if (shape[0] <= 0 || shape[1] <= 0) return NQ_ERR_BAD_DIM;
+    uint64_t elems = 0, wide = 0, scale_bytes = 0;
+    if (!mul_checked((uint64_t)shape[0], (uint64_t)shape[1], &elems) || !mul_checked(elems, 8, &wide) ||
+        !mul_checked((uint64_t)shape[0], 2, &scale_bytes) || elems > I64MAX - scale_bytes)
+        return NQ_ERR_OVERFLOW;
+    if (nbytes != elems + scale_bytes) return NQ_ERR_LENGTH_MISMATCH;
+    if (out_elems) *out_elems = elems;
+    if (out_bytes) *out_bytes = elems * OUT_SIZE[out_dtype];
+    return NQ_OK;
+}
+
+NQ_API int nq_dequantize_fp8_row(int32_t scale_kind, const void *payload, uint64_t nbytes, const int64_t *shape,
+                                 int32_t rank, int32_t out_dtype, void *out, hipStream_t stream) {
+    uint64_t elems = 0;
+    const int st = nq_validate_fp8_row(scale_kind, nbytes, shape, rank, out_dtype, &elems, nullptr);
+    if (st != NQ_OK) return st;
+    if (!payload || !out) return NQ_ERR_NULL_ARG;  // both dimensions are positive: never empty
+    if (((uintptr_t)out % OUT_SIZE[out_dtype]) != 0) return NQ_ERR_NULL_ARG;
+    nq::F8Launch L;
+    L.payload = (const uint8_t *)payload;
+    L.N = (uint64_t)shape[0];
+    L.K = (uint64_t)shape[1];
+    L.out = out;
+    return nq::launch_fp8_row(scale_kind, out_dtype, L, stream);
 }
 
 NQ_API const char *nq_status_string(int status) {

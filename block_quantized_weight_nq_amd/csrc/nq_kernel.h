@@ -210,6 +210,26 @@ NQ_HD void store8(void *out, uint32_t u, const float (&y)[8]) {
     }
 }
 
+// One value at element e, converted as store8 converts it.
+template <int OT>
+NQ_HD void store1(void *out, uint64_t e, float y) {
+    if constexpr (OT == 0) {
+        ((float *)out)[e] = y;
+    } else if constexpr (OT == 1 || OT == 2) {
+        f32x2 v;
+        v.x = y;
+        v.y = 0.0f;
+        uint32_t w;
+        if constexpr (OT == 2)
+            w = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+        else
+            w = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+        ((uint16_t *)out)[e] = (uint16_t)w;
+    } else {
+        ((double *)out)[e] = (double)y;
+    }
+}
+
 constexpr int WG = 256;  // threads per workgroup (4 wave64)
 
 // ---------------------------------------------------------------------------

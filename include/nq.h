@@ -138,6 +138,33 @@ int nq_validate_nvfp4_stacked(uint64_t nbytes, const int64_t *shape, int32_t ran
 int nq_dequantize_nvfp4_stacked(const void *payload, uint64_t nbytes, const int64_t *shape, int32_t rank,
                                 int64_t divisors, int32_t out_dtype, void *out, hipStream_t stream);
 
+/* Row-scaled FP8 (NInfer "tensor-formats" page, section 3.3):
+ * fp8_e4m3fn_row_bf16 (scale_kind NQ_FP8_ROW_BF16) and fp8_e4m3fn_row_fp16
+ * (NQ_FP8_ROW_FP16).  A rank-two [N, K] matrix, both dimensions positive;
+ * value [n, k] is the binary32 product of E4M3FN code c[n, k] and row n's
+ * bfloat16 / binary16 multiplier, converted once to out_dtype (RNE for
+ * f16/bf16, exact for f64).
+ *
+ * Layout (the page defers it to a layout registry it does not print): the
+ * N*K code bytes row-major, then N little-endian 16-bit scale words in row
+ * order.  Length rule: nbytes == N*K + 2*N.
+ *
+ * nq_validate_fp8_row checks, in this order: scale_kind
+ * (NQ_ERR_UNKNOWN_FORMAT), out_dtype, rank == 2 (NQ_ERR_BAD_RANK), shape !=
+ * NULL, both dimensions > 0 (NQ_ERR_BAD_DIM), N*K*8 and nbytes within
+ * INT64_MAX (NQ_ERR_OVERFLOW), then nbytes.  nq_dequantize_fp8_row validates
+ * the same way and then follows nq_dequantize_packed: asynchronous on
+ * `stream`, payload of any alignment (NULL refused), `out` element-aligned
+ * (16-byte alignment takes the vector stores), caller-owned buffers neither
+ * retained nor freed.  Code words 0x7F/0xFF (NaN) and refused scale words
+ * (negative, non-finite) decode by the same formula. */
+typedef enum { NQ_FP8_ROW_BF16 = 0, NQ_FP8_ROW_FP16 = 1 } nq_fp8_row_scale;
+
+int nq_validate_fp8_row(int32_t scale_kind, uint64_t nbytes, const int64_t *shape, int32_t rank,
+                        int32_t out_dtype, uint64_t *out_elems, uint64_t *out_bytes);
+int nq_dequantize_fp8_row(int32_t scale_kind, const void *payload, uint64_t nbytes, const int64_t *shape,
+                          int32_t rank, int32_t out_dtype, void *out, hipStream_t stream);
+
 /* Static description of a status code. */
 const char *nq_status_string(int status);
 

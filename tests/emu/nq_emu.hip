@@ -1,15 +1,22 @@
 // nq_emu.hip -- host emulator of the decode kernels (test infrastructure).
 //
-// Runs the kernels' own per-thread code (process<> from nq_kernel.h) for
+// Runs the kernels' own per-thread code (the staging, decode and store
+// phases of nq_kernel.h, and the row-scaled FP8 thread of nq_fp8row.h) for
 // every workgroup and thread of every launch chunk, sequentially on the CPU,
-// with the launcher's own chunk and grid arithmetic (chunk_args<>).  The
-// payload source checks that every dword read overlaps the payload bytes of
-// its chunk; the caller checks the output guards.  Built host-only.
+// with the launchers' own chunk and grid arithmetic.  The payload sources
+// check that every dword read overlaps the payload bytes of its chunk; the
+// caller checks the output guards.  Built host-only.
+//
+// Built in parts so the instantiations compile in parallel: a part compiled
+// with -DNQ_EMU_PART=p -DNQ_EMU_PARTS=P instantiates the block formats whose
+// id is p mod P and registers them in the dispatch table; the build without
+// NQ_EMU_PART holds the table and the exported entry points.
 #include <cstdio>
 #include <algorithm>
 #include <cstring>
 #include <vector>
 
+#include "../../block_quantized_weight_nq_amd/csrc/nq_fp8row.h"
 #include "../../block_quantized_weight_nq_amd/csrc/nq_kernel.h"
 
 namespace {
@@ -182,6 +189,29 @@ long tile_blocks(int upt) {
 
 }  // namespace
 
+using EmuRun = long (*)(int ot, const uint8_t *payload, uint64_t nbytes, uint64_t nblocks, void *out,
+                       uint32_t max_wgs, uint64_t chunk, int force_upt, uint32_t ndiv, char *err, int errlen);
+extern EmuRun nq_emu_table[nq::NUM_FORMATS];
+
+#if defined(NQ_EMU_PART)
+namespace {
+template <int F>
+void reg() {
+    if constexpr (F % NQ_EMU_PARTS == NQ_EMU_PART) nq_emu_table[F] = &run_ot<F>;
+}
+struct Register {
+    Register() {
+        using namespace nq;
+        reg<Q4_0>(); reg<Q4_1>(); reg<Q5_0>(); reg<Q5_1>(); reg<Q8_0>(); reg<Q8_1>(); reg<Q2_K>(); reg<Q3_K>();
+        reg<Q4_K>(); reg<Q5_K>(); reg<Q6_K>(); reg<Q8_K>(); reg<IQ2_XXS>(); reg<IQ2_XS>(); reg<IQ3_XXS>();
+        reg<IQ1_S>(); reg<IQ4_NL>(); reg<IQ3_S>(); reg<IQ2_S>(); reg<IQ4_XS>(); reg<IQ1_M>(); reg<TQ1_0>();
+        reg<TQ2_0>(); reg<MXFP4>(); reg<NVFP4_GGUF>(); reg<Q1_0>(); reg<Q2_0>(); reg<NVFP4_DIV>();
+    }
+} registered;
+}  // namespace
+#else
+EmuRun nq_emu_table[nq::NUM_FORMATS];
+
 // Returns the number of out-of-payload reads (0 on success), or -1 for a bad format.
 // ndiv: "nvfp4" divisor words after the blocks (stacked sources), 1 otherwise.
 extern "C" __attribute__((visibility("default"))) long nq_emu_decode(int fmt, int ot, const uint8_t *payload,
@@ -189,17 +219,9 @@ extern "C" __attribute__((visibility("default"))) long nq_emu_decode(int fmt, in
                                                                     uint32_t max_wgs, uint64_t chunk_blocks,
                                                                     int force_upt, uint32_t ndiv, char *err,
                                                                     int errlen) {
-    using namespace nq;
-    if (ndiv < 1) ndiv = 1;
-    switch (fmt) {
-#define C(X) \
-    case X: return run_ot<X>(ot, payload, nbytes, nblocks, out, max_wgs, chunk_blocks, force_upt, ndiv, err, errlen);
-        C(Q4_0) C(Q4_1) C(Q5_0) C(Q5_1) C(Q8_0) C(Q8_1) C(Q2_K) C(Q3_K) C(Q4_K) C(Q5_K) C(Q6_K) C(Q8_K)
-        C(IQ2_XXS) C(IQ2_XS) C(IQ3_XXS) C(IQ1_S) C(IQ4_NL) C(IQ3_S) C(IQ2_S) C(IQ4_XS) C(IQ1_M)
-        C(TQ1_0) C(TQ2_0) C(MXFP4) C(NVFP4_GGUF) C(Q1_0) C(Q2_0) C(NVFP4_DIV)
-#undef C
-    default: return -1;
-    }
+    if (fmt < 0 || fmt >= nq::NUM_FORMATS || !nq_emu_table[fmt]) return -1;
+    return nq_emu_table[fmt](ot, payload, nbytes, nblocks, out, max_wgs, chunk_blocks, force_upt,
+                             ndiv < 1 ? 1 : ndiv, err, errlen);
 }
 
 // Whole blocks per staged tile of format fmt at `upt` units per thread, for
@@ -231,3 +253,61 @@ extern "C" __attribute__((visibility("default"))) int nq_emu_choose_upt(int fmt,
     default: return -1;
     }
 }
+
+namespace {
+
+// Row-scaled FP8: the launcher's chunk loop (chunk values per launch) and
+// every thread of every launch, reading through bounds-checked sources.
+template <int SK, int OT>
+long run_fp8_row(const uint8_t *payload, uint64_t N, uint64_t K, void *out, uint64_t chunk, char *err, int errlen) {
+    using namespace nq;
+    constexpr uint64_t OSZ = OT == 0 ? 4 : OT == 3 ? 8 : 2;
+    const F8Launch L{payload, N, K, out};
+    const uint64_t total = N * K;
+    long errors = 0;
+    for (uint64_t E0 = 0; E0 < total; E0 += chunk) {
+        uint32_t grid;
+        const F8Args a = f8_chunk_args<OT>(L, E0, &grid, chunk);
+        const uint64_t n = a.n, r0 = E0 / K, r1 = (E0 + n - 1) / K;
+        Check cc{(uintptr_t)(payload + E0), (uintptr_t)(payload + E0 + n), 0, {0}};
+        Check cs{(uintptr_t)(payload + total + 2 * r0), (uintptr_t)(payload + total + 2 * (r1 + 1)), 0, {0}};
+        const HostSrc csrc{a.cbase, a.clast, &cc}, ssrc{a.sbase, a.slast, &cs};
+        const bool vec = (((uintptr_t)out + E0 * OSZ) & 15) == 0;
+        for (uint32_t i = 0; i < grid * (uint32_t)WG; i++) {
+            if (vec)
+                fp8row_thread<SK, OT, true>(csrc, ssrc, a, i);
+            else
+                fp8row_thread<SK, OT, false>(csrc, ssrc, a, i);
+        }
+        for (Check *c : {&cc, &cs})
+            if (c->errors) {
+                if (errors == 0) snprintf(err, errlen, "%s", c->msg);
+                errors += c->errors;
+            }
+    }
+    return errors;
+}
+
+template <int SK>
+long run_fp8_row_ot(int ot, const uint8_t *p, uint64_t N, uint64_t K, void *out, uint64_t chunk, char *err,
+                    int errlen) {
+    switch (ot) {
+    case 0: return run_fp8_row<SK, 0>(p, N, K, out, chunk, err, errlen);
+    case 1: return run_fp8_row<SK, 1>(p, N, K, out, chunk, err, errlen);
+    case 2: return run_fp8_row<SK, 2>(p, N, K, out, chunk, err, errlen);
+    default: return run_fp8_row<SK, 3>(p, N, K, out, chunk, err, errlen);
+    }
+}
+
+}  // namespace
+
+// Row-scaled FP8 through the kernel's per-thread code; returns out-of-bounds
+// reads (0 on success).  chunk: values per launch (0: the launcher's).
+extern "C" __attribute__((visibility("default"))) long nq_emu_fp8_row(int kind, int ot, const uint8_t *payload,
+                                                                     uint64_t N, uint64_t K, void *out,
+                                                                     uint64_t chunk, char *err, int errlen) {
+    if (chunk == 0) chunk = nq::F8_CHUNK;
+    return kind == 0 ? run_fp8_row_ot<0>(ot, payload, N, K, out, chunk, err, errlen)
+                     : run_fp8_row_ot<1>(ot, payload, N, K, out, chunk, err, errlen);
+}
+#endif  // NQ_EMU_PART

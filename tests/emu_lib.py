@@ -14,10 +14,28 @@ NPT = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "f64": np.float64
 _lib = None
 
 
+PARTS = 6
+
+
 def build():
-    cmd = ["hipcc", "-x", "hip", "--offload-host-only", "-O1", "-std=c++17", "-fPIC", "-shared",
-           "-ffp-contract=off", "-fvisibility=hidden", SRC, "-o", LIB]
-    subprocess.run(cmd, check=True, capture_output=True)
+    """Compile the emulator: PARTS instantiation parts and the dispatch part in parallel, then link."""
+    import concurrent.futures
+    import tempfile
+    flags = ["hipcc", "-x", "hip", "--offload-host-only", "-O1", "-std=c++17", "-fPIC", "-ffp-contract=off",
+             "-fvisibility=hidden"]
+    with tempfile.TemporaryDirectory() as tmp:
+        jobs = [[f"-DNQ_EMU_PART={p}", f"-DNQ_EMU_PARTS={PARTS}"] for p in range(PARTS)] + [[]]
+        objs = [os.path.join(tmp, f"part{i}.o") for i in range(len(jobs))]
+
+        def compile_one(i):
+            return subprocess.run(flags + jobs[i] + ["-c", SRC, "-o", objs[i]], capture_output=True, text=True)
+
+        with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+            results = list(ex.map(compile_one, range(len(jobs))))
+        for r in results:
+            if r.returncode != 0:
+                raise RuntimeError(f"emulator build failed:\n{r.stderr[-4000:]}")
+        subprocess.run(["hipcc", "-shared", "-fPIC"] + objs + ["-o", LIB], check=True, capture_output=True)
 
 
 def _stale():
@@ -39,6 +57,9 @@ def lib():
                                     ctypes.c_int, ctypes.c_uint32, ctypes.c_char_p, ctypes.c_int]
         L.nq_emu_decode.restype = ctypes.c_long
         L.nq_emu_tile_blocks.argtypes = [ctypes.c_int, ctypes.c_int]
+        L.nq_emu_fp8_row.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64,
+                                     ctypes.c_void_p, ctypes.c_uint64, ctypes.c_char_p, ctypes.c_int]
+        L.nq_emu_fp8_row.restype = ctypes.c_long
         L.nq_emu_choose_upt.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint32]
         L.nq_emu_choose_upt.restype = ctypes.c_int
         L.nq_emu_tile_blocks.restype = ctypes.c_long
@@ -81,3 +102,21 @@ def tile_blocks(fmt_id, upt):
 def choose_upt(fmt_id, nunits, resident):
     """The launcher's units per thread for a launch of `nunits` units of a format."""
     return lib().nq_emu_choose_upt(fmt_id, nunits, resident)
+
+
+def decode_fp8_row(kind, payload, N, K, dtype, mis=0, out_mis=0, chunk=0):
+    """Row-scaled FP8 through the emulator; returns (values, out-of-bounds reads, message, guards_ok)."""
+    payload = np.ascontiguousarray(payload, dtype=np.uint8)
+    pbuf, poff = _placed(payload.size, 4, mis)
+    pbuf[:] = 0xEE
+    pbuf[poff:poff + payload.size] = payload
+    n = N * K
+    osz = OSIZE[dtype]
+    obuf, ooff = _placed(n * osz, 16, out_mis)
+    obuf[:] = 0xA5
+    err = ctypes.create_string_buffer(256)
+    rc = lib().nq_emu_fp8_row(kind, {"f32": 0, "f16": 1, "bf16": 2, "f64": 3}[dtype], pbuf.ctypes.data + poff, N, K,
+                              obuf.ctypes.data + ooff, chunk, err, 256)
+    guards = bool(np.all(obuf[:ooff] == 0xA5) and np.all(obuf[ooff + n * osz:] == 0xA5))
+    vals = obuf[ooff:ooff + n * osz].copy().view(NPT[dtype])
+    return vals, rc, err.value.decode(), guards

@@ -151,3 +151,34 @@ def test_nvfp4_stacked_rejects_before_device():
     # empty planes succeed without launching (null pointers allowed when nothing is read or written)
     assert nq.dequantize_nvfp4_stacked_raw(p, 12, [6, 0], 3, 2, 0, 0) == 0
     assert nq.dequantize_nvfp4_stacked_raw(0, 0, [6, 0], 3, 2, 0, 0) == 6
+
+
+FP8_SHAPES = [[3, 5], [1, 1], [0, 5], [3, 0], [-1, 5], [15], [1, 3, 5], [], [2 ** 62, 4], [2 ** 31, 2 ** 31],
+              [14336, 4096]]
+
+
+@pytest.mark.parametrize("fmt", ["fp8_e4m3fn_row_bf16", "fp8_e4m3fn_row_fp16"])
+@pytest.mark.parametrize("shape", FP8_SHAPES)
+def test_fp8_row_length_rule_agrees_with_oracle(fmt, shape):
+    ostatus = {oracle.OK: 0, oracle.ERR_RANK: 3, oracle.ERR_DIM: 4, oracle.ERR_OVERFLOW: 7}
+    st, nbytes, nelems = oracle.sizes_fp8_row(shape)
+    got, ne, ob = nq.validate_fp8_row_status(fmt, nbytes if st == oracle.OK else 0, shape, "f16")
+    assert got == ostatus[st], (shape, got, st)
+    if got == 0:
+        assert ne == nelems and ob == 2 * nelems
+        for delta in (-1, 1, -2, 2):
+            assert nq.validate_fp8_row_status(fmt, nbytes + delta, shape)[0] == 6
+
+
+def test_fp8_row_rejects_before_device():
+    buf = np.zeros(64, dtype=np.uint8)
+    p = buf.ctypes.data
+    assert nq.validate_fp8_row_status(2, 21, [3, 5])[0] == 2      # unknown scale kind
+    assert nq.validate_fp8_row_status(-1, 21, [3, 5])[0] == 2
+    assert nq.validate_fp8_row_status(0, 21, [3, 5], 9)[0] == 8   # bad dtype
+    assert nq.dequantize_fp8_row_raw(0, p, 20, [3, 5], 0, p, 0) == 6
+    assert nq.dequantize_fp8_row_raw(0, 0, 21, [3, 5], 0, p, 0) == 1
+    assert nq.dequantize_fp8_row_raw(0, p, 21, [3, 5], 0, 0, 0) == 1
+    assert nq.dequantize_fp8_row_raw(0, p, 21, [3, 5], 0, p + 2, 0) == 1   # f32 output not element-aligned
+    assert nq.dequantize_fp8_row_raw(1, p, 21, [15], 0, p, 0) == 3
+    assert nq.dequantize_fp8_row_raw(1, p, 0, [0, 5], 0, p, 0) == 4

@@ -151,3 +151,24 @@ def test_emulated_nvfp4_stacked_divisors(rows, K, divisors, upt):
         assert bad == 0, (mis, msg)
         assert guards
         assert _same(got, ref, "f32"), (mis, divisors)
+
+
+@pytest.mark.parametrize("kind,fmt", [(0, "fp8_e4m3fn_row_bf16"), (1, "fp8_e4m3fn_row_fp16")])
+@pytest.mark.parametrize("N,K,chunk", [(7, 48, 0), (5, 33, 0), (3, 1, 0), (1, 4099, 0), (9, 7, 0), (33, 256, 1000),
+                                       (6, 100, 77), (1, 5000, 4096), (40, 16, 160)])
+def test_emulated_fp8_row(kind, fmt, N, K, chunk):
+    """Row-scaled FP8: rows shorter and longer than a thread's 16 values,
+    rows that start inside a thread, partial last threads, launches split
+    mid-row, every payload alignment and output type."""
+    rng = np.random.default_rng(N * 1000 + K)
+    codes = rng.integers(0, 256, size=N * K, dtype=np.uint8)
+    scales = rng.integers(0, 1 << 16, size=N, dtype=np.uint16)
+    p = np.concatenate([codes, scales.astype("<u2").view(np.uint8)])
+    for dtype in ("f32", "bf16", "f16", "f64"):
+        ref = oracle.decode_fp8_row(fmt, p, [N, K], dtype)
+        for mis in range(4):
+            got, bad, msg, guards = emu_lib.decode_fp8_row(kind, p, N, K, dtype, mis=mis, out_mis=2 * (mis & 1),
+                                                           chunk=chunk)
+            assert bad == 0, (mis, msg)
+            assert guards
+            assert _same(got, ref, dtype), (dtype, mis)

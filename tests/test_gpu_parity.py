@@ -302,3 +302,57 @@ def test_nvfp4_stacked_one_divisor_is_plain_nvfp4():
     b = nq.dequantize_packed("nvfp4", payload, [1000, 256], torch.bfloat16)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# Row-scaled FP8: fp8_e4m3fn_row_bf16 / fp8_e4m3fn_row_fp16.
+# ---------------------------------------------------------------------------
+def _fp8_payload(N, K, seed, scale_words=None):
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, size=N * K, dtype=np.uint8)
+    scales = rng.integers(0, 1 << 16, size=N, dtype=np.uint16) if scale_words is None else scale_words
+    return np.concatenate([codes, np.asarray(scales, np.uint16).astype("<u2").view(np.uint8)])
+
+
+def _fp8_check(fmt, p, shape, dtype, pay_off=0, out_off=0):
+    payload, _keep = upload(p, pay_off)
+    n = shape[0] * shape[1]
+    obuf = torch.full((n + out_off + 8,), float("nan"), dtype=TORCH_DT[dtype], device="cuda:0")
+    out = obuf[out_off:out_off + n]
+    nq.dequantize_fp8_row(fmt, payload, shape, TORCH_DT[dtype], out=out)
+    torch.cuda.synchronize()
+    got = to_numpy(out, dtype)
+    ref = oracle.decode_fp8_row(fmt, p, shape, dtype)
+    assert compare.same(got, ref, dtype), f"{fmt} {shape} {dtype}: {compare.describe(got, ref, dtype)}"
+    # the NaN fill around the output is untouched
+    assert bool(torch.isnan(obuf[:out_off]).all()) and bool(torch.isnan(obuf[out_off + n:]).all())
+
+
+@pytest.mark.parametrize("fmt", ["fp8_e4m3fn_row_bf16", "fp8_e4m3fn_row_fp16"])
+@pytest.mark.parametrize("shape", [[7, 48], [5, 33], [3, 1], [1, 4099], [9, 7], [300, 4096], [1025, 96], [2, 70001]])
+def test_fp8_row_every_output_type(fmt, shape):
+    """Random code and scale words (NaN and infinite ones included, compared
+    by class), rows shorter and longer than a thread's 16 values."""
+    p = _fp8_payload(shape[0], shape[1], shape[0] * 31 + shape[1])
+    for dtype in ("f32", "f16", "bf16", "f64"):
+        announce(f"fp8_row {fmt} {shape} {dtype}")
+        _fp8_check(fmt, p, shape, dtype)
+
+
+@pytest.mark.parametrize("fmt", ["fp8_e4m3fn_row_bf16", "fp8_e4m3fn_row_fp16"])
+def test_fp8_row_payload_and_output_offsets(fmt):
+    p = _fp8_payload(37, 200, 5)
+    for off in range(8):
+        for dtype, out_off in (("bf16", off), ("f32", off % 4)):
+            announce(f"fp8_row offsets {fmt} pay_off={off} {dtype} out_off={out_off}")
+            _fp8_check(fmt, p, [37, 200], dtype, pay_off=off, out_off=out_off)
+
+
+def test_fp8_row_full_size():
+    """[14336, 4096] with valid scale words (positive finite), compared in full."""
+    rng = np.random.default_rng(9)
+    bf = (rng.integers(0x3B00, 0x3D00, size=14336)).astype(np.uint16)        # bfloat16 in [2^-9, 2^-5)
+    f16 = (rng.integers(0x1C00, 0x2C00, size=14336)).astype(np.uint16)       # binary16 in [2^-8, 2^-4)
+    for fmt, sw in (("fp8_e4m3fn_row_bf16", bf), ("fp8_e4m3fn_row_fp16", f16)):
+        announce(f"fp8_row full size {fmt}")
+        _fp8_check(fmt, _fp8_payload(14336, 4096, 11, sw), [14336, 4096], "bf16")
