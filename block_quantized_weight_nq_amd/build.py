@@ -54,8 +54,9 @@ def _compile(src, is_kernel, build_dir=BUILD, defines=()):
 def build(jobs=None, verbose=False, out=LIB, defines=()):
     """Compile every source and link the library (default: libnq.so in-tree).
 
-    `defines` are extra -D macros (the tuning knobs NQ_UPT, NQ_WG_PER_CU,
-    NQ_NT_STORE of csrc/nq_kernel.h); a non-default `out` builds elsewhere.
+    `defines` are extra -D macros (the tuning knobs NQ_UPT, NQ_RESIDENT_PER_CU,
+    NQ_NT_STORE, NQ_NTL of csrc/nq_kernel.h and NQ_F8_NB of csrc/nq_fp8row.h);
+    a non-default `out` builds elsewhere.
     """
     build_dir = BUILD if out == LIB else out + ".build"
     os.makedirs(build_dir, exist_ok=True)

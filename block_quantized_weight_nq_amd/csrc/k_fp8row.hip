@@ -10,9 +10,10 @@ static int launch_f8(const F8Launch &L, hipStream_t stream) {
     for (uint64_t E0 = 0; E0 < total; E0 += F8_CHUNK) {
         uint32_t grid;
         const F8Args a = f8_chunk_args<OT>(L, E0, &grid);
-        // units 2i, 2i+1 of a launch start at multiples of 16 values: aligned
-        // when the launch's output is
-        if (((uintptr_t)L.out + E0 * OSZ) % 16 == 0)
+        // every unit starts at a multiple of 8 values: 16-byte aligned when the
+        // launch's output is (for 16-bit outputs; f32/f64 units are 32/64 bytes)
+        const bool vec = ((uintptr_t)L.out + E0 * OSZ) % 16 == 0;
+        if (vec)
             hipLaunchKernelGGL((k_fp8_row<SK, OT, true>), dim3(grid), dim3(WG), 0, stream, a);
         else
             hipLaunchKernelGGL((k_fp8_row<SK, OT, false>), dim3(grid), dim3(WG), 0, stream, a);

@@ -6,17 +6,18 @@
 // once to the output type like every other decode here.  Bytes: the N*K codes
 // row-major, then the N scale words (little-endian 16-bit) in row order.
 //
-// Launch shape: one thread per 16 consecutive values of the flat output, 256
-// threads per workgroup, one workgroup per 4096 values.  A thread reads its
-// 16 codes as one 16-byte window (any payload alignment), the scale word of
-// each row its values touch, and stores two 8-value units (one 16-byte
-// store each for bf16/f16 outputs).  A launch covers at most 2^30 values; the
-// host splits larger matrices into such chunks.
+// Launch shape: units of 8 consecutive values, decoded in wave blocks of 128
+// units (see k_fp8_row): one 1 KiB code load per wave, passed through the
+// wave's own LDS so that each store instruction writes 64 consecutive units
+// (1 KiB for bf16/f16), as in the block decoders.  A launch covers at most
+// 2^30 values; the host splits larger matrices into such chunks.
 #pragma once
 
 #include "nq_kernel.h"
 
 namespace nq {
+
+constexpr uint64_t F8_CHUNK = 1ull << 30;  // values per launch at most
 
 // One launch: values [E0, E0 + n) of the matrix.
 struct F8Args {
@@ -28,7 +29,20 @@ struct F8Args {
     uint32_t smis, slast;   // scale start - sbase (0..3); last dword holding chunk scales
     uint32_t n;             // values in this launch (<= 2^30)
     uint64_t col0;          // column of value E0 (E0 mod K)
+    uint32_t kmul, kshift;  // division by K <= 2^30 as a multiply-shift (f8_div_magic)
 };
+
+// Division of 31-bit numerators by d (1 <= d <= 2^30) as floor(n * m / 2^s):
+// with l = ceil(log2 d), m = floor(2^(31+l) / d) + 1 and s = 31 + l this is
+// exact for every 0 <= n < 2^31 (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994, theorem 4.2 with N = 31);
+// m < 2^32.
+NQ_HD void f8_div_magic(uint64_t d, uint32_t *m, uint32_t *s) {
+    uint32_t l = 0;
+    while ((1ull << l) < d) l++;
+    *m = (uint32_t)((1ull << (31 + l)) / d + 1);
+    *s = 31 + l;
+}
 
 // Exact E4M3FN value: the 7 magnitude bits placed at binary32 bits 26..20
 // give 2^-120 times the value (a binary32 subnormal when the E4M3FN exponent
@@ -49,61 +63,166 @@ NQ_HD float row_scale(uint32_t w) {
 }
 
 // Row of chunk value e relative to the chunk's first row, and the chunk
-// value where the following row starts.
+// value where the following row starts.  col = col0 + e < K + 2^30 (a launch
+// holds at most 2^30 values and col0 < K): for K <= 2^30 it fits 31 bits, and
+// for longer rows the quotient is 0 or 1, so no 64-bit division is needed.
 NQ_HD uint32_t f8_row(const F8Args &a, uint32_t e, uint64_t *next) {
-    const uint64_t col = (uint64_t)a.col0 + e;
-    uint64_t r;
-    if (a.K <= 0xFFFFFFFFull && col <= 0xFFFFFFFFull)
-        r = (uint32_t)col / (uint32_t)a.K;
+    const uint64_t col = a.col0 + e;
+    uint32_t r;
+    if (a.K <= F8_CHUNK)
+        r = (uint32_t)(((uint64_t)(uint32_t)col * a.kmul) >> a.kshift);
     else
-        r = col / a.K;
-    *next = (r + 1) * a.K - a.col0;
-    return (uint32_t)r;
+        r = col >= a.K ? 1u : 0u;
+    *next = (uint64_t)(r + 1) * a.K - a.col0;
+    return r;
 }
 
-// The work of thread i: values 16i .. 16i+15 of the launch (those below n).
-template <int SK, int OT, bool VEC, class Src>
-NQ_HD void fp8row_thread(const Src &csrc, const Src &ssrc, const F8Args &a, uint32_t i) {
-    const uint32_t e = 16u * i;
-    if (e >= a.n) return;
-    const bool full = a.n - e >= 16u;
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    if (full) {
-        window<4>(csrc, a.cmis + e, w);
-    } else {
-        for (uint32_t j = 0; j < a.n - e; j++) w[j >> 2] |= u8_at(csrc, a.cmis + e + j) << (8u * (j & 3u));
-    }
+// Row-scale words are read per unit (rows are long next to a unit, and the
+// lanes of a wave mostly share one row, so these loads hit one cache line).
+// With K >= 8 a unit touches at most two rows: values before the next row's
+// start take the first row's scale, the rest the second's (loaded only then).
+// Whether one of the 4 code bytes of x is a NaN word (magnitude 0x7F): with
+// bit 7 forced on in every byte, such a byte is 0xFF, i.e. a zero byte of the
+// complement, found by the usual borrow test (exact as a yes/no answer).
+NQ_HD uint32_t f8_has_nan(uint32_t x) { return (~(x | 0x80808080u) - 0x01010101u) & 0x80808080u; }
+
+// E4M3FN value of a code byte that is not a NaN word.
+NQ_HD float e4m3fn_exact_finite(uint32_t c) {
+    const float v = M(bits_f32((c & 0x7Fu) << 20), 0x1p120f);
+    return bits_f32(__builtin_bit_cast(uint32_t, v) | ((c & 0x80u) << 24));
+}
+
+template <int SK, class Src>
+NQ_HD void fp8row_values(const Src &ssrc, const F8Args &a, uint32_t u, const uint32_t (&w)[2], float (&y)[8]) {
+    const uint32_t e = 8u * u;
     uint64_t next;
-    uint32_t r = f8_row(a, e, &next);
-    float s = row_scale<SK>(u16_at(ssrc, a.smis + 2u * r));
-    float y[16];
+    const uint32_t r = f8_row(a, e, &next);
+    const float s = row_scale<SK>(u16_at(ssrc, a.smis + 2u * r));
+    const uint32_t split = next - e < 8u ? (uint32_t)(next - e) : 8u;  // first value of the next row
+    if (split == 8u && (f8_has_nan(w[0]) | f8_has_nan(w[1])) == 0u) {  // one row, no NaN words
 #pragma unroll
-    for (uint32_t j = 0; j < 16; j++) {
-        if ((uint64_t)e + j == next && e + j < a.n) {  // a row starts inside this thread's values
-            r++;
-            next += a.K;
-            s = row_scale<SK>(u16_at(ssrc, a.smis + 2u * r));
-        }
-        y[j] = M(e4m3fn_exact(bytek(w[j >> 2], j & 3u)), s);
+        for (uint32_t j = 0; j < 8; j++) y[j] = M(e4m3fn_exact_finite(bytek(w[j >> 2], j & 3u)), s);
+        return;
     }
-    if (full) {
-        float lo[8], hi[8];
+    float s2 = s;
+    if (split < 8u && e + split < a.n) s2 = row_scale<SK>(u16_at(ssrc, a.smis + 2u * (r + 1u)));
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            lo[j] = y[j];
-            hi[j] = y[8 + j];
-        }
-        store8<OT, VEC>(a.out, 2u * i, lo);
-        store8<OT, VEC>(a.out, 2u * i + 1u, hi);
-    } else {
-        for (uint32_t j = 0; j < a.n - e; j++) store1<OT>(a.out, (uint64_t)e + j, y[j]);
+    for (uint32_t j = 0; j < 8; j++) y[j] = M(e4m3fn_exact(bytek(w[j >> 2], j & 3u)), j < split ? s : s2);
+}
+
+// Rows shorter than a unit (K < 8): value by value, each with its own row.
+template <int SK, int OT, class Src>
+NQ_HD void fp8row_values_short_rows(const Src &csrc, const Src &ssrc, const F8Args &a, uint32_t u) {
+    const uint32_t e = 8u * u;
+#pragma unroll 1
+    for (uint32_t j = 0; j < 8u && e + j < a.n; j++) {
+        uint64_t next;
+        const uint32_t r = f8_row(a, e + j, &next);
+        const float s = row_scale<SK>(u16_at(ssrc, a.smis + 2u * r));
+        store1<OT>(a.out, (uint64_t)e + j, M(e4m3fn_exact(u8_at(csrc, a.cmis + e + j)), s));
     }
 }
 
+// One unit read straight from global memory: a byte-shifted two-word window,
+// or byte by byte for the last, partial unit.
+template <int SK, int OT, bool VEC, class Src>
+NQ_HD void fp8row_unit_direct(const Src &csrc, const Src &ssrc, const F8Args &a, uint32_t u) {
+    const uint32_t e = 8u * u;
+    if (e >= a.n) return;
+    if (a.K < 8u) {
+        fp8row_values_short_rows<SK, OT>(csrc, ssrc, a, u);
+        return;
+    }
+    uint32_t w[2] = {0u, 0u};
+    const bool full = a.n - e >= 8u;
+    if (full) {
+        window<2>(csrc, a.cmis + e, w);
+    } else {
+        for (uint32_t j = 0; e + j < a.n; j++) w[j >> 2] |= u8_at(csrc, a.cmis + e + j) << (8u * (j & 3u));
+    }
+    float y[8];
+    fp8row_values<SK>(ssrc, a, u, w, y);
+    if (full) {
+        store8<OT, VEC>(a.out, u, y);
+    } else {
+        for (uint32_t j = 0; e + j < a.n; j++) store1<OT>(a.out, (uint64_t)e + j, y[j]);
+    }
+}
+
+// Work split: a wave block is 128 units (1 KiB of codes).  Wave v of
+// workgroup b takes wave blocks (4b + v) * F8_NB + k, k < F8_NB.  When the
+// codes start on a 4-byte boundary and the block holds 128 whole units, lane
+// l loads 16 consecutive code bytes (units 2l, 2l+1; one 1 KiB load per
+// wave), the wave passes them through its own 1 KiB of LDS, and lane l then
+// decodes units l and 64 + l, so each store instruction of the wave writes
+// 64 consecutive units.  Other blocks decode unit by unit from global memory.
+#ifndef NQ_F8_NB
+#define NQ_F8_NB 2
+#endif
+constexpr int F8_NB = NQ_F8_NB;
+constexpr uint32_t F8_WG_UNITS = 4u * 128u * F8_NB;
+
+NQ_HD uint32_t f8_wave_block(uint32_t b, uint32_t wave, int k) { return (4u * b + wave) * F8_NB + (uint32_t)k; }
+
+// Whether wave block q takes the fast path: codes on a 4-byte boundary, rows
+// of at least 8 values, and 128 whole units in the block.
+NQ_HD bool f8_fast_block(const F8Args &a, uint32_t q) {
+    return a.cmis == 0 && a.K >= 8u && 128u * (q + 1) <= a.n / 8u;
+}
+
+// Phase 1 (fast blocks): lane l's 16 code bytes (units 2l, 2l+1).
+template <class Src>
+NQ_HD void fp8row_stage_load(const Src &csrc, uint32_t q, uint32_t lane, uint32_t (&w)[4]) {
+    csrc.load_stream4(256u * q + 4u * lane, w);
+}
+
+// Phase 2 (fast blocks): lane l decodes units 128q + l and 128q + 64 + l from
+// the wave's LDS words.
+template <int SK, int OT, bool VEC, class Src>
+NQ_HD void fp8row_wave_decode(const Src &ssrc, const F8Args &a, uint32_t q, uint32_t lane, const uint32_t *wbuf) {
+#pragma unroll
+    for (uint32_t h = 0; h < 2; h++) {
+        const uint32_t v = 64u * h + lane;
+        const uint32_t w[2] = {wbuf[2u * v], wbuf[2u * v + 1u]};
+        float y[8];
+        fp8row_values<SK>(ssrc, a, 128u * q + v, w, y);
+        store8<OT, VEC>(a.out, 128u * q + v, y);
+    }
+}
+
+// A workgroup whose wave blocks are all fast issues all of its code loads
+// before its first LDS write; otherwise every unit is read directly.
 template <int SK, int OT, bool VEC>
 __global__ __launch_bounds__(WG) void k_fp8_row(F8Args a) {
-    fp8row_thread<SK, OT, VEC>(DevSrc{a.cbase, a.clast}, DevSrc{a.sbase, a.slast}, a,
-                               blockIdx.x * (uint32_t)WG + threadIdx.x);
+    __shared__ __attribute__((aligned(16))) uint32_t buf[4][F8_NB][256];
+    const uint32_t wave = threadIdx.x / 64u, lane = threadIdx.x % 64u;
+    const DevSrc csrc{a.cbase, a.clast}, ssrc{a.sbase, a.slast};
+    if (f8_fast_block(a, f8_wave_block(blockIdx.x, 3u, F8_NB - 1))) {  // the workgroup's last block
+        uint32_t w[F8_NB][4];
+#pragma unroll
+        for (int k = 0; k < F8_NB; k++) fp8row_stage_load(csrc, f8_wave_block(blockIdx.x, wave, k), lane, w[k]);
+#pragma unroll
+        for (int k = 0; k < F8_NB; k++) {
+            uint32_t *wb = buf[wave][k];
+#pragma unroll
+            for (int j = 0; j < 4; j++) wb[4u * lane + j] = w[k][j];
+        }
+        // the wave's LDS words are written and read by the same wave: a
+        // wave-scope release/acquire around a wave barrier orders them
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int k = 0; k < F8_NB; k++)
+            fp8row_wave_decode<SK, OT, VEC>(ssrc, a, f8_wave_block(blockIdx.x, wave, k), lane, buf[wave][k]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < F8_NB; k++) {
+            const uint32_t q = f8_wave_block(blockIdx.x, wave, k);
+            fp8row_unit_direct<SK, OT, VEC>(csrc, ssrc, a, 128u * q + lane);
+            fp8row_unit_direct<SK, OT, VEC>(csrc, ssrc, a, 128u * q + 64u + lane);
+        }
+    }
 }
 
 // Host side: one matrix, split into launches of at most 2^30 values.
@@ -112,8 +231,6 @@ struct F8Launch {
     uint64_t N, K;
     void *out;               // device
 };
-
-constexpr uint64_t F8_CHUNK = 1ull << 30;
 
 // Arguments of the launch covering values [E0, E0 + min(chunk, rest)).
 template <int OT>
@@ -135,7 +252,10 @@ NQ_HD F8Args f8_chunk_args(const F8Launch &L, uint64_t E0, uint32_t *grid, uint6
     a.K = L.K;
     a.n = (uint32_t)n;
     a.col0 = E0 - r0 * L.K;
-    *grid = (uint32_t)((n + 16u * WG - 1) / (16u * WG));
+    a.kmul = 0;
+    a.kshift = 0;
+    if (L.K <= F8_CHUNK) f8_div_magic(L.K, &a.kmul, &a.kshift);
+    *grid = (uint32_t)((n + 8u * F8_WG_UNITS - 1) / (8u * F8_WG_UNITS));
     return a;
 }
 

@@ -273,11 +273,38 @@ long run_fp8_row(const uint8_t *payload, uint64_t N, uint64_t K, void *out, uint
         Check cs{(uintptr_t)(payload + total + 2 * r0), (uintptr_t)(payload + total + 2 * (r1 + 1)), 0, {0}};
         const HostSrc csrc{a.cbase, a.clast, &cc}, ssrc{a.sbase, a.slast, &cs};
         const bool vec = (((uintptr_t)out + E0 * OSZ) & 15) == 0;
-        for (uint32_t i = 0; i < grid * (uint32_t)WG; i++) {
-            if (vec)
-                fp8row_thread<SK, OT, true>(csrc, ssrc, a, i);
-            else
-                fp8row_thread<SK, OT, false>(csrc, ssrc, a, i);
+        // per workgroup: if its last wave block is fast, every wave stages its
+        // blocks (all lanes), then decodes them; otherwise unit by unit.  LDS
+        // words are poisoned beforehand.
+        std::vector<uint32_t> wbuf(256);
+        for (uint32_t b = 0; b < grid; b++) {
+            const bool fast = f8_fast_block(a, f8_wave_block(b, 3u, F8_NB - 1));
+            for (uint32_t wave = 0; wave < 4u; wave++)
+                for (int k = 0; k < F8_NB; k++) {
+                    const uint32_t q = f8_wave_block(b, wave, k);
+                    if (fast) {
+                        std::fill(wbuf.begin(), wbuf.end(), 0xA5A5A5A5u);
+                        for (uint32_t lane = 0; lane < 64u; lane++) {
+                            uint32_t w[4];
+                            fp8row_stage_load(csrc, q, lane, w);
+                            for (int j = 0; j < 4; j++) wbuf[4u * lane + j] = w[j];
+                        }
+                        for (uint32_t lane = 0; lane < 64u; lane++) {
+                            if (vec)
+                                fp8row_wave_decode<SK, OT, true>(ssrc, a, q, lane, wbuf.data());
+                            else
+                                fp8row_wave_decode<SK, OT, false>(ssrc, a, q, lane, wbuf.data());
+                        }
+                    } else {
+                        for (uint32_t lane = 0; lane < 64u; lane++)
+                            for (uint32_t h = 0; h < 2u; h++) {
+                                if (vec)
+                                    fp8row_unit_direct<SK, OT, true>(csrc, ssrc, a, 128u * q + 64u * h + lane);
+                                else
+                                    fp8row_unit_direct<SK, OT, false>(csrc, ssrc, a, 128u * q + 64u * h + lane);
+                            }
+                    }
+                }
         }
         for (Check *c : {&cc, &cs})
             if (c->errors) {
@@ -309,5 +336,12 @@ extern "C" __attribute__((visibility("default"))) long nq_emu_fp8_row(int kind, 
     if (chunk == 0) chunk = nq::F8_CHUNK;
     return kind == 0 ? run_fp8_row_ot<0>(ot, payload, N, K, out, chunk, err, errlen)
                      : run_fp8_row_ot<1>(ot, payload, N, K, out, chunk, err, errlen);
+}
+// The row division of the row-scaled FP8 kernels: floor(n / d) as computed
+// from f8_div_magic, for the test against plain division.
+extern "C" __attribute__((visibility("default"))) uint32_t nq_emu_f8_div(uint32_t n, uint32_t d) {
+    uint32_t m, sh;
+    nq::f8_div_magic(d, &m, &sh);
+    return (uint32_t)(((uint64_t)n * m) >> sh);
 }
 #endif  // NQ_EMU_PART

@@ -60,6 +60,8 @@ def lib():
         L.nq_emu_fp8_row.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64,
                                      ctypes.c_void_p, ctypes.c_uint64, ctypes.c_char_p, ctypes.c_int]
         L.nq_emu_fp8_row.restype = ctypes.c_long
+        L.nq_emu_f8_div.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
+        L.nq_emu_f8_div.restype = ctypes.c_uint32
         L.nq_emu_choose_upt.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint32]
         L.nq_emu_choose_upt.restype = ctypes.c_int
         L.nq_emu_tile_blocks.restype = ctypes.c_long
@@ -120,3 +122,8 @@ def decode_fp8_row(kind, payload, N, K, dtype, mis=0, out_mis=0, chunk=0):
     guards = bool(np.all(obuf[:ooff] == 0xA5) and np.all(obuf[ooff + n * osz:] == 0xA5))
     vals = obuf[ooff:ooff + n * osz].copy().view(NPT[dtype])
     return vals, rc, err.value.decode(), guards
+
+
+def f8_div(n, d):
+    """The FP8 row kernels' multiply-shift division floor(n / d)."""
+    return lib().nq_emu_f8_div(n, d)

@@ -155,7 +155,8 @@ def test_emulated_nvfp4_stacked_divisors(rows, K, divisors, upt):
 
 @pytest.mark.parametrize("kind,fmt", [(0, "fp8_e4m3fn_row_bf16"), (1, "fp8_e4m3fn_row_fp16")])
 @pytest.mark.parametrize("N,K,chunk", [(7, 48, 0), (5, 33, 0), (3, 1, 0), (1, 4099, 0), (9, 7, 0), (33, 256, 1000),
-                                       (6, 100, 77), (1, 5000, 4096), (40, 16, 160)])
+                                       (6, 100, 77), (1, 5000, 4096), (40, 16, 160), (70, 300, 0),
+                                       (70, 300, 9000), (3, 40000, 0)])
 def test_emulated_fp8_row(kind, fmt, N, K, chunk):
     """Row-scaled FP8: rows shorter and longer than a thread's 16 values,
     rows that start inside a thread, partial last threads, launches split
@@ -172,3 +173,20 @@ def test_emulated_fp8_row(kind, fmt, N, K, chunk):
             assert bad == 0, (mis, msg)
             assert guards
             assert _same(got, ref, dtype), (dtype, mis)
+
+
+def test_fp8_row_division_by_multiplication():
+    """The multiply-shift row division equals floor(n / d) for 31-bit n and
+    every d up to 2^30: all d < 2^12, powers of two and their neighbours,
+    random d; n at 0, 1, d - 1, d, d + 1, around multiples of d, near 2^31."""
+    rng = np.random.default_rng(5)
+    ds = set(range(1, 1 << 12)) | {1 << k for k in range(31)} | {(1 << k) + 1 for k in range(30)}
+    ds |= {(1 << k) - 1 for k in range(2, 31)} | set(int(x) for x in rng.integers(1, 1 << 30, 3000))
+    top = (1 << 31) - 1
+    for d in sorted(ds):
+        q = top // d
+        ns = {0, 1, d - 1, d, d + 1, top, top - 1, q * d, q * d - 1, (q // 2) * d, (q // 2) * d - 1}
+        ns |= set(int(x) for x in rng.integers(0, 1 << 31, 8))
+        for n in ns:
+            if 0 <= n <= top:
+                assert emu_lib.f8_div(n, d) == n // d, (n, d)
