@@ -53,6 +53,7 @@ def lib():
                                          c.c_void_p]
         L.nqo_bf16_to_f32.argtypes = [c.c_uint16]
         L.nqo_bf16_to_f32.restype = c.c_float
+        L.nqo_grouped_absmax.argtypes = [c.c_int, c.c_int, c.c_void_p, c.c_int64, c.c_int64, c.c_void_p, c.c_void_p]
         L.nqo_sizes_nvfp4_stacked.argtypes = [c.POINTER(c.c_int64), c.c_int, c.c_int64, c.POINTER(c.c_uint64),
                                               c.POINTER(c.c_uint64)]
         L.nqo_decode_nvfp4_stacked.argtypes = [c.c_void_p, c.c_uint64, c.POINTER(c.c_int64), c.c_int, c.c_int64,
@@ -182,6 +183,26 @@ def decode_fp8_row(fmt, payload, shape, dtype="f32"):
     if st != OK:
         raise ValueError(f"oracle decode of {fmt} {shape} failed: status {st}")
     return out
+
+
+GQ_SCHEMES = {"q4_g64_fp16": (0, 64, -8, 7), "q5_g64_fp16": (1, 64, -16, 15), "q6_g64_fp16": (2, 64, -32, 31),
+              "q8_g32_fp16": (3, 32, -127, 127)}
+_IN_DTYPES = {"f32": (0, np.float32), "f16": (1, np.uint16), "bf16": (2, np.uint16), "f64": (3, np.float64)}
+
+
+def grouped_absmax(scheme, x, in_dtype="f32"):
+    """grouped_absmax of a [N, K] array (f16/bf16 given as raw uint16 words).
+    Returns (status, codes int8 [N, K], scales uint16 [N, ceil(K/G)])."""
+    sid, G, _, _ = GQ_SCHEMES[scheme]
+    code, npt = _IN_DTYPES[in_dtype]
+    x = np.ascontiguousarray(x, dtype=npt)
+    N, K = x.shape
+    codes = np.zeros((N, K), dtype=np.int8)
+    scales = np.zeros((N, (K + G - 1) // G), dtype=np.uint16)
+    st = lib().nqo_grouped_absmax(sid, code, x.ctypes.data, N, K, codes.ctypes.data, scales.ctypes.data)
+    if st < 0:
+        raise ValueError(f"oracle grouped_absmax rejects {scheme} {x.shape} {in_dtype}")
+    return st, codes, scales
 
 
 def bf16_to_f32(w):

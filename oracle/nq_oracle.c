@@ -825,3 +825,69 @@ int nqo_decode_fp8_row(int scale_kind, const uint8_t *payload, uint64_t nbytes, 
     }
     return NQO_OK;
 }
+
+/* grouped_absmax (NInfer tensor-formats 7.2), step by step for one group of */
+/* binary32 values: amax of |x|; an all-zero group gives scale +0 and codes  */
+/* 0; otherwise raw = RN32(amax / qmax), scale16 = RN16(raw) with 0x0001 in   */
+/* place of +0 and failure on a non-finite scale, inv = RN32(1 / scale32),    */
+/* and each code is RN-to-integral-ties-even(RN32(x * inv)) clamped to        */
+/* [qmin, qmax].  The divisor is qmax, not |qmin|.                            */
+static const struct { int G, qmin, qmax; } GQ_SCHEMES[4] = {
+    {64, -8, 7}, {64, -16, 15}, {64, -32, 31}, {32, -127, 127}};
+
+static float gq_source(int in_dtype, const void *x, uint64_t i)
+{
+    switch (in_dtype) {
+    case 0: return ((const float *)x)[i];
+    case 1: return nqo_f16_to_f32(((const uint16_t *)x)[i]);
+    case 2: return nqo_bf16_to_f32(((const uint16_t *)x)[i]);
+    default: return (float)((const double *)x)[i]; /* C conversion: round to nearest even */
+    }
+}
+
+static int gq_group(int scheme, const float *v, int n, int8_t *code, uint16_t *scale)
+{
+    const int qmin = GQ_SCHEMES[scheme].qmin, qmax = GQ_SCHEMES[scheme].qmax;
+    int status = 0;
+    float amax = 0.0f;
+    for (int i = 0; i < n; i++) {
+        if (!isfinite(v[i])) status |= 1;
+        const float a = fabsf(v[i]);
+        if (a > amax) amax = a;
+    }
+    if (status) return status;
+    if (amax == 0.0f) {
+        *scale = 0x0000;
+        for (int i = 0; i < n; i++) code[i] = 0;
+        return 0;
+    }
+    const float raw = amax / (float)qmax;
+    uint16_t s16 = nqo_f32_to_f16(raw);
+    if (s16 == 0x0000) s16 = 0x0001; /* 2^-24 underflow rescue */
+    if ((s16 & 0x7C00) == 0x7C00) return 2;
+    *scale = s16;
+    const float inv = 1.0f / nqo_f16_to_f32(s16);
+    for (int i = 0; i < n; i++) {
+        const float r = rintf(v[i] * inv); /* default rounding: nearest, ties to even */
+        code[i] = (int8_t)(r < (float)qmin ? qmin : r > (float)qmax ? qmax : (int)r);
+    }
+    return 0;
+}
+
+int nqo_grouped_absmax(int scheme, int in_dtype, const void *x, int64_t N, int64_t K, int8_t *codes,
+                       uint16_t *scales)
+{
+    if (scheme < 0 || scheme > 3 || in_dtype < 0 || in_dtype > 3 || N <= 0 || K <= 0) return -1;
+    const int G = GQ_SCHEMES[scheme].G;
+    const int64_t ng = (K + G - 1) / G;
+    float v[64];
+    int status = 0;
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t g = 0; g < ng; g++) {
+            const int64_t k0 = g * G;
+            const int cnt = (int)(K - k0 < G ? K - k0 : G);
+            for (int i = 0; i < cnt; i++) v[i] = gq_source(in_dtype, x, (uint64_t)(n * K + k0 + i));
+            status |= gq_group(scheme, v, cnt, codes + n * K + k0, scales + n * ng + g);
+        }
+    return status;
+}

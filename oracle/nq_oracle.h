@@ -80,6 +80,18 @@ int nqo_sizes_fp8_row(const int64_t *shape, int rank, uint64_t *nbytes, uint64_t
 int nqo_decode_fp8_row(int scale_kind, const uint8_t *payload, uint64_t nbytes, const int64_t *shape,
                        int rank, int dtype, void *out);
 
+/* grouped_absmax encoder (NInfer tensor-formats section 7.2) for the grouped
+ * integer schemes 0 q4_g64_fp16, 1 q5_g64_fp16, 2 q6_g64_fp16, 3 q8_g32_fp16:
+ * a positive [N, K] matrix of source values (in_dtype 0 binary32, 1 binary16,
+ * 2 bfloat16, 3 binary64, converted to binary32 with round-to-nearest-even)
+ * becomes one signed code per value (codes[n*K + k], one byte each) and one
+ * binary16 scale per row and group of G columns (scales[n*ceil(K/G) + g]; the
+ * last group of a row may be short).  Returns -1 for a bad scheme, dtype or
+ * shape, else status bits: 1 a source value that is not finite in binary32,
+ * 2 a scale that does not fit binary16 (outputs are then unspecified). */
+int nqo_grouped_absmax(int scheme, int in_dtype, const void *x, int64_t N, int64_t K, int8_t *codes,
+                       uint16_t *scales);
+
 /* Decode `nblocks` back-to-back blocks to binary32 (no trailer; `d_w` is the
  * divisor used by "nvfp4" and ignored by every other format). */
 int nqo_decode_blocks_f32(int fmt, const uint8_t *blocks, uint64_t nblocks, float d_w, float *y);

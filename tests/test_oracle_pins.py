@@ -627,3 +627,84 @@ def test_fp8_row_length_rule(shape, want):
         assert nbytes == shape[0] * shape[1] + 2 * shape[0] and nelems == shape[0] * shape[1]
         with pytest.raises(ValueError):
             oracle.decode_fp8_row("fp8_e4m3fn_row_bf16", np.zeros(nbytes - 1, np.uint8), shape)
+
+
+# ---------------------------------------------------------------------------
+# grouped_absmax encoder (NInfer tensor-formats, section 7.2).
+# ---------------------------------------------------------------------------
+def _f32(v):
+    if isinstance(v, str):
+        return np.array([int(v, 16)], np.uint32).view(np.float32)[0]
+    return np.float32(v)
+
+
+def test_grouped_absmax_golden():
+    path = os.path.join(os.path.dirname(__file__), "golden", "grouped_absmax.json")
+    for ex in json.load(open(path))["examples"]:
+        x = np.array([[_f32(v) for v in ex["x"]]], np.float32)
+        st, codes, scales = oracle.grouped_absmax(ex["scheme"], x)
+        assert st == ex["status"], ex["id"]
+        if st == 0:
+            assert list(codes[0]) == ex["codes"], (ex["id"], list(codes[0]))
+            assert [hex(s) for s in scales[0]] == [hex(int(s, 16)) for s in ex["scales"]], ex["id"]
+
+
+@pytest.mark.parametrize("scheme", sorted(oracle.GQ_SCHEMES))
+def test_grouped_absmax_invariants(scheme):
+    """On random rows (log-uniform magnitudes, random signs, zero groups,
+    partial last groups): codes lie in [qmin, qmax]; each scale is the
+    binary16 rounding of amax / qmax (or the rescue, or +0 for a zero group);
+    a code that is not clamped reconstructs its value within half a scale
+    step; with a normal binary16 scale the largest magnitude maps to +-qmax
+    or qmin; zero groups are zero."""
+    sid, G, qmin, qmax = oracle.GQ_SCHEMES[scheme]
+    rng = np.random.default_rng(sid)
+    N, K = 9, 3 * G + 5
+    x = (rng.standard_normal((N, K)) * np.exp2(rng.integers(-34, 12, (N, 1)))).astype(np.float32)
+    x[2, :G] = 0.0
+    x[3, G:2 * G] = -0.0
+    st, codes, scales = oracle.grouped_absmax(scheme, x)
+    assert st == 0
+    assert codes.min() >= qmin and codes.max() <= qmax
+    s32 = torch.from_numpy(scales.astype(np.int32)).to(torch.int16).view(torch.float16).to(torch.float64).numpy()
+    for n in range(N):
+        for g in range((K + G - 1) // G):
+            v = x[n, g * G:(g + 1) * G].astype(np.float64)
+            q = codes[n, g * G:(g + 1) * G].astype(np.float64)
+            amax = np.abs(v).max()
+            if amax == 0:
+                assert scales[n, g] == 0 and not q.any()
+                continue
+            want = np.float64(np.float16(np.float32(amax / qmax)))  # binary16 RNE of the binary32 quotient
+            assert s32[n, g] == (want if want > 0 else 2.0 ** -24)
+            inner = (q > qmin) & (q < qmax)
+            assert np.all(np.abs(v[inner] - s32[n, g] * q[inner]) <= 0.5 * s32[n, g] * (1 + 2.0 ** -20))
+            if s32[n, g] >= 2.0 ** -14:  # a normal binary16 scale is within 2^-11 of amax / qmax
+                top = np.argmax(np.abs(v))
+                assert q[top] in (qmax, qmin, -qmax) and np.sign(q[top]) == np.sign(v[top])
+
+
+def test_grouped_absmax_source_types():
+    """binary16, bfloat16 and binary64 sources encode as their binary32 values
+    (torch converts them independently); a binary64 value past binary32
+    fails as non-finite."""
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((4, 70)) * 3).astype(np.float32)
+    for dt, tdt in (("f16", torch.float16), ("bf16", torch.bfloat16)):
+        t = torch.from_numpy(x).to(tdt)
+        words = t.view(torch.int16).numpy().view(np.uint16)
+        want = oracle.grouped_absmax("q5_g64_fp16", t.to(torch.float32).numpy())
+        got = oracle.grouped_absmax("q5_g64_fp16", words, dt)
+        assert got[0] == 0 and np.array_equal(got[1], want[1]) and np.array_equal(got[2], want[2])
+    x64 = x.astype(np.float64) * (1 + 1e-9)
+    want = oracle.grouped_absmax("q8_g32_fp16", x64.astype(np.float32))
+    got = oracle.grouped_absmax("q8_g32_fp16", x64, "f64")
+    assert np.array_equal(got[1], want[1]) and np.array_equal(got[2], want[2])
+    assert oracle.grouped_absmax("q8_g32_fp16", np.array([[1e39, 1.0]]), "f64")[0] == 1
+
+
+def test_grouped_absmax_rejects_bad_arguments():
+    with pytest.raises(ValueError):
+        oracle.grouped_absmax("q4_g64_fp16", np.zeros((0, 64), np.float32))
+    with pytest.raises(ValueError):
+        oracle.grouped_absmax("q4_g64_fp16", np.zeros((3, 0), np.float32))
