@@ -240,6 +240,46 @@ def fp8_row_measurement(torch, nq, fmt, shape, dtype, launches=60, footprint=1 <
     return res
 
 
+def gq_measurement(torch, nq, scheme, shape, in_dtype, launches=60, footprint=1 << 30, seed=0x6E7A6000):
+    """grouped_absmax encoder over rotating replicas of a normal source with
+    row magnitudes 2^-8 .. 2^4; bytes = source + codes + binary16 scales."""
+    import numpy as np
+    N, K = shape
+    sid, G = nq.GQ_SCHEMES[scheme]
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "f64": torch.float64}[in_dtype]
+    rng = np.random.default_rng(seed)
+    x = torch.from_numpy((rng.standard_normal((N, K)) * np.exp2(rng.integers(-8, 4, (N, 1)))).astype(np.float32))
+    x = x.to(tdt)
+    ng = (K + G - 1) // G
+    nbytes = x.numel() * x.element_size() + N * K + 2 * N * ng
+    reps = max(1, math.ceil(footprint / nbytes))
+    items = [(x.to("cuda:0"), torch.empty((N, K), dtype=torch.int8, device="cuda:0"),
+              torch.empty((N, ng), dtype=torch.int16, device="cuda:0"),
+              torch.empty(1, dtype=torch.int32, device="cuda:0")) for _ in range(reps)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        h = torch.cuda.current_stream().cuda_stream
+        for i in range(launches):
+            xs, c, sc, st = items[i % reps]
+            rc = nq.quantize_grouped_absmax_raw(sid, xs.data_ptr(), shape, nq.DTYPE_CODES[in_dtype], c.data_ptr(),
+                                                sc.data_ptr(), st.data_ptr(), h)
+            if rc != 0:
+                raise nq.NqError(rc, scheme)
+    ms, _ = time_graph(torch, g, 3)
+    torch.cuda.synchronize()
+    if any(int(it[3].item()) for it in items):
+        raise RuntimeError("grouped_absmax reported a failure on the benchmark source")
+    mean_ms = ms / launches
+    gbps = nbytes / (mean_ms * 1e-3) / 1e9
+    res = {"shape": shape, "in": in_dtype, "gbps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+           "mean_launch_us": round(mean_ms * 1e3, 3), "replicas": reps,
+           "elements_per_s": round(N * K / (mean_ms * 1e-3), 1), "bytes_per_launch": nbytes,
+           "note": "two launches per call (status clear + encoder)"}
+    del g, items
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(nq, synth, tensors, fraction=8):
     """The oracle on the first 1/fraction of every tensor's blocks, one thread."""
     import numpy as np
@@ -353,6 +393,10 @@ def main():
                                               0x6E710000 + 77 * nd, "bf16", st2, divisors=nd)
             log(f"{key}: {extra[key]['gbps']} GB/s ({100 * extra[key]['frac_hbm_peak']:.1f}% of peak)")
             del st2
+        for scheme, in_dtype in (("q4_g64_fp16", "bf16"), ("q8_g32_fp16", "f32")):
+            key = f"grouped_absmax {in_dtype}->{scheme}[14336, 4096]"
+            extra[key] = gq_measurement(torch, nq, scheme, [14336, 4096], in_dtype)
+            log(f"{key}: {extra[key]['gbps']} GB/s ({100 * extra[key]['frac_hbm_peak']:.1f}% of peak)")
         for fmt in ("fp8_e4m3fn_row_bf16", "fp8_e4m3fn_row_fp16"):
             key = f"{fmt}[14336, 4096]->bf16"
             extra[key] = fp8_row_measurement(torch, nq, fmt, [14336, 4096], "bf16")

@@ -21,7 +21,9 @@ DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "f64": 3}
 FAMILIES = {0: "simple", 1: "kquant", 2: "iq", 3: "fp4", 4: "ternary"}
 EXPORTS = ["nq_format_count", "nq_format_by_id", "nq_format_query", "nq_validate",
            "nq_dequantize_packed", "nq_validate_nvfp4_stacked", "nq_dequantize_nvfp4_stacked",
-           "nq_validate_fp8_row", "nq_dequantize_fp8_row", "nq_status_string"]
+           "nq_validate_fp8_row", "nq_dequantize_fp8_row", "nq_validate_grouped_absmax",
+           "nq_quantize_grouped_absmax", "nq_status_string"]
+GQ_SCHEMES = {"q4_g64_fp16": (0, 64), "q5_g64_fp16": (1, 64), "q6_g64_fp16": (2, 64), "q8_g32_fp16": (3, 32)}
 FP8_ROW_KINDS = {"fp8_e4m3fn_row_bf16": 0, "fp8_e4m3fn_row_fp16": 1}
 
 
@@ -68,6 +70,10 @@ def _lib():
                                           c.POINTER(c.c_uint64), c.POINTER(c.c_uint64)]
         L.nq_dequantize_fp8_row.argtypes = [c.c_int32, c.c_void_p, c.c_uint64, c.POINTER(c.c_int64), c.c_int32,
                                             c.c_int32, c.c_void_p, c.c_void_p]
+        L.nq_validate_grouped_absmax.argtypes = [c.c_int32, c.POINTER(c.c_int64), c.c_int32, c.c_int32,
+                                                 c.POINTER(c.c_uint64), c.POINTER(c.c_uint64)]
+        L.nq_quantize_grouped_absmax.argtypes = [c.c_int32, c.c_void_p, c.POINTER(c.c_int64), c.c_int32, c.c_int32,
+                                                 c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p]
         L.nq_status_string.argtypes = [c.c_int]
         L.nq_status_string.restype = c.c_char_p
         _LIB = L
@@ -218,6 +224,53 @@ def dequantize_fp8_row(fmt, payload, shape, out_dtype=None, out=None, stream=Non
     if st != NQ_OK:
         raise NqError(st, f"{fmt} {list(shape)}")
     return out
+
+
+def validate_grouped_absmax_status(scheme, shape, in_dtype="f32"):
+    """Raw status of nq_validate_grouped_absmax plus (codes bytes, scales bytes)."""
+    sid = GQ_SCHEMES[scheme][0] if isinstance(scheme, str) else int(scheme)
+    arr, rank = _shape(shape)
+    cb, sb = ctypes.c_uint64(), ctypes.c_uint64()
+    code = in_dtype if isinstance(in_dtype, int) else _dtype_code(in_dtype)
+    st = _lib().nq_validate_grouped_absmax(sid, arr, rank, code, ctypes.byref(cb), ctypes.byref(sb))
+    return st, cb.value, sb.value
+
+
+def quantize_grouped_absmax_raw(scheme_id, x_ptr, shape, in_dtype_code, codes_ptr, scales_ptr, status_ptr,
+                                stream_handle):
+    """Direct call of nq_quantize_grouped_absmax with integer addresses; returns the status."""
+    arr, rank = _shape(shape)
+    return _lib().nq_quantize_grouped_absmax(int(scheme_id), ctypes.c_void_p(x_ptr), arr, rank, in_dtype_code,
+                                             ctypes.c_void_p(codes_ptr), ctypes.c_void_p(scales_ptr),
+                                             ctypes.c_void_p(status_ptr), ctypes.c_void_p(stream_handle))
+
+
+def quantize_grouped_absmax(scheme, x, stream=None, check=True):
+    """Encode a contiguous [N, K] CUDA tensor (float32/float16/bfloat16/float64)
+    with grouped_absmax.  Returns (codes int8 [N, K], scales as int16 words
+    [N, ceil(K/G)], status int32 [1]).  With check=True the call waits for
+    the stream and raises NqError-like ValueError on an encoder failure."""
+    import torch
+    sid, G = GQ_SCHEMES[scheme]
+    if x.dim() != 2 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous rank-2 CUDA tensor")
+    N, K = x.shape
+    codes = torch.empty((N, K), dtype=torch.int8, device=x.device)
+    scales = torch.empty((N, (K + G - 1) // G), dtype=torch.int16, device=x.device)
+    status = torch.empty(1, dtype=torch.int32, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    st = quantize_grouped_absmax_raw(sid, x.data_ptr(), [N, K], _dtype_code(x.dtype), codes.data_ptr(),
+                                     scales.data_ptr(), status.data_ptr(), stream.cuda_stream)
+    if st != NQ_OK:
+        raise NqError(st, f"{scheme} {[N, K]}")
+    if check:
+        stream.synchronize()
+        bits = int(status.item())
+        if bits:
+            raise ValueError(f"grouped_absmax failed: status bits {bits:#x} "
+                             "(1: a source value is not finite, 2: a scale rounds past binary16)")
+    return codes, scales, status
 
 
 def dequantize_packed(fmt, payload, shape, out_dtype=None, out=None, stream=None):

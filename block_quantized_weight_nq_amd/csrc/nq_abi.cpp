@@ -11,6 +11,7 @@
 
 #include "../../include/nq.h"
 #include "nq_fp8row.h"
+#include "nq_gqenc.h"
 #include "nq_launch.h"
 
 #define NQ_API extern "C" __attribute__((visibility("default")))
@@ -244,6 +245,41 @@ NQ_API int nq_dequantize_fp8_row(int32_t scale_kind, const void *payload, uint64
     L.K = (uint64_t)shape[1];
     L.out = out;
     return nq::launch_fp8_row(scale_kind, out_dtype, L, stream);
+}
+
+NQ_API int nq_validate_grouped_absmax(int32_t scheme, const int64_t *shape, int32_t rank, int32_t in_dtype,
+                                      uint64_t *codes_bytes, uint64_t *scales_bytes) {
+    if (scheme < NQ_GQ_Q4_G64 || scheme > NQ_GQ_Q8_G32) return NQ_ERR_UNKNOWN_FORMAT;
+    if (in_dtype < NQ_F32 || in_dtype > NQ_F64) return NQ_ERR_BAD_DTYPE;
+    if (rank != 2) return NQ_ERR_BAD_RANK;
+    if (!shape) return NQ_ERR_NULL_ARG;
+    if (shape[0] <= 0 || shape[1] <= 0) return NQ_ERR_BAD_DIM;
+    const uint64_t N = (uint64_t)shape[0], K = (uint64_t)shape[1], G = (uint64_t)nq::GQ[scheme].G;
+    uint64_t elems = 0, in_bytes = 0, ngroups = 0, sbytes = 0;
+    if (K >= (1ull << 31) || !mul_checked(N, K, &elems) || !mul_checked(elems, OUT_SIZE[in_dtype], &in_bytes) ||
+        !mul_checked(N, (K + G - 1) / G, &ngroups) || !mul_checked(ngroups, 2, &sbytes))
+        return NQ_ERR_OVERFLOW;
+    if (codes_bytes) *codes_bytes = elems;
+    if (scales_bytes) *scales_bytes = sbytes;
+    return NQ_OK;
+}
+
+NQ_API int nq_quantize_grouped_absmax(int32_t scheme, const void *x, const int64_t *shape, int32_t rank,
+                                      int32_t in_dtype, void *codes, void *scales, uint32_t *status,
+                                      hipStream_t stream) {
+    const int st = nq_validate_grouped_absmax(scheme, shape, rank, in_dtype, nullptr, nullptr);
+    if (st != NQ_OK) return st;
+    if (!x || !codes || !scales || !status) return NQ_ERR_NULL_ARG;
+    if ((uintptr_t)x % OUT_SIZE[in_dtype] != 0 || (uintptr_t)scales % 2 != 0 || (uintptr_t)status % 4 != 0)
+        return NQ_ERR_NULL_ARG;
+    nq::GqLaunch L;
+    L.x = x;
+    L.codes = (int8_t *)codes;
+    L.scales = (uint16_t *)scales;
+    L.status = status;
+    L.N = (uint64_t)shape[0];
+    L.K = (uint64_t)shape[1];
+    return nq::launch_grouped_absmax(scheme, in_dtype, L, stream);
 }
 
 NQ_API const char *nq_status_string(int status) {

@@ -29,20 +29,8 @@ struct F8Args {
     uint32_t smis, slast;   // scale start - sbase (0..3); last dword holding chunk scales
     uint32_t n;             // values in this launch (<= 2^30)
     uint64_t col0;          // column of value E0 (E0 mod K)
-    uint32_t kmul, kshift;  // division by K <= 2^30 as a multiply-shift (f8_div_magic)
+    uint32_t kmul, kshift;  // division by K <= 2^30 as a multiply-shift (div_magic)
 };
-
-// Division of 31-bit numerators by d (1 <= d <= 2^30) as floor(n * m / 2^s):
-// with l = ceil(log2 d), m = floor(2^(31+l) / d) + 1 and s = 31 + l this is
-// exact for every 0 <= n < 2^31 (Granlund and Montgomery, "Division by
-// invariant integers using multiplication", 1994, theorem 4.2 with N = 31);
-// m < 2^32.
-NQ_HD void f8_div_magic(uint64_t d, uint32_t *m, uint32_t *s) {
-    uint32_t l = 0;
-    while ((1ull << l) < d) l++;
-    *m = (uint32_t)((1ull << (31 + l)) / d + 1);
-    *s = 31 + l;
-}
 
 // Exact E4M3FN value: the 7 magnitude bits placed at binary32 bits 26..20
 // give 2^-120 times the value (a binary32 subnormal when the E4M3FN exponent
@@ -254,7 +242,7 @@ NQ_HD F8Args f8_chunk_args(const F8Launch &L, uint64_t E0, uint32_t *grid, uint6
     a.col0 = E0 - r0 * L.K;
     a.kmul = 0;
     a.kshift = 0;
-    if (L.K <= F8_CHUNK) f8_div_magic(L.K, &a.kmul, &a.kshift);
+    if (L.K <= F8_CHUNK) div_magic(L.K, &a.kmul, &a.kshift);
     *grid = (uint32_t)((n + 8u * F8_WG_UNITS - 1) / (8u * F8_WG_UNITS));
     return a;
 }

@@ -230,6 +230,18 @@ NQ_HD void store1(void *out, uint64_t e, float y) {
     }
 }
 
+// Division of 31-bit numerators by d (1 <= d <= 2^30) as floor(n * m / 2^s):
+// with l = ceil(log2 d), m = floor(2^(31+l) / d) + 1 and s = 31 + l this is
+// exact for every 0 <= n < 2^31 (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994, theorem 4.2 with N = 31);
+// m < 2^32.  The host computes (m, s) once per launch.
+NQ_HD inline void div_magic(uint64_t d, uint32_t *m, uint32_t *s) {
+    uint32_t l = 0;
+    while ((1ull << l) < d) l++;
+    *m = (uint32_t)((1ull << (31 + l)) / d + 1);
+    *s = 31 + l;
+}
+
 constexpr int WG = 256;  // threads per workgroup (4 wave64)
 
 // ---------------------------------------------------------------------------

@@ -165,6 +165,40 @@ int nq_validate_fp8_row(int32_t scale_kind, uint64_t nbytes, const int64_t *shap
 int nq_dequantize_fp8_row(int32_t scale_kind, const void *payload, uint64_t nbytes, const int64_t *shape,
                           int32_t rank, int32_t out_dtype, void *out, hipStream_t stream);
 
+/* grouped_absmax encoder (NInfer "tensor-formats" page, section 7.2) for the
+ * grouped integer schemes: q4_g64_fp16 (codes -8..7, 64 columns per group),
+ * q5_g64_fp16 (-16..15), q6_g64_fp16 (-32..31), q8_g32_fp16 (-127..127, 32
+ * per group).  For each row and group of a [N, K] source matrix: amax of
+ * |x|; an all-zero group gives scale +0 and zero codes; otherwise raw =
+ * RN32(amax / qmax), scale16 = RN16(raw) (0x0001 if that is +0), inv =
+ * RN32(1 / scale32) and code = clamp(round-half-even(RN32(x * inv)), qmin,
+ * qmax).  Sources of in_dtype f16/bf16/f64 are converted to binary32 first
+ * (RNE).
+ *
+ * Outputs (the page leaves the packed row-split layout undefined): `codes`,
+ * N*K signed bytes row-major; `scales`, N*ceil(K/G) binary16 words row-major
+ * (the last group of a row may be short).  `status` is one device uint32:
+ * the call first clears it on `stream`, then ORs in 1 if a source value is
+ * not finite in binary32 and 2 if a scale rounds past binary16 (the encoder
+ * "fails"; the codes and scales of such groups are then unspecified).  Read
+ * it after the stream reaches this point.
+ *
+ * nq_validate_grouped_absmax checks, in this order: scheme
+ * (NQ_ERR_UNKNOWN_FORMAT), in_dtype (NQ_ERR_BAD_DTYPE), rank == 2
+ * (NQ_ERR_BAD_RANK), shape != NULL, both dimensions > 0 (NQ_ERR_BAD_DIM),
+ * K < 2^31 and the byte counts within INT64_MAX (NQ_ERR_OVERFLOW); it stores
+ * the byte sizes of codes and scales (either pointer may be NULL).
+ * nq_quantize_grouped_absmax validates the same way, then requires x,
+ * codes, scales and status non-NULL, x aligned to its element size, scales
+ * to 2 bytes and status to 4 (NQ_ERR_NULL_ARG), and enqueues the encoder;
+ * the caller owns every buffer.  x must not overlap the outputs. */
+typedef enum { NQ_GQ_Q4_G64 = 0, NQ_GQ_Q5_G64 = 1, NQ_GQ_Q6_G64 = 2, NQ_GQ_Q8_G32 = 3 } nq_grouped_scheme;
+
+int nq_validate_grouped_absmax(int32_t scheme, const int64_t *shape, int32_t rank, int32_t in_dtype,
+                               uint64_t *codes_bytes, uint64_t *scales_bytes);
+int nq_quantize_grouped_absmax(int32_t scheme, const void *x, const int64_t *shape, int32_t rank, int32_t in_dtype,
+                               void *codes, void *scales, uint32_t *status, hipStream_t stream);
+
 /* Static description of a status code. */
 const char *nq_status_string(int status);
 

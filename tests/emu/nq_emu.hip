@@ -17,6 +17,7 @@
 #include <vector>
 
 #include "../../block_quantized_weight_nq_amd/csrc/nq_fp8row.h"
+#include "../../block_quantized_weight_nq_amd/csrc/nq_gqenc.h"
 #include "../../block_quantized_weight_nq_amd/csrc/nq_kernel.h"
 
 namespace {
@@ -337,11 +338,129 @@ extern "C" __attribute__((visibility("default"))) long nq_emu_fp8_row(int kind, 
     return kind == 0 ? run_fp8_row_ot<0>(ot, payload, N, K, out, chunk, err, errlen)
                      : run_fp8_row_ot<1>(ot, payload, N, K, out, chunk, err, errlen);
 }
-// The row division of the row-scaled FP8 kernels: floor(n / d) as computed
-// from f8_div_magic, for the test against plain division.
+// The multiply-shift division of the row-scaled FP8 and encoder kernels:
+// floor(n / d) as computed from div_magic, for the test against plain
+// division.
 extern "C" __attribute__((visibility("default"))) uint32_t nq_emu_f8_div(uint32_t n, uint32_t d) {
     uint32_t m, sh;
-    nq::f8_div_magic(d, &m, &sh);
+    nq::div_magic(d, &m, &sh);
     return (uint32_t)(((uint64_t)n * m) >> sh);
+}
+namespace {
+
+// Source reader of the encoder emulation: element reads and 16-byte reads,
+// each checked against the launch's source elements [0, count).
+template <int ESZ>
+struct GqHostSrc {
+    const void *x;
+    uint64_t count;
+    Check *chk;
+    void check(uint64_t i, uint64_t n) const {
+        if (i + n > count && chk->errors++ == 0)
+            snprintf(chk->msg, sizeof chk->msg, "source elements %llu..%llu past %llu", (unsigned long long)i,
+                     (unsigned long long)(i + n), (unsigned long long)count);
+    }
+    template <int IN>
+    float one(uint64_t i) const {
+        check(i, 1);
+        return nq::gq_word_to_f32<IN>(x, i);
+    }
+    template <int IN>
+    void eight(uint64_t i, float (&v)[8]) const {
+        check(i, 8);
+        if (((uintptr_t)x + i * ESZ) % 16 != 0 && chk->errors++ == 0)
+            snprintf(chk->msg, sizeof chk->msg, "16-byte source load at element %llu is misaligned",
+                     (unsigned long long)i);
+        nq::GqDevSrc{x}.eight<IN>(i, v);
+    }
+};
+
+// The encoder launcher's decisions and chunks, and for every group of every
+// launch its lanes' phases: loads, the amax exchange, the encode and stores.
+template <int S, int IN>
+long run_gq(const void *x, uint64_t N, uint64_t K, int8_t *codes, uint16_t *scales, uint32_t *status, char *err,
+            int errlen) {
+    using namespace nq;
+    constexpr uint64_t ESZ = IN == 0 ? 4 : IN == 3 ? 8 : 2;
+    constexpr uint32_t G = (uint32_t)GQ[S].G, LPG = G / 8u;
+    const bool vin = (uintptr_t)x % 16 == 0 && (K * ESZ) % 16 == 0;
+    const bool vout = (uintptr_t)codes % 4 == 0 && K % 4 == 0;
+    const GqLaunch L{x, codes, scales, status, N, K};
+    *status = 0u;
+    long errors = 0;
+    for (uint64_t r0 = 0; r0 < N;) {
+        uint64_t rows;
+        uint32_t grid;
+        const GqArgs a = gq_chunk_args<S, IN>(L, r0, &rows, &grid);
+        if ((uint64_t)grid * WG < (uint64_t)a.ngroups * LPG) {
+            snprintf(err, errlen, "grid %u too small", grid);
+            return 1;
+        }
+        Check chk{0, 0, 0, {0}};
+        const GqHostSrc<(int)ESZ> src{a.x, rows * K, &chk};
+        for (uint32_t g = 0; g < a.ngroups; g++) {
+            float v[LPG][8], am[LPG];
+            bool bad[LPG];
+            uint64_t off[LPG];
+            uint32_t cnt[LPG];
+            float amax = 0.0f;
+            bool anybad = false;
+            for (uint32_t j = 0; j < LPG; j++) {
+                cnt[j] = gq_chunk(a, (int)G, g, j, &off[j]);
+                if (vin)
+                    gq_load<IN, true>(src, off[j], cnt[j], v[j], &am[j], &bad[j]);
+                else
+                    gq_load<IN, false>(src, off[j], cnt[j], v[j], &am[j], &bad[j]);
+                amax = am[j] > amax ? am[j] : amax;
+                anybad |= bad[j];
+            }
+            for (uint32_t j = 0; j < LPG; j++) {
+                uint32_t s16 = 0;
+                int8_t q[8];
+                const uint32_t st = anybad ? 1u : gq_encode<S>(amax, v[j], &s16, q);
+                if (st) {
+                    *status |= st;
+                    continue;
+                }
+                if (vout)
+                    gq_store<true>(a, off[j], cnt[j], q, g, j, s16);
+                else
+                    gq_store<false>(a, off[j], cnt[j], q, g, j, s16);
+            }
+        }
+        if (chk.errors) {
+            if (errors == 0) snprintf(err, errlen, "%s", chk.msg);
+            errors += chk.errors;
+        }
+        r0 += rows;
+    }
+    return errors;
+}
+
+template <int S>
+long run_gq_in(int in, const void *x, uint64_t N, uint64_t K, int8_t *c, uint16_t *sc, uint32_t *st, char *err,
+               int errlen) {
+    switch (in) {
+    case 0: return run_gq<S, 0>(x, N, K, c, sc, st, err, errlen);
+    case 1: return run_gq<S, 1>(x, N, K, c, sc, st, err, errlen);
+    case 2: return run_gq<S, 2>(x, N, K, c, sc, st, err, errlen);
+    default: return run_gq<S, 3>(x, N, K, c, sc, st, err, errlen);
+    }
+}
+
+}  // namespace
+
+// grouped_absmax through the encoder's own lane code; returns out-of-bounds
+// or misaligned source reads (0 on success) and stores the status bits.
+extern "C" __attribute__((visibility("default"))) long nq_emu_grouped_absmax(int scheme, int in, const void *x,
+                                                                            uint64_t N, uint64_t K, int8_t *codes,
+                                                                            uint16_t *scales, uint32_t *status,
+                                                                            char *err, int errlen) {
+    switch (scheme) {
+    case 0: return run_gq_in<0>(in, x, N, K, codes, scales, status, err, errlen);
+    case 1: return run_gq_in<1>(in, x, N, K, codes, scales, status, err, errlen);
+    case 2: return run_gq_in<2>(in, x, N, K, codes, scales, status, err, errlen);
+    default: return run_gq_in<3>(in, x, N, K, codes, scales, status, err, errlen);
+    }
 }
 #endif  // NQ_EMU_PART

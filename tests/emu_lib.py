@@ -61,6 +61,10 @@ def lib():
                                      ctypes.c_void_p, ctypes.c_uint64, ctypes.c_char_p, ctypes.c_int]
         L.nq_emu_fp8_row.restype = ctypes.c_long
         L.nq_emu_f8_div.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
+        L.nq_emu_grouped_absmax.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64,
+                                            ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_char_p, ctypes.c_int]
+        L.nq_emu_grouped_absmax.restype = ctypes.c_long
         L.nq_emu_f8_div.restype = ctypes.c_uint32
         L.nq_emu_choose_upt.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint32]
         L.nq_emu_choose_upt.restype = ctypes.c_int
@@ -127,3 +131,25 @@ def decode_fp8_row(kind, payload, N, K, dtype, mis=0, out_mis=0, chunk=0):
 def f8_div(n, d):
     """The FP8 row kernels' multiply-shift division floor(n / d)."""
     return lib().nq_emu_f8_div(n, d)
+
+
+def grouped_absmax(scheme_id, G, x, in_code, x_mis=0, codes_mis=0):
+    """The encoder through the emulator.  x: [N, K] array (raw words for
+    f16/bf16).  Returns (status, codes, scales, bad reads, message, guards_ok)."""
+    x = np.ascontiguousarray(x)
+    N, K = x.shape
+    xbuf, xoff = _placed(x.nbytes, 16, x_mis)
+    xbuf[xoff:xoff + x.nbytes] = x.view(np.uint8).ravel()
+    cbuf, coff = _placed(N * K, 16, codes_mis)
+    cbuf[:] = 0xA5
+    ng = (K + G - 1) // G
+    sbuf = np.full(N * ng + 16, 0xA5A5, dtype=np.uint16)
+    status = np.zeros(1, dtype=np.uint32)
+    err = ctypes.create_string_buffer(256)
+    rc = lib().nq_emu_grouped_absmax(scheme_id, in_code, xbuf.ctypes.data + xoff, N, K, cbuf.ctypes.data + coff,
+                                     sbuf.ctypes.data + 16, status.ctypes.data, err, 256)
+    guards = bool(np.all(cbuf[:coff] == 0xA5) and np.all(cbuf[coff + N * K:] == 0xA5) and
+                  np.all(sbuf[:8] == 0xA5A5) and np.all(sbuf[8 + N * ng:] == 0xA5A5))
+    codes = cbuf[coff:coff + N * K].view(np.int8).reshape(N, K).copy()
+    scales = sbuf[8:8 + N * ng].reshape(N, ng).copy()
+    return int(status[0]), codes, scales, rc, err.value.decode(), guards

@@ -182,3 +182,27 @@ def test_fp8_row_rejects_before_device():
     assert nq.dequantize_fp8_row_raw(0, p, 21, [3, 5], 0, p + 2, 0) == 1   # f32 output not element-aligned
     assert nq.dequantize_fp8_row_raw(1, p, 21, [15], 0, p, 0) == 3
     assert nq.dequantize_fp8_row_raw(1, p, 0, [0, 5], 0, p, 0) == 4
+
+
+@pytest.mark.parametrize("scheme,G", [("q4_g64_fp16", 64), ("q8_g32_fp16", 32)])
+def test_grouped_absmax_validation(scheme, G):
+    assert nq.validate_grouped_absmax_status(scheme, [3, 70]) == (0, 210, 3 * ((70 + G - 1) // G) * 2)
+    assert nq.validate_grouped_absmax_status(scheme, [3, 70], "bf16")[0] == 0
+    assert nq.validate_grouped_absmax_status(scheme, [3, 70], 7)[0] == 8
+    assert nq.validate_grouped_absmax_status(scheme, [210])[0] == 3
+    assert nq.validate_grouped_absmax_status(scheme, [0, 70])[0] == 4
+    assert nq.validate_grouped_absmax_status(scheme, [3, -1])[0] == 4
+    assert nq.validate_grouped_absmax_status(scheme, [1, 1 << 31])[0] == 7
+    assert nq.validate_grouped_absmax_status(scheme, [1 << 40, 1 << 30])[0] == 7
+    assert nq.validate_grouped_absmax_status(9, [3, 70])[0] == 2
+
+
+def test_grouped_absmax_rejects_before_device():
+    buf = np.zeros(64, dtype=np.uint32)
+    p = buf.ctypes.data
+    assert nq.quantize_grouped_absmax_raw(0, 0, [2, 8], 0, p, p, p, 0) == 1
+    assert nq.quantize_grouped_absmax_raw(0, p, [2, 8], 0, p, p, 0, 0) == 1
+    assert nq.quantize_grouped_absmax_raw(0, p + 2, [2, 8], 0, p, p, p, 0) == 1   # f32 source misaligned
+    assert nq.quantize_grouped_absmax_raw(0, p, [2, 8], 0, p, p + 1, p, 0) == 1   # scales misaligned
+    assert nq.quantize_grouped_absmax_raw(0, p, [2, 8], 0, p, p, p + 2, 0) == 1   # status misaligned
+    assert nq.quantize_grouped_absmax_raw(4, p, [2, 8], 0, p, p, p, 0) == 2

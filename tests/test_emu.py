@@ -190,3 +190,56 @@ def test_fp8_row_division_by_multiplication():
         for n in ns:
             if 0 <= n <= top:
                 assert emu_lib.f8_div(n, d) == n // d, (n, d)
+
+
+def _gq_source(rng, N, K, in_dtype):
+    x = (rng.standard_normal((N, K)) * np.exp2(rng.integers(-30, 10, (N, 1)))).astype(np.float32)
+    x[0, : min(K, 40)] = 0.0
+    if in_dtype == "f32":
+        return x, x
+    if in_dtype == "f64":
+        x64 = x.astype(np.float64) * (1 + 2.0 ** -30)
+        return x64, x64
+    import torch
+    t = torch.from_numpy(x).to(torch.float16 if in_dtype == "f16" else torch.bfloat16)
+    w = t.view(torch.int16).numpy().view(np.uint16)
+    return w, w
+
+
+@pytest.mark.parametrize("scheme", ["q4_g64_fp16", "q5_g64_fp16", "q6_g64_fp16", "q8_g32_fp16"])
+@pytest.mark.parametrize("in_dtype", ["f32", "f16", "bf16", "f64"])
+def test_emulated_grouped_absmax(scheme, in_dtype):
+    """The encoder's lane code against the oracle: full and short last groups,
+    rows not a multiple of 8 or 4 values, rows shorter than a lane's 8 values,
+    aligned and misaligned sources and code outputs (vector and element
+    paths), zero groups, tiny (rescued) and large scales."""
+    sid, G, _, _ = oracle.GQ_SCHEMES[scheme]
+    code = {"f32": 0, "f16": 1, "bf16": 2, "f64": 3}[in_dtype]
+    esz = {"f32": 4, "f16": 2, "bf16": 2, "f64": 8}[in_dtype]
+    rng = np.random.default_rng(sid * 10 + code)
+    for N, K in ((5, 4 * G), (3, 3 * G + 24), (4, 70), (6, 13), (2, 5), (1, G), (9, 2 * G + 3)):
+        x, ox = _gq_source(rng, N, K, in_dtype)
+        want = oracle.grouped_absmax(scheme, ox, in_dtype)
+        for x_mis, c_mis in ((0, 0), (esz, 1), (0, 2)):
+            st, codes, scales, bad, msg, guards = emu_lib.grouped_absmax(sid, G, x, code, x_mis, c_mis)
+            assert bad == 0, (N, K, x_mis, msg)
+            assert guards
+            assert st == want[0] == 0
+            assert np.array_equal(codes, want[1]), (N, K, x_mis, c_mis)
+            assert np.array_equal(scales, want[2]), (N, K, x_mis, c_mis)
+
+
+def test_emulated_grouped_absmax_failures():
+    """Non-finite sources and scales past binary16 set the same status bits as
+    the oracle (other groups still encode)."""
+    x = np.ones((3, 64), np.float32)
+    x[1, 5] = np.inf
+    x[2, 9] = 8321040.0  # raw scale 65520 for q8 -> binary16 infinity
+    for scheme in ("q8_g32_fp16", "q4_g64_fp16"):
+        sid, G, _, _ = oracle.GQ_SCHEMES[scheme]
+        st, codes, scales, bad, msg, guards = emu_lib.grouped_absmax(sid, G, x, 0)
+        want = oracle.grouped_absmax(scheme, x)
+        assert bad == 0 and guards
+        assert st == want[0]
+        assert np.array_equal(codes[0], want[1][0]) and np.array_equal(scales[0], want[2][0])
+    assert emu_lib.grouped_absmax(3, 32, x, 0)[0] == 3

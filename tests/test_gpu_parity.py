@@ -356,3 +356,72 @@ def test_fp8_row_full_size():
     for fmt, sw in (("fp8_e4m3fn_row_bf16", bf), ("fp8_e4m3fn_row_fp16", f16)):
         announce(f"fp8_row full size {fmt}")
         _fp8_check(fmt, _fp8_payload(14336, 4096, 11, sw), [14336, 4096], "bf16")
+
+
+# ---------------------------------------------------------------------------
+# grouped_absmax encoder (q4/q5/q6_g64_fp16, q8_g32_fp16).
+# ---------------------------------------------------------------------------
+_GQ_TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "f64": torch.float64}
+
+
+def _gq_case(scheme, N, K, in_dtype, seed, x_off=0, c_off=0):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((N, K)) * np.exp2(rng.integers(-30, 10, (N, 1)))).astype(np.float32)
+    x[0, : min(K, 40)] = 0.0
+    t = torch.from_numpy(x).to(_GQ_TORCH[in_dtype])
+    ox = t.view(torch.int16).numpy().view(np.uint16) if in_dtype in ("f16", "bf16") else t.numpy()
+    st, wc, ws = oracle.grouped_absmax(scheme, ox, in_dtype)
+    assert st == 0
+    sid, G = nq.GQ_SCHEMES[scheme]
+    # place the source and the codes at the requested offsets of larger buffers
+    xb = torch.zeros(N * K + 16, dtype=t.dtype, device="cuda:0")
+    xb[x_off:x_off + N * K].copy_(t.reshape(-1))
+    cb = torch.full((N * K + 64,), 0x5A, dtype=torch.int8, device="cuda:0")
+    ng = (K + G - 1) // G
+    sb = torch.full((N * ng + 8,), 0x5A5A, dtype=torch.int16, device="cuda:0")
+    status = torch.full((1,), -1, dtype=torch.int32, device="cuda:0")
+    h = torch.cuda.current_stream().cuda_stream
+    rc = nq.quantize_grouped_absmax_raw(sid, xb.data_ptr() + x_off * xb.element_size(), [N, K],
+                                        nq.DTYPE_CODES[in_dtype], cb.data_ptr() + c_off, sb.data_ptr(),
+                                        status.data_ptr(), h)
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    got_c = cb[c_off:c_off + N * K].cpu().numpy().reshape(N, K)
+    got_s = sb[:N * ng].cpu().numpy().view(np.uint16).reshape(N, ng)
+    assert np.array_equal(got_c, wc), f"{scheme} {N}x{K} {in_dtype} codes differ at {np.argwhere(got_c != wc)[:4]}"
+    assert np.array_equal(got_s, ws), f"{scheme} {N}x{K} {in_dtype} scales differ"
+    assert bool((cb[:c_off] == 0x5A).all()) and bool((cb[c_off + N * K:] == 0x5A).all())
+    assert bool((sb[N * ng:] == 0x5A5A).all())
+
+
+@pytest.mark.parametrize("scheme", ["q4_g64_fp16", "q5_g64_fp16", "q6_g64_fp16", "q8_g32_fp16"])
+@pytest.mark.parametrize("in_dtype", ["f32", "f16", "bf16", "f64"])
+def test_grouped_absmax_matches_oracle(scheme, in_dtype):
+    G = nq.GQ_SCHEMES[scheme][1]
+    for N, K, x_off, c_off in ((33, 4 * G, 0, 0), (7, 3 * G + 24, 0, 0), (5, 70, 1, 3), (9, 13, 0, 1),
+                               (3, 5, 2, 0), (257, 2 * G + 3, 0, 0), (64, 1024, 3, 2)):
+        announce(f"grouped_absmax {scheme} {in_dtype} {N}x{K} x_off={x_off} c_off={c_off}")
+        _gq_case(scheme, N, K, in_dtype, N * 7 + K, x_off, c_off)
+
+
+def test_grouped_absmax_full_size():
+    for scheme, in_dtype in (("q4_g64_fp16", "bf16"), ("q8_g32_fp16", "f32")):
+        announce(f"grouped_absmax full size {scheme} {in_dtype} [4096, 4096]")
+        _gq_case(scheme, 4096, 4096, in_dtype, 99)
+
+
+def test_grouped_absmax_failures_and_status_reset():
+    """Encoder failures set the status bits; the next call clears them."""
+    x = torch.ones((3, 64), dtype=torch.float32, device="cuda:0")
+    x[1, 5] = float("inf")
+    x[2, 9] = 8321040.0  # q8: raw scale 65520 rounds to binary16 infinity
+    announce("grouped_absmax failures")
+    _, _, status = nq.quantize_grouped_absmax("q8_g32_fp16", x, check=False)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 3
+    with pytest.raises(ValueError):
+        nq.quantize_grouped_absmax("q8_g32_fp16", x)
+    y = torch.ones((3, 64), dtype=torch.float32, device="cuda:0")
+    codes, scales, status = nq.quantize_grouped_absmax("q8_g32_fp16", y)
+    assert int(status.item()) == 0 and bool((codes == 127).all())
