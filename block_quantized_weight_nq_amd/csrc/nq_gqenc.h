@@ -13,11 +13,12 @@
 // code byte per value, codes[n*K + k], and one binary16 scale per row and
 // group, scales[n*ceil(K/G) + g]; the last group of a row may be short.
 //
-// Work split: a lane encodes 8 consecutive values of one group; the G/8
+// Work split: a lane encodes VPL consecutive values of one group (32 source
+// bytes: 8 binary32, 16 binary16/bfloat16 or 4 binary64 values); the G/VPL
 // lanes of a group are consecutive lanes of a wave and reduce amax with
-// cross-lane exchanges.  A wave covers 512 values (8 groups of 64 or 16 of
-// 32): its source loads and its code store are contiguous.  Failures set
-// bits of a caller-owned status word with an atomic OR.
+// cross-lane exchanges.  A wave's source loads and code stores are
+// contiguous.  Failures set bits of a caller-owned status word with an
+// atomic OR.
 #pragma once
 
 #include "nq_kernel.h"
@@ -54,16 +55,26 @@ NQ_HD float gq_word_to_f32(const void *x, uint64_t i) {
         return (float)((const double *)x)[i];
 }
 
-// Source reader of the kernels: element by element, or 8 values with 16-byte
-// loads when they start on a 16-byte boundary.
+// Values per lane: 32 source bytes (two 16-byte loads) per lane, so that
+// each load instruction of a wave covers 64 lanes at a 32-byte stride
+// (measured: 16 values of a 4-byte source per lane, at a 64-byte stride, is
+// 23% slower; 8 values of a 2-byte source, 16% slower than 16).
+template <int IN>
+constexpr int gq_vpl() {
+    return IN == 0 ? 8 : IN == 3 ? 4 : 16;
+}
+
+// Source reader of the kernels: element by element, or a lane's VPL values
+// with 16-byte loads when they start on a 16-byte boundary.
 struct GqDevSrc {
     const void *x;
     template <int IN>
     NQ_HD float one(uint64_t i) const { return gq_word_to_f32<IN>(x, i); }
     template <int IN>
-    NQ_HD void eight(uint64_t i, float (&v)[8]) const {
+    NQ_HD void span(uint64_t i, float (&v)[gq_vpl<IN>()]) const {
+        constexpr int GQ_VPL = gq_vpl<IN>();
         constexpr int ESZ = IN == 0 ? 4 : IN == 3 ? 8 : 2;
-        constexpr int NV = 8 * ESZ / 16;  // 16-byte loads
+        constexpr int NV = GQ_VPL * ESZ / 16;  // 16-byte loads
         u32x4 w[NV];
         const u32x4 *p = (const u32x4 *)((const uint8_t *)x + i * ESZ);
 #pragma unroll
@@ -76,7 +87,7 @@ struct GqDevSrc {
         }
         const uint32_t *d = (const uint32_t *)w;
 #pragma unroll
-        for (int k = 0; k < 8; k++) {
+        for (int k = 0; k < GQ_VPL; k++) {
             if constexpr (IN == 0)
                 v[k] = bits_f32(d[k]);
             else if constexpr (IN == 1)
@@ -100,28 +111,31 @@ NQ_HD uint32_t gq_f32_to_f16(float v) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(p, f16x2)) & 0xFFFFu;
 }
 
-// Group g (launch-relative) of lane-chunk j (values j*8 .. j*8+7 of the group):
-// the chunk's source offset from x, and how many of its values exist.
+// Group g (launch-relative) of lane-chunk j (values j*VPL .. j*VPL+VPL-1 of
+// the group): the chunk's source offset from x, and how many of its values
+// exist.
+template <int GQ_VPL>
 NQ_HD uint32_t gq_chunk(const GqArgs &a, int G, uint32_t g, uint32_t j, uint64_t *off) {
     const uint32_t r = (uint32_t)(((uint64_t)g * a.gmul) >> a.gshift);  // row, g / ngr
-    const uint32_t col = (g - r * a.ngr) * (uint32_t)G + 8u * j;
+    const uint32_t col = (g - r * a.ngr) * (uint32_t)G + (uint32_t)GQ_VPL * j;
     *off = (uint64_t)r * a.K + col;
-    return col >= a.K ? 0u : (a.K - col < 8u ? a.K - col : 8u);
+    return col >= a.K ? 0u : (a.K - col < (uint32_t)GQ_VPL ? a.K - col : (uint32_t)GQ_VPL);
 }
 
-// Phase 1: a lane's 8 source values (zeros past the group's end), their
+// Phase 1: a lane's GQ_VPL source values (zeros past the group's end), their
 // amax and whether one is not finite.
-template <int IN, bool VECIN, class Src>
-NQ_HD void gq_load(const Src &src, uint64_t off, uint32_t cnt, float (&v)[8], float *amax, bool *bad) {
-    if (VECIN && cnt == 8u) {
-        src.template eight<IN>(off, v);
+template <int IN, bool VECIN, class Src, int GQ_VPL = gq_vpl<IN>()>
+NQ_HD void gq_load(const Src &src, uint64_t off, uint32_t cnt, float (&v)[GQ_VPL], float *amax, bool *bad) {
+    if (VECIN && cnt == (uint32_t)GQ_VPL) {
+        src.template span<IN>(off, v);
     } else {
-        for (int k = 0; k < 8; k++) v[k] = (uint32_t)k < cnt ? src.template one<IN>(off + (uint64_t)k) : 0.0f;
+        for (int k = 0; k < GQ_VPL; k++)
+            v[k] = (uint32_t)k < cnt ? src.template one<IN>(off + (uint64_t)k) : 0.0f;
     }
     float m = 0.0f;
     bool b = false;
 #pragma unroll
-    for (int k = 0; k < 8; k++) {
+    for (int k = 0; k < GQ_VPL; k++) {
         b |= !gq_finite(v[k]);
         const float t = __builtin_fabsf(v[k]);
         m = t > m ? t : m;
@@ -132,13 +146,13 @@ NQ_HD void gq_load(const Src &src, uint64_t off, uint32_t cnt, float (&v)[8], fl
 
 // Phase 3: the group's scale word from its amax (every lane of the group
 // computes it), and the lane's codes.  Returns status bits.
-template <int S>
-NQ_HD uint32_t gq_encode(float amax, const float (&v)[8], uint32_t *s16_out, int8_t (&q)[8]) {
+template <int S, int GQ_VPL>
+NQ_HD uint32_t gq_encode(float amax, const float (&v)[GQ_VPL], uint32_t *s16_out, int8_t (&q)[GQ_VPL]) {
     constexpr int qmin = GQ[S].qmin, qmax = GQ[S].qmax;
     if (amax == 0.0f) {
         *s16_out = 0u;
 #pragma unroll
-        for (int k = 0; k < 8; k++) q[k] = 0;
+        for (int k = 0; k < GQ_VPL; k++) q[k] = 0;
         return 0u;
     }
     const float raw = amax / (float)qmax;  // correctly rounded binary32 division
@@ -148,29 +162,38 @@ NQ_HD uint32_t gq_encode(float amax, const float (&v)[8], uint32_t *s16_out, int
     if ((s16 & 0x7C00u) == 0x7C00u) return 2u;
     const float inv = 1.0f / f16(s16);
 #pragma unroll
-    for (int k = 0; k < 8; k++) {
+    for (int k = 0; k < GQ_VPL; k++) {
         const float r = __builtin_rintf(M(v[k], inv));  // round half to even
         q[k] = (int8_t)(r < (float)qmin ? qmin : r > (float)qmax ? qmax : (int)r);
     }
     return 0u;
 }
 
-// Phase 3 stores: the lane's codes (8 bytes, or the cnt that exist) and, for
-// the group's first lane, the scale word.
-template <bool VECOUT>
-NQ_HD void gq_store(const GqArgs &a, uint64_t off, uint32_t cnt, const int8_t (&q)[8], uint32_t g, uint32_t j,
-                    uint32_t s16) {
-    if (VECOUT && cnt == 8u) {
-        uint32_t lo = 0u, hi = 0u;
+// Phase 3 stores: the lane's codes (GQ_VPL bytes, or the cnt that exist) and,
+// for the group's first lane, the scale word.
+template <bool VECOUT, int GQ_VPL>
+NQ_HD void gq_store(const GqArgs &a, uint64_t off, uint32_t cnt, const int8_t (&q)[GQ_VPL], uint32_t g,
+                    uint32_t j, uint32_t s16) {
+    if (VECOUT && cnt == (uint32_t)GQ_VPL) {
+        uint32_t w[GQ_VPL / 4];
 #pragma unroll
-        for (int k = 0; k < 4; k++) {
-            lo |= (uint32_t)(uint8_t)q[k] << (8 * k);
-            hi |= (uint32_t)(uint8_t)q[4 + k] << (8 * k);
+        for (int d = 0; d < GQ_VPL / 4; d++) {
+            w[d] = 0u;
+#pragma unroll
+            for (int k = 0; k < 4; k++) w[d] |= (uint32_t)(uint8_t)q[4 * d + k] << (8 * k);
         }
-        u32x2a4 w;
-        w.x = lo;
-        w.y = hi;
-        *(u32x2a4 *)(a.codes + off) = w;
+        uint32_t *p = (uint32_t *)(a.codes + off);
+        if constexpr (GQ_VPL == 4) {
+            p[0] = w[0];
+        } else {
+#pragma unroll
+            for (int d = 0; d < GQ_VPL / 4; d += 2) {
+                u32x2a4 v;
+                v.x = w[d];
+                v.y = w[d + 1];
+                *(u32x2a4 *)(p + d) = v;
+            }
+        }
     } else {
         for (uint32_t k = 0; k < cnt; k++) a.codes[off + k] = q[k];
     }
@@ -180,13 +203,14 @@ NQ_HD void gq_store(const GqArgs &a, uint64_t off, uint32_t cnt, const int8_t (&
 template <int S, int IN, bool VECIN, bool VECOUT>
 __global__ __launch_bounds__(WG) void k_grouped_absmax(GqArgs a) {
     constexpr int G = GQ[S].G;
-    constexpr uint32_t LPG = (uint32_t)G / 8u;  // lanes per group
+    constexpr int GQ_VPL = gq_vpl<IN>();
+    constexpr uint32_t LPG = (uint32_t)(G / GQ_VPL);  // lanes per group
     const uint32_t lin = blockIdx.x * (uint32_t)WG + threadIdx.x;
     const uint32_t g = lin / LPG, j = lin % LPG;
     const bool live = g < a.ngroups;
     uint64_t off = 0;
-    const uint32_t cnt = live ? gq_chunk(a, G, g, j, &off) : 0u;
-    float v[8];
+    const uint32_t cnt = live ? gq_chunk<GQ_VPL>(a, G, g, j, &off) : 0u;
+    float v[GQ_VPL];
     float amax;
     bool bad;
     gq_load<IN, VECIN>(GqDevSrc{a.x}, off, cnt, v, &amax, &bad);
@@ -200,13 +224,13 @@ __global__ __launch_bounds__(WG) void k_grouped_absmax(GqArgs a) {
     }
     if (!live) return;
     uint32_t s16 = 0;
-    int8_t q[8];
+    int8_t q[GQ_VPL];
     const uint32_t st = bad ? 1u : gq_encode<S>(amax, v, &s16, q);
     if (st != 0u) {
         if (j == 0u) atomicOr(a.status, st);
         return;
     }
-    gq_store<VECOUT>(a, off, cnt, q, g, j, s16);
+    gq_store<VECOUT, GQ_VPL>(a, off, cnt, q, g, j, s16);
 }
 
 // Host side: one matrix, split into launches of at most 2^30 groups.
@@ -224,7 +248,7 @@ constexpr uint64_t GQ_CHUNK_GROUPS = 1ull << 30;  // groups per launch at most
 // limit), with its row count and grid size.
 template <int S, int IN>
 NQ_HD GqArgs gq_chunk_args(const GqLaunch &L, uint64_t r0, uint64_t *rows, uint32_t *grid) {
-    constexpr uint64_t G = (uint64_t)GQ[S].G, LPG = G / 8;
+    constexpr uint64_t G = (uint64_t)GQ[S].G, LPG = G / (uint64_t)gq_vpl<IN>();
     constexpr uint64_t ESZ = IN == 0 ? 4 : IN == 3 ? 8 : 2;
     const uint64_t ngr = (L.K + G - 1) / G;
     const uint64_t per = GQ_CHUNK_GROUPS / ngr;  // ngr <= 2^26, so per >= 16

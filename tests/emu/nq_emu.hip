@@ -366,12 +366,12 @@ struct GqHostSrc {
         return nq::gq_word_to_f32<IN>(x, i);
     }
     template <int IN>
-    void eight(uint64_t i, float (&v)[8]) const {
-        check(i, 8);
+    void span(uint64_t i, float (&v)[nq::gq_vpl<IN>()]) const {
+        check(i, nq::gq_vpl<IN>());
         if (((uintptr_t)x + i * ESZ) % 16 != 0 && chk->errors++ == 0)
             snprintf(chk->msg, sizeof chk->msg, "16-byte source load at element %llu is misaligned",
                      (unsigned long long)i);
-        nq::GqDevSrc{x}.eight<IN>(i, v);
+        nq::GqDevSrc{x}.span<IN>(i, v);
     }
 };
 
@@ -382,7 +382,8 @@ long run_gq(const void *x, uint64_t N, uint64_t K, int8_t *codes, uint16_t *scal
             int errlen) {
     using namespace nq;
     constexpr uint64_t ESZ = IN == 0 ? 4 : IN == 3 ? 8 : 2;
-    constexpr uint32_t G = (uint32_t)GQ[S].G, LPG = G / 8u;
+    constexpr int GQ_VPL = gq_vpl<IN>();
+    constexpr uint32_t G = (uint32_t)GQ[S].G, LPG = G / (uint32_t)GQ_VPL;
     const bool vin = (uintptr_t)x % 16 == 0 && (K * ESZ) % 16 == 0;
     const bool vout = (uintptr_t)codes % 4 == 0 && K % 4 == 0;
     const GqLaunch L{x, codes, scales, status, N, K};
@@ -399,14 +400,14 @@ long run_gq(const void *x, uint64_t N, uint64_t K, int8_t *codes, uint16_t *scal
         Check chk{0, 0, 0, {0}};
         const GqHostSrc<(int)ESZ> src{a.x, rows * K, &chk};
         for (uint32_t g = 0; g < a.ngroups; g++) {
-            float v[LPG][8], am[LPG];
+            float v[LPG][GQ_VPL], am[LPG];
             bool bad[LPG];
             uint64_t off[LPG];
             uint32_t cnt[LPG];
             float amax = 0.0f;
             bool anybad = false;
             for (uint32_t j = 0; j < LPG; j++) {
-                cnt[j] = gq_chunk(a, (int)G, g, j, &off[j]);
+                cnt[j] = gq_chunk<GQ_VPL>(a, (int)G, g, j, &off[j]);
                 if (vin)
                     gq_load<IN, true>(src, off[j], cnt[j], v[j], &am[j], &bad[j]);
                 else
@@ -416,16 +417,16 @@ long run_gq(const void *x, uint64_t N, uint64_t K, int8_t *codes, uint16_t *scal
             }
             for (uint32_t j = 0; j < LPG; j++) {
                 uint32_t s16 = 0;
-                int8_t q[8];
+                int8_t q[GQ_VPL];
                 const uint32_t st = anybad ? 1u : gq_encode<S>(amax, v[j], &s16, q);
                 if (st) {
                     *status |= st;
                     continue;
                 }
                 if (vout)
-                    gq_store<true>(a, off[j], cnt[j], q, g, j, s16);
+                    gq_store<true, GQ_VPL>(a, off[j], cnt[j], q, g, j, s16);
                 else
-                    gq_store<false>(a, off[j], cnt[j], q, g, j, s16);
+                    gq_store<false, GQ_VPL>(a, off[j], cnt[j], q, g, j, s16);
             }
         }
         if (chk.errors) {
