@@ -67,6 +67,9 @@ def lib():
         L.nqo_e4m3fn_to_f32.argtypes = [c.c_uint8]
         L.nqo_e4m3fn_to_f32.restype = c.c_float
         L.nqo_convert.argtypes = [c.c_void_p, c.c_uint64, c.c_int, c.c_void_p]
+        L.nqo_quantize_q8_1.argtypes = [c.c_int, c.c_void_p, c.c_int64, c.c_int64, c.c_void_p]
+        L.nqo_gemv_q8_1.argtypes = [c.c_int, c.c_void_p, c.c_uint64, c.c_int64, c.c_int64, c.c_void_p, c.c_int64,
+                                    c.c_void_p, c.c_void_p]
         L.nqo_grid_rows.argtypes = [c.c_int]
         L.nqo_grid_width.argtypes = [c.c_int]
         L.nqo_grid_value.argtypes = [c.c_int, c.c_int, c.c_int]
@@ -203,6 +206,34 @@ def grouped_absmax(scheme, x, in_dtype="f32"):
     if st < 0:
         raise ValueError(f"oracle grouped_absmax rejects {scheme} {x.shape} {in_dtype}")
     return st, codes, scales
+
+
+def quantize_q8_1(x, in_dtype="f32"):
+    """q8_1 activation blocks of a [M, K] array (K % 32 == 0; f16/bf16 given as
+    raw uint16 words).  Returns (status, blocks uint8 [M, K/32, 36])."""
+    code, npt = _IN_DTYPES[in_dtype]
+    x = np.ascontiguousarray(x, dtype=npt)
+    M, K = x.shape
+    blocks = np.zeros((M, K // 32, 36), dtype=np.uint8)
+    st = lib().nqo_quantize_q8_1(code, x.ctypes.data, M, K, blocks.ctypes.data)
+    if st < 0:
+        raise ValueError(f"oracle quantize_q8_1 rejects {x.shape} {in_dtype}")
+    return st, blocks
+
+
+def gemv_q8_1(fmt, weight, N, K, xq, M):
+    """y[M, N] = x_hat[M, K] @ w_hat[N, K]^T in binary64 and the criterion's
+    scale env[M, N] (see nqo_gemv_q8_1)."""
+    idx = info(fmt)[0]
+    weight = np.ascontiguousarray(weight, dtype=np.uint8)
+    xq = np.ascontiguousarray(xq, dtype=np.uint8)
+    y = np.empty((M, N), dtype=np.float64)
+    env = np.empty((M, N), dtype=np.float64)
+    st = lib().nqo_gemv_q8_1(idx, weight.ctypes.data, weight.size, N, K, xq.ctypes.data, M, y.ctypes.data,
+                             env.ctypes.data)
+    if st != OK:
+        raise ValueError(f"oracle gemv_q8_1 of {fmt} [{N}, {K}] x {M} failed: status {st}")
+    return y, env
 
 
 def bf16_to_f32(w):

@@ -18,6 +18,7 @@
 #include "codebooks_hex.h"
 
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* ------------------------------------------------------------------------ */
@@ -890,4 +891,126 @@ int nqo_grouped_absmax(int scheme, int in_dtype, const void *x, int64_t N, int64
             status |= gq_group(scheme, v, cnt, codes + n * K + k0, scales + n * ng + g);
         }
     return status;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Linear products with q8_1 activations (NInfer tensor-formats: the         */
+/* paragraph on products over gguf_* weights -- the activation becomes ggml  */
+/* q8_1 numbers, one binary16 scale and one sum per 32 values, and products  */
+/* accumulate in FP32 -- and the consumer paragraph of the conformance       */
+/* section: reduction order and intermediate precision are the kernel's, and */
+/* the Op result is judged against an independent oracle under a named       */
+/* criterion).                                                               */
+/*                                                                           */
+/* Activation quantizer.  The pages name the q8_1 numbers but not the rule   */
+/* that assigns them; this oracle uses the 8-bit, 32-value absmax rule of    */
+/* section 7.2 (q8_g32_fp16, gq_group above) for the codes and the scale d,  */
+/* and stores as the sum field RN16(d32 * (sum of the 32 codes)): the        */
+/* binary16 of the block's represented sum.  d32 has at most 11 significant  */
+/* bits and |sum| <= 32 * 127 < 2^12, so that product is exact in binary32   */
+/* and the field takes one rounding.  Blocks are gguf q8_1 blocks (packed-   */
+/* layout table of the DequantizePacked page): d at byte 0, the sum at 2,    */
+/* the 32 signed codes at 4..35.                                             */
+int nqo_quantize_q8_1(int in_dtype, const void *x, int64_t M, int64_t K, uint8_t *blocks)
+{
+    if (in_dtype < 0 || in_dtype > 3 || M <= 0 || K <= 0 || K % 32 != 0) return -1;
+    const int64_t kb = K / 32;
+    int status = 0;
+    float v[32];
+    int8_t q[32];
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t c = 0; c < kb; c++) {
+            uint8_t *b = blocks + (uint64_t)(m * kb + c) * 36u;
+            for (int i = 0; i < 32; i++) v[i] = gq_source(in_dtype, x, (uint64_t)(m * K + c * 32 + i));
+            uint16_t d16 = 0;
+            const int st = gq_group(3, v, 32, q, &d16);
+            if (st) { /* the encoder fails: the block is unspecified (zeroed here) */
+                status |= st;
+                memset(b, 0, 36);
+                continue;
+            }
+            int sum = 0;
+            for (int i = 0; i < 32; i++) sum += q[i];
+            const uint16_t s16 = nqo_f32_to_f16(nqo_f16_to_f32(d16) * (float)sum);
+            if ((s16 & 0x7C00) == 0x7C00) status |= 4;
+            b[0] = (uint8_t)(d16 & 0xFF);
+            b[1] = (uint8_t)(d16 >> 8);
+            b[2] = (uint8_t)(s16 & 0xFF);
+            b[3] = (uint8_t)(s16 >> 8);
+            for (int i = 0; i < 32; i++) b[4 + i] = (uint8_t)q[i];
+        }
+    return status;
+}
+
+/* Code bytes of the formats whose decode formula adds a term that does not  */
+/* depend on the weight's own code (q4_1 and q5_1: + m; q2_k, q4_k, q5_k:   */
+/* - RN32(dmin * m_sub)), from the packed-layout table.  With those bytes    */
+/* zeroed every code is 0 and the block decodes to exactly that term.        */
+static int offset_code_bytes(int fmt, int *lo, int *hi)
+{
+    switch (fmt) {
+    case F_Q4_1: *lo = 4; *hi = 20; return 1;   /* q@4..19 */
+    case F_Q5_1: *lo = 4; *hi = 24; return 1;   /* high@4..7, q@8..23 */
+    case F_Q2_K: *lo = 16; *hi = 80; return 1;  /* q@16..79 */
+    case F_Q4_K: *lo = 16; *hi = 144; return 1; /* q@16..143 */
+    case F_Q5_K: *lo = 16; *hi = 176; return 1; /* high@16..47, q@48..175 */
+    default: return 0;
+    }
+}
+
+/* The product y[m][n] = sum_k w[n][k] * x[m][k] of a gguf_* weight [N, K]   */
+/* (each value the format's decoded binary32 weight) and M q8_1 activation   */
+/* rows of K values (each d32 * q, exact in binary32), in binary64: every    */
+/* product is exact (at most 24 + 18 significant bits) and the sum runs in k */
+/* order.  env[m][n] = sum_k |x[m][k]| * E[n][k], the scale of the error     */
+/* criterion, with E = |w| for formats whose value is a scale times a code   */
+/* and E = |w| + 2 |o| for the five formats above (o: the code-independent   */
+/* term), since a kernel may sum the scaled codes and that term apart and    */
+/* |scale * code| + |o| <= |w| + 2 |o|.                                      */
+int nqo_gemv_q8_1(int fmt, const uint8_t *w, uint64_t nbytes, int64_t N, int64_t K, const uint8_t *xq,
+                  int64_t M, double *y, double *env)
+{
+    if (fmt < 0 || fmt >= (int)(sizeof FORMATS / sizeof FORMATS[0]) || FORMATS[fmt].trailer != 0)
+        return NQO_ERR_FORMAT;
+    if (N <= 0 || K <= 0 || M <= 0) return NQO_ERR_DIM;
+    if (K % 32 != 0) return NQO_ERR_ALIGN;
+    const int64_t wshape[2] = {N, K}, xshape[2] = {M, K};
+    uint64_t need = 0, ne = 0, xbytes = 0;
+    int st = nqo_sizes(fmt, wshape, 2, &need, &ne);
+    if (st != NQO_OK) return st;
+    if (need != nbytes) return NQO_ERR_LENGTH;
+    st = nqo_sizes(F_Q8_1, xshape, 2, &xbytes, NULL);
+    if (st != NQO_OK) return st;
+    float *wh = malloc((size_t)(N * K) * sizeof(float));
+    float *o = calloc((size_t)(N * K), sizeof(float));
+    float *xh = malloc((size_t)(M * K) * sizeof(float));
+    uint8_t *wz = NULL;
+    if (!wh || !o || !xh) { st = NQO_ERR_OVERFLOW; goto done; }
+    if ((st = nqo_decode(fmt, w, nbytes, wshape, 2, NQO_F32, wh)) != NQO_OK) goto done;
+    if ((st = nqo_decode(F_Q8_1, xq, xbytes, xshape, 2, NQO_F32, xh)) != NQO_OK) goto done;
+    int lo, hi;
+    if (offset_code_bytes(fmt, &lo, &hi)) {
+        const uint64_t S = (uint64_t)FORMATS[fmt].S;
+        if (!(wz = malloc(nbytes))) { st = NQO_ERR_OVERFLOW; goto done; }
+        memcpy(wz, w, nbytes);
+        for (uint64_t b = 0; b < nbytes / S; b++) memset(wz + b * S + lo, 0, (size_t)(hi - lo));
+        if ((st = nqo_decode(fmt, wz, nbytes, wshape, 2, NQO_F32, o)) != NQO_OK) goto done;
+    }
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t n = 0; n < N; n++) {
+            double acc = 0.0, e = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                const double wv = wh[n * K + k], xv = xh[m * K + k];
+                acc += wv * xv;
+                e += fabs(xv) * (fabs(wv) + 2.0 * fabs((double)o[n * K + k]));
+            }
+            y[m * N + n] = acc;
+            if (env) env[m * N + n] = e;
+        }
+done:
+    free(wh);
+    free(o);
+    free(xh);
+    free(wz);
+    return st;
 }

@@ -92,6 +92,27 @@ int nqo_decode_fp8_row(int scale_kind, const uint8_t *payload, uint64_t nbytes, 
 int nqo_grouped_absmax(int scheme, int in_dtype, const void *x, int64_t N, int64_t K, int8_t *codes,
                        uint16_t *scales);
 
+/* Linear products with q8_1 activations (NInfer "tensor-formats": products
+ * over gguf_* weights quantize the activation to q8_1 numbers and accumulate
+ * in FP32; the Op is judged against an independent oracle).
+ *
+ * nqo_quantize_q8_1: M rows of K source values (K % 32 == 0; in_dtype as in
+ * nqo_grouped_absmax) become M*K/32 gguf q8_1 blocks of 36 bytes (binary16 d
+ * at 0, binary16 sum at 2, 32 signed codes at 4): codes and d by the
+ * q8_g32_fp16 rule of section 7.2, sum = RN16(d32 * sum of codes).  Returns
+ * -1 for bad arguments, else status bits: 1 a non-finite source, 2 a scale
+ * past binary16 (that block is zeroed), 4 a sum past binary16.
+ *
+ * nqo_gemv_q8_1: y[m*N + n] = sum_k w[n][k] * x[m][k] in binary64 for a
+ * gguf_* weight [N, K] and q8_1 activations [M, K]; env[m*N + n] (may be
+ * NULL) = sum_k |x| * E, E = |w| + 2|o| where o is the code-independent term
+ * of q4_1, q5_1, q2_k, q4_k and q5_k, E = |w| otherwise.  Returns an
+ * NQO_ERR_* code (NQO_ERR_FORMAT for "nvfp4" and out-of-range indices,
+ * NQO_ERR_ALIGN for K % 32 != 0). */
+int nqo_quantize_q8_1(int in_dtype, const void *x, int64_t M, int64_t K, uint8_t *blocks);
+int nqo_gemv_q8_1(int fmt, const uint8_t *w, uint64_t nbytes, int64_t N, int64_t K, const uint8_t *xq,
+                  int64_t M, double *y, double *env);
+
 /* Decode `nblocks` back-to-back blocks to binary32 (no trailer; `d_w` is the
  * divisor used by "nvfp4" and ignored by every other format). */
 int nqo_decode_blocks_f32(int fmt, const uint8_t *blocks, uint64_t nblocks, float d_w, float *y);
