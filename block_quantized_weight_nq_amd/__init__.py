@@ -22,7 +22,9 @@ FAMILIES = {0: "simple", 1: "kquant", 2: "iq", 3: "fp4", 4: "ternary"}
 EXPORTS = ["nq_format_count", "nq_format_by_id", "nq_format_query", "nq_validate",
            "nq_dequantize_packed", "nq_validate_nvfp4_stacked", "nq_dequantize_nvfp4_stacked",
            "nq_validate_fp8_row", "nq_dequantize_fp8_row", "nq_validate_grouped_absmax",
-           "nq_quantize_grouped_absmax", "nq_status_string"]
+           "nq_quantize_grouped_absmax", "nq_validate_quantize_q8_1", "nq_quantize_q8_1",
+           "nq_validate_gemv_q8_1", "nq_gemv_q8_1", "nq_status_string"]
+GEMV_MAX_M = 8
 GQ_SCHEMES = {"q4_g64_fp16": (0, 64), "q5_g64_fp16": (1, 64), "q6_g64_fp16": (2, 64), "q8_g32_fp16": (3, 32)}
 FP8_ROW_KINDS = {"fp8_e4m3fn_row_bf16": 0, "fp8_e4m3fn_row_fp16": 1}
 
@@ -74,6 +76,12 @@ def _lib():
                                                  c.POINTER(c.c_uint64), c.POINTER(c.c_uint64)]
         L.nq_quantize_grouped_absmax.argtypes = [c.c_int32, c.c_void_p, c.POINTER(c.c_int64), c.c_int32, c.c_int32,
                                                  c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p]
+        L.nq_validate_quantize_q8_1.argtypes = [c.POINTER(c.c_int64), c.c_int32, c.c_int32, c.POINTER(c.c_uint64)]
+        L.nq_quantize_q8_1.argtypes = [c.c_void_p, c.POINTER(c.c_int64), c.c_int32, c.c_int32, c.c_void_p,
+                                       c.c_void_p, c.c_void_p]
+        L.nq_validate_gemv_q8_1.argtypes = [c.c_int32, c.c_uint64, c.c_int64, c.c_int64, c.c_int64]
+        L.nq_gemv_q8_1.argtypes = [c.c_int32, c.c_void_p, c.c_uint64, c.c_int64, c.c_int64, c.c_void_p,
+                                   c.c_int64, c.c_void_p, c.c_void_p]
         L.nq_status_string.argtypes = [c.c_int]
         L.nq_status_string.restype = c.c_char_p
         _LIB = L
@@ -271,6 +279,84 @@ def quantize_grouped_absmax(scheme, x, stream=None, check=True):
             raise ValueError(f"grouped_absmax failed: status bits {bits:#x} "
                              "(1: a source value is not finite, 2: a scale rounds past binary16)")
     return codes, scales, status
+
+
+def validate_quantize_q8_1_status(shape, in_dtype="f32"):
+    """Raw status of nq_validate_quantize_q8_1 plus the blocks' byte size."""
+    arr, rank = _shape(shape)
+    nb = ctypes.c_uint64()
+    code = in_dtype if isinstance(in_dtype, int) else _dtype_code(in_dtype)
+    st = _lib().nq_validate_quantize_q8_1(arr, rank, code, ctypes.byref(nb))
+    return st, nb.value
+
+
+def quantize_q8_1_raw(x_ptr, shape, in_dtype_code, blocks_ptr, status_ptr, stream_handle):
+    """Direct call of nq_quantize_q8_1 with integer addresses; returns the status."""
+    arr, rank = _shape(shape)
+    return _lib().nq_quantize_q8_1(ctypes.c_void_p(x_ptr), arr, rank, in_dtype_code, ctypes.c_void_p(blocks_ptr),
+                                   ctypes.c_void_p(status_ptr), ctypes.c_void_p(stream_handle))
+
+
+def quantize_q8_1(x, stream=None, check=True):
+    """q8_1 activation blocks of a contiguous [M, K] CUDA tensor (float32 /
+    float16 / bfloat16 / float64, K % 32 == 0).  Returns (blocks uint8
+    [M, K/32, 36], status int32 [1]).  With check=True the call waits for the
+    stream and raises ValueError on a non-finite source or a scale past
+    binary16."""
+    import torch
+    if x.dim() != 2 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous rank-2 CUDA tensor")
+    M, K = x.shape
+    blocks = torch.empty((M, K // 32, 36), dtype=torch.uint8, device=x.device)
+    status = torch.empty(1, dtype=torch.int32, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    st = quantize_q8_1_raw(x.data_ptr(), [M, K], _dtype_code(x.dtype), blocks.data_ptr(), status.data_ptr(),
+                           stream.cuda_stream)
+    if st != NQ_OK:
+        raise NqError(st, f"q8_1 {[M, K]}")
+    if check:
+        stream.synchronize()
+        bits = int(status.item())
+        if bits & 3:
+            raise ValueError(f"q8_1 quantization failed: status bits {bits:#x} "
+                             "(1: a source value is not finite, 2: a scale rounds past binary16)")
+    return blocks, status
+
+
+def validate_gemv_q8_1_status(fmt, nbytes, N, K, M):
+    fid = fmt if isinstance(fmt, int) else format_query(fmt).id
+    return _lib().nq_validate_gemv_q8_1(fid, nbytes, N, K, M)
+
+
+def gemv_q8_1_raw(fmt_id, w_ptr, nbytes, N, K, xq_ptr, M, y_ptr, stream_handle):
+    """Direct call of nq_gemv_q8_1 with integer addresses; returns the status."""
+    return _lib().nq_gemv_q8_1(int(fmt_id), ctypes.c_void_p(w_ptr), nbytes, N, K, ctypes.c_void_p(xq_ptr), M,
+                               ctypes.c_void_p(y_ptr), ctypes.c_void_p(stream_handle))
+
+
+def gemv_q8_1(fmt, weight, N, K, xq, out=None, stream=None):
+    """y[M, N] (float32) = x[M, K] @ w[N, K]^T for a rank-1 uint8 CUDA weight
+    payload of `fmt` (a "gguf:" format) and q8_1 activation blocks `xq`
+    ([M, K/32, 36] uint8, as quantize_q8_1 returns), M <= 8."""
+    import torch
+    fid = fmt if isinstance(fmt, int) else format_query(fmt).id
+    if not weight.is_cuda or not xq.is_cuda or xq.dtype != torch.uint8 or not xq.is_contiguous():
+        raise ValueError("weight and xq must be CUDA uint8 tensors, xq contiguous")
+    M = xq.numel() // (K // 32 * 36) if K % 32 == 0 and K > 0 else 0
+    if xq.numel() != M * (K // 32) * 36:
+        raise ValueError("xq holds a whole number of activation rows of K / 32 blocks")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=weight.device)
+    elif out.dtype != torch.float32 or not out.is_contiguous() or out.numel() != M * N:
+        raise ValueError("out must be a contiguous float32 tensor of M * N elements")
+    if stream is None:
+        stream = torch.cuda.current_stream(weight.device)
+    st = gemv_q8_1_raw(fid, weight.data_ptr(), weight.numel(), N, K, xq.data_ptr(), M, out.data_ptr(),
+                       stream.cuda_stream)
+    if st != NQ_OK:
+        raise NqError(st, f"{fmt} [{N}, {K}] x {M}")
+    return out
 
 
 def dequantize_packed(fmt, payload, shape, out_dtype=None, out=None, stream=None):

@@ -25,7 +25,8 @@ LIB = os.path.join(HERE, "libnq.so")
 ARCH = os.environ.get("NQ_OFFLOAD_ARCH", "gfx950")
 
 KERNEL_SOURCES = ["k_simple.hip", "k_kquant.hip", "k_iq.hip", "k_fp4.hip", "k_ternary.hip", "k_fp8row.hip",
-                  "k_gqenc.hip"]
+                  "k_gqenc.hip", "k_q8_1.hip", "k_gemv_simple.hip", "k_gemv_kquant.hip", "k_gemv_iq.hip",
+                  "k_gemv_fp4t.hip"]
 HOST_SOURCES = ["nq_abi.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-ffp-contract=off",

@@ -1,0 +1,17 @@
+// k_gemv_kquant.hip -- products with q8_1 activations, kquant formats (instantiated per format and activation-row count).
+#include "nq_launch.h"
+
+namespace nq {
+int launch_gemv_kquant(int fmt, const GvLaunch &L, hipStream_t s) {
+    switch (fmt) {
+    case Q2_K: return launch_gemv_f<Q2_K>(L, s);
+    case Q3_K: return launch_gemv_f<Q3_K>(L, s);
+    case Q4_K: return launch_gemv_f<Q4_K>(L, s);
+    case Q5_K: return launch_gemv_f<Q5_K>(L, s);
+    case Q6_K: return launch_gemv_f<Q6_K>(L, s);
+    case Q8_K: return launch_gemv_f<Q8_K>(L, s);
+    case IQ4_XS: return launch_gemv_f<IQ4_XS>(L, s);
+    default: return 2;  // NQ_ERR_UNKNOWN_FORMAT
+    }
+}
+}  // namespace nq

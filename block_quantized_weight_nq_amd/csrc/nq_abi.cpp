@@ -11,6 +11,7 @@
 
 #include "../../include/nq.h"
 #include "nq_fp8row.h"
+#include "nq_gemv.h"
 #include "nq_gqenc.h"
 #include "nq_launch.h"
 
@@ -280,6 +281,71 @@ NQ_API int nq_quantize_grouped_absmax(int32_t scheme, const void *x, const int64
     L.N = (uint64_t)shape[0];
     L.K = (uint64_t)shape[1];
     return nq::launch_grouped_absmax(scheme, in_dtype, L, stream);
+}
+
+NQ_API int nq_validate_quantize_q8_1(const int64_t *shape, int32_t rank, int32_t in_dtype,
+                                     uint64_t *blocks_bytes) {
+    if (in_dtype < NQ_F32 || in_dtype > NQ_F64) return NQ_ERR_BAD_DTYPE;
+    if (rank != 2) return NQ_ERR_BAD_RANK;
+    if (!shape) return NQ_ERR_NULL_ARG;
+    if (shape[0] <= 0 || shape[1] <= 0) return NQ_ERR_BAD_DIM;
+    if (shape[1] % 32 != 0) return NQ_ERR_NOT_BLOCK_ALIGNED;
+    uint64_t elems = 0, in_bytes = 0, blocks = 0, bytes = 0;
+    if (!mul_checked((uint64_t)shape[0], (uint64_t)shape[1], &elems) ||
+        !mul_checked(elems, OUT_SIZE[in_dtype], &in_bytes) ||
+        !mul_checked((uint64_t)shape[0], (uint64_t)shape[1] / 32, &blocks) || !mul_checked(blocks, 36, &bytes))
+        return NQ_ERR_OVERFLOW;
+    if (blocks_bytes) *blocks_bytes = bytes;
+    return NQ_OK;
+}
+
+NQ_API int nq_quantize_q8_1(const void *x, const int64_t *shape, int32_t rank, int32_t in_dtype, void *blocks,
+                            uint32_t *status, hipStream_t stream) {
+    const int st = nq_validate_quantize_q8_1(shape, rank, in_dtype, nullptr);
+    if (st != NQ_OK) return st;
+    if (!x || !blocks || !status) return NQ_ERR_NULL_ARG;
+    if ((uintptr_t)x % OUT_SIZE[in_dtype] != 0 || (uintptr_t)blocks % 4 != 0 || (uintptr_t)status % 4 != 0)
+        return NQ_ERR_NULL_ARG;
+    nq::Q81Launch L;
+    L.x = x;
+    L.nblocks = (uint64_t)shape[0] * ((uint64_t)shape[1] / 32);
+    L.blocks = (uint32_t *)blocks;
+    L.status = status;
+    return nq::launch_quantize_q8_1(in_dtype, L, stream);
+}
+
+NQ_API int nq_validate_gemv_q8_1(int32_t format, uint64_t nbytes, int64_t N, int64_t K, int64_t M) {
+    if (format < 0 || format >= nq::NUM_FORMATS || TRAILER_OF(format) != 0) return NQ_ERR_UNKNOWN_FORMAT;
+    if (N <= 0 || K <= 0 || M <= 0 || M > nq::GV_MAX_M) return NQ_ERR_BAD_DIM;
+    if (K % B_OF(format) != 0) return NQ_ERR_NOT_BLOCK_ALIGNED;
+    if (N >= (1ll << 31) || K >= (1ll << 31)) return NQ_ERR_OVERFLOW;
+    uint64_t bytes = 0;
+    if (!mul_checked((uint64_t)N, (uint64_t)(K / B_OF(format)) * (uint64_t)S_OF(format), &bytes))
+        return NQ_ERR_OVERFLOW;
+    if (nbytes != bytes) return NQ_ERR_LENGTH_MISMATCH;
+    return NQ_OK;
+}
+
+NQ_API int nq_gemv_q8_1(int32_t format, const void *weight, uint64_t nbytes, int64_t N, int64_t K,
+                        const void *xq, int64_t M, float *y, hipStream_t stream) {
+    const int st = nq_validate_gemv_q8_1(format, nbytes, N, K, M);
+    if (st != NQ_OK) return st;
+    if (!weight || !xq || !y) return NQ_ERR_NULL_ARG;
+    if ((uintptr_t)xq % 4 != 0 || (uintptr_t)y % 4 != 0) return NQ_ERR_NULL_ARG;
+    nq::GvLaunch L;
+    L.w = (const uint8_t *)weight;
+    L.N = (uint64_t)N;
+    L.K = (uint64_t)K;
+    L.M = (uint64_t)M;
+    L.xq = (const uint8_t *)xq;
+    L.y = y;
+    L.resident = resident_workgroups();
+    switch (REGISTRY[format].family) {
+    case NQ_FAMILY_SIMPLE: return nq::launch_gemv_simple(format, L, stream);
+    case NQ_FAMILY_KQUANT: return nq::launch_gemv_kquant(format, L, stream);
+    case NQ_FAMILY_IQ: return nq::launch_gemv_iq(format, L, stream);
+    default: return nq::launch_gemv_fp4t(format, L, stream);
+    }
 }
 
 NQ_API const char *nq_status_string(int status) {

@@ -199,6 +199,55 @@ int nq_validate_grouped_absmax(int32_t scheme, const int64_t *shape, int32_t ran
 int nq_quantize_grouped_absmax(int32_t scheme, const void *x, const int64_t *shape, int32_t rank, int32_t in_dtype,
                                void *codes, void *scales, uint32_t *status, hipStream_t stream);
 
+/* Products with q8_1 activations (NInfer "tensor-formats" page: a product
+ * over a gguf_* weight quantizes the activation to ggml q8_1 numbers, one
+ * binary16 scale and one sum per 32 values, and accumulates in FP32; the
+ * kernel's reduction order and intermediate precision are its own, and the
+ * result is judged against an independent oracle under a named criterion).
+ *
+ * nq_quantize_q8_1: a [M, K] activation (shape[0] = M rows, shape[1] = K,
+ * K % 32 == 0; in_dtype f32/f16/bf16/f64, converted to binary32 with RNE)
+ * becomes M*K/32 gguf q8_1 blocks of 36 bytes, row-major (block c of row m at
+ * byte 36*(m*K/32 + c)): binary16 d at byte 0, binary16 sum at 2, 32 signed
+ * codes at 4.  The pages name q8_1 numbers but not the rule that assigns
+ * them; the codes and d follow the q8_g32_fp16 rule of section 7.2 (see
+ * nq_quantize_grouped_absmax), and the sum is RN16(d32 * sum of the codes),
+ * a product exact in binary32.  `status` (one device uint32) is cleared on
+ * `stream` first, then ORed with 1 for a non-finite source, 2 for a scale
+ * past binary16 (that block is then all zero bytes) and 4 for a sum past
+ * binary16 (the sum field is then infinite).
+ * nq_validate_quantize_q8_1 checks in_dtype (NQ_ERR_BAD_DTYPE), rank == 2
+ * (NQ_ERR_BAD_RANK), shape (NQ_ERR_NULL_ARG), both dimensions > 0
+ * (NQ_ERR_BAD_DIM), K % 32 (NQ_ERR_NOT_BLOCK_ALIGNED) and the byte counts
+ * (NQ_ERR_OVERFLOW), and stores the blocks' byte size.  nq_quantize_q8_1
+ * also requires x, blocks and status non-NULL, x aligned to its element size
+ * and blocks and status to 4 bytes (NQ_ERR_NULL_ARG).  The caller owns every
+ * buffer; x must not overlap the outputs.
+ *
+ * nq_gemv_q8_1: y[m*N + n] = sum_k w[n][k] * x[m][k] (binary32 output,
+ * row-major [M, N]) for a gguf_* weight payload of N rows of K values
+ * (`format` one of the 27 "gguf:" ids, nbytes = N * (K/B) * S) and M q8_1
+ * activation rows as nq_quantize_q8_1 writes them, 1 <= M <= 8; w is the
+ * format's decoded binary32 weight and x[m][k] = d32 * code.  Accumulation
+ * is binary32 with fused multiply-adds in an order fixed per launch shape, so
+ * repeated calls give identical bits; against the exact sum the error stays
+ * below gamma(K + 8) * sum_k |x| E + (K + 8) * 2^-148, gamma(n) = n u /
+ * (1 - n u), u = 2^-24, with E = |w|, or |w| + 2|o| for q4_1, q5_1, q2_k,
+ * q4_k and q5_k (o: the weight's value at code 0).
+ * nq_validate_gemv_q8_1 checks the format (NQ_ERR_UNKNOWN_FORMAT, also for
+ * "nvfp4"), N, K > 0 and 1 <= M <= 8 (NQ_ERR_BAD_DIM), K % B
+ * (NQ_ERR_NOT_BLOCK_ALIGNED), N, K < 2^31 (NQ_ERR_OVERFLOW) and nbytes
+ * (NQ_ERR_LENGTH_MISMATCH).  nq_gemv_q8_1 also requires weight, xq and y
+ * non-NULL and xq and y aligned to 4 bytes (NQ_ERR_NULL_ARG), then enqueues
+ * the product on `stream`.  The caller owns every buffer; y must not overlap
+ * the inputs. */
+int nq_validate_quantize_q8_1(const int64_t *shape, int32_t rank, int32_t in_dtype, uint64_t *blocks_bytes);
+int nq_quantize_q8_1(const void *x, const int64_t *shape, int32_t rank, int32_t in_dtype, void *blocks,
+                     uint32_t *status, hipStream_t stream);
+int nq_validate_gemv_q8_1(int32_t format, uint64_t nbytes, int64_t N, int64_t K, int64_t M);
+int nq_gemv_q8_1(int32_t format, const void *weight, uint64_t nbytes, int64_t N, int64_t K, const void *xq,
+                 int64_t M, float *y, hipStream_t stream);
+
 /* Static description of a status code. */
 const char *nq_status_string(int status);
 

@@ -17,6 +17,7 @@
 #include <vector>
 
 #include "../../block_quantized_weight_nq_amd/csrc/nq_fp8row.h"
+#include "../../block_quantized_weight_nq_amd/csrc/nq_gemv.h"
 #include "../../block_quantized_weight_nq_amd/csrc/nq_gqenc.h"
 #include "../../block_quantized_weight_nq_amd/csrc/nq_kernel.h"
 
@@ -188,17 +189,82 @@ long tile_blocks(int upt) {
     }
 }
 
+// Products with q8_1 activations: the launcher's row chunks (max_rows > 0
+// overrides the launcher's limit) and, per launch, every workgroup of the
+// grid-stride loop, every wave and lane (gv_lane through a bounds-checked
+// weight source), then the waves' butterfly sums in the kernel's order.
+template <int F, int MT>
+long run_gemv(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y, uint32_t resident,
+              uint64_t max_rows, char *err, int errlen) {
+    using namespace nq;
+    constexpr int RW = gv_rw<MT>();
+    const GvLaunch L{w, N, K, M, xq, y, resident};
+    const uint64_t lim = max_rows ? max_rows : gv_max_rows<F>(L);
+    const uint64_t row_bytes = K / (uint64_t)block_values(F) * (uint64_t)block_bytes(F);
+    std::vector<uint64_t> t8(TabSpec<F>::n8 > 0 ? TabSpec<F>::n8 : 1);
+    std::vector<uint32_t> t4(TabSpec<F>::n4 > 0 ? TabSpec<F>::n4 : 1);
+    for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) gv_fill_tables<F>(t8.data(), t4.data(), tid);
+    const Tab tab{t8.data(), t4.data(), nullptr, nullptr, 0xFFFFFFFFu, 1u};
+    long errors = 0;
+    for (uint64_t r0 = 0; r0 < N;) {
+        const uint64_t rows = N - r0 < lim ? N - r0 : lim;
+        uint32_t grid;
+        const GvArgs a = gv_args<F, MT>(L, r0, rows, &grid);
+        Check chk{(uintptr_t)(w + r0 * row_bytes), (uintptr_t)(w + (r0 + rows) * row_bytes), 0, {0}};
+        const HostSrc src{a.wbase, a.wlast, &chk};
+        for (uint32_t b = 0; b < grid; b++)
+            for (uint32_t g = b; g * (4u * RW) < a.rows; g += grid)
+                for (uint32_t wave = 0; wave < 4u; wave++) {
+                    const uint32_t rb = (g * 4u + wave) * (uint32_t)RW;
+                    static float acc[64][RW][MT];
+                    for (uint32_t lane = 0; lane < 64u; lane++) gv_lane<F, MT, RW>(src, tab, a, rb, lane, acc[lane]);
+                    for (int rr = 0; rr < RW; rr++)
+                        for (int m = 0; m < MT; m++) {
+                            float v[64], nv[64];
+                            for (int l = 0; l < 64; l++) v[l] = acc[l][rr][m];
+                            for (int off = 32; off >= 1; off >>= 1) {
+                                for (int l = 0; l < 64; l++) nv[l] = v[l] + v[l ^ off];
+                                std::copy(nv, nv + 64, v);
+                            }
+                            const uint32_t r = rb + (uint32_t)rr;
+                            if (r < a.rows && m < (int)a.M) a.y[(uint64_t)m * a.ldy + r] = v[0];
+                        }
+                }
+        if (chk.errors) {
+            if (errors == 0) snprintf(err, errlen, "%s", chk.msg);
+            errors += chk.errors;
+        }
+        r0 += rows;
+    }
+    return errors;
+}
+
+template <int F>
+long run_gemv_m(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y, uint32_t res,
+                uint64_t max_rows, char *err, int errlen) {
+    if (M <= 1) return run_gemv<F, 1>(w, N, K, xq, M, y, res, max_rows, err, errlen);
+    if (M <= 2) return run_gemv<F, 2>(w, N, K, xq, M, y, res, max_rows, err, errlen);
+    if (M <= 4) return run_gemv<F, 4>(w, N, K, xq, M, y, res, max_rows, err, errlen);
+    return run_gemv<F, 8>(w, N, K, xq, M, y, res, max_rows, err, errlen);
+}
+
 }  // namespace
 
 using EmuRun = long (*)(int ot, const uint8_t *payload, uint64_t nbytes, uint64_t nblocks, void *out,
                        uint32_t max_wgs, uint64_t chunk, int force_upt, uint32_t ndiv, char *err, int errlen);
 extern EmuRun nq_emu_table[nq::NUM_FORMATS];
+using EmuGemv = long (*)(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y,
+                         uint32_t resident, uint64_t max_rows, char *err, int errlen);
+extern EmuGemv nq_emu_gemv_table[nq::NUM_FORMATS];
 
 #if defined(NQ_EMU_PART)
 namespace {
 template <int F>
 void reg() {
-    if constexpr (F % NQ_EMU_PARTS == NQ_EMU_PART) nq_emu_table[F] = &run_ot<F>;
+    if constexpr (F % NQ_EMU_PARTS == NQ_EMU_PART) {
+        nq_emu_table[F] = &run_ot<F>;
+        if constexpr (F != nq::NVFP4_DIV) nq_emu_gemv_table[F] = &run_gemv_m<F>;
+    }
 }
 struct Register {
     Register() {
@@ -212,6 +278,17 @@ struct Register {
 }  // namespace
 #else
 EmuRun nq_emu_table[nq::NUM_FORMATS];
+EmuGemv nq_emu_gemv_table[nq::NUM_FORMATS];
+
+// Product with q8_1 activations through the kernel's lane code; returns
+// out-of-payload weight reads (0 on success), or -1 for a format without one.
+extern "C" __attribute__((visibility("default"))) long nq_emu_gemv_q8_1(int fmt, const uint8_t *w, uint64_t N,
+                                                                       uint64_t K, const uint8_t *xq, uint64_t M,
+                                                                       float *y, uint32_t resident,
+                                                                       uint64_t max_rows, char *err, int errlen) {
+    if (fmt < 0 || fmt >= nq::NUM_FORMATS || !nq_emu_gemv_table[fmt]) return -1;
+    return nq_emu_gemv_table[fmt](w, N, K, xq, M, y, resident, max_rows, err, errlen);
+}
 
 // Returns the number of out-of-payload reads (0 on success), or -1 for a bad format.
 // ndiv: "nvfp4" divisor words after the blocks (stacked sources), 1 otherwise.
@@ -462,6 +539,78 @@ extern "C" __attribute__((visibility("default"))) long nq_emu_grouped_absmax(int
     case 1: return run_gq_in<1>(in, x, N, K, codes, scales, status, err, errlen);
     case 2: return run_gq_in<2>(in, x, N, K, codes, scales, status, err, errlen);
     default: return run_gq_in<3>(in, x, N, K, codes, scales, status, err, errlen);
+    }
+}
+namespace {
+
+// q8_1 quantizer: the launcher's chunks and, per block, its lanes' phases:
+// loads (bounds-checked), the amax / failure exchange, the encode, the code
+// sum exchange and the stores.
+template <int IN>
+long run_q81(const void *x, uint64_t nblocks, uint32_t *blocks, uint32_t *status, uint64_t chunk, char *err,
+             int errlen) {
+    using namespace nq;
+    constexpr uint64_t ESZ = IN == 0 ? 4 : IN == 3 ? 8 : 2;
+    constexpr int VPL = gq_vpl<IN>();
+    constexpr uint32_t LPB = q81_lanes<IN>();
+    const bool vin = (uintptr_t)x % 16 == 0;
+    *status = 0u;
+    long errors = 0;
+    for (uint64_t b0 = 0; b0 < nblocks; b0 += chunk) {
+        Q81Args a;
+        a.x = (const uint8_t *)x + b0 * 32 * ESZ;
+        a.blocks = blocks + b0 * 9;
+        a.status = status;
+        a.nblocks = (uint32_t)(nblocks - b0 < chunk ? nblocks - b0 : chunk);
+        Check chk{0, 0, 0, {0}};
+        const GqHostSrc<(int)ESZ> src{a.x, (uint64_t)a.nblocks * 32u, &chk};
+        for (uint32_t b = 0; b < a.nblocks; b++) {
+            float v[LPB][VPL], am[LPB];
+            bool bad[LPB];
+            float amax = 0.0f;
+            bool anybad = false;
+            for (uint32_t j = 0; j < LPB; j++) {
+                if (vin)
+                    gq_load<IN, true>(src, (uint64_t)b * 32u + j * (uint32_t)VPL, (uint32_t)VPL, v[j], &am[j], &bad[j]);
+                else
+                    gq_load<IN, false>(src, (uint64_t)b * 32u + j * (uint32_t)VPL, (uint32_t)VPL, v[j], &am[j],
+                                       &bad[j]);
+                amax = am[j] > amax ? am[j] : amax;
+                anybad |= bad[j];
+            }
+            int8_t q[LPB][VPL];
+            uint32_t d16[LPB], st[LPB];
+            int sum = 0;
+            for (uint32_t j = 0; j < LPB; j++) {
+                st[j] = q81_encode<VPL>(amax, anybad, v[j], &d16[j], q[j]);
+                for (int k = 0; k < VPL; k++) sum += q[j][k];
+            }
+            for (uint32_t j = 0; j < LPB; j++) {
+                const uint32_t bits = q81_store<VPL>(a, b, j, q[j], d16[j], sum, st[j]);
+                if (j == 0u) *status |= bits;
+            }
+        }
+        if (chk.errors) {
+            if (errors == 0) snprintf(err, errlen, "%s", chk.msg);
+            errors += chk.errors;
+        }
+    }
+    return errors;
+}
+
+}  // namespace
+
+// The q8_1 quantizer through its lane code; chunk: blocks per launch (0: the
+// launcher's).  Returns out-of-bounds or misaligned source reads.
+extern "C" __attribute__((visibility("default"))) long nq_emu_quantize_q8_1(int in, const void *x, uint64_t nblocks,
+                                                                           uint32_t *blocks, uint32_t *status,
+                                                                           uint64_t chunk, char *err, int errlen) {
+    if (chunk == 0) chunk = nq::Q81_CHUNK;
+    switch (in) {
+    case 0: return run_q81<0>(x, nblocks, blocks, status, chunk, err, errlen);
+    case 1: return run_q81<1>(x, nblocks, blocks, status, chunk, err, errlen);
+    case 2: return run_q81<2>(x, nblocks, blocks, status, chunk, err, errlen);
+    default: return run_q81<3>(x, nblocks, blocks, status, chunk, err, errlen);
     }
 }
 #endif  // NQ_EMU_PART

@@ -69,6 +69,13 @@ def lib():
         L.nq_emu_choose_upt.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint32]
         L.nq_emu_choose_upt.restype = ctypes.c_int
         L.nq_emu_tile_blocks.restype = ctypes.c_long
+        L.nq_emu_gemv_q8_1.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64,
+                                       ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint32,
+                                       ctypes.c_uint64, ctypes.c_char_p, ctypes.c_int]
+        L.nq_emu_gemv_q8_1.restype = ctypes.c_long
+        L.nq_emu_quantize_q8_1.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_uint64, ctypes.c_char_p, ctypes.c_int]
+        L.nq_emu_quantize_q8_1.restype = ctypes.c_long
         _lib = L
     return _lib
 
@@ -153,3 +160,40 @@ def grouped_absmax(scheme_id, G, x, in_code, x_mis=0, codes_mis=0):
     codes = cbuf[coff:coff + N * K].view(np.int8).reshape(N, K).copy()
     scales = sbuf[8:8 + N * ng].reshape(N, ng).copy()
     return int(status[0]), codes, scales, rc, err.value.decode(), guards
+
+
+def gemv_q8_1(fmt_id, w, N, K, xq, M, w_mis=0, resident=2048, max_rows=0):
+    """The product through the emulator.  w: payload bytes, xq: q8_1 blocks.
+    Returns (y float32 [M, N], bad reads, message, guards_ok)."""
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    wbuf, woff = _placed(w.size, 16, w_mis)
+    wbuf[woff:woff + w.size] = w
+    xq = np.ascontiguousarray(xq, dtype=np.uint8).reshape(-1)
+    xbuf, xoff = _placed(xq.size, 16, 0)
+    xbuf[xoff:xoff + xq.size] = xq
+    ybuf = np.full(M * N + 32, np.float32(np.nan), dtype=np.float32)
+    err = ctypes.create_string_buffer(256)
+    rc = lib().nq_emu_gemv_q8_1(fmt_id, wbuf.ctypes.data + woff, N, K, xbuf.ctypes.data + xoff, M,
+                                ybuf.ctypes.data + 64, resident, max_rows, err, 256)
+    y = ybuf[16:16 + M * N].reshape(M, N).copy()
+    guards = bool(np.all(np.isnan(ybuf[:16])) and np.all(np.isnan(ybuf[16 + M * N:])))
+    return y, rc, err.value.decode(), guards
+
+
+def quantize_q8_1(x, in_code, x_mis=0, chunk=0):
+    """The q8_1 quantizer through the emulator.  x: [M, K] array (raw words
+    for f16/bf16).  Returns (status, blocks uint8 [M, K/32, 36], bad reads,
+    message, guards_ok)."""
+    x = np.ascontiguousarray(x)
+    M, K = x.shape
+    xbuf, xoff = _placed(x.nbytes, 16, x_mis)
+    xbuf[xoff:xoff + x.nbytes] = x.view(np.uint8).ravel()
+    nb = M * K // 32
+    bbuf = np.full(nb * 9 + 8, 0xA5A5A5A5, dtype=np.uint32)
+    status = np.zeros(1, dtype=np.uint32)
+    err = ctypes.create_string_buffer(256)
+    rc = lib().nq_emu_quantize_q8_1(in_code, xbuf.ctypes.data + xoff, nb, bbuf.ctypes.data + 16,
+                                    status.ctypes.data, chunk, err, 256)
+    guards = bool(np.all(bbuf[:4] == 0xA5A5A5A5) and np.all(bbuf[4 + nb * 9:] == 0xA5A5A5A5))
+    blocks = bbuf[4:4 + nb * 9].view(np.uint8).reshape(M, K // 32, 36).copy()
+    return int(status[0]), blocks, rc, err.value.decode(), guards

@@ -206,3 +206,56 @@ def test_grouped_absmax_rejects_before_device():
     assert nq.quantize_grouped_absmax_raw(0, p, [2, 8], 0, p, p + 1, p, 0) == 1   # scales misaligned
     assert nq.quantize_grouped_absmax_raw(0, p, [2, 8], 0, p, p, p + 2, 0) == 1   # status misaligned
     assert nq.quantize_grouped_absmax_raw(4, p, [2, 8], 0, p, p, p, 0) == 2
+
+
+def test_quantize_q8_1_validation():
+    assert nq.validate_quantize_q8_1_status([3, 64]) == (0, 3 * 2 * 36)
+    assert nq.validate_quantize_q8_1_status([1, 4096], "bf16") == (0, 128 * 36)
+    assert nq.validate_quantize_q8_1_status([3, 64], 7)[0] == 8
+    assert nq.validate_quantize_q8_1_status([192])[0] == 3
+    assert nq.validate_quantize_q8_1_status([0, 64])[0] == 4
+    assert nq.validate_quantize_q8_1_status([3, -32])[0] == 4
+    assert nq.validate_quantize_q8_1_status([3, 48])[0] == 5
+    assert nq.validate_quantize_q8_1_status([1 << 40, 1 << 30])[0] == 7
+
+
+def test_quantize_q8_1_rejects_before_device():
+    buf = np.zeros(64, dtype=np.uint32)
+    p = buf.ctypes.data
+    assert nq.quantize_q8_1_raw(0, [2, 32], 0, p, p, 0) == 1
+    assert nq.quantize_q8_1_raw(p, [2, 32], 0, 0, p, 0) == 1
+    assert nq.quantize_q8_1_raw(p, [2, 32], 0, p, 0, 0) == 1
+    assert nq.quantize_q8_1_raw(p + 2, [2, 32], 0, p, p, 0) == 1   # f32 source misaligned
+    assert nq.quantize_q8_1_raw(p, [2, 32], 0, p + 2, p, 0) == 1   # blocks misaligned
+    assert nq.quantize_q8_1_raw(p, [2, 32], 0, p, p + 1, 0) == 1   # status misaligned
+    assert nq.quantize_q8_1_raw(p, [2, 33], 0, p, p, 0) == 5
+    assert nq.quantize_q8_1_raw(p, [2, 32], 9, p, p, 0) == 8
+
+
+@pytest.mark.parametrize("fmt", [f for f in oracle.format_names() if f.startswith("gguf:")])
+def test_gemv_length_rule_agrees_with_oracle(fmt):
+    _, B, S, _ = oracle.info(fmt)
+    N, K = 3, 2 * B
+    assert nq.validate_gemv_q8_1_status(fmt, N * 2 * S, N, K, 1) == 0
+    assert nq.validate_gemv_q8_1_status(fmt, N * 2 * S, N, K, 8) == 0
+    assert nq.validate_gemv_q8_1_status(fmt, N * 2 * S + 1, N, K, 1) == 6
+    assert nq.validate_gemv_q8_1_status(fmt, N * 2 * S, N, K, 9) == 4
+    assert nq.validate_gemv_q8_1_status(fmt, N * 2 * S, N, K, 0) == 4
+    assert nq.validate_gemv_q8_1_status(fmt, 0, 0, K, 1) == 4
+    assert nq.validate_gemv_q8_1_status(fmt, N * 2 * S, N, K + 32 if B > 32 else K + 16, 1) == 5
+    assert oracle.sizes(fmt, [N, K])[1] == N * 2 * S
+
+
+def test_gemv_rejects_before_device():
+    buf = np.zeros(256, dtype=np.uint32)
+    p = buf.ctypes.data
+    q8 = nq.format_query("gguf:q8_0").id
+    assert nq.validate_gemv_q8_1_status("nvfp4", 40, 1, 64, 1) == 2
+    assert nq.validate_gemv_q8_1_status(99, 34, 1, 32, 1) == 2
+    assert nq.validate_gemv_q8_1_status(q8, 34 << 31, 1 << 31, 32, 1) == 7
+    assert nq.gemv_q8_1_raw(q8, 0, 34, 1, 32, p, 1, p, 0) == 1
+    assert nq.gemv_q8_1_raw(q8, p, 34, 1, 32, 0, 1, p, 0) == 1
+    assert nq.gemv_q8_1_raw(q8, p, 34, 1, 32, p, 1, 0, 0) == 1
+    assert nq.gemv_q8_1_raw(q8, p, 34, 1, 32, p + 2, 1, p, 0) == 1   # activation blocks misaligned
+    assert nq.gemv_q8_1_raw(q8, p, 34, 1, 32, p, 1, p + 2, 0) == 1   # output misaligned
+    assert nq.gemv_q8_1_raw(q8, p, 35, 1, 32, p, 1, p, 0) == 6

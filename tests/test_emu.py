@@ -243,3 +243,80 @@ def test_emulated_grouped_absmax_failures():
         assert st == want[0]
         assert np.array_equal(codes[0], want[1][0]) and np.array_equal(scales[0], want[2][0])
     assert emu_lib.grouped_absmax(3, 32, x, 0)[0] == 3
+
+
+# --------------------------------------------------------------------------
+# Products with q8_1 activations and the q8_1 quantizer, through the
+# kernels' lane code on the CPU: every weight read is bounds-checked, the
+# output guards must hold, the product meets the oracle's criterion and the
+# quantizer matches the oracle bit for bit.
+# --------------------------------------------------------------------------
+from linear_criterion import check as linear_check  # noqa: E402
+
+GGUF = [f for f in FORMATS if f.startswith("gguf:")]
+
+
+def _act(M, K, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K)) * 2.0
+    x[:, rng.integers(0, K, size=max(1, K // 61))] *= 30.0
+    return x
+
+
+@pytest.mark.parametrize("fmt", GGUF)
+def test_emu_gemv_matches_oracle(fmt):
+    idx, B, S, _ = oracle.info(fmt)
+    K = 2 * max(B, 256)
+    for N, M, w_mis, resident, max_rows in [(13, 1, 0, 2048, 0), (11, 2, 3, 1, 0), (9, 3, 1, 2048, 4),
+                                            (6, 8, 2, 2, 5)]:
+        w = synth.payload(fmt, N * K // B, 91 + N, synth.binade(-6, -2, False))
+        _, xq = oracle.quantize_q8_1(_act(M, K, N).astype(np.float32))
+        y, rc, msg, guards = emu_lib.gemv_q8_1(idx, w, N, K, xq, M, w_mis=w_mis, resident=resident,
+                                               max_rows=max_rows)
+        assert rc == 0, msg
+        assert guards
+        ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
+        linear_check(y, ref, env, K, f"{fmt} N={N} M={M}")
+
+
+def test_emu_gemv_rejects_nvfp4_with_divisor():
+    y, rc, _, _ = emu_lib.gemv_q8_1(nq.format_query("nvfp4").id, np.zeros(40, np.uint8), 1, 64,
+                                    np.zeros(72, np.uint8), 1)
+    assert rc == -1
+
+
+@pytest.mark.parametrize("in_dtype,code", [("f32", 0), ("f16", 1), ("bf16", 2), ("f64", 3)])
+def test_emu_quantize_q8_1_matches_oracle(in_dtype, code):
+    M, K = 3, 352
+    x = _act(M, K, 5)
+    x[1, 64:96] = 0.0                 # an all-zero block
+    x[2, 160] = 1e-30                 # a tiny block
+    x[0, 96:128] = 65024.0            # a block whose sum overflows binary16
+    if in_dtype == "f32":
+        xs = x.astype(np.float32)
+    elif in_dtype == "f16":
+        xs = x.astype(np.float16).view(np.uint16)
+    elif in_dtype == "bf16":
+        xs = oracle.convert(x.astype(np.float32), "bf16").reshape(M, K)
+    else:
+        xs = x
+    ost, ob = oracle.quantize_q8_1(xs, in_dtype)
+    assert ost == 4
+    esz = xs.dtype.itemsize
+    for mis in sorted({0, esz, 2 * esz, 8}):
+        st, b, rc, msg, guards = emu_lib.quantize_q8_1(xs, code, x_mis=mis, chunk=5)
+        assert rc == 0, msg
+        assert guards
+        assert st == ost
+        assert np.array_equal(b, ob), f"{in_dtype} mis={mis}"
+
+
+def test_emu_quantize_q8_1_failures():
+    x = _act(2, 96, 3).astype(np.float32)
+    x[0, 3] = np.nan
+    x[1, 70] = 2.0 ** 23
+    ost, ob = oracle.quantize_q8_1(x)
+    st, b, rc, msg, guards = emu_lib.quantize_q8_1(x, 0)
+    assert rc == 0 and guards
+    assert st == ost == 3
+    assert np.array_equal(b, ob)

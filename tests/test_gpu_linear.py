@@ -1,0 +1,183 @@
+"""GPU (gfx950) products with q8_1 activations through the C ABI, against the oracle.
+
+The q8_1 quantizer is integer / byte work and must match the oracle bit for
+bit.  The product's accumulation order is the kernel's, so it must meet the
+oracle's criterion (tests/linear_criterion.py); repeated calls must agree bit
+for bit.  Sizes span many workgroups with ragged row counts; the full-size
+weights are checked on sampled rows in the launch configuration the
+benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_weight_nq_amd as nq
+import oracle
+import synth
+from gpu_util import announce, upload
+from linear_criterion import check as linear_check
+
+pytestmark = pytest.mark.gpu
+
+GGUF = [f for f in oracle.format_names() if f.startswith("gguf:")]
+TORCH_IN = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "f64": torch.float64}
+
+
+def _act(M, K, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K)) * 2.0
+    x[:, rng.integers(0, K, size=max(1, K // 61))] *= 30.0
+    return x
+
+
+def _source(x, in_dtype):
+    """(oracle source array, torch CPU tensor of the same words)."""
+    if in_dtype == "f32":
+        xs = x.astype(np.float32)
+        return xs, torch.from_numpy(xs)
+    if in_dtype == "f64":
+        return x, torch.from_numpy(x.copy())
+    if in_dtype == "f16":
+        xs = x.astype(np.float16).view(np.uint16)
+        return xs, torch.from_numpy(xs.view(np.int16).copy()).view(torch.float16)
+    xs = oracle.convert(x.astype(np.float32), "bf16").reshape(x.shape)
+    return xs, torch.from_numpy(xs.view(np.int16).copy()).view(torch.bfloat16)
+
+
+def _device_x(t, elem_off):
+    """t on cuda:0 at element offset elem_off of its allocation."""
+    buf = torch.zeros(t.numel() + elem_off + 8, dtype=t.dtype, device="cuda:0")
+    view = buf[elem_off:elem_off + t.numel()].view(t.shape)
+    view.copy_(t.to("cuda:0"))
+    return view, buf
+
+
+def _blocks_np(b):
+    return b.cpu().numpy()
+
+
+@pytest.mark.parametrize("in_dtype", ["f32", "f16", "bf16", "f64"])
+@pytest.mark.parametrize("shape", [[3, 352], [5, 4096], [1, 14336], [8, 11008]])
+def test_quantize_q8_1_matches_oracle(in_dtype, shape):
+    M, K = shape
+    x = _act(M, K, 17 * M + K)
+    x[0, 64:96] = 0.0                   # an all-zero block
+    x[-1, 32] = 1e-30                   # a block of tiny values
+    x[-1, 96:128] = 65024.0             # a block whose sum overflows binary16
+    xs, xt = _source(x, in_dtype)
+    ost, ob = oracle.quantize_q8_1(xs, in_dtype)
+    for off in (0, 1, 3):               # 16-byte aligned, then element offsets
+        announce(f"quantize_q8_1 {in_dtype} {shape} off={off}")
+        xd, _keep = _device_x(xt, off)
+        blocks, status = nq.quantize_q8_1(xd, check=False)
+        torch.cuda.synchronize()
+        assert int(status.item()) == ost
+        assert np.array_equal(_blocks_np(blocks), ob), f"{in_dtype} {shape} off={off}"
+
+
+def test_quantize_q8_1_failures_and_status_reset():
+    x = _act(2, 128, 5).astype(np.float32)
+    x[0, 3] = np.nan
+    x[1, 70] = 2.0 ** 23
+    ost, ob = oracle.quantize_q8_1(x)
+    announce("quantize_q8_1 failures")
+    blocks, status = nq.quantize_q8_1(torch.from_numpy(x).cuda(), check=False)
+    torch.cuda.synchronize()
+    assert int(status.item()) == ost == 3
+    assert np.array_equal(_blocks_np(blocks), ob)
+    with pytest.raises(ValueError):
+        nq.quantize_q8_1(torch.from_numpy(x).cuda())
+    # the status word is cleared by every call
+    good = _act(2, 128, 6).astype(np.float32)
+    blocks, status = nq.quantize_q8_1(torch.from_numpy(good).cuda(), check=True)
+    assert int(status.item()) == 0
+
+
+def _gemv(fmt, w_np, N, K, xq_np, w_off=0, stream=None):
+    w, _keep = upload(w_np, w_off)
+    xq = torch.from_numpy(np.ascontiguousarray(xq_np)).cuda()
+    y = nq.gemv_q8_1(fmt, w, N, K, xq, stream=stream)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def _weights(fmt, N, K, seed):
+    _, B, _, _ = oracle.info(fmt)
+    return synth.payload(fmt, N * K // B, seed, synth.binade(-6, -2, fmt in ("gguf:q4_0", "gguf:q8_0")))
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 8])
+@pytest.mark.parametrize("fmt", GGUF)
+def test_gemv_every_format(fmt, M):
+    _, B, _, _ = oracle.info(fmt)
+    N, K = 37, 3 * max(B, 256)          # ragged against the rows a workgroup takes
+    w = _weights(fmt, N, K, 300 + M)
+    _, xq = oracle.quantize_q8_1(_act(M, K, M).astype(np.float32))
+    ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
+    for w_off in (0, 1, 3):
+        announce(f"gemv {fmt} N={N} K={K} M={M} w_off={w_off}")
+        y = _gemv(fmt, w, N, K, xq, w_off)
+        linear_check(y, ref, env, K, f"{fmt} M={M} w_off={w_off}")
+
+
+@pytest.mark.parametrize("fmt", ["gguf:q4_k", "gguf:iq2_xxs", "gguf:q8_0"])
+def test_gemv_repeats_bit_for_bit_and_on_a_side_stream(fmt):
+    N, K, M = 300, 4096, 2
+    w = _weights(fmt, N, K, 8)
+    _, xq = oracle.quantize_q8_1(_act(M, K, 9).astype(np.float32))
+    announce(f"gemv repeat {fmt}")
+    a = _gemv(fmt, w, N, K, xq)
+    b = _gemv(fmt, w, N, K, xq)
+    s = torch.cuda.Stream()
+    c = _gemv(fmt, w, N, K, xq, stream=s)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert np.array_equal(a.view(np.uint32), c.view(np.uint32))
+
+
+def test_gemv_codebook_formats_loop_over_rows():
+    """Codebook formats cap the grid at the resident workgroups and loop; a
+    weight with more rows than that covers the loop."""
+    fmt, N, K, M = "gguf:iq2_xxs", 40000, 256, 1
+    w = _weights(fmt, N, K, 4)
+    _, xq = oracle.quantize_q8_1(_act(M, K, 4).astype(np.float32))
+    announce(f"gemv {fmt} N={N}")
+    y = _gemv(fmt, w, N, K, xq)
+    rows = np.r_[0:64, 16380:16400, N - 64:N]
+    sub = w.reshape(N, -1)[rows].ravel()
+    ref, env = oracle.gemv_q8_1(fmt, sub, rows.size, K, xq, M)
+    linear_check(y[:, rows], ref, env, K, fmt)
+
+
+FULL = [("gguf:q4_k", 14336, 4096), ("gguf:q6_k", 4096, 14336), ("gguf:q8_0", 4096, 4096),
+        ("gguf:tq2_0", 1024, 4096), ("gguf:iq2_xxs", 14336, 4096), ("gguf:iq4_xs", 4096, 14336),
+        ("gguf:mxfp4", 14336, 4096), ("gguf:q5_k", 4096, 4096)]
+
+
+@pytest.mark.parametrize("fmt,N,K", FULL)
+def test_gemv_full_size_sampled_rows(fmt, N, K):
+    """Llama-3-8B-shaped weights, M = 1 (the benchmark's launch): every output
+    computed on the GPU, sampled rows against the oracle."""
+    M = 1
+    w = _weights(fmt, N, K, 77)
+    _, xq = oracle.quantize_q8_1(_act(M, K, 1).astype(np.float32))
+    announce(f"gemv full {fmt} [{N}, {K}]")
+    y = _gemv(fmt, w, N, K, xq)
+    rng = np.random.default_rng(N + K)
+    rows = np.unique(np.r_[0, 1, N - 1, rng.integers(0, N, size=61)])
+    sub = w.reshape(N, -1)[rows].ravel()
+    ref, env = oracle.gemv_q8_1(fmt, sub, rows.size, K, xq, M)
+    linear_check(y[:, rows], ref, env, K, fmt)
+    assert np.all(np.isfinite(y))
+
+
+def test_gemv_metadata_errors():
+    w = torch.zeros(34 * 4, dtype=torch.uint8, device="cuda:0")
+    xq = torch.zeros(36, dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(nq.NqError):
+        nq.gemv_q8_1("nvfp4", w, 1, 64, torch.zeros(72, dtype=torch.uint8, device="cuda:0"))
+    with pytest.raises(nq.NqError):
+        nq.gemv_q8_1("gguf:q8_0", w[:33], 1, 32, xq)       # payload short
+    with pytest.raises(nq.NqError):                        # nine activation rows
+        nq.gemv_q8_1("gguf:q8_0", w[:34], 1, 32, torch.zeros(36 * 9, dtype=torch.uint8, device="cuda:0"))
+    with pytest.raises(nq.NqError):
+        nq.gemv_q8_1("gguf:q4_k", w, 1, 32, xq)            # K not a multiple of 256

@@ -20,6 +20,7 @@ import pytest
 
 import oracle
 import synth
+from linear_criterion import criterion
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 GGUF = [f for f in oracle.format_names() if f.startswith("gguf:")]
@@ -183,18 +184,9 @@ def test_gemv_errors():
 
 
 # --------------------------------------------------------------------------
-# The criterion: |y - y_ref| <= gamma(K + 8) * env + (K + 8) * 2^-148, with
-# gamma(n) = n u / (1 - n u), u = 2^-24: the bound of any binary32 summation
-# of K terms (each a product, or a scaled exact integer partial sum, with at
-# most a few extra roundings) over the magnitudes that are summed.  Several
-# float32 evaluation orders must stay inside it.
+# The criterion (tests/linear_criterion.py) admits float32 evaluations in
+# several orders and rejects a gross mistake.
 # --------------------------------------------------------------------------
-def criterion(K, env):
-    n = K + 8
-    u = 2.0 ** -24
-    return n * u / (1 - n * u) * env + n * 2.0 ** -148
-
-
 @pytest.mark.parametrize("fmt", ["gguf:q4_k", "gguf:q6_k", "gguf:q8_0", "gguf:iq2_xxs", "gguf:q4_1"])
 def test_criterion_admits_float32_orders(fmt):
     N, K, M = 16, 1024, 2
