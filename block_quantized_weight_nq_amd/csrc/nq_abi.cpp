@@ -68,19 +68,22 @@ void fill_info(int id, nq_format_info *out) {
 constexpr int MAX_DEVICES = 64;
 std::atomic<int> g_cu_count[MAX_DEVICES];
 
-// Workgroups the current device holds at once (the scale of the tile-size
-// choice).
-uint32_t resident_workgroups() {
+// Compute units of the current device.
+uint32_t compute_units() {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return 2048;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return 256;
     int cu = g_cu_count[dev].load(std::memory_order_relaxed);
     if (cu <= 0) {
         if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
             cu = 256;
         g_cu_count[dev].store(cu, std::memory_order_relaxed);
     }
-    return (uint32_t)cu * NQ_RESIDENT_PER_CU;
+    return (uint32_t)cu;
 }
+
+// Workgroups the current device holds at once (the scale of the tile-size
+// choice).
+uint32_t resident_workgroups() { return compute_units() * NQ_RESIDENT_PER_CU; }
 
 }  // namespace
 
@@ -339,7 +342,7 @@ NQ_API int nq_gemv_q8_1(int32_t format, const void *weight, uint64_t nbytes, int
     L.M = (uint64_t)M;
     L.xq = (const uint8_t *)xq;
     L.y = y;
-    L.resident = resident_workgroups();
+    L.cus = compute_units();
     switch (REGISTRY[format].family) {
     case NQ_FAMILY_SIMPLE: return nq::launch_gemv_simple(format, L, stream);
     case NQ_FAMILY_KQUANT: return nq::launch_gemv_kquant(format, L, stream);

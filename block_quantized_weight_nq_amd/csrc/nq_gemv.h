@@ -14,13 +14,13 @@
 // exact in binary32.  Output: gguf q8_1 blocks (36 bytes: d, sum, 32 codes).
 //
 // Product: y[m][n] = sum_k w[n][k] * d[m][k/32] * q[m][k] for weight rows n
-// and activation rows m < M <= 8, in binary32 with fused multiply-adds.  A
-// wave owns RW weight rows; its 64 lanes take the row's 8-value units in
-// turn (lane l: units l, l+64, ...), decode each unit exactly as the decode
-// kernels do, and keep one FP32 partial per (row, activation row); the
+// and activation rows m < M <= 8, accumulated in binary32.  A wave owns a
+// weight row: it stages the row's bytes in LDS, its 64 lanes take the row's
+// items in turn and keep one FP32 partial per activation row, and the
 // partials then meet in a fixed cross-lane tree, so every run gives the same
-// bits.  Lanes that handle the same unit for several rows read the unit's
-// activation codes once.
+// bits.  Integer items (q4_0, q8_0, q4_k, q6_k) form exact 8-bit dot
+// products with the activation codes; the other formats decode 8-value
+// units to binary32 as the decode kernels do.
 #pragma once
 
 #include "nq_gqenc.h"
@@ -122,6 +122,21 @@ __global__ __launch_bounds__(WG) void k_quantize_q8_1(Q81Args a) {
 
 // ------------------------------------------------------------------ product
 
+// Persistent waves: wave w of workgroup b takes rows 4b + w, 4b + w + step,
+// ... (step = 4 * grid), so the grid sweeps the weight matrix front to back.
+// A wave walks its rows in chunks of whole blocks (at most GV_CHUNK_BYTES,
+// 256 16-byte groups at any start offset): while the lanes compute the
+// current chunk from the wave's LDS region, the next chunk's loads (four
+// coalesced 16-byte loads per lane) are already in flight.  The activation
+// (codes, scales and exact code sums per 32-value block) is staged in LDS
+// once per workgroup when it fits, so the compute phase touches LDS only and
+// never waits on the prefetch.
+constexpr uint32_t GV_CHUNK_BYTES = 4080;
+constexpr int GV_NL = 4;                                   // groups a lane stages per chunk
+constexpr uint32_t GV_WAVE_DW = 4u * (64u * GV_NL + 1u);   // LDS dwords per wave: 256 groups + padding
+constexpr uint32_t GV_WAVES = (uint32_t)WG / 64u;
+constexpr uint32_t GV_ACT_LDS_MAX = 20480;                 // activation bytes staged in LDS at most
+
 struct GvArgs {
     const uint32_t *wbase;  // weight bytes of this launch's first row, aligned down to 4 bytes
     uint32_t wmis;          // that row's start - wbase (0..3)
@@ -131,65 +146,359 @@ struct GvArgs {
     uint32_t rows;          // weight rows in this launch
     uint32_t row_bytes;     // bytes per weight row, K / B * S
     uint32_t K;             // values per row
+    uint32_t kb;            // activation blocks per row, K / 32
     uint32_t xrow;          // dwords per activation row, K / 32 * 9
     uint32_t ldy;           // N
     uint32_t M;             // activation rows, 1 .. MT
+    uint32_t nbr;           // blocks per row
+    uint32_t cb;            // blocks per chunk
 };
 
-// Sum over the 64 lanes of a wave in a fixed butterfly order; every lane ends
-// with the same value.
-__device__ inline float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+// Sum over the 64 lanes of a wave with DPP steps, in a fixed order: lane
+// pairs, quads, half-rows and rows (each lane then holds its row's sum), then
+// row 1 += row 0 and row 3 += row 2, then rows 2 and 3 += lane 31.  Lane 63
+// holds ((r3 + r2) + (r1 + r0)), bit for bit the value of an XOR butterfly
+// over offsets 1, 2, ..., 32 (every step adds two equal-shaped partials, and
+// binary32 addition commutes).
+template <int CTRL, int ROWS>
+__device__ inline float dpp_add(float v) {
+    const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xF, false);
+    return v + __builtin_bit_cast(float, t);
+}
+
+__device__ inline float wave_sum63(float v) {
+    v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    v = dpp_add<0x141, 0xF>(v);  // row_half_mirror
+    v = dpp_add<0x140, 0xF>(v);  // row_mirror
+    v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
     return v;
 }
 
-// q8_1 code j (0..7) of the two dwords c.
-NQ_HD float q8_code(const uint32_t (&c)[2], int j) {
-    return (float)(int8_t)(c[j >> 2] >> (8 * (j & 3)));
+__device__ inline void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// One lane's partial sums for the RW weight rows r0.. of its wave: the row's
-// units lane, lane + 64, ..., each decoded to 8 binary32 weights and
-// multiplied with the unit's 8 activation codes (FMA chain), then scaled by
-// the activation block's d and added to the partial.
-template <int F, int MT, int RW, class Src>
-NQ_HD void gv_lane(const Src &src, const Tab &tab, const GvArgs &a, uint32_t r0, uint32_t lane,
-                   float (&acc)[RW][MT]) {
-    constexpr uint32_t UPB = (uint32_t)block_values(F) / 8u, S = (uint32_t)block_bytes(F);
+// Signed 4 x 8-bit dot product with accumulation (v_dot4 on the GPU).
+NQ_HD int dot4(uint32_t a, uint32_t b, int c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+#else
+    for (int k = 0; k < 4; k++) c += (int)(int8_t)(a >> (8 * k)) * (int)(int8_t)(b >> (8 * k));
+    return c;
+#endif
+}
+
+constexpr uint32_t ONES8 = 0x01010101u;
+
+// LDS dwords of the staged activation: M*K code bytes, then M*K/32 scales
+// (binary32), then M*K/32 code sums (int32).
+NQ_HD uint32_t gv_act_dw(const GvArgs &a) { return a.M * (a.K / 4u + 2u * a.kb); }
+
+// Activation staging, strided over the workgroup's threads.
+NQ_HD void gv_stage_act(const GvArgs &a, uint32_t *lds, uint32_t tid, uint32_t nthreads) {
+    float *dl = (float *)(lds + a.M * a.K / 4u);
+    int *sl = (int *)(dl + a.M * a.kb);
+    for (uint32_t i = tid; i < a.M * a.kb; i += nthreads) {
+        const uint32_t m = i / a.kb, blk = i - m * a.kb;
+        const uint32_t *p = a.xq + (uint64_t)m * a.xrow + (uint64_t)blk * 9u;
+        int sum = 0;
+        uint32_t *c = lds + (m * a.K + blk * 32u) / 4u;
 #pragma unroll
-    for (int rr = 0; rr < RW; rr++)
+        for (int j = 0; j < 8; j++) {
+            const uint32_t w = p[1 + j];
+            c[j] = w;
+            sum = dot4(ONES8, w, sum);
+        }
+        dl[i] = f16(p[0] & 0xFFFFu);
+        sl[i] = sum;
+    }
+}
+
+// Activation reader: q8_1 block ab of activation row m as its 8 code dwords,
+// its scale (binary32) and the exact sum of its codes; from LDS, or from the
+// blocks in global memory (the sum then computed).
+template <bool ALDS>
+struct GvAct {
+    const uint32_t *xq;
+    const uint32_t *lds;
+    uint32_t K, kb, xrow, M;
+    NQ_HD float block(uint32_t m, uint32_t ab, uint32_t (&c)[8], int *S) const {
+        if constexpr (ALDS) {
+            const uint32_t *cp = lds + (m * K + ab * 32u) / 4u;
 #pragma unroll
-        for (int m = 0; m < MT; m++) acc[rr][m] = 0.0f;
-    const uint32_t U = a.K >> 3;
-    for (uint32_t u = lane; u < U; u += 64u) {
-        const uint32_t xo = (u >> 2) * 9u, co = 1u + 2u * (u & 3u);
-        float xd[MT];
-        uint32_t xc[MT][2];
+            for (int j = 0; j < 8; j++) c[j] = cp[j];
+            const float *dl = (const float *)(lds + M * K / 4u);
+            *S = ((const int *)(dl + M * kb))[m * kb + ab];
+            return dl[m * kb + ab];
+        } else {
+            const uint32_t *p = xq + (uint64_t)m * xrow + (uint64_t)ab * 9u;
+            const u32x4a4 v0 = *(const u32x4a4 *)(p + 1), v1 = *(const u32x4a4 *)(p + 5);
+            c[0] = v0.x; c[1] = v0.y; c[2] = v0.z; c[3] = v0.w;
+            c[4] = v1.x; c[5] = v1.y; c[6] = v1.z; c[7] = v1.w;
+            int s = 0;
+#pragma unroll
+            for (int j = 0; j < 8; j++) s = dot4(ONES8, c[j], s);
+            *S = s;
+            return f16(p[0] & 0xFFFFu);
+        }
+    }
+    // the 8 codes (2 dwords) of unit u (8 values) and its block's scale
+    NQ_HD float unit(uint32_t m, uint32_t u, uint32_t (&c)[2]) const {
+        const uint32_t ab = u >> 2, co = 2u * (u & 3u);
+        if constexpr (ALDS) {
+            const uint32_t *cp = lds + (m * K + ab * 32u) / 4u + co;
+            c[0] = cp[0];
+            c[1] = cp[1];
+            return ((const float *)(lds + M * K / 4u))[m * kb + ab];
+        } else {
+            const uint32_t *p = xq + (uint64_t)m * xrow + (uint64_t)ab * 9u;
+            c[0] = p[1u + co];
+            c[1] = p[2u + co];
+            return f16(p[0] & 0xFFFFu);
+        }
+    }
+};
+
+// Items of the integer paths: a lane takes a group of weights of one block,
+// decodes them to 8-bit integers and multiplies them with the activation
+// codes of the same columns by 4-way dot products (exact integer sums); each
+// exact sum is then scaled in binary32 and added to the lane's partial.
+// Formats without such a path use 8-value units decoded exactly as the
+// decode kernels do (binary32), multiplied with the codes by an FMA chain.
+template <int F>
+struct GvItem {
+    static constexpr bool INT = F == Q4_0 || F == Q8_0 || F == Q4_K || F == Q6_K;
+    // items per block
+    static constexpr uint32_t IPB = F == Q4_K || F == Q6_K ? 4u : INT ? 1u : (uint32_t)block_values(F) / 8u;
+};
+
+// The K-quant 6-bit sub-scale and min of sub-block k (0..7) from the 12
+// packed bytes (three dwords), without branches: with j = k mod 4 and b1,
+// b2, b3 byte j of the three dwords, k < 4 takes (b1 & 63, b2 & 63) and
+// k >= 4 takes ((b3 & 15) | (b1 >> 6) << 4, (b3 >> 4) | (b2 >> 6) << 4).
+NQ_HD void kq_scale_min(const uint32_t (&h)[3], uint32_t k, uint32_t *sc, uint32_t *mn) {
+    const uint32_t sh = 8u * (k & 3u);
+    const uint32_t b1 = (h[0] >> sh) & 0xFFu, b2 = (h[1] >> sh) & 0xFFu, b3 = (h[2] >> sh) & 0xFFu;
+    const bool hi = k >= 4u;
+    *sc = hi ? (b3 & 15u) | ((b1 >> 6) << 4) : b1 & 63u;
+    *mn = hi ? (b3 >> 4) | ((b2 >> 6) << 4) : b2 & 63u;
+}
+
+// Item `part` of the block at LDS byte offset bo; b is the block's index in
+// its row (for the activation columns).
+template <int F, int MT, class Src, class Act>
+NQ_HD void gv_item(const Src &s, uint32_t bo, uint32_t b, uint32_t part, uint32_t nm, const Act &act,
+                   const Tab &tab, float (&acc)[MT]) {
+    constexpr uint32_t LO4 = 0x0F0F0F0Fu;
+    if constexpr (F == Q8_0) {
+        // d at 0, 32 signed codes at 2: w = d * q
+        const float d = f16(u16_at(s, bo));
+        uint32_t q[8];
+        window<8>(s, bo + 2u, q);
 #pragma unroll
         for (int m = 0; m < MT; m++) {
-            if (m < (int)a.M) {
-                const uint32_t *p = a.xq + (uint64_t)m * a.xrow + xo;
-                xd[m] = f16(p[0] & 0xFFFFu);
-                xc[m][0] = p[co];
-                xc[m][1] = p[co + 1u];
-            }
-        }
+            if (m >= (int)nm) continue;
+            uint32_t c[8];
+            int S;
+            const float dx = act.block((uint32_t)m, b, c, &S);
+            int I = 0;
 #pragma unroll
-        for (int rr = 0; rr < RW; rr++) {
-            const uint32_t r = r0 + (uint32_t)rr;
-            if (r >= a.rows) continue;
-            float w[8];
-            decode_unit<F>(src, a.wmis + r * a.row_bytes + (u / UPB) * S, u % UPB, tab, w);
+            for (int j = 0; j < 8; j++) I = dot4(q[j], c[j], I);
+            acc[m] = __builtin_fmaf(d * (float)I, dx, acc[m]);
+        }
+    } else if constexpr (F == Q4_0) {
+        // d at 0, 16 bytes at 2: value j < 16 the low nibble of byte j, j >= 16
+        // the high nibble of byte j - 16; w = d * (v - 8)
+        const float d = f16(u16_at(s, bo));
+        uint32_t q[4];
+        window<4>(s, bo + 2u, q);
+#pragma unroll
+        for (int m = 0; m < MT; m++) {
+            if (m >= (int)nm) continue;
+            uint32_t c[8];
+            int S;
+            const float dx = act.block((uint32_t)m, b, c, &S);
+            int I = 0;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                I = dot4(q[j] & LO4, c[j], I);
+                I = dot4((q[j] >> 4) & LO4, c[4 + j], I);
+            }
+            acc[m] = __builtin_fmaf(d * (float)(I - 8 * S), dx, acc[m]);
+        }
+    } else if constexpr (F == Q4_K) {
+        // part g: values 64g .. 64g+63, the low (sub-block 2g) and high
+        // (sub-block 2g+1) nibbles of bytes 16 + 32g .. 16 + 32g + 31;
+        // w = RN32(d * sc) * v - RN32(dmin * m)
+        uint32_t h[4], q[8];
+        window<4>(s, bo, h);
+        window<8>(s, bo + 16u + 32u * part, q);
+        const float d = f16(h[0] & 0xFFFFu), dmin = f16(h[0] >> 16);
+        const uint32_t hs[3] = {h[1], h[2], h[3]};
+        uint32_t sc0, m0, sc1, m1;
+        kq_scale_min(hs, 2u * part, &sc0, &m0);
+        kq_scale_min(hs, 2u * part + 1u, &sc1, &m1);
+        const float A0 = M(d, (float)sc0), B0 = M(dmin, (float)m0);
+        const float A1 = M(d, (float)sc1), B1 = M(dmin, (float)m1);
+        const uint32_t ab = 8u * b + 2u * part;
+#pragma unroll
+        for (int m = 0; m < MT; m++) {
+            if (m >= (int)nm) continue;
+            uint32_t c[8];
+            int S;
+            float dx = act.block((uint32_t)m, ab, c, &S);
+            int I = 0;
+#pragma unroll
+            for (int j = 0; j < 8; j++) I = dot4(q[j] & LO4, c[j], I);
+            acc[m] = __builtin_fmaf(A0 * (float)I - B0 * (float)S, dx, acc[m]);
+            dx = act.block((uint32_t)m, ab + 1u, c, &S);
+            I = 0;
+#pragma unroll
+            for (int j = 0; j < 8; j++) I = dot4((q[j] >> 4) & LO4, c[j], I);
+            acc[m] = __builtin_fmaf(A1 * (float)I - B1 * (float)S, dx, acc[m]);
+        }
+    } else if constexpr (F == Q6_K) {
+        // part p = 2h + c0: values 128h + 32c + i (i < 32) for c = c0 and
+        // c0 + 2: low 4 bits from byte 64h + 32c0 + i (low nibble for c0,
+        // high for c0 + 2), high 2 bits from byte 128 + 32h + i (bits 2c);
+        // w = RN32(d * sc[16-value sub-block]) * (v - 32)
+        const uint32_t hh = part >> 1, c0 = part & 1u;
+        uint32_t ql[8], qh[8], sw[2];
+        window<8>(s, bo + 64u * hh + 32u * c0, ql);
+        window<8>(s, bo + 128u + 32u * hh, qh);
+        window<2>(s, bo + 192u + 8u * hh + 2u * c0, sw);
+        const float d = f16(u16_at(s, bo + 208u));
+#pragma unroll
+        for (int e = 0; e < 2; e++) {
+            const uint32_t c = c0 + 2u * (uint32_t)e;
+            uint32_t v[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                v[j] = ((e ? ql[j] >> 4 : ql[j]) & LO4) | (((qh[j] >> (2u * c)) & 0x03030303u) << 4);
+            const float D0 = M(d, (float)(int8_t)(sw[e] & 0xFFu));
+            const float D1 = M(d, (float)(int8_t)((sw[e] >> 8) & 0xFFu));
+            const uint32_t ab = 8u * b + 4u * hh + c;
 #pragma unroll
             for (int m = 0; m < MT; m++) {
-                if (m >= (int)a.M) continue;
-                float t = w[0] * q8_code(xc[m], 0);
+                if (m >= (int)nm) continue;
+                uint32_t cx[8];
+                int S;
+                const float dx = act.block((uint32_t)m, ab, cx, &S);
+                int I0 = 0, I1 = 0, S0 = 0;
 #pragma unroll
-                for (int j = 1; j < 8; j++) t = __builtin_fmaf(w[j], q8_code(xc[m], j), t);
-                acc[rr][m] = __builtin_fmaf(t, xd[m], acc[rr][m]);
+                for (int j = 0; j < 4; j++) {
+                    I0 = dot4(v[j], cx[j], I0);
+                    S0 = dot4(ONES8, cx[j], S0);
+                    I1 = dot4(v[4 + j], cx[4 + j], I1);
+                }
+                const int S1 = S - S0;
+                acc[m] = __builtin_fmaf(D0 * (float)(I0 - 32 * S0) + D1 * (float)(I1 - 32 * S1), dx, acc[m]);
             }
         }
+    } else {
+        // unit `part` (8 values) decoded as the decode kernels decode it
+        float w[8];
+        decode_unit<F>(s, bo, part, tab, w);
+        const uint32_t u = b * ((uint32_t)block_values(F) / 8u) + part;  // unit index in the row
+#pragma unroll
+        for (int m = 0; m < MT; m++) {
+            if (m >= (int)nm) continue;
+            uint32_t xc[2];
+            const float dx = act.unit((uint32_t)m, u, xc);
+            float t = w[0] * (float)(int8_t)xc[0];
+#pragma unroll
+            for (int j = 1; j < 8; j++) t = __builtin_fmaf(w[j], (float)(int8_t)(xc[j >> 2] >> (8 * (j & 3))), t);
+            acc[m] = __builtin_fmaf(t, dx, acc[m]);
+        }
+    }
+}
+
+// A chunk of row r: blocks c0 .. c0+nb-1, spanning 16-byte groups g0..g1 of
+// the launch's weight bytes; its first block sits at LDS byte o0 of the
+// wave's region.
+struct GvChunk {
+    uint32_t r, c0, nb, g0, g1, o0;
+};
+
+NQ_HD GvChunk gv_chunk(const GvArgs &a, uint32_t r, uint32_t c0) {
+    const uint32_t S = a.row_bytes / a.nbr;
+    GvChunk c;
+    c.r = r;
+    c.c0 = c0;
+    c.nb = a.nbr - c0 < a.cb ? a.nbr - c0 : a.cb;
+    const uint32_t p0 = a.wmis + r * a.row_bytes + c0 * S, p1 = p0 + c.nb * S - 1u;
+    c.g0 = p0 >> 4;
+    c.g1 = p1 >> 4;
+    c.o0 = p0 & 15u;
+    return c;
+}
+
+// The chunk after (r, c0) in a wave's sequence: the row's next chunk, else
+// the first chunk of row r + step.
+NQ_HD void gv_advance(const GvArgs &a, uint32_t step, uint32_t *r, uint32_t *c0) {
+    *c0 += a.cb;
+    if (*c0 >= a.nbr) {
+        *c0 = 0u;
+        *r += step;
+    }
+}
+
+// Chunk staging, lane part, in two steps: the lane's GV_NL 16-byte loads
+// of groups g0 + lane + 64k (clamped to g1: lanes past the chunk repeat its
+// last group, same address and value) into registers, and later their
+// stores into the wave's LDS region (group g at dword 4 (g - g0)).  A group
+// that passes the last weight dword (wlast) is loaded as the 16 bytes that
+// end there and shifted into place, zero-filled; every load is in bounds
+// (a launch holds at least 16 bytes) and none depends on a branch.
+template <class Src>
+NQ_HD void gv_issue(const Src &src, uint32_t wlast, const GvChunk &c, uint32_t lane, uint32_t (&v)[GV_NL][4]) {
+#pragma unroll
+    for (int k = 0; k < GV_NL; k++) {
+        const uint32_t g0 = c.g0 + lane + 64u * (uint32_t)k;
+        const uint32_t i = 4u * (g0 < c.g1 ? g0 : c.g1);
+        src.load_stream4(i + 3u <= wlast ? i : wlast - 3u, v[k]);
+    }
+}
+
+// The stores of gv_issue's loads (the shift of a group that passed wlast is
+// applied here, once the data has arrived, so the loads stay in flight
+// until then).
+NQ_HD void gv_put(const GvChunk &c, uint32_t wlast, uint32_t lane, const uint32_t (&v)[GV_NL][4], uint32_t *lds) {
+    const bool whole = 4u * c.g1 + 3u <= wlast;  // the same for the whole wave: only a launch's last group passes
+#pragma unroll
+    for (int k = 0; k < GV_NL; k++) {
+        const uint32_t g0 = c.g0 + lane + 64u * (uint32_t)k, g = g0 < c.g1 ? g0 : c.g1;
+        uint32_t *d = lds + 4u * (g - c.g0);
+        if (whole) {
+            d[0] = v[k][0];
+            d[1] = v[k][1];
+            d[2] = v[k][2];
+            d[3] = v[k][3];
+        } else {
+            const uint32_t i = 4u * g, sh = i + 3u <= wlast ? 0u : i - (wlast - 3u);  // 0 .. 3
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const uint32_t x1 = e + 1 < 4 ? v[k][e + 1] : 0u, x2 = e + 2 < 4 ? v[k][e + 2] : 0u,
+                               x3 = e + 3 < 4 ? v[k][e + 3] : 0u;
+                d[e] = sh == 0u ? v[k][e] : sh == 1u ? x1 : sh == 2u ? x2 : x3;
+            }
+        }
+    }
+}
+
+// A lane's items of a staged chunk: items lane, lane + 64, ... in block order.
+template <int F, int MT, class Act>
+NQ_HD void gv_chunk_items(const LdsSrc &s, const GvChunk &c, uint32_t lane, uint32_t nm, const Act &act,
+                          const Tab &tab, float (&acc)[MT]) {
+    constexpr uint32_t IPB = GvItem<F>::IPB, S = (uint32_t)block_bytes(F);
+    const uint32_t n = c.nb * IPB;
+    for (uint32_t i = lane; i < n; i += 64u) {
+        const uint32_t bl = i / IPB;
+        gv_item<F, MT>(s, c.o0 + bl * S, c.c0 + bl, i - bl * IPB, nm, act, tab, acc);
     }
 }
 
@@ -207,44 +516,62 @@ NQ_HD void gv_fill_tables(uint64_t *t8, uint32_t *t4, uint32_t tid) {
     }
 }
 
-// Workgroup g (and g + grid, ...) takes weight rows 4*RW*g .. 4*RW*g + 4*RW - 1,
-// wave w of it rows 4*RW*g + RW*w ...
-template <int F, int MT, int RW>
-__global__ __launch_bounds__(WG) void k_gemv_unit(GvArgs a) {
+template <int F, int MT, bool ALDS>
+__global__ __launch_bounds__(WG) void k_gemv(GvArgs a) {
     using TS = TabSpec<F>;
     __shared__ uint64_t t8[TS::n8 > 0 ? TS::n8 : 1];
     __shared__ uint32_t t4[TS::n4 > 0 ? TS::n4 : 1];
-    if constexpr (TS::n8 + TS::n4 > 0) {
-        gv_fill_tables<F>(t8, t4, threadIdx.x);
-        __syncthreads();
-    }
+    extern __shared__ __attribute__((aligned(16))) uint32_t gv_lds[];
+    if constexpr (TS::n8 + TS::n4 > 0) gv_fill_tables<F>(t8, t4, threadIdx.x);
+    if constexpr (ALDS) gv_stage_act(a, gv_lds, threadIdx.x, WG);
+    if constexpr (ALDS || TS::n8 + TS::n4 > 0) __syncthreads();
     const Tab tab{t8, t4, nullptr, nullptr, 0xFFFFFFFFu, 1u};
+    const GvAct<ALDS> act{a.xq, gv_lds, a.K, a.kb, a.xrow, a.M};
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const uint32_t step = gridDim.x * GV_WAVES;
+    uint32_t *lds = gv_lds + (ALDS ? gv_act_dw(a) : 0u) + wave * GV_WAVE_DW;
     const DevSrc src{a.wbase, a.wlast};
-    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
-    for (uint32_t g = blockIdx.x; g * (4u * RW) < a.rows; g += gridDim.x) {
-        const uint32_t r0 = (g * 4u + wave) * (uint32_t)RW;
-        float acc[RW][MT];
-        gv_lane<F, MT, RW>(src, tab, a, r0, lane, acc);
+    uint32_t r = blockIdx.x * GV_WAVES + wave, c0 = 0u;
+    if (r >= a.rows) return;  // no workgroup barrier follows
+    GvChunk cur = gv_chunk(a, r, c0);
+    uint32_t v[GV_NL][4];
+    gv_issue(src, a.wlast, cur, lane, v);
+    float acc[MT];
 #pragma unroll
-        for (int rr = 0; rr < RW; rr++) {
-            const uint32_t r = r0 + (uint32_t)rr;
+    for (int m = 0; m < MT; m++) acc[m] = 0.0f;
+    for (;;) {
+        wave_lds_sync();  // the previous chunk's readers are done
+        gv_put(cur, a.wlast, lane, v, lds);
+        wave_lds_sync();
+        gv_advance(a, step, &r, &c0);
+        const bool more = r < a.rows;
+        GvChunk nxt = cur;
+        if (more) {
+            nxt = gv_chunk(a, r, c0);
+            gv_issue(src, a.wlast, nxt, lane, v);  // in flight while this chunk is computed
+        }
+        gv_chunk_items<F, MT>(LdsSrc{lds, 4u * (cur.g1 - cur.g0) + 3u}, cur, lane, a.M, act, tab, acc);
+        if (cur.c0 + cur.nb >= a.nbr) {
 #pragma unroll
             for (int m = 0; m < MT; m++) {
-                const float s = wave_sum(acc[rr][m]);
-                if (lane == 0u && r < a.rows && m < (int)a.M) a.y[(uint64_t)m * a.ldy + r] = s;
+                const float sum = wave_sum63(acc[m]);
+                if (lane == 63u && m < (int)a.M) a.y[(uint64_t)m * a.ldy + cur.r] = sum;
+                acc[m] = 0.0f;
             }
         }
+        if (!more) break;
+        cur = nxt;
     }
 }
 
-// Arguments and grid size of the launch for rows r0 .. r0 + rows - 1.
 // Host description of one product call.
 struct GvLaunch {
     const uint8_t *w;   // device weight payload [N, K]
     uint64_t N, K, M;
     const uint8_t *xq;  // device q8_1 activation blocks [M, K / 32]
     float *y;           // device output [M, N]
-    uint32_t resident;  // workgroups the device holds at once
+    uint32_t cus;       // compute units of the device
 };
 
 struct Q81Launch {
@@ -254,18 +581,13 @@ struct Q81Launch {
     uint32_t *status;
 };
 
-// Rows per wave: two when at most two activation rows (the unit's codes are
-// shared by both rows), else one (register budget).
-template <int MT>
-constexpr int gv_rw() {
-    return MT <= 2 ? 2 : 1;
-}
+// Activation staged in LDS when its codes, scales and sums fit the budget.
+inline bool gv_act_in_lds(uint64_t M, uint64_t K) { return M * (K + K / 32 * 8) <= GV_ACT_LDS_MAX; }
 
-template <int F, int MT>
-GvArgs gv_args(const GvLaunch &L, uint64_t r0, uint64_t rows, uint32_t *grid) {
-    constexpr int RW = gv_rw<MT>();
-    constexpr bool TABLES = TabSpec<F>::n8 + TabSpec<F>::n4 > 0;
-    const uint64_t row_bytes = L.K / (uint64_t)block_values(F) * (uint64_t)block_bytes(F);
+template <int F>
+GvArgs gv_args(const GvLaunch &L, uint64_t r0, uint64_t rows) {
+    constexpr uint64_t S = (uint64_t)block_bytes(F);
+    const uint64_t nbr = L.K / (uint64_t)block_values(F), row_bytes = nbr * S;
     const uint8_t *start = L.w + r0 * row_bytes;
     GvArgs a;
     a.wbase = (const uint32_t *)((uintptr_t)start & ~(uintptr_t)3);
@@ -276,14 +598,26 @@ GvArgs gv_args(const GvLaunch &L, uint64_t r0, uint64_t rows, uint32_t *grid) {
     a.rows = (uint32_t)rows;
     a.row_bytes = (uint32_t)row_bytes;
     a.K = (uint32_t)L.K;
+    a.kb = (uint32_t)(L.K / 32);
     a.xrow = (uint32_t)(L.K / 32 * 9);
     a.ldy = (uint32_t)L.N;
     a.M = (uint32_t)L.M;
-    uint64_t groups = (rows + 4u * RW - 1) / (4u * RW);
-    // formats with codebooks fill them per workgroup: fewer workgroups, each looping
-    if (TABLES && groups > L.resident) groups = L.resident;
-    *grid = (uint32_t)groups;
+    a.nbr = (uint32_t)nbr;
+    const uint64_t cb = GV_CHUNK_BYTES / S;  // every block is at most 292 bytes
+    a.cb = (uint32_t)(cb < nbr ? cb : nbr);
     return a;
+}
+
+// LDS bytes of a launch: the staged activation (when in LDS) and the waves' regions.
+inline uint32_t gv_lds_bytes(const GvArgs &a, bool alds) {
+    return 4u * ((alds ? gv_act_dw(a) : 0u) + GV_WAVES * GV_WAVE_DW);
+}
+
+// Workgroups of a launch: as many as the device keeps resident (the waves
+// persist), and no more than the rows need.
+inline uint32_t gv_grid(uint64_t rows, uint32_t resident) {
+    const uint64_t need = (rows + GV_WAVES - 1) / GV_WAVES;
+    return (uint32_t)(need < resident ? need : resident);
 }
 
 // Rows per launch: every weight byte offset of a launch fits 32 bits.
@@ -292,18 +626,29 @@ uint64_t gv_max_rows(const GvLaunch &L) {
     return 0xFFFFFFF0ull / (L.K / (uint64_t)block_values(F) * (uint64_t)block_bytes(F));
 }
 
-template <int F, int MT>
-int launch_gemv_mt(const GvLaunch &L, hipStream_t stream) {
+template <int F, int MT, bool ALDS>
+int launch_gemv_lds(const GvLaunch &L, hipStream_t stream) {
     const uint64_t max_rows = gv_max_rows<F>(L);
     for (uint64_t r0 = 0; r0 < L.N;) {
         const uint64_t rows = L.N - r0 < max_rows ? L.N - r0 : max_rows;
-        uint32_t grid;
-        const GvArgs a = gv_args<F, MT>(L, r0, rows, &grid);
-        hipLaunchKernelGGL((k_gemv_unit<F, MT, gv_rw<MT>()>), dim3(grid), dim3(WG), 0, stream, a);
+        const GvArgs a = gv_args<F>(L, r0, rows);
+        const uint32_t lds = gv_lds_bytes(a, ALDS);
+        int per_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)k_gemv<F, MT, ALDS>, WG, lds) !=
+                hipSuccess ||
+            per_cu < 1)
+            per_cu = 1;
+        const uint32_t grid = gv_grid(rows, (uint32_t)per_cu * L.cus);
+        hipLaunchKernelGGL((k_gemv<F, MT, ALDS>), dim3(grid), dim3(WG), lds, stream, a);
         if (hipGetLastError() != hipSuccess) return 9;  // NQ_ERR_HIP
         r0 += rows;
     }
     return 0;
+}
+
+template <int F, int MT>
+int launch_gemv_mt(const GvLaunch &L, hipStream_t stream) {
+    return gv_act_in_lds(L.M, L.K) ? launch_gemv_lds<F, MT, true>(L, stream) : launch_gemv_lds<F, MT, false>(L, stream);
 }
 
 template <int F>

@@ -189,16 +189,37 @@ long tile_blocks(int upt) {
     }
 }
 
-// Products with q8_1 activations: the launcher's row chunks (max_rows > 0
-// overrides the launcher's limit) and, per launch, every workgroup of the
-// grid-stride loop, every wave and lane (gv_lane through a bounds-checked
-// weight source), then the waves' butterfly sums in the kernel's order.
-template <int F, int MT>
-long run_gemv(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y, uint32_t resident,
-              uint64_t max_rows, char *err, int errlen) {
+// The kernel's DPP wave sum, step by step: each step adds to every lane of
+// the enabled rows the value its DPP source lane held before the step
+// (disabled rows add +0); returns lane 63.
+float dpp_sum63(float (&v)[64]) {
+    auto step = [&](auto src_of, unsigned rows) {
+        float t[64];
+        for (int l = 0; l < 64; l++) t[l] = (rows >> (l >> 4)) & 1u ? v[src_of(l)] : 0.0f;
+        for (int l = 0; l < 64; l++) v[l] = v[l] + t[l];
+    };
+    step([](int l) { return (l & ~3) | (l & 3) ^ 1; }, 0xFu);        // quad_perm [1,0,3,2]
+    step([](int l) { return (l & ~3) | (l & 3) ^ 2; }, 0xFu);        // quad_perm [2,3,0,1]
+    step([](int l) { return (l & ~7) | (7 - (l & 7)); }, 0xFu);      // row_half_mirror
+    step([](int l) { return (l & ~15) | (15 - (l & 15)); }, 0xFu);   // row_mirror
+    step([](int l) { return (l & ~15) - 1; }, 0xAu);                  // row_bcast:15 (rows 1, 3)
+    step([](int l) { return 31; }, 0xCu);                             // row_bcast:31 (rows 2, 3)
+    return v[63];
+}
+
+// Products with q8_1 activations: the launcher's row launches (max_rows > 0
+// overrides the launcher's limit) and, per launch, a grid of `resident`
+// workgroups (capped as the launcher caps it): the workgroup's activation
+// staging and tables, then every wave's chunk sequence as the kernel walks
+// it: the lanes' loads (through a bounds-checked source) and stores into a
+// poisoned LDS region, whose bytes are then compared with the payload, the
+// lanes' items, and at each row's end the wave's butterfly sum in the
+// kernel's order.
+template <int F, int MT, bool ALDS>
+long run_gemv_lds(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y,
+                  uint32_t resident, uint64_t max_rows, char *err, int errlen) {
     using namespace nq;
-    constexpr int RW = gv_rw<MT>();
-    const GvLaunch L{w, N, K, M, xq, y, resident};
+    const GvLaunch L{w, N, K, M, xq, y, 0u};
     const uint64_t lim = max_rows ? max_rows : gv_max_rows<F>(L);
     const uint64_t row_bytes = K / (uint64_t)block_values(F) * (uint64_t)block_bytes(F);
     std::vector<uint64_t> t8(TabSpec<F>::n8 > 0 ? TabSpec<F>::n8 : 1);
@@ -208,28 +229,61 @@ long run_gemv(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint6
     long errors = 0;
     for (uint64_t r0 = 0; r0 < N;) {
         const uint64_t rows = N - r0 < lim ? N - r0 : lim;
-        uint32_t grid;
-        const GvArgs a = gv_args<F, MT>(L, r0, rows, &grid);
+        const GvArgs a = gv_args<F>(L, r0, rows);
+        const uint32_t lds_bytes = gv_lds_bytes(a, ALDS);
+        if (lds_bytes > 65536u) {
+            snprintf(err, errlen, "LDS request %u bytes", lds_bytes);
+            return 1;
+        }
+        const uint32_t grid = gv_grid(rows, resident);
         Check chk{(uintptr_t)(w + r0 * row_bytes), (uintptr_t)(w + (r0 + rows) * row_bytes), 0, {0}};
         const HostSrc src{a.wbase, a.wlast, &chk};
+        std::vector<uint32_t> act_lds(ALDS ? gv_act_dw(a) : 1u, 0xA5A5A5A5u);
+        if (ALDS)
+            for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) gv_stage_act(a, act_lds.data(), tid, WG);
+        const GvAct<ALDS> act{a.xq, act_lds.data(), a.K, a.kb, a.xrow, a.M};
+        std::vector<uint32_t> lds(GV_WAVE_DW);
+        const uint32_t step = grid * GV_WAVES;
         for (uint32_t b = 0; b < grid; b++)
-            for (uint32_t g = b; g * (4u * RW) < a.rows; g += grid)
-                for (uint32_t wave = 0; wave < 4u; wave++) {
-                    const uint32_t rb = (g * 4u + wave) * (uint32_t)RW;
-                    static float acc[64][RW][MT];
-                    for (uint32_t lane = 0; lane < 64u; lane++) gv_lane<F, MT, RW>(src, tab, a, rb, lane, acc[lane]);
-                    for (int rr = 0; rr < RW; rr++)
+            for (uint32_t wave = 0; wave < GV_WAVES; wave++) {
+                uint32_t r = b * GV_WAVES + wave, c0 = 0;
+                if (r >= a.rows) continue;
+                static float acc[64][MT];
+                for (uint32_t lane = 0; lane < 64u; lane++)
+                    for (int m = 0; m < MT; m++) acc[lane][m] = 0.0f;
+                GvChunk cur = gv_chunk(a, r, c0);
+                for (;;) {
+                    if (cur.g1 - cur.g0 + 1u > 64u * GV_NL) {
+                        snprintf(err, errlen, "chunk of %u groups past the wave's loads", cur.g1 - cur.g0 + 1u);
+                        return 1;
+                    }
+                    std::fill(lds.begin(), lds.end(), 0xA5A5A5A5u);
+                    for (uint32_t lane = 0; lane < 64u; lane++) {
+                        uint32_t v[GV_NL][4];
+                        gv_issue(src, a.wlast, cur, lane, v);
+                        gv_put(cur, a.wlast, lane, v, lds.data());
+                    }
+                    const uint8_t *cb = (const uint8_t *)lds.data() + cur.o0;
+                    const uint8_t *pb = (const uint8_t *)a.wbase + a.wmis + (uint64_t)cur.r * a.row_bytes +
+                                        (uint64_t)cur.c0 * block_bytes(F);
+                    if (memcmp(cb, pb, (size_t)cur.nb * block_bytes(F)) != 0 && chk.errors++ == 0)
+                        snprintf(chk.msg, sizeof chk.msg, "staged chunk of row %u differs from the payload", cur.r);
+                    const LdsSrc s{lds.data(), 4u * (cur.g1 - cur.g0) + 3u};
+                    for (uint32_t lane = 0; lane < 64u; lane++)
+                        gv_chunk_items<F, MT>(s, cur, lane, a.M, act, tab, acc[lane]);
+                    if (cur.c0 + cur.nb >= a.nbr) {
                         for (int m = 0; m < MT; m++) {
-                            float v[64], nv[64];
-                            for (int l = 0; l < 64; l++) v[l] = acc[l][rr][m];
-                            for (int off = 32; off >= 1; off >>= 1) {
-                                for (int l = 0; l < 64; l++) nv[l] = v[l] + v[l ^ off];
-                                std::copy(nv, nv + 64, v);
-                            }
-                            const uint32_t r = rb + (uint32_t)rr;
-                            if (r < a.rows && m < (int)a.M) a.y[(uint64_t)m * a.ldy + r] = v[0];
+                            float v[64];
+                            for (int l = 0; l < 64; l++) v[l] = acc[l][m];
+                            if (m < (int)a.M) a.y[(uint64_t)m * a.ldy + cur.r] = dpp_sum63(v);
+                            for (int l = 0; l < 64; l++) acc[l][m] = 0.0f;
                         }
+                    }
+                    gv_advance(a, step, &r, &c0);
+                    if (r >= a.rows) break;
+                    cur = gv_chunk(a, r, c0);
                 }
+            }
         if (chk.errors) {
             if (errors == 0) snprintf(err, errlen, "%s", chk.msg);
             errors += chk.errors;
@@ -237,6 +291,13 @@ long run_gemv(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint6
         r0 += rows;
     }
     return errors;
+}
+
+template <int F, int MT>
+long run_gemv(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y, uint32_t resident,
+              uint64_t max_rows, char *err, int errlen) {
+    return nq::gv_act_in_lds(M, K) ? run_gemv_lds<F, MT, true>(w, N, K, xq, M, y, resident, max_rows, err, errlen)
+                                   : run_gemv_lds<F, MT, false>(w, N, K, xq, M, y, resident, max_rows, err, errlen);
 }
 
 template <int F>

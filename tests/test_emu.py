@@ -320,3 +320,19 @@ def test_emu_quantize_q8_1_failures():
     assert rc == 0 and guards
     assert st == ost == 3
     assert np.array_equal(b, ob)
+
+
+@pytest.mark.parametrize("fmt,K", [("gguf:q8_0", 16384), ("gguf:q4_k", 28672), ("gguf:q6_k", 16384),
+                                   ("gguf:q4_1", 24576), ("gguf:iq4_xs", 24576)])
+def test_emu_gemv_rows_staged_in_chunks(fmt, K):
+    """Rows longer than one staged chunk are staged and summed chunk by chunk."""
+    idx, B, S, _ = oracle.info(fmt)
+    assert K // B * S > 12288
+    N, M = 3, 2
+    w = synth.payload(fmt, N * K // B, 5, synth.binade(-6, -2, False))
+    _, xq = oracle.quantize_q8_1(_act(M, K, 8).astype(np.float32))
+    y, rc, msg, guards = emu_lib.gemv_q8_1(idx, w, N, K, xq, M, w_mis=1)
+    assert rc == 0, msg
+    assert guards
+    ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
+    linear_check(y, ref, env, K, fmt)

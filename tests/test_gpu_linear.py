@@ -181,3 +181,16 @@ def test_gemv_metadata_errors():
         nq.gemv_q8_1("gguf:q8_0", w[:34], 1, 32, torch.zeros(36 * 9, dtype=torch.uint8, device="cuda:0"))
     with pytest.raises(nq.NqError):
         nq.gemv_q8_1("gguf:q4_k", w, 1, 32, xq)            # K not a multiple of 256
+
+
+@pytest.mark.parametrize("fmt,K", [("gguf:q8_0", 16384), ("gguf:q4_k", 28672), ("gguf:q6_k", 16384),
+                                   ("gguf:q4_1", 24576), ("gguf:iq4_xs", 24576)])
+def test_gemv_rows_staged_in_chunks(fmt, K):
+    """Rows longer than one staged chunk (12 KiB) are staged chunk by chunk."""
+    N, M = 21, 2
+    w = _weights(fmt, N, K, 12)
+    _, xq = oracle.quantize_q8_1(_act(M, K, 12).astype(np.float32))
+    ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
+    announce(f"gemv chunked {fmt} K={K}")
+    y = _gemv(fmt, w, N, K, xq, 2)
+    linear_check(y, ref, env, K, fmt)
