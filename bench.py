@@ -31,15 +31,18 @@ OUT_CODES = {"f32": 0, "f16": 1, "bf16": 2, "f64": 3}
 OUT_SIZE = {"f32": 4, "f16": 2, "bf16": 2, "f64": 8}
 
 
+# The sources the decode kernels are built from (the kernels the counter profile covers).
+DECODE_SOURCES = ["iq_grids.h", "nq_decode.h", "nq_kernel.h", "k_simple.hip", "k_kquant.hip", "k_iq.hip",
+                  "k_fp4.hip", "k_ternary.hip"]
+
+
 def sources_sha256():
-    """Hash of the kernel sources without comments (the build the counter profile was taken on)."""
-    import glob
+    """Hash of the decode kernels' sources without comments (the build the counter profile was taken on)."""
     import re
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
     csrc = os.path.join(here, "block_quantized_weight_nq_amd", "csrc")
-    files = sorted(glob.glob(os.path.join(csrc, "*.h")) + glob.glob(os.path.join(csrc, "*.hip")) +
-                   glob.glob(os.path.join(csrc, "*.cpp")))
+    files = sorted(os.path.join(csrc, f) for f in DECODE_SOURCES)
     h = hashlib.sha256()
     for f in files:
         h.update(os.path.basename(f).encode())
@@ -280,6 +283,46 @@ def gq_measurement(torch, nq, scheme, shape, in_dtype, launches=60, footprint=1 
     return res
 
 
+def gemv_measurement(torch, nq, synth, fmt, shape, M, launches=60, footprint=1 << 30, seed=0x6E7C7000):
+    """Products with q8_1 activations (nq_gemv_q8_1) over rotating replicas of
+    a weight [N, K]; bytes = weight payload + q8_1 activation blocks + binary32
+    output, each counted once per launch (the activation is read from cache by
+    every workgroup)."""
+    import numpy as np
+    N, K = shape
+    info = nq.format_query(fmt)
+    nbytes_w = N * K // info.block_values * info.block_bytes
+    host = synth.payload(fmt, N * K // info.block_values, seed, synth.binade(-6, -2, False))
+    w0 = torch.from_numpy(host).to("cuda:0")
+    reps = max(1, math.ceil(footprint / nbytes_w))
+    ws = [w0] + [w0.clone() for _ in range(reps - 1)]
+    rng = np.random.default_rng(seed)
+    x = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to("cuda:0")
+    xq, _ = nq.quantize_q8_1(x)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        h = torch.cuda.current_stream().cuda_stream
+        for i in range(launches):
+            rc = nq.gemv_q8_1_raw(info.id, ws[i % reps].data_ptr(), nbytes_w, N, K, xq.data_ptr(), M, y.data_ptr(), h)
+            if rc != 0:
+                raise nq.NqError(rc, fmt)
+    ms, _ = time_graph(torch, g, 3)
+    mean_ms = ms / launches
+    nbytes = nbytes_w + xq.numel() + 4 * M * N
+    gbps = nbytes / (mean_ms * 1e-3) / 1e9
+    res = {"shape": shape, "M": M, "gbps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+           "weight_gbps": round(nbytes_w / (mean_ms * 1e-3) / 1e9, 1), "mean_launch_us": round(mean_ms * 1e3, 3),
+           "replicas": reps, "weights_per_s": round(N * K / (mean_ms * 1e-3), 1), "bytes_per_launch": nbytes}
+    del g, ws, w0
+    torch.cuda.empty_cache()
+    return res
+
+
+GEMV_CASES = [("gguf:q4_k", 1), ("gguf:q6_k", 1), ("gguf:q8_0", 1), ("gguf:q4_0", 1), ("gguf:iq4_xs", 1),
+              ("gguf:mxfp4", 1), ("gguf:iq2_xxs", 1), ("gguf:tq2_0", 1), ("gguf:q4_k", 8), ("gguf:q8_0", 8)]
+
+
 def cpu_baseline(nq, synth, tensors, fraction=8):
     """The oracle on the first 1/fraction of every tensor's blocks, one thread."""
     import numpy as np
@@ -305,6 +348,47 @@ def cpu_baseline(nq, synth, tensors, fraction=8):
             "elements_per_s": round(total_elems / secs, 1)}
 
 
+def gemv_cpu_baseline(synth, fmt="gguf:q4_k", shape=(14336, 4096), rows=14336, seed=0x6E7C7000):
+    """The oracle's product (binary64) on the first `rows` rows of one weight,
+    M = 1, one thread."""
+    import numpy as np
+    import oracle
+    N, K = shape
+    _, B, S, _ = oracle.info(fmt)
+    w = synth.payload(fmt, rows * K // B, seed, synth.binade(-6, -2, False))
+    x = np.random.default_rng(seed).standard_normal((1, K)).astype(np.float32)
+    t0 = time.perf_counter()
+    _, xq = oracle.quantize_q8_1(x)
+    oracle.gemv_q8_1(fmt, w, rows, K, xq, 1)
+    secs = time.perf_counter() - t0
+    nbytes = w.size + xq.size + 4 * rows
+    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{fmt} rows 0..{rows - 1} of [{N}, {K}], M = 1 ({secs:.1f} s on one host core)",
+            "weights_per_s": round(rows * K / secs, 1)}
+
+
+def gemv_only(torch, nq, synth, args):
+    """The product measurements alone (one JSON line): every GEMV_CASES entry
+    at both shapes, the dominant one's roofline, and the oracle beside it."""
+    res = {}
+    for fmt, M in GEMV_CASES:
+        for shape in ([14336, 4096], [4096, 14336]):
+            key = f"gemv_q8_1 {fmt}{shape} M={M}"
+            res[key] = gemv_measurement(torch, nq, synth, fmt, shape, M)
+            log(f"{key}: {res[key]['gbps']} GB/s ({100 * res[key]['frac_hbm_peak']:.1f}% of peak)")
+    head = res["gemv_q8_1 gguf:q4_k[14336, 4096] M=1"]
+    roofline = {"bound": "hbm", "achieved": head["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": head["frac_hbm_peak"], "traffic": None, "kernel": "k_gemv gguf:q4_k M=1",
+                "bytes_per_launch": head["bytes_per_launch"], "mean_launch_us": head["mean_launch_us"]}
+    cpu = None if args.no_cpu_baseline else gemv_cpu_baseline(synth)
+    line = {"metric": "gemv_q8_1 GB/s (weight + activation + output) per launch, 1\u00d7MI355X",
+            "value": head["gbps"], "unit": "GB/s", "n_gpus": 1, "higher_is_better": True, "dtype": "f32",
+            "data": "synthetic",
+            "config": {"workload": "q4_k weight [14336, 4096] x one q8_1 activation row, rotating replicas"},
+            "roofline": roofline, "cpu_baseline": cpu, "cases": res}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -312,6 +396,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-per-format", action="store_true", help="skip the rotating per-workload timings")
+    ap.add_argument("--gemv-only", action="store_true",
+                    help="measure only the products with q8_1 activations (one JSON line of its own)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
                     help="first run a plain device copy of this many MiB (for counter calibration)")
     args = ap.parse_args()
@@ -341,6 +427,10 @@ def main():
         torch.cuda.synchronize()
         log(f"copy calibration: 3 x {args.calibrate_copy} MiB device copies done")
         del a, b
+
+    if args.gemv_only:
+        gemv_only(torch, nq, synth, args)
+        return
 
     tensors, _ = workloads.config5()
     staging = staging_buffer(torch, tensors, nq)
@@ -401,6 +491,12 @@ def main():
             key = f"{fmt}[14336, 4096]->bf16"
             extra[key] = fp8_row_measurement(torch, nq, fmt, [14336, 4096], "bf16")
             log(f"{key}: {extra[key]['gbps']} GB/s ({100 * extra[key]['frac_hbm_peak']:.1f}% of peak)")
+        # products with q8_1 activations: the decode-phase shapes of a Llama-3-8B layer
+        for fmt, M in GEMV_CASES:
+            for shape in ([14336, 4096], [4096, 14336]):
+                key = f"gemv_q8_1 {fmt}{shape} M={M}"
+                extra[key] = gemv_measurement(torch, nq, synth, fmt, shape, M)
+                log(f"{key}: {extra[key]['gbps']} GB/s ({100 * extra[key]['frac_hbm_peak']:.1f}% of peak)")
 
     cpu = None
     if not args.no_cpu_baseline:
