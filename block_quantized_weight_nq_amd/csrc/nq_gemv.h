@@ -124,16 +124,31 @@ __global__ __launch_bounds__(WG) void k_quantize_q8_1(Q81Args a) {
 
 // Persistent waves: wave w of workgroup b takes rows 4b + w, 4b + w + step,
 // ... (step = 4 * grid), so the grid sweeps the weight matrix front to back.
-// A wave walks its rows in chunks of whole blocks (at most GV_CHUNK_BYTES,
-// 256 16-byte groups at any start offset): while the lanes compute the
-// current chunk from the wave's LDS region, the next chunk's loads (four
-// coalesced 16-byte loads per lane) are already in flight.  The activation
+// A wave walks its rows in chunks of whole blocks (at most gv_chunk_bytes,
+// 64 * gv_nl 16-byte groups at any start offset; two whole rows per chunk
+// when they fit): while the lanes compute the current chunk from the wave's
+// LDS region, the next chunk's loads (gv_nl coalesced 16-byte loads per
+// lane) are already in flight.  The activation
 // (codes, scales and exact code sums per 32-value block) is staged in LDS
 // once per workgroup when it fits, so the compute phase touches LDS only and
 // never waits on the prefetch.
-constexpr uint32_t GV_CHUNK_BYTES = 4080;
-constexpr int GV_NL = 4;                                   // groups a lane stages per chunk
-constexpr uint32_t GV_WAVE_DW = 4u * (64u * GV_NL + 1u);   // LDS dwords per wave: 256 groups + padding
+// Per chunk a lane issues gv_nl<RW>() 16-byte loads: 5 when a chunk holds two
+// rows (a pair of 2304-byte q4_k rows of 4096 values fits), else 4 (the
+// measured best for single rows).
+template <int RW>
+constexpr int gv_nl() {
+    return RW == 2 ? 5 : 4;
+}
+// Chunk bytes: whole blocks spanning at most 64 * gv_nl 16-byte groups at any start offset.
+template <int RW>
+constexpr uint32_t gv_chunk_bytes() {
+    return 1024u * (uint32_t)gv_nl<RW>() - 16u;
+}
+// LDS dwords per wave: the groups plus one group of padding.
+template <int RW>
+constexpr uint32_t gv_wave_dw() {
+    return 4u * (64u * (uint32_t)gv_nl<RW>() + 1u);
+}
 constexpr uint32_t GV_WAVES = (uint32_t)WG / 64u;
 constexpr uint32_t GV_ACT_LDS_MAX = 20480;                 // activation bytes staged in LDS at most
 
@@ -152,6 +167,7 @@ struct GvArgs {
     uint32_t M;             // activation rows, 1 .. MT
     uint32_t nbr;           // blocks per row
     uint32_t cb;            // blocks per chunk
+    uint32_t rw;            // rows a chunk holds: 2 when two whole rows fit one chunk, else 1
 };
 
 // Sum over the 64 lanes of a wave with DPP steps, in a fixed order: lane
@@ -269,11 +285,28 @@ struct GvAct {
 // exact sum is then scaled in binary32 and added to the lane's partial.
 // Formats without such a path use 8-value units decoded exactly as the
 // decode kernels do (binary32), multiplied with the codes by an FMA chain.
+// An item is taken in three steps: its weights (gv_w, once per row), its
+// activation columns (gv_a, once per activation row, shared by the rows of
+// a chunk) and the product (gv_dot).
 template <int F>
 struct GvItem {
     static constexpr bool INT = F == Q4_0 || F == Q8_0 || F == Q4_K || F == Q6_K;
     // items per block
     static constexpr uint32_t IPB = F == Q4_K || F == Q6_K ? 4u : INT ? 1u : (uint32_t)block_values(F) / 8u;
+};
+
+// Decoded weights of one item (the fields a format uses).
+struct GvW {
+    uint32_t q[16];
+    float f[8];
+};
+
+// Activation columns of one item for one activation row: up to two q8_1
+// blocks' codes, scales and exact code sums.
+struct GvA {
+    uint32_t c[16];
+    float d[2];
+    int S[2];
 };
 
 // The K-quant 6-bit sub-scale and min of sub-block k (0..7) from the 12
@@ -283,53 +316,29 @@ struct GvItem {
 NQ_HD void kq_scale_min(const uint32_t (&h)[3], uint32_t k, uint32_t *sc, uint32_t *mn) {
     const uint32_t sh = 8u * (k & 3u);
     const uint32_t b1 = (h[0] >> sh) & 0xFFu, b2 = (h[1] >> sh) & 0xFFu, b3 = (h[2] >> sh) & 0xFFu;
-    const bool hi = k >= 4u;
-    *sc = hi ? (b3 & 15u) | ((b1 >> 6) << 4) : b1 & 63u;
-    *mn = hi ? (b3 >> 4) | ((b2 >> 6) << 4) : b2 & 63u;
+    const uint32_t hi = 0u - (uint32_t)(k >= 4u);  // all ones for k >= 4
+    *sc = (((b3 & 15u) | ((b1 >> 6) << 4)) & hi) | ((b1 & 63u) & ~hi);
+    *mn = (((b3 >> 4) | ((b2 >> 6) << 4)) & hi) | ((b2 & 63u) & ~hi);
 }
 
-// Item `part` of the block at LDS byte offset bo; b is the block's index in
-// its row (for the activation columns).
-template <int F, int MT, class Src, class Act>
-NQ_HD void gv_item(const Src &s, uint32_t bo, uint32_t b, uint32_t part, uint32_t nm, const Act &act,
-                   const Tab &tab, float (&acc)[MT]) {
-    constexpr uint32_t LO4 = 0x0F0F0F0Fu;
+// Weights of item `part` of the block at LDS byte offset bo.
+template <int F, class Src>
+NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w) {
     if constexpr (F == Q8_0) {
         // d at 0, 32 signed codes at 2: w = d * q
-        const float d = f16(u16_at(s, bo));
+        w.f[0] = f16(u16_at(s, bo));
         uint32_t q[8];
         window<8>(s, bo + 2u, q);
 #pragma unroll
-        for (int m = 0; m < MT; m++) {
-            if (m >= (int)nm) continue;
-            uint32_t c[8];
-            int S;
-            const float dx = act.block((uint32_t)m, b, c, &S);
-            int I = 0;
-#pragma unroll
-            for (int j = 0; j < 8; j++) I = dot4(q[j], c[j], I);
-            acc[m] = __builtin_fmaf(d * (float)I, dx, acc[m]);
-        }
+        for (int j = 0; j < 8; j++) w.q[j] = q[j];
     } else if constexpr (F == Q4_0) {
         // d at 0, 16 bytes at 2: value j < 16 the low nibble of byte j, j >= 16
         // the high nibble of byte j - 16; w = d * (v - 8)
-        const float d = f16(u16_at(s, bo));
+        w.f[0] = f16(u16_at(s, bo));
         uint32_t q[4];
         window<4>(s, bo + 2u, q);
 #pragma unroll
-        for (int m = 0; m < MT; m++) {
-            if (m >= (int)nm) continue;
-            uint32_t c[8];
-            int S;
-            const float dx = act.block((uint32_t)m, b, c, &S);
-            int I = 0;
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                I = dot4(q[j] & LO4, c[j], I);
-                I = dot4((q[j] >> 4) & LO4, c[4 + j], I);
-            }
-            acc[m] = __builtin_fmaf(d * (float)(I - 8 * S), dx, acc[m]);
-        }
+        for (int j = 0; j < 4; j++) w.q[j] = q[j];
     } else if constexpr (F == Q4_K) {
         // part g: values 64g .. 64g+63, the low (sub-block 2g) and high
         // (sub-block 2g+1) nibbles of bytes 16 + 32g .. 16 + 32g + 31;
@@ -342,30 +351,18 @@ NQ_HD void gv_item(const Src &s, uint32_t bo, uint32_t b, uint32_t part, uint32_
         uint32_t sc0, m0, sc1, m1;
         kq_scale_min(hs, 2u * part, &sc0, &m0);
         kq_scale_min(hs, 2u * part + 1u, &sc1, &m1);
-        const float A0 = M(d, (float)sc0), B0 = M(dmin, (float)m0);
-        const float A1 = M(d, (float)sc1), B1 = M(dmin, (float)m1);
-        const uint32_t ab = 8u * b + 2u * part;
+        w.f[0] = M(d, (float)sc0);
+        w.f[1] = M(dmin, (float)m0);
+        w.f[2] = M(d, (float)sc1);
+        w.f[3] = M(dmin, (float)m1);
 #pragma unroll
-        for (int m = 0; m < MT; m++) {
-            if (m >= (int)nm) continue;
-            uint32_t c[8];
-            int S;
-            float dx = act.block((uint32_t)m, ab, c, &S);
-            int I = 0;
-#pragma unroll
-            for (int j = 0; j < 8; j++) I = dot4(q[j] & LO4, c[j], I);
-            acc[m] = __builtin_fmaf(A0 * (float)I - B0 * (float)S, dx, acc[m]);
-            dx = act.block((uint32_t)m, ab + 1u, c, &S);
-            I = 0;
-#pragma unroll
-            for (int j = 0; j < 8; j++) I = dot4((q[j] >> 4) & LO4, c[j], I);
-            acc[m] = __builtin_fmaf(A1 * (float)I - B1 * (float)S, dx, acc[m]);
-        }
+        for (int j = 0; j < 8; j++) w.q[j] = q[j];
     } else if constexpr (F == Q6_K) {
         // part p = 2h + c0: values 128h + 32c + i (i < 32) for c = c0 and
         // c0 + 2: low 4 bits from byte 64h + 32c0 + i (low nibble for c0,
         // high for c0 + 2), high 2 bits from byte 128 + 32h + i (bits 2c);
         // w = RN32(d * sc[16-value sub-block]) * (v - 32)
+        constexpr uint32_t LO4 = 0x0F0F0F0Fu;
         const uint32_t hh = part >> 1, c0 = part & 1u;
         uint32_t ql[8], qh[8], sw[2];
         window<8>(s, bo + 64u * hh + 32u * c0, ql);
@@ -375,62 +372,111 @@ NQ_HD void gv_item(const Src &s, uint32_t bo, uint32_t b, uint32_t part, uint32_
 #pragma unroll
         for (int e = 0; e < 2; e++) {
             const uint32_t c = c0 + 2u * (uint32_t)e;
-            uint32_t v[8];
 #pragma unroll
             for (int j = 0; j < 8; j++)
-                v[j] = ((e ? ql[j] >> 4 : ql[j]) & LO4) | (((qh[j] >> (2u * c)) & 0x03030303u) << 4);
-            const float D0 = M(d, (float)(int8_t)(sw[e] & 0xFFu));
-            const float D1 = M(d, (float)(int8_t)((sw[e] >> 8) & 0xFFu));
-            const uint32_t ab = 8u * b + 4u * hh + c;
-#pragma unroll
-            for (int m = 0; m < MT; m++) {
-                if (m >= (int)nm) continue;
-                uint32_t cx[8];
-                int S;
-                const float dx = act.block((uint32_t)m, ab, cx, &S);
-                int I0 = 0, I1 = 0, S0 = 0;
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    I0 = dot4(v[j], cx[j], I0);
-                    S0 = dot4(ONES8, cx[j], S0);
-                    I1 = dot4(v[4 + j], cx[4 + j], I1);
-                }
-                const int S1 = S - S0;
-                acc[m] = __builtin_fmaf(D0 * (float)(I0 - 32 * S0) + D1 * (float)(I1 - 32 * S1), dx, acc[m]);
-            }
+                w.q[8 * e + j] = ((e ? ql[j] >> 4 : ql[j]) & LO4) | (((qh[j] >> (2u * c)) & 0x03030303u) << 4);
+            w.f[2 * e] = M(d, (float)(int8_t)(sw[e] & 0xFFu));
+            w.f[2 * e + 1] = M(d, (float)(int8_t)((sw[e] >> 8) & 0xFFu));
         }
     } else {
         // unit `part` (8 values) decoded as the decode kernels decode it
-        float w[8];
-        decode_unit<F>(s, bo, part, tab, w);
-        const uint32_t u = b * ((uint32_t)block_values(F) / 8u) + part;  // unit index in the row
-#pragma unroll
-        for (int m = 0; m < MT; m++) {
-            if (m >= (int)nm) continue;
-            uint32_t xc[2];
-            const float dx = act.unit((uint32_t)m, u, xc);
-            float t = w[0] * (float)(int8_t)xc[0];
-#pragma unroll
-            for (int j = 1; j < 8; j++) t = __builtin_fmaf(w[j], (float)(int8_t)(xc[j >> 2] >> (8 * (j & 3))), t);
-            acc[m] = __builtin_fmaf(t, dx, acc[m]);
-        }
+        decode_unit<F>(s, bo, part, tab, w.f);
     }
 }
 
-// A chunk of row r: blocks c0 .. c0+nb-1, spanning 16-byte groups g0..g1 of
-// the launch's weight bytes; its first block sits at LDS byte o0 of the
-// wave's region.
+// Activation columns of item `part` of block b (the block's index in its
+// row) for activation row m.
+template <int F, class Act>
+NQ_HD void gv_a(const Act &act, uint32_t m, uint32_t b, uint32_t part, GvA &x) {
+    uint32_t c[8];
+    if constexpr (F == Q8_0 || F == Q4_0) {
+        x.d[0] = act.block(m, b, c, &x.S[0]);
+#pragma unroll
+        for (int j = 0; j < 8; j++) x.c[j] = c[j];
+    } else if constexpr (F == Q4_K || F == Q6_K) {
+        // q4_k: blocks 8b + 2g and 8b + 2g + 1; q6_k: 8b + 4h + c0 and 8b + 4h + c0 + 2
+        const uint32_t ab = F == Q4_K ? 8u * b + 2u * part : 8u * b + 4u * (part >> 1) + (part & 1u);
+        const uint32_t ab1 = F == Q4_K ? ab + 1u : ab + 2u;
+        x.d[0] = act.block(m, ab, c, &x.S[0]);
+#pragma unroll
+        for (int j = 0; j < 8; j++) x.c[j] = c[j];
+        x.d[1] = act.block(m, ab1, c, &x.S[1]);
+#pragma unroll
+        for (int j = 0; j < 8; j++) x.c[8 + j] = c[j];
+    } else {
+        uint32_t c2[2];
+        x.d[0] = act.unit(m, b * ((uint32_t)block_values(F) / 8u) + part, c2);
+        x.c[0] = c2[0];
+        x.c[1] = c2[1];
+    }
+}
+
+// The item's product with one activation row, added to acc.
+template <int F>
+NQ_HD float gv_dot(const GvW &w, const GvA &x, float acc) {
+    constexpr uint32_t LO4 = 0x0F0F0F0Fu;
+    if constexpr (F == Q8_0) {
+        int I = 0;
+#pragma unroll
+        for (int j = 0; j < 8; j++) I = dot4(w.q[j], x.c[j], I);
+        return __builtin_fmaf(w.f[0] * (float)I, x.d[0], acc);
+    } else if constexpr (F == Q4_0) {
+        int I = 0;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            I = dot4(w.q[j] & LO4, x.c[j], I);
+            I = dot4((w.q[j] >> 4) & LO4, x.c[4 + j], I);
+        }
+        return __builtin_fmaf(w.f[0] * (float)(I - 8 * x.S[0]), x.d[0], acc);
+    } else if constexpr (F == Q4_K) {
+        int I0 = 0, I1 = 0;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            I0 = dot4(w.q[j] & LO4, x.c[j], I0);
+            I1 = dot4((w.q[j] >> 4) & LO4, x.c[8 + j], I1);
+        }
+        acc = __builtin_fmaf(w.f[0] * (float)I0 - w.f[1] * (float)x.S[0], x.d[0], acc);
+        return __builtin_fmaf(w.f[2] * (float)I1 - w.f[3] * (float)x.S[1], x.d[1], acc);
+    } else if constexpr (F == Q6_K) {
+#pragma unroll
+        for (int e = 0; e < 2; e++) {
+            int I0 = 0, I1 = 0, S0 = 0;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                I0 = dot4(w.q[8 * e + j], x.c[8 * e + j], I0);
+                S0 = dot4(ONES8, x.c[8 * e + j], S0);
+                I1 = dot4(w.q[8 * e + 4 + j], x.c[8 * e + 4 + j], I1);
+            }
+            const int S1 = x.S[e] - S0;
+            acc = __builtin_fmaf(w.f[2 * e] * (float)(I0 - 32 * S0) + w.f[2 * e + 1] * (float)(I1 - 32 * S1),
+                                 x.d[e], acc);
+        }
+        return acc;
+    } else {
+        float t = w.f[0] * (float)(int8_t)x.c[0];
+#pragma unroll
+        for (int j = 1; j < 8; j++) t = __builtin_fmaf(w.f[j], (float)(int8_t)(x.c[j >> 2] >> (8 * (j & 3))), t);
+        return __builtin_fmaf(t, x.d[0], acc);
+    }
+}
+
+// A chunk: blocks c0 .. c0+nb-1 of rows r .. r+rw-1 (rw = 2 only for two
+// whole rows), spanning 16-byte groups g0..g1 of the launch's weight bytes;
+// its first block sits at LDS byte o0 of the wave's region, row r+1's at
+// o0 + row_bytes.
 struct GvChunk {
-    uint32_t r, c0, nb, g0, g1, o0;
+    uint32_t r, rw, c0, nb, g0, g1, o0;
 };
 
 NQ_HD GvChunk gv_chunk(const GvArgs &a, uint32_t r, uint32_t c0) {
     const uint32_t S = a.row_bytes / a.nbr;
     GvChunk c;
     c.r = r;
+    c.rw = a.rw == 2u && r + 1u < a.rows ? 2u : 1u;
     c.c0 = c0;
     c.nb = a.nbr - c0 < a.cb ? a.nbr - c0 : a.cb;
-    const uint32_t p0 = a.wmis + r * a.row_bytes + c0 * S, p1 = p0 + c.nb * S - 1u;
+    const uint32_t p0 = a.wmis + r * a.row_bytes + c0 * S;
+    const uint32_t p1 = p0 + (c.rw - 1u) * a.row_bytes + c.nb * S - 1u;
     c.g0 = p0 >> 4;
     c.g1 = p1 >> 4;
     c.o0 = p0 & 15u;
@@ -438,26 +484,26 @@ NQ_HD GvChunk gv_chunk(const GvArgs &a, uint32_t r, uint32_t c0) {
 }
 
 // The chunk after (r, c0) in a wave's sequence: the row's next chunk, else
-// the first chunk of row r + step.
+// the first chunk of the wave's next row group (step groups of rw rows on).
 NQ_HD void gv_advance(const GvArgs &a, uint32_t step, uint32_t *r, uint32_t *c0) {
     *c0 += a.cb;
     if (*c0 >= a.nbr) {
         *c0 = 0u;
-        *r += step;
+        *r += step * a.rw;
     }
 }
 
-// Chunk staging, lane part, in two steps: the lane's GV_NL 16-byte loads
+// Chunk staging, lane part, in two steps: the lane's NL 16-byte loads
 // of groups g0 + lane + 64k (clamped to g1: lanes past the chunk repeat its
 // last group, same address and value) into registers, and later their
 // stores into the wave's LDS region (group g at dword 4 (g - g0)).  A group
 // that passes the last weight dword (wlast) is loaded as the 16 bytes that
 // end there and shifted into place, zero-filled; every load is in bounds
 // (a launch holds at least 16 bytes) and none depends on a branch.
-template <class Src>
-NQ_HD void gv_issue(const Src &src, uint32_t wlast, const GvChunk &c, uint32_t lane, uint32_t (&v)[GV_NL][4]) {
+template <int NL, class Src>
+NQ_HD void gv_issue(const Src &src, uint32_t wlast, const GvChunk &c, uint32_t lane, uint32_t (&v)[NL][4]) {
 #pragma unroll
-    for (int k = 0; k < GV_NL; k++) {
+    for (int k = 0; k < NL; k++) {
         const uint32_t g0 = c.g0 + lane + 64u * (uint32_t)k;
         const uint32_t i = 4u * (g0 < c.g1 ? g0 : c.g1);
         src.load_stream4(i + 3u <= wlast ? i : wlast - 3u, v[k]);
@@ -467,10 +513,11 @@ NQ_HD void gv_issue(const Src &src, uint32_t wlast, const GvChunk &c, uint32_t l
 // The stores of gv_issue's loads (the shift of a group that passed wlast is
 // applied here, once the data has arrived, so the loads stay in flight
 // until then).
-NQ_HD void gv_put(const GvChunk &c, uint32_t wlast, uint32_t lane, const uint32_t (&v)[GV_NL][4], uint32_t *lds) {
+template <int NL>
+NQ_HD void gv_put(const GvChunk &c, uint32_t wlast, uint32_t lane, const uint32_t (&v)[NL][4], uint32_t *lds) {
     const bool whole = 4u * c.g1 + 3u <= wlast;  // the same for the whole wave: only a launch's last group passes
 #pragma unroll
-    for (int k = 0; k < GV_NL; k++) {
+    for (int k = 0; k < NL; k++) {
         const uint32_t g0 = c.g0 + lane + 64u * (uint32_t)k, g = g0 < c.g1 ? g0 : c.g1;
         uint32_t *d = lds + 4u * (g - c.g0);
         if (whole) {
@@ -490,15 +537,29 @@ NQ_HD void gv_put(const GvChunk &c, uint32_t wlast, uint32_t lane, const uint32_
     }
 }
 
-// A lane's items of a staged chunk: items lane, lane + 64, ... in block order.
-template <int F, int MT, class Act>
-NQ_HD void gv_chunk_items(const LdsSrc &s, const GvChunk &c, uint32_t lane, uint32_t nm, const Act &act,
-                          const Tab &tab, float (&acc)[MT]) {
+// A lane's positions of a staged chunk (items lane, lane + 64, ... of one
+// row's blocks c0..c0+nb-1): per position the weights of each of the chunk's
+// rows, then per activation row its columns, used by every row.
+template <int F, int MT, int RW, class Act>
+NQ_HD void gv_chunk_items(const LdsSrc &s, const GvChunk &c, uint32_t lane, uint32_t nm, uint32_t row_bytes,
+                          const Act &act, const Tab &tab, float (&acc)[RW][MT]) {
     constexpr uint32_t IPB = GvItem<F>::IPB, S = (uint32_t)block_bytes(F);
     const uint32_t n = c.nb * IPB;
     for (uint32_t i = lane; i < n; i += 64u) {
-        const uint32_t bl = i / IPB;
-        gv_item<F, MT>(s, c.o0 + bl * S, c.c0 + bl, i - bl * IPB, nm, act, tab, acc);
+        const uint32_t bl = i / IPB, part = i - bl * IPB;
+        GvW w[RW];
+#pragma unroll
+        for (int rr = 0; rr < RW; rr++)
+            if ((uint32_t)rr < c.rw) gv_w<F>(s, c.o0 + (uint32_t)rr * row_bytes + bl * S, part, tab, w[rr]);
+#pragma unroll
+        for (int m = 0; m < MT; m++) {
+            if (m >= (int)nm) continue;
+            GvA x;
+            gv_a<F>(act, (uint32_t)m, c.c0 + bl, part, x);
+#pragma unroll
+            for (int rr = 0; rr < RW; rr++)
+                if ((uint32_t)rr < c.rw) acc[rr][m] = gv_dot<F>(w[rr], x, acc[rr][m]);
+        }
     }
 }
 
@@ -516,7 +577,7 @@ NQ_HD void gv_fill_tables(uint64_t *t8, uint32_t *t4, uint32_t tid) {
     }
 }
 
-template <int F, int MT, bool ALDS>
+template <int F, int MT, bool ALDS, int RW>
 __global__ __launch_bounds__(WG) void k_gemv(GvArgs a) {
     using TS = TabSpec<F>;
     __shared__ uint64_t t8[TS::n8 > 0 ? TS::n8 : 1];
@@ -527,41 +588,69 @@ __global__ __launch_bounds__(WG) void k_gemv(GvArgs a) {
     if constexpr (ALDS || TS::n8 + TS::n4 > 0) __syncthreads();
     const Tab tab{t8, t4, nullptr, nullptr, 0xFFFFFFFFu, 1u};
     const GvAct<ALDS> act{a.xq, gv_lds, a.K, a.kb, a.xrow, a.M};
+    constexpr int NL = gv_nl<RW>();
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const uint32_t step = gridDim.x * GV_WAVES;
-    uint32_t *lds = gv_lds + (ALDS ? gv_act_dw(a) : 0u) + wave * GV_WAVE_DW;
+    uint32_t *lds = gv_lds + (ALDS ? gv_act_dw(a) : 0u) + wave * gv_wave_dw<RW>();
     const DevSrc src{a.wbase, a.wlast};
-    uint32_t r = blockIdx.x * GV_WAVES + wave, c0 = 0u;
+    uint32_t r = (blockIdx.x * GV_WAVES + wave) * a.rw, c0 = 0u;
     if (r >= a.rows) return;  // no workgroup barrier follows
     GvChunk cur = gv_chunk(a, r, c0);
-    uint32_t v[GV_NL][4];
-    gv_issue(src, a.wlast, cur, lane, v);
-    float acc[MT];
+    uint32_t v[NL][4];
+    gv_issue<NL>(src, a.wlast, cur, lane, v);
+    float acc[RW][MT], done[RW][MT];
 #pragma unroll
-    for (int m = 0; m < MT; m++) acc[m] = 0.0f;
+    for (int rr = 0; rr < RW; rr++)
+#pragma unroll
+        for (int m = 0; m < MT; m++) acc[rr][m] = 0.0f;
+    uint32_t done_r = 0xFFFFFFFFu, done_rw = 0u;  // finished rows whose sums are not stored yet
     for (;;) {
         wave_lds_sync();  // the previous chunk's readers are done
-        gv_put(cur, a.wlast, lane, v, lds);
+        gv_put<NL>(cur, a.wlast, lane, v, lds);
         wave_lds_sync();
+        // Finished rows are stored here, before the next chunk's loads: the
+        // memory counter is in order, so stores issued after them would
+        // hold up the wait for them.
+        if (done_r != 0xFFFFFFFFu) {
+#pragma unroll
+            for (int rr = 0; rr < RW; rr++)
+#pragma unroll
+                for (int m = 0; m < MT; m++)
+                    if (lane == 63u && (uint32_t)rr < done_rw && m < (int)a.M)
+                        a.y[(uint64_t)m * a.ldy + done_r + (uint32_t)rr] = done[rr][m];
+            done_r = 0xFFFFFFFFu;
+        }
         gv_advance(a, step, &r, &c0);
         const bool more = r < a.rows;
         GvChunk nxt = cur;
         if (more) {
             nxt = gv_chunk(a, r, c0);
-            gv_issue(src, a.wlast, nxt, lane, v);  // in flight while this chunk is computed
+            gv_issue<NL>(src, a.wlast, nxt, lane, v);  // in flight while this chunk is computed
         }
-        gv_chunk_items<F, MT>(LdsSrc{lds, 4u * (cur.g1 - cur.g0) + 3u}, cur, lane, a.M, act, tab, acc);
+        gv_chunk_items<F, MT, RW>(LdsSrc{lds, 4u * (cur.g1 - cur.g0) + 3u}, cur, lane, a.M, a.row_bytes, act, tab,
+                              acc);
         if (cur.c0 + cur.nb >= a.nbr) {
 #pragma unroll
-            for (int m = 0; m < MT; m++) {
-                const float sum = wave_sum63(acc[m]);
-                if (lane == 63u && m < (int)a.M) a.y[(uint64_t)m * a.ldy + cur.r] = sum;
-                acc[m] = 0.0f;
-            }
+            for (int rr = 0; rr < RW; rr++)
+#pragma unroll
+                for (int m = 0; m < MT; m++) {
+                    done[rr][m] = (uint32_t)rr < cur.rw ? wave_sum63(acc[rr][m]) : 0.0f;
+                    acc[rr][m] = 0.0f;
+                }
+            done_r = cur.r;
+            done_rw = cur.rw;
         }
         if (!more) break;
         cur = nxt;
+    }
+    if (done_r != 0xFFFFFFFFu) {
+#pragma unroll
+        for (int rr = 0; rr < RW; rr++)
+#pragma unroll
+            for (int m = 0; m < MT; m++)
+                if (lane == 63u && (uint32_t)rr < done_rw && m < (int)a.M)
+                    a.y[(uint64_t)m * a.ldy + done_r + (uint32_t)rr] = done[rr][m];
     }
 }
 
@@ -580,6 +669,9 @@ struct Q81Launch {
     uint32_t *blocks;
     uint32_t *status;
 };
+
+// Chunks hold row pairs when two whole rows fit one pair chunk.
+inline bool gv_pairs(uint64_t row_bytes) { return 2 * row_bytes <= gv_chunk_bytes<2>(); }
 
 // Activation staged in LDS when its codes, scales and sums fit the budget.
 inline bool gv_act_in_lds(uint64_t M, uint64_t K) { return M * (K + K / 32 * 8) <= GV_ACT_LDS_MAX; }
@@ -603,20 +695,25 @@ GvArgs gv_args(const GvLaunch &L, uint64_t r0, uint64_t rows) {
     a.ldy = (uint32_t)L.N;
     a.M = (uint32_t)L.M;
     a.nbr = (uint32_t)nbr;
-    const uint64_t cb = GV_CHUNK_BYTES / S;  // every block is at most 292 bytes
-    a.cb = (uint32_t)(cb < nbr ? cb : nbr);
+    // row pairs when two rows fit a pair chunk; else chunks of at most the
+    // single-row chunk bytes (every block is at most 292 bytes), the row's
+    // chunks as even as whole blocks allow
+    a.rw = gv_pairs(row_bytes) ? 2u : 1u;
+    const uint64_t cmax = (a.rw == 2u ? gv_chunk_bytes<2>() : gv_chunk_bytes<1>()) / S;
+    const uint64_t nch = (nbr + cmax - 1) / cmax;
+    a.cb = (uint32_t)((nbr + nch - 1) / nch);
     return a;
 }
 
 // LDS bytes of a launch: the staged activation (when in LDS) and the waves' regions.
 inline uint32_t gv_lds_bytes(const GvArgs &a, bool alds) {
-    return 4u * ((alds ? gv_act_dw(a) : 0u) + GV_WAVES * GV_WAVE_DW);
+    return 4u * ((alds ? gv_act_dw(a) : 0u) + GV_WAVES * (a.rw == 2u ? gv_wave_dw<2>() : gv_wave_dw<1>()));
 }
 
 // Workgroups of a launch: as many as the device keeps resident (the waves
-// persist), and no more than the rows need.
-inline uint32_t gv_grid(uint64_t rows, uint32_t resident) {
-    const uint64_t need = (rows + GV_WAVES - 1) / GV_WAVES;
+// persist), and no more than the row groups (rw rows each) need.
+inline uint32_t gv_grid(const GvArgs &a, uint32_t resident) {
+    const uint64_t groups = (a.rows + a.rw - 1) / a.rw, need = (groups + GV_WAVES - 1) / GV_WAVES;
     return (uint32_t)(need < resident ? need : resident);
 }
 
@@ -626,24 +723,32 @@ uint64_t gv_max_rows(const GvLaunch &L) {
     return 0xFFFFFFF0ull / (L.K / (uint64_t)block_values(F) * (uint64_t)block_bytes(F));
 }
 
-template <int F, int MT, bool ALDS>
-int launch_gemv_lds(const GvLaunch &L, hipStream_t stream) {
+template <int F, int MT, bool ALDS, int RW>
+int launch_gemv_rw(const GvLaunch &L, hipStream_t stream) {
     const uint64_t max_rows = gv_max_rows<F>(L);
     for (uint64_t r0 = 0; r0 < L.N;) {
         const uint64_t rows = L.N - r0 < max_rows ? L.N - r0 : max_rows;
         const GvArgs a = gv_args<F>(L, r0, rows);
         const uint32_t lds = gv_lds_bytes(a, ALDS);
         int per_cu = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)k_gemv<F, MT, ALDS>, WG, lds) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)k_gemv<F, MT, ALDS, RW>, WG, lds) !=
                 hipSuccess ||
             per_cu < 1)
             per_cu = 1;
-        const uint32_t grid = gv_grid(rows, (uint32_t)per_cu * L.cus);
-        hipLaunchKernelGGL((k_gemv<F, MT, ALDS>), dim3(grid), dim3(WG), lds, stream, a);
+        const uint32_t grid = gv_grid(a, (uint32_t)per_cu * L.cus);
+        hipLaunchKernelGGL((k_gemv<F, MT, ALDS, RW>), dim3(grid), dim3(WG), lds, stream, a);
         if (hipGetLastError() != hipSuccess) return 9;  // NQ_ERR_HIP
         r0 += rows;
     }
     return 0;
+}
+
+// Row pairs only where two rows fit one chunk (the rows-per-chunk count
+// fixes the registers the items hold).
+template <int F, int MT, bool ALDS>
+int launch_gemv_lds(const GvLaunch &L, hipStream_t stream) {
+    const uint64_t row_bytes = L.K / (uint64_t)block_values(F) * (uint64_t)block_bytes(F);
+    return gv_pairs(row_bytes) ? launch_gemv_rw<F, MT, ALDS, 2>(L, stream) : launch_gemv_rw<F, MT, ALDS, 1>(L, stream);
 }
 
 template <int F, int MT>

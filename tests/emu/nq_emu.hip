@@ -215,7 +215,7 @@ float dpp_sum63(float (&v)[64]) {
 // poisoned LDS region, whose bytes are then compared with the payload, the
 // lanes' items, and at each row's end the wave's butterfly sum in the
 // kernel's order.
-template <int F, int MT, bool ALDS>
+template <int F, int MT, bool ALDS, int RW>
 long run_gemv_lds(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y,
                   uint32_t resident, uint64_t max_rows, char *err, int errlen) {
     using namespace nq;
@@ -230,54 +230,66 @@ long run_gemv_lds(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, u
     for (uint64_t r0 = 0; r0 < N;) {
         const uint64_t rows = N - r0 < lim ? N - r0 : lim;
         const GvArgs a = gv_args<F>(L, r0, rows);
+        if (a.rw != (uint32_t)RW) {
+            snprintf(err, errlen, "rows per chunk %u, kernel built for %d", a.rw, RW);
+            return 1;
+        }
         const uint32_t lds_bytes = gv_lds_bytes(a, ALDS);
         if (lds_bytes > 65536u) {
             snprintf(err, errlen, "LDS request %u bytes", lds_bytes);
             return 1;
         }
-        const uint32_t grid = gv_grid(rows, resident);
+        const uint32_t grid = gv_grid(a, resident);
         Check chk{(uintptr_t)(w + r0 * row_bytes), (uintptr_t)(w + (r0 + rows) * row_bytes), 0, {0}};
         const HostSrc src{a.wbase, a.wlast, &chk};
         std::vector<uint32_t> act_lds(ALDS ? gv_act_dw(a) : 1u, 0xA5A5A5A5u);
         if (ALDS)
             for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) gv_stage_act(a, act_lds.data(), tid, WG);
         const GvAct<ALDS> act{a.xq, act_lds.data(), a.K, a.kb, a.xrow, a.M};
-        std::vector<uint32_t> lds(GV_WAVE_DW);
+        std::vector<uint32_t> lds(gv_wave_dw<RW>());
+        constexpr int NL = gv_nl<RW>();
         const uint32_t step = grid * GV_WAVES;
         for (uint32_t b = 0; b < grid; b++)
             for (uint32_t wave = 0; wave < GV_WAVES; wave++) {
-                uint32_t r = b * GV_WAVES + wave, c0 = 0;
+                uint32_t r = (b * GV_WAVES + wave) * a.rw, c0 = 0;
                 if (r >= a.rows) continue;
-                static float acc[64][MT];
+                static float acc[64][RW][MT];
                 for (uint32_t lane = 0; lane < 64u; lane++)
-                    for (int m = 0; m < MT; m++) acc[lane][m] = 0.0f;
+                    for (int rr = 0; rr < RW; rr++)
+                        for (int m = 0; m < MT; m++) acc[lane][rr][m] = 0.0f;
                 GvChunk cur = gv_chunk(a, r, c0);
                 for (;;) {
-                    if (cur.g1 - cur.g0 + 1u > 64u * GV_NL) {
+                    if (cur.g1 - cur.g0 + 1u > 64u * NL) {
                         snprintf(err, errlen, "chunk of %u groups past the wave's loads", cur.g1 - cur.g0 + 1u);
                         return 1;
                     }
                     std::fill(lds.begin(), lds.end(), 0xA5A5A5A5u);
                     for (uint32_t lane = 0; lane < 64u; lane++) {
-                        uint32_t v[GV_NL][4];
-                        gv_issue(src, a.wlast, cur, lane, v);
-                        gv_put(cur, a.wlast, lane, v, lds.data());
+                        uint32_t v[NL][4];
+                        gv_issue<NL>(src, a.wlast, cur, lane, v);
+                        gv_put<NL>(cur, a.wlast, lane, v, lds.data());
                     }
-                    const uint8_t *cb = (const uint8_t *)lds.data() + cur.o0;
-                    const uint8_t *pb = (const uint8_t *)a.wbase + a.wmis + (uint64_t)cur.r * a.row_bytes +
-                                        (uint64_t)cur.c0 * block_bytes(F);
-                    if (memcmp(cb, pb, (size_t)cur.nb * block_bytes(F)) != 0 && chk.errors++ == 0)
-                        snprintf(chk.msg, sizeof chk.msg, "staged chunk of row %u differs from the payload", cur.r);
+                    for (uint32_t rr = 0; rr < cur.rw; rr++) {
+                        const uint8_t *cb = (const uint8_t *)lds.data() + cur.o0 + rr * a.row_bytes;
+                        const uint8_t *pb = (const uint8_t *)a.wbase + a.wmis + (uint64_t)(cur.r + rr) * a.row_bytes +
+                                            (uint64_t)cur.c0 * block_bytes(F);
+                        if (memcmp(cb, pb, (size_t)cur.nb * block_bytes(F)) != 0 && chk.errors++ == 0)
+                            snprintf(chk.msg, sizeof chk.msg, "staged chunk of row %u differs from the payload",
+                                     cur.r + rr);
+                    }
                     const LdsSrc s{lds.data(), 4u * (cur.g1 - cur.g0) + 3u};
                     for (uint32_t lane = 0; lane < 64u; lane++)
-                        gv_chunk_items<F, MT>(s, cur, lane, a.M, act, tab, acc[lane]);
+                        gv_chunk_items<F, MT, RW>(s, cur, lane, a.M, a.row_bytes, act, tab, acc[lane]);
                     if (cur.c0 + cur.nb >= a.nbr) {
-                        for (int m = 0; m < MT; m++) {
-                            float v[64];
-                            for (int l = 0; l < 64; l++) v[l] = acc[l][m];
-                            if (m < (int)a.M) a.y[(uint64_t)m * a.ldy + cur.r] = dpp_sum63(v);
-                            for (int l = 0; l < 64; l++) acc[l][m] = 0.0f;
-                        }
+                        for (uint32_t rr = 0; rr < cur.rw; rr++)
+                            for (int m = 0; m < MT; m++) {
+                                float v[64];
+                                for (int l = 0; l < 64; l++) v[l] = acc[l][rr][m];
+                                if (m < (int)a.M) a.y[(uint64_t)m * a.ldy + cur.r + rr] = dpp_sum63(v);
+                            }
+                        for (uint32_t lane = 0; lane < 64u; lane++)
+                            for (int rr = 0; rr < RW; rr++)
+                                for (int m = 0; m < MT; m++) acc[lane][rr][m] = 0.0f;
                     }
                     gv_advance(a, step, &r, &c0);
                     if (r >= a.rows) break;
@@ -293,11 +305,19 @@ long run_gemv_lds(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, u
     return errors;
 }
 
+template <int F, int MT, bool ALDS>
+long run_gemv_alds(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y,
+                   uint32_t resident, uint64_t max_rows, char *err, int errlen) {
+    const uint64_t row_bytes = K / (uint64_t)nq::block_values(F) * (uint64_t)nq::block_bytes(F);
+    return nq::gv_pairs(row_bytes) ? run_gemv_lds<F, MT, ALDS, 2>(w, N, K, xq, M, y, resident, max_rows, err, errlen)
+                                   : run_gemv_lds<F, MT, ALDS, 1>(w, N, K, xq, M, y, resident, max_rows, err, errlen);
+}
+
 template <int F, int MT>
 long run_gemv(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y, uint32_t resident,
               uint64_t max_rows, char *err, int errlen) {
-    return nq::gv_act_in_lds(M, K) ? run_gemv_lds<F, MT, true>(w, N, K, xq, M, y, resident, max_rows, err, errlen)
-                                   : run_gemv_lds<F, MT, false>(w, N, K, xq, M, y, resident, max_rows, err, errlen);
+    return nq::gv_act_in_lds(M, K) ? run_gemv_alds<F, MT, true>(w, N, K, xq, M, y, resident, max_rows, err, errlen)
+                                   : run_gemv_alds<F, MT, false>(w, N, K, xq, M, y, resident, max_rows, err, errlen);
 }
 
 template <int F>
