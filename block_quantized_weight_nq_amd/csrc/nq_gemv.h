@@ -290,10 +290,21 @@ struct GvAct {
 // a chunk) and the product (gv_dot).
 template <int F>
 struct GvItem {
-    static constexpr bool INT = F == Q4_0 || F == Q8_0 || F == Q4_K || F == Q6_K;
+    // 32-value blocks (one item each)
+    static constexpr bool B32 = F == Q4_0 || F == Q4_1 || F == Q5_0 || F == Q5_1 || F == Q8_0 || F == Q8_1 ||
+                                F == IQ4_NL || F == MXFP4;
+    // 256-value blocks in 32-value items
+    static constexpr bool I32 = F == IQ4_XS || F == Q8_K || F == TQ2_0;
+    static constexpr bool INT = B32 || I32 || F == Q4_K || F == Q5_K || F == Q6_K || F == NVFP4_GGUF;
     // items per block
-    static constexpr uint32_t IPB = F == Q4_K || F == Q6_K ? 4u : INT ? 1u : (uint32_t)block_values(F) / 8u;
+    static constexpr uint32_t IPB = B32 ? 1u : I32 ? 8u : (F == Q4_K || F == Q5_K || F == Q6_K) ? 4u
+                                  : F == NVFP4_GGUF ? 2u : (uint32_t)block_values(F) / 8u;
 };
+
+// 5-bit codes: byte k of the result is bit 4 of 16 * (bit k of b), k < 4
+// (b's four low bits spread one per byte by a multiply that keeps the four
+// shifted copies apart).
+NQ_HD uint32_t spread4(uint32_t b) { return ((b & 15u) * 0x00204081u & 0x01010101u) << 4; }
 
 // Decoded weights of one item (the fields a format uses).
 struct GvW {
@@ -339,6 +350,135 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
         window<4>(s, bo + 2u, q);
 #pragma unroll
         for (int j = 0; j < 4; j++) w.q[j] = q[j];
+    } else if constexpr (F == Q8_1) {
+        // d at 0, the sum at 2 (not used), 32 signed codes at 4: w = d * q
+        w.f[0] = f16(u16_at(s, bo));
+        uint32_t q[8];
+        window<8>(s, bo + 4u, q);
+#pragma unroll
+        for (int j = 0; j < 8; j++) w.q[j] = q[j];
+    } else if constexpr (F == Q8_K) {
+        // binary32 d at 0, 256 signed codes at 4 (part p: codes 32p .. 32p+31): w = RN32(d * q)
+        uint32_t h[1], q[8];
+        window<1>(s, bo, h);
+        window<8>(s, bo + 4u + 32u * part, q);
+        w.f[0] = bits_f32(h[0]);
+#pragma unroll
+        for (int j = 0; j < 8; j++) w.q[j] = q[j];
+    } else if constexpr (F == Q4_1 || F == IQ4_NL || F == MXFP4) {
+        // nibbles (value j < 16 the low nibble of byte j, j >= 16 the high
+        // nibble of byte j - 16) of 16 bytes; q4_1: d at 0, m at 2, bytes at
+        // 4, w = d * v + m; iq4_nl: d at 0, bytes at 2, w = d * IQ4[v];
+        // mxfp4: E8M0 byte at 0, bytes at 1, w = half-scale * V[v] (the
+        // doubled E2M1 table)
+        constexpr uint32_t LO4 = 0x0F0F0F0Fu;
+        uint32_t q[4];
+        if constexpr (F == Q4_1) {
+            w.f[0] = f16(u16_at(s, bo));
+            w.f[1] = f16(u16_at(s, bo + 2u));
+            window<4>(s, bo + 4u, q);
+        } else if constexpr (F == IQ4_NL) {
+            w.f[0] = f16(u16_at(s, bo));
+            window<4>(s, bo + 2u, q);
+        } else {
+            const uint32_t e = u8_at(s, bo);
+            w.f[0] = bits_f32(e < 2u ? (0x00200000u << e) : ((e - 1u) << 23));
+            window<4>(s, bo + 1u, q);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const uint32_t lo = q[j] & LO4, hi = (q[j] >> 4) & LO4;
+            if constexpr (F == Q4_1) {
+                w.q[j] = lo;
+                w.q[4 + j] = hi;
+            } else if constexpr (F == IQ4_NL) {
+                w.q[j] = lut16(IQ4T0, IQ4T1, IQ4T2, IQ4T3, lo);
+                w.q[4 + j] = lut16(IQ4T0, IQ4T1, IQ4T2, IQ4T3, hi);
+            } else {
+                w.q[j] = lut16(FP4T0, FP4T1, FP4T2, FP4T3, lo);
+                w.q[4 + j] = lut16(FP4T0, FP4T1, FP4T2, FP4T3, hi);
+            }
+        }
+    } else if constexpr (F == Q5_0 || F == Q5_1) {
+        // value j = nibble j (as q4_0) + 16 * bit j of the 32-bit high word;
+        // q5_0: d at 0, high at 2, bytes at 6, w = d * (v - 16); q5_1: d at 0,
+        // m at 2, high at 4, bytes at 8, w = d * v + m
+        constexpr uint32_t LO4 = 0x0F0F0F0Fu;
+        const uint32_t ho = F == Q5_0 ? 2u : 4u;
+        uint32_t hw[1], q[4];
+        window<1>(s, bo + ho, hw);
+        window<4>(s, bo + ho + 4u, q);
+        w.f[0] = f16(u16_at(s, bo));
+        if constexpr (F == Q5_1) w.f[1] = f16(u16_at(s, bo + 2u));
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            w.q[j] = (q[j] & LO4) | spread4(hw[0] >> (4 * j));
+            w.q[4 + j] = ((q[j] >> 4) & LO4) | spread4(hw[0] >> (16 + 4 * j));
+        }
+    } else if constexpr (F == IQ4_XS) {
+        // part k: values 32k .. 32k+31, nibbles (as q4_0) of bytes 8 + 16k ..;
+        // w = RN32(d * s_k) * IQ4[v], s_k = scale nibble k + 16 * high bits 2k,2k+1 - 32
+        constexpr uint32_t LO4 = 0x0F0F0F0Fu;
+        uint32_t hdr[2], q[4];
+        window<2>(s, bo, hdr);
+        window<4>(s, bo + 8u + 16u * part, q);
+        const float d = f16(hdr[0] & 0xFFFFu);
+        const uint32_t high = hdr[0] >> 16;
+        const uint32_t lo = (bytek(hdr[1], part >> 1) >> (4u * (part & 1u))) & 15u;
+        const uint32_t sk = lo + 16u * ((high >> (2u * part)) & 3u);
+        w.f[0] = M(d, (float)((int)sk - 32));
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            w.q[j] = lut16(IQ4T0, IQ4T1, IQ4T2, IQ4T3, q[j] & LO4);
+            w.q[4 + j] = lut16(IQ4T0, IQ4T1, IQ4T2, IQ4T3, (q[j] >> 4) & LO4);
+        }
+    } else if constexpr (F == TQ2_0) {
+        // part c: values 32c + i, bits 2(c mod 4) of byte 32(c / 4) + i; d at
+        // 64; w = d * (v - 1)
+        uint32_t q[8];
+        window<8>(s, bo + 32u * (part >> 2), q);
+        w.f[0] = f16(u16_at(s, bo + 64u));
+#pragma unroll
+        for (int j = 0; j < 8; j++) w.q[j] = (q[j] >> (2u * (part & 3u))) & 0x03030303u;
+    } else if constexpr (F == NVFP4_GGUF) {
+        // part p: groups 2p and 2p+1 (16 values each); group g's E4M3 scale
+        // byte at g, its codes the low then the high nibbles of bytes
+        // 4 + 8g .. 4 + 8g + 7; w = half-scale(g) * V[v]
+        constexpr uint32_t LO4 = 0x0F0F0F0Fu;
+        uint32_t q[4];
+        window<4>(s, bo + 4u + 16u * part, q);
+        const uint32_t sb = u16_at(s, bo + 2u * part);
+        w.f[0] = nvfp4_half_scale(sb & 0xFFu);
+        w.f[1] = nvfp4_half_scale(sb >> 8);
+#pragma unroll
+        for (int e = 0; e < 2; e++) {
+            w.q[4 * e + 0] = lut16(FP4T0, FP4T1, FP4T2, FP4T3, q[2 * e] & LO4);
+            w.q[4 * e + 1] = lut16(FP4T0, FP4T1, FP4T2, FP4T3, q[2 * e + 1] & LO4);
+            w.q[4 * e + 2] = lut16(FP4T0, FP4T1, FP4T2, FP4T3, (q[2 * e] >> 4) & LO4);
+            w.q[4 * e + 3] = lut16(FP4T0, FP4T1, FP4T2, FP4T3, (q[2 * e + 1] >> 4) & LO4);
+        }
+    } else if constexpr (F == Q5_K) {
+        // part g as q4_k, codes from bytes 48 + 32g .. plus 16 * bit 2g (low
+        // half) or 2g+1 (high half) of bytes 16 .. 47
+        constexpr uint32_t LO4 = 0x0F0F0F0Fu;
+        uint32_t h[4], q[8], qh[8];
+        window<4>(s, bo, h);
+        window<8>(s, bo + 48u + 32u * part, q);
+        window<8>(s, bo + 16u, qh);
+        const float d = f16(h[0] & 0xFFFFu), dmin = f16(h[0] >> 16);
+        const uint32_t hs[3] = {h[1], h[2], h[3]};
+        uint32_t sc0, m0, sc1, m1;
+        kq_scale_min(hs, 2u * part, &sc0, &m0);
+        kq_scale_min(hs, 2u * part + 1u, &sc1, &m1);
+        w.f[0] = M(d, (float)sc0);
+        w.f[1] = M(dmin, (float)m0);
+        w.f[2] = M(d, (float)sc1);
+        w.f[3] = M(dmin, (float)m1);
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            w.q[j] = (q[j] & LO4) | (((qh[j] >> (2u * part)) & 0x01010101u) << 4);
+            w.q[8 + j] = ((q[j] >> 4) & LO4) | (((qh[j] >> (2u * part + 1u)) & 0x01010101u) << 4);
+        }
     } else if constexpr (F == Q4_K) {
         // part g: values 64g .. 64g+63, the low (sub-block 2g) and high
         // (sub-block 2g+1) nibbles of bytes 16 + 32g .. 16 + 32g + 31;
@@ -389,14 +529,17 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
 template <int F, class Act>
 NQ_HD void gv_a(const Act &act, uint32_t m, uint32_t b, uint32_t part, GvA &x) {
     uint32_t c[8];
-    if constexpr (F == Q8_0 || F == Q4_0) {
-        x.d[0] = act.block(m, b, c, &x.S[0]);
+    if constexpr (GvItem<F>::B32 || GvItem<F>::I32 || F == NVFP4_GGUF) {
+        // the item's 32 values are activation block b (32-value blocks),
+        // 8b + part (32-value items of 256-value blocks) or 2b + part (nvfp4)
+        const uint32_t ab = GvItem<F>::B32 ? b : GvItem<F>::I32 ? 8u * b + part : 2u * b + part;
+        x.d[0] = act.block(m, ab, c, &x.S[0]);
 #pragma unroll
         for (int j = 0; j < 8; j++) x.c[j] = c[j];
-    } else if constexpr (F == Q4_K || F == Q6_K) {
-        // q4_k: blocks 8b + 2g and 8b + 2g + 1; q6_k: 8b + 4h + c0 and 8b + 4h + c0 + 2
-        const uint32_t ab = F == Q4_K ? 8u * b + 2u * part : 8u * b + 4u * (part >> 1) + (part & 1u);
-        const uint32_t ab1 = F == Q4_K ? ab + 1u : ab + 2u;
+    } else if constexpr (F == Q4_K || F == Q5_K || F == Q6_K) {
+        // q4_k / q5_k: blocks 8b + 2g and 8b + 2g + 1; q6_k: 8b + 4h + c0 and 8b + 4h + c0 + 2
+        const uint32_t ab = F != Q6_K ? 8u * b + 2u * part : 8u * b + 4u * (part >> 1) + (part & 1u);
+        const uint32_t ab1 = F != Q6_K ? ab + 1u : ab + 2u;
         x.d[0] = act.block(m, ab, c, &x.S[0]);
 #pragma unroll
         for (int j = 0; j < 8; j++) x.c[j] = c[j];
@@ -415,11 +558,34 @@ NQ_HD void gv_a(const Act &act, uint32_t m, uint32_t b, uint32_t part, GvA &x) {
 template <int F>
 NQ_HD float gv_dot(const GvW &w, const GvA &x, float acc) {
     constexpr uint32_t LO4 = 0x0F0F0F0Fu;
-    if constexpr (F == Q8_0) {
+    if constexpr (F == Q8_0 || F == Q8_1 || F == Q8_K || F == IQ4_NL || F == MXFP4 || F == IQ4_XS) {
+        // w = scale * (8-bit integer): the scale times the exact dot product
         int I = 0;
 #pragma unroll
         for (int j = 0; j < 8; j++) I = dot4(w.q[j], x.c[j], I);
         return __builtin_fmaf(w.f[0] * (float)I, x.d[0], acc);
+    } else if constexpr (F == Q4_1 || F == Q5_1) {
+        // w = d * v + m: d times the dot product plus m times the codes' sum
+        int I = 0;
+#pragma unroll
+        for (int j = 0; j < 8; j++) I = dot4(w.q[j], x.c[j], I);
+        return __builtin_fmaf(w.f[0] * (float)I + w.f[1] * (float)x.S[0], x.d[0], acc);
+    } else if constexpr (F == Q5_0 || F == TQ2_0) {
+        // w = d * (v - o), o = 16 or 1: exact integer offset through the codes' sum
+        constexpr int O = F == Q5_0 ? 16 : 1;
+        int I = 0;
+#pragma unroll
+        for (int j = 0; j < 8; j++) I = dot4(w.q[j], x.c[j], I);
+        return __builtin_fmaf(w.f[0] * (float)(I - O * x.S[0]), x.d[0], acc);
+    } else if constexpr (F == NVFP4_GGUF) {
+        // two 16-value groups with their own scales in one activation block
+        int I0 = 0, I1 = 0;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            I0 = dot4(w.q[j], x.c[j], I0);
+            I1 = dot4(w.q[4 + j], x.c[4 + j], I1);
+        }
+        return __builtin_fmaf(w.f[0] * (float)I0 + w.f[1] * (float)I1, x.d[0], acc);
     } else if constexpr (F == Q4_0) {
         int I = 0;
 #pragma unroll
@@ -428,12 +594,17 @@ NQ_HD float gv_dot(const GvW &w, const GvA &x, float acc) {
             I = dot4((w.q[j] >> 4) & LO4, x.c[4 + j], I);
         }
         return __builtin_fmaf(w.f[0] * (float)(I - 8 * x.S[0]), x.d[0], acc);
-    } else if constexpr (F == Q4_K) {
+    } else if constexpr (F == Q4_K || F == Q5_K) {
         int I0 = 0, I1 = 0;
 #pragma unroll
         for (int j = 0; j < 8; j++) {
-            I0 = dot4(w.q[j] & LO4, x.c[j], I0);
-            I1 = dot4((w.q[j] >> 4) & LO4, x.c[8 + j], I1);
+            if constexpr (F == Q4_K) {
+                I0 = dot4(w.q[j] & LO4, x.c[j], I0);
+                I1 = dot4((w.q[j] >> 4) & LO4, x.c[8 + j], I1);
+            } else {
+                I0 = dot4(w.q[j], x.c[j], I0);
+                I1 = dot4(w.q[8 + j], x.c[8 + j], I1);
+            }
         }
         acc = __builtin_fmaf(w.f[0] * (float)I0 - w.f[1] * (float)x.S[0], x.d[0], acc);
         return __builtin_fmaf(w.f[2] * (float)I1 - w.f[3] * (float)x.S[1], x.d[1], acc);
