@@ -132,12 +132,12 @@ __global__ __launch_bounds__(WG) void k_quantize_q8_1(Q81Args a) {
 // (codes, scales and exact code sums per 32-value block) is staged in LDS
 // once per workgroup when it fits, so the compute phase touches LDS only and
 // never waits on the prefetch.
-// Per chunk a lane issues gv_nl<RW>() 16-byte loads: 5 when a chunk holds two
-// rows (a pair of 2304-byte q4_k rows of 4096 values fits), else 4 (the
-// measured best for single rows).
+// Per chunk a lane issues gv_nl<RW>() 16-byte loads: 5 when a chunk holds
+// two or four rows (a pair of 2304-byte q4_k rows of 4096 values fits), else
+// 4 (the measured best for single rows).
 template <int RW>
 constexpr int gv_nl() {
-    return RW == 2 ? 5 : 4;
+    return RW >= 2 ? 5 : 4;
 }
 // Chunk bytes: whole blocks spanning at most 64 * gv_nl 16-byte groups at any start offset.
 template <int RW>
@@ -167,7 +167,7 @@ struct GvArgs {
     uint32_t M;             // activation rows, 1 .. MT
     uint32_t nbr;           // blocks per row
     uint32_t cb;            // blocks per chunk
-    uint32_t rw;            // rows a chunk holds: 2 when two whole rows fit one chunk, else 1
+    uint32_t rw;            // rows a chunk holds: 4 or 2 when that many whole rows fit one chunk, else 1
 };
 
 // Sum over the 64 lanes of a wave with DPP steps, in a fixed order: lane
@@ -214,6 +214,13 @@ constexpr uint32_t ONES8 = 0x01010101u;
 // (binary32), then M*K/32 code sums (int32).
 NQ_HD uint32_t gv_act_dw(const GvArgs &a) { return a.M * (a.K / 4u + 2u * a.kb); }
 
+// Position of 16-byte code group g of an activation row in LDS: when K is a
+// multiple of 128, group g sits at g ^ ((g >> 3) & 7) (a swap inside each
+// aligned run of eight groups), so that lanes reading the groups of
+// consecutive 32-value blocks (or of every other one) fall in distinct LDS
+// banks; otherwise at g.
+NQ_HD uint32_t act_group(uint32_t K, uint32_t g) { return (K & 127u) == 0u ? g ^ ((g >> 3) & 7u) : g; }
+
 // Activation staging, strided over the workgroup's threads.
 NQ_HD void gv_stage_act(const GvArgs &a, uint32_t *lds, uint32_t tid, uint32_t nthreads) {
     float *dl = (float *)(lds + a.M * a.K / 4u);
@@ -222,11 +229,11 @@ NQ_HD void gv_stage_act(const GvArgs &a, uint32_t *lds, uint32_t tid, uint32_t n
         const uint32_t m = i / a.kb, blk = i - m * a.kb;
         const uint32_t *p = a.xq + (uint64_t)m * a.xrow + (uint64_t)blk * 9u;
         int sum = 0;
-        uint32_t *c = lds + (m * a.K + blk * 32u) / 4u;
+        uint32_t *row = lds + m * a.K / 4u;
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             const uint32_t w = p[1 + j];
-            c[j] = w;
+            row[4u * act_group(a.K, 2u * blk + (uint32_t)(j >> 2)) + (uint32_t)(j & 3)] = w;
             sum = dot4(ONES8, w, sum);
         }
         dl[i] = f16(p[0] & 0xFFFFu);
@@ -244,9 +251,13 @@ struct GvAct {
     uint32_t K, kb, xrow, M;
     NQ_HD float block(uint32_t m, uint32_t ab, uint32_t (&c)[8], int *S) const {
         if constexpr (ALDS) {
-            const uint32_t *cp = lds + (m * K + ab * 32u) / 4u;
+            const uint32_t *row = lds + m * K / 4u;
+            const uint32_t *c0 = row + 4u * act_group(K, 2u * ab), *c1 = row + 4u * act_group(K, 2u * ab + 1u);
 #pragma unroll
-            for (int j = 0; j < 8; j++) c[j] = cp[j];
+            for (int j = 0; j < 4; j++) {
+                c[j] = c0[j];
+                c[4 + j] = c1[j];
+            }
             const float *dl = (const float *)(lds + M * K / 4u);
             *S = ((const int *)(dl + M * kb))[m * kb + ab];
             return dl[m * kb + ab];
@@ -266,7 +277,7 @@ struct GvAct {
     NQ_HD float unit(uint32_t m, uint32_t u, uint32_t (&c)[2]) const {
         const uint32_t ab = u >> 2, co = 2u * (u & 3u);
         if constexpr (ALDS) {
-            const uint32_t *cp = lds + (m * K + ab * 32u) / 4u + co;
+            const uint32_t *cp = lds + m * K / 4u + 4u * act_group(K, 2u * ab + (co >> 2)) + (co & 3u);
             c[0] = cp[0];
             c[1] = cp[1];
             return ((const float *)(lds + M * K / 4u))[m * kb + ab];
@@ -631,10 +642,10 @@ NQ_HD float gv_dot(const GvW &w, const GvA &x, float acc) {
     }
 }
 
-// A chunk: blocks c0 .. c0+nb-1 of rows r .. r+rw-1 (rw = 2 only for two
-// whole rows), spanning 16-byte groups g0..g1 of the launch's weight bytes;
-// its first block sits at LDS byte o0 of the wave's region, row r+1's at
-// o0 + row_bytes.
+// A chunk: blocks c0 .. c0+nb-1 of rows r .. r+rw-1 (rw > 1 only for whole
+// rows), spanning 16-byte groups g0..g1 of the launch's weight bytes; its
+// first block sits at LDS byte o0 of the wave's region, row r+i's at
+// o0 + i * row_bytes.
 struct GvChunk {
     uint32_t r, rw, c0, nb, g0, g1, o0;
 };
@@ -643,7 +654,7 @@ NQ_HD GvChunk gv_chunk(const GvArgs &a, uint32_t r, uint32_t c0) {
     const uint32_t S = a.row_bytes / a.nbr;
     GvChunk c;
     c.r = r;
-    c.rw = a.rw == 2u && r + 1u < a.rows ? 2u : 1u;
+    c.rw = a.rows - r < a.rw ? a.rows - r : a.rw;
     c.c0 = c0;
     c.nb = a.nbr - c0 < a.cb ? a.nbr - c0 : a.cb;
     const uint32_t p0 = a.wmis + r * a.row_bytes + c0 * S;
@@ -841,8 +852,10 @@ struct Q81Launch {
     uint32_t *status;
 };
 
-// Chunks hold row pairs when two whole rows fit one pair chunk.
-inline bool gv_pairs(uint64_t row_bytes) { return 2 * row_bytes <= gv_chunk_bytes<2>(); }
+// Whole rows a chunk holds: 4 or 2 when they fit one chunk, else 1.
+inline uint32_t gv_rows_per_chunk(uint64_t row_bytes) {
+    return 4 * row_bytes <= gv_chunk_bytes<4>() ? 4u : 2 * row_bytes <= gv_chunk_bytes<2>() ? 2u : 1u;
+}
 
 // Activation staged in LDS when its codes, scales and sums fit the budget.
 inline bool gv_act_in_lds(uint64_t M, uint64_t K) { return M * (K + K / 32 * 8) <= GV_ACT_LDS_MAX; }
@@ -866,11 +879,11 @@ GvArgs gv_args(const GvLaunch &L, uint64_t r0, uint64_t rows) {
     a.ldy = (uint32_t)L.N;
     a.M = (uint32_t)L.M;
     a.nbr = (uint32_t)nbr;
-    // row pairs when two rows fit a pair chunk; else chunks of at most the
-    // single-row chunk bytes (every block is at most 292 bytes), the row's
-    // chunks as even as whole blocks allow
-    a.rw = gv_pairs(row_bytes) ? 2u : 1u;
-    const uint64_t cmax = (a.rw == 2u ? gv_chunk_bytes<2>() : gv_chunk_bytes<1>()) / S;
+    // four or two whole rows per chunk when they fit; else chunks of at
+    // most the single-row chunk bytes (every block is at most 292 bytes),
+    // the row's chunks as even as whole blocks allow
+    a.rw = gv_rows_per_chunk(row_bytes);
+    const uint64_t cmax = (a.rw > 1u ? gv_chunk_bytes<2>() : gv_chunk_bytes<1>()) / S;
     const uint64_t nch = (nbr + cmax - 1) / cmax;
     a.cb = (uint32_t)((nbr + nch - 1) / nch);
     return a;
@@ -878,7 +891,7 @@ GvArgs gv_args(const GvLaunch &L, uint64_t r0, uint64_t rows) {
 
 // LDS bytes of a launch: the staged activation (when in LDS) and the waves' regions.
 inline uint32_t gv_lds_bytes(const GvArgs &a, bool alds) {
-    return 4u * ((alds ? gv_act_dw(a) : 0u) + GV_WAVES * (a.rw == 2u ? gv_wave_dw<2>() : gv_wave_dw<1>()));
+    return 4u * ((alds ? gv_act_dw(a) : 0u) + GV_WAVES * (a.rw > 1u ? gv_wave_dw<2>() : gv_wave_dw<1>()));
 }
 
 // Workgroups of a launch: as many as the device keeps resident (the waves
@@ -914,12 +927,16 @@ int launch_gemv_rw(const GvLaunch &L, hipStream_t stream) {
     return 0;
 }
 
-// Row pairs only where two rows fit one chunk (the rows-per-chunk count
-// fixes the registers the items hold).
+// The rows-per-chunk count is a template parameter: it fixes the registers
+// the items hold.
 template <int F, int MT, bool ALDS>
 int launch_gemv_lds(const GvLaunch &L, hipStream_t stream) {
     const uint64_t row_bytes = L.K / (uint64_t)block_values(F) * (uint64_t)block_bytes(F);
-    return gv_pairs(row_bytes) ? launch_gemv_rw<F, MT, ALDS, 2>(L, stream) : launch_gemv_rw<F, MT, ALDS, 1>(L, stream);
+    switch (gv_rows_per_chunk(row_bytes)) {
+    case 4: return launch_gemv_rw<F, MT, ALDS, 4>(L, stream);
+    case 2: return launch_gemv_rw<F, MT, ALDS, 2>(L, stream);
+    default: return launch_gemv_rw<F, MT, ALDS, 1>(L, stream);
+    }
 }
 
 template <int F, int MT>

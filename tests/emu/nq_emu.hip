@@ -309,8 +309,11 @@ template <int F, int MT, bool ALDS>
 long run_gemv_alds(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y,
                    uint32_t resident, uint64_t max_rows, char *err, int errlen) {
     const uint64_t row_bytes = K / (uint64_t)nq::block_values(F) * (uint64_t)nq::block_bytes(F);
-    return nq::gv_pairs(row_bytes) ? run_gemv_lds<F, MT, ALDS, 2>(w, N, K, xq, M, y, resident, max_rows, err, errlen)
-                                   : run_gemv_lds<F, MT, ALDS, 1>(w, N, K, xq, M, y, resident, max_rows, err, errlen);
+    switch (nq::gv_rows_per_chunk(row_bytes)) {
+    case 4: return run_gemv_lds<F, MT, ALDS, 4>(w, N, K, xq, M, y, resident, max_rows, err, errlen);
+    case 2: return run_gemv_lds<F, MT, ALDS, 2>(w, N, K, xq, M, y, resident, max_rows, err, errlen);
+    default: return run_gemv_lds<F, MT, ALDS, 1>(w, N, K, xq, M, y, resident, max_rows, err, errlen);
+    }
 }
 
 template <int F, int MT>

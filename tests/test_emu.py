@@ -336,3 +336,19 @@ def test_emu_gemv_rows_staged_in_chunks(fmt, K):
     assert guards
     ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
     linear_check(y, ref, env, K, fmt)
+
+
+@pytest.mark.parametrize("fmt,K", [("gguf:q8_0", 160), ("gguf:q4_0", 96), ("gguf:q4_1", 224), ("gguf:iq4_nl", 32),
+                                   ("gguf:mxfp4", 288), ("gguf:nvfp4", 192)])
+def test_emu_gemv_k_not_a_multiple_of_128(fmt, K):
+    """The activation's LDS layout is swizzled only when K is a multiple of
+    128; other K take the plain layout."""
+    idx, B, S, _ = oracle.info(fmt)
+    N, M = 7, 3
+    w = synth.payload(fmt, N * K // B, 21, synth.binade(-6, -2, False))
+    _, xq = oracle.quantize_q8_1(_act(M, K, 4).astype(np.float32))
+    y, rc, msg, guards = emu_lib.gemv_q8_1(idx, w, N, K, xq, M, w_mis=3)
+    assert rc == 0, msg
+    assert guards
+    ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
+    linear_check(y, ref, env, K, fmt)

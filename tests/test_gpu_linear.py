@@ -194,3 +194,15 @@ def test_gemv_rows_staged_in_chunks(fmt, K):
     announce(f"gemv chunked {fmt} K={K}")
     y = _gemv(fmt, w, N, K, xq, 2)
     linear_check(y, ref, env, K, fmt)
+
+
+@pytest.mark.parametrize("fmt,K", [("gguf:q8_0", 160), ("gguf:q4_0", 96), ("gguf:mxfp4", 288), ("gguf:nvfp4", 192)])
+def test_gemv_k_not_a_multiple_of_128(fmt, K):
+    """Other K take the activation's plain LDS layout."""
+    N, M = 300, 3
+    w = _weights(fmt, N, K, 31)
+    _, xq = oracle.quantize_q8_1(_act(M, K, 31).astype(np.float32))
+    ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
+    announce(f"gemv {fmt} K={K}")
+    y = _gemv(fmt, w, N, K, xq, 1)
+    linear_check(y, ref, env, K, fmt)
