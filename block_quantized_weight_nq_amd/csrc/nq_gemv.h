@@ -304,11 +304,16 @@ struct GvItem {
     // 32-value blocks (one item each)
     static constexpr bool B32 = F == Q4_0 || F == Q4_1 || F == Q5_0 || F == Q5_1 || F == Q8_0 || F == Q8_1 ||
                                 F == IQ4_NL || F == MXFP4;
-    // 256-value blocks in 32-value items
-    static constexpr bool I32 = F == IQ4_XS || F == Q8_K || F == TQ2_0;
-    static constexpr bool INT = B32 || I32 || F == Q4_K || F == Q5_K || F == Q6_K || F == NVFP4_GGUF;
+    // 256-value blocks in 32-value items (the IQ formats' 32-value groups)
+    static constexpr bool IQ = F == IQ2_XXS || F == IQ2_XS || F == IQ2_S || F == IQ3_XXS || F == IQ3_S ||
+                               F == IQ1_S || F == IQ1_M;
+    static constexpr bool I32 = F == IQ4_XS || F == Q8_K || F == TQ2_0 || F == Q2_K || F == Q3_K || IQ;
+    // 128- and 64-value blocks in 32-value items
+    static constexpr bool S32 = F == Q1_0 || F == Q2_0;
+    static constexpr bool INT = B32 || I32 || S32 || F == Q4_K || F == Q5_K || F == Q6_K || F == NVFP4_GGUF;
     // items per block
-    static constexpr uint32_t IPB = B32 ? 1u : I32 ? 8u : (F == Q4_K || F == Q5_K || F == Q6_K) ? 4u
+    static constexpr uint32_t IPB = B32 ? 1u : I32 ? 8u : S32 ? (uint32_t)block_values(F) / 32u
+                                  : (F == Q4_K || F == Q5_K || F == Q6_K) ? 4u
                                   : F == NVFP4_GGUF ? 2u : (uint32_t)block_values(F) / 8u;
 };
 
@@ -316,6 +321,18 @@ struct GvItem {
 // (b's four low bits spread one per byte by a multiply that keeps the four
 // shifted copies apart).
 NQ_HD uint32_t spread4(uint32_t b) { return ((b & 15u) * 0x00204081u & 0x01010101u) << 4; }
+
+// Four bits of b as four bytes 0 or 1 (the spread4 multiply without the shift).
+NQ_HD uint32_t bits4(uint32_t b) { return (b & 15u) * 0x00204081u & 0x01010101u; }
+
+// Byte mask of four sign bits: byte k is 0xFF when bit k of b is set.
+NQ_HD uint32_t signmask4(uint32_t b) { return bits4(b) * 0xFFu; }
+
+// The four 2-bit fields of byte b as four bytes (LSB field first).
+NQ_HD uint32_t crumbs4(uint32_t b) { return (b | (b << 6) | (b << 12) | (b << 18)) & 0x03030303u; }
+
+// IQ sign byte: seven stored bits and their parity as bit 7.
+NQ_HD uint32_t iq_signs8(uint32_t s7) { return s7 | (parity7(s7) << 7); }
 
 // Decoded weights of one item (the fields a format uses).
 struct GvW {
@@ -490,6 +507,187 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
             w.q[j] = (q[j] & LO4) | (((qh[j] >> (2u * part)) & 0x01010101u) << 4);
             w.q[8 + j] = ((q[j] >> 4) & LO4) | (((qh[j] >> (2u * part + 1u)) & 0x01010101u) << 4);
         }
+    } else if constexpr (F == Q2_K) {
+        // part c: values 32c + i, bits 2(c mod 4) of byte 16 + 32(c / 4) + i;
+        // sub-block scale bytes 2c, 2c+1 (low nibble: scale, high: min);
+        // d at 80, dmin at 82; w = RN32(d * (s mod 16)) * v - RN32(dmin * (s / 16))
+        uint32_t q[8], h[1];
+        window<8>(s, bo + 16u + 32u * (part >> 2), q);
+        window<1>(s, bo + 80u, h);
+        const uint32_t sc = u16_at(s, bo + 2u * part);
+        const float d = f16(h[0] & 0xFFFFu), dmin = f16(h[0] >> 16);
+        w.f[0] = M(d, (float)(sc & 15u));
+        w.f[1] = M(dmin, (float)((sc >> 4) & 15u));
+        w.f[2] = M(d, (float)((sc >> 8) & 15u));
+        w.f[3] = M(dmin, (float)(sc >> 12));
+#pragma unroll
+        for (int j = 0; j < 8; j++) w.q[j] = (q[j] >> (2u * (part & 3u))) & 0x03030303u;
+    } else if constexpr (F == Q3_K) {
+        // part c: v = bits 2(c mod 4) of byte 32 + 32(c / 4) + i, plus 4 * bit c
+        // of mask byte i; code v + 4h - 4; sub-block k scale l + 16a - 32 (l:
+        // nibble k / 8 of byte 96 + k mod 8, a: bits 2(k / 4) of byte 104 + k
+        // mod 4); d at 108; w = RN32(d * s) * (v - 4 (1 - h))
+        uint32_t q[8], mk[8], sc[3];
+        window<8>(s, bo + 32u + 32u * (part >> 2), q);
+        window<8>(s, bo, mk);
+        window<3>(s, bo + 96u, sc);
+        const float d = f16(u16_at(s, bo + 108u));
+#pragma unroll
+        for (int e = 0; e < 2; e++) {
+            const uint32_t k = 2u * part + (uint32_t)e, lk = k & 7u;
+            const uint32_t l = (bytek(lk < 4u ? sc[0] : sc[1], lk & 3u) >> (4u * (k >> 3))) & 15u;
+            const uint32_t a = (bytek(sc[2], k & 3u) >> (2u * (k >> 2))) & 3u;
+            w.f[e] = M(d, (float)((int)(l + 16u * a) - 32));
+        }
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            w.q[j] = ((q[j] >> (2u * (part & 3u))) & 0x03030303u) | (((mk[j] >> part) & 0x01010101u) << 2);
+    } else if constexpr (F == Q1_0) {
+        // part p: values 32p + i, bit i mod 8 of byte 2 + 4p + i / 8; w = +-d (d
+        // for a set bit): code 2b - 1
+        uint32_t q[1];
+        window<1>(s, bo + 2u + 4u * part, q);
+        w.f[0] = f16(u16_at(s, bo));
+#pragma unroll
+        for (int j = 0; j < 8; j++) w.q[j] = bits4(q[0] >> (4 * j));
+    } else if constexpr (F == Q2_0) {
+        // part p: values 32p + 4t + k, bits 2k of byte 2 + 8p + t; w = d * (v - 1)
+        uint32_t q[2];
+        window<2>(s, bo + 2u + 8u * part, q);
+        w.f[0] = f16(u16_at(s, bo));
+#pragma unroll
+        for (int j = 0; j < 8; j++) w.q[j] = crumbs4(bytek(q[j >> 2], (uint32_t)(j & 3)));
+    } else if constexpr (GvItem<F>::IQ) {
+        // group g = part (32 values, units 4g .. 4g+3): per unit its 8 grid
+        // bytes (w.q[2l], w.q[2l+1]) and those bytes under its negative signs
+        // (w.q[8 + 2l], w.q[9 + 2l]); the scales in w.f (see gv_dot)
+        const uint32_t g = part;
+        const float d = F == IQ1_M ? 0.0f : f16(u16_at(s, bo));
+        if constexpr (F == IQ2_XXS || F == IQ3_XXS) {
+            // iq2_xxs: 4 index bytes then the aux word at 2 + 8g; iq3_xxs: index
+            // pairs at 2 + 8g, the aux word at 66 + 4g; seven sign bits per unit
+            // (+ parity), scale nibble aux >> 28
+            uint32_t ix[2], aux[1];
+            window<2>(s, bo + 2u + 8u * g, ix);
+            if constexpr (F == IQ2_XXS)
+                aux[0] = ix[1];
+            else
+                window<1>(s, bo + 66u + 4u * g, aux);
+            w.f[0] = M(M(d, A(0.5f, (float)(aux[0] >> 28))), F == IQ2_XXS ? 0.25f : 0.5f);
+#pragma unroll
+            for (int l = 0; l < 4; l++) {
+                uint32_t g0, g1;
+                if constexpr (F == IQ2_XXS) {
+                    const uint64_t row = tab.iq2xxs(bytek(ix[0], (uint32_t)l));
+                    g0 = (uint32_t)row;
+                    g1 = (uint32_t)(row >> 32);
+                } else {
+                    const uint32_t i2 = (ix[l >> 1] >> (16 * (l & 1))) & 0xFFFFu;
+                    g0 = tab.iq3xxs(i2 & 0xFFu);
+                    g1 = tab.iq3xxs(i2 >> 8);
+                }
+                const uint32_t sg = iq_signs8((aux[0] >> (7u * (uint32_t)l)) & 127u);
+                w.q[2 * l] = g0;
+                w.q[2 * l + 1] = g1;
+                w.q[8 + 2 * l] = g0 & signmask4(sg);
+                w.q[9 + 2 * l] = g1 & signmask4(sg >> 4);
+            }
+        } else if constexpr (F == IQ2_XS || F == IQ2_S) {
+            // two scale nibbles per group (units 0-1 and 2-3): iq2_xs at byte
+            // 66 + g, iq2_s at 74 + g; c = RN32(RN32(d * (0.5 + t)) * 0.25)
+            const uint32_t sb = u8_at(s, bo + (F == IQ2_XS ? 66u : 74u) + g);
+            w.f[0] = M(M(d, A(0.5f, (float)(sb & 15u))), 0.25f);
+            w.f[1] = M(M(d, A(0.5f, (float)(sb >> 4))), 0.25f);
+            uint32_t wd[2], lo[1], sgn[1];
+            uint32_t hi = 0;
+            if constexpr (F == IQ2_XS) {
+                window<2>(s, bo + 2u + 8u * g, wd);  // four 16-bit words: 9-bit index, 7 sign bits
+            } else {
+                window<1>(s, bo + 2u + 4u * g, lo);   // four index low bytes
+                window<1>(s, bo + 34u + 4u * g, sgn); // four sign bytes
+                hi = u8_at(s, bo + 66u + g);          // four 2-bit index high parts
+            }
+#pragma unroll
+            for (int l = 0; l < 4; l++) {
+                uint64_t row;
+                uint32_t sg;
+                if constexpr (F == IQ2_XS) {
+                    const uint32_t word = (wd[l >> 1] >> (16 * (l & 1))) & 0xFFFFu;
+                    row = tab.iq2xs(word & 511u);
+                    sg = iq_signs8(word >> 9);
+                } else {
+                    row = tab.iq2s(bytek(lo[0], (uint32_t)l) | (((hi >> (2 * l)) & 3u) << 8));
+                    sg = bytek(sgn[0], (uint32_t)l);
+                }
+                const uint32_t g0 = (uint32_t)row, g1 = (uint32_t)(row >> 32);
+                w.q[2 * l] = g0;
+                w.q[2 * l + 1] = g1;
+                w.q[8 + 2 * l] = g0 & signmask4(sg);
+                w.q[9 + 2 * l] = g1 & signmask4(sg >> 4);
+            }
+        } else if constexpr (F == IQ3_S) {
+            // index pairs at 2 + 8g with a ninth bit each from byte 66 + g, sign
+            // bytes at 74 + 4g, scale nibble g mod 2 of byte 106 + g / 2:
+            // c = RN32(d * (1 + 2 t))
+            uint32_t ix[2], sgn[1];
+            window<2>(s, bo + 2u + 8u * g, ix);
+            window<1>(s, bo + 74u + 4u * g, sgn);
+            const uint32_t h = u8_at(s, bo + 66u + g);
+            const uint32_t sc = u8_at(s, bo + 106u + (g >> 1));
+            w.f[0] = M(d, (float)(1u + 2u * ((sc >> (4u * (g & 1u))) & 15u)));
+#pragma unroll
+            for (int l = 0; l < 4; l++) {
+                const uint32_t i2 = (ix[l >> 1] >> (16 * (l & 1))) & 0xFFFFu;
+                const uint32_t g0 = tab.iq3s((i2 & 0xFFu) | (((h >> (2 * l)) & 1u) << 8));
+                const uint32_t g1 = tab.iq3s((i2 >> 8) | (((h >> (2 * l + 1)) & 1u) << 8));
+                const uint32_t sg = bytek(sgn[0], (uint32_t)l);
+                w.q[2 * l] = g0;
+                w.q[2 * l + 1] = g1;
+                w.q[8 + 2 * l] = g0 & signmask4(sg);
+                w.q[9 + 2 * l] = g1 & signmask4(sg >> 4);
+            }
+        } else if constexpr (F == IQ1_S) {
+            // index low bytes at 2 + 4g, the group word a at 34 + 2g (3 index
+            // bits per unit, scale bits 12-14, delta sign bit 15); grid bytes
+            // hold value + 1; w = RN32(d * (2 t + 1)) * (v + delta)
+            uint32_t ix[1];
+            window<1>(s, bo + 2u + 4u * g, ix);
+            const uint32_t a = u16_at(s, bo + 34u + 2u * g);
+            w.f[0] = M(d, (float)(2u * ((a >> 12) & 7u) + 1u));
+            w.f[1] = (a & 0x8000u) ? -0.125f : 0.125f;
+#pragma unroll
+            for (int l = 0; l < 4; l++) {
+                const uint64_t row = tab.iq1s(bytek(ix[0], (uint32_t)l) | (((a >> (3 * l)) & 7u) << 8));
+                w.q[2 * l] = (uint32_t)row;
+                w.q[2 * l + 1] = (uint32_t)(row >> 32);
+            }
+        } else {  // IQ1_M
+            // index low bytes at 4g, a nibble per unit (bytes 32 + 2g, 33 + 2g:
+            // 3 index bits, delta sign bit 3), scale words at 48 (3 bits per
+            // pair of units; the binary16 d in their top nibbles)
+            uint32_t ix[1], hw[1], sw[2];
+            window<1>(s, bo + 4u * g, ix);
+            window<1>(s, bo + 32u + 2u * g, hw);  // the unit nibbles of this group (low 16 bits)
+            window<2>(s, bo + 48u, sw);
+            const uint32_t dbits = ((sw[0] & 0xFFFFu) >> 12) | ((sw[0] >> 28) << 4) | (((sw[1] & 0xFFFFu) >> 12) << 8) |
+                                   ((sw[1] >> 28) << 12);
+            const float dm = f16(dbits);
+            const uint32_t kw = g >> 1;
+            const uint32_t wg = ((kw >> 1) == 0u ? sw[0] : sw[1]) >> (16u * (kw & 1u));
+#pragma unroll
+            for (int p = 0; p < 2; p++) {
+                const uint32_t t = (wg >> (6u * (g & 1u) + 3u * (uint32_t)p)) & 7u;
+                w.f[p] = M(dm, (float)(2u * t + 1u));
+            }
+#pragma unroll
+            for (int l = 0; l < 4; l++) {
+                const uint32_t an = (hw[0] >> (4 * l)) & 15u;
+                const uint64_t row = tab.iq1s(bytek(ix[0], (uint32_t)l) | ((an & 7u) << 8));
+                w.q[2 * l] = (uint32_t)row;
+                w.q[2 * l + 1] = (uint32_t)(row >> 32);
+                w.f[2 + l] = (an & 8u) ? -0.125f : 0.125f;
+            }
+        }
     } else if constexpr (F == Q4_K) {
         // part g: values 64g .. 64g+63, the low (sub-block 2g) and high
         // (sub-block 2g+1) nibbles of bytes 16 + 32g .. 16 + 32g + 31;
@@ -540,10 +738,10 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
 template <int F, class Act>
 NQ_HD void gv_a(const Act &act, uint32_t m, uint32_t b, uint32_t part, GvA &x) {
     uint32_t c[8];
-    if constexpr (GvItem<F>::B32 || GvItem<F>::I32 || F == NVFP4_GGUF) {
-        // the item's 32 values are activation block b (32-value blocks),
-        // 8b + part (32-value items of 256-value blocks) or 2b + part (nvfp4)
-        const uint32_t ab = GvItem<F>::B32 ? b : GvItem<F>::I32 ? 8u * b + part : 2u * b + part;
+    if constexpr (GvItem<F>::B32 || GvItem<F>::I32 || GvItem<F>::S32 || F == NVFP4_GGUF) {
+        // the item's 32 values are activation block b (32-value blocks) or
+        // IPB b + part (32-value items of larger blocks)
+        const uint32_t ab = GvItem<F>::B32 ? b : GvItem<F>::IPB * b + part;
         x.d[0] = act.block(m, ab, c, &x.S[0]);
 #pragma unroll
         for (int j = 0; j < 8; j++) x.c[j] = c[j];
@@ -597,6 +795,74 @@ NQ_HD float gv_dot(const GvW &w, const GvA &x, float acc) {
             I1 = dot4(w.q[4 + j], x.c[4 + j], I1);
         }
         return __builtin_fmaf(w.f[0] * (float)I0 + w.f[1] * (float)I1, x.d[0], acc);
+    } else if constexpr (F == Q2_K) {
+        // two 16-value sub-blocks, each RN32(d * s) * I - RN32(dmin * m) * S
+        int I0 = 0, I1 = 0, S0 = 0;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            I0 = dot4(w.q[j], x.c[j], I0);
+            S0 = dot4(ONES8, x.c[j], S0);
+            I1 = dot4(w.q[4 + j], x.c[4 + j], I1);
+        }
+        const int S1 = x.S[0] - S0;
+        return __builtin_fmaf((w.f[0] * (float)I0 - w.f[1] * (float)S0) + (w.f[2] * (float)I1 - w.f[3] * (float)S1),
+                              x.d[0], acc);
+    } else if constexpr (F == Q3_K) {
+        // two 16-value sub-blocks of codes v + 4h - 4
+        int I0 = 0, I1 = 0, S0 = 0;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            I0 = dot4(w.q[j], x.c[j], I0);
+            S0 = dot4(ONES8, x.c[j], S0);
+            I1 = dot4(w.q[4 + j], x.c[4 + j], I1);
+        }
+        const int S1 = x.S[0] - S0;
+        return __builtin_fmaf(w.f[0] * (float)(I0 - 4 * S0) + w.f[1] * (float)(I1 - 4 * S1), x.d[0], acc);
+    } else if constexpr (F == Q1_0 || F == Q2_0) {
+        // q1_0: codes 2b - 1; q2_0: v - 1
+        int I = 0;
+#pragma unroll
+        for (int j = 0; j < 8; j++) I = dot4(w.q[j], x.c[j], I);
+        const int V = F == Q1_0 ? 2 * I - x.S[0] : I - x.S[0];
+        return __builtin_fmaf(w.f[0] * (float)V, x.d[0], acc);
+    } else if constexpr (F == IQ2_XXS || F == IQ3_XXS || F == IQ3_S) {
+        // signed grid values: dot(g, x) - 2 dot(g under the negative signs, x); one scale
+        int I = 0, N = 0;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            I = dot4(w.q[j], x.c[j], I);
+            N = dot4(w.q[8 + j], x.c[j], N);
+        }
+        return __builtin_fmaf(w.f[0] * (float)(I - 2 * N), x.d[0], acc);
+    } else if constexpr (F == IQ2_XS || F == IQ2_S) {
+        // as above with a scale per pair of units (words 0-3: units 0-1)
+        int I0 = 0, I1 = 0, N0 = 0, N1 = 0;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            I0 = dot4(w.q[j], x.c[j], I0);
+            N0 = dot4(w.q[8 + j], x.c[j], N0);
+            I1 = dot4(w.q[4 + j], x.c[4 + j], I1);
+            N1 = dot4(w.q[12 + j], x.c[4 + j], N1);
+        }
+        return __builtin_fmaf(w.f[0] * (float)(I0 - 2 * N0) + w.f[1] * (float)(I1 - 2 * N1), x.d[0], acc);
+    } else if constexpr (F == IQ1_S) {
+        // codes are grid bytes - 1: dot(g, x) - S; plus delta * S; one scale
+        int I = 0;
+#pragma unroll
+        for (int j = 0; j < 8; j++) I = dot4(w.q[j], x.c[j], I);
+        const float T = (float)(I - x.S[0]) + w.f[1] * (float)x.S[0];  // exact: integers and eighths
+        return __builtin_fmaf(w.f[0] * T, x.d[0], acc);
+    } else if constexpr (F == IQ1_M) {
+        // per unit: dot(g, x) - S_l + delta_l * S_l (S_l the unit's 8 codes);
+        // a scale per pair of units
+        float T[2] = {0.0f, 0.0f};
+#pragma unroll
+        for (int l = 0; l < 4; l++) {
+            const int Sl = dot4(ONES8, x.c[2 * l + 1], dot4(ONES8, x.c[2 * l], 0));
+            const int Il = dot4(w.q[2 * l + 1], x.c[2 * l + 1], dot4(w.q[2 * l], x.c[2 * l], 0));
+            T[l >> 1] = T[l >> 1] + ((float)(Il - Sl) + w.f[2 + l] * (float)Sl);  // exact: integers and eighths
+        }
+        return __builtin_fmaf(w.f[0] * T[0] + w.f[1] * T[1], x.d[0], acc);
     } else if constexpr (F == Q4_0) {
         int I = 0;
 #pragma unroll
