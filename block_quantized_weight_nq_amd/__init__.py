@@ -23,7 +23,8 @@ EXPORTS = ["nq_format_count", "nq_format_by_id", "nq_format_query", "nq_validate
            "nq_dequantize_packed", "nq_validate_nvfp4_stacked", "nq_dequantize_nvfp4_stacked",
            "nq_validate_fp8_row", "nq_dequantize_fp8_row", "nq_validate_grouped_absmax",
            "nq_quantize_grouped_absmax", "nq_validate_quantize_q8_1", "nq_quantize_q8_1",
-           "nq_validate_gemv_q8_1", "nq_gemv_q8_1", "nq_status_string"]
+           "nq_validate_gemv_q8_1", "nq_gemv_q8_1", "nq_validate_gemm_q8_1", "nq_gemm_q8_1",
+           "nq_status_string"]
 GEMV_MAX_M = 8
 GQ_SCHEMES = {"q4_g64_fp16": (0, 64), "q5_g64_fp16": (1, 64), "q6_g64_fp16": (2, 64), "q8_g32_fp16": (3, 32)}
 FP8_ROW_KINDS = {"fp8_e4m3fn_row_bf16": 0, "fp8_e4m3fn_row_fp16": 1}
@@ -81,6 +82,9 @@ def _lib():
                                        c.c_void_p, c.c_void_p]
         L.nq_validate_gemv_q8_1.argtypes = [c.c_int32, c.c_uint64, c.c_int64, c.c_int64, c.c_int64]
         L.nq_gemv_q8_1.argtypes = [c.c_int32, c.c_void_p, c.c_uint64, c.c_int64, c.c_int64, c.c_void_p,
+                                   c.c_int64, c.c_void_p, c.c_void_p]
+        L.nq_validate_gemm_q8_1.argtypes = [c.c_int32, c.c_uint64, c.c_int64, c.c_int64, c.c_int64]
+        L.nq_gemm_q8_1.argtypes = [c.c_int32, c.c_void_p, c.c_uint64, c.c_int64, c.c_int64, c.c_void_p,
                                    c.c_int64, c.c_void_p, c.c_void_p]
         L.nq_status_string.argtypes = [c.c_int]
         L.nq_status_string.restype = c.c_char_p
@@ -335,10 +339,18 @@ def gemv_q8_1_raw(fmt_id, w_ptr, nbytes, N, K, xq_ptr, M, y_ptr, stream_handle):
                                ctypes.c_void_p(y_ptr), ctypes.c_void_p(stream_handle))
 
 
-def gemv_q8_1(fmt, weight, N, K, xq, out=None, stream=None):
-    """y[M, N] (float32) = x[M, K] @ w[N, K]^T for a rank-1 uint8 CUDA weight
-    payload of `fmt` (a "gguf:" format) and q8_1 activation blocks `xq`
-    ([M, K/32, 36] uint8, as quantize_q8_1 returns), M <= 8."""
+def validate_gemm_q8_1_status(fmt, nbytes, N, K, M):
+    fid = fmt if isinstance(fmt, int) else format_query(fmt).id
+    return _lib().nq_validate_gemm_q8_1(fid, nbytes, N, K, M)
+
+
+def gemm_q8_1_raw(fmt_id, w_ptr, nbytes, N, K, xq_ptr, M, y_ptr, stream_handle):
+    """Direct call of nq_gemm_q8_1 with integer addresses; returns the status."""
+    return _lib().nq_gemm_q8_1(int(fmt_id), ctypes.c_void_p(w_ptr), nbytes, N, K, ctypes.c_void_p(xq_ptr), M,
+                               ctypes.c_void_p(y_ptr), ctypes.c_void_p(stream_handle))
+
+
+def _product(raw, fmt, weight, N, K, xq, out, stream):
     import torch
     fid = fmt if isinstance(fmt, int) else format_query(fmt).id
     if not weight.is_cuda or not xq.is_cuda or xq.dtype != torch.uint8 or not xq.is_contiguous():
@@ -352,11 +364,23 @@ def gemv_q8_1(fmt, weight, N, K, xq, out=None, stream=None):
         raise ValueError("out must be a contiguous float32 tensor of M * N elements")
     if stream is None:
         stream = torch.cuda.current_stream(weight.device)
-    st = gemv_q8_1_raw(fid, weight.data_ptr(), weight.numel(), N, K, xq.data_ptr(), M, out.data_ptr(),
-                       stream.cuda_stream)
+    st = raw(fid, weight.data_ptr(), weight.numel(), N, K, xq.data_ptr(), M, out.data_ptr(), stream.cuda_stream)
     if st != NQ_OK:
         raise NqError(st, f"{fmt} [{N}, {K}] x {M}")
     return out
+
+
+def gemv_q8_1(fmt, weight, N, K, xq, out=None, stream=None):
+    """y[M, N] (float32) = x[M, K] @ w[N, K]^T for a rank-1 uint8 CUDA weight
+    payload of `fmt` (a "gguf:" format) and q8_1 activation blocks `xq`
+    ([M, K/32, 36] uint8, as quantize_q8_1 returns), M <= 8."""
+    return _product(gemv_q8_1_raw, fmt, weight, N, K, xq, out, stream)
+
+
+def gemm_q8_1(fmt, weight, N, K, xq, out=None, stream=None):
+    """As gemv_q8_1 for any number of activation rows M >= 1 (more than 8 on
+    the matrix cores)."""
+    return _product(gemm_q8_1_raw, fmt, weight, N, K, xq, out, stream)
 
 
 def dequantize_packed(fmt, payload, shape, out_dtype=None, out=None, stream=None):

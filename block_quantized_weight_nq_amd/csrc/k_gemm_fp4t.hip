@@ -1,0 +1,14 @@
+// k_gemm_fp4t.hip -- batched products with q8_1 activations, FP4 and ternary formats (instantiated per format).
+#include "nq_launch.h"
+
+namespace nq {
+int launch_gemm_fp4t(int fmt, const GvLaunch &L, hipStream_t s) {
+    switch (fmt) {
+    case MXFP4: return launch_gemm_f<MXFP4>(L, s);
+    case NVFP4_GGUF: return launch_gemm_f<NVFP4_GGUF>(L, s);
+    case TQ1_0: return launch_gemm_f<TQ1_0>(L, s);
+    case TQ2_0: return launch_gemm_f<TQ2_0>(L, s);
+    default: return 2;  // NQ_ERR_UNKNOWN_FORMAT
+    }
+}
+}  // namespace nq

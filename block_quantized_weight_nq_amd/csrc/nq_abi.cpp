@@ -317,6 +317,15 @@ NQ_API int nq_quantize_q8_1(const void *x, const int64_t *shape, int32_t rank, i
     return nq::launch_quantize_q8_1(in_dtype, L, stream);
 }
 
+static int launch_gemv_family(int32_t format, const nq::GvLaunch &L, hipStream_t stream) {
+    switch (REGISTRY[format].family) {
+    case NQ_FAMILY_SIMPLE: return nq::launch_gemv_simple(format, L, stream);
+    case NQ_FAMILY_KQUANT: return nq::launch_gemv_kquant(format, L, stream);
+    case NQ_FAMILY_IQ: return nq::launch_gemv_iq(format, L, stream);
+    default: return nq::launch_gemv_fp4t(format, L, stream);
+    }
+}
+
 NQ_API int nq_validate_gemv_q8_1(int32_t format, uint64_t nbytes, int64_t N, int64_t K, int64_t M) {
     if (format < 0 || format >= nq::NUM_FORMATS || TRAILER_OF(format) != 0) return NQ_ERR_UNKNOWN_FORMAT;
     if (N <= 0 || K <= 0 || M <= 0 || M > nq::GV_MAX_M) return NQ_ERR_BAD_DIM;
@@ -343,12 +352,55 @@ NQ_API int nq_gemv_q8_1(int32_t format, const void *weight, uint64_t nbytes, int
     L.xq = (const uint8_t *)xq;
     L.y = y;
     L.cus = compute_units();
-    switch (REGISTRY[format].family) {
-    case NQ_FAMILY_SIMPLE: return nq::launch_gemv_simple(format, L, stream);
-    case NQ_FAMILY_KQUANT: return nq::launch_gemv_kquant(format, L, stream);
-    case NQ_FAMILY_IQ: return nq::launch_gemv_iq(format, L, stream);
-    default: return nq::launch_gemv_fp4t(format, L, stream);
+    return launch_gemv_family(format, L, stream);
+}
+
+NQ_API int nq_validate_gemm_q8_1(int32_t format, uint64_t nbytes, int64_t N, int64_t K, int64_t M) {
+    if (format < 0 || format >= nq::NUM_FORMATS || TRAILER_OF(format) != 0) return NQ_ERR_UNKNOWN_FORMAT;
+    if (N <= 0 || K <= 0 || M <= 0) return NQ_ERR_BAD_DIM;
+    if (K % B_OF(format) != 0) return NQ_ERR_NOT_BLOCK_ALIGNED;
+    if (N >= (1ll << 31) || K >= (1ll << 31) || M >= (1ll << 31)) return NQ_ERR_OVERFLOW;
+    uint64_t bytes = 0, xbytes = 0, ybytes = 0;
+    if (!mul_checked((uint64_t)M, (uint64_t)(K / 32) * 36u, &xbytes) || !mul_checked((uint64_t)M, (uint64_t)N * 4u, &ybytes))
+        return NQ_ERR_OVERFLOW;
+    if (!mul_checked((uint64_t)N, (uint64_t)(K / B_OF(format)) * (uint64_t)S_OF(format), &bytes))
+        return NQ_ERR_OVERFLOW;
+    if (nbytes != bytes) return NQ_ERR_LENGTH_MISMATCH;
+    return NQ_OK;
+}
+
+NQ_API int nq_gemm_q8_1(int32_t format, const void *weight, uint64_t nbytes, int64_t N, int64_t K,
+                        const void *xq, int64_t M, float *y, hipStream_t stream) {
+    const int st = nq_validate_gemm_q8_1(format, nbytes, N, K, M);
+    if (st != NQ_OK) return st;
+    if (!weight || !xq || !y) return NQ_ERR_NULL_ARG;
+    if ((uintptr_t)xq % 4 != 0 || (uintptr_t)y % 4 != 0) return NQ_ERR_NULL_ARG;
+    nq::GvLaunch L;
+    L.w = (const uint8_t *)weight;
+    L.N = (uint64_t)N;
+    L.K = (uint64_t)K;
+    L.M = (uint64_t)M;
+    L.xq = (const uint8_t *)xq;
+    L.y = y;
+    L.cus = compute_units();
+    if (M > nq::GV_MAX_M && format != nq::TQ1_0) {
+        switch (REGISTRY[format].family) {
+        case NQ_FAMILY_SIMPLE: return nq::launch_gemm_simple(format, L, stream);
+        case NQ_FAMILY_KQUANT: return nq::launch_gemm_kquant(format, L, stream);
+        case NQ_FAMILY_IQ: return nq::launch_gemm_iq(format, L, stream);
+        default: return nq::launch_gemm_fp4t(format, L, stream);
+        }
     }
+    // the single-row kernel, 8 activation rows per launch
+    for (int64_t m0 = 0; m0 < M; m0 += nq::GV_MAX_M) {
+        nq::GvLaunch l = L;
+        l.M = (uint64_t)(M - m0 < nq::GV_MAX_M ? M - m0 : nq::GV_MAX_M);
+        l.xq = L.xq + (uint64_t)m0 * (uint64_t)(K / 32) * 36u;
+        l.y = L.y + (uint64_t)m0 * (uint64_t)N;
+        const int r = launch_gemv_family(format, l, stream);
+        if (r != NQ_OK) return r;
+    }
+    return NQ_OK;
 }
 
 NQ_API const char *nq_status_string(int status) {

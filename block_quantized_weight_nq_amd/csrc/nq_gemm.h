@@ -1,0 +1,543 @@
+// nq_gemm.h -- batched products (many activation rows) of packed gguf_*
+// weights with q8_1 activations on the 8-bit integer matrix cores.
+//
+// NInfer "tensor-formats" page, GGUF linear operations: the activation is
+// quantized to ggml q8_1 blocks (one binary16 scale per 32 values) and the
+// product accumulates in FP32.  The value each weight stands for is the one
+// the format's decoder gives (the gguf "Packed layouts" of the second page).
+//
+// Spans.  Every 32 consecutive values of a weight row (a span; no span
+// crosses a block) are rewritten as 32 signed 8-bit codes c with, per half of
+// 16 values (or per span for formats with one scale per 32 values), a scale
+// ws and an offset ow such that w = ws * c + ow.  Then, with an activation
+// block's scale d, codes q and exact half sums S_h,
+//     sum over the span of w * d * q = d * sum_h (ws_h * I_h + ow_h * S_h),
+// I_h = sum of c * q over the half (exact integers).  The I_h come from
+// v_mfma_i32_16x16x32_i8 (a 16 x 16 tile of exact 32-term integer dot
+// products); scales with 16-value halves take two MFMAs per span, each with
+// the activation codes of the other half set to zero.  The scaling is done
+// in binary32, per span and half:
+//     acc = fma(RN(ws_h * d), I_h, acc),  acc = fma(ow_h, d * S_h, acc)
+// (d * S_h is exact: at most 11 by 12 significant bits).  The offset term
+// exists for the five affine formats (q4_1, q5_1, q2_k, q4_k, q5_k); for
+// the others ws * c equals the decoded weight exactly.
+//
+// Tiling.  A workgroup (4 waves) owns a tile of 128 weight rows by 64
+// activation rows and walks K in steps of 256 values: its threads rewrite the
+// step's weight spans into LDS (codes, scales, offsets) and copy the
+// activation codes, scales and d * S terms next to them; then each wave
+// computes a 64 x 32 sub-tile, span by span, in a fixed order, so every run
+// of a launch shape gives the same bits.  Tiles that share weight rows are
+// given to workgroups of one XCD (workgroups go to the 8 XCDs in turn), so
+// the weight bytes come from one L2.
+#pragma once
+
+#include "nq_gemv.h"
+
+namespace nq {
+
+constexpr uint32_t GM_BN = 128;            // weight rows per tile
+constexpr uint32_t GM_BM = 64;             // activation rows per tile
+constexpr uint32_t GM_SP = 8;              // spans per K step (256 values)
+constexpr uint32_t GM_CSW = 8u * GM_SP + 4u;  // LDS dwords per code row (256 code bytes + 16 of padding)
+constexpr uint64_t GM_MAX_MROWS = 1ull << 16;  // activation rows per launch
+
+template <int F>
+struct GmFmt {
+    // one scale per 16 values
+    static constexpr bool U16 = F == Q2_K || F == Q3_K || F == Q6_K || F == IQ2_XS || F == IQ2_S || F == IQ1_M ||
+                                F == NVFP4_GGUF;
+    // a code-independent term
+    static constexpr bool AFF = F == Q4_1 || F == Q5_1 || F == Q2_K || F == Q4_K || F == Q5_K;
+    // formats with a span rewrite (tq1_0 has none: its products run through
+    // the single-row kernel)
+    static constexpr bool OK = F != TQ1_0 && F != NVFP4_DIV;
+    static constexpr uint32_t NH = U16 ? 2u : 1u;  // scales per span
+    static constexpr uint32_t SPB = (uint32_t)block_values(F) / 32u;  // spans per block
+    // LDS layout (dwords): weight codes [128][GM_CSW], scales [8][NH][128],
+    // offsets [8][NH][128] (affine formats), activation codes [64][GM_CSW],
+    // scales [8][64], d * S terms [8][NH][64] (affine formats)
+    static constexpr uint32_t WS = GM_BN * GM_CSW;
+    static constexpr uint32_t WO = WS + GM_SP * NH * GM_BN;
+    static constexpr uint32_t XC = WO + (AFF ? GM_SP * NH * GM_BN : 0u);
+    static constexpr uint32_t XD = XC + GM_BM * GM_CSW;
+    static constexpr uint32_t XT = XD + GM_SP * GM_BM;
+    static constexpr uint32_t DW = XT + (AFF ? GM_SP * NH * GM_BM : 0u);
+};
+
+struct GmArgs {
+    const uint32_t *wbase;  // weight bytes of this launch's first row, aligned down to 4 bytes
+    uint32_t wmis;          // that row's start - wbase (0..3)
+    uint32_t wlast;         // last dword holding weight bytes of this launch, from wbase
+    const uint32_t *xq;     // q8_1 blocks of this launch's first activation row (9 dwords each)
+    float *y;               // output of this launch's first activation and weight row
+    uint32_t rows;          // weight rows in this launch
+    uint32_t row_bytes;     // bytes per weight row
+    uint32_t kspans;        // K / 32
+    uint32_t xrow;          // dwords per activation row, K / 32 * 9
+    uint32_t ldy;           // N
+    uint32_t M;             // activation rows in this launch
+    uint32_t mt;            // activation-row tiles
+    uint32_t xq8, xr8;      // workgroups / 8 and workgroups mod 8
+};
+
+// A span rewritten: 32 codes (8 dwords, value order) and per half its scale
+// and offset.
+struct GmSpan {
+    uint32_t c[8];
+    float ws[2];
+    float ow[2];
+};
+
+// Weight source in global memory: dword loads of any window length from a
+// 4-byte-aligned base (16-byte vector loads, then 8 and 4 bytes); `last` is
+// the last dword holding payload bytes, and a window's extra dword is clamped
+// to it.
+struct GmSrc {
+    const uint32_t *base;
+    uint32_t last;
+    template <int N>
+    NQ_HD void load(uint32_t i, uint32_t (&r)[N]) const {
+        const uint32_t *p = base + i;
+#pragma unroll
+        for (int k = 0; k + 4 <= N; k += 4) {
+            const u32x4a4 v = *(const u32x4a4 *)(p + k);
+            r[k] = v.x;
+            r[k + 1] = v.y;
+            r[k + 2] = v.z;
+            r[k + 3] = v.w;
+        }
+        constexpr int k2 = N / 4 * 4;
+        if constexpr (N - k2 >= 2) {
+            const u32x2a4 v = *(const u32x2a4 *)(p + k2);
+            r[k2] = v.x;
+            r[k2 + 1] = v.y;
+        }
+        if constexpr ((N - k2) % 2 == 1) r[N - 1] = p[N - 1];
+    }
+    NQ_HD uint32_t dw(uint32_t i) const { return base[i]; }
+    NQ_HD uint32_t dwx(uint32_t i) const { return base[i < last ? i : last]; }
+};
+
+// Byte-wise c - o for bytes c < 128 and 0 <= o <= 128: no borrow crosses a
+// byte, and the result bytes are the two's-complement differences.
+NQ_HD uint32_t bsub(uint32_t c, uint32_t o) { return ((c | 0x80808080u) - o) ^ 0x80808080u; }
+
+// Span p of the block at byte offset bo.
+template <int F, class Src>
+NQ_HD void gm_span(const Src &s, uint32_t bo, uint32_t p, const Tab &tab, GmSpan &o) {
+    constexpr uint32_t LO4 = 0x0F0F0F0Fu;
+    o.ow[0] = o.ow[1] = 0.0f;
+    if constexpr (F == Q4_K || F == Q5_K) {
+        // sub-block p: nibble plane p mod 2 of the 32 code bytes of pair p / 2
+        // (q4_k at 16, q5_k at 48), q5_k's fifth bit from bit p of bytes 16..47;
+        // w = RN32(d * sc) * v - RN32(dmin * m)
+        uint32_t h[4], q[8];
+        window<4>(s, bo, h);
+        window<8>(s, bo + (F == Q4_K ? 16u : 48u) + 32u * (p >> 1), q);
+        const float d = f16(h[0] & 0xFFFFu), dmin = f16(h[0] >> 16);
+        const uint32_t hs[3] = {h[1], h[2], h[3]};
+        uint32_t sc, mn;
+        kq_scale_min(hs, p, &sc, &mn);
+        o.ws[0] = o.ws[1] = M(d, (float)sc);
+        o.ow[0] = o.ow[1] = -M(dmin, (float)mn);
+        const uint32_t sh = 4u * (p & 1u);
+        if constexpr (F == Q4_K) {
+#pragma unroll
+            for (int j = 0; j < 8; j++) o.c[j] = (q[j] >> sh) & LO4;
+        } else {
+            uint32_t qh[8];
+            window<8>(s, bo + 16u, qh);
+#pragma unroll
+            for (int j = 0; j < 8; j++) o.c[j] = ((q[j] >> sh) & LO4) | (((qh[j] >> p) & 0x01010101u) << 4);
+        }
+    } else if constexpr (F == Q6_K) {
+        // values 32p + i: with h = p / 4, c = p mod 4, the low 4 bits are
+        // nibble c / 2 of byte 64h + 32(c mod 2) + i, the high 2 bits bits 2c
+        // of byte 128 + 32h + i; the 16-value sub-blocks 2p and 2p + 1 take the
+        // signed scale bytes 192 + 2p and 193 + 2p; w = RN32(d * sc) * (v - 32)
+        const uint32_t hh = p >> 2, c = p & 3u;
+        uint32_t ql[8], qh[8];
+        window<8>(s, bo + 64u * hh + 32u * (c & 1u), ql);
+        window<8>(s, bo + 128u + 32u * hh, qh);
+        const uint32_t sw = u16_at(s, bo + 192u + 2u * p);
+        const float d = f16(u16_at(s, bo + 208u));
+        o.ws[0] = M(d, (float)(int8_t)(sw & 0xFFu));
+        o.ws[1] = M(d, (float)(int8_t)(sw >> 8));
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            o.c[j] = bsub(((ql[j] >> (4u * (c >> 1))) & LO4) | (((qh[j] >> (2u * c)) & 0x03030303u) << 4), 0x20202020u);
+    } else {
+        // the single-row kernel's item p (whole span), then its codes made
+        // signed and its scales and offsets sorted into halves
+        GvW w;
+        gv_w<F>(s, bo, p, tab, w);
+        if constexpr (F == Q8_0 || F == Q8_1 || F == Q8_K || F == IQ4_NL || F == MXFP4 || F == IQ4_XS) {
+#pragma unroll
+            for (int j = 0; j < 8; j++) o.c[j] = w.q[j];
+            o.ws[0] = o.ws[1] = w.f[0];
+        } else if constexpr (F == Q4_0) {
+            // codes v - 8 (the low nibbles first, then the high)
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                o.c[j] = bsub(w.q[j] & LO4, 0x08080808u);
+                o.c[4 + j] = bsub((w.q[j] >> 4) & LO4, 0x08080808u);
+            }
+            o.ws[0] = o.ws[1] = w.f[0];
+        } else if constexpr (F == Q4_1 || F == Q5_1) {
+            // w = d * v + m
+#pragma unroll
+            for (int j = 0; j < 8; j++) o.c[j] = w.q[j];
+            o.ws[0] = o.ws[1] = w.f[0];
+            o.ow[0] = o.ow[1] = w.f[1];
+        } else if constexpr (F == Q5_0 || F == TQ2_0 || F == Q2_0 || F == Q3_K) {
+            // w = scale * (v - o), o = 16, 1, 1, 4
+            constexpr uint32_t O = F == Q5_0 ? 0x10101010u : F == Q3_K ? 0x04040404u : 0x01010101u;
+#pragma unroll
+            for (int j = 0; j < 8; j++) o.c[j] = bsub(w.q[j], O);
+            o.ws[0] = w.f[0];
+            o.ws[1] = F == Q3_K ? w.f[1] : w.f[0];
+        } else if constexpr (F == Q1_0) {
+            // code 2b - 1: byte 0xFF - 0xFE b
+#pragma unroll
+            for (int j = 0; j < 8; j++) o.c[j] = ~(w.q[j] * 0xFEu);
+            o.ws[0] = o.ws[1] = w.f[0];
+        } else if constexpr (F == Q2_K) {
+            // two sub-blocks: w = RN32(d * s) * v - RN32(dmin * m)
+#pragma unroll
+            for (int j = 0; j < 8; j++) o.c[j] = w.q[j];
+            o.ws[0] = w.f[0];
+            o.ow[0] = -w.f[1];
+            o.ws[1] = w.f[2];
+            o.ow[1] = -w.f[3];
+        } else if constexpr (F == NVFP4_GGUF) {
+            // two 16-value groups, doubled E2M1 codes, half scales
+#pragma unroll
+            for (int j = 0; j < 8; j++) o.c[j] = w.q[j];
+            o.ws[0] = w.f[0];
+            o.ws[1] = w.f[1];
+        } else if constexpr (F == IQ2_XXS || F == IQ3_XXS || F == IQ3_S || F == IQ2_XS || F == IQ2_S) {
+            // grid bytes g (< 128) and the bytes n = g under the negative
+            // signs: the signed value is g where n = 0 and -g where n = g
+#pragma unroll
+            for (int j = 0; j < 8; j++) o.c[j] = (w.q[j] ^ w.q[8 + j]) | bsub(0u, w.q[8 + j]);
+            o.ws[0] = w.f[0];
+            o.ws[1] = F == IQ2_XS || F == IQ2_S ? w.f[1] : w.f[0];
+        } else if constexpr (F == IQ1_S || F == IQ1_M) {
+            // grid bytes hold v + 1 (v in -1, 0, 1); w = scale * (v + delta),
+            // delta = +-1/8: codes 8v + 8 delta = 8 g - 8 + 8 delta, scale / 8
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const float dl = F == IQ1_S ? w.f[1] : w.f[2 + (j >> 1)];
+                o.c[j] = bsub(w.q[j] << 3, dl < 0.0f ? 0x09090909u : 0x07070707u);
+            }
+            o.ws[0] = M(w.f[0], 0.125f);
+            o.ws[1] = F == IQ1_M ? M(w.f[1], 0.125f) : o.ws[0];
+        } else {
+            static_assert(F < 0, "format without a span rewrite");
+        }
+    }
+}
+
+// Workgroup id -> (weight tile, activation tile): ids go to the XCDs in turn
+// (id mod 8); each XCD's ids take a contiguous range of tile numbers, and
+// tile numbers run over activation tiles first, so the tiles of one group of
+// weight rows fall on one XCD.  A bijection of [0, grid).
+NQ_HD void gm_tile(const GmArgs &a, uint32_t id, uint32_t *n0, uint32_t *m0) {
+    const uint32_t x = id & 7u, j = id >> 3;
+    const uint32_t L = (x < a.xr8 ? x * (a.xq8 + 1u) : a.xr8 * (a.xq8 + 1u) + (x - a.xr8) * a.xq8) + j;
+    *m0 = (L % a.mt) * GM_BM;
+    *n0 = (L / a.mt) * GM_BN;
+}
+
+// K step: the spans t0 .. t0+7 of weight rows n0 .. n0+127, rewritten into
+// LDS, strided over the workgroup's threads (rows past the launch and spans
+// past K are zeros).
+template <int F, class Src>
+NQ_HD void gm_stage_w(const GmArgs &a, const Src &src, const Tab &tab, uint32_t n0, uint32_t t0, uint32_t tid,
+                      uint32_t *lds) {
+    using G = GmFmt<F>;
+    constexpr uint32_t S = (uint32_t)block_bytes(F);
+    for (uint32_t i = tid; i < GM_BN * GM_SP; i += WG) {
+        const uint32_t n = i / GM_SP, sp = i % GM_SP, t = t0 + sp;
+        GmSpan o;
+        if (n0 + n < a.rows && t < a.kspans) {
+            const uint32_t b = t / G::SPB;
+            gm_span<F>(src, a.wmis + (n0 + n) * a.row_bytes + b * S, t - b * G::SPB, tab, o);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; j++) o.c[j] = 0u;
+            o.ws[0] = o.ws[1] = o.ow[0] = o.ow[1] = 0.0f;
+        }
+        uint32_t *cw = lds + n * GM_CSW + 8u * sp;
+#pragma unroll
+        for (int j = 0; j < 8; j++) cw[j] = o.c[j];
+        float *ws = (float *)(lds + G::WS), *ow = (float *)(lds + G::WO);
+#pragma unroll
+        for (uint32_t h = 0; h < G::NH; h++) {
+            ws[(sp * G::NH + h) * GM_BN + n] = o.ws[h];
+            if constexpr (G::AFF) ow[(sp * G::NH + h) * GM_BN + n] = o.ow[h];
+        }
+    }
+}
+
+// K step, activation side: blocks t0 .. t0+7 of activation rows m0 .. m0+63
+// (codes, binary32 scale, and for the affine formats d times the exact code
+// sum of each half), strided over the workgroup's threads.
+template <int F>
+NQ_HD void gm_stage_x(const GmArgs &a, uint32_t m0, uint32_t t0, uint32_t tid, uint32_t *lds) {
+    using G = GmFmt<F>;
+    for (uint32_t i = tid; i < GM_BM * GM_SP; i += WG) {
+        const uint32_t m = i / GM_SP, sp = i % GM_SP, t = t0 + sp;
+        uint32_t c[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        float d = 0.0f;
+        if (m0 + m < a.M && t < a.kspans) {
+            const uint32_t *p = a.xq + (uint64_t)(m0 + m) * a.xrow + (uint64_t)t * 9u;
+            const u32x4a4 v0 = *(const u32x4a4 *)(p + 1), v1 = *(const u32x4a4 *)(p + 5);
+            c[0] = v0.x; c[1] = v0.y; c[2] = v0.z; c[3] = v0.w;
+            c[4] = v1.x; c[5] = v1.y; c[6] = v1.z; c[7] = v1.w;
+            d = f16(p[0] & 0xFFFFu);
+        }
+        uint32_t *cx = lds + G::XC + m * GM_CSW + 8u * sp;
+#pragma unroll
+        for (int j = 0; j < 8; j++) cx[j] = c[j];
+        ((float *)(lds + G::XD))[sp * GM_BM + m] = d;
+        if constexpr (G::AFF) {
+            int S0 = 0, S1 = 0;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                S0 = dot4(ONES8, c[j], S0);
+                S1 = dot4(ONES8, c[4 + j], S1);
+            }
+            float *xt = (float *)(lds + G::XT);
+            if constexpr (G::U16) {
+                xt[(2u * sp) * GM_BM + m] = d * (float)S0;
+                xt[(2u * sp + 1u) * GM_BM + m] = d * (float)S1;
+            } else {
+                xt[sp * GM_BM + m] = d * (float)(S0 + S1);
+            }
+        }
+    }
+}
+
+// MFMA operands of span sp for a lane of wave w (sub-tile: weight rows
+// 64 (w mod 2) + 16 i + .., activation rows 32 (w / 2) + 16 j + ..): the
+// lane supplies row lane mod 16 of each 16-row group, code bytes
+// 8 (lane / 16) .. + 7 of the span.
+struct GmOps {
+    uint64_t A[4];  // weight rows
+    uint64_t B[2];  // activation rows
+};
+
+NQ_HD uint64_t lds_u64(const uint32_t *p) { return (uint64_t)p[0] | ((uint64_t)p[1] << 32); }
+
+template <int F>
+NQ_HD void gm_ops(const uint32_t *lds, uint32_t w, uint32_t lane, uint32_t sp, GmOps &o) {
+    using G = GmFmt<F>;
+    const uint32_t r = lane & 15u, k = 8u * sp + 2u * (lane >> 4);
+    const uint32_t nb = 64u * (w & 1u), mb = 32u * (w >> 1);
+#pragma unroll
+    for (int i = 0; i < 4; i++) o.A[i] = lds_u64(lds + (nb + 16u * (uint32_t)i + r) * GM_CSW + k);
+#pragma unroll
+    for (int j = 0; j < 2; j++) o.B[j] = lds_u64(lds + G::XC + (mb + 16u * (uint32_t)j + r) * GM_CSW + k);
+}
+
+// Activation operand for half h of a span with 16-value scales: lanes 0-31
+// hold code bytes 0-15, lanes 32-63 bytes 16-31; the other half is zeroed.
+template <int F>
+NQ_HD uint64_t gm_half(uint64_t b, uint32_t lane, uint32_t h) {
+    if constexpr (GmFmt<F>::U16)
+        return (lane >> 5) == h ? b : 0ull;
+    else
+        return b;
+}
+
+// Integer results of a span for one lane: I[h][i][j][e] is the dot product of
+// weight row 64 (w mod 2) + 16 i + 4 (lane / 16) + e with activation row
+// 32 (w / 2) + 16 j + lane mod 16 over half h (or the whole span).
+template <int F>
+struct GmI {
+    int v[GmFmt<F>::NH][4][2][4];
+};
+
+// The span's scaling into the lane's accumulators (fixed order: per output,
+// the halves, then the offsets).
+template <int F>
+NQ_HD void gm_epi(const uint32_t *lds, uint32_t w, uint32_t lane, uint32_t sp, const GmI<F> &I,
+                  float (&acc)[4][2][4]) {
+    using G = GmFmt<F>;
+    const uint32_t nb = 64u * (w & 1u) + 4u * (lane >> 4), mb = 32u * (w >> 1) + (lane & 15u);
+    const float *ws = (const float *)(lds + G::WS), *ow = (const float *)(lds + G::WO);
+    const float *xd = (const float *)(lds + G::XD), *xt = (const float *)(lds + G::XT);
+    float d[2], T[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        d[j] = xd[sp * GM_BM + mb + 16u * (uint32_t)j];
+#pragma unroll
+        for (uint32_t h = 0; h < G::NH; h++)
+            T[h][j] = G::AFF ? xt[(sp * G::NH + h) * GM_BM + mb + 16u * (uint32_t)j] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        float sw[2][4], so[2][4];
+#pragma unroll
+        for (uint32_t h = 0; h < G::NH; h++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const uint32_t n = (sp * G::NH + h) * GM_BN + nb + 16u * (uint32_t)i + (uint32_t)e;
+                sw[h][e] = ws[n];
+                so[h][e] = G::AFF ? ow[n] : 0.0f;
+            }
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                float a = acc[i][j][e];
+#pragma unroll
+                for (uint32_t h = 0; h < G::NH; h++) a = __builtin_fmaf(sw[h][e] * d[j], (float)I.v[h][i][j][e], a);
+                if constexpr (G::AFF) {
+#pragma unroll
+                    for (uint32_t h = 0; h < G::NH; h++) a = __builtin_fmaf(so[h][e], T[h][j], a);
+                }
+                acc[i][j][e] = a;
+            }
+    }
+}
+
+// The lane's outputs: y[m][n] for its 4 x 2 x 4 (row, activation row) pairs
+// inside the launch.
+NQ_HD void gm_store(const GmArgs &a, uint32_t n0, uint32_t m0, uint32_t w, uint32_t lane,
+                    const float (&acc)[4][2][4]) {
+    const uint32_t nb = n0 + 64u * (w & 1u) + 4u * (lane >> 4), mb = m0 + 32u * (w >> 1) + (lane & 15u);
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const uint32_t m = mb + 16u * (uint32_t)j;
+        if (m >= a.M) continue;
+        float *yr = a.y + (uint64_t)m * a.ldy;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const uint32_t n = nb + 16u * (uint32_t)i + (uint32_t)e;
+                if (n < a.rows) yr[n] = acc[i][j][e];
+            }
+    }
+}
+
+typedef int gm_i32x4 __attribute__((ext_vector_type(4)));
+
+template <int F>
+__global__ __launch_bounds__(WG) void k_gemm(GmArgs a) {
+    using G = GmFmt<F>;
+    using TS = TabSpec<F>;
+    __shared__ uint64_t t8[TS::n8 > 0 ? TS::n8 : 1];
+    __shared__ uint32_t t4[TS::n4 > 0 ? TS::n4 : 1];
+    __shared__ __attribute__((aligned(16))) uint32_t lds[G::DW];
+    if constexpr (TS::n8 + TS::n4 > 0) gv_fill_tables<F>(t8, t4, threadIdx.x);
+    const Tab tab{t8, t4, nullptr, nullptr, 0xFFFFFFFFu, 1u};
+    const GmSrc src{a.wbase, a.wlast};
+    uint32_t n0, m0;
+    gm_tile(a, blockIdx.x, &n0, &m0);
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t w = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    float acc[4][2][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) acc[i][j][e] = 0.0f;
+    for (uint32_t t0 = 0; t0 < a.kspans; t0 += GM_SP) {
+        __syncthreads();  // the previous step's readers are done (and the tables are filled)
+        gm_stage_w<F>(a, src, tab, n0, t0, threadIdx.x, lds);
+        gm_stage_x<F>(a, m0, t0, threadIdx.x, lds);
+        __syncthreads();
+        const uint32_t nsp = a.kspans - t0 < GM_SP ? a.kspans - t0 : GM_SP;
+        for (uint32_t sp = 0; sp < nsp; sp++) {
+            GmOps o;
+            gm_ops<F>(lds, w, lane, sp, o);
+            GmI<F> I;
+#pragma unroll
+            for (uint32_t h = 0; h < G::NH; h++)
+#pragma unroll
+                for (int j = 0; j < 2; j++) {
+                    const uint64_t b = gm_half<F>(o.B[j], lane, h);
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const gm_i32x4 z = {0, 0, 0, 0};
+                        const gm_i32x4 r = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)o.A[i], (long)b, z, 0, 0, 0);
+#pragma unroll
+                        for (int e = 0; e < 4; e++) I.v[h][i][j][e] = r[e];
+                    }
+                }
+            gm_epi<F>(lds, w, lane, sp, I, acc);
+        }
+    }
+    gm_store(a, n0, m0, w, lane, acc);
+}
+
+// ------------------------------------------------------------------ host side
+
+template <int F>
+GmArgs gm_args(const GvLaunch &L, uint64_t r0, uint64_t rows, uint64_t m0, uint64_t mrows) {
+    constexpr uint64_t S = (uint64_t)block_bytes(F);
+    const uint64_t nbr = L.K / (uint64_t)block_values(F), row_bytes = nbr * S;
+    const uint8_t *start = L.w + r0 * row_bytes;
+    GmArgs a;
+    a.wbase = (const uint32_t *)((uintptr_t)start & ~(uintptr_t)3);
+    a.wmis = (uint32_t)((uintptr_t)start & 3u);
+    a.wlast = (uint32_t)((a.wmis + rows * row_bytes - 1) / 4);
+    a.xq = (const uint32_t *)L.xq + m0 * (L.K / 32 * 9);
+    a.y = L.y + m0 * L.N + r0;
+    a.rows = (uint32_t)rows;
+    a.row_bytes = (uint32_t)row_bytes;
+    a.kspans = (uint32_t)(L.K / 32);
+    a.xrow = (uint32_t)(L.K / 32 * 9);
+    a.ldy = (uint32_t)L.N;
+    a.M = (uint32_t)mrows;
+    a.mt = (uint32_t)((mrows + GM_BM - 1) / GM_BM);
+    const uint64_t grid = (rows + GM_BN - 1) / GM_BN * a.mt;
+    a.xq8 = (uint32_t)(grid / 8);
+    a.xr8 = (uint32_t)(grid % 8);
+    return a;
+}
+
+inline uint32_t gm_grid(const GmArgs &a) { return 8u * a.xq8 + a.xr8; }
+
+// Weight rows per launch: byte offsets fit 32 bits, whole tiles when more
+// than one, and at most 2^24 rows (the grid stays below 2^31).
+template <int F>
+uint64_t gm_max_rows(const GvLaunch &L) {
+    uint64_t r = gv_max_rows<F>(L);
+    if (r > (1ull << 24)) r = 1ull << 24;
+    return r >= GM_BN ? r / GM_BN * GM_BN : r;
+}
+
+template <int F>
+int launch_gemm_mfma(const GvLaunch &L, hipStream_t stream) {
+    const uint64_t max_rows = gm_max_rows<F>(L);
+    for (uint64_t m0 = 0; m0 < L.M; m0 += GM_MAX_MROWS) {
+        const uint64_t mrows = L.M - m0 < GM_MAX_MROWS ? L.M - m0 : GM_MAX_MROWS;
+        for (uint64_t r0 = 0; r0 < L.N;) {
+            const uint64_t rows = L.N - r0 < max_rows ? L.N - r0 : max_rows;
+            const GmArgs a = gm_args<F>(L, r0, rows, m0, mrows);
+            hipLaunchKernelGGL((k_gemm<F>), dim3(gm_grid(a)), dim3(WG), 0, stream, a);
+            if (hipGetLastError() != hipSuccess) return 9;  // NQ_ERR_HIP
+            r0 += rows;
+        }
+    }
+    return 0;
+}
+
+// Products with more than 8 activation rows on the matrix cores (formats
+// with a span rewrite; the others, and fewer rows, go through the
+// single-row kernel).
+template <int F>
+int launch_gemm_f(const GvLaunch &L, hipStream_t stream) {
+    if constexpr (GmFmt<F>::OK)
+        return launch_gemm_mfma<F>(L, stream);
+    else
+        return 2;  // NQ_ERR_UNKNOWN_FORMAT
+}
+
+}  // namespace nq

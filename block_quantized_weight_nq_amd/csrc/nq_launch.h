@@ -1,7 +1,7 @@
 // nq_launch.h -- internal: per-family launch entry points.
 #pragma once
 #include <hip/hip_runtime.h>
-#include "nq_gemv.h"
+#include "nq_gemm.h"
 #include "nq_kernel.h"
 
 namespace nq {
@@ -14,5 +14,9 @@ int launch_gemv_simple(int fmt, const GvLaunch &L, hipStream_t s);
 int launch_gemv_kquant(int fmt, const GvLaunch &L, hipStream_t s);
 int launch_gemv_iq(int fmt, const GvLaunch &L, hipStream_t s);
 int launch_gemv_fp4t(int fmt, const GvLaunch &L, hipStream_t s);
+int launch_gemm_simple(int fmt, const GvLaunch &L, hipStream_t s);
+int launch_gemm_kquant(int fmt, const GvLaunch &L, hipStream_t s);
+int launch_gemm_iq(int fmt, const GvLaunch &L, hipStream_t s);
+int launch_gemm_fp4t(int fmt, const GvLaunch &L, hipStream_t s);
 int launch_quantize_q8_1(int in_dtype, const Q81Launch &L, hipStream_t s);
 }  // namespace nq

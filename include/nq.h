@@ -248,6 +248,24 @@ int nq_validate_gemv_q8_1(int32_t format, uint64_t nbytes, int64_t N, int64_t K,
 int nq_gemv_q8_1(int32_t format, const void *weight, uint64_t nbytes, int64_t N, int64_t K, const void *xq,
                  int64_t M, float *y, hipStream_t stream);
 
+/* nq_gemm_q8_1: the same product for any number of activation rows M >= 1
+ * (the page's GGUF linear operation over a batch), with the same argument
+ * meaning, layouts, criterion and determinism.  Up to 8 rows it makes the
+ * launches nq_gemv_q8_1 makes (identical bits); with more rows every 32
+ * weight values become signed 8-bit codes with a binary32 scale (and an
+ * offset for q4_1, q5_1, q2_k, q4_k and q5_k), their exact integer dot
+ * products with the activation codes come from the 8-bit matrix cores, and
+ * each is scaled and added in binary32 (gguf:tq1_0 runs through the
+ * single-row kernel, 8 activation rows per launch).
+ * nq_validate_gemm_q8_1 checks as nq_validate_gemv_q8_1 except that M may
+ * be any count >= 1 with M * K / 32 * 36 and M * N representable
+ * (NQ_ERR_OVERFLOW).  nq_gemm_q8_1 requires weight, xq and y non-NULL and
+ * xq and y aligned to 4 bytes (NQ_ERR_NULL_ARG), then enqueues the product on
+ * `stream`.  The caller owns every buffer; y must not overlap the inputs. */
+int nq_validate_gemm_q8_1(int32_t format, uint64_t nbytes, int64_t N, int64_t K, int64_t M);
+int nq_gemm_q8_1(int32_t format, const void *weight, uint64_t nbytes, int64_t N, int64_t K, const void *xq,
+                 int64_t M, float *y, hipStream_t stream);
+
 /* Static description of a status code. */
 const char *nq_status_string(int status);
 

@@ -17,7 +17,7 @@
 #include <vector>
 
 #include "../../block_quantized_weight_nq_amd/csrc/nq_fp8row.h"
-#include "../../block_quantized_weight_nq_amd/csrc/nq_gemv.h"
+#include "../../block_quantized_weight_nq_amd/csrc/nq_gemm.h"
 #include "../../block_quantized_weight_nq_amd/csrc/nq_gqenc.h"
 #include "../../block_quantized_weight_nq_amd/csrc/nq_kernel.h"
 
@@ -332,6 +332,116 @@ long run_gemv_m(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uin
     return run_gemv<F, 8>(w, N, K, xq, M, y, res, max_rows, err, errlen);
 }
 
+// The 16 x 16 x 32 8-bit matrix instruction of one wave: lane l supplies row
+// l mod 16 of A and column l mod 16 of B, code bytes k = 8 (l / 16) .. + 7 of
+// each; lane l receives D[4 (l / 16) + e][l mod 16], e = 0..3.
+void mfma_i8_16x16x32(const uint64_t (&A)[64], const uint64_t (&B)[64], int (&D)[64][4]) {
+    int a[16][32], b[32][16];
+    for (int l = 0; l < 64; l++)
+        for (int t = 0; t < 8; t++) {
+            a[l % 16][8 * (l / 16) + t] = (int)(int8_t)(uint8_t)(A[l] >> (8 * t));
+            b[8 * (l / 16) + t][l % 16] = (int)(int8_t)(uint8_t)(B[l] >> (8 * t));
+        }
+    for (int l = 0; l < 64; l++)
+        for (int e = 0; e < 4; e++) {
+            const int i = 4 * (l / 16) + e, j = l % 16;
+            int sum = 0;
+            for (int k = 0; k < 32; k++) sum += a[i][k] * b[k][j];
+            D[l][e] = sum;
+        }
+}
+
+// Batched product on the matrix cores: the launcher's launches (max_rows /
+// max_mrows > 0 override its weight-row and activation-row limits), and per
+// launch every workgroup of the grid as the kernel runs it: its tile (each
+// tile must be met exactly once), per K step the threads' staging into a
+// poisoned LDS image (weight reads through a bounds-checked source), then per
+// span and wave the lanes' operands, the matrix instruction and the lanes'
+// scaling, and at the end the lanes' stores.
+template <int F>
+long run_gemm(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y, uint64_t max_rows,
+              uint64_t max_mrows, char *err, int errlen) {
+    using namespace nq;
+    using G = GmFmt<F>;
+    const GvLaunch L{w, N, K, M, xq, y, 0u};
+    const uint64_t lim = max_rows ? max_rows : gm_max_rows<F>(L);
+    const uint64_t mlim = max_mrows ? max_mrows : GM_MAX_MROWS;
+    const uint64_t row_bytes = K / (uint64_t)block_values(F) * (uint64_t)block_bytes(F);
+    std::vector<uint64_t> t8(TabSpec<F>::n8 > 0 ? TabSpec<F>::n8 : 1);
+    std::vector<uint32_t> t4(TabSpec<F>::n4 > 0 ? TabSpec<F>::n4 : 1);
+    for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) gv_fill_tables<F>(t8.data(), t4.data(), tid);
+    const Tab tab{t8.data(), t4.data(), nullptr, nullptr, 0xFFFFFFFFu, 1u};
+    std::vector<uint32_t> lds(G::DW);
+    static float acc[4][64][4][2][4];
+    static GmOps ops[64];
+    static GmI<F> I[64];
+    long errors = 0;
+    for (uint64_t m0 = 0; m0 < M; m0 += mlim) {
+        const uint64_t mrows = M - m0 < mlim ? M - m0 : mlim;
+        for (uint64_t r0 = 0; r0 < N;) {
+            const uint64_t rows = N - r0 < lim ? N - r0 : lim;
+            const GmArgs a = gm_args<F>(L, r0, rows, m0, mrows);
+            Check chk{(uintptr_t)(w + r0 * row_bytes), (uintptr_t)(w + (r0 + rows) * row_bytes), 0, {0}};
+            const HostSrc src{a.wbase, a.wlast, &chk};
+            const uint32_t grid = gm_grid(a);
+            const uint32_t nt = (uint32_t)((rows + GM_BN - 1) / GM_BN);
+            if ((uint64_t)grid != (uint64_t)nt * a.mt) {
+                snprintf(err, errlen, "grid %u for %u x %u tiles", grid, nt, a.mt);
+                return 1;
+            }
+            std::vector<char> seen(grid, 0);
+            for (uint32_t id = 0; id < grid; id++) {
+                uint32_t n0, mt0;
+                gm_tile(a, id, &n0, &mt0);
+                const uint64_t tile = (uint64_t)(n0 / GM_BN) * a.mt + mt0 / GM_BM;
+                if (n0 % GM_BN || mt0 % GM_BM || tile >= grid || seen[tile]++) {
+                    snprintf(err, errlen, "workgroup %u: tile (%u, %u) out of range or met twice", id, n0, mt0);
+                    return 1;
+                }
+                for (auto &wv : acc)
+                    for (auto &ln : wv)
+                        for (auto &i4 : ln)
+                            for (auto &j2 : i4)
+                                for (float &v : j2) v = 0.0f;
+                for (uint32_t t0 = 0; t0 < a.kspans; t0 += GM_SP) {
+                    std::fill(lds.begin(), lds.end(), 0xA5A5A5A5u);
+                    for (uint32_t tid = 0; tid < (uint32_t)WG; tid++)
+                        gm_stage_w<F>(a, src, tab, n0, t0, tid, lds.data());
+                    for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) gm_stage_x<F>(a, mt0, t0, tid, lds.data());
+                    const uint32_t nsp = a.kspans - t0 < GM_SP ? a.kspans - t0 : GM_SP;
+                    for (uint32_t sp = 0; sp < nsp; sp++)
+                        for (uint32_t wv = 0; wv < 4u; wv++) {
+                            for (uint32_t lane = 0; lane < 64u; lane++) gm_ops<F>(lds.data(), wv, lane, sp, ops[lane]);
+                            for (uint32_t h = 0; h < G::NH; h++)
+                                for (int j = 0; j < 2; j++)
+                                    for (int i = 0; i < 4; i++) {
+                                        uint64_t A[64], B[64];
+                                        int D[64][4];
+                                        for (uint32_t l = 0; l < 64u; l++) {
+                                            A[l] = ops[l].A[i];
+                                            B[l] = gm_half<F>(ops[l].B[j], l, h);
+                                        }
+                                        mfma_i8_16x16x32(A, B, D);
+                                        for (int l = 0; l < 64; l++)
+                                            for (int e = 0; e < 4; e++) I[l].v[h][i][j][e] = D[l][e];
+                                    }
+                            for (uint32_t lane = 0; lane < 64u; lane++)
+                                gm_epi<F>(lds.data(), wv, lane, sp, I[lane], acc[wv][lane]);
+                        }
+                }
+                for (uint32_t wv = 0; wv < 4u; wv++)
+                    for (uint32_t lane = 0; lane < 64u; lane++) gm_store(a, n0, mt0, wv, lane, acc[wv][lane]);
+            }
+            if (chk.errors) {
+                if (errors == 0) snprintf(err, errlen, "%s", chk.msg);
+                errors += chk.errors;
+            }
+            r0 += rows;
+        }
+    }
+    return errors;
+}
+
 }  // namespace
 
 using EmuRun = long (*)(int ot, const uint8_t *payload, uint64_t nbytes, uint64_t nblocks, void *out,
@@ -340,6 +450,9 @@ extern EmuRun nq_emu_table[nq::NUM_FORMATS];
 using EmuGemv = long (*)(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y,
                          uint32_t resident, uint64_t max_rows, char *err, int errlen);
 extern EmuGemv nq_emu_gemv_table[nq::NUM_FORMATS];
+using EmuGemm = long (*)(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y,
+                         uint64_t max_rows, uint64_t max_mrows, char *err, int errlen);
+extern EmuGemm nq_emu_gemm_table[nq::NUM_FORMATS];
 
 #if defined(NQ_EMU_PART)
 namespace {
@@ -348,6 +461,7 @@ void reg() {
     if constexpr (F % NQ_EMU_PARTS == NQ_EMU_PART) {
         nq_emu_table[F] = &run_ot<F>;
         if constexpr (F != nq::NVFP4_DIV) nq_emu_gemv_table[F] = &run_gemv_m<F>;
+        if constexpr (nq::GmFmt<F>::OK) nq_emu_gemm_table[F] = &run_gemm<F>;
     }
 }
 struct Register {
@@ -363,6 +477,18 @@ struct Register {
 #else
 EmuRun nq_emu_table[nq::NUM_FORMATS];
 EmuGemv nq_emu_gemv_table[nq::NUM_FORMATS];
+EmuGemm nq_emu_gemm_table[nq::NUM_FORMATS];
+
+// Batched product on the matrix cores through the kernel's lane code;
+// returns out-of-payload weight reads (0 on success), or -1 for a format
+// without a span rewrite.
+extern "C" __attribute__((visibility("default"))) long nq_emu_gemm_q8_1(int fmt, const uint8_t *w, uint64_t N,
+                                                                       uint64_t K, const uint8_t *xq, uint64_t M,
+                                                                       float *y, uint64_t max_rows,
+                                                                       uint64_t max_mrows, char *err, int errlen) {
+    if (fmt < 0 || fmt >= nq::NUM_FORMATS || !nq_emu_gemm_table[fmt]) return -1;
+    return nq_emu_gemm_table[fmt](w, N, K, xq, M, y, max_rows, max_mrows, err, errlen);
+}
 
 // Product with q8_1 activations through the kernel's lane code; returns
 // out-of-payload weight reads (0 on success), or -1 for a format without one.

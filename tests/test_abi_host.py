@@ -259,3 +259,37 @@ def test_gemv_rejects_before_device():
     assert nq.gemv_q8_1_raw(q8, p, 34, 1, 32, p + 2, 1, p, 0) == 1   # activation blocks misaligned
     assert nq.gemv_q8_1_raw(q8, p, 34, 1, 32, p, 1, p + 2, 0) == 1   # output misaligned
     assert nq.gemv_q8_1_raw(q8, p, 35, 1, 32, p, 1, p, 0) == 6
+
+
+@pytest.mark.parametrize("fmt", ["gguf:q8_0", "gguf:q4_k", "gguf:iq2_xxs", "gguf:tq1_0", "gguf:nvfp4"])
+def test_gemm_validation(fmt):
+    """The batched product takes any M >= 1 and otherwise checks as the
+    single-row product."""
+    _, B, S, _ = oracle.info(fmt)
+    N, K = 3, 2 * B
+    for M in (1, 8, 9, 64, 5000):
+        assert nq.validate_gemm_q8_1_status(fmt, N * 2 * S, N, K, M) == 0
+    assert nq.validate_gemm_q8_1_status(fmt, N * 2 * S, N, K, 0) == 4
+    assert nq.validate_gemm_q8_1_status(fmt, N * 2 * S, N, K, -1) == 4
+    assert nq.validate_gemm_q8_1_status(fmt, N * 2 * S + 1, N, K, 9) == 6
+    assert nq.validate_gemm_q8_1_status(fmt, 0, 0, K, 9) == 4
+    assert nq.validate_gemm_q8_1_status(fmt, N * 2 * S, N, K + 32 if B > 32 else K + 16, 9) == 5
+    assert nq.validate_gemm_q8_1_status(fmt, N * 2 * S, N, K, 1 << 31) == 7
+
+
+def test_gemm_rejects_before_device():
+    buf = np.zeros(256, dtype=np.uint32)
+    p = buf.ctypes.data
+    q8 = nq.format_query("gguf:q8_0").id
+    assert nq.validate_gemm_q8_1_status("nvfp4", 40, 1, 64, 9) == 2
+    assert nq.validate_gemm_q8_1_status(99, 34, 1, 32, 9) == 2
+    assert nq.validate_gemm_q8_1_status(q8, 34 << 31, 1 << 31, 32, 9) == 7
+    # output bytes M * N * 4 past 2^63 - 1, then just below
+    assert nq.validate_gemm_q8_1_status(q8, 34 * ((1 << 31) - 1), (1 << 31) - 1, 32, (1 << 31) - 1) == 7
+    assert nq.validate_gemm_q8_1_status(q8, 34 * ((1 << 31) - 1), (1 << 31) - 1, 32, 1 << 30) == 0
+    assert nq.gemm_q8_1_raw(q8, 0, 34, 1, 32, p, 9, p, 0) == 1
+    assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, 0, 9, p, 0) == 1
+    assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, p, 9, 0, 0) == 1
+    assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, p + 2, 9, p, 0) == 1   # activation blocks misaligned
+    assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, p, 9, p + 2, 0) == 1   # output misaligned
+    assert nq.gemm_q8_1_raw(q8, p, 35, 1, 32, p, 9, p, 0) == 6

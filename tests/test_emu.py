@@ -352,3 +352,56 @@ def test_emu_gemv_k_not_a_multiple_of_128(fmt, K):
     assert guards
     ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
     linear_check(y, ref, env, K, fmt)
+
+
+# --------------------------------------------------------------------------
+# Batched products on the matrix cores (more than 8 activation rows): the
+# workgroups' staging, the lanes' operands and scaling around an emulated
+# 16 x 16 x 32 8-bit matrix instruction, bounds-checked weight reads, every
+# tile met exactly once.
+# --------------------------------------------------------------------------
+GEMM_FMTS = [f for f in GGUF if f != "gguf:tq1_0"]
+
+
+def _gemm_k(B):
+    """K that leaves a partial last K step (256 values) where the block size allows."""
+    return 352 if B == 32 else 384 if B in (64, 128) else 768
+
+
+@pytest.mark.parametrize("fmt", GEMM_FMTS)
+def test_emu_gemm_matches_oracle(fmt):
+    idx, B, S, _ = oracle.info(fmt)
+    K = _gemm_k(B)
+    for N, M, w_mis, max_rows, max_mrows in [(150, 9, 0, 0, 0), (37, 70, 1, 0, 0), (260, 65, 3, 128, 0),
+                                             (130, 100, 2, 0, 40)]:
+        w = synth.payload(fmt, N * K // B, 7 + N, synth.binade(-6, -2, False))
+        _, xq = oracle.quantize_q8_1(_act(M, K, M).astype(np.float32))
+        y, rc, msg, guards = emu_lib.gemm_q8_1(idx, w, N, K, xq, M, w_mis=w_mis, max_rows=max_rows,
+                                               max_mrows=max_mrows)
+        assert rc == 0, msg
+        assert guards
+        ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
+        linear_check(y, ref, env, K, f"{fmt} N={N} M={M}")
+
+
+def test_emu_gemm_tile_order_covers_every_tile():
+    """Grids that are not multiples of the 8 XCDs: every tile once (checked by
+    the emulator) and the product right."""
+    fmt = "gguf:q8_0"
+    idx, B, S, _ = oracle.info(fmt)
+    K = 64
+    for N, M in [(1100, 200), (1025, 9), (129, 577)]:
+        w = synth.payload(fmt, N * K // B, N, synth.binade(-6, -2, True))
+        _, xq = oracle.quantize_q8_1(_act(M, K, 3).astype(np.float32))
+        y, rc, msg, guards = emu_lib.gemm_q8_1(idx, w, N, K, xq, M)
+        assert rc == 0, msg
+        assert guards
+        ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
+        linear_check(y, ref, env, K, f"{fmt} N={N} M={M}")
+
+
+def test_emu_gemm_has_no_tq1_0_rewrite():
+    """tq1_0 products take the single-row kernel (the entry point routes them)."""
+    y, rc, _, _ = emu_lib.gemm_q8_1(oracle.info("gguf:tq1_0")[0], np.zeros(54, np.uint8), 1, 256,
+                                    np.zeros(36 * 8 * 9, np.uint8), 9)
+    assert rc == -1

@@ -206,3 +206,91 @@ def test_gemv_k_not_a_multiple_of_128(fmt, K):
     announce(f"gemv {fmt} K={K}")
     y = _gemv(fmt, w, N, K, xq, 1)
     linear_check(y, ref, env, K, fmt)
+
+
+# --------------------------------------------------------------------------
+# Batched products (any number of activation rows; more than 8 on the matrix
+# cores, tq1_0 through the single-row kernel 8 rows at a time).
+# --------------------------------------------------------------------------
+def _gemm(fmt, w_np, N, K, xq_np, w_off=0, stream=None):
+    w, _keep = upload(w_np, w_off)
+    xq = torch.from_numpy(np.ascontiguousarray(xq_np)).cuda()
+    y = nq.gemm_q8_1(fmt, w, N, K, xq, stream=stream)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def _gemm_k(B):
+    """K that leaves a partial last K step (256 values) where the block size allows."""
+    return 352 if B == 32 else 384 if B in (64, 128) else 768
+
+
+@pytest.mark.parametrize("fmt", GGUF)
+def test_gemm_every_format(fmt):
+    _, B, _, _ = oracle.info(fmt)
+    K = _gemm_k(B)
+    for N, M, w_off in [(300, 70, 0), (37, 9, 1), (129, 130, 3)]:
+        w = _weights(fmt, N, K, 400 + M)
+        _, xq = oracle.quantize_q8_1(_act(M, K, M).astype(np.float32))
+        ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
+        announce(f"gemm {fmt} N={N} K={K} M={M} w_off={w_off}")
+        y = _gemm(fmt, w, N, K, xq, w_off)
+        linear_check(y, ref, env, K, f"{fmt} N={N} M={M} w_off={w_off}")
+
+
+@pytest.mark.parametrize("fmt", ["gguf:q4_k", "gguf:iq3_s", "gguf:q5_0", "gguf:tq1_0"])
+def test_gemm_up_to_8_rows_is_the_single_row_product(fmt):
+    _, B, _, _ = oracle.info(fmt)
+    N, K = 77, 2 * max(B, 256)
+    w = _weights(fmt, N, K, 5)
+    for M in (1, 3, 8):
+        _, xq = oracle.quantize_q8_1(_act(M, K, 40 + M).astype(np.float32))
+        announce(f"gemm vs gemv {fmt} M={M}")
+        a = _gemm(fmt, w, N, K, xq)
+        b = _gemv(fmt, w, N, K, xq)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", ["gguf:q4_k", "gguf:q6_k", "gguf:iq2_xxs", "gguf:q4_1"])
+def test_gemm_repeats_bit_for_bit_and_on_a_side_stream(fmt):
+    N, K, M = 300, 1024, 100
+    w = _weights(fmt, N, K, 8)
+    _, xq = oracle.quantize_q8_1(_act(M, K, 9).astype(np.float32))
+    announce(f"gemm repeat {fmt}")
+    a = _gemm(fmt, w, N, K, xq)
+    b = _gemm(fmt, w, N, K, xq)
+    c = _gemm(fmt, w, N, K, xq, stream=torch.cuda.Stream())
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert np.array_equal(a.view(np.uint32), c.view(np.uint32))
+
+
+GEMM_FULL = [("gguf:q4_k", 14336, 4096, 512), ("gguf:q8_0", 4096, 14336, 512), ("gguf:q6_k", 4096, 4096, 200),
+             ("gguf:iq4_xs", 14336, 4096, 64), ("gguf:iq2_xxs", 4096, 4096, 100), ("gguf:q2_k", 1024, 14336, 72)]
+
+
+@pytest.mark.parametrize("fmt,N,K,M", GEMM_FULL)
+def test_gemm_full_size_sampled_rows(fmt, N, K, M):
+    """Llama-3-8B-shaped weights with a batch of activation rows: every output
+    computed on the GPU, sampled weight rows (all activation rows) against the
+    oracle."""
+    w = _weights(fmt, N, K, 78)
+    _, xq = oracle.quantize_q8_1(_act(M, K, 2).astype(np.float32))
+    announce(f"gemm full {fmt} [{N}, {K}] x {M}")
+    y = _gemm(fmt, w, N, K, xq)
+    rng = np.random.default_rng(N + K + M)
+    rows = np.unique(np.r_[0, 127, 128, N - 1, rng.integers(0, N, size=36)])
+    sub = w.reshape(N, -1)[rows].ravel()
+    ref, env = oracle.gemv_q8_1(fmt, sub, rows.size, K, xq, M)
+    linear_check(y[:, rows], ref, env, K, fmt)
+    assert np.all(np.isfinite(y))
+
+
+def test_gemm_metadata_errors():
+    w = torch.zeros(34 * 4, dtype=torch.uint8, device="cuda:0")
+    xq = torch.zeros(36 * 9, dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(nq.NqError):
+        nq.gemm_q8_1("nvfp4", w, 1, 64, torch.zeros(72 * 9, dtype=torch.uint8, device="cuda:0"))
+    with pytest.raises(nq.NqError):
+        nq.gemm_q8_1("gguf:q8_0", w[:33], 1, 32, xq)       # payload short
+    with pytest.raises(nq.NqError):
+        nq.gemm_q8_1("gguf:q4_k", w, 1, 32, xq)            # K not a multiple of 256
