@@ -323,6 +323,93 @@ GEMV_CASES = [("gguf:q4_k", 1), ("gguf:q6_k", 1), ("gguf:q8_0", 1), ("gguf:q4_0"
               ("gguf:mxfp4", 1), ("gguf:iq2_xxs", 1), ("gguf:tq2_0", 1), ("gguf:q4_k", 8), ("gguf:q8_0", 8)]
 
 
+# Batched products (nq_gemm_q8_1, more than 8 activation rows): integer
+# operations 2 * M * N * K per launch.  The 8-bit matrix cores' dense peak is
+# 5.0 POP/s; the binding limit is the vector ALU, which scales every exact
+# 32-value dot product in binary32 (convert, product of the two scales,
+# fused multiply-add: 3 wave instructions per output and span).  256 CUs x 4
+# SIMDs x 16 lanes x 2.4 GHz = 39.3 T lane operations/s, / 3 per 32
+# multiply-adds, x 2 operations each = 838.9 TOP/s.
+MFMA_I8_PEAK_TOPS = 5000.0
+GEMM_ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 3 * 32 * 2 / 1e12
+
+
+def gemm_measurement(torch, nq, synth, fmt, shape, M, launches=20, footprint=1 << 30, seed=0x6E7C8000):
+    """Batched products with q8_1 activations over rotating weight replicas;
+    TOP/s = 2 M N K per mean launch time."""
+    import numpy as np
+    N, K = shape
+    info = nq.format_query(fmt)
+    nbytes_w = N * K // info.block_values * info.block_bytes
+    host = synth.payload(fmt, N * K // info.block_values, seed, synth.binade(-6, -2, False))
+    w0 = torch.from_numpy(host).to("cuda:0")
+    reps = max(1, math.ceil(footprint / nbytes_w))
+    ws = [w0] + [w0.clone() for _ in range(reps - 1)]
+    rng = np.random.default_rng(seed)
+    x = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to("cuda:0")
+    xq, _ = nq.quantize_q8_1(x)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        h = torch.cuda.current_stream().cuda_stream
+        for i in range(launches):
+            rc = nq.gemm_q8_1_raw(info.id, ws[i % reps].data_ptr(), nbytes_w, N, K, xq.data_ptr(), M, y.data_ptr(), h)
+            if rc != 0:
+                raise nq.NqError(rc, fmt)
+    ms, _ = time_graph(torch, g, 3)
+    mean_ms = ms / launches
+    tops = 2.0 * M * N * K / (mean_ms * 1e-3) / 1e12
+    res = {"shape": shape, "M": M, "tops": round(tops, 1), "frac_alu_peak": round(tops / GEMM_ALU_PEAK_TOPS, 4),
+           "frac_mfma_i8_peak": round(tops / MFMA_I8_PEAK_TOPS, 4), "mean_launch_us": round(mean_ms * 1e3, 3),
+           "weight_gbps": round(nbytes_w / (mean_ms * 1e-3) / 1e9, 1), "replicas": reps}
+    del g, ws, w0
+    torch.cuda.empty_cache()
+    return res
+
+
+GEMM_CASES = [("gguf:q4_k", 512), ("gguf:q8_0", 512), ("gguf:q6_k", 512), ("gguf:q4_0", 512), ("gguf:iq4_xs", 512),
+              ("gguf:iq2_xxs", 512), ("gguf:q4_k", 64), ("gguf:q4_k", 2048)]
+
+
+def gemm_cpu_baseline(synth, fmt="gguf:q4_k", shape=(14336, 4096), rows=7168, M=512, seed=0x6E7C8000):
+    """The oracle's product (binary64) on the first `rows` weight rows with M
+    activation rows, one thread."""
+    import numpy as np
+    import oracle
+    N, K = shape
+    _, B, S, _ = oracle.info(fmt)
+    w = synth.payload(fmt, rows * K // B, seed, synth.binade(-6, -2, False))
+    x = np.random.default_rng(seed).standard_normal((M, K)).astype(np.float32)
+    t0 = time.perf_counter()
+    _, xq = oracle.quantize_q8_1(x)
+    oracle.gemv_q8_1(fmt, w, rows, K, xq, M)
+    secs = time.perf_counter() - t0
+    return {"value": round(2.0 * M * rows * K / secs / 1e12, 6), "unit": "TOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{fmt} rows 0..{rows - 1} of [{N}, {K}] x {M} activation rows ({secs:.1f} s on one host core)"}
+
+
+def gemm_only(torch, nq, synth, args):
+    """The batched-product measurements alone (one JSON line): every GEMM_CASES
+    entry at both shapes, the headline case's roofline, and the oracle beside it."""
+    res = {}
+    for fmt, M in GEMM_CASES:
+        for shape in ([14336, 4096], [4096, 14336]):
+            key = f"gemm_q8_1 {fmt}{shape} M={M}"
+            res[key] = gemm_measurement(torch, nq, synth, fmt, shape, M)
+            log(f"{key}: {res[key]['tops']} TOP/s ({100 * res[key]['frac_alu_peak']:.1f}% of the ALU bound)")
+    head = res["gemm_q8_1 gguf:q4_k[14336, 4096] M=512"]
+    roofline = {"bound": "alu", "achieved": head["tops"], "peak": round(GEMM_ALU_PEAK_TOPS, 1), "unit": "TOP/s",
+                "frac": head["frac_alu_peak"], "traffic": None, "kernel": "k_gemm gguf:q4_k M=512",
+                "mfma_i8_peak": MFMA_I8_PEAK_TOPS, "frac_mfma_i8_peak": head["frac_mfma_i8_peak"],
+                "mean_launch_us": head["mean_launch_us"]}
+    cpu = None if args.no_cpu_baseline else gemm_cpu_baseline(synth)
+    line = {"metric": "gemm_q8_1 TOP/s (2 M N K per launch), 1\u00d7MI355X", "value": head["tops"], "unit": "TOP/s",
+            "n_gpus": 1, "higher_is_better": True, "dtype": "i8xi8->i32, f32 scaling", "data": "synthetic",
+            "config": {"workload": "q4_k weight [14336, 4096] x 512 q8_1 activation rows, rotating replicas"},
+            "roofline": roofline, "cpu_baseline": cpu, "cases": res}
+    print(json.dumps(line), flush=True)
+
+
 def cpu_baseline(nq, synth, tensors, fraction=8):
     """The oracle on the first 1/fraction of every tensor's blocks, one thread."""
     import numpy as np
@@ -398,6 +485,8 @@ def main():
     ap.add_argument("--no-per-format", action="store_true", help="skip the rotating per-workload timings")
     ap.add_argument("--gemv-only", action="store_true",
                     help="measure only the products with q8_1 activations (one JSON line of its own)")
+    ap.add_argument("--gemm-only", action="store_true",
+                    help="measure only the batched products on the matrix cores (one JSON line of its own)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
                     help="first run a plain device copy of this many MiB (for counter calibration)")
     args = ap.parse_args()
@@ -430,6 +519,9 @@ def main():
 
     if args.gemv_only:
         gemv_only(torch, nq, synth, args)
+        return
+    if args.gemm_only:
+        gemm_only(torch, nq, synth, args)
         return
 
     tensors, _ = workloads.config5()
@@ -497,6 +589,12 @@ def main():
                 key = f"gemv_q8_1 {fmt}{shape} M={M}"
                 extra[key] = gemv_measurement(torch, nq, synth, fmt, shape, M)
                 log(f"{key}: {extra[key]['gbps']} GB/s ({100 * extra[key]['frac_hbm_peak']:.1f}% of peak)")
+        # batched products (prefill-like activation batches) on the matrix cores
+        for fmt, M in GEMM_CASES:
+            for shape in ([14336, 4096], [4096, 14336]):
+                key = f"gemm_q8_1 {fmt}{shape} M={M}"
+                extra[key] = gemm_measurement(torch, nq, synth, fmt, shape, M)
+                log(f"{key}: {extra[key]['tops']} TOP/s ({100 * extra[key]['frac_alu_peak']:.1f}% of the ALU bound)")
 
     cpu = None
     if not args.no_cpu_baseline:

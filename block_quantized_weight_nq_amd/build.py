@@ -12,6 +12,10 @@ include/nq.h.  Flags that matter for exactness:
   correctly rounded division;
 * ``-Xclang -target-feature -Xclang -packed-fp32-ops`` is passed as given (the
   build never emits packed-fp32 VALU instructions).
+
+The matrix-core product units (k_gemm_*.hip) also take
+``-mllvm -amdgpu-mfma-vgpr-form=1``: MFMA results land in VGPRs, so the
+binary32 scaling reads them without an AGPR copy per value.
 """
 import concurrent.futures
 import os
@@ -44,9 +48,13 @@ def _hipcc():
     raise RuntimeError("hipcc not found")
 
 
+MFMA_UNITS = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+
+
 def _compile(src, is_kernel, build_dir=BUILD, defines=()):
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *COMMON, *DEVICE, *[f"-D{d}" for d in defines], "-x", "hip", "-c",
+    extra = MFMA_UNITS if src.startswith("k_gemm_") else []
+    cmd = [_hipcc(), *COMMON, *DEVICE, *extra, *[f"-D{d}" for d in defines], "-x", "hip", "-c",
            os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
