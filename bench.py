@@ -349,11 +349,16 @@ def gemm_measurement(torch, nq, synth, fmt, shape, M, launches=20, footprint=1 <
     x = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to("cuda:0")
     xq, _ = nq.quantize_q8_1(x)
     y = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+    st, ws_bytes = nq.gemm_q8_1_workspace(info.id, N, K, M)
+    if st != 0:
+        raise nq.NqError(st, fmt)
+    work = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device="cuda:0")
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         h = torch.cuda.current_stream().cuda_stream
         for i in range(launches):
-            rc = nq.gemm_q8_1_raw(info.id, ws[i % reps].data_ptr(), nbytes_w, N, K, xq.data_ptr(), M, y.data_ptr(), h)
+            rc = nq.gemm_q8_1_raw(info.id, ws[i % reps].data_ptr(), nbytes_w, N, K, xq.data_ptr(), M, y.data_ptr(),
+                                  work.data_ptr(), ws_bytes, h)
             if rc != 0:
                 raise nq.NqError(rc, fmt)
     ms, _ = time_graph(torch, g, 3)
@@ -361,8 +366,9 @@ def gemm_measurement(torch, nq, synth, fmt, shape, M, launches=20, footprint=1 <
     tops = 2.0 * M * N * K / (mean_ms * 1e-3) / 1e12
     res = {"shape": shape, "M": M, "tops": round(tops, 1), "frac_alu_peak": round(tops / GEMM_ALU_PEAK_TOPS, 4),
            "frac_mfma_i8_peak": round(tops / MFMA_I8_PEAK_TOPS, 4), "mean_launch_us": round(mean_ms * 1e3, 3),
-           "weight_gbps": round(nbytes_w / (mean_ms * 1e-3) / 1e9, 1), "replicas": reps}
-    del g, ws, w0
+           "weight_gbps": round(nbytes_w / (mean_ms * 1e-3) / 1e9, 1), "replicas": reps,
+           "k_splits": ws_bytes // (4 * M * N) if ws_bytes else 1}
+    del g, ws, w0, work
     torch.cuda.empty_cache()
     return res
 

@@ -23,7 +23,7 @@ EXPORTS = ["nq_format_count", "nq_format_by_id", "nq_format_query", "nq_validate
            "nq_dequantize_packed", "nq_validate_nvfp4_stacked", "nq_dequantize_nvfp4_stacked",
            "nq_validate_fp8_row", "nq_dequantize_fp8_row", "nq_validate_grouped_absmax",
            "nq_quantize_grouped_absmax", "nq_validate_quantize_q8_1", "nq_quantize_q8_1",
-           "nq_validate_gemv_q8_1", "nq_gemv_q8_1", "nq_validate_gemm_q8_1", "nq_gemm_q8_1",
+           "nq_validate_gemv_q8_1", "nq_gemv_q8_1", "nq_validate_gemm_q8_1", "nq_gemm_q8_1_workspace", "nq_gemm_q8_1",
            "nq_status_string"]
 GEMV_MAX_M = 8
 GQ_SCHEMES = {"q4_g64_fp16": (0, 64), "q5_g64_fp16": (1, 64), "q6_g64_fp16": (2, 64), "q8_g32_fp16": (3, 32)}
@@ -84,8 +84,9 @@ def _lib():
         L.nq_gemv_q8_1.argtypes = [c.c_int32, c.c_void_p, c.c_uint64, c.c_int64, c.c_int64, c.c_void_p,
                                    c.c_int64, c.c_void_p, c.c_void_p]
         L.nq_validate_gemm_q8_1.argtypes = [c.c_int32, c.c_uint64, c.c_int64, c.c_int64, c.c_int64]
+        L.nq_gemm_q8_1_workspace.argtypes = [c.c_int32, c.c_int64, c.c_int64, c.c_int64, c.POINTER(c.c_uint64)]
         L.nq_gemm_q8_1.argtypes = [c.c_int32, c.c_void_p, c.c_uint64, c.c_int64, c.c_int64, c.c_void_p,
-                                   c.c_int64, c.c_void_p, c.c_void_p]
+                                   c.c_int64, c.c_void_p, c.c_void_p, c.c_uint64, c.c_void_p]
         L.nq_status_string.argtypes = [c.c_int]
         L.nq_status_string.restype = c.c_char_p
         _LIB = L
@@ -344,10 +345,19 @@ def validate_gemm_q8_1_status(fmt, nbytes, N, K, M):
     return _lib().nq_validate_gemm_q8_1(fid, nbytes, N, K, M)
 
 
-def gemm_q8_1_raw(fmt_id, w_ptr, nbytes, N, K, xq_ptr, M, y_ptr, stream_handle):
+def gemm_q8_1_workspace(fmt, N, K, M):
+    """(status, workspace bytes) of the batched product for this shape on the current device."""
+    fid = fmt if isinstance(fmt, int) else format_query(fmt).id
+    b = ctypes.c_uint64(0)
+    st = _lib().nq_gemm_q8_1_workspace(fid, N, K, M, ctypes.byref(b))
+    return st, b.value
+
+
+def gemm_q8_1_raw(fmt_id, w_ptr, nbytes, N, K, xq_ptr, M, y_ptr, ws_ptr, ws_bytes, stream_handle):
     """Direct call of nq_gemm_q8_1 with integer addresses; returns the status."""
     return _lib().nq_gemm_q8_1(int(fmt_id), ctypes.c_void_p(w_ptr), nbytes, N, K, ctypes.c_void_p(xq_ptr), M,
-                               ctypes.c_void_p(y_ptr), ctypes.c_void_p(stream_handle))
+                               ctypes.c_void_p(y_ptr), ctypes.c_void_p(ws_ptr), ws_bytes,
+                               ctypes.c_void_p(stream_handle))
 
 
 def _product(raw, fmt, weight, N, K, xq, out, stream):
@@ -377,10 +387,29 @@ def gemv_q8_1(fmt, weight, N, K, xq, out=None, stream=None):
     return _product(gemv_q8_1_raw, fmt, weight, N, K, xq, out, stream)
 
 
-def gemm_q8_1(fmt, weight, N, K, xq, out=None, stream=None):
+def gemm_q8_1(fmt, weight, N, K, xq, out=None, stream=None, split=True):
     """As gemv_q8_1 for any number of activation rows M >= 1 (more than 8 on
-    the matrix cores)."""
-    return _product(gemm_q8_1_raw, fmt, weight, N, K, xq, out, stream)
+    the matrix cores).  With split=True the workspace the product may use is
+    allocated from torch on `stream` (K then splits where the shape asks for
+    it); split=False runs unsplit."""
+    import torch
+    fid = fmt if isinstance(fmt, int) else format_query(fmt).id
+    M = xq.numel() // (K // 32 * 36) if K % 32 == 0 and K > 0 else 0
+    ws, ws_bytes = None, 0
+    if split and M > 0:
+        st, ws_bytes = gemm_q8_1_workspace(fid, N, K, M)
+        if st != NQ_OK:
+            raise NqError(st, f"{fmt} [{N}, {K}] x {M}")
+        if ws_bytes:
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=weight.device)
+            if stream is not None:
+                ws.record_stream(stream)
+
+    def raw(fid_, w_ptr, nbytes, N_, K_, xq_ptr, M_, y_ptr, h):
+        return gemm_q8_1_raw(fid_, w_ptr, nbytes, N_, K_, xq_ptr, M_, y_ptr, ws.data_ptr() if ws is not None else 0,
+                             ws_bytes, h)
+
+    return _product(raw, fmt, weight, N, K, xq, out, stream)
 
 
 def dequantize_packed(fmt, payload, shape, out_dtype=None, out=None, stream=None):

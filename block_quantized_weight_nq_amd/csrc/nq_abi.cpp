@@ -369,12 +369,31 @@ NQ_API int nq_validate_gemm_q8_1(int32_t format, uint64_t nbytes, int64_t N, int
     return NQ_OK;
 }
 
+NQ_API int nq_gemm_q8_1_workspace(int32_t format, int64_t N, int64_t K, int64_t M, uint64_t *bytes) {
+    if (!bytes) return NQ_ERR_NULL_ARG;
+    *bytes = 0;
+    if (format < 0 || format >= nq::NUM_FORMATS || TRAILER_OF(format) != 0) return NQ_ERR_UNKNOWN_FORMAT;
+    if (N <= 0 || K <= 0 || M <= 0) return NQ_ERR_BAD_DIM;
+    if (K % B_OF(format) != 0) return NQ_ERR_NOT_BLOCK_ALIGNED;
+    uint64_t wbytes = 0;
+    if (N >= (1ll << 31) || K >= (1ll << 31) || M >= (1ll << 31) ||
+        !mul_checked((uint64_t)N, (uint64_t)(K / B_OF(format)) * (uint64_t)S_OF(format), &wbytes))
+        return NQ_ERR_OVERFLOW;
+    const int st = nq_validate_gemm_q8_1(format, wbytes, N, K, M);
+    if (st != NQ_OK) return st;
+    if (M > nq::GV_MAX_M && format != nq::TQ1_0)
+        *bytes = nq::gm_workspace_bytes(nq::gm_plan((uint64_t)N, (uint64_t)K, (uint64_t)M, compute_units()),
+                                        (uint64_t)M, (uint64_t)N);
+    return NQ_OK;
+}
+
 NQ_API int nq_gemm_q8_1(int32_t format, const void *weight, uint64_t nbytes, int64_t N, int64_t K,
-                        const void *xq, int64_t M, float *y, hipStream_t stream) {
+                        const void *xq, int64_t M, float *y, void *workspace, uint64_t workspace_bytes,
+                        hipStream_t stream) {
     const int st = nq_validate_gemm_q8_1(format, nbytes, N, K, M);
     if (st != NQ_OK) return st;
     if (!weight || !xq || !y) return NQ_ERR_NULL_ARG;
-    if ((uintptr_t)xq % 4 != 0 || (uintptr_t)y % 4 != 0) return NQ_ERR_NULL_ARG;
+    if ((uintptr_t)xq % 4 != 0 || (uintptr_t)y % 4 != 0 || (uintptr_t)workspace % 4 != 0) return NQ_ERR_NULL_ARG;
     nq::GvLaunch L;
     L.w = (const uint8_t *)weight;
     L.N = (uint64_t)N;
@@ -385,10 +404,10 @@ NQ_API int nq_gemm_q8_1(int32_t format, const void *weight, uint64_t nbytes, int
     L.cus = compute_units();
     if (M > nq::GV_MAX_M && format != nq::TQ1_0) {
         switch (REGISTRY[format].family) {
-        case NQ_FAMILY_SIMPLE: return nq::launch_gemm_simple(format, L, stream);
-        case NQ_FAMILY_KQUANT: return nq::launch_gemm_kquant(format, L, stream);
-        case NQ_FAMILY_IQ: return nq::launch_gemm_iq(format, L, stream);
-        default: return nq::launch_gemm_fp4t(format, L, stream);
+        case NQ_FAMILY_SIMPLE: return nq::launch_gemm_simple(format, L, workspace, workspace_bytes, stream);
+        case NQ_FAMILY_KQUANT: return nq::launch_gemm_kquant(format, L, workspace, workspace_bytes, stream);
+        case NQ_FAMILY_IQ: return nq::launch_gemm_iq(format, L, workspace, workspace_bytes, stream);
+        default: return nq::launch_gemm_fp4t(format, L, workspace, workspace_bytes, stream);
         }
     }
     // the single-row kernel, 8 activation rows per launch

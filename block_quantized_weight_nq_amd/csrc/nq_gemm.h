@@ -79,6 +79,9 @@ struct GmArgs {
     uint32_t M;             // activation rows in this launch
     uint32_t mt;            // activation-row tiles
     uint32_t xq8, xr8;      // workgroups / 8 and workgroups mod 8
+    uint32_t nsplit;        // K splits (1: none)
+    uint32_t sps;           // K steps per split
+    uint64_t ysplit;        // elements between two splits' partial outputs (M * N)
 };
 
 // A span rewritten: 32 codes (8 dwords, value order) and per half its scale
@@ -239,82 +242,99 @@ NQ_HD void gm_span(const Src &s, uint32_t bo, uint32_t p, const Tab &tab, GmSpan
     }
 }
 
-// Workgroup id -> (weight tile, activation tile): ids go to the XCDs in turn
-// (id mod 8); each XCD's ids take a contiguous range of tile numbers, and
-// tile numbers run over activation tiles first, so the tiles of one group of
-// weight rows fall on one XCD.  A bijection of [0, grid).
-NQ_HD void gm_tile(const GmArgs &a, uint32_t id, uint32_t *n0, uint32_t *m0) {
+// Workgroup id -> (weight tile, activation tile, K split): ids go to the
+// XCDs in turn (id mod 8); each XCD's ids take a contiguous range of
+// numbers, and numbers run over K splits first, then activation tiles, so the
+// work on one group of weight rows falls on one XCD.  A bijection of
+// [0, grid).
+NQ_HD void gm_tile(const GmArgs &a, uint32_t id, uint32_t *n0, uint32_t *m0, uint32_t *ks) {
     const uint32_t x = id & 7u, j = id >> 3;
     const uint32_t L = (x < a.xr8 ? x * (a.xq8 + 1u) : a.xr8 * (a.xq8 + 1u) + (x - a.xr8) * a.xq8) + j;
-    *m0 = (L % a.mt) * GM_BM;
-    *n0 = (L / a.mt) * GM_BN;
+    const uint32_t T = L / a.nsplit;
+    *ks = L - T * a.nsplit;
+    *m0 = (T % a.mt) * GM_BM;
+    *n0 = (T / a.mt) * GM_BN;
 }
 
 // K step: the spans t0 .. t0+7 of weight rows n0 .. n0+127, rewritten into
-// LDS, strided over the workgroup's threads (rows past the launch and spans
-// past K are zeros).
+// LDS; thread tid takes items tid + WG r (r < 4), item i = (row i / 8, span
+// i mod 8).  The loads take no branch (an item past the launch's rows or
+// past K reads the launch's first span and is then zeroed), so the four
+// items' loads are all in flight at once.
 template <int F, class Src>
 NQ_HD void gm_stage_w(const GmArgs &a, const Src &src, const Tab &tab, uint32_t n0, uint32_t t0, uint32_t tid,
                       uint32_t *lds) {
     using G = GmFmt<F>;
     constexpr uint32_t S = (uint32_t)block_bytes(F);
-    for (uint32_t i = tid; i < GM_BN * GM_SP; i += WG) {
-        const uint32_t n = i / GM_SP, sp = i % GM_SP, t = t0 + sp;
-        GmSpan o;
-        if (n0 + n < a.rows && t < a.kspans) {
-            const uint32_t b = t / G::SPB;
-            gm_span<F>(src, a.wmis + (n0 + n) * a.row_bytes + b * S, t - b * G::SPB, tab, o);
-        } else {
+    constexpr uint32_t R = GM_BN * GM_SP / (uint32_t)WG;
+    static_assert(GM_BN * GM_SP % (uint32_t)WG == 0, "whole items per thread");
+    GmSpan o[R];
+    bool ok[R];
 #pragma unroll
-            for (int j = 0; j < 8; j++) o.c[j] = 0u;
-            o.ws[0] = o.ws[1] = o.ow[0] = o.ow[1] = 0.0f;
-        }
+    for (uint32_t r = 0; r < R; r++) {
+        const uint32_t i = tid + (uint32_t)WG * r, n = i / GM_SP, t = t0 + i % GM_SP;
+        ok[r] = n0 + n < a.rows && t < a.kspans;
+        const uint32_t nn = ok[r] ? n0 + n : 0u, tt = ok[r] ? t : 0u, b = tt / G::SPB;
+        gm_span<F>(src, a.wmis + nn * a.row_bytes + b * S, tt - b * G::SPB, tab, o[r]);
+    }
+    float *ws = (float *)(lds + G::WS), *ow = (float *)(lds + G::WO);
+#pragma unroll
+    for (uint32_t r = 0; r < R; r++) {
+        const uint32_t i = tid + (uint32_t)WG * r, n = i / GM_SP, sp = i % GM_SP;
         uint32_t *cw = lds + n * GM_CSW + 8u * sp;
 #pragma unroll
-        for (int j = 0; j < 8; j++) cw[j] = o.c[j];
-        float *ws = (float *)(lds + G::WS), *ow = (float *)(lds + G::WO);
+        for (int j = 0; j < 8; j++) cw[j] = ok[r] ? o[r].c[j] : 0u;
 #pragma unroll
         for (uint32_t h = 0; h < G::NH; h++) {
-            ws[(sp * G::NH + h) * GM_BN + n] = o.ws[h];
-            if constexpr (G::AFF) ow[(sp * G::NH + h) * GM_BN + n] = o.ow[h];
+            ws[(sp * G::NH + h) * GM_BN + n] = ok[r] ? o[r].ws[h] : 0.0f;
+            if constexpr (G::AFF) ow[(sp * G::NH + h) * GM_BN + n] = ok[r] ? o[r].ow[h] : 0.0f;
         }
     }
 }
 
 // K step, activation side: blocks t0 .. t0+7 of activation rows m0 .. m0+63
 // (codes, binary32 scale, and for the affine formats d times the exact code
-// sum of each half), strided over the workgroup's threads.
+// sum of each half); thread tid takes items tid + WG r (r < 2), item i =
+// (row i / 8, block i mod 8), loaded without branches as above.
 template <int F>
 NQ_HD void gm_stage_x(const GmArgs &a, uint32_t m0, uint32_t t0, uint32_t tid, uint32_t *lds) {
     using G = GmFmt<F>;
-    for (uint32_t i = tid; i < GM_BM * GM_SP; i += WG) {
-        const uint32_t m = i / GM_SP, sp = i % GM_SP, t = t0 + sp;
-        uint32_t c[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-        float d = 0.0f;
-        if (m0 + m < a.M && t < a.kspans) {
-            const uint32_t *p = a.xq + (uint64_t)(m0 + m) * a.xrow + (uint64_t)t * 9u;
-            const u32x4a4 v0 = *(const u32x4a4 *)(p + 1), v1 = *(const u32x4a4 *)(p + 5);
-            c[0] = v0.x; c[1] = v0.y; c[2] = v0.z; c[3] = v0.w;
-            c[4] = v1.x; c[5] = v1.y; c[6] = v1.z; c[7] = v1.w;
-            d = f16(p[0] & 0xFFFFu);
-        }
+    constexpr uint32_t R = GM_BM * GM_SP / (uint32_t)WG;
+    static_assert(GM_BM * GM_SP % (uint32_t)WG == 0, "whole items per thread");
+    uint32_t c[R][8];
+    float d[R];
+    bool ok[R];
+#pragma unroll
+    for (uint32_t r = 0; r < R; r++) {
+        const uint32_t i = tid + (uint32_t)WG * r, m = i / GM_SP, t = t0 + i % GM_SP;
+        ok[r] = m0 + m < a.M && t < a.kspans;
+        const uint32_t *p = a.xq + (ok[r] ? (uint64_t)(m0 + m) * a.xrow + (uint64_t)t * 9u : 0ull);
+        const u32x4a4 v0 = *(const u32x4a4 *)(p + 1), v1 = *(const u32x4a4 *)(p + 5);
+        c[r][0] = v0.x; c[r][1] = v0.y; c[r][2] = v0.z; c[r][3] = v0.w;
+        c[r][4] = v1.x; c[r][5] = v1.y; c[r][6] = v1.z; c[r][7] = v1.w;
+        d[r] = f16(p[0] & 0xFFFFu);
+    }
+#pragma unroll
+    for (uint32_t r = 0; r < R; r++) {
+        const uint32_t i = tid + (uint32_t)WG * r, m = i / GM_SP, sp = i % GM_SP;
+        const float dr = ok[r] ? d[r] : 0.0f;
         uint32_t *cx = lds + G::XC + m * GM_CSW + 8u * sp;
 #pragma unroll
-        for (int j = 0; j < 8; j++) cx[j] = c[j];
-        ((float *)(lds + G::XD))[sp * GM_BM + m] = d;
+        for (int j = 0; j < 8; j++) cx[j] = ok[r] ? c[r][j] : 0u;
+        ((float *)(lds + G::XD))[sp * GM_BM + m] = dr;
         if constexpr (G::AFF) {
             int S0 = 0, S1 = 0;
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-                S0 = dot4(ONES8, c[j], S0);
-                S1 = dot4(ONES8, c[4 + j], S1);
+                S0 = dot4(ONES8, c[r][j], S0);
+                S1 = dot4(ONES8, c[r][4 + j], S1);
             }
             float *xt = (float *)(lds + G::XT);
             if constexpr (G::U16) {
-                xt[(2u * sp) * GM_BM + m] = d * (float)S0;
-                xt[(2u * sp + 1u) * GM_BM + m] = d * (float)S1;
+                xt[(2u * sp) * GM_BM + m] = dr * (float)S0;
+                xt[(2u * sp + 1u) * GM_BM + m] = dr * (float)S1;
             } else {
-                xt[sp * GM_BM + m] = d * (float)(S0 + S1);
+                xt[sp * GM_BM + m] = dr * (float)(S0 + S1);
             }
         }
     }
@@ -405,15 +425,15 @@ NQ_HD void gm_epi(const uint32_t *lds, uint32_t w, uint32_t lane, uint32_t sp, c
 }
 
 // The lane's outputs: y[m][n] for its 4 x 2 x 4 (row, activation row) pairs
-// inside the launch.
-NQ_HD void gm_store(const GmArgs &a, uint32_t n0, uint32_t m0, uint32_t w, uint32_t lane,
+// inside the launch (with K splits: split ks's partial output).
+NQ_HD void gm_store(const GmArgs &a, uint32_t n0, uint32_t m0, uint32_t ks, uint32_t w, uint32_t lane,
                     const float (&acc)[4][2][4]) {
     const uint32_t nb = n0 + 64u * (w & 1u) + 4u * (lane >> 4), mb = m0 + 32u * (w >> 1) + (lane & 15u);
 #pragma unroll
     for (int j = 0; j < 2; j++) {
         const uint32_t m = mb + 16u * (uint32_t)j;
         if (m >= a.M) continue;
-        float *yr = a.y + (uint64_t)m * a.ldy;
+        float *yr = a.y + (uint64_t)ks * a.ysplit + (uint64_t)m * a.ldy;
 #pragma unroll
         for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -436,8 +456,8 @@ __global__ __launch_bounds__(WG) void k_gemm(GmArgs a) {
     if constexpr (TS::n8 + TS::n4 > 0) gv_fill_tables<F>(t8, t4, threadIdx.x);
     const Tab tab{t8, t4, nullptr, nullptr, 0xFFFFFFFFu, 1u};
     const GmSrc src{a.wbase, a.wlast};
-    uint32_t n0, m0;
-    gm_tile(a, blockIdx.x, &n0, &m0);
+    uint32_t n0, m0, ks;
+    gm_tile(a, blockIdx.x, &n0, &m0, &ks);
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t w = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     float acc[4][2][4];
@@ -447,12 +467,13 @@ __global__ __launch_bounds__(WG) void k_gemm(GmArgs a) {
         for (int j = 0; j < 2; j++)
 #pragma unroll
             for (int e = 0; e < 4; e++) acc[i][j][e] = 0.0f;
-    for (uint32_t t0 = 0; t0 < a.kspans; t0 += GM_SP) {
+    const uint32_t tb = ks * a.sps * GM_SP, te0 = tb + a.sps * GM_SP, te = te0 < a.kspans ? te0 : a.kspans;
+    for (uint32_t t0 = tb; t0 < te; t0 += GM_SP) {
         __syncthreads();  // the previous step's readers are done (and the tables are filled)
         gm_stage_w<F>(a, src, tab, n0, t0, threadIdx.x, lds);
         gm_stage_x<F>(a, m0, t0, threadIdx.x, lds);
         __syncthreads();
-        const uint32_t nsp = a.kspans - t0 < GM_SP ? a.kspans - t0 : GM_SP;
+        const uint32_t nsp = te - t0 < GM_SP ? te - t0 : GM_SP;
         for (uint32_t sp = 0; sp < nsp; sp++) {
             GmOps o;
             gm_ops<F>(lds, w, lane, sp, o);
@@ -473,13 +494,57 @@ __global__ __launch_bounds__(WG) void k_gemm(GmArgs a) {
             gm_epi<F>(lds, w, lane, sp, I, acc);
         }
     }
-    gm_store(a, n0, m0, w, lane, acc);
+    gm_store(a, n0, m0, ks, w, lane, acc);
+}
+
+// The K splits' partial outputs summed in split order: y[i] = ((p0 + p1) + p2) ...
+template <int U>
+__global__ __launch_bounds__(WG) void k_gemm_sum(const float *part, float *y, uint64_t n, uint32_t nsplit) {
+    for (uint64_t i = (uint64_t)blockIdx.x * WG + threadIdx.x; i < n; i += (uint64_t)gridDim.x * WG) {
+        float v = part[i];
+        for (uint32_t s = 1; s < nsplit; s++) v = v + part[(uint64_t)s * n + i];
+        y[i] = v;
+    }
 }
 
 // ------------------------------------------------------------------ host side
 
+// K split plan of a call: when the tiles are fewer than two per compute
+// unit and K is long (8 steps or more), K is cut into nsplit ranges of sps
+// steps (at least 4 each) so that about two workgroups per compute unit
+// run; the partial outputs (nsplit * M * N binary32 values, at most 2 GiB)
+// then go to a workspace and are summed in split order.  The plan depends
+// only on N, K, M and the compute-unit count.
+struct GmPlan {
+    uint32_t nsplit, sps;
+};
+
+inline GmPlan gm_plan(uint64_t N, uint64_t K, uint64_t M, uint32_t cus) {
+    const uint64_t steps = (K / 32 + GM_SP - 1) / GM_SP;
+    const uint64_t tiles = (N + GM_BN - 1) / GM_BN * ((M + GM_BM - 1) / GM_BM);
+    const uint64_t target = 2ull * (cus ? cus : 1u);
+    GmPlan p{1u, (uint32_t)steps};
+    if (tiles >= target || steps < 8) return p;
+    uint64_t S = (target + tiles - 1) / tiles;
+    if (S > steps / 4) S = steps / 4;
+    if (S < 2) return p;
+    const uint64_t sps = (steps + S - 1) / S;
+    S = (steps + sps - 1) / sps;
+    if (S < 2 || S * M * N * 4 > (1ull << 31)) return p;
+    p.nsplit = (uint32_t)S;
+    p.sps = (uint32_t)sps;
+    return p;
+}
+
+inline uint64_t gm_workspace_bytes(const GmPlan &p, uint64_t M, uint64_t N) {
+    return p.nsplit > 1 ? (uint64_t)p.nsplit * M * N * 4 : 0;
+}
+
+// One launch: weight rows r0 .. r0+rows-1, activation rows m0 .. m0+mrows-1,
+// outputs into `out` ([M, N], or the [nsplit, M, N] partials).
 template <int F>
-GmArgs gm_args(const GvLaunch &L, uint64_t r0, uint64_t rows, uint64_t m0, uint64_t mrows) {
+GmArgs gm_args(const GvLaunch &L, uint64_t r0, uint64_t rows, uint64_t m0, uint64_t mrows, const GmPlan &p,
+               float *out) {
     constexpr uint64_t S = (uint64_t)block_bytes(F);
     const uint64_t nbr = L.K / (uint64_t)block_values(F), row_bytes = nbr * S;
     const uint8_t *start = L.w + r0 * row_bytes;
@@ -488,7 +553,7 @@ GmArgs gm_args(const GvLaunch &L, uint64_t r0, uint64_t rows, uint64_t m0, uint6
     a.wmis = (uint32_t)((uintptr_t)start & 3u);
     a.wlast = (uint32_t)((a.wmis + rows * row_bytes - 1) / 4);
     a.xq = (const uint32_t *)L.xq + m0 * (L.K / 32 * 9);
-    a.y = L.y + m0 * L.N + r0;
+    a.y = out + m0 * L.N + r0;
     a.rows = (uint32_t)rows;
     a.row_bytes = (uint32_t)row_bytes;
     a.kspans = (uint32_t)(L.K / 32);
@@ -496,7 +561,10 @@ GmArgs gm_args(const GvLaunch &L, uint64_t r0, uint64_t rows, uint64_t m0, uint6
     a.ldy = (uint32_t)L.N;
     a.M = (uint32_t)mrows;
     a.mt = (uint32_t)((mrows + GM_BM - 1) / GM_BM);
-    const uint64_t grid = (rows + GM_BN - 1) / GM_BN * a.mt;
+    a.nsplit = p.nsplit;
+    a.sps = p.sps;
+    a.ysplit = L.M * L.N;
+    const uint64_t grid = (rows + GM_BN - 1) / GM_BN * a.mt * p.nsplit;
     a.xq8 = (uint32_t)(grid / 8);
     a.xr8 = (uint32_t)(grid % 8);
     return a;
@@ -513,18 +581,30 @@ uint64_t gm_max_rows(const GvLaunch &L) {
     return r >= GM_BN ? r / GM_BN * GM_BN : r;
 }
 
+// The call's launches; `ws` (ws_bytes) is the caller's workspace: with at
+// least gm_workspace_bytes of the plan, K is split as planned, else not.
 template <int F>
-int launch_gemm_mfma(const GvLaunch &L, hipStream_t stream) {
+int launch_gemm_mfma(const GvLaunch &L, void *ws, uint64_t ws_bytes, hipStream_t stream) {
     const uint64_t max_rows = gm_max_rows<F>(L);
+    GmPlan p = gm_plan(L.N, L.K, L.M, L.cus);
+    const bool split = p.nsplit > 1 && ws != nullptr && ws_bytes >= gm_workspace_bytes(p, L.M, L.N);
+    if (!split) p = GmPlan{1u, (uint32_t)((L.K / 32 + GM_SP - 1) / GM_SP)};
+    float *out = split ? (float *)ws : L.y;
     for (uint64_t m0 = 0; m0 < L.M; m0 += GM_MAX_MROWS) {
         const uint64_t mrows = L.M - m0 < GM_MAX_MROWS ? L.M - m0 : GM_MAX_MROWS;
         for (uint64_t r0 = 0; r0 < L.N;) {
             const uint64_t rows = L.N - r0 < max_rows ? L.N - r0 : max_rows;
-            const GmArgs a = gm_args<F>(L, r0, rows, m0, mrows);
+            const GmArgs a = gm_args<F>(L, r0, rows, m0, mrows, p, out);
             hipLaunchKernelGGL((k_gemm<F>), dim3(gm_grid(a)), dim3(WG), 0, stream, a);
             if (hipGetLastError() != hipSuccess) return 9;  // NQ_ERR_HIP
             r0 += rows;
         }
+    }
+    if (split) {
+        const uint64_t n = L.M * L.N, blocks = (n + WG - 1) / WG;
+        hipLaunchKernelGGL((k_gemm_sum<0>), dim3((uint32_t)(blocks < 8192 ? blocks : 8192)), dim3(WG), 0, stream,
+                           (const float *)ws, L.y, n, p.nsplit);
+        if (hipGetLastError() != hipSuccess) return 9;  // NQ_ERR_HIP
     }
     return 0;
 }
@@ -533,9 +613,9 @@ int launch_gemm_mfma(const GvLaunch &L, hipStream_t stream) {
 // with a span rewrite; the others, and fewer rows, go through the
 // single-row kernel).
 template <int F>
-int launch_gemm_f(const GvLaunch &L, hipStream_t stream) {
+int launch_gemm_f(const GvLaunch &L, void *ws, uint64_t ws_bytes, hipStream_t stream) {
     if constexpr (GmFmt<F>::OK)
-        return launch_gemm_mfma<F>(L, stream);
+        return launch_gemm_mfma<F>(L, ws, ws_bytes, stream);
     else
         return 2;  // NQ_ERR_UNKNOWN_FORMAT
 }

@@ -14,9 +14,9 @@ int launch_gemv_simple(int fmt, const GvLaunch &L, hipStream_t s);
 int launch_gemv_kquant(int fmt, const GvLaunch &L, hipStream_t s);
 int launch_gemv_iq(int fmt, const GvLaunch &L, hipStream_t s);
 int launch_gemv_fp4t(int fmt, const GvLaunch &L, hipStream_t s);
-int launch_gemm_simple(int fmt, const GvLaunch &L, hipStream_t s);
-int launch_gemm_kquant(int fmt, const GvLaunch &L, hipStream_t s);
-int launch_gemm_iq(int fmt, const GvLaunch &L, hipStream_t s);
-int launch_gemm_fp4t(int fmt, const GvLaunch &L, hipStream_t s);
+int launch_gemm_simple(int fmt, const GvLaunch &L, void *ws, uint64_t ws_bytes, hipStream_t s);
+int launch_gemm_kquant(int fmt, const GvLaunch &L, void *ws, uint64_t ws_bytes, hipStream_t s);
+int launch_gemm_iq(int fmt, const GvLaunch &L, void *ws, uint64_t ws_bytes, hipStream_t s);
+int launch_gemm_fp4t(int fmt, const GvLaunch &L, void *ws, uint64_t ws_bytes, hipStream_t s);
 int launch_quantize_q8_1(int in_dtype, const Q81Launch &L, hipStream_t s);
 }  // namespace nq

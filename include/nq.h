@@ -250,21 +250,34 @@ int nq_gemv_q8_1(int32_t format, const void *weight, uint64_t nbytes, int64_t N,
 
 /* nq_gemm_q8_1: the same product for any number of activation rows M >= 1
  * (the page's GGUF linear operation over a batch), with the same argument
- * meaning, layouts, criterion and determinism.  Up to 8 rows it makes the
- * launches nq_gemv_q8_1 makes (identical bits); with more rows every 32
- * weight values become signed 8-bit codes with a binary32 scale (and an
- * offset for q4_1, q5_1, q2_k, q4_k and q5_k), their exact integer dot
- * products with the activation codes come from the 8-bit matrix cores, and
- * each is scaled and added in binary32 (gguf:tq1_0 runs through the
- * single-row kernel, 8 activation rows per launch).
+ * meaning, layouts and criterion.  Up to 8 rows it makes the launches
+ * nq_gemv_q8_1 makes (identical bits); with more rows every 32 weight values
+ * become signed 8-bit codes with a binary32 scale (and an offset for q4_1,
+ * q5_1, q2_k, q4_k and q5_k), their exact integer dot products with the
+ * activation codes come from the 8-bit matrix cores, and each is scaled and
+ * added in binary32 (gguf:tq1_0 runs through the single-row kernel, 8
+ * activation rows per launch).
+ * When the output has few tiles and K is long, K is split over workgroups:
+ * each split's partial output goes to `workspace` (device memory the caller
+ * owns, at least the size nq_gemm_q8_1_workspace reports, 4-byte aligned, not
+ * overlapping the other buffers, and not used by another call until this
+ * call's work on `stream` is done), and the partials are summed in split
+ * order by a second launch.  With workspace NULL or smaller than that size
+ * the product runs unsplit.  Repeated calls with the same shape, device and
+ * workspace choice (given or not) give identical bits.
  * nq_validate_gemm_q8_1 checks as nq_validate_gemv_q8_1 except that M may
- * be any count >= 1 with M * K / 32 * 36 and M * N representable
- * (NQ_ERR_OVERFLOW).  nq_gemm_q8_1 requires weight, xq and y non-NULL and
- * xq and y aligned to 4 bytes (NQ_ERR_NULL_ARG), then enqueues the product on
- * `stream`.  The caller owns every buffer; y must not overlap the inputs. */
+ * be any count >= 1 below 2^31 with M * K / 32 * 36 and M * N * 4 below 2^63
+ * (NQ_ERR_OVERFLOW).  nq_gemm_q8_1_workspace runs the same checks (nbytes
+ * taken as the format's length rule) and stores the workspace size for the
+ * shape on the current device (0 when the product would not split; `bytes`
+ * NULL: NQ_ERR_NULL_ARG).  nq_gemm_q8_1 requires weight, xq and y non-NULL
+ * and xq, y and workspace aligned to 4 bytes (NQ_ERR_NULL_ARG), then
+ * enqueues the product on `stream`.  The caller owns every buffer; y must not
+ * overlap the inputs. */
 int nq_validate_gemm_q8_1(int32_t format, uint64_t nbytes, int64_t N, int64_t K, int64_t M);
+int nq_gemm_q8_1_workspace(int32_t format, int64_t N, int64_t K, int64_t M, uint64_t *bytes);
 int nq_gemm_q8_1(int32_t format, const void *weight, uint64_t nbytes, int64_t N, int64_t K, const void *xq,
-                 int64_t M, float *y, hipStream_t stream);
+                 int64_t M, float *y, void *workspace, uint64_t workspace_bytes, hipStream_t stream);
 
 /* Static description of a status code. */
 const char *nq_status_string(int status);

@@ -352,15 +352,16 @@ void mfma_i8_16x16x32(const uint64_t (&A)[64], const uint64_t (&B)[64], int (&D)
 }
 
 // Batched product on the matrix cores: the launcher's launches (max_rows /
-// max_mrows > 0 override its weight-row and activation-row limits), and per
-// launch every workgroup of the grid as the kernel runs it: its tile (each
-// tile must be met exactly once), per K step the threads' staging into a
+// max_mrows > 0 override its weight-row and activation-row limits; cus > 0
+// plans K splits for that many compute units, with a workspace), and per
+// launch every workgroup of the grid as the kernel runs it: its tile and K
+// split (each met exactly once), per K step the threads' staging into a
 // poisoned LDS image (weight reads through a bounds-checked source), then per
 // span and wave the lanes' operands, the matrix instruction and the lanes'
-// scaling, and at the end the lanes' stores.
+// scaling, and at the end the lanes' stores; then the partials' sum.
 template <int F>
 long run_gemm(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y, uint64_t max_rows,
-              uint64_t max_mrows, char *err, int errlen) {
+              uint64_t max_mrows, uint32_t cus, uint32_t *nsplit_out, char *err, int errlen) {
     using namespace nq;
     using G = GmFmt<F>;
     const GvLaunch L{w, N, K, M, xq, y, 0u};
@@ -376,26 +377,32 @@ long run_gemm(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint6
     static GmOps ops[64];
     static GmI<F> I[64];
     long errors = 0;
+    GmPlan plan = gm_plan(N, K, M, cus);
+    if (cus == 0 || plan.nsplit < 2) plan = GmPlan{1u, (uint32_t)((K / 32 + GM_SP - 1) / GM_SP)};
+    *nsplit_out = plan.nsplit;
+    std::vector<float> part(plan.nsplit > 1 ? gm_workspace_bytes(plan, M, N) / 4 : 0, 0.0f / 0.0f);
+    float *out = plan.nsplit > 1 ? part.data() : y;
     for (uint64_t m0 = 0; m0 < M; m0 += mlim) {
         const uint64_t mrows = M - m0 < mlim ? M - m0 : mlim;
         for (uint64_t r0 = 0; r0 < N;) {
             const uint64_t rows = N - r0 < lim ? N - r0 : lim;
-            const GmArgs a = gm_args<F>(L, r0, rows, m0, mrows);
+            const GmArgs a = gm_args<F>(L, r0, rows, m0, mrows, plan, out);
             Check chk{(uintptr_t)(w + r0 * row_bytes), (uintptr_t)(w + (r0 + rows) * row_bytes), 0, {0}};
             const HostSrc src{a.wbase, a.wlast, &chk};
             const uint32_t grid = gm_grid(a);
             const uint32_t nt = (uint32_t)((rows + GM_BN - 1) / GM_BN);
-            if ((uint64_t)grid != (uint64_t)nt * a.mt) {
-                snprintf(err, errlen, "grid %u for %u x %u tiles", grid, nt, a.mt);
+            if ((uint64_t)grid != (uint64_t)nt * a.mt * a.nsplit) {
+                snprintf(err, errlen, "grid %u for %u x %u tiles x %u splits", grid, nt, a.mt, a.nsplit);
                 return 1;
             }
             std::vector<char> seen(grid, 0);
             for (uint32_t id = 0; id < grid; id++) {
-                uint32_t n0, mt0;
-                gm_tile(a, id, &n0, &mt0);
-                const uint64_t tile = (uint64_t)(n0 / GM_BN) * a.mt + mt0 / GM_BM;
-                if (n0 % GM_BN || mt0 % GM_BM || tile >= grid || seen[tile]++) {
-                    snprintf(err, errlen, "workgroup %u: tile (%u, %u) out of range or met twice", id, n0, mt0);
+                uint32_t n0, mt0, ks;
+                gm_tile(a, id, &n0, &mt0, &ks);
+                const uint64_t tile = ((uint64_t)(n0 / GM_BN) * a.mt + mt0 / GM_BM) * a.nsplit + ks;
+                if (n0 % GM_BN || mt0 % GM_BM || ks >= a.nsplit || tile >= grid || seen[tile]++) {
+                    snprintf(err, errlen, "workgroup %u: tile (%u, %u, %u) out of range or met twice", id, n0, mt0,
+                             ks);
                     return 1;
                 }
                 for (auto &wv : acc)
@@ -403,12 +410,14 @@ long run_gemm(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint6
                         for (auto &i4 : ln)
                             for (auto &j2 : i4)
                                 for (float &v : j2) v = 0.0f;
-                for (uint32_t t0 = 0; t0 < a.kspans; t0 += GM_SP) {
+                const uint32_t tb = ks * a.sps * GM_SP, te0 = tb + a.sps * GM_SP,
+                               te = te0 < a.kspans ? te0 : a.kspans;
+                for (uint32_t t0 = tb; t0 < te; t0 += GM_SP) {
                     std::fill(lds.begin(), lds.end(), 0xA5A5A5A5u);
                     for (uint32_t tid = 0; tid < (uint32_t)WG; tid++)
                         gm_stage_w<F>(a, src, tab, n0, t0, tid, lds.data());
                     for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) gm_stage_x<F>(a, mt0, t0, tid, lds.data());
-                    const uint32_t nsp = a.kspans - t0 < GM_SP ? a.kspans - t0 : GM_SP;
+                    const uint32_t nsp = te - t0 < GM_SP ? te - t0 : GM_SP;
                     for (uint32_t sp = 0; sp < nsp; sp++)
                         for (uint32_t wv = 0; wv < 4u; wv++) {
                             for (uint32_t lane = 0; lane < 64u; lane++) gm_ops<F>(lds.data(), wv, lane, sp, ops[lane]);
@@ -430,13 +439,21 @@ long run_gemm(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint6
                         }
                 }
                 for (uint32_t wv = 0; wv < 4u; wv++)
-                    for (uint32_t lane = 0; lane < 64u; lane++) gm_store(a, n0, mt0, wv, lane, acc[wv][lane]);
+                    for (uint32_t lane = 0; lane < 64u; lane++) gm_store(a, n0, mt0, ks, wv, lane, acc[wv][lane]);
             }
             if (chk.errors) {
                 if (errors == 0) snprintf(err, errlen, "%s", chk.msg);
                 errors += chk.errors;
             }
             r0 += rows;
+        }
+    }
+    if (plan.nsplit > 1) {
+        const uint64_t n = M * N;
+        for (uint64_t i = 0; i < n; i++) {
+            float v = part[i];
+            for (uint32_t sidx = 1; sidx < plan.nsplit; sidx++) v = v + part[(uint64_t)sidx * n + i];
+            y[i] = v;
         }
     }
     return errors;
@@ -451,7 +468,8 @@ using EmuGemv = long (*)(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t
                          uint32_t resident, uint64_t max_rows, char *err, int errlen);
 extern EmuGemv nq_emu_gemv_table[nq::NUM_FORMATS];
 using EmuGemm = long (*)(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y,
-                         uint64_t max_rows, uint64_t max_mrows, char *err, int errlen);
+                         uint64_t max_rows, uint64_t max_mrows, uint32_t cus, uint32_t *nsplit, char *err,
+                         int errlen);
 extern EmuGemm nq_emu_gemm_table[nq::NUM_FORMATS];
 
 #if defined(NQ_EMU_PART)
@@ -485,9 +503,10 @@ EmuGemm nq_emu_gemm_table[nq::NUM_FORMATS];
 extern "C" __attribute__((visibility("default"))) long nq_emu_gemm_q8_1(int fmt, const uint8_t *w, uint64_t N,
                                                                        uint64_t K, const uint8_t *xq, uint64_t M,
                                                                        float *y, uint64_t max_rows,
-                                                                       uint64_t max_mrows, char *err, int errlen) {
+                                                                       uint64_t max_mrows, uint32_t cus,
+                                                                       uint32_t *nsplit, char *err, int errlen) {
     if (fmt < 0 || fmt >= nq::NUM_FORMATS || !nq_emu_gemm_table[fmt]) return -1;
-    return nq_emu_gemm_table[fmt](w, N, K, xq, M, y, max_rows, max_mrows, err, errlen);
+    return nq_emu_gemm_table[fmt](w, N, K, xq, M, y, max_rows, max_mrows, cus, nsplit, err, errlen);
 }
 
 // Product with q8_1 activations through the kernel's lane code; returns

@@ -75,7 +75,8 @@ def lib():
         L.nq_emu_gemv_q8_1.restype = ctypes.c_long
         L.nq_emu_gemm_q8_1.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64,
                                        ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint64,
-                                       ctypes.c_uint64, ctypes.c_char_p, ctypes.c_int]
+                                       ctypes.c_uint64, ctypes.c_uint32, ctypes.POINTER(ctypes.c_uint32),
+                                       ctypes.c_char_p, ctypes.c_int]
         L.nq_emu_gemm_q8_1.restype = ctypes.c_long
         L.nq_emu_quantize_q8_1.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_uint64, ctypes.c_char_p, ctypes.c_int]
@@ -184,9 +185,10 @@ def gemv_q8_1(fmt_id, w, N, K, xq, M, w_mis=0, resident=2048, max_rows=0):
     return y, rc, err.value.decode(), guards
 
 
-def gemm_q8_1(fmt_id, w, N, K, xq, M, w_mis=0, max_rows=0, max_mrows=0):
-    """The matrix-core product through the emulator.  Returns (y float32
-    [M, N], bad reads, message, guards_ok); bad reads is -1 for a format
+def gemm_q8_1(fmt_id, w, N, K, xq, M, w_mis=0, max_rows=0, max_mrows=0, cus=0, with_splits=False):
+    """The matrix-core product through the emulator (cus > 0: K split as
+    planned for that many compute units).  Returns (y float32 [M, N], bad
+    reads, message, guards_ok[, K splits]); bad reads is -1 for a format
     without a span rewrite."""
     w = np.ascontiguousarray(w, dtype=np.uint8)
     wbuf, woff = _placed(w.size, 16, w_mis)
@@ -196,10 +198,13 @@ def gemm_q8_1(fmt_id, w, N, K, xq, M, w_mis=0, max_rows=0, max_mrows=0):
     xbuf[xoff:xoff + xq.size] = xq
     ybuf = np.full(M * N + 32, np.float32(np.nan), dtype=np.float32)
     err = ctypes.create_string_buffer(256)
+    ns = ctypes.c_uint32(0)
     rc = lib().nq_emu_gemm_q8_1(fmt_id, wbuf.ctypes.data + woff, N, K, xbuf.ctypes.data + xoff, M,
-                                ybuf.ctypes.data + 64, max_rows, max_mrows, err, 256)
+                                ybuf.ctypes.data + 64, max_rows, max_mrows, cus, ctypes.byref(ns), err, 256)
     y = ybuf[16:16 + M * N].reshape(M, N).copy()
     guards = bool(np.all(np.isnan(ybuf[:16])) and np.all(np.isnan(ybuf[16 + M * N:])))
+    if with_splits:
+        return y, rc, err.value.decode(), guards, ns.value
     return y, rc, err.value.decode(), guards
 
 

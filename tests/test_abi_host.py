@@ -287,9 +287,26 @@ def test_gemm_rejects_before_device():
     # output bytes M * N * 4 past 2^63 - 1, then just below
     assert nq.validate_gemm_q8_1_status(q8, 34 * ((1 << 31) - 1), (1 << 31) - 1, 32, (1 << 31) - 1) == 7
     assert nq.validate_gemm_q8_1_status(q8, 34 * ((1 << 31) - 1), (1 << 31) - 1, 32, 1 << 30) == 0
-    assert nq.gemm_q8_1_raw(q8, 0, 34, 1, 32, p, 9, p, 0) == 1
-    assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, 0, 9, p, 0) == 1
-    assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, p, 9, 0, 0) == 1
-    assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, p + 2, 9, p, 0) == 1   # activation blocks misaligned
-    assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, p, 9, p + 2, 0) == 1   # output misaligned
-    assert nq.gemm_q8_1_raw(q8, p, 35, 1, 32, p, 9, p, 0) == 6
+    assert nq.gemm_q8_1_raw(q8, 0, 34, 1, 32, p, 9, p, 0, 0, 0) == 1
+    assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, 0, 9, p, 0, 0, 0) == 1
+    assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, p, 9, 0, 0, 0, 0) == 1
+    assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, p + 2, 9, p, 0, 0, 0) == 1   # activation blocks misaligned
+    assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, p, 9, p + 2, 0, 0, 0) == 1   # output misaligned
+    assert nq.gemm_q8_1_raw(q8, p, 35, 1, 32, p, 9, p, 0, 0, 0) == 6
+    assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, p, 9, p, p + 2, 64, 0) == 1   # workspace misaligned
+
+
+def test_gemm_workspace_sizes():
+    """Splits only for more than 8 rows, few tiles and long K (no GPU: 256
+    compute units assumed), never for tq1_0; sizes nsplit * M * N * 4."""
+    assert nq.gemm_q8_1_workspace("gguf:q4_k", 4096, 14336, 8) == (0, 0)
+    assert nq.gemm_q8_1_workspace("gguf:tq1_0", 4096, 14336, 64) == (0, 0)
+    assert nq.gemm_q8_1_workspace("gguf:q4_k", 14336, 4096, 2048)[1] == 0      # 3584 tiles
+    assert nq.gemm_q8_1_workspace("gguf:q4_k", 4096, 1024, 64)[1] == 0         # 4 K steps
+    st, b = nq.gemm_q8_1_workspace("gguf:q4_k", 4096, 14336, 64)              # 32 tiles, 56 steps
+    assert st == 0 and b > 0 and b % (64 * 4096 * 4) == 0
+    assert 2 <= b // (64 * 4096 * 4) <= 14
+    st, b = nq.gemm_q8_1_workspace("gguf:q8_0", 4096, 14336, 512)             # 256 tiles: two splits
+    assert st == 0 and b == 2 * 512 * 4096 * 4
+    assert nq.gemm_q8_1_workspace("nvfp4", 1, 64, 9)[0] == 2
+    assert nq.gemm_q8_1_workspace("gguf:q4_k", 1, 100, 9)[0] == 5

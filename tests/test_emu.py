@@ -405,3 +405,19 @@ def test_emu_gemm_has_no_tq1_0_rewrite():
     y, rc, _, _ = emu_lib.gemm_q8_1(oracle.info("gguf:tq1_0")[0], np.zeros(54, np.uint8), 1, 256,
                                     np.zeros(36 * 8 * 9, np.uint8), 9)
     assert rc == -1
+
+
+@pytest.mark.parametrize("fmt", ["gguf:q4_k", "gguf:q8_0", "gguf:q6_k", "gguf:q2_k", "gguf:iq2_xs", "gguf:q4_1"])
+def test_emu_gemm_split_k(fmt):
+    """K split over workgroups (planned for a small device), partials summed in
+    split order: the criterion holds; every tile and split is met once."""
+    idx, B, S, _ = oracle.info(fmt)
+    for N, K, M, cus in [(200, 4096, 20, 64), (130, 2304, 70, 16)]:
+        w = synth.payload(fmt, N * K // B, N + M, synth.binade(-6, -2, False))
+        _, xq = oracle.quantize_q8_1(_act(M, K, 6).astype(np.float32))
+        y, rc, msg, guards, ns = emu_lib.gemm_q8_1(idx, w, N, K, xq, M, w_mis=1, cus=cus, with_splits=True)
+        assert rc == 0, msg
+        assert guards
+        assert ns >= 2
+        ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
+        linear_check(y, ref, env, K, f"{fmt} N={N} K={K} M={M} splits={ns}")

@@ -212,10 +212,10 @@ def test_gemv_k_not_a_multiple_of_128(fmt, K):
 # Batched products (any number of activation rows; more than 8 on the matrix
 # cores, tq1_0 through the single-row kernel 8 rows at a time).
 # --------------------------------------------------------------------------
-def _gemm(fmt, w_np, N, K, xq_np, w_off=0, stream=None):
+def _gemm(fmt, w_np, N, K, xq_np, w_off=0, stream=None, split=True):
     w, _keep = upload(w_np, w_off)
     xq = torch.from_numpy(np.ascontiguousarray(xq_np)).cuda()
-    y = nq.gemm_q8_1(fmt, w, N, K, xq, stream=stream)
+    y = nq.gemm_q8_1(fmt, w, N, K, xq, stream=stream, split=split)
     torch.cuda.synchronize()
     return y.cpu().numpy()
 
@@ -265,7 +265,8 @@ def test_gemm_repeats_bit_for_bit_and_on_a_side_stream(fmt):
 
 
 GEMM_FULL = [("gguf:q4_k", 14336, 4096, 512), ("gguf:q8_0", 4096, 14336, 512), ("gguf:q6_k", 4096, 4096, 200),
-             ("gguf:iq4_xs", 14336, 4096, 64), ("gguf:iq2_xxs", 4096, 4096, 100), ("gguf:q2_k", 1024, 14336, 72)]
+             ("gguf:iq4_xs", 14336, 4096, 64), ("gguf:iq2_xxs", 4096, 4096, 100), ("gguf:q2_k", 1024, 14336, 72),
+             ("gguf:q4_k", 4096, 14336, 64)]
 
 
 @pytest.mark.parametrize("fmt,N,K,M", GEMM_FULL)
@@ -294,3 +295,27 @@ def test_gemm_metadata_errors():
         nq.gemm_q8_1("gguf:q8_0", w[:33], 1, 32, xq)       # payload short
     with pytest.raises(nq.NqError):
         nq.gemm_q8_1("gguf:q4_k", w, 1, 32, xq)            # K not a multiple of 256
+
+
+@pytest.mark.parametrize("fmt,N,K,M", [("gguf:q4_k", 4096, 14336, 64), ("gguf:q6_k", 1000, 8192, 20),
+                                       ("gguf:q4_1", 500, 4096, 100)])
+def test_gemm_split_k(fmt, N, K, M):
+    """Shapes with few tiles and long K split K over workgroups (a workspace
+    is given): split and unsplit products both meet the criterion on sampled
+    rows, and each repeats bit for bit."""
+    st, ws_bytes = nq.gemm_q8_1_workspace(fmt, N, K, M)
+    assert st == 0 and ws_bytes > 0
+    w = _weights(fmt, N, K, 55)
+    _, xq = oracle.quantize_q8_1(_act(M, K, 56).astype(np.float32))
+    announce(f"gemm split {fmt} [{N}, {K}] x {M}")
+    a = _gemm(fmt, w, N, K, xq, split=True)
+    b = _gemm(fmt, w, N, K, xq, split=False)
+    a2 = _gemm(fmt, w, N, K, xq, split=True)
+    b2 = _gemm(fmt, w, N, K, xq, split=False)
+    assert np.array_equal(a.view(np.uint32), a2.view(np.uint32))
+    assert np.array_equal(b.view(np.uint32), b2.view(np.uint32))
+    rows = np.unique(np.r_[0, N - 1, np.random.default_rng(N).integers(0, N, size=30)])
+    sub = w.reshape(N, -1)[rows].ravel()
+    ref, env = oracle.gemv_q8_1(fmt, sub, rows.size, K, xq, M)
+    linear_check(a[:, rows], ref, env, K, f"{fmt} split")
+    linear_check(b[:, rows], ref, env, K, f"{fmt} unsplit")
