@@ -210,3 +210,20 @@ def test_criterion_admits_float32_orders(fmt):
     # and a gross mistake does not: drop one 32-value block of every row
     bad = blk - part[:, :, 3]
     assert np.any(np.abs(bad.astype(np.float64) - y) > tol)
+
+
+@pytest.mark.parametrize("fmt", ["gguf:q4_k", "gguf:q8_0", "gguf:iq2_xs", "gguf:q2_k", "gguf:tq1_0"])
+def test_gemv_matches_numpy_many_rows(fmt):
+    """The same product with more activation rows than the single-row kernel
+    takes (the batched product's reference)."""
+    N, K = _shape(fmt)
+    M = 40
+    w = _weights(fmt, N, K, 4321)
+    _, xq = oracle.quantize_q8_1(_act(M, K, 6).astype(np.float32))
+    y, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
+    wh = oracle.decode(fmt, w, [N, K]).astype(np.float64).reshape(N, K)
+    xh = oracle.decode("gguf:q8_1", xq.reshape(-1), [M, K]).astype(np.float64).reshape(M, K)
+    ref = xh @ wh.T
+    mag = np.abs(xh) @ np.abs(wh).T
+    assert np.all(np.abs(y - ref) <= 4 * K * 2.0 ** -53 * mag)
+    assert np.all(env >= mag * (1 - 1e-12))
