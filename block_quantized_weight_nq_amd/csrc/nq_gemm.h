@@ -20,7 +20,8 @@
 //     acc = fma(RN(ws_h * d), I_h, acc),  acc = fma(ow_h, d * S_h, acc)
 // (d * S_h is exact: at most 11 by 12 significant bits).  The offset term
 // exists for the five affine formats (q4_1, q5_1, q2_k, q4_k, q5_k); for
-// the others ws * c equals the decoded weight exactly.
+// the others ws * c equals the decoded weight exactly.  Every gguf format
+// has a rewrite.
 //
 // Tiling.  A workgroup (4 waves) owns a tile of 128 weight rows by 64
 // activation rows and walks K in steps of 256 values: its threads rewrite the
@@ -49,9 +50,8 @@ struct GmFmt {
                                 F == NVFP4_GGUF;
     // a code-independent term
     static constexpr bool AFF = F == Q4_1 || F == Q5_1 || F == Q2_K || F == Q4_K || F == Q5_K;
-    // formats with a span rewrite (tq1_0 has none: its products run through
-    // the single-row kernel)
-    static constexpr bool OK = F != TQ1_0 && F != NVFP4_DIV;
+    // formats with a span rewrite (every gguf format)
+    static constexpr bool OK = F != NVFP4_DIV;
     static constexpr uint32_t NH = U16 ? 2u : 1u;  // scales per span
     static constexpr uint32_t SPB = (uint32_t)block_values(F) / 32u;  // spans per block
     // LDS layout (dwords): weight codes [128][GM_CSW], scales [8][NH][128],
@@ -122,10 +122,6 @@ struct GmSrc {
     NQ_HD uint32_t dwx(uint32_t i) const { return base[i < last ? i : last]; }
 };
 
-// Byte-wise c - o for bytes c < 128 and 0 <= o <= 128: no borrow crosses a
-// byte, and the result bytes are the two's-complement differences.
-NQ_HD uint32_t bsub(uint32_t c, uint32_t o) { return ((c | 0x80808080u) - o) ^ 0x80808080u; }
-
 // Span p of the block at byte offset bo.
 template <int F, class Src>
 NQ_HD void gm_span(const Src &s, uint32_t bo, uint32_t p, const Tab &tab, GmSpan &o) {
@@ -175,7 +171,8 @@ NQ_HD void gm_span(const Src &s, uint32_t bo, uint32_t p, const Tab &tab, GmSpan
         // signed and its scales and offsets sorted into halves
         GvW w;
         gv_w<F>(s, bo, p, tab, w);
-        if constexpr (F == Q8_0 || F == Q8_1 || F == Q8_K || F == IQ4_NL || F == MXFP4 || F == IQ4_XS) {
+        if constexpr (F == Q8_0 || F == Q8_1 || F == Q8_K || F == IQ4_NL || F == MXFP4 || F == IQ4_XS ||
+                      F == TQ1_0) {
 #pragma unroll
             for (int j = 0; j < 8; j++) o.c[j] = w.q[j];
             o.ws[0] = o.ws[1] = w.f[0];

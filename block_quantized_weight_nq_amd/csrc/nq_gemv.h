@@ -18,9 +18,9 @@
 // weight row: it stages the row's bytes in LDS, its 64 lanes take the row's
 // items in turn and keep one FP32 partial per activation row, and the
 // partials then meet in a fixed cross-lane tree, so every run gives the same
-// bits.  Integer items (q4_0, q8_0, q4_k, q6_k) form exact 8-bit dot
-// products with the activation codes; the other formats decode 8-value
-// units to binary32 as the decode kernels do.
+// bits.  Every gguf format takes integer items: its weights become 8-bit
+// integers whose exact dot products with the activation codes are scaled in
+// binary32 (the decoded-unit path below remains for formats without one).
 #pragma once
 
 #include "nq_gqenc.h"
@@ -307,7 +307,7 @@ struct GvItem {
     // 256-value blocks in 32-value items (the IQ formats' 32-value groups)
     static constexpr bool IQ = F == IQ2_XXS || F == IQ2_XS || F == IQ2_S || F == IQ3_XXS || F == IQ3_S ||
                                F == IQ1_S || F == IQ1_M;
-    static constexpr bool I32 = F == IQ4_XS || F == Q8_K || F == TQ2_0 || F == Q2_K || F == Q3_K || IQ;
+    static constexpr bool I32 = F == IQ4_XS || F == Q8_K || F == TQ2_0 || F == TQ1_0 || F == Q2_K || F == Q3_K || IQ;
     // 128- and 64-value blocks in 32-value items
     static constexpr bool S32 = F == Q1_0 || F == Q2_0;
     static constexpr bool INT = B32 || I32 || S32 || F == Q4_K || F == Q5_K || F == Q6_K || F == NVFP4_GGUF;
@@ -333,6 +333,42 @@ NQ_HD uint32_t crumbs4(uint32_t b) { return (b | (b << 6) | (b << 12) | (b << 18
 
 // IQ sign byte: seven stored bits and their parity as bit 7.
 NQ_HD uint32_t iq_signs8(uint32_t s7) { return s7 | (parity7(s7) << 7); }
+
+// Byte-wise c - o for bytes c < 128 and 0 <= o <= 128: no borrow crosses a
+// byte, and the result bytes are the two's-complement differences.
+NQ_HD uint32_t bsub(uint32_t c, uint32_t o) { return ((c | 0x80808080u) - o) ^ 0x80808080u; }
+
+// Four base-3 digits as signed codes: byte b of the result is digit k of
+// byte b of w minus 1, by the decoder's digit rule floor(3 * ((byte * 3^k)
+// mod 256) / 256), two bytes per multiply in 16-bit fields (byte * 3^k <=
+// 20655 and 3 * 255 stay inside a field).
+NQ_HD uint32_t trits4(uint32_t w, uint32_t k) {
+    const uint32_t m = pow3(k);
+    const uint32_t e = ((((w & 0x00FF00FFu) * m) & 0x00FF00FFu) * 3u >> 8) & 0x00030003u;
+    const uint32_t o = (((((w >> 8) & 0x00FF00FFu) * m) & 0x00FF00FFu) * 3u >> 8) & 0x00030003u;
+    return bsub(e | (o << 8), 0x01010101u);
+}
+
+// The 32 codes (digit - 1, value order) of 32-value item p (< 8) of a tq1_0
+// block: values 32k + i (k < 5, i < 32) are digit k of byte i, values
+// 160 + 16k + i (k < 5, i < 16) digit k of byte 32 + i, values 240 + 4k + i
+// (k < 4, i < 4) digit k of byte 48 + i.  Branch-free over the item (a
+// wave's lanes take different items): each half reads one 16-byte window
+// and one digit.
+template <class Src>
+NQ_HD void tq1_item(const Src &s, uint32_t bo, uint32_t p, uint32_t (&c)[8]) {
+    const bool lo = p < 5u, tail = p == 7u;
+    const uint32_t k1 = lo ? p : tail ? 4u : 2u * (p - 5u);
+    uint32_t q1[4], q2[4], h[1];
+    window<4>(s, bo + (lo ? 0u : 32u), q1);
+    window<4>(s, bo + (lo ? 16u : 32u), q2);
+    window<1>(s, bo + 48u, h);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        c[j] = trits4(q1[j], k1);
+        c[4 + j] = tail ? trits4(h[0], (uint32_t)j) : trits4(q2[j], lo ? p : k1 + 1u);
+    }
+}
 
 // Decoded weights of one item (the fields a format uses).
 struct GvW {
@@ -468,6 +504,13 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
         w.f[0] = f16(u16_at(s, bo + 64u));
 #pragma unroll
         for (int j = 0; j < 8; j++) w.q[j] = (q[j] >> (2u * (part & 3u))) & 0x03030303u;
+    } else if constexpr (F == TQ1_0) {
+        // part p: 32 base-3 digits (tq1_item); d at 52; w = d * (digit - 1)
+        uint32_t c[8];
+        tq1_item(s, bo, part, c);
+        w.f[0] = f16(u16_at(s, bo + 52u));
+#pragma unroll
+        for (int j = 0; j < 8; j++) w.q[j] = c[j];
     } else if constexpr (F == NVFP4_GGUF) {
         // part p: groups 2p and 2p+1 (16 values each); group g's E4M3 scale
         // byte at g, its codes the low then the high nibbles of bytes
@@ -767,7 +810,7 @@ NQ_HD void gv_a(const Act &act, uint32_t m, uint32_t b, uint32_t part, GvA &x) {
 template <int F>
 NQ_HD float gv_dot(const GvW &w, const GvA &x, float acc) {
     constexpr uint32_t LO4 = 0x0F0F0F0Fu;
-    if constexpr (F == Q8_0 || F == Q8_1 || F == Q8_K || F == IQ4_NL || F == MXFP4 || F == IQ4_XS) {
+    if constexpr (F == Q8_0 || F == Q8_1 || F == Q8_K || F == IQ4_NL || F == MXFP4 || F == IQ4_XS || F == TQ1_0) {
         // w = scale * (8-bit integer): the scale times the exact dot product
         int I = 0;
 #pragma unroll

@@ -255,8 +255,7 @@ int nq_gemv_q8_1(int32_t format, const void *weight, uint64_t nbytes, int64_t N,
  * become signed 8-bit codes with a binary32 scale (and an offset for q4_1,
  * q5_1, q2_k, q4_k and q5_k), their exact integer dot products with the
  * activation codes come from the 8-bit matrix cores, and each is scaled and
- * added in binary32 (gguf:tq1_0 runs through the single-row kernel, 8
- * activation rows per launch).
+ * added in binary32.
  * When the output has few tiles and K is long, K is split over workgroups:
  * each split's partial output goes to `workspace` (device memory the caller
  * owns, at least the size nq_gemm_q8_1_workspace reports, 4-byte aligned, not

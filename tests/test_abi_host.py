@@ -298,9 +298,9 @@ def test_gemm_rejects_before_device():
 
 def test_gemm_workspace_sizes():
     """Splits only for more than 8 rows, few tiles and long K (no GPU: 256
-    compute units assumed), never for tq1_0; sizes nsplit * M * N * 4."""
+    compute units assumed); sizes nsplit * M * N * 4."""
     assert nq.gemm_q8_1_workspace("gguf:q4_k", 4096, 14336, 8) == (0, 0)
-    assert nq.gemm_q8_1_workspace("gguf:tq1_0", 4096, 14336, 64) == (0, 0)
+    assert nq.gemm_q8_1_workspace("gguf:tq1_0", 4096, 14336, 64)[1] > 0
     assert nq.gemm_q8_1_workspace("gguf:q4_k", 14336, 4096, 2048)[1] == 0      # 3584 tiles
     assert nq.gemm_q8_1_workspace("gguf:q4_k", 4096, 1024, 64)[1] == 0         # 4 K steps
     st, b = nq.gemm_q8_1_workspace("gguf:q4_k", 4096, 14336, 64)              # 32 tiles, 56 steps

@@ -360,7 +360,7 @@ def test_emu_gemv_k_not_a_multiple_of_128(fmt, K):
 # 16 x 16 x 32 8-bit matrix instruction, bounds-checked weight reads, every
 # tile met exactly once.
 # --------------------------------------------------------------------------
-GEMM_FMTS = [f for f in GGUF if f != "gguf:tq1_0"]
+GEMM_FMTS = GGUF
 
 
 def _gemm_k(B):
@@ -399,12 +399,6 @@ def test_emu_gemm_tile_order_covers_every_tile():
         ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
         linear_check(y, ref, env, K, f"{fmt} N={N} M={M}")
 
-
-def test_emu_gemm_has_no_tq1_0_rewrite():
-    """tq1_0 products take the single-row kernel (the entry point routes them)."""
-    y, rc, _, _ = emu_lib.gemm_q8_1(oracle.info("gguf:tq1_0")[0], np.zeros(54, np.uint8), 1, 256,
-                                    np.zeros(36 * 8 * 9, np.uint8), 9)
-    assert rc == -1
 
 
 @pytest.mark.parametrize("fmt", ["gguf:q4_k", "gguf:q8_0", "gguf:q6_k", "gguf:q2_k", "gguf:iq2_xs", "gguf:q4_1"])
