@@ -273,30 +273,13 @@ struct GvAct {
             return f16(p[0] & 0xFFFFu);
         }
     }
-    // the 8 codes (2 dwords) of unit u (8 values) and its block's scale
-    NQ_HD float unit(uint32_t m, uint32_t u, uint32_t (&c)[2]) const {
-        const uint32_t ab = u >> 2, co = 2u * (u & 3u);
-        if constexpr (ALDS) {
-            const uint32_t *cp = lds + m * K / 4u + 4u * act_group(K, 2u * ab + (co >> 2)) + (co & 3u);
-            c[0] = cp[0];
-            c[1] = cp[1];
-            return ((const float *)(lds + M * K / 4u))[m * kb + ab];
-        } else {
-            const uint32_t *p = xq + (uint64_t)m * xrow + (uint64_t)ab * 9u;
-            c[0] = p[1u + co];
-            c[1] = p[2u + co];
-            return f16(p[0] & 0xFFFFu);
-        }
-    }
 };
 
 // Items of the integer paths: a lane takes a group of weights of one block,
 // decodes them to 8-bit integers and multiplies them with the activation
 // codes of the same columns by 4-way dot products (exact integer sums); each
 // exact sum is then scaled in binary32 and added to the lane's partial.
-// Formats without such a path use 8-value units decoded exactly as the
-// decode kernels do (binary32), multiplied with the codes by an FMA chain.
-// An item is taken in three steps: its weights (gv_w, once per row), its
+// Every gguf format has such a path.  An item is taken in three steps: its weights (gv_w, once per row), its
 // activation columns (gv_a, once per activation row, shared by the rows of
 // a chunk) and the product (gv_dot).
 template <int F>
@@ -311,10 +294,10 @@ struct GvItem {
     // 128- and 64-value blocks in 32-value items
     static constexpr bool S32 = F == Q1_0 || F == Q2_0;
     static constexpr bool INT = B32 || I32 || S32 || F == Q4_K || F == Q5_K || F == Q6_K || F == NVFP4_GGUF;
+    static_assert(INT || F == NVFP4_DIV, "every gguf format takes integer items");
     // items per block
     static constexpr uint32_t IPB = B32 ? 1u : I32 ? 8u : S32 ? (uint32_t)block_values(F) / 32u
-                                  : (F == Q4_K || F == Q5_K || F == Q6_K) ? 4u
-                                  : F == NVFP4_GGUF ? 2u : (uint32_t)block_values(F) / 8u;
+                                  : (F == Q4_K || F == Q5_K || F == Q6_K) ? 4u : 2u;
 };
 
 // 5-bit codes: byte k of the result is bit 4 of 16 * (bit k of b), k < 4
@@ -771,8 +754,7 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
             w.f[2 * e + 1] = M(d, (float)(int8_t)((sw[e] >> 8) & 0xFFu));
         }
     } else {
-        // unit `part` (8 values) decoded as the decode kernels decode it
-        decode_unit<F>(s, bo, part, tab, w.f);
+        static_assert(F < 0, "format without integer items");
     }
 }
 
@@ -799,10 +781,7 @@ NQ_HD void gv_a(const Act &act, uint32_t m, uint32_t b, uint32_t part, GvA &x) {
 #pragma unroll
         for (int j = 0; j < 8; j++) x.c[8 + j] = c[j];
     } else {
-        uint32_t c2[2];
-        x.d[0] = act.unit(m, b * ((uint32_t)block_values(F) / 8u) + part, c2);
-        x.c[0] = c2[0];
-        x.c[1] = c2[1];
+        static_assert(F < 0, "format without integer items");
     }
 }
 
@@ -944,10 +923,8 @@ NQ_HD float gv_dot(const GvW &w, const GvA &x, float acc) {
         }
         return acc;
     } else {
-        float t = w.f[0] * (float)(int8_t)x.c[0];
-#pragma unroll
-        for (int j = 1; j < 8; j++) t = __builtin_fmaf(w.f[j], (float)(int8_t)(x.c[j >> 2] >> (8 * (j & 3))), t);
-        return __builtin_fmaf(t, x.d[0], acc);
+        static_assert(F < 0, "format without integer items");
+        return acc;
     }
 }
 
