@@ -319,3 +319,19 @@ def test_gemm_split_k(fmt, N, K, M):
     ref, env = oracle.gemv_q8_1(fmt, sub, rows.size, K, xq, M)
     linear_check(a[:, rows], ref, env, K, f"{fmt} split")
     linear_check(b[:, rows], ref, env, K, f"{fmt} unsplit")
+
+
+def test_gemm_more_activation_rows_than_one_launch_takes():
+    """65600 activation rows: the matrix-core product launches 65536 rows at a
+    time; sampled activation rows on both sides of the boundary, every weight
+    row, against the oracle."""
+    fmt, N, K, M = "gguf:q8_0", 40, 64, 65600
+    w = _weights(fmt, N, K, 91)
+    x = _act(M, K, 92).astype(np.float32)
+    _, xq = oracle.quantize_q8_1(x)
+    announce(f"gemm {fmt} [{N}, {K}] x {M}")
+    y = _gemm(fmt, w, N, K, xq)
+    rows = np.r_[0:40, 65500:65600]
+    ref, env = oracle.gemv_q8_1(fmt, w, N, K, np.ascontiguousarray(xq[rows]), rows.size)
+    linear_check(y[rows], ref, env, K, f"{fmt} M={M}")
+    assert np.all(np.isfinite(y))
