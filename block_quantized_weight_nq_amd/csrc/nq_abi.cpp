@@ -382,8 +382,9 @@ NQ_API int nq_gemm_q8_1_workspace(int32_t format, int64_t N, int64_t K, int64_t 
     const int st = nq_validate_gemm_q8_1(format, wbytes, N, K, M);
     if (st != NQ_OK) return st;
     if (M > nq::GV_MAX_M)
-        *bytes = nq::gm_workspace_bytes(nq::gm_plan((uint64_t)N, (uint64_t)K, (uint64_t)M, compute_units()),
-                                        (uint64_t)M, (uint64_t)N);
+        *bytes = nq::gm_ws_layout(format, nq::gm_plan((uint64_t)N, (uint64_t)K, (uint64_t)M, compute_units()),
+                                  (uint64_t)N, (uint64_t)K, (uint64_t)M)
+                     .total;
     return NQ_OK;
 }
 
@@ -393,7 +394,7 @@ NQ_API int nq_gemm_q8_1(int32_t format, const void *weight, uint64_t nbytes, int
     const int st = nq_validate_gemm_q8_1(format, nbytes, N, K, M);
     if (st != NQ_OK) return st;
     if (!weight || !xq || !y) return NQ_ERR_NULL_ARG;
-    if ((uintptr_t)xq % 4 != 0 || (uintptr_t)y % 4 != 0 || (uintptr_t)workspace % 4 != 0) return NQ_ERR_NULL_ARG;
+    if ((uintptr_t)xq % 4 != 0 || (uintptr_t)y % 4 != 0 || (uintptr_t)workspace % 16 != 0) return NQ_ERR_NULL_ARG;
     nq::GvLaunch L;
     L.w = (const uint8_t *)weight;
     L.N = (uint64_t)N;

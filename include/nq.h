@@ -258,19 +258,22 @@ int nq_gemv_q8_1(int32_t format, const void *weight, uint64_t nbytes, int64_t N,
  * added in binary32.
  * When the output has few tiles and K is long, K is split over workgroups:
  * each split's partial output goes to `workspace` (device memory the caller
- * owns, at least the size nq_gemm_q8_1_workspace reports, 4-byte aligned, not
- * overlapping the other buffers, and not used by another call until this
- * call's work on `stream` is done), and the partials are summed in split
- * order by a second launch.  With workspace NULL or smaller than that size
- * the product runs unsplit.  Repeated calls with the same shape, device and
- * workspace choice (given or not) give identical bits.
+ * owns, at least the size nq_gemm_q8_1_workspace reports, 16-byte aligned,
+ * not overlapping the other buffers, and not used by another call until
+ * this call's work on `stream` is done), and the partials are summed in
+ * split order by a second launch.  Above 1024 activation rows the weight's
+ * 8-bit codes, scales and offsets are also written there once per call
+ * (same values, same bits).  With workspace NULL or smaller than that size
+ * the product runs unsplit and without the once-per-call rewrite.  Repeated
+ * calls with the same shape, device and workspace choice (given or not)
+ * give identical bits.
  * nq_validate_gemm_q8_1 checks as nq_validate_gemv_q8_1 except that M may
  * be any count >= 1 below 2^31 with M * K / 32 * 36 and M * N * 4 below 2^63
  * (NQ_ERR_OVERFLOW).  nq_gemm_q8_1_workspace runs the same checks (nbytes
  * taken as the format's length rule) and stores the workspace size for the
  * shape on the current device (0 when the product would not split; `bytes`
  * NULL: NQ_ERR_NULL_ARG).  nq_gemm_q8_1 requires weight, xq and y non-NULL
- * and xq, y and workspace aligned to 4 bytes (NQ_ERR_NULL_ARG), then
+ * and xq and y aligned to 4 bytes and workspace to 16 (NQ_ERR_NULL_ARG), then
  * enqueues the product on `stream`.  The caller owns every buffer; y must not
  * overlap the inputs. */
 int nq_validate_gemm_q8_1(int32_t format, uint64_t nbytes, int64_t N, int64_t K, int64_t M);

@@ -377,16 +377,39 @@ long run_gemm(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint6
     static GmOps ops[64];
     static GmI<F> I[64];
     long errors = 0;
+    // cus > 0: a device of that many CUs with the workspace the plan asks
+    // for; 0: no workspace (neither split nor per-call rewrite)
     GmPlan plan = gm_plan(N, K, M, cus);
-    if (cus == 0 || plan.nsplit < 2) plan = GmPlan{1u, (uint32_t)((K / 32 + GM_SP - 1) / GM_SP)};
-    *nsplit_out = plan.nsplit;
-    std::vector<float> part(plan.nsplit > 1 ? gm_workspace_bytes(plan, M, N) / 4 : 0, 0.0f / 0.0f);
-    float *out = plan.nsplit > 1 ? part.data() : y;
+    if (cus == 0) plan = GmPlan{1u, (uint32_t)((K / 32 + GM_SP - 1) / GM_SP), false};
+    *nsplit_out = plan.nsplit | (plan.rewrite_once ? 1u << 16 : 0u);
+    const GmWsLayout wl = gm_ws_layout(F, plan, N, K, M);
+    std::vector<uint8_t> wsbuf(wl.total + 256, 0xA5);
+    uint8_t *wsp = wsbuf.data() + (256 - (uintptr_t)wsbuf.data() % 256) % 256;
+    float *part = (float *)wsp;
+    float *out = plan.nsplit > 1 ? part : y;
+    uint8_t *canon = plan.rewrite_once ? wsp : nullptr;
+    if (canon) {  // the rewrite launches, one item per thread
+        for (uint64_t r0 = 0; r0 < N;) {
+            const uint64_t rows = N - r0 < lim ? N - r0 : lim;
+            const GmArgs a = gm_args<F>(L, r0, rows, 0, 1, plan, out, canon, &wl);
+            Check chk{(uintptr_t)(w + r0 * row_bytes), (uintptr_t)(w + (r0 + rows) * row_bytes), 0, {0}};
+            const HostSrc src{a.wbase, a.wlast, &chk};
+            const uint64_t items = rows * (K / 32), blocks = (items + WG - 1) / WG;
+            for (uint64_t g = 0; g < blocks * WG; g++)
+                gm_rewrite_item<F>(a, src, tab, g, (uint32_t *)(canon + wl.codes + r0 * K),
+                                   (float *)(canon + wl.scales) + r0, (float *)(canon + wl.offsets) + r0);
+            if (chk.errors) {
+                if (errors == 0) snprintf(err, errlen, "rewrite: %s", chk.msg);
+                errors += chk.errors;
+            }
+            r0 += rows;
+        }
+    }
     for (uint64_t m0 = 0; m0 < M; m0 += mlim) {
         const uint64_t mrows = M - m0 < mlim ? M - m0 : mlim;
         for (uint64_t r0 = 0; r0 < N;) {
             const uint64_t rows = N - r0 < lim ? N - r0 : lim;
-            const GmArgs a = gm_args<F>(L, r0, rows, m0, mrows, plan, out);
+            const GmArgs a = gm_args<F>(L, r0, rows, m0, mrows, plan, out, canon, &wl);
             Check chk{(uintptr_t)(w + r0 * row_bytes), (uintptr_t)(w + (r0 + rows) * row_bytes), 0, {0}};
             const HostSrc src{a.wbase, a.wlast, &chk};
             const uint32_t grid = gm_grid(a);
@@ -414,8 +437,12 @@ long run_gemm(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint6
                                te = te0 < a.kspans ? te0 : a.kspans;
                 for (uint32_t t0 = tb; t0 < te; t0 += GM_SP) {
                     std::fill(lds.begin(), lds.end(), 0xA5A5A5A5u);
-                    for (uint32_t tid = 0; tid < (uint32_t)WG; tid++)
-                        gm_stage_w<F>(a, src, tab, n0, t0, tid, lds.data());
+                    for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) {
+                        if (a.cw)
+                            gm_stage_wc<F>(a, n0, t0, tid, lds.data());
+                        else
+                            gm_stage_w<F>(a, src, tab, n0, t0, tid, lds.data());
+                    }
                     for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) gm_stage_x<F>(a, mt0, t0, tid, lds.data());
                     const uint32_t nsp = te - t0 < GM_SP ? te - t0 : GM_SP;
                     for (uint32_t sp = 0; sp < nsp; sp++)

@@ -186,9 +186,11 @@ def gemv_q8_1(fmt_id, w, N, K, xq, M, w_mis=0, resident=2048, max_rows=0):
 
 
 def gemm_q8_1(fmt_id, w, N, K, xq, M, w_mis=0, max_rows=0, max_mrows=0, cus=0, with_splits=False):
-    """The matrix-core product through the emulator (cus > 0: K split as
-    planned for that many compute units).  Returns (y float32 [M, N], bad
-    reads, message, guards_ok[, K splits]); bad reads is -1 for a format
+    """The matrix-core product through the emulator (cus > 0: a device of
+    that many compute units with the workspace its plan asks for: K split,
+    and the weight rewritten once per call for more than 64 activation rows;
+    0: no workspace).  Returns (y float32 [M, N], bad reads, message,
+    guards_ok[, (K splits, rewritten once)]); bad reads is -1 for a format
     without a span rewrite."""
     w = np.ascontiguousarray(w, dtype=np.uint8)
     wbuf, woff = _placed(w.size, 16, w_mis)
@@ -204,7 +206,7 @@ def gemm_q8_1(fmt_id, w, N, K, xq, M, w_mis=0, max_rows=0, max_mrows=0, cus=0, w
     y = ybuf[16:16 + M * N].reshape(M, N).copy()
     guards = bool(np.all(np.isnan(ybuf[:16])) and np.all(np.isnan(ybuf[16 + M * N:])))
     if with_splits:
-        return y, rc, err.value.decode(), guards, ns.value
+        return y, rc, err.value.decode(), guards, (ns.value & 0xFFFF, bool(ns.value >> 16))
     return y, rc, err.value.decode(), guards
 
 

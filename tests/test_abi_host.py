@@ -293,20 +293,29 @@ def test_gemm_rejects_before_device():
     assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, p + 2, 9, p, 0, 0, 0) == 1   # activation blocks misaligned
     assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, p, 9, p + 2, 0, 0, 0) == 1   # output misaligned
     assert nq.gemm_q8_1_raw(q8, p, 35, 1, 32, p, 9, p, 0, 0, 0) == 6
-    assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, p, 9, p, p + 2, 64, 0) == 1   # workspace misaligned
+    assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, p, 9, p, p + 8, 64, 0) == 1   # workspace not 16-byte aligned
 
 
 def test_gemm_workspace_sizes():
-    """Splits only for more than 8 rows, few tiles and long K (no GPU: 256
-    compute units assumed); sizes nsplit * M * N * 4."""
+    """The workspace holds the K-split partials (more than 8 rows, few tiles,
+    long K; no GPU: 256 compute units assumed) and, above 1024 activation rows,
+    the weight rewritten once: N K code bytes, then K / 32 * NH * N binary32
+    scales and, for the affine formats, as many offsets (each part rounded
+    up to 256 bytes)."""
     assert nq.gemm_q8_1_workspace("gguf:q4_k", 4096, 14336, 8) == (0, 0)
-    assert nq.gemm_q8_1_workspace("gguf:tq1_0", 4096, 14336, 64)[1] > 0
-    assert nq.gemm_q8_1_workspace("gguf:q4_k", 14336, 4096, 2048)[1] == 0      # 3584 tiles
-    assert nq.gemm_q8_1_workspace("gguf:q4_k", 4096, 1024, 64)[1] == 0         # 4 K steps
-    st, b = nq.gemm_q8_1_workspace("gguf:q4_k", 4096, 14336, 64)              # 32 tiles, 56 steps
+    assert nq.gemm_q8_1_workspace("gguf:q4_k", 4096, 1024, 64) == (0, 0)      # 4 K steps, one activation tile
+    st, b = nq.gemm_q8_1_workspace("gguf:q4_k", 4096, 14336, 64)              # 32 tiles, 56 steps: split only
     assert st == 0 and b > 0 and b % (64 * 4096 * 4) == 0
     assert 2 <= b // (64 * 4096 * 4) <= 14
-    st, b = nq.gemm_q8_1_workspace("gguf:q8_0", 4096, 14336, 512)             # 256 tiles: two splits
-    assert st == 0 and b == 2 * 512 * 4096 * 4
+    assert nq.gemm_q8_1_workspace("gguf:tq1_0", 4096, 14336, 64)[1] > 0
+    # 3584 tiles: no split; q4_k: 14336 * 4096 code bytes, scales and offsets 128 * 14336 * 4 each
+    assert nq.gemm_q8_1_workspace("gguf:q4_k", 14336, 4096, 2048) == (0, 58720256 + 2 * 7340032)
+    # q6_k: two scales per span, no offsets
+    assert nq.gemm_q8_1_workspace("gguf:q6_k", 14336, 4096, 2048) == (0, 58720256 + 2 * 7340032)
+    assert nq.gemm_q8_1_workspace("gguf:q8_0", 14336, 4096, 2048) == (0, 58720256 + 7340032)
+    # 256 tiles: two K splits (2 * 512 * 4096 binary32), no rewrite at 512 rows
+    assert nq.gemm_q8_1_workspace("gguf:q8_0", 4096, 14336, 512) == (0, 16777216)
+    assert nq.gemm_q8_1_workspace("gguf:q8_0", 14336, 4096, 1024) == (0, 0)
+    assert nq.gemm_q8_1_workspace("gguf:q8_0", 14336, 4096, 1025) == (0, 58720256 + 7340032)
     assert nq.gemm_q8_1_workspace("nvfp4", 1, 64, 9)[0] == 2
     assert nq.gemm_q8_1_workspace("gguf:q4_k", 1, 100, 9)[0] == 5

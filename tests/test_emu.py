@@ -372,16 +372,18 @@ def _gemm_k(B):
 def test_emu_gemm_matches_oracle(fmt):
     idx, B, S, _ = oracle.info(fmt)
     K = _gemm_k(B)
-    for N, M, w_mis, max_rows, max_mrows in [(150, 9, 0, 0, 0), (37, 70, 1, 0, 0), (260, 65, 3, 128, 0),
-                                             (130, 100, 2, 0, 40)]:
+    for N, M, w_mis, max_rows, max_mrows, cus in [(150, 9, 0, 0, 0, 0), (37, 70, 1, 0, 0, 0),
+                                                  (260, 65, 3, 128, 0, 256), (130, 100, 2, 0, 40, 256),
+                                                  (37, 1100, 1, 0, 500, 256), (140, 1030, 2, 128, 0, 256)]:
         w = synth.payload(fmt, N * K // B, 7 + N, synth.binade(-6, -2, False))
         _, xq = oracle.quantize_q8_1(_act(M, K, M).astype(np.float32))
-        y, rc, msg, guards = emu_lib.gemm_q8_1(idx, w, N, K, xq, M, w_mis=w_mis, max_rows=max_rows,
-                                               max_mrows=max_mrows)
+        y, rc, msg, guards, (ns, once) = emu_lib.gemm_q8_1(idx, w, N, K, xq, M, w_mis=w_mis, max_rows=max_rows,
+                                                            max_mrows=max_mrows, cus=cus, with_splits=True)
         assert rc == 0, msg
         assert guards
+        assert once == (cus > 0 and M > 1024)
         ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
-        linear_check(y, ref, env, K, f"{fmt} N={N} M={M}")
+        linear_check(y, ref, env, K, f"{fmt} N={N} M={M} rewritten once={once}")
 
 
 def test_emu_gemm_tile_order_covers_every_tile():
@@ -409,9 +411,11 @@ def test_emu_gemm_split_k(fmt):
     for N, K, M, cus in [(200, 4096, 20, 64), (130, 2304, 70, 16)]:
         w = synth.payload(fmt, N * K // B, N + M, synth.binade(-6, -2, False))
         _, xq = oracle.quantize_q8_1(_act(M, K, 6).astype(np.float32))
-        y, rc, msg, guards, ns = emu_lib.gemm_q8_1(idx, w, N, K, xq, M, w_mis=1, cus=cus, with_splits=True)
+        y, rc, msg, guards, (ns, once) = emu_lib.gemm_q8_1(idx, w, N, K, xq, M, w_mis=1, cus=cus,
+                                                            with_splits=True)
         assert rc == 0, msg
         assert guards
         assert ns >= 2
+        assert not once
         ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
         linear_check(y, ref, env, K, f"{fmt} N={N} K={K} M={M} splits={ns}")

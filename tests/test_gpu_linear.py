@@ -335,3 +335,23 @@ def test_gemm_more_activation_rows_than_one_launch_takes():
     ref, env = oracle.gemv_q8_1(fmt, w, N, K, np.ascontiguousarray(xq[rows]), rows.size)
     linear_check(y[rows], ref, env, K, f"{fmt} M={M}")
     assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("fmt", ["gguf:q4_k", "gguf:q2_k", "gguf:iq2_s", "gguf:q8_0", "gguf:tq1_0", "gguf:q5_1"])
+def test_gemm_weight_rewritten_once_is_the_same_product(fmt):
+    """Above 1024 activation rows the weight is rewritten once per call into
+    the workspace; the tiles then copy the same codes and scales they would
+    rewrite themselves, so the bits equal the workspace-free product's (K below
+    8 steps: no K split)."""
+    _, B, _, _ = oracle.info(fmt)
+    N, K, M = 300, 1024, 1100
+    st, ws_bytes = nq.gemm_q8_1_workspace(fmt, N, K, M)
+    assert st == 0 and ws_bytes >= N * K
+    w = _weights(fmt, N, K, 61)
+    _, xq = oracle.quantize_q8_1(_act(M, K, 62).astype(np.float32))
+    announce(f"gemm rewrite once {fmt}")
+    a = _gemm(fmt, w, N, K, xq, w_off=1, split=True)
+    b = _gemm(fmt, w, N, K, xq, w_off=1, split=False)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
+    linear_check(a, ref, env, K, fmt)
