@@ -367,7 +367,7 @@ def gemm_measurement(torch, nq, synth, fmt, shape, M, launches=20, footprint=1 <
     res = {"shape": shape, "M": M, "tops": round(tops, 1), "frac_alu_peak": round(tops / GEMM_ALU_PEAK_TOPS, 4),
            "frac_mfma_i8_peak": round(tops / MFMA_I8_PEAK_TOPS, 4), "mean_launch_us": round(mean_ms * 1e3, 3),
            "weight_gbps": round(nbytes_w / (mean_ms * 1e-3) / 1e9, 1), "replicas": reps,
-           "k_splits": ws_bytes // (4 * M * N) if ws_bytes else 1}
+           "workspace_bytes": ws_bytes}
     del g, ws, w0, work
     torch.cuda.empty_cache()
     return res

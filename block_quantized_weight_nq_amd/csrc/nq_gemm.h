@@ -340,14 +340,18 @@ NQ_HD void gm_stage_wc(const GmArgs &a, uint32_t n0, uint32_t t0, uint32_t tid, 
     }
 }
 
-// The per-call rewrite, item g of a launch (row g mod rows, span g / rows:
-// consecutive items are consecutive rows, so the scale stores coalesce):
-// codes to cw (K bytes per row), scales and offsets to cs / co.
+// The per-call rewrite, item g of a launch: groups of 8 items are 8
+// consecutive spans of one row (their codes 256 contiguous bytes), groups
+// run over the rows first (row (g / 8) mod rows, spans 8 ((g / 8) / rows)
+// + g mod 8); codes to cw (K bytes per row), scales and offsets to cs / co.
+NQ_HD uint64_t gm_rewrite_items(uint32_t rows, uint32_t kspans) { return (uint64_t)rows * ((kspans + 7u) / 8u) * 8u; }
+
 template <int F, class Src>
 NQ_HD void gm_rewrite_item(const GmArgs &a, const Src &src, const Tab &tab, uint64_t g, uint32_t *cw, float *cs,
                            float *co) {
     using G = GmFmt<F>;
-    const uint32_t n = (uint32_t)(g % a.rows), t = (uint32_t)(g / a.rows);
+    const uint64_t g8 = g >> 3;
+    const uint32_t n = (uint32_t)(g8 % a.rows), t = (uint32_t)(g8 / a.rows) * 8u + (uint32_t)(g & 7u);
     if (t >= a.kspans) return;
     const uint32_t b = t / G::SPB;
     GmSpan o;
@@ -715,7 +719,7 @@ int launch_gemm_mfma(const GvLaunch &L, void *ws, uint64_t ws_bytes, hipStream_t
         for (uint64_t r0 = 0; r0 < L.N;) {
             const uint64_t rows = L.N - r0 < max_rows ? L.N - r0 : max_rows;
             const GmArgs a = gm_args<F>(L, r0, rows, 0, 1, p, out, canon, &wl);
-            const uint64_t items = rows * (L.K / 32), blocks = (items + WG - 1) / WG;
+            const uint64_t blocks = (gm_rewrite_items(a.rows, a.kspans) + WG - 1) / WG;
             hipLaunchKernelGGL((k_gemm_rewrite<F>), dim3((uint32_t)blocks), dim3(WG), 0, stream, a,
                                (uint32_t *)(canon + wl.codes + r0 * L.K), (float *)(canon + wl.scales) + r0,
                                (float *)(canon + wl.offsets) + r0);

@@ -394,7 +394,7 @@ long run_gemm(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint6
             const GmArgs a = gm_args<F>(L, r0, rows, 0, 1, plan, out, canon, &wl);
             Check chk{(uintptr_t)(w + r0 * row_bytes), (uintptr_t)(w + (r0 + rows) * row_bytes), 0, {0}};
             const HostSrc src{a.wbase, a.wlast, &chk};
-            const uint64_t items = rows * (K / 32), blocks = (items + WG - 1) / WG;
+            const uint64_t blocks = (gm_rewrite_items(a.rows, a.kspans) + WG - 1) / WG;
             for (uint64_t g = 0; g < blocks * WG; g++)
                 gm_rewrite_item<F>(a, src, tab, g, (uint32_t *)(canon + wl.codes + r0 * K),
                                    (float *)(canon + wl.scales) + r0, (float *)(canon + wl.offsets) + r0);
