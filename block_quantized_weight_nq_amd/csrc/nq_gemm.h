@@ -4,7 +4,8 @@
 // NInfer "tensor-formats" page, GGUF linear operations: the activation is
 // quantized to ggml q8_1 blocks (one binary16 scale per 32 values) and the
 // product accumulates in FP32.  The value each weight stands for is the one
-// the format's decoder gives (the gguf "Packed layouts" of the second page).
+// the format's decoder gives (DequantizePacked decoding specification,
+// "Packed layouts and decoding" and "Mathematical decoding rules").
 //
 // Spans.  Every 32 consecutive values of a weight row (a span; no span
 // crosses a block) are rewritten as 32 signed 8-bit codes c with, per half of
@@ -30,7 +31,10 @@
 // computes a 64 x 32 sub-tile, span by span, in a fixed order, so every run
 // of a launch shape gives the same bits.  Tiles that share weight rows are
 // given to workgroups of one XCD (workgroups go to the 8 XCDs in turn), so
-// the weight bytes come from one L2.
+// the weight bytes come from one L2.  With a workspace, shapes with few
+// tiles and long K split K over workgroups (partial outputs summed in split
+// order by a second launch), and large batches have the weight rewritten
+// once per call so that the tiles copy it (gm_plan).
 #pragma once
 
 #include "nq_gemv.h"

@@ -419,3 +419,26 @@ def test_emu_gemm_split_k(fmt):
         assert not once
         ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
         linear_check(y, ref, env, K, f"{fmt} N={N} K={K} M={M} splits={ns}")
+
+
+@pytest.mark.parametrize("M", [3, 70])
+def test_emu_products_over_non_finite_scales(M):
+    """Rows with an infinite or NaN weight scale give non-finite outputs on
+    both sides (which non-finite value may differ); the other rows meet the
+    criterion (single-row kernel for 3 activation rows, matrix cores for 70)."""
+    fmt, N, K = "gguf:q8_0", 40, 256
+    idx, B, S, _ = oracle.info(fmt)
+    w = synth.payload(fmt, N * K // B, 71, synth.binade(-6, -2, True)).copy()
+    blk = w.reshape(N, K // 32, 34)
+    blk[3, 1, 0:2] = [0x00, 0x7C]
+    blk[5, 0, 0:2] = [0x00, 0x7E]
+    _, xq = oracle.quantize_q8_1(_act(M, K, 72).astype(np.float32))
+    ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
+    run = emu_lib.gemv_q8_1 if M <= 8 else emu_lib.gemm_q8_1
+    y, rc, msg, guards = run(idx, w, N, K, xq, M)
+    assert rc == 0, msg
+    assert guards
+    bad = np.zeros(N, bool)
+    bad[[3, 5]] = True
+    assert not np.any(np.isfinite(y[:, bad])) and not np.any(np.isfinite(ref[:, bad]))
+    linear_check(y[:, ~bad], ref[:, ~bad], env[:, ~bad], K, f"{fmt} finite rows")

@@ -355,3 +355,24 @@ def test_gemm_weight_rewritten_once_is_the_same_product(fmt):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
     ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
     linear_check(a, ref, env, K, fmt)
+
+
+@pytest.mark.parametrize("M", [3, 70])
+def test_products_over_non_finite_scales(M):
+    """A weight block with an infinite and one with a NaN binary16 scale: the
+    outputs of those rows are non-finite in both the kernels and the oracle
+    (which non-finite value may differ: the integer paths scale an exact
+    integer sum); every other output meets the criterion."""
+    fmt, N, K = "gguf:q8_0", 40, 256
+    w = _weights(fmt, N, K, 71).copy()
+    blk = w.reshape(N, K // 32, 34)
+    blk[3, 1, 0:2] = [0x00, 0x7C]   # +inf
+    blk[5, 0, 0:2] = [0x00, 0x7E]   # NaN
+    _, xq = oracle.quantize_q8_1(_act(M, K, 72).astype(np.float32))
+    ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
+    announce(f"non-finite scales M={M}")
+    y = _gemm(fmt, w, N, K, xq)
+    bad = np.zeros(N, bool)
+    bad[[3, 5]] = True
+    assert not np.any(np.isfinite(y[:, bad])) and not np.any(np.isfinite(ref[:, bad]))
+    linear_check(y[:, ~bad], ref[:, ~bad], env[:, ~bad], K, f"{fmt} finite rows")
