@@ -18,10 +18,13 @@
 // products); scales with 16-value halves take two MFMAs per span, each with
 // the activation codes of the other half set to zero.  The scaling is done
 // in binary32, per span and half:
-//     acc = fma(RN(ws_h * d), I_h, acc),  acc = fma(ow_h, d * S_h, acc)
-// (d * S_h is exact: at most 11 by 12 significant bits).  The offset term
-// exists for the five affine formats (q4_1, q5_1, q2_k, q4_k, q5_k); for
-// the others ws * c equals the decoded weight exactly.  Every gguf format
+//     acc = fma(RN(ws_h * d), I_h, acc)
+// and, for the five affine formats (q4_1, q5_1, q2_k, q4_k, q5_k), the
+// offset terms ow_h * (d * S_h) of a K step (d * S_h is exact: at most 11 by
+// 12 significant bits) are added four spans at a time by
+// v_mfma_f32_16x16x4_f32, the binary32 matrix instruction, into the same
+// accumulators; for the other formats ws * c equals the decoded weight
+// exactly.  Every gguf format
 // has a rewrite.
 //
 // Tiling.  A workgroup (4 waves) owns a tile of 128 weight rows by 64
@@ -459,33 +462,26 @@ struct GmI {
 };
 
 // The span's scaling into the lane's accumulators (fixed order: per output,
-// the halves, then the offsets).
+// the halves).  The affine formats' offset terms are added per K step by
+// gm_offsets on the matrix cores.
 template <int F>
 NQ_HD void gm_epi(const uint32_t *lds, uint32_t w, uint32_t lane, uint32_t sp, const GmI<F> &I,
                   float (&acc)[4][2][4]) {
     using G = GmFmt<F>;
     const uint32_t nb = 64u * (w & 1u) + 4u * (lane >> 4), mb = 32u * (w >> 1) + (lane & 15u);
-    const float *ws = (const float *)(lds + G::WS), *ow = (const float *)(lds + G::WO);
-    const float *xd = (const float *)(lds + G::XD), *xt = (const float *)(lds + G::XT);
-    float d[2], T[2][2];
+    const float *ws = (const float *)(lds + G::WS);
+    const float *xd = (const float *)(lds + G::XD);
+    float d[2];
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-        d[j] = xd[sp * GM_BM + mb + 16u * (uint32_t)j];
-#pragma unroll
-        for (uint32_t h = 0; h < G::NH; h++)
-            T[h][j] = G::AFF ? xt[(sp * G::NH + h) * GM_BM + mb + 16u * (uint32_t)j] : 0.0f;
-    }
+    for (int j = 0; j < 2; j++) d[j] = xd[sp * GM_BM + mb + 16u * (uint32_t)j];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        float sw[2][4], so[2][4];
+        float sw[2][4];
 #pragma unroll
         for (uint32_t h = 0; h < G::NH; h++)
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const uint32_t n = (sp * G::NH + h) * GM_BN + nb + 16u * (uint32_t)i + (uint32_t)e;
-                sw[h][e] = ws[n];
-                so[h][e] = G::AFF ? ow[n] : 0.0f;
-            }
+            for (int e = 0; e < 4; e++)
+                sw[h][e] = ws[(sp * G::NH + h) * GM_BN + nb + 16u * (uint32_t)i + (uint32_t)e];
 #pragma unroll
         for (int j = 0; j < 2; j++)
 #pragma unroll
@@ -493,13 +489,30 @@ NQ_HD void gm_epi(const uint32_t *lds, uint32_t w, uint32_t lane, uint32_t sp, c
                 float a = acc[i][j][e];
 #pragma unroll
                 for (uint32_t h = 0; h < G::NH; h++) a = __builtin_fmaf(sw[h][e] * d[j], (float)I.v[h][i][j][e], a);
-                if constexpr (G::AFF) {
-#pragma unroll
-                    for (uint32_t h = 0; h < G::NH; h++) a = __builtin_fmaf(so[h][e], T[h][j], a);
-                }
                 acc[i][j][e] = a;
             }
     }
+}
+
+// Offset terms of the affine formats for one K step: with k = span * NH +
+// half, they add sum_k ow[k][n] * (d S)[k][m] to every output, a product of
+// the [n, k] offsets and the [k, m] terms.  v_mfma_f32_16x16x4_f32 adds four
+// k at a time into the accumulators (A[i][k]: lane l supplies row l mod 16,
+// k = l / 16; B[k][j] likewise; the result has the int8 tiles' lane layout).
+// Operands of quad q for a lane (k past the step's nk are zeros).
+template <int F>
+NQ_HD void gm_offsets_ops(const uint32_t *lds, uint32_t w, uint32_t lane, uint32_t q, uint32_t nk, float (&A)[4],
+                          float (&B)[2]) {
+    using G = GmFmt<F>;
+    const uint32_t k = 4u * q + (lane >> 4), r = lane & 15u;
+    const uint32_t nb = 64u * (w & 1u), mb = 32u * (w >> 1);
+    const float *ow = (const float *)(lds + G::WO), *xt = (const float *)(lds + G::XT);
+    const bool in = k < nk;
+    const uint32_t kk = in ? k : 0u;
+#pragma unroll
+    for (int i = 0; i < 4; i++) A[i] = in ? ow[kk * GM_BN + nb + 16u * (uint32_t)i + r] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 2; j++) B[j] = in ? xt[kk * GM_BM + mb + 16u * (uint32_t)j + r] : 0.0f;
 }
 
 // The lane's outputs: y[m][n] for its 4 x 2 x 4 (row, activation row) pairs
@@ -573,6 +586,23 @@ __global__ __launch_bounds__(WG) void k_gemm(GmArgs a) {
                     }
                 }
             gm_epi<F>(lds, w, lane, sp, I, acc);
+        }
+        if constexpr (G::AFF) {
+            typedef float gm_f32x4 __attribute__((ext_vector_type(4)));
+            const uint32_t nk = nsp * G::NH;
+            for (uint32_t q = 0; 4u * q < nk; q++) {
+                float A[4], B[2];
+                gm_offsets_ops<F>(lds, w, lane, q, nk, A, B);
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+#pragma unroll
+                    for (int j = 0; j < 2; j++) {
+                        gm_f32x4 c = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+                        c = __builtin_amdgcn_mfma_f32_16x16x4f32(A[i], B[j], c, 0, 0, 0);
+#pragma unroll
+                        for (int e = 0; e < 4; e++) acc[i][j][e] = c[e];
+                    }
+            }
         }
     }
     gm_store(a, n0, m0, ks, w, lane, acc);

@@ -11,6 +11,7 @@
 // with -DNQ_EMU_PART=p -DNQ_EMU_PARTS=P instantiates the block formats whose
 // id is p mod P and registers them in the dispatch table; the build without
 // NQ_EMU_PART holds the table and the exported entry points.
+#include <cmath>
 #include <cstdio>
 #include <algorithm>
 #include <cstring>
@@ -351,6 +352,21 @@ void mfma_i8_16x16x32(const uint64_t (&A)[64], const uint64_t (&B)[64], int (&D)
         }
 }
 
+// The 16 x 16 x 4 binary32 matrix instruction of one wave (D = C + A B):
+// lane l supplies A[l mod 16][l / 16] and B[l / 16][l mod 16] and holds
+// C / D[4 (l / 16) + e][l mod 16]; the sum is formed here as a chain of
+// fused multiply-adds in k order (the hardware's internal order may differ
+// in the last bits; the results are judged by the criterion).
+void mfma_f32_16x16x4(const float (&A)[64], const float (&B)[64], float (&C)[64][4]) {
+    for (int l = 0; l < 64; l++)
+        for (int e = 0; e < 4; e++) {
+            const int i = 4 * (l / 16) + e, j = l % 16;
+            float c = C[l][e];
+            for (int k = 0; k < 4; k++) c = std::fma(A[16 * k + i], B[16 * k + j], c);
+            C[l][e] = c;
+        }
+}
+
 // Batched product on the matrix cores: the launcher's launches (max_rows /
 // max_mrows > 0 override its weight-row and activation-row limits; cus > 0
 // plans K splits for that many compute units, with a workspace), and per
@@ -464,6 +480,31 @@ long run_gemm(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint6
                             for (uint32_t lane = 0; lane < 64u; lane++)
                                 gm_epi<F>(lds.data(), wv, lane, sp, I[lane], acc[wv][lane]);
                         }
+                    if constexpr (G::AFF) {
+                        const uint32_t nk = nsp * G::NH;
+                        for (uint32_t q = 0; 4u * q < nk; q++)
+                            for (uint32_t wv = 0; wv < 4u; wv++) {
+                                float Al[64][4], Bl[64][2];
+                                for (uint32_t lane = 0; lane < 64u; lane++) {
+                                    float a4[4], b2[2];
+                                    gm_offsets_ops<F>(lds.data(), wv, lane, q, nk, a4, b2);
+                                    for (int i = 0; i < 4; i++) Al[lane][i] = a4[i];
+                                    for (int j = 0; j < 2; j++) Bl[lane][j] = b2[j];
+                                }
+                                for (int i = 0; i < 4; i++)
+                                    for (int j = 0; j < 2; j++) {
+                                        float A[64], B[64], C[64][4];
+                                        for (int l = 0; l < 64; l++) {
+                                            A[l] = Al[l][i];
+                                            B[l] = Bl[l][j];
+                                            for (int e = 0; e < 4; e++) C[l][e] = acc[wv][l][i][j][e];
+                                        }
+                                        mfma_f32_16x16x4(A, B, C);
+                                        for (int l = 0; l < 64; l++)
+                                            for (int e = 0; e < 4; e++) acc[wv][l][i][j][e] = C[l][e];
+                                    }
+                            }
+                    }
                 }
                 for (uint32_t wv = 0; wv < 4u; wv++)
                     for (uint32_t lane = 0; lane < 64u; lane++) gm_store(a, n0, mt0, ks, wv, lane, acc[wv][lane]);
