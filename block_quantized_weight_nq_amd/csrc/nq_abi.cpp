@@ -381,7 +381,7 @@ NQ_API int nq_gemm_q8_1_workspace(int32_t format, int64_t N, int64_t K, int64_t 
         return NQ_ERR_OVERFLOW;
     const int st = nq_validate_gemm_q8_1(format, wbytes, N, K, M);
     if (st != NQ_OK) return st;
-    if (M > nq::GV_MAX_M)
+    if ((uint64_t)M >= nq::GM_MIN_M)
         *bytes = nq::gm_ws_layout(format, nq::gm_plan((uint64_t)N, (uint64_t)K, (uint64_t)M, compute_units()),
                                   (uint64_t)N, (uint64_t)K, (uint64_t)M)
                      .total;
@@ -403,7 +403,7 @@ NQ_API int nq_gemm_q8_1(int32_t format, const void *weight, uint64_t nbytes, int
     L.xq = (const uint8_t *)xq;
     L.y = y;
     L.cus = compute_units();
-    if (M > nq::GV_MAX_M) {
+    if ((uint64_t)M >= nq::GM_MIN_M) {
         switch (REGISTRY[format].family) {
         case NQ_FAMILY_SIMPLE: return nq::launch_gemm_simple(format, L, workspace, workspace_bytes, stream);
         case NQ_FAMILY_KQUANT: return nq::launch_gemm_kquant(format, L, workspace, workspace_bytes, stream);
@@ -411,7 +411,7 @@ NQ_API int nq_gemm_q8_1(int32_t format, const void *weight, uint64_t nbytes, int
         default: return nq::launch_gemm_fp4t(format, L, workspace, workspace_bytes, stream);
         }
     }
-    // the single-row kernel, 8 activation rows per launch
+    // fewer rows: the single-row kernel (one launch)
     for (int64_t m0 = 0; m0 < M; m0 += nq::GV_MAX_M) {
         nq::GvLaunch l = L;
         l.M = (uint64_t)(M - m0 < nq::GV_MAX_M ? M - m0 : nq::GV_MAX_M);

@@ -45,10 +45,11 @@
 namespace nq {
 
 constexpr uint32_t GM_BN = 128;            // weight rows per tile
-constexpr uint32_t GM_BM = 64;             // activation rows per tile
+constexpr uint32_t GM_BM = 64;             // activation rows per tile (32 for batches of at most 32 rows)
 constexpr uint32_t GM_SP = 8;              // spans per K step (256 values)
 constexpr uint32_t GM_CSW = 8u * GM_SP + 4u;  // LDS dwords per code row (256 code bytes + 16 of padding)
 constexpr uint64_t GM_MAX_MROWS = 1ull << 16;  // activation rows per launch
+constexpr uint64_t GM_MIN_M = 5;  // fewer activation rows take the single-row kernel (faster there)
 constexpr uint64_t GM_REWRITE_ONCE_M = 1024;   // more activation rows: the weight is rewritten once per call
 
 // one scale per 16 values
@@ -58,8 +59,13 @@ NQ_HD constexpr bool gm_u16(int f) {
 // a code-independent term
 NQ_HD constexpr bool gm_aff(int f) { return f == Q4_1 || f == Q5_1 || f == Q2_K || f == Q4_K || f == Q5_K; }
 
-template <int F>
+// Activation rows per tile: 32 for batches of at most 32 rows (one 16-row
+// subtile per wave), else 64 (two).
+NQ_HD uint32_t gm_bm(uint64_t M) { return M <= 32u ? 32u : GM_BM; }
+
+template <int F, int MJ = 2>
 struct GmFmt {
+    static constexpr uint32_t BM = 16u * 2u * (uint32_t)MJ;  // activation rows per tile
     static constexpr bool U16 = gm_u16(F);
     static constexpr bool AFF = gm_aff(F);
     // formats with a span rewrite (every gguf format)
@@ -67,14 +73,14 @@ struct GmFmt {
     static constexpr uint32_t NH = U16 ? 2u : 1u;  // scales per span
     static constexpr uint32_t SPB = (uint32_t)block_values(F) / 32u;  // spans per block
     // LDS layout (dwords): weight codes [128][GM_CSW], scales [8][NH][128],
-    // offsets [8][NH][128] (affine formats), activation codes [64][GM_CSW],
-    // scales [8][64], d * S terms [8][NH][64] (affine formats)
+    // offsets [8][NH][128] (affine formats), activation codes [BM][GM_CSW],
+    // scales [8][BM], d * S terms [8][NH][BM] (affine formats)
     static constexpr uint32_t WS = GM_BN * GM_CSW;
     static constexpr uint32_t WO = WS + GM_SP * NH * GM_BN;
     static constexpr uint32_t XC = WO + (AFF ? GM_SP * NH * GM_BN : 0u);
-    static constexpr uint32_t XD = XC + GM_BM * GM_CSW;
-    static constexpr uint32_t XT = XD + GM_SP * GM_BM;
-    static constexpr uint32_t DW = XT + (AFF ? GM_SP * NH * GM_BM : 0u);
+    static constexpr uint32_t XD = XC + BM * GM_CSW;
+    static constexpr uint32_t XT = XD + GM_SP * BM;
+    static constexpr uint32_t DW = XT + (AFF ? GM_SP * NH * BM : 0u);
 };
 
 struct GmArgs {
@@ -90,6 +96,7 @@ struct GmArgs {
     uint32_t ldy;           // N
     uint32_t M;             // activation rows in this launch
     uint32_t mt;            // activation-row tiles
+    uint32_t bm;            // activation rows per tile
     uint32_t xq8, xr8;      // workgroups / 8 and workgroups mod 8
     uint32_t nsplit;        // K splits (1: none)
     uint32_t sps;           // K steps per split
@@ -266,7 +273,7 @@ NQ_HD void gm_tile(const GmArgs &a, uint32_t id, uint32_t *n0, uint32_t *m0, uin
     const uint32_t L = (x < a.xr8 ? x * (a.xq8 + 1u) : a.xr8 * (a.xq8 + 1u) + (x - a.xr8) * a.xq8) + j;
     const uint32_t T = L / a.nsplit;
     *ks = L - T * a.nsplit;
-    *m0 = (T % a.mt) * GM_BM;
+    *m0 = (T % a.mt) * a.bm;
     *n0 = (T / a.mt) * GM_BN;
 }
 
@@ -373,15 +380,15 @@ NQ_HD void gm_rewrite_item(const GmArgs &a, const Src &src, const Tab &tab, uint
     }
 }
 
-// K step, activation side: blocks t0 .. t0+7 of activation rows m0 .. m0+63
-// (codes, binary32 scale, and for the affine formats d times the exact code
-// sum of each half); thread tid takes items tid + WG r (r < 2), item i =
-// (row i / 8, block i mod 8), loaded without branches as above.
-template <int F>
+// K step, activation side: blocks t0 .. t0+7 of activation rows m0 ..
+// m0+BM-1 (codes, binary32 scale, and for the affine formats d times the
+// exact code sum of each half); thread tid takes items tid + WG r (r < BM /
+// 32), item i = (row i / 8, block i mod 8), loaded without branches as above.
+template <int F, int MJ>
 NQ_HD void gm_stage_x(const GmArgs &a, uint32_t m0, uint32_t t0, uint32_t tid, uint32_t *lds) {
-    using G = GmFmt<F>;
-    constexpr uint32_t R = GM_BM * GM_SP / (uint32_t)WG;
-    static_assert(GM_BM * GM_SP % (uint32_t)WG == 0, "whole items per thread");
+    using G = GmFmt<F, MJ>;
+    constexpr uint32_t R = G::BM * GM_SP / (uint32_t)WG;
+    static_assert(G::BM * GM_SP % (uint32_t)WG == 0, "whole items per thread");
     uint32_t c[R][8];
     float d[R];
     bool ok[R];
@@ -402,7 +409,7 @@ NQ_HD void gm_stage_x(const GmArgs &a, uint32_t m0, uint32_t t0, uint32_t tid, u
         uint32_t *cx = lds + G::XC + m * GM_CSW + 8u * sp;
 #pragma unroll
         for (int j = 0; j < 8; j++) cx[j] = ok[r] ? c[r][j] : 0u;
-        ((float *)(lds + G::XD))[sp * GM_BM + m] = dr;
+        ((float *)(lds + G::XD))[sp * G::BM + m] = dr;
         if constexpr (G::AFF) {
             int S0 = 0, S1 = 0;
 #pragma unroll
@@ -412,35 +419,36 @@ NQ_HD void gm_stage_x(const GmArgs &a, uint32_t m0, uint32_t t0, uint32_t tid, u
             }
             float *xt = (float *)(lds + G::XT);
             if constexpr (G::U16) {
-                xt[(2u * sp) * GM_BM + m] = dr * (float)S0;
-                xt[(2u * sp + 1u) * GM_BM + m] = dr * (float)S1;
+                xt[(2u * sp) * G::BM + m] = dr * (float)S0;
+                xt[(2u * sp + 1u) * G::BM + m] = dr * (float)S1;
             } else {
-                xt[sp * GM_BM + m] = dr * (float)(S0 + S1);
+                xt[sp * G::BM + m] = dr * (float)(S0 + S1);
             }
         }
     }
 }
 
 // MFMA operands of span sp for a lane of wave w (sub-tile: weight rows
-// 64 (w mod 2) + 16 i + .., activation rows 32 (w / 2) + 16 j + ..): the
+// 64 (w mod 2) + 16 i + .., activation rows 16 MJ (w / 2) + 16 j + ..): the
 // lane supplies row lane mod 16 of each 16-row group, code bytes
 // 8 (lane / 16) .. + 7 of the span.
+template <int MJ>
 struct GmOps {
-    uint64_t A[4];  // weight rows
-    uint64_t B[2];  // activation rows
+    uint64_t A[4];   // weight rows
+    uint64_t B[MJ];  // activation rows
 };
 
 NQ_HD uint64_t lds_u64(const uint32_t *p) { return (uint64_t)p[0] | ((uint64_t)p[1] << 32); }
 
-template <int F>
-NQ_HD void gm_ops(const uint32_t *lds, uint32_t w, uint32_t lane, uint32_t sp, GmOps &o) {
-    using G = GmFmt<F>;
+template <int F, int MJ>
+NQ_HD void gm_ops(const uint32_t *lds, uint32_t w, uint32_t lane, uint32_t sp, GmOps<MJ> &o) {
+    using G = GmFmt<F, MJ>;
     const uint32_t r = lane & 15u, k = 8u * sp + 2u * (lane >> 4);
-    const uint32_t nb = 64u * (w & 1u), mb = 32u * (w >> 1);
+    const uint32_t nb = 64u * (w & 1u), mb = 16u * (uint32_t)MJ * (w >> 1);
 #pragma unroll
     for (int i = 0; i < 4; i++) o.A[i] = lds_u64(lds + (nb + 16u * (uint32_t)i + r) * GM_CSW + k);
 #pragma unroll
-    for (int j = 0; j < 2; j++) o.B[j] = lds_u64(lds + G::XC + (mb + 16u * (uint32_t)j + r) * GM_CSW + k);
+    for (int j = 0; j < MJ; j++) o.B[j] = lds_u64(lds + G::XC + (mb + 16u * (uint32_t)j + r) * GM_CSW + k);
 }
 
 // Activation operand for half h of a span with 16-value scales: lanes 0-31
@@ -455,25 +463,25 @@ NQ_HD uint64_t gm_half(uint64_t b, uint32_t lane, uint32_t h) {
 
 // Integer results of a span for one lane: I[h][i][j][e] is the dot product of
 // weight row 64 (w mod 2) + 16 i + 4 (lane / 16) + e with activation row
-// 32 (w / 2) + 16 j + lane mod 16 over half h (or the whole span).
-template <int F>
+// 16 MJ (w / 2) + 16 j + lane mod 16 over half h (or the whole span).
+template <int F, int MJ>
 struct GmI {
-    int v[GmFmt<F>::NH][4][2][4];
+    int v[GmFmt<F>::NH][4][MJ][4];
 };
 
 // The span's scaling into the lane's accumulators (fixed order: per output,
 // the halves).  The affine formats' offset terms are added per K step by
 // gm_offsets on the matrix cores.
-template <int F>
-NQ_HD void gm_epi(const uint32_t *lds, uint32_t w, uint32_t lane, uint32_t sp, const GmI<F> &I,
-                  float (&acc)[4][2][4]) {
-    using G = GmFmt<F>;
-    const uint32_t nb = 64u * (w & 1u) + 4u * (lane >> 4), mb = 32u * (w >> 1) + (lane & 15u);
+template <int F, int MJ>
+NQ_HD void gm_epi(const uint32_t *lds, uint32_t w, uint32_t lane, uint32_t sp, const GmI<F, MJ> &I,
+                  float (&acc)[4][MJ][4]) {
+    using G = GmFmt<F, MJ>;
+    const uint32_t nb = 64u * (w & 1u) + 4u * (lane >> 4), mb = 16u * (uint32_t)MJ * (w >> 1) + (lane & 15u);
     const float *ws = (const float *)(lds + G::WS);
     const float *xd = (const float *)(lds + G::XD);
-    float d[2];
+    float d[MJ];
 #pragma unroll
-    for (int j = 0; j < 2; j++) d[j] = xd[sp * GM_BM + mb + 16u * (uint32_t)j];
+    for (int j = 0; j < MJ; j++) d[j] = xd[sp * G::BM + mb + 16u * (uint32_t)j];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         float sw[2][4];
@@ -483,7 +491,7 @@ NQ_HD void gm_epi(const uint32_t *lds, uint32_t w, uint32_t lane, uint32_t sp, c
             for (int e = 0; e < 4; e++)
                 sw[h][e] = ws[(sp * G::NH + h) * GM_BN + nb + 16u * (uint32_t)i + (uint32_t)e];
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int j = 0; j < MJ; j++)
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 float a = acc[i][j][e];
@@ -500,28 +508,29 @@ NQ_HD void gm_epi(const uint32_t *lds, uint32_t w, uint32_t lane, uint32_t sp, c
 // k at a time into the accumulators (A[i][k]: lane l supplies row l mod 16,
 // k = l / 16; B[k][j] likewise; the result has the int8 tiles' lane layout).
 // Operands of quad q for a lane (k past the step's nk are zeros).
-template <int F>
+template <int F, int MJ>
 NQ_HD void gm_offsets_ops(const uint32_t *lds, uint32_t w, uint32_t lane, uint32_t q, uint32_t nk, float (&A)[4],
-                          float (&B)[2]) {
-    using G = GmFmt<F>;
+                          float (&B)[MJ]) {
+    using G = GmFmt<F, MJ>;
     const uint32_t k = 4u * q + (lane >> 4), r = lane & 15u;
-    const uint32_t nb = 64u * (w & 1u), mb = 32u * (w >> 1);
+    const uint32_t nb = 64u * (w & 1u), mb = 16u * (uint32_t)MJ * (w >> 1);
     const float *ow = (const float *)(lds + G::WO), *xt = (const float *)(lds + G::XT);
     const bool in = k < nk;
     const uint32_t kk = in ? k : 0u;
 #pragma unroll
     for (int i = 0; i < 4; i++) A[i] = in ? ow[kk * GM_BN + nb + 16u * (uint32_t)i + r] : 0.0f;
 #pragma unroll
-    for (int j = 0; j < 2; j++) B[j] = in ? xt[kk * GM_BM + mb + 16u * (uint32_t)j + r] : 0.0f;
+    for (int j = 0; j < MJ; j++) B[j] = in ? xt[kk * G::BM + mb + 16u * (uint32_t)j + r] : 0.0f;
 }
 
-// The lane's outputs: y[m][n] for its 4 x 2 x 4 (row, activation row) pairs
-// inside the launch (with K splits: split ks's partial output).
+// The lane's outputs: y[m][n] for its 4 x MJ x 4 (row, activation row)
+// pairs inside the launch (with K splits: split ks's partial output).
+template <int MJ>
 NQ_HD void gm_store(const GmArgs &a, uint32_t n0, uint32_t m0, uint32_t ks, uint32_t w, uint32_t lane,
-                    const float (&acc)[4][2][4]) {
-    const uint32_t nb = n0 + 64u * (w & 1u) + 4u * (lane >> 4), mb = m0 + 32u * (w >> 1) + (lane & 15u);
+                    const float (&acc)[4][MJ][4]) {
+    const uint32_t nb = n0 + 64u * (w & 1u) + 4u * (lane >> 4), mb = m0 + 16u * (uint32_t)MJ * (w >> 1) + (lane & 15u);
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
+    for (int j = 0; j < MJ; j++) {
         const uint32_t m = mb + 16u * (uint32_t)j;
         if (m >= a.M) continue;
         float *yr = a.y + (uint64_t)ks * a.ysplit + (uint64_t)m * a.ldy;
@@ -537,9 +546,9 @@ NQ_HD void gm_store(const GmArgs &a, uint32_t n0, uint32_t m0, uint32_t ks, uint
 
 typedef int gm_i32x4 __attribute__((ext_vector_type(4)));
 
-template <int F>
+template <int F, int MJ>
 __global__ __launch_bounds__(WG) void k_gemm(GmArgs a) {
-    using G = GmFmt<F>;
+    using G = GmFmt<F, MJ>;
     using TS = TabSpec<F>;
     __shared__ uint64_t t8[TS::n8 > 0 ? TS::n8 : 1];
     __shared__ uint32_t t4[TS::n4 > 0 ? TS::n4 : 1];
@@ -551,11 +560,11 @@ __global__ __launch_bounds__(WG) void k_gemm(GmArgs a) {
     gm_tile(a, blockIdx.x, &n0, &m0, &ks);
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t w = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    float acc[4][2][4];
+    float acc[4][MJ][4];
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int j = 0; j < MJ; j++)
 #pragma unroll
             for (int e = 0; e < 4; e++) acc[i][j][e] = 0.0f;
     const uint32_t tb = ks * a.sps * GM_SP, te0 = tb + a.sps * GM_SP, te = te0 < a.kspans ? te0 : a.kspans;
@@ -565,17 +574,17 @@ __global__ __launch_bounds__(WG) void k_gemm(GmArgs a) {
             gm_stage_wc<F>(a, n0, t0, threadIdx.x, lds);
         else
             gm_stage_w<F>(a, src, tab, n0, t0, threadIdx.x, lds);
-        gm_stage_x<F>(a, m0, t0, threadIdx.x, lds);
+        gm_stage_x<F, MJ>(a, m0, t0, threadIdx.x, lds);
         __syncthreads();
         const uint32_t nsp = te - t0 < GM_SP ? te - t0 : GM_SP;
         for (uint32_t sp = 0; sp < nsp; sp++) {
-            GmOps o;
-            gm_ops<F>(lds, w, lane, sp, o);
-            GmI<F> I;
+            GmOps<MJ> o;
+            gm_ops<F, MJ>(lds, w, lane, sp, o);
+            GmI<F, MJ> I;
 #pragma unroll
             for (uint32_t h = 0; h < G::NH; h++)
 #pragma unroll
-                for (int j = 0; j < 2; j++) {
+                for (int j = 0; j < MJ; j++) {
                     const uint64_t b = gm_half<F>(o.B[j], lane, h);
 #pragma unroll
                     for (int i = 0; i < 4; i++) {
@@ -585,18 +594,18 @@ __global__ __launch_bounds__(WG) void k_gemm(GmArgs a) {
                         for (int e = 0; e < 4; e++) I.v[h][i][j][e] = r[e];
                     }
                 }
-            gm_epi<F>(lds, w, lane, sp, I, acc);
+            gm_epi<F, MJ>(lds, w, lane, sp, I, acc);
         }
         if constexpr (G::AFF) {
             typedef float gm_f32x4 __attribute__((ext_vector_type(4)));
             const uint32_t nk = nsp * G::NH;
             for (uint32_t q = 0; 4u * q < nk; q++) {
-                float A[4], B[2];
-                gm_offsets_ops<F>(lds, w, lane, q, nk, A, B);
+                float A[4], B[MJ];
+                gm_offsets_ops<F, MJ>(lds, w, lane, q, nk, A, B);
 #pragma unroll
                 for (int i = 0; i < 4; i++)
 #pragma unroll
-                    for (int j = 0; j < 2; j++) {
+                    for (int j = 0; j < MJ; j++) {
                         gm_f32x4 c = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
                         c = __builtin_amdgcn_mfma_f32_16x16x4f32(A[i], B[j], c, 0, 0, 0);
 #pragma unroll
@@ -605,7 +614,7 @@ __global__ __launch_bounds__(WG) void k_gemm(GmArgs a) {
             }
         }
     }
-    gm_store(a, n0, m0, ks, w, lane, acc);
+    gm_store<MJ>(a, n0, m0, ks, w, lane, acc);
 }
 
 // The per-call weight rewrite (one item per thread).
@@ -653,7 +662,7 @@ struct GmPlan {
 
 inline GmPlan gm_plan(uint64_t N, uint64_t K, uint64_t M, uint32_t cus) {
     const uint64_t steps = (K / 32 + GM_SP - 1) / GM_SP;
-    const uint64_t tiles = (N + GM_BN - 1) / GM_BN * ((M + GM_BM - 1) / GM_BM);
+    const uint64_t bm = gm_bm(M), tiles = (N + GM_BN - 1) / GM_BN * ((M + bm - 1) / bm);
     const uint64_t target = 2ull * (cus ? cus : 1u);
     GmPlan p{1u, (uint32_t)steps, M > GM_REWRITE_ONCE_M};
     if (tiles >= target || steps < 8) return p;
@@ -711,7 +720,8 @@ GmArgs gm_args(const GvLaunch &L, uint64_t r0, uint64_t rows, uint64_t m0, uint6
     a.xrow = (uint32_t)(L.K / 32 * 9);
     a.ldy = (uint32_t)L.N;
     a.M = (uint32_t)mrows;
-    a.mt = (uint32_t)((mrows + GM_BM - 1) / GM_BM);
+    a.bm = gm_bm(L.M);
+    a.mt = (uint32_t)((mrows + a.bm - 1) / a.bm);
     a.nsplit = p.nsplit;
     a.sps = p.sps;
     a.ysplit = L.M * L.N;
@@ -766,7 +776,10 @@ int launch_gemm_mfma(const GvLaunch &L, void *ws, uint64_t ws_bytes, hipStream_t
         for (uint64_t r0 = 0; r0 < L.N;) {
             const uint64_t rows = L.N - r0 < max_rows ? L.N - r0 : max_rows;
             const GmArgs a = gm_args<F>(L, r0, rows, m0, mrows, p, out, canon, &wl);
-            hipLaunchKernelGGL((k_gemm<F>), dim3(gm_grid(a)), dim3(WG), 0, stream, a);
+            if (a.bm == GM_BM)
+                hipLaunchKernelGGL((k_gemm<F, 2>), dim3(gm_grid(a)), dim3(WG), 0, stream, a);
+            else
+                hipLaunchKernelGGL((k_gemm<F, 1>), dim3(gm_grid(a)), dim3(WG), 0, stream, a);
             if (hipGetLastError() != hipSuccess) return 9;  // NQ_ERR_HIP
             r0 += rows;
         }

@@ -250,12 +250,12 @@ int nq_gemv_q8_1(int32_t format, const void *weight, uint64_t nbytes, int64_t N,
 
 /* nq_gemm_q8_1: the same product for any number of activation rows M >= 1
  * (the page's GGUF linear operation over a batch), with the same argument
- * meaning, layouts and criterion.  Up to 8 rows it makes the launches
- * nq_gemv_q8_1 makes (identical bits); with more rows every 32 weight values
- * become signed 8-bit codes with a binary32 scale (and an offset for q4_1,
- * q5_1, q2_k, q4_k and q5_k), their exact integer dot products with the
- * activation codes come from the 8-bit matrix cores, and each is scaled and
- * added in binary32.
+ * meaning, layouts and criterion.  Up to 4 rows it makes the launch
+ * nq_gemv_q8_1 makes (identical bits); with 5 or more rows every 32 weight
+ * values become signed 8-bit codes with a binary32 scale (and an offset for
+ * q4_1, q5_1, q2_k, q4_k and q5_k), their exact integer dot products with
+ * the activation codes come from the 8-bit matrix cores, and each is scaled
+ * and added in binary32.
  * When the output has few tiles and K is long, K is split over workgroups:
  * each split's partial output goes to `workspace` (device memory the caller
  * owns, at least the size nq_gemm_q8_1_workspace reports, 16-byte aligned,

@@ -229,7 +229,7 @@ def _gemm_k(B):
 def test_gemm_every_format(fmt):
     _, B, _, _ = oracle.info(fmt)
     K = _gemm_k(B)
-    for N, M, w_off in [(300, 70, 0), (37, 9, 1), (129, 130, 3)]:
+    for N, M, w_off in [(300, 70, 0), (37, 9, 1), (129, 130, 3), (150, 5, 2)]:
         w = _weights(fmt, N, K, 400 + M)
         _, xq = oracle.quantize_q8_1(_act(M, K, M).astype(np.float32))
         ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
@@ -239,11 +239,11 @@ def test_gemm_every_format(fmt):
 
 
 @pytest.mark.parametrize("fmt", ["gguf:q4_k", "gguf:iq3_s", "gguf:q5_0", "gguf:tq1_0"])
-def test_gemm_up_to_8_rows_is_the_single_row_product(fmt):
+def test_gemm_up_to_4_rows_is_the_single_row_product(fmt):
     _, B, _, _ = oracle.info(fmt)
     N, K = 77, 2 * max(B, 256)
     w = _weights(fmt, N, K, 5)
-    for M in (1, 3, 8):
+    for M in (1, 3, 4):
         _, xq = oracle.quantize_q8_1(_act(M, K, 40 + M).astype(np.float32))
         announce(f"gemm vs gemv {fmt} M={M}")
         a = _gemm(fmt, w, N, K, xq)
