@@ -443,3 +443,19 @@ def test_emu_products_over_non_finite_scales(M):
     bad[[3, 5]] = True
     assert not np.any(np.isfinite(y[:, bad])) and not np.any(np.isfinite(ref[:, bad]))
     linear_check(y[:, ~bad], ref[:, ~bad], env[:, ~bad], K, f"{fmt} finite rows")
+
+
+@pytest.mark.parametrize("fmt,N,K,M", [("gguf:q8_0", 1, 32, 5), ("gguf:q8_0", 1, 32, 33), ("gguf:q4_k", 1, 256, 32),
+                                       ("gguf:q2_k", 3, 256, 65), ("gguf:iq1_m", 2, 256, 6)])
+def test_emu_gemm_tiny_shapes(fmt, N, K, M):
+    """One weight row, one span or one block of K, activation rows at the
+    tile-height boundaries."""
+    idx, B, S, _ = oracle.info(fmt)
+    w = synth.payload(fmt, N * K // B, N + K + M, synth.binade(-6, -2, False))
+    _, xq = oracle.quantize_q8_1(_act(M, K, 11).astype(np.float32))
+    for cus in (0, 256):
+        y, rc, msg, guards = emu_lib.gemm_q8_1(idx, w, N, K, xq, M, w_mis=1, cus=cus)
+        assert rc == 0, msg
+        assert guards
+        ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
+        linear_check(y, ref, env, K, f"{fmt} [{N}, {K}] x {M}")

@@ -376,3 +376,17 @@ def test_products_over_non_finite_scales(M):
     bad[[3, 5]] = True
     assert not np.any(np.isfinite(y[:, bad])) and not np.any(np.isfinite(ref[:, bad]))
     linear_check(y[:, ~bad], ref[:, ~bad], env[:, ~bad], K, f"{fmt} finite rows")
+
+
+@pytest.mark.parametrize("fmt,N,K,M", [("gguf:q8_0", 1, 32, 5), ("gguf:q8_0", 1, 32, 33), ("gguf:q4_k", 1, 256, 32),
+                                       ("gguf:q2_k", 3, 256, 65), ("gguf:iq1_m", 2, 256, 6), ("gguf:q6_k", 5, 256, 4)])
+def test_gemm_tiny_shapes(fmt, N, K, M):
+    """One weight row, one span or one block of K, activation rows at the
+    boundaries of the tile heights and of the single-row kernel."""
+    w = _weights(fmt, N, K, N + K + M)
+    _, xq = oracle.quantize_q8_1(_act(M, K, 11).astype(np.float32))
+    ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
+    announce(f"gemm tiny {fmt} [{N}, {K}] x {M}")
+    for split in (True, False):
+        y = _gemm(fmt, w, N, K, xq, w_off=1, split=split)
+        linear_check(y, ref, env, K, f"{fmt} [{N}, {K}] x {M}")
