@@ -59,13 +59,25 @@ NQ_HD constexpr bool gm_u16(int f) {
 // a code-independent term
 NQ_HD constexpr bool gm_aff(int f) { return f == Q4_1 || f == Q5_1 || f == Q2_K || f == Q4_K || f == Q5_K; }
 
-// Activation rows per tile: 32 for batches of at most 32 rows (one 16-row
-// subtile per wave), else 64 (two).
-NQ_HD uint32_t gm_bm(uint64_t M) { return M <= 32u ? 32u : GM_BM; }
+// Activation rows per tile: 16 for batches of at most 16 rows, 32 for at
+// most 32, else 64.
+NQ_HD uint32_t gm_bm(uint64_t M) { return M <= 16u ? 16u : M <= 32u ? 32u : GM_BM; }
 
-template <int F, int MJ = 2>
+// Wave layout of a tile: each of the 4 waves computes NI 16-row weight
+// subtiles by MJ 16-row activation subtiles; WN waves side by side along the
+// 128 weight rows, WM along the activation rows.  (NI, MJ) = (4, 2): 64
+// activation rows, (4, 1): 32, (2, 1): 16.
+template <int NI, int MJ>
+struct GmShape {
+    static constexpr uint32_t WN = 8u / (uint32_t)NI, WM = 4u / WN, BM = 16u * (uint32_t)MJ * WM;
+    static_assert(WN * WM == 4u && 16u * (uint32_t)NI * WN == 128u, "4 waves over 128 weight rows");
+    NQ_HD static uint32_t nb(uint32_t w) { return 16u * (uint32_t)NI * (w % WN); }
+    NQ_HD static uint32_t mb(uint32_t w) { return 16u * (uint32_t)MJ * (w / WN); }
+};
+
+template <int F, int BMT = 64>
 struct GmFmt {
-    static constexpr uint32_t BM = 16u * 2u * (uint32_t)MJ;  // activation rows per tile
+    static constexpr uint32_t BM = (uint32_t)BMT;  // activation rows per tile
     static constexpr bool U16 = gm_u16(F);
     static constexpr bool AFF = gm_aff(F);
     // formats with a span rewrite (every gguf format)
@@ -384,18 +396,18 @@ NQ_HD void gm_rewrite_item(const GmArgs &a, const Src &src, const Tab &tab, uint
 // m0+BM-1 (codes, binary32 scale, and for the affine formats d times the
 // exact code sum of each half); thread tid takes items tid + WG r (r < BM /
 // 32), item i = (row i / 8, block i mod 8), loaded without branches as above.
-template <int F, int MJ>
+template <int F, int BMT>
 NQ_HD void gm_stage_x(const GmArgs &a, uint32_t m0, uint32_t t0, uint32_t tid, uint32_t *lds) {
-    using G = GmFmt<F, MJ>;
-    constexpr uint32_t R = G::BM * GM_SP / (uint32_t)WG;
-    static_assert(G::BM * GM_SP % (uint32_t)WG == 0, "whole items per thread");
+    using G = GmFmt<F, BMT>;
+    // BM * 8 items: whole multiples of the workgroup, or (16 rows) half of it
+    constexpr uint32_t R = (G::BM * GM_SP + (uint32_t)WG - 1u) / (uint32_t)WG;
     uint32_t c[R][8];
     float d[R];
     bool ok[R];
 #pragma unroll
     for (uint32_t r = 0; r < R; r++) {
         const uint32_t i = tid + (uint32_t)WG * r, m = i / GM_SP, t = t0 + i % GM_SP;
-        ok[r] = m0 + m < a.M && t < a.kspans;
+        ok[r] = i < G::BM * GM_SP && m0 + m < a.M && t < a.kspans;
         const uint32_t *p = a.xq + (ok[r] ? (uint64_t)(m0 + m) * a.xrow + (uint64_t)t * 9u : 0ull);
         const u32x4a4 v0 = *(const u32x4a4 *)(p + 1), v1 = *(const u32x4a4 *)(p + 5);
         c[r][0] = v0.x; c[r][1] = v0.y; c[r][2] = v0.z; c[r][3] = v0.w;
@@ -405,6 +417,7 @@ NQ_HD void gm_stage_x(const GmArgs &a, uint32_t m0, uint32_t t0, uint32_t tid, u
 #pragma unroll
     for (uint32_t r = 0; r < R; r++) {
         const uint32_t i = tid + (uint32_t)WG * r, m = i / GM_SP, sp = i % GM_SP;
+        if (i >= G::BM * GM_SP) continue;  // (16-row tiles) threads past the tile's items
         const float dr = ok[r] ? d[r] : 0.0f;
         uint32_t *cx = lds + G::XC + m * GM_CSW + 8u * sp;
 #pragma unroll
@@ -429,24 +442,25 @@ NQ_HD void gm_stage_x(const GmArgs &a, uint32_t m0, uint32_t t0, uint32_t tid, u
 }
 
 // MFMA operands of span sp for a lane of wave w (sub-tile: weight rows
-// 64 (w mod 2) + 16 i + .., activation rows 16 MJ (w / 2) + 16 j + ..): the
+// GmShape::nb(w) + 16 i + .., activation rows GmShape::mb(w) + 16 j + ..): the
 // lane supplies row lane mod 16 of each 16-row group, code bytes
 // 8 (lane / 16) .. + 7 of the span.
-template <int MJ>
+template <int NI, int MJ>
 struct GmOps {
-    uint64_t A[4];   // weight rows
+    uint64_t A[NI];  // weight rows
     uint64_t B[MJ];  // activation rows
 };
 
 NQ_HD uint64_t lds_u64(const uint32_t *p) { return (uint64_t)p[0] | ((uint64_t)p[1] << 32); }
 
-template <int F, int MJ>
-NQ_HD void gm_ops(const uint32_t *lds, uint32_t w, uint32_t lane, uint32_t sp, GmOps<MJ> &o) {
-    using G = GmFmt<F, MJ>;
+template <int F, int NI, int MJ>
+NQ_HD void gm_ops(const uint32_t *lds, uint32_t w, uint32_t lane, uint32_t sp, GmOps<NI, MJ> &o) {
+    using Sh = GmShape<NI, MJ>;
+    using G = GmFmt<F, Sh::BM>;
     const uint32_t r = lane & 15u, k = 8u * sp + 2u * (lane >> 4);
-    const uint32_t nb = 64u * (w & 1u), mb = 16u * (uint32_t)MJ * (w >> 1);
+    const uint32_t nb = Sh::nb(w), mb = Sh::mb(w);
 #pragma unroll
-    for (int i = 0; i < 4; i++) o.A[i] = lds_u64(lds + (nb + 16u * (uint32_t)i + r) * GM_CSW + k);
+    for (int i = 0; i < NI; i++) o.A[i] = lds_u64(lds + (nb + 16u * (uint32_t)i + r) * GM_CSW + k);
 #pragma unroll
     for (int j = 0; j < MJ; j++) o.B[j] = lds_u64(lds + G::XC + (mb + 16u * (uint32_t)j + r) * GM_CSW + k);
 }
@@ -462,28 +476,29 @@ NQ_HD uint64_t gm_half(uint64_t b, uint32_t lane, uint32_t h) {
 }
 
 // Integer results of a span for one lane: I[h][i][j][e] is the dot product of
-// weight row 64 (w mod 2) + 16 i + 4 (lane / 16) + e with activation row
-// 16 MJ (w / 2) + 16 j + lane mod 16 over half h (or the whole span).
-template <int F, int MJ>
+// weight row nb(w) + 16 i + 4 (lane / 16) + e with activation row
+// mb(w) + 16 j + lane mod 16 over half h (or the whole span).
+template <int F, int NI, int MJ>
 struct GmI {
-    int v[GmFmt<F>::NH][4][MJ][4];
+    int v[GmFmt<F>::NH][NI][MJ][4];
 };
 
 // The span's scaling into the lane's accumulators (fixed order: per output,
 // the halves).  The affine formats' offset terms are added per K step by
 // gm_offsets on the matrix cores.
-template <int F, int MJ>
-NQ_HD void gm_epi(const uint32_t *lds, uint32_t w, uint32_t lane, uint32_t sp, const GmI<F, MJ> &I,
-                  float (&acc)[4][MJ][4]) {
-    using G = GmFmt<F, MJ>;
-    const uint32_t nb = 64u * (w & 1u) + 4u * (lane >> 4), mb = 16u * (uint32_t)MJ * (w >> 1) + (lane & 15u);
+template <int F, int NI, int MJ>
+NQ_HD void gm_epi(const uint32_t *lds, uint32_t w, uint32_t lane, uint32_t sp, const GmI<F, NI, MJ> &I,
+                  float (&acc)[NI][MJ][4]) {
+    using Sh = GmShape<NI, MJ>;
+    using G = GmFmt<F, Sh::BM>;
+    const uint32_t nb = Sh::nb(w) + 4u * (lane >> 4), mb = Sh::mb(w) + (lane & 15u);
     const float *ws = (const float *)(lds + G::WS);
     const float *xd = (const float *)(lds + G::XD);
     float d[MJ];
 #pragma unroll
     for (int j = 0; j < MJ; j++) d[j] = xd[sp * G::BM + mb + 16u * (uint32_t)j];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < NI; i++) {
         float sw[2][4];
 #pragma unroll
         for (uint32_t h = 0; h < G::NH; h++)
@@ -508,34 +523,36 @@ NQ_HD void gm_epi(const uint32_t *lds, uint32_t w, uint32_t lane, uint32_t sp, c
 // k at a time into the accumulators (A[i][k]: lane l supplies row l mod 16,
 // k = l / 16; B[k][j] likewise; the result has the int8 tiles' lane layout).
 // Operands of quad q for a lane (k past the step's nk are zeros).
-template <int F, int MJ>
-NQ_HD void gm_offsets_ops(const uint32_t *lds, uint32_t w, uint32_t lane, uint32_t q, uint32_t nk, float (&A)[4],
+template <int F, int NI, int MJ>
+NQ_HD void gm_offsets_ops(const uint32_t *lds, uint32_t w, uint32_t lane, uint32_t q, uint32_t nk, float (&A)[NI],
                           float (&B)[MJ]) {
-    using G = GmFmt<F, MJ>;
+    using Sh = GmShape<NI, MJ>;
+    using G = GmFmt<F, Sh::BM>;
     const uint32_t k = 4u * q + (lane >> 4), r = lane & 15u;
-    const uint32_t nb = 64u * (w & 1u), mb = 16u * (uint32_t)MJ * (w >> 1);
+    const uint32_t nb = Sh::nb(w), mb = Sh::mb(w);
     const float *ow = (const float *)(lds + G::WO), *xt = (const float *)(lds + G::XT);
     const bool in = k < nk;
     const uint32_t kk = in ? k : 0u;
 #pragma unroll
-    for (int i = 0; i < 4; i++) A[i] = in ? ow[kk * GM_BN + nb + 16u * (uint32_t)i + r] : 0.0f;
+    for (int i = 0; i < NI; i++) A[i] = in ? ow[kk * GM_BN + nb + 16u * (uint32_t)i + r] : 0.0f;
 #pragma unroll
     for (int j = 0; j < MJ; j++) B[j] = in ? xt[kk * G::BM + mb + 16u * (uint32_t)j + r] : 0.0f;
 }
 
-// The lane's outputs: y[m][n] for its 4 x MJ x 4 (row, activation row)
+// The lane's outputs: y[m][n] for its NI x MJ x 4 (row, activation row)
 // pairs inside the launch (with K splits: split ks's partial output).
-template <int MJ>
+template <int NI, int MJ>
 NQ_HD void gm_store(const GmArgs &a, uint32_t n0, uint32_t m0, uint32_t ks, uint32_t w, uint32_t lane,
-                    const float (&acc)[4][MJ][4]) {
-    const uint32_t nb = n0 + 64u * (w & 1u) + 4u * (lane >> 4), mb = m0 + 16u * (uint32_t)MJ * (w >> 1) + (lane & 15u);
+                    const float (&acc)[NI][MJ][4]) {
+    using Sh = GmShape<NI, MJ>;
+    const uint32_t nb = n0 + Sh::nb(w) + 4u * (lane >> 4), mb = m0 + Sh::mb(w) + (lane & 15u);
 #pragma unroll
     for (int j = 0; j < MJ; j++) {
         const uint32_t m = mb + 16u * (uint32_t)j;
         if (m >= a.M) continue;
         float *yr = a.y + (uint64_t)ks * a.ysplit + (uint64_t)m * a.ldy;
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+        for (int i = 0; i < NI; i++)
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const uint32_t n = nb + 16u * (uint32_t)i + (uint32_t)e;
@@ -546,9 +563,10 @@ NQ_HD void gm_store(const GmArgs &a, uint32_t n0, uint32_t m0, uint32_t ks, uint
 
 typedef int gm_i32x4 __attribute__((ext_vector_type(4)));
 
-template <int F, int MJ>
+template <int F, int NI, int MJ>
 __global__ __launch_bounds__(WG) void k_gemm(GmArgs a) {
-    using G = GmFmt<F, MJ>;
+    using Sh = GmShape<NI, MJ>;
+    using G = GmFmt<F, Sh::BM>;
     using TS = TabSpec<F>;
     __shared__ uint64_t t8[TS::n8 > 0 ? TS::n8 : 1];
     __shared__ uint32_t t4[TS::n4 > 0 ? TS::n4 : 1];
@@ -560,9 +578,9 @@ __global__ __launch_bounds__(WG) void k_gemm(GmArgs a) {
     gm_tile(a, blockIdx.x, &n0, &m0, &ks);
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t w = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    float acc[4][MJ][4];
+    float acc[NI][MJ][4];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < NI; i++)
 #pragma unroll
         for (int j = 0; j < MJ; j++)
 #pragma unroll
@@ -574,36 +592,36 @@ __global__ __launch_bounds__(WG) void k_gemm(GmArgs a) {
             gm_stage_wc<F>(a, n0, t0, threadIdx.x, lds);
         else
             gm_stage_w<F>(a, src, tab, n0, t0, threadIdx.x, lds);
-        gm_stage_x<F, MJ>(a, m0, t0, threadIdx.x, lds);
+        gm_stage_x<F, Sh::BM>(a, m0, t0, threadIdx.x, lds);
         __syncthreads();
         const uint32_t nsp = te - t0 < GM_SP ? te - t0 : GM_SP;
         for (uint32_t sp = 0; sp < nsp; sp++) {
-            GmOps<MJ> o;
-            gm_ops<F, MJ>(lds, w, lane, sp, o);
-            GmI<F, MJ> I;
+            GmOps<NI, MJ> o;
+            gm_ops<F, NI, MJ>(lds, w, lane, sp, o);
+            GmI<F, NI, MJ> I;
 #pragma unroll
             for (uint32_t h = 0; h < G::NH; h++)
 #pragma unroll
                 for (int j = 0; j < MJ; j++) {
                     const uint64_t b = gm_half<F>(o.B[j], lane, h);
 #pragma unroll
-                    for (int i = 0; i < 4; i++) {
+                    for (int i = 0; i < NI; i++) {
                         const gm_i32x4 z = {0, 0, 0, 0};
                         const gm_i32x4 r = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)o.A[i], (long)b, z, 0, 0, 0);
 #pragma unroll
                         for (int e = 0; e < 4; e++) I.v[h][i][j][e] = r[e];
                     }
                 }
-            gm_epi<F, MJ>(lds, w, lane, sp, I, acc);
+            gm_epi<F, NI, MJ>(lds, w, lane, sp, I, acc);
         }
         if constexpr (G::AFF) {
             typedef float gm_f32x4 __attribute__((ext_vector_type(4)));
             const uint32_t nk = nsp * G::NH;
             for (uint32_t q = 0; 4u * q < nk; q++) {
-                float A[4], B[MJ];
-                gm_offsets_ops<F, MJ>(lds, w, lane, q, nk, A, B);
+                float A[NI], B[MJ];
+                gm_offsets_ops<F, NI, MJ>(lds, w, lane, q, nk, A, B);
 #pragma unroll
-                for (int i = 0; i < 4; i++)
+                for (int i = 0; i < NI; i++)
 #pragma unroll
                     for (int j = 0; j < MJ; j++) {
                         gm_f32x4 c = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
@@ -614,7 +632,7 @@ __global__ __launch_bounds__(WG) void k_gemm(GmArgs a) {
             }
         }
     }
-    gm_store<MJ>(a, n0, m0, ks, w, lane, acc);
+    gm_store<NI, MJ>(a, n0, m0, ks, w, lane, acc);
 }
 
 // The per-call weight rewrite (one item per thread).
@@ -776,10 +794,12 @@ int launch_gemm_mfma(const GvLaunch &L, void *ws, uint64_t ws_bytes, hipStream_t
         for (uint64_t r0 = 0; r0 < L.N;) {
             const uint64_t rows = L.N - r0 < max_rows ? L.N - r0 : max_rows;
             const GmArgs a = gm_args<F>(L, r0, rows, m0, mrows, p, out, canon, &wl);
-            if (a.bm == GM_BM)
-                hipLaunchKernelGGL((k_gemm<F, 2>), dim3(gm_grid(a)), dim3(WG), 0, stream, a);
+            if (a.bm == 64u)
+                hipLaunchKernelGGL((k_gemm<F, 4, 2>), dim3(gm_grid(a)), dim3(WG), 0, stream, a);
+            else if (a.bm == 32u)
+                hipLaunchKernelGGL((k_gemm<F, 4, 1>), dim3(gm_grid(a)), dim3(WG), 0, stream, a);
             else
-                hipLaunchKernelGGL((k_gemm<F, 1>), dim3(gm_grid(a)), dim3(WG), 0, stream, a);
+                hipLaunchKernelGGL((k_gemm<F, 2, 1>), dim3(gm_grid(a)), dim3(WG), 0, stream, a);
             if (hipGetLastError() != hipSuccess) return 9;  // NQ_ERR_HIP
             r0 += rows;
         }

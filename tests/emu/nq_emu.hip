@@ -375,11 +375,12 @@ void mfma_f32_16x16x4(const float (&A)[64], const float (&B)[64], float (&C)[64]
 // poisoned LDS image (weight reads through a bounds-checked source), then per
 // span and wave the lanes' operands, the matrix instruction and the lanes'
 // scaling, and at the end the lanes' stores; then the partials' sum.
-template <int F, int MJ>
-long run_gemm_mj(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y,
+template <int F, int NI, int MJ>
+long run_gemm_sh(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y,
                  uint64_t max_rows, uint64_t max_mrows, uint32_t cus, uint32_t *nsplit_out, char *err, int errlen) {
     using namespace nq;
-    using G = GmFmt<F, MJ>;
+    using Sh = GmShape<NI, MJ>;
+    using G = GmFmt<F, Sh::BM>;
     const GvLaunch L{w, N, K, M, xq, y, 0u};
     const uint64_t lim = max_rows ? max_rows : gm_max_rows<F>(L);
     const uint64_t mlim = max_mrows ? max_mrows : GM_MAX_MROWS;
@@ -389,9 +390,9 @@ long run_gemm_mj(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, ui
     for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) gv_fill_tables<F>(t8.data(), t4.data(), tid);
     const Tab tab{t8.data(), t4.data(), nullptr, nullptr, 0xFFFFFFFFu, 1u};
     std::vector<uint32_t> lds(G::DW);
-    static float acc[4][64][4][MJ][4];
-    static GmOps<MJ> ops[64];
-    static GmI<F, MJ> I[64];
+    static float acc[4][64][NI][MJ][4];
+    static GmOps<NI, MJ> ops[64];
+    static GmI<F, NI, MJ> I[64];
     long errors = 0;
     // cus > 0: a device of that many CUs with the workspace the plan asks
     // for; 0: no workspace (neither split nor per-call rewrite)
@@ -463,15 +464,16 @@ long run_gemm_mj(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, ui
                         else
                             gm_stage_w<F>(a, src, tab, n0, t0, tid, lds.data());
                     }
-                    for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) gm_stage_x<F, MJ>(a, mt0, t0, tid, lds.data());
+                    for (uint32_t tid = 0; tid < (uint32_t)WG; tid++)
+                        gm_stage_x<F, Sh::BM>(a, mt0, t0, tid, lds.data());
                     const uint32_t nsp = te - t0 < GM_SP ? te - t0 : GM_SP;
                     for (uint32_t sp = 0; sp < nsp; sp++)
                         for (uint32_t wv = 0; wv < 4u; wv++) {
                             for (uint32_t lane = 0; lane < 64u; lane++)
-                                gm_ops<F, MJ>(lds.data(), wv, lane, sp, ops[lane]);
+                                gm_ops<F, NI, MJ>(lds.data(), wv, lane, sp, ops[lane]);
                             for (uint32_t h = 0; h < G::NH; h++)
                                 for (int j = 0; j < MJ; j++)
-                                    for (int i = 0; i < 4; i++) {
+                                    for (int i = 0; i < NI; i++) {
                                         uint64_t A[64], B[64];
                                         int D[64][4];
                                         for (uint32_t l = 0; l < 64u; l++) {
@@ -483,20 +485,20 @@ long run_gemm_mj(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, ui
                                             for (int e = 0; e < 4; e++) I[l].v[h][i][j][e] = D[l][e];
                                     }
                             for (uint32_t lane = 0; lane < 64u; lane++)
-                                gm_epi<F, MJ>(lds.data(), wv, lane, sp, I[lane], acc[wv][lane]);
+                                gm_epi<F, NI, MJ>(lds.data(), wv, lane, sp, I[lane], acc[wv][lane]);
                         }
                     if constexpr (G::AFF) {
                         const uint32_t nk = nsp * G::NH;
                         for (uint32_t q = 0; 4u * q < nk; q++)
                             for (uint32_t wv = 0; wv < 4u; wv++) {
-                                float Al[64][4], Bl[64][MJ];
+                                float Al[64][NI], Bl[64][MJ];
                                 for (uint32_t lane = 0; lane < 64u; lane++) {
-                                    float a4[4], b2[MJ];
-                                    gm_offsets_ops<F, MJ>(lds.data(), wv, lane, q, nk, a4, b2);
-                                    for (int i = 0; i < 4; i++) Al[lane][i] = a4[i];
+                                    float a4[NI], b2[MJ];
+                                    gm_offsets_ops<F, NI, MJ>(lds.data(), wv, lane, q, nk, a4, b2);
+                                    for (int i = 0; i < NI; i++) Al[lane][i] = a4[i];
                                     for (int j = 0; j < MJ; j++) Bl[lane][j] = b2[j];
                                 }
-                                for (int i = 0; i < 4; i++)
+                                for (int i = 0; i < NI; i++)
                                     for (int j = 0; j < MJ; j++) {
                                         float A[64], B[64], C[64][4];
                                         for (int l = 0; l < 64; l++) {
@@ -513,7 +515,7 @@ long run_gemm_mj(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, ui
                 }
                 for (uint32_t wv = 0; wv < 4u; wv++)
                     for (uint32_t lane = 0; lane < 64u; lane++)
-                        gm_store<MJ>(a, n0, mt0, ks, wv, lane, acc[wv][lane]);
+                        gm_store<NI, MJ>(a, n0, mt0, ks, wv, lane, acc[wv][lane]);
             }
             if (chk.errors) {
                 if (errors == 0) snprintf(err, errlen, "%s", chk.msg);
@@ -537,9 +539,10 @@ long run_gemm_mj(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, ui
 template <int F>
 long run_gemm(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y, uint64_t max_rows,
               uint64_t max_mrows, uint32_t cus, uint32_t *nsplit_out, char *err, int errlen) {
-    if (nq::gm_bm(M) == nq::GM_BM)
-        return run_gemm_mj<F, 2>(w, N, K, xq, M, y, max_rows, max_mrows, cus, nsplit_out, err, errlen);
-    return run_gemm_mj<F, 1>(w, N, K, xq, M, y, max_rows, max_mrows, cus, nsplit_out, err, errlen);
+    const uint32_t bm = nq::gm_bm(M);
+    if (bm == 64u) return run_gemm_sh<F, 4, 2>(w, N, K, xq, M, y, max_rows, max_mrows, cus, nsplit_out, err, errlen);
+    if (bm == 32u) return run_gemm_sh<F, 4, 1>(w, N, K, xq, M, y, max_rows, max_mrows, cus, nsplit_out, err, errlen);
+    return run_gemm_sh<F, 2, 1>(w, N, K, xq, M, y, max_rows, max_mrows, cus, nsplit_out, err, errlen);
 }
 
 }  // namespace

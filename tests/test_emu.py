@@ -375,7 +375,8 @@ def test_emu_gemm_matches_oracle(fmt):
     for N, M, w_mis, max_rows, max_mrows, cus in [(150, 9, 0, 0, 0, 0), (37, 70, 1, 0, 0, 0),
                                                   (260, 65, 3, 128, 0, 256), (130, 100, 2, 0, 40, 256),
                                                   (37, 1100, 1, 0, 500, 256), (140, 1030, 2, 128, 0, 256),
-                                                  (60, 32, 1, 0, 0, 0), (200, 21, 3, 0, 0, 256)]:
+                                                  (60, 32, 1, 0, 0, 0), (200, 21, 3, 0, 0, 256),
+                                                  (140, 16, 2, 0, 0, 0), (37, 7, 1, 0, 0, 256)]:
         w = synth.payload(fmt, N * K // B, 7 + N, synth.binade(-6, -2, False))
         _, xq = oracle.quantize_q8_1(_act(M, K, M).astype(np.float32))
         y, rc, msg, guards, (ns, once) = emu_lib.gemm_q8_1(idx, w, N, K, xq, M, w_mis=w_mis, max_rows=max_rows,
