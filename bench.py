@@ -374,7 +374,7 @@ def gemm_measurement(torch, nq, synth, fmt, shape, M, launches=20, footprint=1 <
 
 
 GEMM_CASES = [("gguf:q4_k", 512), ("gguf:q8_0", 512), ("gguf:q6_k", 512), ("gguf:q4_0", 512), ("gguf:iq4_xs", 512),
-              ("gguf:iq2_xxs", 512), ("gguf:q4_k", 64), ("gguf:q4_k", 2048)]
+              ("gguf:iq2_xxs", 512), ("gguf:q4_k", 16), ("gguf:q4_k", 64), ("gguf:q4_k", 2048)]
 
 
 def gemm_cpu_baseline(synth, fmt="gguf:q4_k", shape=(14336, 4096), rows=7168, M=512, seed=0x6E7C8000):
