@@ -390,3 +390,18 @@ def test_gemm_tiny_shapes(fmt, N, K, M):
     for split in (True, False):
         y = _gemm(fmt, w, N, K, xq, w_off=1, split=split)
         linear_check(y, ref, env, K, f"{fmt} [{N}, {K}] x {M}")
+
+
+@pytest.mark.parametrize("fmt,M", [("gguf:q4_k", 20), ("gguf:q8_0", 9), ("gguf:iq3_s", 40)])
+def test_gemm_long_rows(fmt, M):
+    """K = 28672 (112 K steps): many steps per workgroup, K split over
+    workgroups, small-batch tile heights; sampled rows against the oracle."""
+    N, K = 600, 28672
+    w = _weights(fmt, N, K, 81)
+    _, xq = oracle.quantize_q8_1(_act(M, K, 82).astype(np.float32))
+    announce(f"gemm long rows {fmt} [{N}, {K}] x {M}")
+    y = _gemm(fmt, w, N, K, xq)
+    rows = np.unique(np.r_[0, 127, 128, N - 1, np.random.default_rng(M).integers(0, N, size=20)])
+    sub = w.reshape(N, -1)[rows].ravel()
+    ref, env = oracle.gemv_q8_1(fmt, sub, rows.size, K, xq, M)
+    linear_check(y[:, rows], ref, env, K, f"{fmt} K={K} M={M}")
