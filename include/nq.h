@@ -255,7 +255,7 @@ int nq_gemv_q8_1(int32_t format, const void *weight, uint64_t nbytes, int64_t N,
  * values become signed 8-bit codes with a binary32 scale (and an offset for
  * q4_1, q5_1, q2_k, q4_k and q5_k), their exact integer dot products with
  * the activation codes come from the 8-bit matrix cores, and each is scaled
- * and added in binary32.
+ * and added in binary32 (tiles of 16, 32 or 64 activation rows by M).
  * When the output has few tiles and K is long, K is split over workgroups:
  * each split's partial output goes to `workspace` (device memory the caller
  * owns, at least the size nq_gemm_q8_1_workspace reports, 16-byte aligned,
@@ -271,8 +271,8 @@ int nq_gemv_q8_1(int32_t format, const void *weight, uint64_t nbytes, int64_t N,
  * be any count >= 1 below 2^31 with M * K / 32 * 36 and M * N * 4 below 2^63
  * (NQ_ERR_OVERFLOW).  nq_gemm_q8_1_workspace runs the same checks (nbytes
  * taken as the format's length rule) and stores the workspace size for the
- * shape on the current device (0 when the product would not split; `bytes`
- * NULL: NQ_ERR_NULL_ARG).  nq_gemm_q8_1 requires weight, xq and y non-NULL
+ * shape on the current device (0 when the product would neither split K nor
+ * rewrite the weight once; `bytes` NULL: NQ_ERR_NULL_ARG).  nq_gemm_q8_1 requires weight, xq and y non-NULL
  * and xq and y aligned to 4 bytes and workspace to 16 (NQ_ERR_NULL_ARG), then
  * enqueues the product on `stream`.  The caller owns every buffer; y must not
  * overlap the inputs. */
