@@ -66,7 +66,8 @@ def build(jobs=None, verbose=False, out=LIB, defines=()):
     """Compile every source and link the library (default: libnq.so in-tree).
 
     `defines` are extra -D macros (the tuning knobs NQ_UPT, NQ_RESIDENT_PER_CU,
-    NQ_NT_STORE, NQ_NTL of csrc/nq_kernel.h and NQ_F8_NB of csrc/nq_fp8row.h);
+    NQ_NT_STORE, NQ_NTL of csrc/nq_kernel.h, NQ_F8_NB of csrc/nq_fp8row.h and
+    NQ_GM_SP4_TILES of csrc/nq_gemm.h);
     a non-default `out` builds elsewhere.
     """
     build_dir = BUILD if out == LIB else out + ".build"

@@ -28,7 +28,10 @@
 // has a rewrite.
 //
 // Tiling.  A workgroup (4 waves) owns a tile of 128 weight rows by 64
-// activation rows and walks K in steps of 256 values: its threads rewrite the
+// activation rows and walks K in steps of 256 values (128 on grids of at
+// least three 64-row tiles per compute unit: half the LDS, so more
+// workgroups share a compute unit and hide each other's staging): its
+// threads rewrite the
 // step's weight spans into LDS (codes, scales, offsets) and copy the
 // activation codes, scales and d * S terms next to them; then each wave
 // computes a 64 x 32 sub-tile, span by span, in a fixed order, so every run
@@ -37,7 +40,10 @@
 // the weight bytes come from one L2.  With a workspace, shapes with few
 // tiles and long K split K over workgroups (partial outputs summed in split
 // order by a second launch), and large batches have the weight rewritten
-// once per call so that the tiles copy it (gm_plan).
+// once per call so that the tiles copy it (gm_plan).  Without offset terms
+// the step length leaves every output the same sum in the same order; the
+// affine formats add their offset terms once per step, so the two step
+// lengths round them in a different order.
 #pragma once
 
 #include "nq_gemv.h"
@@ -46,8 +52,12 @@ namespace nq {
 
 constexpr uint32_t GM_BN = 128;            // weight rows per tile
 constexpr uint32_t GM_BM = 64;             // activation rows per tile (32 for batches of at most 32 rows)
-constexpr uint32_t GM_SP = 8;              // spans per K step (256 values)
-constexpr uint32_t GM_CSW = 8u * GM_SP + 4u;  // LDS dwords per code row (256 code bytes + 16 of padding)
+constexpr uint32_t GM_SP = 8;              // spans per K step (256 values; 4 on large grids, gm_plan)
+#ifndef NQ_GM_SP4_TILES
+#define NQ_GM_SP4_TILES 3
+#endif
+// 64-row tiles per compute unit from which K steps hold 4 spans
+constexpr uint32_t GM_SP4_TILES_PER_CU = NQ_GM_SP4_TILES;
 constexpr uint64_t GM_MAX_MROWS = 1ull << 16;  // activation rows per launch
 constexpr uint64_t GM_MIN_M = 5;  // fewer activation rows take the single-row kernel (faster there)
 constexpr uint64_t GM_REWRITE_ONCE_M = 1024;   // more activation rows: the weight is rewritten once per call
@@ -75,24 +85,26 @@ struct GmShape {
     NQ_HD static uint32_t mb(uint32_t w) { return 16u * (uint32_t)MJ * (w / WN); }
 };
 
-template <int F, int BMT = 64>
+template <int F, int BMT = 64, int SPT = 8>
 struct GmFmt {
     static constexpr uint32_t BM = (uint32_t)BMT;  // activation rows per tile
+    static constexpr uint32_t SP = (uint32_t)SPT;  // spans per K step
+    static constexpr uint32_t CSW = 8u * SP + 4u;  // LDS dwords per code row (the step's codes + 16 bytes)
     static constexpr bool U16 = gm_u16(F);
     static constexpr bool AFF = gm_aff(F);
     // formats with a span rewrite (every gguf format)
     static constexpr bool OK = F != NVFP4_DIV;
     static constexpr uint32_t NH = U16 ? 2u : 1u;  // scales per span
     static constexpr uint32_t SPB = (uint32_t)block_values(F) / 32u;  // spans per block
-    // LDS layout (dwords): weight codes [128][GM_CSW], scales [8][NH][128],
-    // offsets [8][NH][128] (affine formats), activation codes [BM][GM_CSW],
-    // scales [8][BM], d * S terms [8][NH][BM] (affine formats)
-    static constexpr uint32_t WS = GM_BN * GM_CSW;
-    static constexpr uint32_t WO = WS + GM_SP * NH * GM_BN;
-    static constexpr uint32_t XC = WO + (AFF ? GM_SP * NH * GM_BN : 0u);
-    static constexpr uint32_t XD = XC + BM * GM_CSW;
-    static constexpr uint32_t XT = XD + GM_SP * BM;
-    static constexpr uint32_t DW = XT + (AFF ? GM_SP * NH * BM : 0u);
+    // LDS layout (dwords): weight codes [128][CSW], scales [SP][NH][128],
+    // offsets [SP][NH][128] (affine formats), activation codes [BM][CSW],
+    // scales [SP][BM], d * S terms [SP][NH][BM] (affine formats)
+    static constexpr uint32_t WS = GM_BN * CSW;
+    static constexpr uint32_t WO = WS + SP * NH * GM_BN;
+    static constexpr uint32_t XC = WO + (AFF ? SP * NH * GM_BN : 0u);
+    static constexpr uint32_t XD = XC + BM * CSW;
+    static constexpr uint32_t XT = XD + SP * BM;
+    static constexpr uint32_t DW = XT + (AFF ? SP * NH * BM : 0u);
 };
 
 struct GmArgs {
@@ -289,23 +301,23 @@ NQ_HD void gm_tile(const GmArgs &a, uint32_t id, uint32_t *n0, uint32_t *m0, uin
     *n0 = (T / a.mt) * GM_BN;
 }
 
-// K step: the spans t0 .. t0+7 of weight rows n0 .. n0+127, rewritten into
-// LDS; thread tid takes items tid + WG r (r < 4), item i = (row i / 8, span
-// i mod 8).  The loads take no branch (an item past the launch's rows or
-// past K reads the launch's first span and is then zeroed), so the four
-// items' loads are all in flight at once.
-template <int F, class Src>
+// K step: the spans t0 .. t0+SP-1 of weight rows n0 .. n0+127, rewritten
+// into LDS; thread tid takes items tid + WG r (r < SP / 2), item i = (row
+// i / SP, span i mod SP).  The loads take no branch (an item past the
+// launch's rows or past K reads the launch's first span and is then zeroed),
+// so the items' loads are all in flight at once.
+template <int F, int SP, class Src>
 NQ_HD void gm_stage_w(const GmArgs &a, const Src &src, const Tab &tab, uint32_t n0, uint32_t t0, uint32_t tid,
                       uint32_t *lds) {
-    using G = GmFmt<F>;
+    using G = GmFmt<F, 64, SP>;
     constexpr uint32_t S = (uint32_t)block_bytes(F);
-    constexpr uint32_t R = GM_BN * GM_SP / (uint32_t)WG;
-    static_assert(GM_BN * GM_SP % (uint32_t)WG == 0, "whole items per thread");
+    constexpr uint32_t R = GM_BN * G::SP / (uint32_t)WG;
+    static_assert(GM_BN * G::SP % (uint32_t)WG == 0, "whole items per thread");
     GmSpan o[R];
     bool ok[R];
 #pragma unroll
     for (uint32_t r = 0; r < R; r++) {
-        const uint32_t i = tid + (uint32_t)WG * r, n = i / GM_SP, t = t0 + i % GM_SP;
+        const uint32_t i = tid + (uint32_t)WG * r, n = i / G::SP, t = t0 + i % G::SP;
         ok[r] = n0 + n < a.rows && t < a.kspans;
         const uint32_t nn = ok[r] ? n0 + n : 0u, tt = ok[r] ? t : 0u, b = tt / G::SPB;
         gm_span<F>(src, a.wmis + nn * a.row_bytes + b * S, tt - b * G::SPB, tab, o[r]);
@@ -313,8 +325,8 @@ NQ_HD void gm_stage_w(const GmArgs &a, const Src &src, const Tab &tab, uint32_t 
     float *ws = (float *)(lds + G::WS), *ow = (float *)(lds + G::WO);
 #pragma unroll
     for (uint32_t r = 0; r < R; r++) {
-        const uint32_t i = tid + (uint32_t)WG * r, n = i / GM_SP, sp = i % GM_SP;
-        uint32_t *cw = lds + n * GM_CSW + 8u * sp;
+        const uint32_t i = tid + (uint32_t)WG * r, n = i / G::SP, sp = i % G::SP;
+        uint32_t *cw = lds + n * G::CSW + 8u * sp;
 #pragma unroll
         for (int j = 0; j < 8; j++) cw[j] = ok[r] ? o[r].c[j] : 0u;
 #pragma unroll
@@ -328,16 +340,16 @@ NQ_HD void gm_stage_w(const GmArgs &a, const Src &src, const Tab &tab, uint32_t 
 // K step from the weight rewritten once per call: the same LDS contents as
 // gm_stage_w, copied (two 16-byte loads of codes and the scales / offsets
 // per item, no per-format work).
-template <int F>
+template <int F, int SP>
 NQ_HD void gm_stage_wc(const GmArgs &a, uint32_t n0, uint32_t t0, uint32_t tid, uint32_t *lds) {
-    using G = GmFmt<F>;
-    constexpr uint32_t R = GM_BN * GM_SP / (uint32_t)WG;
+    using G = GmFmt<F, 64, SP>;
+    constexpr uint32_t R = GM_BN * G::SP / (uint32_t)WG;
     uint32_t c[R][8];
     float sw[R][2], so[R][2];
     bool ok[R];
 #pragma unroll
     for (uint32_t r = 0; r < R; r++) {
-        const uint32_t i = tid + (uint32_t)WG * r, n = i / GM_SP, t = t0 + i % GM_SP;
+        const uint32_t i = tid + (uint32_t)WG * r, n = i / G::SP, t = t0 + i % G::SP;
         ok[r] = n0 + n < a.rows && t < a.kspans;
         const uint32_t nn = ok[r] ? n0 + n : 0u, tt = ok[r] ? t : 0u;
         const uint32_t *p = a.cw + (uint64_t)nn * a.kspans * 8u + (uint64_t)tt * 8u;
@@ -354,8 +366,8 @@ NQ_HD void gm_stage_wc(const GmArgs &a, uint32_t n0, uint32_t t0, uint32_t tid, 
     float *ws = (float *)(lds + G::WS), *ow = (float *)(lds + G::WO);
 #pragma unroll
     for (uint32_t r = 0; r < R; r++) {
-        const uint32_t i = tid + (uint32_t)WG * r, n = i / GM_SP, sp = i % GM_SP;
-        uint32_t *cw = lds + n * GM_CSW + 8u * sp;
+        const uint32_t i = tid + (uint32_t)WG * r, n = i / G::SP, sp = i % G::SP;
+        uint32_t *cw = lds + n * G::CSW + 8u * sp;
 #pragma unroll
         for (int j = 0; j < 8; j++) cw[j] = ok[r] ? c[r][j] : 0u;
 #pragma unroll
@@ -392,22 +404,22 @@ NQ_HD void gm_rewrite_item(const GmArgs &a, const Src &src, const Tab &tab, uint
     }
 }
 
-// K step, activation side: blocks t0 .. t0+7 of activation rows m0 ..
+// K step, activation side: blocks t0 .. t0+SP-1 of activation rows m0 ..
 // m0+BM-1 (codes, binary32 scale, and for the affine formats d times the
-// exact code sum of each half); thread tid takes items tid + WG r (r < BM /
-// 32), item i = (row i / 8, block i mod 8), loaded without branches as above.
-template <int F, int BMT>
+// exact code sum of each half); thread tid takes items tid + WG r, item i =
+// (row i / SP, block i mod SP), loaded without branches as above.
+template <int F, int BMT, int SP>
 NQ_HD void gm_stage_x(const GmArgs &a, uint32_t m0, uint32_t t0, uint32_t tid, uint32_t *lds) {
-    using G = GmFmt<F, BMT>;
-    // BM * 8 items: whole multiples of the workgroup, or (16 rows) half of it
-    constexpr uint32_t R = (G::BM * GM_SP + (uint32_t)WG - 1u) / (uint32_t)WG;
+    using G = GmFmt<F, BMT, SP>;
+    // BM * SP items: whole multiples of the workgroup, or (16 rows) half of it
+    constexpr uint32_t R = (G::BM * G::SP + (uint32_t)WG - 1u) / (uint32_t)WG;
     uint32_t c[R][8];
     float d[R];
     bool ok[R];
 #pragma unroll
     for (uint32_t r = 0; r < R; r++) {
-        const uint32_t i = tid + (uint32_t)WG * r, m = i / GM_SP, t = t0 + i % GM_SP;
-        ok[r] = i < G::BM * GM_SP && m0 + m < a.M && t < a.kspans;
+        const uint32_t i = tid + (uint32_t)WG * r, m = i / G::SP, t = t0 + i % G::SP;
+        ok[r] = i < G::BM * G::SP && m0 + m < a.M && t < a.kspans;
         const uint32_t *p = a.xq + (ok[r] ? (uint64_t)(m0 + m) * a.xrow + (uint64_t)t * 9u : 0ull);
         const u32x4a4 v0 = *(const u32x4a4 *)(p + 1), v1 = *(const u32x4a4 *)(p + 5);
         c[r][0] = v0.x; c[r][1] = v0.y; c[r][2] = v0.z; c[r][3] = v0.w;
@@ -416,10 +428,10 @@ NQ_HD void gm_stage_x(const GmArgs &a, uint32_t m0, uint32_t t0, uint32_t tid, u
     }
 #pragma unroll
     for (uint32_t r = 0; r < R; r++) {
-        const uint32_t i = tid + (uint32_t)WG * r, m = i / GM_SP, sp = i % GM_SP;
-        if (i >= G::BM * GM_SP) continue;  // (16-row tiles) threads past the tile's items
+        const uint32_t i = tid + (uint32_t)WG * r, m = i / G::SP, sp = i % G::SP;
+        if (i >= G::BM * G::SP) continue;  // (16-row tiles) threads past the tile's items
         const float dr = ok[r] ? d[r] : 0.0f;
-        uint32_t *cx = lds + G::XC + m * GM_CSW + 8u * sp;
+        uint32_t *cx = lds + G::XC + m * G::CSW + 8u * sp;
 #pragma unroll
         for (int j = 0; j < 8; j++) cx[j] = ok[r] ? c[r][j] : 0u;
         ((float *)(lds + G::XD))[sp * G::BM + m] = dr;
@@ -453,16 +465,16 @@ struct GmOps {
 
 NQ_HD uint64_t lds_u64(const uint32_t *p) { return (uint64_t)p[0] | ((uint64_t)p[1] << 32); }
 
-template <int F, int NI, int MJ>
+template <int F, int NI, int MJ, int SP>
 NQ_HD void gm_ops(const uint32_t *lds, uint32_t w, uint32_t lane, uint32_t sp, GmOps<NI, MJ> &o) {
     using Sh = GmShape<NI, MJ>;
-    using G = GmFmt<F, Sh::BM>;
+    using G = GmFmt<F, Sh::BM, SP>;
     const uint32_t r = lane & 15u, k = 8u * sp + 2u * (lane >> 4);
     const uint32_t nb = Sh::nb(w), mb = Sh::mb(w);
 #pragma unroll
-    for (int i = 0; i < NI; i++) o.A[i] = lds_u64(lds + (nb + 16u * (uint32_t)i + r) * GM_CSW + k);
+    for (int i = 0; i < NI; i++) o.A[i] = lds_u64(lds + (nb + 16u * (uint32_t)i + r) * G::CSW + k);
 #pragma unroll
-    for (int j = 0; j < MJ; j++) o.B[j] = lds_u64(lds + G::XC + (mb + 16u * (uint32_t)j + r) * GM_CSW + k);
+    for (int j = 0; j < MJ; j++) o.B[j] = lds_u64(lds + G::XC + (mb + 16u * (uint32_t)j + r) * G::CSW + k);
 }
 
 // Activation operand for half h of a span with 16-value scales: lanes 0-31
@@ -486,11 +498,11 @@ struct GmI {
 // The span's scaling into the lane's accumulators (fixed order: per output,
 // the halves).  The affine formats' offset terms are added per K step by
 // gm_offsets on the matrix cores.
-template <int F, int NI, int MJ>
+template <int F, int NI, int MJ, int SP>
 NQ_HD void gm_epi(const uint32_t *lds, uint32_t w, uint32_t lane, uint32_t sp, const GmI<F, NI, MJ> &I,
                   float (&acc)[NI][MJ][4]) {
     using Sh = GmShape<NI, MJ>;
-    using G = GmFmt<F, Sh::BM>;
+    using G = GmFmt<F, Sh::BM, SP>;
     const uint32_t nb = Sh::nb(w) + 4u * (lane >> 4), mb = Sh::mb(w) + (lane & 15u);
     const float *ws = (const float *)(lds + G::WS);
     const float *xd = (const float *)(lds + G::XD);
@@ -523,11 +535,11 @@ NQ_HD void gm_epi(const uint32_t *lds, uint32_t w, uint32_t lane, uint32_t sp, c
 // k at a time into the accumulators (A[i][k]: lane l supplies row l mod 16,
 // k = l / 16; B[k][j] likewise; the result has the int8 tiles' lane layout).
 // Operands of quad q for a lane (k past the step's nk are zeros).
-template <int F, int NI, int MJ>
+template <int F, int NI, int MJ, int SP>
 NQ_HD void gm_offsets_ops(const uint32_t *lds, uint32_t w, uint32_t lane, uint32_t q, uint32_t nk, float (&A)[NI],
                           float (&B)[MJ]) {
     using Sh = GmShape<NI, MJ>;
-    using G = GmFmt<F, Sh::BM>;
+    using G = GmFmt<F, Sh::BM, SP>;
     const uint32_t k = 4u * q + (lane >> 4), r = lane & 15u;
     const uint32_t nb = Sh::nb(w), mb = Sh::mb(w);
     const float *ow = (const float *)(lds + G::WO), *xt = (const float *)(lds + G::XT);
@@ -563,10 +575,10 @@ NQ_HD void gm_store(const GmArgs &a, uint32_t n0, uint32_t m0, uint32_t ks, uint
 
 typedef int gm_i32x4 __attribute__((ext_vector_type(4)));
 
-template <int F, int NI, int MJ>
+template <int F, int NI, int MJ, int SP>
 __global__ __launch_bounds__(WG) void k_gemm(GmArgs a) {
     using Sh = GmShape<NI, MJ>;
-    using G = GmFmt<F, Sh::BM>;
+    using G = GmFmt<F, Sh::BM, SP>;
     using TS = TabSpec<F>;
     __shared__ uint64_t t8[TS::n8 > 0 ? TS::n8 : 1];
     __shared__ uint32_t t4[TS::n4 > 0 ? TS::n4 : 1];
@@ -585,19 +597,19 @@ __global__ __launch_bounds__(WG) void k_gemm(GmArgs a) {
         for (int j = 0; j < MJ; j++)
 #pragma unroll
             for (int e = 0; e < 4; e++) acc[i][j][e] = 0.0f;
-    const uint32_t tb = ks * a.sps * GM_SP, te0 = tb + a.sps * GM_SP, te = te0 < a.kspans ? te0 : a.kspans;
-    for (uint32_t t0 = tb; t0 < te; t0 += GM_SP) {
+    const uint32_t tb = ks * a.sps * G::SP, te0 = tb + a.sps * G::SP, te = te0 < a.kspans ? te0 : a.kspans;
+    for (uint32_t t0 = tb; t0 < te; t0 += G::SP) {
         __syncthreads();  // the previous step's readers are done (and the tables are filled)
         if (a.cw)
-            gm_stage_wc<F>(a, n0, t0, threadIdx.x, lds);
+            gm_stage_wc<F, SP>(a, n0, t0, threadIdx.x, lds);
         else
-            gm_stage_w<F>(a, src, tab, n0, t0, threadIdx.x, lds);
-        gm_stage_x<F, Sh::BM>(a, m0, t0, threadIdx.x, lds);
+            gm_stage_w<F, SP>(a, src, tab, n0, t0, threadIdx.x, lds);
+        gm_stage_x<F, Sh::BM, SP>(a, m0, t0, threadIdx.x, lds);
         __syncthreads();
-        const uint32_t nsp = te - t0 < GM_SP ? te - t0 : GM_SP;
+        const uint32_t nsp = te - t0 < G::SP ? te - t0 : G::SP;
         for (uint32_t sp = 0; sp < nsp; sp++) {
             GmOps<NI, MJ> o;
-            gm_ops<F, NI, MJ>(lds, w, lane, sp, o);
+            gm_ops<F, NI, MJ, SP>(lds, w, lane, sp, o);
             GmI<F, NI, MJ> I;
 #pragma unroll
             for (uint32_t h = 0; h < G::NH; h++)
@@ -612,14 +624,14 @@ __global__ __launch_bounds__(WG) void k_gemm(GmArgs a) {
                         for (int e = 0; e < 4; e++) I.v[h][i][j][e] = r[e];
                     }
                 }
-            gm_epi<F, NI, MJ>(lds, w, lane, sp, I, acc);
+            gm_epi<F, NI, MJ, SP>(lds, w, lane, sp, I, acc);
         }
         if constexpr (G::AFF) {
             typedef float gm_f32x4 __attribute__((ext_vector_type(4)));
             const uint32_t nk = nsp * G::NH;
             for (uint32_t q = 0; 4u * q < nk; q++) {
                 float A[NI], B[MJ];
-                gm_offsets_ops<F, NI, MJ>(lds, w, lane, q, nk, A, B);
+                gm_offsets_ops<F, NI, MJ, SP>(lds, w, lane, q, nk, A, B);
 #pragma unroll
                 for (int i = 0; i < NI; i++)
 #pragma unroll
@@ -671,18 +683,29 @@ __global__ __launch_bounds__(WG) void k_gemm_sum(const float *part, float *y, ui
 // is rewritten once into the workspace (codes, scales, offsets) and the
 // tiles copy it, instead of each tile rewriting it (measured +2 to +11% at
 // 2048 rows, a loss at 512 and below: the copy is about twice the packed
-// bytes).  The results are the same bits either way for (2).  The plan depends only on N, K, M and the
-// compute-unit count.
+// bytes).  The results are the same bits either way for (2).  (3) With
+// 64-row tiles, at least three per compute unit, K steps hold 4 spans
+// instead of 8 (measured 5-23% faster there, up to 45% slower at two tiles
+// per compute unit).  The plan depends only on N, K, M and the compute-unit
+// count.
 struct GmPlan {
     uint32_t nsplit, sps;
     bool rewrite_once;  // the weight rewritten once per call (into the workspace)
+    uint32_t sp;        // spans per K step (4 or 8)
 };
 
+// The plan without a workspace: no K split, the weight rewritten per tile.
+inline GmPlan gm_plan_plain(const GmPlan &p, uint64_t K) {
+    return GmPlan{1u, (uint32_t)((K / 32 + p.sp - 1) / p.sp), false, p.sp};
+}
+
 inline GmPlan gm_plan(uint64_t N, uint64_t K, uint64_t M, uint32_t cus) {
-    const uint64_t steps = (K / 32 + GM_SP - 1) / GM_SP;
     const uint64_t bm = gm_bm(M), tiles = (N + GM_BN - 1) / GM_BN * ((M + bm - 1) / bm);
-    const uint64_t target = 2ull * (cus ? cus : 1u);
-    GmPlan p{1u, (uint32_t)steps, M > GM_REWRITE_ONCE_M};
+    const uint64_t c = cus ? cus : 1u;
+    const uint32_t sp = bm == 64u && tiles >= GM_SP4_TILES_PER_CU * c ? 4u : GM_SP;
+    const uint64_t steps = (K / 32 + sp - 1) / sp;
+    const uint64_t target = 2ull * c;
+    GmPlan p{1u, (uint32_t)steps, M > GM_REWRITE_ONCE_M, sp};
     if (tiles >= target || steps < 8) return p;
     uint64_t S = (target + tiles - 1) / tiles;
     if (S > steps / 4) S = steps / 4;
@@ -772,7 +795,7 @@ int launch_gemm_mfma(const GvLaunch &L, void *ws, uint64_t ws_bytes, hipStream_t
     GmPlan p = gm_plan(L.N, L.K, L.M, L.cus);
     const bool use = ws != nullptr && ws_bytes >= gm_ws_layout(F, p, L.N, L.K, L.M).total &&
                      (p.nsplit > 1 || p.rewrite_once);
-    if (!use) p = GmPlan{1u, (uint32_t)((L.K / 32 + GM_SP - 1) / GM_SP), false};
+    if (!use) p = gm_plan_plain(p, L.K);
     const GmWsLayout wl = gm_ws_layout(F, p, L.N, L.K, L.M);
     const bool split = p.nsplit > 1;
     float *out = split ? (float *)ws : L.y;
@@ -794,12 +817,14 @@ int launch_gemm_mfma(const GvLaunch &L, void *ws, uint64_t ws_bytes, hipStream_t
         for (uint64_t r0 = 0; r0 < L.N;) {
             const uint64_t rows = L.N - r0 < max_rows ? L.N - r0 : max_rows;
             const GmArgs a = gm_args<F>(L, r0, rows, m0, mrows, p, out, canon, &wl);
-            if (a.bm == 64u)
-                hipLaunchKernelGGL((k_gemm<F, 4, 2>), dim3(gm_grid(a)), dim3(WG), 0, stream, a);
+            if (a.bm == 64u && p.sp == 4u)
+                hipLaunchKernelGGL((k_gemm<F, 4, 2, 4>), dim3(gm_grid(a)), dim3(WG), 0, stream, a);
+            else if (a.bm == 64u)
+                hipLaunchKernelGGL((k_gemm<F, 4, 2, 8>), dim3(gm_grid(a)), dim3(WG), 0, stream, a);
             else if (a.bm == 32u)
-                hipLaunchKernelGGL((k_gemm<F, 4, 1>), dim3(gm_grid(a)), dim3(WG), 0, stream, a);
+                hipLaunchKernelGGL((k_gemm<F, 4, 1, 8>), dim3(gm_grid(a)), dim3(WG), 0, stream, a);
             else
-                hipLaunchKernelGGL((k_gemm<F, 2, 1>), dim3(gm_grid(a)), dim3(WG), 0, stream, a);
+                hipLaunchKernelGGL((k_gemm<F, 2, 1, 8>), dim3(gm_grid(a)), dim3(WG), 0, stream, a);
             if (hipGetLastError() != hipSuccess) return 9;  // NQ_ERR_HIP
             r0 += rows;
         }

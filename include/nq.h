@@ -255,7 +255,9 @@ int nq_gemv_q8_1(int32_t format, const void *weight, uint64_t nbytes, int64_t N,
  * values become signed 8-bit codes with a binary32 scale (and an offset for
  * q4_1, q5_1, q2_k, q4_k and q5_k), their exact integer dot products with
  * the activation codes come from the 8-bit matrix cores, and each is scaled
- * and added in binary32 (tiles of 16, 32 or 64 activation rows by M).
+ * and added in binary32 (tiles of 16, 32 or 64 activation rows by M; K in
+ * steps of 256 values, or 128 on grids of at least three 64-row tiles per
+ * compute unit).
  * When the output has few tiles and K is long, K is split over workgroups:
  * each split's partial output goes to `workspace` (device memory the caller
  * owns, at least the size nq_gemm_q8_1_workspace reports, 16-byte aligned,

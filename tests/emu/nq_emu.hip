@@ -375,12 +375,12 @@ void mfma_f32_16x16x4(const float (&A)[64], const float (&B)[64], float (&C)[64]
 // poisoned LDS image (weight reads through a bounds-checked source), then per
 // span and wave the lanes' operands, the matrix instruction and the lanes'
 // scaling, and at the end the lanes' stores; then the partials' sum.
-template <int F, int NI, int MJ>
+template <int F, int NI, int MJ, int SP>
 long run_gemm_sh(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y,
-                 uint64_t max_rows, uint64_t max_mrows, uint32_t cus, uint32_t *nsplit_out, char *err, int errlen) {
+                 uint64_t max_rows, uint64_t max_mrows, const nq::GmPlan &plan, char *err, int errlen) {
     using namespace nq;
     using Sh = GmShape<NI, MJ>;
-    using G = GmFmt<F, Sh::BM>;
+    using G = GmFmt<F, Sh::BM, SP>;
     const GvLaunch L{w, N, K, M, xq, y, 0u};
     const uint64_t lim = max_rows ? max_rows : gm_max_rows<F>(L);
     const uint64_t mlim = max_mrows ? max_mrows : GM_MAX_MROWS;
@@ -394,11 +394,10 @@ long run_gemm_sh(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, ui
     static GmOps<NI, MJ> ops[64];
     static GmI<F, NI, MJ> I[64];
     long errors = 0;
-    // cus > 0: a device of that many CUs with the workspace the plan asks
-    // for; 0: no workspace (neither split nor per-call rewrite)
-    GmPlan plan = gm_plan(N, K, M, cus);
-    if (cus == 0) plan = GmPlan{1u, (uint32_t)((K / 32 + GM_SP - 1) / GM_SP), false};
-    *nsplit_out = plan.nsplit | (plan.rewrite_once ? 1u << 16 : 0u);
+    if (plan.sp != G::SP) {
+        snprintf(err, errlen, "K step of %u spans, kernel built for %u", plan.sp, G::SP);
+        return 1;
+    }
     const GmWsLayout wl = gm_ws_layout(F, plan, N, K, M);
     std::vector<uint8_t> wsbuf(wl.total + 256, 0xA5);
     uint8_t *wsp = wsbuf.data() + (256 - (uintptr_t)wsbuf.data() % 256) % 256;
@@ -454,23 +453,23 @@ long run_gemm_sh(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, ui
                         for (auto &i4 : ln)
                             for (auto &j2 : i4)
                                 for (float &v : j2) v = 0.0f;
-                const uint32_t tb = ks * a.sps * GM_SP, te0 = tb + a.sps * GM_SP,
+                const uint32_t tb = ks * a.sps * G::SP, te0 = tb + a.sps * G::SP,
                                te = te0 < a.kspans ? te0 : a.kspans;
-                for (uint32_t t0 = tb; t0 < te; t0 += GM_SP) {
+                for (uint32_t t0 = tb; t0 < te; t0 += G::SP) {
                     std::fill(lds.begin(), lds.end(), 0xA5A5A5A5u);
                     for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) {
                         if (a.cw)
-                            gm_stage_wc<F>(a, n0, t0, tid, lds.data());
+                            gm_stage_wc<F, SP>(a, n0, t0, tid, lds.data());
                         else
-                            gm_stage_w<F>(a, src, tab, n0, t0, tid, lds.data());
+                            gm_stage_w<F, SP>(a, src, tab, n0, t0, tid, lds.data());
                     }
                     for (uint32_t tid = 0; tid < (uint32_t)WG; tid++)
-                        gm_stage_x<F, Sh::BM>(a, mt0, t0, tid, lds.data());
-                    const uint32_t nsp = te - t0 < GM_SP ? te - t0 : GM_SP;
+                        gm_stage_x<F, Sh::BM, SP>(a, mt0, t0, tid, lds.data());
+                    const uint32_t nsp = te - t0 < G::SP ? te - t0 : G::SP;
                     for (uint32_t sp = 0; sp < nsp; sp++)
                         for (uint32_t wv = 0; wv < 4u; wv++) {
                             for (uint32_t lane = 0; lane < 64u; lane++)
-                                gm_ops<F, NI, MJ>(lds.data(), wv, lane, sp, ops[lane]);
+                                gm_ops<F, NI, MJ, SP>(lds.data(), wv, lane, sp, ops[lane]);
                             for (uint32_t h = 0; h < G::NH; h++)
                                 for (int j = 0; j < MJ; j++)
                                     for (int i = 0; i < NI; i++) {
@@ -485,7 +484,7 @@ long run_gemm_sh(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, ui
                                             for (int e = 0; e < 4; e++) I[l].v[h][i][j][e] = D[l][e];
                                     }
                             for (uint32_t lane = 0; lane < 64u; lane++)
-                                gm_epi<F, NI, MJ>(lds.data(), wv, lane, sp, I[lane], acc[wv][lane]);
+                                gm_epi<F, NI, MJ, SP>(lds.data(), wv, lane, sp, I[lane], acc[wv][lane]);
                         }
                     if constexpr (G::AFF) {
                         const uint32_t nk = nsp * G::NH;
@@ -494,7 +493,7 @@ long run_gemm_sh(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, ui
                                 float Al[64][NI], Bl[64][MJ];
                                 for (uint32_t lane = 0; lane < 64u; lane++) {
                                     float a4[NI], b2[MJ];
-                                    gm_offsets_ops<F, NI, MJ>(lds.data(), wv, lane, q, nk, a4, b2);
+                                    gm_offsets_ops<F, NI, MJ, SP>(lds.data(), wv, lane, q, nk, a4, b2);
                                     for (int i = 0; i < NI; i++) Al[lane][i] = a4[i];
                                     for (int j = 0; j < MJ; j++) Bl[lane][j] = b2[j];
                                 }
@@ -535,14 +534,22 @@ long run_gemm_sh(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, ui
     return errors;
 }
 
-// The launcher's tile height for M activation rows.
+// The launcher's plan and kernel for M activation rows: cus > 0 plans for a
+// device of that many compute units with the workspace the plan asks for;
+// 0: no workspace (neither split nor per-call rewrite) and 8-span K steps.
+// *plan_out: nsplit, bit 16 the per-call rewrite, bit 17 4-span K steps.
 template <int F>
 long run_gemm(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y, uint64_t max_rows,
-              uint64_t max_mrows, uint32_t cus, uint32_t *nsplit_out, char *err, int errlen) {
-    const uint32_t bm = nq::gm_bm(M);
-    if (bm == 64u) return run_gemm_sh<F, 4, 2>(w, N, K, xq, M, y, max_rows, max_mrows, cus, nsplit_out, err, errlen);
-    if (bm == 32u) return run_gemm_sh<F, 4, 1>(w, N, K, xq, M, y, max_rows, max_mrows, cus, nsplit_out, err, errlen);
-    return run_gemm_sh<F, 2, 1>(w, N, K, xq, M, y, max_rows, max_mrows, cus, nsplit_out, err, errlen);
+              uint64_t max_mrows, uint32_t cus, uint32_t *plan_out, char *err, int errlen) {
+    using namespace nq;
+    GmPlan p = gm_plan(N, K, M, cus);
+    if (cus == 0) p = gm_plan_plain(GmPlan{1u, 0u, false, GM_SP}, K);
+    *plan_out = p.nsplit | (p.rewrite_once ? 1u << 16 : 0u) | (p.sp == 4u ? 1u << 17 : 0u);
+    const uint32_t bm = gm_bm(M);
+    if (bm == 64u && p.sp == 4u) return run_gemm_sh<F, 4, 2, 4>(w, N, K, xq, M, y, max_rows, max_mrows, p, err, errlen);
+    if (bm == 64u) return run_gemm_sh<F, 4, 2, 8>(w, N, K, xq, M, y, max_rows, max_mrows, p, err, errlen);
+    if (bm == 32u) return run_gemm_sh<F, 4, 1, 8>(w, N, K, xq, M, y, max_rows, max_mrows, p, err, errlen);
+    return run_gemm_sh<F, 2, 1, 8>(w, N, K, xq, M, y, max_rows, max_mrows, p, err, errlen);
 }
 
 }  // namespace

@@ -35,7 +35,9 @@ def build():
         for r in results:
             if r.returncode != 0:
                 raise RuntimeError(f"emulator build failed:\n{r.stderr[-4000:]}")
-        subprocess.run(["hipcc", "-shared", "-fPIC"] + objs + ["-o", LIB], check=True, capture_output=True)
+        part = LIB + f".{os.getpid()}.tmp"  # linked next to LIB, then renamed onto it (atomic)
+        subprocess.run(["hipcc", "-shared", "-fPIC"] + objs + ["-o", part], check=True, capture_output=True)
+        os.replace(part, LIB)
 
 
 def _stale():
@@ -50,7 +52,11 @@ def lib():
     global _lib
     if _lib is None:
         if _stale():
-            build()
+            import fcntl
+            with open(LIB + ".lock", "w") as lk:  # one builder among parallel test processes
+                fcntl.flock(lk, fcntl.LOCK_EX)
+                if _stale():
+                    build()
         L = ctypes.CDLL(LIB)
         L.nq_emu_decode.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64,
                                     ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64,
@@ -190,8 +196,8 @@ def gemm_q8_1(fmt_id, w, N, K, xq, M, w_mis=0, max_rows=0, max_mrows=0, cus=0, w
     that many compute units with the workspace its plan asks for: K split,
     and the weight rewritten once per call for more than 64 activation rows;
     0: no workspace).  Returns (y float32 [M, N], bad reads, message,
-    guards_ok[, (K splits, rewritten once)]); bad reads is -1 for a format
-    without a span rewrite."""
+    guards_ok[, (K splits, rewritten once, 4-span K steps)]); bad reads is
+    -1 for a format without a span rewrite."""
     w = np.ascontiguousarray(w, dtype=np.uint8)
     wbuf, woff = _placed(w.size, 16, w_mis)
     wbuf[woff:woff + w.size] = w
@@ -206,7 +212,8 @@ def gemm_q8_1(fmt_id, w, N, K, xq, M, w_mis=0, max_rows=0, max_mrows=0, cus=0, w
     y = ybuf[16:16 + M * N].reshape(M, N).copy()
     guards = bool(np.all(np.isnan(ybuf[:16])) and np.all(np.isnan(ybuf[16 + M * N:])))
     if with_splits:
-        return y, rc, err.value.decode(), guards, (ns.value & 0xFFFF, bool(ns.value >> 16))
+        return y, rc, err.value.decode(), guards, (ns.value & 0xFFFF, bool(ns.value >> 16 & 1),
+                                                   bool(ns.value >> 17 & 1))
     return y, rc, err.value.decode(), guards
 
 

@@ -368,24 +368,36 @@ def _gemm_k(B):
     return 352 if B == 32 else 384 if B in (64, 128) else 768
 
 
+def _sp4_planned(N, M, cus):
+    """64-row tiles, at least three per compute unit: 4-span K steps."""
+    bm = 16 if M <= 16 else 32 if M <= 32 else 64
+    return cus > 0 and bm == 64 and -(-N // 128) * -(-M // bm) >= 3 * cus
+
+
 @pytest.mark.parametrize("fmt", GEMM_FMTS)
 def test_emu_gemm_matches_oracle(fmt):
+    """Every gguf format over ragged tiles and K steps, launch limits, both
+    K step lengths (cus = 1 plans 4-span steps for grids of three or more
+    64-row tiles), with and without the per-call rewrite."""
     idx, B, S, _ = oracle.info(fmt)
     K = _gemm_k(B)
     for N, M, w_mis, max_rows, max_mrows, cus in [(150, 9, 0, 0, 0, 0), (37, 70, 1, 0, 0, 0),
-                                                  (260, 65, 3, 128, 0, 256), (130, 100, 2, 0, 40, 256),
-                                                  (37, 1100, 1, 0, 500, 256), (140, 1030, 2, 128, 0, 256),
+                                                  (260, 65, 3, 128, 0, 256), (130, 100, 2, 0, 40, 1),
+                                                  (37, 1100, 1, 0, 500, 256), (140, 1030, 2, 128, 0, 1),
                                                   (60, 32, 1, 0, 0, 0), (200, 21, 3, 0, 0, 256),
-                                                  (140, 16, 2, 0, 0, 0), (37, 7, 1, 0, 0, 256)]:
+                                                  (140, 16, 2, 0, 0, 0), (37, 7, 1, 0, 0, 256),
+                                                  (300, 130, 1, 0, 0, 1)]:
         w = synth.payload(fmt, N * K // B, 7 + N, synth.binade(-6, -2, False))
         _, xq = oracle.quantize_q8_1(_act(M, K, M).astype(np.float32))
-        y, rc, msg, guards, (ns, once) = emu_lib.gemm_q8_1(idx, w, N, K, xq, M, w_mis=w_mis, max_rows=max_rows,
-                                                            max_mrows=max_mrows, cus=cus, with_splits=True)
+        y, rc, msg, guards, (ns, once, sp4) = emu_lib.gemm_q8_1(idx, w, N, K, xq, M, w_mis=w_mis,
+                                                                 max_rows=max_rows, max_mrows=max_mrows, cus=cus,
+                                                                 with_splits=True)
         assert rc == 0, msg
         assert guards
         assert once == (cus > 0 and M > 1024)
+        assert sp4 == _sp4_planned(N, M, cus)
         ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
-        linear_check(y, ref, env, K, f"{fmt} N={N} M={M} rewritten once={once}")
+        linear_check(y, ref, env, K, f"{fmt} N={N} M={M} rewritten once={once} 4-span steps={sp4}")
 
 
 def test_emu_gemm_tile_order_covers_every_tile():
@@ -413,12 +425,12 @@ def test_emu_gemm_split_k(fmt):
     for N, K, M, cus in [(200, 4096, 20, 64), (130, 2304, 70, 16)]:
         w = synth.payload(fmt, N * K // B, N + M, synth.binade(-6, -2, False))
         _, xq = oracle.quantize_q8_1(_act(M, K, 6).astype(np.float32))
-        y, rc, msg, guards, (ns, once) = emu_lib.gemm_q8_1(idx, w, N, K, xq, M, w_mis=1, cus=cus,
-                                                            with_splits=True)
+        y, rc, msg, guards, (ns, once, sp4) = emu_lib.gemm_q8_1(idx, w, N, K, xq, M, w_mis=1, cus=cus,
+                                                                 with_splits=True)
         assert rc == 0, msg
         assert guards
         assert ns >= 2
-        assert not once
+        assert not once and not sp4
         ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
         linear_check(y, ref, env, K, f"{fmt} N={N} K={K} M={M} splits={ns}")
 

@@ -286,6 +286,26 @@ def test_gemm_full_size_sampled_rows(fmt, N, K, M):
     assert np.all(np.isfinite(y))
 
 
+@pytest.mark.parametrize("fmt", GGUF)
+def test_gemm_four_span_k_steps(fmt):
+    """A grid of at least three 64-row tiles per compute unit (96 weight tiles
+    by 9 activation tiles, the last one 8 rows; K ragged against the 4-span
+    step where the block size allows) takes K steps of 128 values on a
+    256-compute-unit device: sampled
+    weight rows, every activation row, against the oracle."""
+    _, B, _, _ = oracle.info(fmt)
+    N, K, M = 12288, _gemm_k(B), 520
+    w = _weights(fmt, N, K, 93)
+    _, xq = oracle.quantize_q8_1(_act(M, K, 94).astype(np.float32))
+    announce(f"gemm 4-span steps {fmt} [{N}, {K}] x {M}")
+    y = _gemm(fmt, w, N, K, xq, w_off=1)
+    rows = np.unique(np.r_[0, 127, 128, N - 1, np.random.default_rng(K).integers(0, N, size=28)])
+    sub = w.reshape(N, -1)[rows].ravel()
+    ref, env = oracle.gemv_q8_1(fmt, sub, rows.size, K, xq, M)
+    linear_check(y[:, rows], ref, env, K, f"{fmt} 4-span steps")
+    assert np.all(np.isfinite(y))
+
+
 def test_gemm_metadata_errors():
     w = torch.zeros(34 * 4, dtype=torch.uint8, device="cuda:0")
     xq = torch.zeros(36 * 9, dtype=torch.uint8, device="cuda:0")
@@ -337,24 +357,29 @@ def test_gemm_more_activation_rows_than_one_launch_takes():
     assert np.all(np.isfinite(y))
 
 
+@pytest.mark.parametrize("N", [300, 6144])
 @pytest.mark.parametrize("fmt", ["gguf:q4_k", "gguf:q2_k", "gguf:iq2_s", "gguf:q8_0", "gguf:tq1_0", "gguf:q5_1"])
-def test_gemm_weight_rewritten_once_is_the_same_product(fmt):
+def test_gemm_weight_rewritten_once_is_the_same_product(fmt, N):
     """Above 1024 activation rows the weight is rewritten once per call into
     the workspace; the tiles then copy the same codes and scales they would
     rewrite themselves, so the bits equal the workspace-free product's (K below
-    8 steps: no K split)."""
-    _, B, _, _ = oracle.info(fmt)
-    N, K, M = 300, 1024, 1100
+    8 steps: no K split; 6144 weight rows make 864 tiles: 128-value K steps
+    on 256 compute units, either way).  All rows (300) or sampled rows (6144)
+    against the oracle."""
+    K, M = 1024, 1100
     st, ws_bytes = nq.gemm_q8_1_workspace(fmt, N, K, M)
     assert st == 0 and ws_bytes >= N * K
     w = _weights(fmt, N, K, 61)
     _, xq = oracle.quantize_q8_1(_act(M, K, 62).astype(np.float32))
-    announce(f"gemm rewrite once {fmt}")
+    announce(f"gemm rewrite once {fmt} N={N}")
     a = _gemm(fmt, w, N, K, xq, w_off=1, split=True)
     b = _gemm(fmt, w, N, K, xq, w_off=1, split=False)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
-    ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
-    linear_check(a, ref, env, K, fmt)
+    rows = np.arange(N) if N <= 300 else np.unique(np.r_[0, 127, 128, N - 1,
+                                                         np.random.default_rng(N).integers(0, N, size=28)])
+    sub = w.reshape(N, -1)[rows].ravel()
+    ref, env = oracle.gemv_q8_1(fmt, sub, rows.size, K, xq, M)
+    linear_check(a[:, rows], ref, env, K, f"{fmt} N={N}")
 
 
 @pytest.mark.parametrize("M", [3, 70])
