@@ -388,10 +388,11 @@ def gemv_q8_1(fmt, weight, N, K, xq, out=None, stream=None):
 
 
 def gemm_q8_1(fmt, weight, N, K, xq, out=None, stream=None, split=True):
-    """As gemv_q8_1 for any number of activation rows M >= 1 (more than 8 on
+    """As gemv_q8_1 for any number of activation rows M >= 1 (5 or more on
     the matrix cores).  With split=True the workspace the product may use is
-    allocated from torch on `stream` (K then splits where the shape asks for
-    it); split=False runs unsplit."""
+    allocated from torch on `stream` (K then splits, and the weight is
+    rewritten once, where the shape asks for it); split=False runs without a
+    workspace."""
     import torch
     fid = fmt if isinstance(fmt, int) else format_query(fmt).id
     M = xq.numel() // (K // 32 * 36) if K % 32 == 0 and K > 0 else 0

@@ -60,7 +60,10 @@ constexpr uint32_t GM_SP = 8;              // spans per K step (256 values; 4 on
 constexpr uint32_t GM_SP4_TILES_PER_CU = NQ_GM_SP4_TILES;
 constexpr uint64_t GM_MAX_MROWS = 1ull << 16;  // activation rows per launch
 constexpr uint64_t GM_MIN_M = 5;  // fewer activation rows take the single-row kernel (faster there)
-constexpr uint64_t GM_REWRITE_ONCE_M = 1024;   // more activation rows: the weight is rewritten once per call
+#ifndef NQ_GM_REWRITE_M
+#define NQ_GM_REWRITE_M 256
+#endif
+constexpr uint64_t GM_REWRITE_ONCE_M = NQ_GM_REWRITE_M;  // more activation rows: the weight is rewritten once per call
 
 // one scale per 16 values
 NQ_HD constexpr bool gm_u16(int f) {
@@ -678,12 +681,12 @@ __global__ __launch_bounds__(WG) void k_gemm_sum(const float *part, float *y, ui
 // K is long (8 steps or more), K is cut into nsplit ranges of sps steps (at
 // least 4 each) so that about two workgroups per compute unit run; the
 // partial outputs (nsplit * M * N binary32 values, at most 2 GiB) go to the
-// workspace and are summed in split order.  (2) With more than 1024
-// activation rows (17 or more activation tiles per weight tile) the weight
-// is rewritten once into the workspace (codes, scales, offsets) and the
-// tiles copy it, instead of each tile rewriting it (measured +2 to +11% at
-// 2048 rows, a loss at 512 and below: the copy is about twice the packed
-// bytes).  The results are the same bits either way for (2).  (3) With
+// workspace and are summed in split order.  (2) With more than 256
+// activation rows (5 or more activation tiles per weight tile) the weight is
+// rewritten once into the workspace (codes, scales, offsets) and the tiles
+// copy it, instead of each tile rewriting it (measured up to +23% from 384
+// rows, 1 to 15% slower at 144 to 256 rows: the copy is about twice the
+// packed bytes).  The results are the same bits either way for (2).  (3) With
 // 64-row tiles, at least three per compute unit, K steps hold 4 spans
 // instead of 8 (measured 5-23% faster there, up to 45% slower at two tiles
 // per compute unit).  The plan depends only on N, K, M and the compute-unit

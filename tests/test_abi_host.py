@@ -298,7 +298,7 @@ def test_gemm_rejects_before_device():
 
 def test_gemm_workspace_sizes():
     """The workspace holds the K-split partials (5 rows or more, few tiles,
-    long K; no GPU: 256 compute units assumed) and, above 1024 activation rows,
+    long K; no GPU: 256 compute units assumed) and, above 256 activation rows,
     the weight rewritten once: N K code bytes, then K / 32 * NH * N binary32
     scales and, for the affine formats, as many offsets (each part rounded
     up to 256 bytes)."""
@@ -314,9 +314,11 @@ def test_gemm_workspace_sizes():
     # q6_k: two scales per span, no offsets
     assert nq.gemm_q8_1_workspace("gguf:q6_k", 14336, 4096, 2048) == (0, 58720256 + 2 * 7340032)
     assert nq.gemm_q8_1_workspace("gguf:q8_0", 14336, 4096, 2048) == (0, 58720256 + 7340032)
-    # 256 tiles: two K splits (2 * 512 * 4096 binary32), no rewrite at 512 rows
-    assert nq.gemm_q8_1_workspace("gguf:q8_0", 4096, 14336, 512) == (0, 16777216)
-    assert nq.gemm_q8_1_workspace("gguf:q8_0", 14336, 4096, 1024) == (0, 0)
-    assert nq.gemm_q8_1_workspace("gguf:q8_0", 14336, 4096, 1025) == (0, 58720256 + 7340032)
+    # 256 tiles: two K splits (2 * 512 * 4096 binary32), then the rewrite (4096 * 14336 code bytes,
+    # 448 * 4096 scales)
+    assert nq.gemm_q8_1_workspace("gguf:q8_0", 4096, 14336, 512) == (0, 16777216 + 58720256 + 7340032)
+    # 4 K steps: no split; the rewrite from 257 rows (14336 * 1024 code bytes, 32 * 14336 scales)
+    assert nq.gemm_q8_1_workspace("gguf:q8_0", 14336, 1024, 256) == (0, 0)
+    assert nq.gemm_q8_1_workspace("gguf:q8_0", 14336, 1024, 257) == (0, 14680064 + 1835008)
     assert nq.gemm_q8_1_workspace("nvfp4", 1, 64, 9)[0] == 2
     assert nq.gemm_q8_1_workspace("gguf:q4_k", 1, 100, 9)[0] == 5

@@ -394,7 +394,7 @@ def test_emu_gemm_matches_oracle(fmt):
                                                                  with_splits=True)
         assert rc == 0, msg
         assert guards
-        assert once == (cus > 0 and M > 1024)
+        assert once == (cus > 0 and M > 256)
         assert sp4 == _sp4_planned(N, M, cus)
         ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
         linear_check(y, ref, env, K, f"{fmt} N={N} M={M} rewritten once={once} 4-span steps={sp4}")

@@ -360,7 +360,7 @@ def test_gemm_more_activation_rows_than_one_launch_takes():
 @pytest.mark.parametrize("N", [300, 6144])
 @pytest.mark.parametrize("fmt", ["gguf:q4_k", "gguf:q2_k", "gguf:iq2_s", "gguf:q8_0", "gguf:tq1_0", "gguf:q5_1"])
 def test_gemm_weight_rewritten_once_is_the_same_product(fmt, N):
-    """Above 1024 activation rows the weight is rewritten once per call into
+    """Above 256 activation rows the weight is rewritten once per call into
     the workspace; the tiles then copy the same codes and scales they would
     rewrite themselves, so the bits equal the workspace-free product's (K below
     8 steps: no K split; 6144 weight rows make 864 tiles: 128-value K steps
