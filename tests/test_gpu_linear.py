@@ -291,14 +291,17 @@ def test_gemm_four_span_k_steps(fmt):
     """A grid of at least three 64-row tiles per compute unit (96 weight tiles
     by 9 activation tiles, the last one 8 rows; K ragged against the 4-span
     step where the block size allows) takes K steps of 128 values on a
-    256-compute-unit device: sampled
-    weight rows, every activation row, against the oracle."""
+    256-compute-unit device, with the weight rewritten once (workspace) or
+    per tile (none): the same bits both ways, and sampled weight rows,
+    every activation row, against the oracle."""
     _, B, _, _ = oracle.info(fmt)
     N, K, M = 12288, _gemm_k(B), 520
     w = _weights(fmt, N, K, 93)
     _, xq = oracle.quantize_q8_1(_act(M, K, 94).astype(np.float32))
     announce(f"gemm 4-span steps {fmt} [{N}, {K}] x {M}")
-    y = _gemm(fmt, w, N, K, xq, w_off=1)
+    y = _gemm(fmt, w, N, K, xq, w_off=1, split=True)
+    y2 = _gemm(fmt, w, N, K, xq, w_off=1, split=False)
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
     rows = np.unique(np.r_[0, 127, 128, N - 1, np.random.default_rng(K).integers(0, N, size=28)])
     sub = w.reshape(N, -1)[rows].ravel()
     ref, env = oracle.gemv_q8_1(fmt, sub, rows.size, K, xq, M)
