@@ -578,8 +578,14 @@ NQ_HD void gm_store(const GmArgs &a, uint32_t n0, uint32_t m0, uint32_t ks, uint
 
 typedef int gm_i32x4 __attribute__((ext_vector_type(4)));
 
+// With 128-value K steps the LDS of four workgroups fits a compute unit;
+// asking for four waves per SIMD keeps the kernels with a few more than 128
+// VGPRs (q2_k, iq2_s, nvfp4) at that occupancy, at the cost of a few
+// spilled registers (measured +3 to +16% for those three at 512 and 2048
+// activation rows, the others unchanged).
+
 template <int F, int NI, int MJ, int SP>
-__global__ __launch_bounds__(WG) void k_gemm(GmArgs a) {
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(SP == 4 ? 4 : 1))) void k_gemm(GmArgs a) {
     using Sh = GmShape<NI, MJ>;
     using G = GmFmt<F, Sh::BM, SP>;
     using TS = TabSpec<F>;
