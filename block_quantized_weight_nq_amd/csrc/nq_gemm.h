@@ -685,7 +685,8 @@ __global__ __launch_bounds__(WG) void k_gemm_sum(const float *part, float *y, ui
 
 // Plan of a call: (1) when the tiles are fewer than two per compute unit and
 // K is long (8 steps or more), K is cut into nsplit ranges of sps steps (at
-// least 4 each) so that about two workgroups per compute unit run; the
+// least 4 each) so that about two workgroups per compute unit run (three
+// with 64-row tiles, (3)); the
 // partial outputs (nsplit * M * N binary32 values, at most 2 GiB) go to the
 // workspace and are summed in split order.  (2) With more than 256
 // activation rows (5 or more activation tiles per weight tile) the weight is
@@ -695,36 +696,41 @@ __global__ __launch_bounds__(WG) void k_gemm_sum(const float *part, float *y, ui
 // packed bytes).  The results are the same bits either way for (2).  (3) With
 // 64-row tiles, at least three per compute unit, K steps hold 4 spans
 // instead of 8 (measured 5-23% faster there, up to 45% slower at two tiles
-// per compute unit).  The plan depends only on N, K, M and the compute-unit
-// count.
+// per compute unit); with one to two such tiles per compute unit, K is split
+// for three workgroups per compute unit, also in 4-span steps (measured up
+// to +27%).  The plan depends only on N, K, M and the compute-unit count.
 struct GmPlan {
     uint32_t nsplit, sps;
     bool rewrite_once;  // the weight rewritten once per call (into the workspace)
     uint32_t sp;        // spans per K step (4 or 8)
 };
 
-// The plan without a workspace: no K split, the weight rewritten per tile.
+// The plan without a workspace: no K split (and then 8-span steps where the
+// 4-span ones came with a split), the weight rewritten per tile.
 inline GmPlan gm_plan_plain(const GmPlan &p, uint64_t K) {
-    return GmPlan{1u, (uint32_t)((K / 32 + p.sp - 1) / p.sp), false, p.sp};
+    const uint32_t sp = p.nsplit > 1 ? GM_SP : p.sp;
+    return GmPlan{1u, (uint32_t)((K / 32 + sp - 1) / sp), false, sp};
 }
 
 inline GmPlan gm_plan(uint64_t N, uint64_t K, uint64_t M, uint32_t cus) {
     const uint64_t bm = gm_bm(M), tiles = (N + GM_BN - 1) / GM_BN * ((M + bm - 1) / bm);
     const uint64_t c = cus ? cus : 1u;
-    const uint32_t sp = bm == 64u && tiles >= GM_SP4_TILES_PER_CU * c ? 4u : GM_SP;
-    const uint64_t steps = (K / 32 + sp - 1) / sp;
-    const uint64_t target = 2ull * c;
-    GmPlan p{1u, (uint32_t)steps, M > GM_REWRITE_ONCE_M, sp};
-    if (tiles >= target || steps < 8) return p;
+    const uint32_t sp0 = bm == 64u && tiles >= GM_SP4_TILES_PER_CU * c ? 4u : GM_SP;
+    const GmPlan p{1u, (uint32_t)((K / 32 + sp0 - 1) / sp0), M > GM_REWRITE_ONCE_M, sp0};
+    if (tiles >= 2ull * c) return p;
+    // K split; with 64-row tiles, one or two per compute unit, into 4-span
+    // steps and enough ranges for three workgroups per compute unit
+    const bool mid = bm == 64u && tiles >= c;
+    const uint32_t sp = mid ? 4u : GM_SP;
+    const uint64_t steps = (K / 32 + sp - 1) / sp, target = (mid ? 3ull : 2ull) * c;
+    if (steps < 8) return p;
     uint64_t S = (target + tiles - 1) / tiles;
     if (S > steps / 4) S = steps / 4;
     if (S < 2) return p;
     const uint64_t sps = (steps + S - 1) / S;
     S = (steps + sps - 1) / sps;
     if (S < 2 || S * M * N * 4 > (1ull << 31)) return p;
-    p.nsplit = (uint32_t)S;
-    p.sps = (uint32_t)sps;
-    return p;
+    return GmPlan{(uint32_t)S, (uint32_t)sps, p.rewrite_once, sp};
 }
 
 // Workspace layout: the split partials (nsplit * M * N binary32), then the

@@ -314,11 +314,13 @@ def test_gemm_workspace_sizes():
     # q6_k: two scales per span, no offsets
     assert nq.gemm_q8_1_workspace("gguf:q6_k", 14336, 4096, 2048) == (0, 58720256 + 2 * 7340032)
     assert nq.gemm_q8_1_workspace("gguf:q8_0", 14336, 4096, 2048) == (0, 58720256 + 7340032)
-    # 256 tiles: two K splits (2 * 512 * 4096 binary32), then the rewrite (4096 * 14336 code bytes,
-    # 448 * 4096 scales)
-    assert nq.gemm_q8_1_workspace("gguf:q8_0", 4096, 14336, 512) == (0, 16777216 + 58720256 + 7340032)
-    # 4 K steps: no split; the rewrite from 257 rows (14336 * 1024 code bytes, 32 * 14336 scales)
-    assert nq.gemm_q8_1_workspace("gguf:q8_0", 14336, 1024, 256) == (0, 0)
-    assert nq.gemm_q8_1_workspace("gguf:q8_0", 14336, 1024, 257) == (0, 14680064 + 1835008)
+    # 256 tiles, one per compute unit: three K splits (3 * 512 * 4096 binary32), then the rewrite
+    # (4096 * 14336 code bytes, 448 * 4096 scales)
+    assert nq.gemm_q8_1_workspace("gguf:q8_0", 4096, 14336, 512) == (0, 25165824 + 58720256 + 7340032)
+    # 448 tiles (one to two per compute unit): two K splits in 4-span steps (2 * 256 * 14336 binary32)
+    assert nq.gemm_q8_1_workspace("gguf:q8_0", 14336, 1024, 256) == (0, 29360128)
+    # 1024 and 1280 tiles: no split; the rewrite from 257 rows (32768 * 1024 code bytes, 32 * 32768 scales)
+    assert nq.gemm_q8_1_workspace("gguf:q8_0", 32768, 1024, 256) == (0, 0)
+    assert nq.gemm_q8_1_workspace("gguf:q8_0", 32768, 1024, 257) == (0, 33554432 + 4194304)
     assert nq.gemm_q8_1_workspace("nvfp4", 1, 64, 9)[0] == 2
     assert nq.gemm_q8_1_workspace("gguf:q4_k", 1, 100, 9)[0] == 5

@@ -368,10 +368,12 @@ def _gemm_k(B):
     return 352 if B == 32 else 384 if B in (64, 128) else 768
 
 
-def _sp4_planned(N, M, cus):
-    """64-row tiles, at least three per compute unit: 4-span K steps."""
+def _sp4_planned(N, M, cus, nsplit):
+    """4-span K steps: 64-row tiles, at least three per compute unit, or one
+    to two per compute unit with K split."""
     bm = 16 if M <= 16 else 32 if M <= 32 else 64
-    return cus > 0 and bm == 64 and -(-N // 128) * -(-M // bm) >= 3 * cus
+    tiles = -(-N // 128) * -(-M // bm)
+    return cus > 0 and bm == 64 and (tiles >= 3 * cus or (cus <= tiles < 2 * cus and nsplit >= 2))
 
 
 @pytest.mark.parametrize("fmt", GEMM_FMTS)
@@ -395,7 +397,7 @@ def test_emu_gemm_matches_oracle(fmt):
         assert rc == 0, msg
         assert guards
         assert once == (cus > 0 and M > 256)
-        assert sp4 == _sp4_planned(N, M, cus)
+        assert sp4 == _sp4_planned(N, M, cus, ns)
         ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
         linear_check(y, ref, env, K, f"{fmt} N={N} M={M} rewritten once={once} 4-span steps={sp4}")
 
@@ -420,9 +422,11 @@ def test_emu_gemm_tile_order_covers_every_tile():
 @pytest.mark.parametrize("fmt", ["gguf:q4_k", "gguf:q8_0", "gguf:q6_k", "gguf:q2_k", "gguf:iq2_xs", "gguf:q4_1"])
 def test_emu_gemm_split_k(fmt):
     """K split over workgroups (planned for a small device), partials summed in
-    split order: the criterion holds; every tile and split is met once."""
+    split order: the criterion holds; every tile and split is met once.  The
+    last shape has one to two 64-row tiles per compute unit (9 on 8): three
+    splits in 4-span K steps."""
     idx, B, S, _ = oracle.info(fmt)
-    for N, K, M, cus in [(200, 4096, 20, 64), (130, 2304, 70, 16)]:
+    for N, K, M, cus in [(200, 4096, 20, 64), (130, 2304, 70, 16), (300, 2304, 130, 8)]:
         w = synth.payload(fmt, N * K // B, N + M, synth.binade(-6, -2, False))
         _, xq = oracle.quantize_q8_1(_act(M, K, 6).astype(np.float32))
         y, rc, msg, guards, (ns, once, sp4) = emu_lib.gemm_q8_1(idx, w, N, K, xq, M, w_mis=1, cus=cus,
@@ -430,7 +434,7 @@ def test_emu_gemm_split_k(fmt):
         assert rc == 0, msg
         assert guards
         assert ns >= 2
-        assert not once and not sp4
+        assert not once and sp4 == (cus == 8)
         ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
         linear_check(y, ref, env, K, f"{fmt} N={N} K={K} M={M} splits={ns}")
 
