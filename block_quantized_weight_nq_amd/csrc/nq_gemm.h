@@ -686,7 +686,7 @@ __global__ __launch_bounds__(WG) void k_gemm_sum(const float *part, float *y, ui
 // Plan of a call: (1) when the tiles are fewer than two per compute unit and
 // K is long (8 steps or more), K is cut into nsplit ranges of sps steps (at
 // least 4 each) so that about two workgroups per compute unit run (three
-// with 64-row tiles, (3)); the
+// with enough 64-row tiles, (3)); the
 // partial outputs (nsplit * M * N binary32 values, at most 2 GiB) go to the
 // workspace and are summed in split order.  (2) With more than 256
 // activation rows (5 or more activation tiles per weight tile) the weight is
@@ -696,9 +696,10 @@ __global__ __launch_bounds__(WG) void k_gemm_sum(const float *part, float *y, ui
 // packed bytes).  The results are the same bits either way for (2).  (3) With
 // 64-row tiles, at least three per compute unit, K steps hold 4 spans
 // instead of 8 (measured 5-23% faster there, up to 45% slower at two tiles
-// per compute unit); with one to two such tiles per compute unit, K is split
-// for three workgroups per compute unit, also in 4-span steps (measured up
-// to +27%).  The plan depends only on N, K, M and the compute-unit count.
+// per compute unit); with five eighths to two such tiles per compute unit,
+// K is split for three workgroups per compute unit, also in 4-span steps
+// (measured up to +46%; at half a tile per compute unit and below it lost
+// up to 32%).  The plan depends only on N, K, M and the compute-unit count.
 struct GmPlan {
     uint32_t nsplit, sps;
     bool rewrite_once;  // the weight rewritten once per call (into the workspace)
@@ -718,9 +719,9 @@ inline GmPlan gm_plan(uint64_t N, uint64_t K, uint64_t M, uint32_t cus) {
     const uint32_t sp0 = bm == 64u && tiles >= GM_SP4_TILES_PER_CU * c ? 4u : GM_SP;
     const GmPlan p{1u, (uint32_t)((K / 32 + sp0 - 1) / sp0), M > GM_REWRITE_ONCE_M, sp0};
     if (tiles >= 2ull * c) return p;
-    // K split; with 64-row tiles, one or two per compute unit, into 4-span
-    // steps and enough ranges for three workgroups per compute unit
-    const bool mid = bm == 64u && tiles >= c;
+    // K split; with 64-row tiles, five eighths to two per compute unit, into
+    // 4-span steps and enough ranges for three workgroups per compute unit
+    const bool mid = bm == 64u && 8u * tiles >= 5u * c;
     const uint32_t sp = mid ? 4u : GM_SP;
     const uint64_t steps = (K / 32 + sp - 1) / sp, target = (mid ? 3ull : 2ull) * c;
     if (steps < 8) return p;

@@ -317,7 +317,7 @@ def test_gemm_workspace_sizes():
     # 256 tiles, one per compute unit: three K splits (3 * 512 * 4096 binary32), then the rewrite
     # (4096 * 14336 code bytes, 448 * 4096 scales)
     assert nq.gemm_q8_1_workspace("gguf:q8_0", 4096, 14336, 512) == (0, 25165824 + 58720256 + 7340032)
-    # 448 tiles (one to two per compute unit): two K splits in 4-span steps (2 * 256 * 14336 binary32)
+    # 448 tiles (under two per compute unit): two K splits in 4-span steps (2 * 256 * 14336 binary32)
     assert nq.gemm_q8_1_workspace("gguf:q8_0", 14336, 1024, 256) == (0, 29360128)
     # 1024 and 1280 tiles: no split; the rewrite from 257 rows (32768 * 1024 code bytes, 32 * 32768 scales)
     assert nq.gemm_q8_1_workspace("gguf:q8_0", 32768, 1024, 256) == (0, 0)
