@@ -29,11 +29,12 @@
 //
 // Tiling.  A workgroup (4 waves) owns a tile of 128 weight rows by 64
 // activation rows and walks K in steps of 256 values (128 on grids of at
-// least three 64-row tiles per compute unit: half the LDS, so more
+// least three 64-row tiles per compute unit, and with K split over five
+// eighths to two such tiles per compute unit: half the LDS, so more
 // workgroups share a compute unit and hide each other's staging): its
-// threads rewrite the
-// step's weight spans into LDS (codes, scales, offsets) and copy the
-// activation codes, scales and d * S terms next to them; then each wave
+// threads rewrite the step's weight spans into LDS (codes, scales, offsets)
+// and copy the activation codes, scales and d * S terms next to them; then
+// each wave
 // computes a 64 x 32 sub-tile, span by span, in a fixed order, so every run
 // of a launch shape gives the same bits.  Tiles that share weight rows are
 // given to workgroups of one XCD (workgroups go to the 8 XCDs in turn), so
