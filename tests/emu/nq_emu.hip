@@ -602,6 +602,24 @@ extern "C" __attribute__((visibility("default"))) long nq_emu_gemm_q8_1(int fmt,
     return nq_emu_gemm_table[fmt](w, N, K, xq, M, y, max_rows, max_mrows, cus, nsplit, err, errlen);
 }
 
+// The batched product's plan on a device of `cus` compute units, as the
+// launcher makes it: out = {K splits, steps per split, spans per step,
+// weight rewritten once, tile height, workspace bytes, and the plan without
+// a workspace: K splits, steps per split, spans per step}.
+extern "C" __attribute__((visibility("default"))) void nq_emu_gemm_plan(int fmt, uint64_t N, uint64_t K, uint64_t M,
+                                                                       uint32_t cus, uint64_t *out) {
+    const nq::GmPlan p = nq::gm_plan(N, K, M, cus), q = nq::gm_plan_plain(p, K);
+    out[0] = p.nsplit;
+    out[1] = p.sps;
+    out[2] = p.sp;
+    out[3] = p.rewrite_once ? 1u : 0u;
+    out[4] = nq::gm_bm(M);
+    out[5] = nq::gm_ws_layout(fmt, p, N, K, M).total;
+    out[6] = q.nsplit;
+    out[7] = q.sps;
+    out[8] = q.sp;
+}
+
 // Product with q8_1 activations through the kernel's lane code; returns
 // out-of-payload weight reads (0 on success), or -1 for a format without one.
 extern "C" __attribute__((visibility("default"))) long nq_emu_gemv_q8_1(int fmt, const uint8_t *w, uint64_t N,

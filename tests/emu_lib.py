@@ -84,6 +84,9 @@ def lib():
                                        ctypes.c_uint64, ctypes.c_uint32, ctypes.POINTER(ctypes.c_uint32),
                                        ctypes.c_char_p, ctypes.c_int]
         L.nq_emu_gemm_q8_1.restype = ctypes.c_long
+        L.nq_emu_gemm_plan.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
+                                       ctypes.c_uint32, ctypes.c_void_p]
+        L.nq_emu_gemm_plan.restype = None
         L.nq_emu_quantize_q8_1.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_uint64, ctypes.c_char_p, ctypes.c_int]
         L.nq_emu_quantize_q8_1.restype = ctypes.c_long
@@ -215,6 +218,17 @@ def gemm_q8_1(fmt_id, w, N, K, xq, M, w_mis=0, max_rows=0, max_mrows=0, cus=0, w
         return y, rc, err.value.decode(), guards, (ns.value & 0xFFFF, bool(ns.value >> 16 & 1),
                                                    bool(ns.value >> 17 & 1))
     return y, rc, err.value.decode(), guards
+
+
+def gemm_plan(fmt_id, N, K, M, cus):
+    """The batched product's plan on `cus` compute units: a dict of nsplit,
+    sps (steps per split), sp (spans per step), once (weight rewritten once),
+    bm (tile height), ws (workspace bytes) and, without a workspace, the
+    plain plan's nsplit, sps and sp (plain_*)."""
+    out = np.zeros(9, dtype=np.uint64)
+    lib().nq_emu_gemm_plan(fmt_id, N, K, M, cus, out.ctypes.data)
+    keys = ["nsplit", "sps", "sp", "once", "bm", "ws", "plain_nsplit", "plain_sps", "plain_sp"]
+    return {k: int(v) for k, v in zip(keys, out)}
 
 
 def quantize_q8_1(x, in_code, x_mis=0, chunk=0):

@@ -440,6 +440,52 @@ def test_emu_gemm_split_k(fmt):
         linear_check(y, ref, env, K, f"{fmt} N={N} K={K} M={M} splits={ns}")
 
 
+def _up(x):
+    return -(-x // 256) * 256
+
+
+@pytest.mark.parametrize("fmt", ["gguf:q4_k", "gguf:q6_k", "gguf:q8_0"])
+def test_emu_gemm_plan_invariants(fmt):
+    """The batched product's plan on 256 compute units at Llama-3-8B shapes:
+    the tile height follows M; the K splits cover K with none empty (at least
+    4 steps each, partials at most 2 GiB, only below two tiles per compute
+    unit); 4-span steps only with 64-row tiles; the weight rewritten once
+    exactly above 256 rows; the workspace is the partials plus the rewritten
+    codes, scales and (q4_k) offsets, each rounded up to 256 bytes; without
+    a workspace the plan is unsplit, in 8-span steps where 4-span ones came
+    with a split."""
+    idx = oracle.info(fmt)[0]
+    nh, aff = (2, False) if fmt == "gguf:q6_k" else (1, fmt == "gguf:q4_k")
+    for N, K in [(4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336), (128256, 4096), (300, 1024)]:
+        for M in [5, 16, 17, 32, 33, 64, 65, 128, 192, 256, 257, 384, 512, 768, 1024, 2048, 4096]:
+            p = emu_lib.gemm_plan(idx, N, K, M, 256)
+            bm = 16 if M <= 16 else 32 if M <= 32 else 64
+            assert p["bm"] == bm
+            tiles = -(-N // 128) * -(-M // bm)
+            steps = -(-(K // 32) // p["sp"])
+            assert p["sp"] in (4, 8) and (p["sp"] == 4) <= (bm == 64)
+            assert p["nsplit"] * p["sps"] >= steps and (p["nsplit"] - 1) * p["sps"] < steps
+            if p["nsplit"] > 1:
+                assert tiles < 512 and p["sps"] >= 4 and p["nsplit"] * M * N * 4 <= 1 << 31
+            else:
+                assert p["sps"] == steps
+                assert (p["sp"] == 4) == (bm == 64 and tiles >= 768)
+            assert p["once"] == (M > 256)
+            ws = _up(p["nsplit"] * M * N * 4) if p["nsplit"] > 1 else 0
+            if p["once"]:
+                ws += _up(N * K) + _up(K // 32 * nh * N * 4) * (2 if aff else 1)
+            assert p["ws"] == ws, (N, K, M)
+            assert p["plain_nsplit"] == 1 and p["plain_sp"] == (p["sp"] if p["nsplit"] == 1 else 8)
+            assert p["plain_sps"] == -(-(K // 32) // p["plain_sp"])
+    # plans the measurements quote
+    plan = lambda N, K, M: (lambda p: (p["nsplit"], p["sp"], p["bm"]))(emu_lib.gemm_plan(idx, N, K, M, 256))
+    assert plan(14336, 4096, 512) == (1, 4, 64)     # 896 tiles
+    assert plan(4096, 14336, 512) == (3, 4, 64)     # 256 tiles: three splits in 4-span steps
+    assert plan(4096, 14336, 384) == (4, 4, 64)     # 192 tiles
+    assert plan(4096, 14336, 64) == (14, 8, 64)     # 32 tiles, 56 steps
+    assert plan(14336, 4096, 16) == (4, 8, 16)      # 112 tiles of 16 rows
+
+
 @pytest.mark.parametrize("M", [3, 70])
 def test_emu_products_over_non_finite_scales(M):
     """Rows with an infinite or NaN weight scale give non-finite outputs on
