@@ -449,7 +449,8 @@ def test_emu_gemm_plan_invariants(fmt):
     """The batched product's plan on 256 compute units at Llama-3-8B shapes:
     the tile height follows M; the K splits cover K with none empty (at least
     4 steps each, partials at most 2 GiB, only below two tiles per compute
-    unit); 4-span steps only with 64-row tiles; the weight rewritten once
+    unit; 64-row tiles in 8-span steps within 512 workgroups); 4-span steps
+    only with 64-row tiles; the weight rewritten once
     exactly above 256 rows; the workspace is the partials plus the rewritten
     codes, scales and (q4_k) offsets, each rounded up to 256 bytes; without
     a workspace the plan is unsplit, in 8-span steps where 4-span ones came
@@ -467,6 +468,8 @@ def test_emu_gemm_plan_invariants(fmt):
             assert p["nsplit"] * p["sps"] >= steps and (p["nsplit"] - 1) * p["sps"] < steps
             if p["nsplit"] > 1:
                 assert tiles < 512 and p["sps"] >= 4 and p["nsplit"] * M * N * 4 <= 1 << 31
+                if bm == 64 and p["sp"] == 8:
+                    assert tiles * p["nsplit"] <= 512  # one pass of two workgroups per compute unit
             else:
                 assert p["sps"] == steps
                 assert (p["sp"] == 4) == (bm == 64 and tiles >= 768)
@@ -484,6 +487,7 @@ def test_emu_gemm_plan_invariants(fmt):
     assert plan(4096, 14336, 384) == (4, 4, 64)     # 192 tiles
     assert plan(4096, 14336, 64) == (14, 8, 64)     # 32 tiles, 56 steps
     assert plan(14336, 4096, 16) == (4, 8, 16)      # 112 tiles of 16 rows
+    assert plan(1024, 4096, 1100) == (3, 8, 64)     # 144 tiles: 3 splits (432 workgroups), not 4 (576)
 
 
 @pytest.mark.parametrize("M", [3, 70])

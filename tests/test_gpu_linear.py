@@ -322,14 +322,16 @@ def test_gemm_metadata_errors():
 
 @pytest.mark.parametrize("fmt,N,K,M", [("gguf:q4_k", 4096, 14336, 64), ("gguf:q6_k", 1000, 8192, 20),
                                        ("gguf:q4_1", 500, 4096, 100), ("gguf:q2_k", 4096, 14336, 512),
-                                       ("gguf:iq2_s", 12288, 1024, 200), ("gguf:q6_k", 4096, 14336, 384)])
+                                       ("gguf:iq2_s", 12288, 1024, 200), ("gguf:q6_k", 4096, 14336, 384),
+                                       ("gguf:q8_0", 1024, 4096, 1100)])
 def test_gemm_split_k(fmt, N, K, M):
     """Shapes with few tiles and long K split K over workgroups (a workspace
     is given): split and unsplit products both meet the criterion on sampled
     rows, and each repeats bit for bit.  The last three have five eighths to
     two 64-row tiles per compute unit on 256 compute units (256, 384 and 192):
     K split in 4-span steps (with the weight rewritten once too above 256
-    activation rows)."""
+    activation rows); [1024, 4096] x 1100 has 144 tiles: 3 splits in 8-span
+    steps, the count rounded down to stay within 512 workgroups."""
     st, ws_bytes = nq.gemm_q8_1_workspace(fmt, N, K, M)
     assert st == 0 and ws_bytes > 0
     w = _weights(fmt, N, K, 55)
