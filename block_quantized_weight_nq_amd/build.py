@@ -67,7 +67,7 @@ def build(jobs=None, verbose=False, out=LIB, defines=()):
 
     `defines` are extra -D macros (the tuning knobs NQ_UPT, NQ_RESIDENT_PER_CU,
     NQ_NT_STORE, NQ_NTL of csrc/nq_kernel.h, NQ_F8_NB of csrc/nq_fp8row.h and
-    NQ_GM_SP4_TILES of csrc/nq_gemm.h);
+    NQ_GM_REWRITE_M of csrc/nq_gemm.h);
     a non-default `out` builds elsewhere.
     """
     build_dir = BUILD if out == LIB else out + ".build"

@@ -28,8 +28,8 @@
 // has a rewrite.
 //
 // Tiling.  A workgroup (4 waves) owns a tile of 128 weight rows by 64
-// activation rows and walks K in steps of 256 values (128 on grids of at
-// least three 64-row tiles per compute unit, and with K split over five
+// activation rows and walks K in steps of 256 values (128 on grids of more
+// than two 64-row tiles per compute unit, and with K split over five
 // eighths to two such tiles per compute unit: half the LDS, so more
 // workgroups share a compute unit and hide each other's staging): its
 // threads rewrite the step's weight spans into LDS (codes, scales, offsets)
@@ -54,11 +54,6 @@ namespace nq {
 constexpr uint32_t GM_BN = 128;            // weight rows per tile
 constexpr uint32_t GM_BM = 64;             // activation rows per tile (32 for batches of at most 32 rows)
 constexpr uint32_t GM_SP = 8;              // spans per K step (256 values; 4 on large grids, gm_plan)
-#ifndef NQ_GM_SP4_TILES
-#define NQ_GM_SP4_TILES 3
-#endif
-// 64-row tiles per compute unit from which K steps hold 4 spans
-constexpr uint32_t GM_SP4_TILES_PER_CU = NQ_GM_SP4_TILES;
 constexpr uint64_t GM_MAX_MROWS = 1ull << 16;  // activation rows per launch
 constexpr uint64_t GM_MIN_M = 5;  // fewer activation rows take the single-row kernel (faster there)
 #ifndef NQ_GM_REWRITE_M
@@ -695,9 +690,10 @@ __global__ __launch_bounds__(WG) void k_gemm_sum(const float *part, float *y, ui
 // copy it, instead of each tile rewriting it (measured up to +23% from 384
 // rows, 1 to 15% slower at 144 to 256 rows: the copy is about twice the
 // packed bytes).  The results are the same bits either way for (2).  (3) With
-// 64-row tiles, at least three per compute unit, K steps hold 4 spans
-// instead of 8 (measured 5-23% faster there, up to 45% slower at two tiles
-// per compute unit); with five eighths to two such tiles per compute unit,
+// 64-row tiles, more than two per compute unit, K steps hold 4 spans
+// instead of 8 (measured 9-25% faster between two and three, 5-23% above;
+// at exactly two, one pass of 8-span workgroups, up to 45% slower); with
+// five eighths to two such tiles per compute unit,
 // K is split for three workgroups per compute unit, also in 4-span steps
 // (measured up to +46%; at half a tile per compute unit and below it lost
 // up to 32%).  The plan depends only on N, K, M and the compute-unit count.
@@ -717,7 +713,7 @@ inline GmPlan gm_plan_plain(const GmPlan &p, uint64_t K) {
 inline GmPlan gm_plan(uint64_t N, uint64_t K, uint64_t M, uint32_t cus) {
     const uint64_t bm = gm_bm(M), tiles = (N + GM_BN - 1) / GM_BN * ((M + bm - 1) / bm);
     const uint64_t c = cus ? cus : 1u;
-    const uint32_t sp0 = bm == 64u && tiles >= GM_SP4_TILES_PER_CU * c ? 4u : GM_SP;
+    const uint32_t sp0 = bm == 64u && tiles > 2ull * c ? 4u : GM_SP;
     const GmPlan p{1u, (uint32_t)((K / 32 + sp0 - 1) / sp0), M > GM_REWRITE_ONCE_M, sp0};
     if (tiles >= 2ull * c) return p;
     // K split; with 64-row tiles, five eighths to two per compute unit, into

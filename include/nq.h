@@ -256,7 +256,7 @@ int nq_gemv_q8_1(int32_t format, const void *weight, uint64_t nbytes, int64_t N,
  * q4_1, q5_1, q2_k, q4_k and q5_k), their exact integer dot products with
  * the activation codes come from the 8-bit matrix cores, and each is scaled
  * and added in binary32 (tiles of 16, 32 or 64 activation rows by M; K in
- * steps of 256 values, or 128 on grids of at least three 64-row tiles per
+ * steps of 256 values, or 128 on grids of more than two 64-row tiles per
  * compute unit and with K split over five eighths to two of them).
  * When the output has few tiles and K is long, K is split over workgroups:
  * each split's partial output goes to `workspace` (device memory the caller

@@ -266,7 +266,7 @@ def test_gemm_repeats_bit_for_bit_and_on_a_side_stream(fmt):
 
 GEMM_FULL = [("gguf:q4_k", 14336, 4096, 512), ("gguf:q8_0", 4096, 14336, 512), ("gguf:q6_k", 4096, 4096, 200),
              ("gguf:iq4_xs", 14336, 4096, 64), ("gguf:iq2_xxs", 4096, 4096, 100), ("gguf:q2_k", 1024, 14336, 72),
-             ("gguf:q4_k", 4096, 14336, 64)]
+             ("gguf:q4_k", 4096, 14336, 64), ("gguf:q6_k", 14336, 4096, 320)]
 
 
 @pytest.mark.parametrize("fmt,N,K,M", GEMM_FULL)
@@ -288,7 +288,7 @@ def test_gemm_full_size_sampled_rows(fmt, N, K, M):
 
 @pytest.mark.parametrize("fmt", GGUF)
 def test_gemm_four_span_k_steps(fmt):
-    """A grid of at least three 64-row tiles per compute unit (96 weight tiles
+    """A grid of more than two 64-row tiles per compute unit (96 weight tiles
     by 9 activation tiles, the last one 8 rows; K ragged against the 4-span
     step where the block size allows) takes K steps of 128 values on a
     256-compute-unit device, with the weight rewritten once (workspace) or
