@@ -2,19 +2,26 @@
 """Decode throughput of packed block-quantized weights on one MI355X.
 
 A step decodes the whole Llama-3-8B-shaped weight set (226 tensors; formats
-q4_k, q6_k, q8_0, nvfp4, tq2_0 in rotation) to bf16, back to back on one
-stream, with every payload already resident in HBM.  The JSON line reports:
+q4_k, q6_k, q8_0, nvfp4, tq2_0 in rotation) to bf16 on one stream, with every
+payload already resident in HBM: one nq_dequantize_packed_many call, which
+decodes the tensors of each format in one launch.  The same step made of 226
+single-tensor calls (nq_dequantize_packed) is timed beside it.  The JSON line
+reports:
 
   value          (payload + output bytes of the step) / (seconds per step)
   roofline       the dominant kernel (most total time) against MI355X HBM
                  peak: its algorithmic bytes per launch over its mean launch
-                 duration, timed with HIP events on the launch stream
-  cpu_baseline   the oracle, single-threaded on the host, on a bounded sample
-                 (the first eighth of each tensor's blocks)
-  per_format     every format of the step, plus the remaining workloads
-                 (q4_k/q6_k [4096,4096], mxfp4/nvfp4 [14336,4096], the IQ set
-                 [4096,14336] to f32 and bf16), each timed over rotating
-                 replicas so no launch reads a payload out of a warm cache
+                 duration, timed with HIP events on the launch stream; beside
+                 it the measured ceiling of a plain streaming kernel with the
+                 same read and write bytes (nq_measure_stream)
+  cpu_baseline   the oracle, single-threaded and pinned to one host core, on
+                 a bounded sample (the first third of each tensor's blocks)
+  per_format     every format of the step; every one of the 28 formats at
+                 [14336, 4096] -> bf16; the remaining workloads (q8_0/q4_0
+                 [64, 4096] -> f32, launch-bound; q4_k/q6_k [4096, 4096];
+                 mxfp4/nvfp4 [14336, 4096]; the IQ set [4096, 14336] to f32
+                 and bf16), each timed over rotating replicas so no launch
+                 reads a payload out of a warm cache
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -33,7 +40,8 @@ OUT_SIZE = {"f32": 4, "f16": 2, "bf16": 2, "f64": 8}
 
 # The sources the decode kernels are built from (the kernels the counter profile covers).
 DECODE_SOURCES = ["iq_grids.h", "nq_decode.h", "nq_kernel.h", "k_simple.hip", "k_kquant.hip", "k_iq.hip",
-                  "k_fp4.hip", "k_ternary.hip"]
+                  "k_fp4.hip", "k_ternary.hip", "k_many_simple.hip", "k_many_kquant.hip", "k_many_iq.hip",
+                  "k_many_fp4.hip", "k_many_ternary.hip"]
 
 
 def sources_sha256():
@@ -103,6 +111,9 @@ class Tensor:
         self.algo_bytes = self.nbytes + nel * OUT_SIZE[dtype]
         self.seed, self.recipe = seed, recipe
 
+    def desc(self):
+        return (self.fid, self.payload.data_ptr(), self.nbytes, self.shape, self.out.data_ptr())
+
     def launch(self, nq, stream_handle):
         if self.divisors > 1:
             st = nq.dequantize_nvfp4_stacked_raw(self.payload.data_ptr(), self.nbytes, self.shape, self.divisors,
@@ -169,30 +180,113 @@ def time_eager(torch, nq, items, steps, warmup):
     return (time.perf_counter() - t0) * 1e3 / steps, start.elapsed_time(end) / steps
 
 
+def capture_many(torch, call):
+    """A HIP graph holding one many-tensor call on torch's capture stream."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call.run(torch.cuda.current_stream().cuda_stream)
+    return g
+
+
+def time_eager_many(torch, call, steps, warmup):
+    """Wall and event milliseconds per eager many-tensor call."""
+    stream = torch.cuda.current_stream()
+    handle = stream.cuda_stream
+    for _ in range(warmup):
+        call.run(handle)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        call.run(handle)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps, start.elapsed_time(end) / steps
+
+
+def many_launches(n):
+    """Launches of a many-tensor call over n tensors of one format (64 to a launch)."""
+    return (n + 63) // 64
+
+
 def per_format_times(torch, nq, items, reps):
-    """Per format: one graph of all its launches in the step, timed by events."""
+    """Per format: one many-tensor call over the step's tensors of that format
+    (one launch per 64 tensors), graph-captured and timed by events on the
+    replay stream."""
     out = {}
     for fmt in dict.fromkeys(it.fmt for it in items):
         sel = [it for it in items if it.fmt == fmt]
-        g = capture(torch, nq, sel)
+        call = nq.ManyCall([it.desc() for it in sel], OUT_CODES["bf16"])
+        g = capture_many(torch, call)
         ms, _ = time_graph(torch, g, reps)
         nbytes = sum(it.algo_bytes for it in sel)
+        nl = many_launches(len(sel))
         gbps = nbytes / (ms * 1e-3) / 1e9
-        out[fmt] = {"gbps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
-                    "launches": len(sel), "mean_launch_us": round(ms * 1e3 / len(sel), 3),
-                    "bytes_per_launch": round(nbytes / len(sel)), "total_ms": ms}
+        out[fmt] = {"gbps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "tensors": len(sel),
+                    "launches": nl, "mean_launch_us": round(ms * 1e3 / nl, 3), "bytes_per_launch": round(nbytes / nl),
+                    "read_bytes_per_launch": round(sum(it.nbytes for it in sel) / nl), "total_ms": ms}
         del g
     return out
 
 
+STREAM_CONFIGS = [(c, f) for c in (1, 2, 4, 8) for f in (3, 2)]  # chunks per thread; NT load (1) and NT store (2)
+
+
+def stream_ceiling(torch, nq, read_bytes, write_bytes, launches=40, configs=STREAM_CONFIGS):
+    """nq_measure_stream (the decode's traffic, no arithmetic) over a cold
+    rotation, in each tile size and cache policy of `configs`: the best GB/s
+    of read + write bytes per mean launch time, with every configuration's."""
+    rb, wb = -(-read_bytes // 16) * 16, -(-write_bytes // 16) * 16
+    reps = cold_replicas(rb, rb + wb) if rb + wb < (2 << 30) else 1
+    launches = max(launches, reps)
+    bufs = [(torch.empty(rb, dtype=torch.uint8, device="cuda:0").fill_(r + 1),
+             torch.empty(wb, dtype=torch.uint8, device="cuda:0")) for r in range(reps)]
+    runs = {}
+    for c, flags in configs:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            h = torch.cuda.current_stream().cuda_stream
+            for i in range(launches):
+                src, dst = bufs[i % reps]
+                st = nq.measure_stream_raw(src.data_ptr(), rb, dst.data_ptr(), wb, c, flags, h)
+                if st != 0:
+                    raise nq.NqError(st, "measure_stream")
+        ms, _ = time_graph(torch, g, 3)
+        del g
+        mean_ms = ms / launches
+        runs[f"c{c}{'_ntl' if flags & 1 else ''}{'_nts' if flags & 2 else ''}"] = \
+            (round((rb + wb) / (mean_ms * 1e-3) / 1e9, 1), round(mean_ms * 1e3, 3))
+    del bufs
+    torch.cuda.empty_cache()
+    best = max(runs, key=lambda k: runs[k][0])
+    return {"gbps": runs[best][0], "frac_hbm_peak": round(runs[best][0] / HBM_PEAK_GBPS, 4), "read_bytes": rb,
+            "write_bytes": wb, "mean_launch_us": runs[best][1], "replicas": reps, "best": best,
+            "kernel": "k_stream (nq_measure_stream)", "gbps_by_config": {k: v[0] for k, v in runs.items()}}
+
+
+def cold_replicas(read_bytes, total_bytes, cap=2048):
+    """Replicas for a rotation that reads HBM on every launch: the read
+    buffers alone pass 1 GiB (four times MI355X's 256 MB last-level cache,
+    which keeps payloads that ordinary loads bring in) and all buffers pass
+    2 GiB."""
+    return max(2, min(cap, max(math.ceil((1 << 30) / max(1, read_bytes)), math.ceil((2 << 30) / total_bytes))))
+
+
 def rotating_measurement(torch, nq, synth, name, fmt, shape, recipe, seed, dtype, staging, launches=60,
-                         footprint=1 << 30, divisors=1):
-    """Mean launch time of one workload over replicas whose total footprint defeats the caches."""
+                         divisors=1):
+    """Mean launch time of one workload over a cold rotation of replicas
+    (cold_replicas; at least one launch per replica)."""
     first = Tensor(name, fmt, shape, recipe, seed, dtype, staging, torch, nq, synth, divisors)
-    reps = max(1, math.ceil(footprint / first.algo_bytes))
+    reps = cold_replicas(first.nbytes, first.algo_bytes)
+    launches = max(launches, reps)
     items = [first]
-    for r in range(1, reps):
-        items.append(Tensor(name, fmt, shape, recipe, seed, dtype, staging, torch, nq, synth, divisors))
+    for r in range(1, reps):  # same payload bytes, own buffers
+        t = Tensor.__new__(Tensor)
+        t.__dict__.update(first.__dict__)
+        t.payload = first.payload.clone()
+        t.out = torch.empty_like(first.out)
+        items.append(t)
     order = [items[i % reps] for i in range(launches)]
     g = capture(torch, nq, order)
     ms, _ = time_graph(torch, g, 3)
@@ -206,7 +300,7 @@ def rotating_measurement(torch, nq, synth, name, fmt, shape, recipe, seed, dtype
     return res
 
 
-def fp8_row_measurement(torch, nq, fmt, shape, dtype, launches=60, footprint=1 << 30, seed=0x6E7F8000):
+def fp8_row_measurement(torch, nq, fmt, shape, dtype, launches=60, seed=0x6E7F8000):
     """Row-scaled FP8 decode over rotating replicas: random code words with the
     NaN words replaced, positive normal scale words ([2^-9, 2^-5) for bfloat16,
     [2^-8, 2^-4) for binary16)."""
@@ -220,7 +314,8 @@ def fp8_row_measurement(torch, nq, fmt, shape, dtype, launches=60, footprint=1 <
     host = torch.from_numpy(np.concatenate([codes, scales.view(np.uint8)]))
     nbytes = host.numel()
     out_bytes = N * K * OUT_SIZE[dtype]
-    reps = max(1, math.ceil(footprint / (nbytes + out_bytes)))
+    reps = cold_replicas(nbytes, nbytes + out_bytes)
+    launches = max(launches, reps)
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "f64": torch.float64}[dtype]
     items = [(host.to("cuda:0"), torch.empty(N * K, dtype=tdt, device="cuda:0")) for _ in range(reps)]
     kind = nq.FP8_ROW_KINDS[fmt]
@@ -243,7 +338,7 @@ def fp8_row_measurement(torch, nq, fmt, shape, dtype, launches=60, footprint=1 <
     return res
 
 
-def gq_measurement(torch, nq, scheme, shape, in_dtype, launches=60, footprint=1 << 30, seed=0x6E7A6000):
+def gq_measurement(torch, nq, scheme, shape, in_dtype, launches=60, seed=0x6E7A6000):
     """grouped_absmax encoder over rotating replicas of a normal source with
     row magnitudes 2^-8 .. 2^4; bytes = source + codes + binary16 scales."""
     import numpy as np
@@ -255,7 +350,8 @@ def gq_measurement(torch, nq, scheme, shape, in_dtype, launches=60, footprint=1 
     x = x.to(tdt)
     ng = (K + G - 1) // G
     nbytes = x.numel() * x.element_size() + N * K + 2 * N * ng
-    reps = max(1, math.ceil(footprint / nbytes))
+    reps = cold_replicas(x.numel() * x.element_size(), nbytes)
+    launches = max(launches, reps)
     items = [(x.to("cuda:0"), torch.empty((N, K), dtype=torch.int8, device="cuda:0"),
               torch.empty((N, ng), dtype=torch.int16, device="cuda:0"),
               torch.empty(1, dtype=torch.int32, device="cuda:0")) for _ in range(reps)]
@@ -283,7 +379,7 @@ def gq_measurement(torch, nq, scheme, shape, in_dtype, launches=60, footprint=1 
     return res
 
 
-def gemv_measurement(torch, nq, synth, fmt, shape, M, launches=60, footprint=1 << 30, seed=0x6E7C7000):
+def gemv_measurement(torch, nq, synth, fmt, shape, M, launches=60, seed=0x6E7C7000):
     """Products with q8_1 activations (nq_gemv_q8_1) over rotating replicas of
     a weight [N, K]; bytes = weight payload + q8_1 activation blocks + binary32
     output, each counted once per launch (the activation is read from cache by
@@ -294,7 +390,8 @@ def gemv_measurement(torch, nq, synth, fmt, shape, M, launches=60, footprint=1 <
     nbytes_w = N * K // info.block_values * info.block_bytes
     host = synth.payload(fmt, N * K // info.block_values, seed, synth.binade(-6, -2, False))
     w0 = torch.from_numpy(host).to("cuda:0")
-    reps = max(1, math.ceil(footprint / nbytes_w))
+    reps = cold_replicas(nbytes_w, nbytes_w)
+    launches = max(launches, reps)
     ws = [w0] + [w0.clone() for _ in range(reps - 1)]
     rng = np.random.default_rng(seed)
     x = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to("cuda:0")
@@ -334,7 +431,7 @@ MFMA_I8_PEAK_TOPS = 5000.0
 GEMM_ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 3 * 32 * 2 / 1e12
 
 
-def gemm_measurement(torch, nq, synth, fmt, shape, M, launches=20, footprint=1 << 30, seed=0x6E7C8000):
+def gemm_measurement(torch, nq, synth, fmt, shape, M, launches=20, seed=0x6E7C8000):
     """Batched products with q8_1 activations over rotating weight replicas;
     TOP/s = 2 M N K per mean launch time."""
     import numpy as np
@@ -343,7 +440,8 @@ def gemm_measurement(torch, nq, synth, fmt, shape, M, launches=20, footprint=1 <
     nbytes_w = N * K // info.block_values * info.block_bytes
     host = synth.payload(fmt, N * K // info.block_values, seed, synth.binade(-6, -2, False))
     w0 = torch.from_numpy(host).to("cuda:0")
-    reps = max(1, math.ceil(footprint / nbytes_w))
+    reps = cold_replicas(nbytes_w, nbytes_w)
+    launches = max(launches, reps)
     ws = [w0] + [w0.clone() for _ in range(reps - 1)]
     rng = np.random.default_rng(seed)
     x = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to("cuda:0")
@@ -416,13 +514,42 @@ def gemm_only(torch, nq, synth, args):
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(nq, synth, tensors, fraction=8):
-    """The oracle on the first 1/fraction of every tensor's blocks, one thread."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+class pinned_to_one_core:
+    """Run the enclosed code with this process's CPU affinity set to one core
+    (the first it may use), restored afterwards."""
+
+    def __enter__(self):
+        self.before = os.sched_getaffinity(0)
+        self.core = min(self.before)
+        os.sched_setaffinity(0, {self.core})
+        return self
+
+    def __exit__(self, *exc):
+        os.sched_setaffinity(0, self.before)
+        return False
+
+
+def cpu_baseline(nq, synth, tensors, fraction=3):
+    """The oracle on the first 1/fraction of every tensor's blocks, one thread
+    pinned to one host core (payload generation, which is multithreaded, stays
+    outside the timed calls)."""
     import numpy as np
     import oracle
     total_bytes = 0
     total_elems = 0
     secs = 0.0
+    samples = []
     for name, fmt, shape, recipe, seed in tensors:
         _, B, S, T = oracle.info(fmt)
         nb = math.prod(shape) // B
@@ -430,15 +557,19 @@ def cpu_baseline(nq, synth, tensors, fraction=8):
         p = synth.payload(fmt, ns, seed, recipe)
         if T:
             p[-4:] = np.array([synth.divisor_bits(seed)], "<u4").view(np.uint8)
-        t0 = time.perf_counter()
-        oracle.decode(fmt, p, [ns * B], "bf16")
-        secs += time.perf_counter() - t0
-        total_bytes += p.size + ns * B * 2
-        total_elems += ns * B
+        samples.append((fmt, p, ns * B))
+    with pinned_to_one_core() as pin:
+        for fmt, p, n in samples:
+            t0 = time.perf_counter()
+            oracle.decode(fmt, p, [n], "bf16")
+            secs += time.perf_counter() - t0
+            total_bytes += p.size + n * 2
+            total_elems += n
     return {"value": round(total_bytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"first 1/{fraction} of the blocks of each of the {len(tensors)} tensors "
-                      f"({total_elems / 1e9:.3f} G values to bf16, {secs:.1f} s on one host core)",
-            "elements_per_s": round(total_elems / secs, 1)}
+                      f"({total_elems / 1e9:.3f} G values to bf16, {secs:.1f} s on host core {pin.core})",
+            "elements_per_s": round(total_elems / secs, 1), "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+            "affinity_before_pinning": len(pin.before), "pinned_core": pin.core}
 
 
 def gemv_cpu_baseline(synth, fmt="gguf:q4_k", shape=(14336, 4096), rows=14336, seed=0x6E7C7000):
@@ -540,37 +671,71 @@ def main():
     payload_bytes = sum(it.nbytes for it in items)
     elems = sum(it.nelems for it in items)
 
-    eager_wall_ms, eager_event_ms = time_eager(torch, nq, items, args.steps, args.warmup)
-    log(f"eager step: wall {eager_wall_ms:.3f} ms, events {eager_event_ms:.3f} ms")
-    step_graph = capture(torch, nq, items)
+    # the step: one many-tensor call (one launch per format here)
+    call = nq.ManyCall([it.desc() for it in items], OUT_CODES["bf16"])
+    eager_wall_ms, eager_event_ms = time_eager_many(torch, call, args.steps, args.warmup)
+    log(f"eager step (one many-tensor call): wall {eager_wall_ms:.3f} ms, events {eager_event_ms:.3f} ms")
+    step_graph = capture_many(torch, call)
     graph_ms, graph_wall_ms = time_graph(torch, step_graph, args.steps, warmup=args.warmup)
-    log(f"graph step: events {graph_ms:.3f} ms, wall {graph_wall_ms:.3f} ms")
+    log(f"graph step (one many-tensor call): events {graph_ms:.3f} ms, wall {graph_wall_ms:.3f} ms")
     del step_graph
     ms_per_step = graph_wall_ms
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # the same step as 226 single-tensor calls
+    pt_graph = capture(torch, nq, items)
+    pt_ms, pt_wall_ms = time_graph(torch, pt_graph, args.steps, warmup=args.warmup)
+    del pt_graph
+    pt_eager_wall_ms, pt_eager_event_ms = time_eager(torch, nq, items, max(2, args.steps // 2), 1)
+    log(f"graph step (226 single-tensor calls): events {pt_ms:.3f} ms, wall {pt_wall_ms:.3f} ms "
+        f"({step_bytes / (pt_wall_ms * 1e-3) / 1e9:.1f} GB/s)")
 
     formats = per_format_times(torch, nq, items, reps=max(2, args.steps // 2))
     dom = max(formats, key=lambda f: formats[f]["total_ms"])
     d = formats[dom]
     achieved = d["bytes_per_launch"] / (d["mean_launch_us"] * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": profiled_traffic(dom),
-                "kernel": f"k_decode {dom} -> bf16",
-                "bytes_per_launch": d["bytes_per_launch"], "mean_launch_us": d["mean_launch_us"]}
     for f in formats.values():
         del f["total_ms"]
-    del items
+    del items, call
     torch.cuda.empty_cache()
+    ceiling = stream_ceiling(torch, nq, d["read_bytes_per_launch"], d["bytes_per_launch"] - d["read_bytes_per_launch"],
+                             launches=10)
+    log(f"stream ceiling at {dom}'s read/write bytes: {ceiling['gbps']} GB/s")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": profiled_traffic(dom),
+                "kernel": f"k_decode_many {dom} -> bf16 ({d['tensors']} tensors per launch)",
+                "bytes_per_launch": d["bytes_per_launch"], "mean_launch_us": d["mean_launch_us"],
+                "copy_ceiling": ceiling, "frac_of_copy_ceiling": round(achieved / ceiling["gbps"], 4)}
 
     extra = {}
+    ceilings = {}
     if not args.no_per_format:
-        for cfg in (2, 3, 4):
+        # streaming ceilings at representative read:write mixes (bytes per value)
+        for key, (rb, wb) in {"1:1 copy": (1, 1), "q4_k -> bf16": (0.5625, 2), "q8_0 -> bf16": (1.0625, 2),
+                              "iq2_xxs -> f32": (0.2578, 4)}.items():
+            n = 58720256
+            ceilings[key] = stream_ceiling(torch, nq, int(rb * n), int(wb * n))
+            log(f"stream ceiling {key}: {ceilings[key]['gbps']} GB/s")
+        # every format at the [14336, 4096] shape -> bf16
+        st_all = torch.empty(14336 * 4096 // 256 * 292 + 4, dtype=torch.uint8, pin_memory=True)
+        for fid in range(nq.format_count()):
+            fmt = nq.format_by_id(fid).name.decode()
+            key = f"all_formats {fmt}[14336, 4096]->bf16"
+            extra[key] = rotating_measurement(torch, nq, synth, key, fmt, [14336, 4096], workloads.recipe_for(fmt),
+                                              0x6E718000 + fid, "bf16", st_all)
+            log(f"{key}: {extra[key]['gbps']} GB/s ({100 * extra[key]['frac_hbm_peak']:.1f}% of peak)")
+        del st_all
+        for cfg in (1, 2, 3, 4):
             ts, dtypes = workloads.CONFIGS[cfg]()
             st2 = staging_buffer(torch, ts, nq)
             for name, fmt, shape, recipe, seed in ts:
                 for dt in dtypes:
                     key = f"{name}->{dt}"
                     extra[key] = rotating_measurement(torch, nq, synth, name, fmt, shape, recipe, seed, dt, st2)
+                    if cfg == 1:
+                        extra[key]["launch_bound"] = True
+                        extra[key]["note"] = ("1.1-1.3 MB per launch: the launch's start-up and drain, not HBM, "
+                                              "set its time")
                     log(f"{key}: {extra[key]['gbps']} GB/s ({100 * extra[key]['frac_hbm_peak']:.1f}% of peak)")
             del st2
         # nvfp4 planes stacked from two and eight sources (a gate/up pair, eight experts' slices)
@@ -605,20 +770,27 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(nq, synth, tensors)
-        log(f"cpu baseline: {cpu['value']} GB/s ({cpu['sample']})")
+        log(f"cpu baseline: {cpu['value']} GB/s ({cpu['sample']}; {cpu['cpu_model']}, nproc {cpu['nproc']})")
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "llama3-8b weight set: 226 tensors, q4_k/q6_k/q8_0/nvfp4/tq2_0 rotation -> bf16",
+                   "output_dtype": "bf16", "call": "one nq_dequantize_packed_many per step (one launch per format)",
                    "tensors": len(tensors), "elements": elems, "payload_bytes": payload_bytes,
                    "output_bytes": step_bytes - payload_bytes, "graph_event_ms_per_step": round(graph_ms, 4),
                    "eager_wall_ms_per_step": round(eager_wall_ms, 4), "eager_event_ms_per_step": round(eager_event_ms, 4),
-                   "frac_hbm_peak": round(value / HBM_PEAK_GBPS, 4)},
+                   "frac_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+                   "single_tensor_calls": {
+                       "launches_per_step": len(tensors), "graph_wall_ms_per_step": round(pt_wall_ms, 4),
+                       "graph_event_ms_per_step": round(pt_ms, 4),
+                       "eager_wall_ms_per_step": round(pt_eager_wall_ms, 4),
+                       "eager_event_ms_per_step": round(pt_eager_event_ms, 4),
+                       "gbps": round(step_bytes / (pt_wall_ms * 1e-3) / 1e9, 1)}},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "per_format": {"step": formats, "workloads": extra},
+        "per_format": {"step": formats, "ceilings": ceilings, "workloads": extra},
     }
     print(json.dumps(line), flush=True)
 

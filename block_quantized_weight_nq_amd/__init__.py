@@ -16,11 +16,12 @@ LIB_PATH = os.path.join(_HERE, "libnq.so")
 NQ_OK = 0
 STATUS_NAMES = {0: "NQ_OK", 1: "NQ_ERR_NULL_ARG", 2: "NQ_ERR_UNKNOWN_FORMAT", 3: "NQ_ERR_BAD_RANK",
                 4: "NQ_ERR_BAD_DIM", 5: "NQ_ERR_NOT_BLOCK_ALIGNED", 6: "NQ_ERR_LENGTH_MISMATCH",
-                7: "NQ_ERR_OVERFLOW", 8: "NQ_ERR_BAD_DTYPE", 9: "NQ_ERR_HIP", 10: "NQ_ERR_BAD_DIVISORS"}
+                7: "NQ_ERR_OVERFLOW", 8: "NQ_ERR_BAD_DTYPE", 9: "NQ_ERR_HIP", 10: "NQ_ERR_BAD_DIVISORS",
+                11: "NQ_ERR_MISALIGNED"}
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "f64": 3}
 FAMILIES = {0: "simple", 1: "kquant", 2: "iq", 3: "fp4", 4: "ternary"}
 EXPORTS = ["nq_format_count", "nq_format_by_id", "nq_format_query", "nq_validate",
-           "nq_dequantize_packed", "nq_validate_nvfp4_stacked", "nq_dequantize_nvfp4_stacked",
+           "nq_dequantize_packed", "nq_dequantize_packed_many", "nq_measure_stream", "nq_validate_nvfp4_stacked", "nq_dequantize_nvfp4_stacked",
            "nq_validate_fp8_row", "nq_dequantize_fp8_row", "nq_validate_grouped_absmax",
            "nq_quantize_grouped_absmax", "nq_validate_quantize_q8_1", "nq_quantize_q8_1",
            "nq_validate_gemv_q8_1", "nq_gemv_q8_1", "nq_validate_gemm_q8_1", "nq_gemm_q8_1_workspace", "nq_gemm_q8_1",
@@ -47,6 +48,12 @@ class FormatInfo(ctypes.Structure):
                 f"S={self.block_bytes}, trailer={self.trailer_bytes}, family={FAMILIES[self.family]})")
 
 
+class TensorDesc(ctypes.Structure):
+    """nq_tensor: one tensor of nq_dequantize_packed_many."""
+    _fields_ = [("format", ctypes.c_int32), ("rank", ctypes.c_int32), ("shape", ctypes.POINTER(ctypes.c_int64)),
+                ("payload", ctypes.c_void_p), ("nbytes", ctypes.c_uint64), ("out", ctypes.c_void_p)]
+
+
 _LIB = None
 
 
@@ -65,6 +72,10 @@ def _lib():
                                   c.POINTER(c.c_uint64), c.POINTER(c.c_uint64)]
         L.nq_dequantize_packed.argtypes = [c.c_int32, c.c_void_p, c.c_uint64, c.POINTER(c.c_int64),
                                            c.c_int32, c.c_int32, c.c_void_p, c.c_void_p]
+        L.nq_dequantize_packed_many.argtypes = [c.POINTER(TensorDesc), c.c_int32, c.c_int32, c.POINTER(c.c_int32),
+                                                c.c_void_p]
+        L.nq_measure_stream.argtypes = [c.c_void_p, c.c_uint64, c.c_void_p, c.c_uint64, c.c_int32, c.c_int32,
+                                        c.c_void_p]
         L.nq_validate_nvfp4_stacked.argtypes = [c.c_uint64, c.POINTER(c.c_int64), c.c_int32, c.c_int64,
                                                 c.c_int32, c.POINTER(c.c_uint64), c.POINTER(c.c_uint64)]
         L.nq_dequantize_nvfp4_stacked.argtypes = [c.c_void_p, c.c_uint64, c.POINTER(c.c_int64), c.c_int32,
@@ -157,6 +168,78 @@ def dequantize_packed_raw(fmt_id, payload_ptr, nbytes, shape, out_dtype_code, ou
     return _lib().nq_dequantize_packed(fmt_id, ctypes.c_void_p(payload_ptr), nbytes, arr, rank,
                                        out_dtype_code, ctypes.c_void_p(out_ptr),
                                        ctypes.c_void_p(stream_handle))
+
+
+class ManyCall:
+    """A prepared nq_dequantize_packed_many call: the tensor array is built
+    once and reused by every run(stream_handle) (argument marshalling only).
+    descs: (format id, payload address, nbytes, shape, out address) per tensor."""
+
+    def __init__(self, descs, out_dtype_code):
+        self.n = len(descs)
+        self.code = int(out_dtype_code)
+        self.arr = (TensorDesc * max(1, self.n))()
+        self._shapes = []
+        for i, (fid, p, nbytes, shape, o) in enumerate(descs):
+            sh, rank = _shape(shape)
+            self._shapes.append(sh)
+            self.arr[i] = TensorDesc(int(fid), rank, ctypes.cast(sh, ctypes.POINTER(ctypes.c_int64)),
+                                     ctypes.c_void_p(p), int(nbytes), ctypes.c_void_p(o))
+        self.failed = ctypes.c_int32(-1)
+
+    def run_status(self, stream_handle):
+        st = _lib().nq_dequantize_packed_many(self.arr if self.n else None, self.n, self.code,
+                                              ctypes.byref(self.failed), ctypes.c_void_p(stream_handle))
+        return st, self.failed.value
+
+    def run(self, stream_handle):
+        st, failed = self.run_status(stream_handle)
+        if st != NQ_OK:
+            raise NqError(st, f"tensor {failed}")
+
+
+def dequantize_packed_many_raw(descs, out_dtype_code, stream_handle):
+    """Direct call of nq_dequantize_packed_many.  descs: (format id, payload
+    address, nbytes, shape, out address) per tensor.  Returns (status, index
+    of the failing tensor or -1)."""
+    return ManyCall(descs, out_dtype_code).run_status(stream_handle)
+
+
+def dequantize_packed_many(items, out_dtype=None, stream=None):
+    """Decode several tensors in as few launches as their formats allow.
+
+    items: (fmt, payload, shape) or (fmt, payload, shape, out) per tensor, with
+    payload a rank-1 uint8 CUDA tensor.  Returns the output tensors (new ones
+    where out is not given), decoded on `stream` (default: the current stream).
+    """
+    import torch
+    descs, outs = [], []
+    for it in items:
+        fmt, payload, shape = it[0], it[1], it[2]
+        out = it[3] if len(it) > 3 else None
+        fid = fmt if isinstance(fmt, int) else format_query(fmt).id
+        code, out, stream = _prepare(payload, shape, out_dtype if out_dtype is not None else
+                                     (out.dtype if out is not None else torch.float32), out, stream)
+        descs.append((fid, payload.data_ptr(), payload.numel(), shape, out.data_ptr()))
+        outs.append(out)
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if out_dtype is None:
+        out_dtype = outs[0].dtype if outs else torch.float32
+    st, failed = dequantize_packed_many_raw(descs, _dtype_code(out_dtype), stream.cuda_stream)
+    if st != NQ_OK:
+        raise NqError(st, f"tensor {failed}")
+    return outs
+
+
+STREAM_NT_LOAD, STREAM_NT_STORE = 1, 2
+
+
+def measure_stream_raw(src_ptr, src_bytes, dst_ptr, dst_bytes, chunks_per_thread, flags, stream_handle):
+    """nq_measure_stream (measurement aid): read src_bytes, write dst_bytes; returns the status."""
+    return _lib().nq_measure_stream(ctypes.c_void_p(src_ptr), int(src_bytes), ctypes.c_void_p(dst_ptr),
+                                    int(dst_bytes), int(chunks_per_thread), int(flags),
+                                    ctypes.c_void_p(stream_handle))
 
 
 def validate_nvfp4_stacked_status(nbytes, shape, divisors, out_dtype="f32"):

@@ -31,7 +31,8 @@ ARCH = os.environ.get("NQ_OFFLOAD_ARCH", "gfx950")
 KERNEL_SOURCES = ["k_simple.hip", "k_kquant.hip", "k_iq.hip", "k_fp4.hip", "k_ternary.hip", "k_fp8row.hip",
                   "k_gqenc.hip", "k_q8_1.hip", "k_gemv_simple.hip", "k_gemv_kquant.hip", "k_gemv_iq.hip",
                   "k_gemv_fp4t.hip", "k_gemm_simple.hip", "k_gemm_kquant.hip", "k_gemm_iq.hip",
-                  "k_gemm_fp4t.hip"]
+                  "k_gemm_fp4t.hip", "k_many_simple.hip", "k_many_kquant.hip", "k_many_iq.hip", "k_many_fp4.hip",
+                  "k_many_ternary.hip", "k_measure.hip"]
 HOST_SOURCES = ["nq_abi.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-ffp-contract=off",

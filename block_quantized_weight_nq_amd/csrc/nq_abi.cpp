@@ -7,9 +7,11 @@
 // "tensor-formats" page carried as gguf:nvfp4 blocks plus a 4-byte binary32
 // divisor.
 #include <atomic>
+#include <vector>
 #include <string.h>
 
 #include "../../include/nq.h"
+#include "../../include/nq_measure.h"
 #include "nq_fp8row.h"
 #include "nq_gemv.h"
 #include "nq_gqenc.h"
@@ -147,7 +149,7 @@ int launch_validated(int32_t format, const void *payload, uint64_t nbytes, uint6
     if (nbytes > 0 && !payload) return NQ_ERR_NULL_ARG;
     if (elems == 0) return NQ_OK;
     if (!out) return NQ_ERR_NULL_ARG;
-    if (((uintptr_t)out % OUT_SIZE[out_dtype]) != 0) return NQ_ERR_NULL_ARG;
+    if (((uintptr_t)out % OUT_SIZE[out_dtype]) != 0) return NQ_ERR_MISALIGNED;
     nq::LaunchArgs L;
     L.payload = (const uint8_t *)payload;
     L.nbytes = nbytes;
@@ -176,6 +178,80 @@ NQ_API int nq_dequantize_packed(int32_t format, const void *payload, uint64_t nb
     if (st != NQ_OK) return st;
     // one divisor: its group is the whole tensor
     return launch_validated(format, payload, nbytes, elems, out_dtype, out, 1u, elems / 8 ? elems / 8 : 1, stream);
+}
+
+namespace {
+
+int launch_many_family(int32_t format, int ot, bool vec, const nq::ManyItem *items, int n, hipStream_t stream) {
+    const uint32_t resident = resident_workgroups();
+    switch (REGISTRY[format].family) {
+    case NQ_FAMILY_SIMPLE: return nq::launch_many_simple(format, ot, vec, items, n, resident, stream);
+    case NQ_FAMILY_KQUANT: return nq::launch_many_kquant(format, ot, vec, items, n, resident, stream);
+    case NQ_FAMILY_IQ: return nq::launch_many_iq(format, ot, vec, items, n, resident, stream);
+    case NQ_FAMILY_FP4: return nq::launch_many_fp4(format, ot, vec, items, n, resident, stream);
+    default: return nq::launch_many_ternary(format, ot, vec, items, n, resident, stream);
+    }
+}
+
+}  // namespace
+
+NQ_API int nq_dequantize_packed_many(const nq_tensor *tensors, int32_t count, int32_t out_dtype, int32_t *failed,
+                                     hipStream_t stream) {
+    if (failed) *failed = -1;
+    if (count < 0) return NQ_ERR_BAD_DIM;
+    if (count > 0 && !tensors) return NQ_ERR_NULL_ARG;
+    if (out_dtype < NQ_F32 || out_dtype > NQ_F64) return NQ_ERR_BAD_DTYPE;
+    // every tensor is checked before anything is launched
+    std::vector<uint64_t> elems((size_t)count);
+    for (int32_t i = 0; i < count; i++) {
+        const nq_tensor &t = tensors[i];
+        int st = nq_validate(t.format, t.nbytes, t.shape, t.rank, out_dtype, &elems[(size_t)i], nullptr);
+        if (st == NQ_OK && t.nbytes > 0 && !t.payload) st = NQ_ERR_NULL_ARG;
+        if (st == NQ_OK && elems[(size_t)i] > 0 && !t.out) st = NQ_ERR_NULL_ARG;
+        if (st == NQ_OK && elems[(size_t)i] > 0 && (uintptr_t)t.out % OUT_SIZE[out_dtype] != 0)
+            st = NQ_ERR_MISALIGNED;
+        if (st != NQ_OK) {
+            if (failed) *failed = i;
+            return st;
+        }
+    }
+    // one group per (format, 16-byte aligned output or not), in order of first appearance
+    std::vector<char> done((size_t)count, 0);
+    std::vector<nq::ManyItem> group;
+    for (int32_t i = 0; i < count; i++) {
+        if (done[(size_t)i] || elems[(size_t)i] == 0) continue;
+        const int32_t f = tensors[i].format;
+        const bool vec = ((uintptr_t)tensors[i].out & 15u) == 0;
+        group.clear();
+        for (int32_t j = i; j < count; j++) {
+            const nq_tensor &t = tensors[j];
+            if (done[(size_t)j] || elems[(size_t)j] == 0 || t.format != f || (((uintptr_t)t.out & 15u) == 0) != vec)
+                continue;
+            done[(size_t)j] = 1;
+            nq::ManyItem it;
+            it.payload = (const uint8_t *)t.payload;
+            it.nbytes = t.nbytes;
+            it.nblocks = elems[(size_t)j] / (uint64_t)B_OF(f);
+            it.out = t.out;
+            group.push_back(it);
+        }
+        const int st = launch_many_family(f, out_dtype, vec, group.data(), (int)group.size(), stream);
+        if (st != NQ_OK) return st;
+    }
+    return NQ_OK;
+}
+
+NQ_API int nq_measure_stream(const void *src, uint64_t src_bytes, void *dst, uint64_t dst_bytes,
+                             int32_t chunks_per_thread, int32_t flags, hipStream_t stream) {
+    if (!src || !dst) return NQ_ERR_NULL_ARG;
+    if ((uintptr_t)src % 16 != 0 || (uintptr_t)dst % 16 != 0) return NQ_ERR_MISALIGNED;
+    if (dst_bytes == 0 || src_bytes > dst_bytes || src_bytes % 16 != 0 || dst_bytes % 16 != 0)
+        return NQ_ERR_BAD_DIM;
+    const int c = chunks_per_thread;
+    if ((c != 1 && c != 2 && c != 4 && c != 8) || (flags & ~3) != 0) return NQ_ERR_BAD_DIM;
+    if (dst_bytes > (1ull << 40)) return NQ_ERR_OVERFLOW;
+    return nq::launch_stream(src, src_bytes, dst, dst_bytes, c, (flags & NQ_STREAM_NT_LOAD) != 0,
+                             (flags & NQ_STREAM_NT_STORE) != 0, stream);
 }
 
 NQ_API int nq_validate_nvfp4_stacked(uint64_t nbytes, const int64_t *shape, int32_t rank, int64_t divisors,
@@ -242,7 +318,7 @@ NQ_API int nq_dequantize_fp8_row(int32_t scale_kind, const void *payload, uint64
     const int st = nq_validate_fp8_row(scale_kind, nbytes, shape, rank, out_dtype, &elems, nullptr);
     if (st != NQ_OK) return st;
     if (!payload || !out) return NQ_ERR_NULL_ARG;  // both dimensions are positive: never empty
-    if (((uintptr_t)out % OUT_SIZE[out_dtype]) != 0) return NQ_ERR_NULL_ARG;
+    if (((uintptr_t)out % OUT_SIZE[out_dtype]) != 0) return NQ_ERR_MISALIGNED;
     nq::F8Launch L;
     L.payload = (const uint8_t *)payload;
     L.N = (uint64_t)shape[0];
@@ -275,7 +351,7 @@ NQ_API int nq_quantize_grouped_absmax(int32_t scheme, const void *x, const int64
     if (st != NQ_OK) return st;
     if (!x || !codes || !scales || !status) return NQ_ERR_NULL_ARG;
     if ((uintptr_t)x % OUT_SIZE[in_dtype] != 0 || (uintptr_t)scales % 2 != 0 || (uintptr_t)status % 4 != 0)
-        return NQ_ERR_NULL_ARG;
+        return NQ_ERR_MISALIGNED;
     nq::GqLaunch L;
     L.x = x;
     L.codes = (int8_t *)codes;
@@ -308,7 +384,7 @@ NQ_API int nq_quantize_q8_1(const void *x, const int64_t *shape, int32_t rank, i
     if (st != NQ_OK) return st;
     if (!x || !blocks || !status) return NQ_ERR_NULL_ARG;
     if ((uintptr_t)x % OUT_SIZE[in_dtype] != 0 || (uintptr_t)blocks % 4 != 0 || (uintptr_t)status % 4 != 0)
-        return NQ_ERR_NULL_ARG;
+        return NQ_ERR_MISALIGNED;
     nq::Q81Launch L;
     L.x = x;
     L.nblocks = (uint64_t)shape[0] * ((uint64_t)shape[1] / 32);
@@ -343,7 +419,7 @@ NQ_API int nq_gemv_q8_1(int32_t format, const void *weight, uint64_t nbytes, int
     const int st = nq_validate_gemv_q8_1(format, nbytes, N, K, M);
     if (st != NQ_OK) return st;
     if (!weight || !xq || !y) return NQ_ERR_NULL_ARG;
-    if ((uintptr_t)xq % 4 != 0 || (uintptr_t)y % 4 != 0) return NQ_ERR_NULL_ARG;
+    if ((uintptr_t)xq % 4 != 0 || (uintptr_t)y % 4 != 0) return NQ_ERR_MISALIGNED;
     nq::GvLaunch L;
     L.w = (const uint8_t *)weight;
     L.N = (uint64_t)N;
@@ -394,7 +470,8 @@ NQ_API int nq_gemm_q8_1(int32_t format, const void *weight, uint64_t nbytes, int
     const int st = nq_validate_gemm_q8_1(format, nbytes, N, K, M);
     if (st != NQ_OK) return st;
     if (!weight || !xq || !y) return NQ_ERR_NULL_ARG;
-    if ((uintptr_t)xq % 4 != 0 || (uintptr_t)y % 4 != 0 || (uintptr_t)workspace % 16 != 0) return NQ_ERR_NULL_ARG;
+    if ((uintptr_t)xq % 4 != 0 || (uintptr_t)y % 4 != 0 || (uintptr_t)workspace % 16 != 0)
+        return NQ_ERR_MISALIGNED;
     nq::GvLaunch L;
     L.w = (const uint8_t *)weight;
     L.N = (uint64_t)N;
@@ -426,16 +503,17 @@ NQ_API int nq_gemm_q8_1(int32_t format, const void *weight, uint64_t nbytes, int
 NQ_API const char *nq_status_string(int status) {
     switch (status) {
     case NQ_OK: return "ok";
-    case NQ_ERR_NULL_ARG: return "a required pointer is NULL or misaligned";
+    case NQ_ERR_NULL_ARG: return "a required pointer is NULL";
     case NQ_ERR_UNKNOWN_FORMAT: return "unknown format identifier";
     case NQ_ERR_BAD_RANK: return "shape rank must be at least 1";
-    case NQ_ERR_BAD_DIM: return "shape has a negative dimension";
+    case NQ_ERR_BAD_DIM: return "a dimension or count is outside its allowed range";
     case NQ_ERR_NOT_BLOCK_ALIGNED: return "last dimension is not a multiple of the block size";
     case NQ_ERR_LENGTH_MISMATCH: return "payload length differs from the length rule";
     case NQ_ERR_OVERFLOW: return "byte or element count overflows";
     case NQ_ERR_BAD_DTYPE: return "unknown output dtype";
     case NQ_ERR_HIP: return "HIP launch failed";
     case NQ_ERR_BAD_DIVISORS: return "divisors must be in [1, 2^30] and divide the row count";
+    case NQ_ERR_MISALIGNED: return "a pointer is not aligned as the call requires";
     default: return "unknown status";
     }
 }

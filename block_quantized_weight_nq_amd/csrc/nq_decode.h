@@ -378,30 +378,36 @@ NQ_HD void unit_iq4_xs(const Src &src, uint32_t bo, uint32_t s, float (&y)[8]) {
 
 // TQ1_0: sequences (0,32,5), (32,16,5), (48,4,4); t = floor(3((b 3^p) mod 256)/256) - 1.
 NQ_HD uint32_t pow3(uint32_t p) { return p == 0 ? 1u : p == 1 ? 3u : p == 2 ? 9u : p == 3 ? 27u : 81u; }
-NQ_HD int trit(uint32_t b, uint32_t p) { return (int)((3u * ((b * pow3(p)) & 255u)) >> 8) - 1; }
 
+// Digit k of each byte of w (byte b of the result: floor(3 * ((byte * 3^k)
+// mod 256) / 256), 0..2), two bytes per multiply in 16-bit fields: byte *
+// 3^k <= 20655 and 3 * 255 stay inside a field.
+NQ_HD uint32_t digits4(uint32_t w, uint32_t k) {
+    const uint32_t m = pow3(k);
+    const uint32_t e = ((((w & 0x00FF00FFu) * m) & 0x00FF00FFu) * 3u >> 8) & 0x00030003u;
+    const uint32_t o = (((((w >> 8) & 0x00FF00FFu) * m) & 0x00FF00FFu) * 3u >> 8) & 0x00030003u;
+    return e | (o << 8);
+}
+
+// Unit s of a tq1_0 block, without branches (a wave's lanes hold every s):
+// s < 20 takes digit s/4 of bytes 8(s mod 4) .. +7; 20 <= s < 30 digit
+// (s-20)/2 of bytes 32 + 8((s-20) mod 2) .. +7; s >= 30 digits 2(s-30) and
+// 2(s-30)+1 of bytes 48..51 (outputs 240 + 4k + i: digit k of byte 48 + i).
+// One 8-byte window per unit (at 44 for s >= 30, whose upper half holds
+// bytes 48..51); y = M(d, digit - 1).
 template <class Src>
 NQ_HD void unit_tq1_0(const Src &src, uint32_t bo, uint32_t s, float (&y)[8]) {
     const float d = f16(u16_at(src, bo + 52));
-    if (s < 20u) {
-        uint32_t q[2];
-        window<2>(src, bo + 8u * (s & 3u), q);
-        const uint32_t p = s >> 2;
+    const bool first = s < 20u, tail = s >= 30u;
+    const uint32_t off = first ? 8u * (s & 3u) : tail ? 44u : 32u + 8u * ((s - 20u) & 1u);
+    const uint32_t p0 = first ? s >> 2 : tail ? 2u * (s - 30u) : (s - 20u) >> 1;
+    uint32_t q[2];
+    window<2>(src, bo + off, q);
+    uint32_t c[2];
+    c[0] = opaque(digits4(tail ? q[1] : q[0], p0));
+    c[1] = opaque(digits4(q[1], tail ? p0 + 1u : p0));
 #pragma unroll
-        for (int j = 0; j < 8; j++) y[j] = M(d, (float)trit(bytek(q[j >> 2], (uint32_t)(j & 3)), p));
-    } else if (s < 30u) {
-        uint32_t q[2];
-        window<2>(src, bo + 32 + 8u * ((s - 20u) & 1u), q);
-        const uint32_t p = (s - 20u) >> 1;
-#pragma unroll
-        for (int j = 0; j < 8; j++) y[j] = M(d, (float)trit(bytek(q[j >> 2], (uint32_t)(j & 3)), p));
-    } else {
-        uint32_t q[1];
-        window<1>(src, bo + 48, q);
-        const uint32_t p0 = 2u * (s - 30u);
-#pragma unroll
-        for (int j = 0; j < 8; j++) y[j] = M(d, (float)trit(bytek(q[0], (uint32_t)(j & 3)), p0 + (uint32_t)(j >> 2)));
-    }
+    for (int j = 0; j < 8; j++) y[j] = M(d, (float)code_at(c, j) - 1.0f);
 }
 
 // TQ2_0: y = M(d, v-1), v = P(q,2,32).

@@ -322,15 +322,8 @@ NQ_HD uint32_t iq_signs8(uint32_t s7) { return s7 | (parity7(s7) << 7); }
 NQ_HD uint32_t bsub(uint32_t c, uint32_t o) { return ((c | 0x80808080u) - o) ^ 0x80808080u; }
 
 // Four base-3 digits as signed codes: byte b of the result is digit k of
-// byte b of w minus 1, by the decoder's digit rule floor(3 * ((byte * 3^k)
-// mod 256) / 256), two bytes per multiply in 16-bit fields (byte * 3^k <=
-// 20655 and 3 * 255 stay inside a field).
-NQ_HD uint32_t trits4(uint32_t w, uint32_t k) {
-    const uint32_t m = pow3(k);
-    const uint32_t e = ((((w & 0x00FF00FFu) * m) & 0x00FF00FFu) * 3u >> 8) & 0x00030003u;
-    const uint32_t o = (((((w >> 8) & 0x00FF00FFu) * m) & 0x00FF00FFu) * 3u >> 8) & 0x00030003u;
-    return bsub(e | (o << 8), 0x01010101u);
-}
+// byte b of w minus 1 (the decoder's digit rule, digits4).
+NQ_HD uint32_t trits4(uint32_t w, uint32_t k) { return bsub(digits4(w, k), 0x01010101u); }
 
 // The 32 codes (digit - 1, value order) of 32-value item p (< 8) of a tq1_0
 // block: values 32k + i (k < 5, i < 32) are digit k of byte i, values

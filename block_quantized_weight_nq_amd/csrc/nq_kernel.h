@@ -16,14 +16,21 @@
 #include "nq_decode.h"
 
 // Tuning knobs (compile-time; the defaults are the measured best on MI355X):
-//   NQ_NTL        1: staging loads are non-temporal (each payload byte is read once)
+//   NQ_NTL        1: load_stream4 (the row-scaled FP8 and product kernels'
+//                 streaming loads) is non-temporal
+//   NQ_STAGE_NT   the decode's staging loads: -1 (default) per format
+//                 (staging_nt), 0 ordinary, 1 non-temporal for every format
 //   NQ_UPT        units (8 outputs) per thread per tile for every launch
 //                 (default: chosen per launch from its size, see choose_upt)
+//   NQ_UPT_MAX    cap on that choice for every format (default: per format, upt_max)
 //   NQ_RESIDENT_PER_CU  workgroups a compute unit holds at once, the scale of
 //                 the per-launch tile-size choice
 //   NQ_NT_STORE   non-temporal output stores: 0 never, 1 always, 2 16-bit outputs only
 #ifndef NQ_NTL
 #define NQ_NTL 1
+#endif
+#ifndef NQ_STAGE_NT
+#define NQ_STAGE_NT -1
 #endif
 #ifndef NQ_RESIDENT_PER_CU
 #define NQ_RESIDENT_PER_CU 8
@@ -69,18 +76,23 @@ struct DevSrc {
     NQ_HD uint32_t dw(uint32_t i) const { return base[i]; }
     // the extra dword of a window, clamped to the last payload dword
     NQ_HD uint32_t dwx(uint32_t i) const { return base[i < last ? i : last]; }
-    // 16 bytes that are read once (non-temporal when NQ_NTL).
-    NQ_HD void load_stream4(uint32_t i, uint32_t (&r)[4]) const {
-#if NQ_NTL && defined(__HIP_DEVICE_COMPILE__)
-        const u32x4a4 v = __builtin_nontemporal_load((const u32x4a4 *)(base + i));
-#else
-        const u32x4a4 v = *(const u32x4a4 *)(base + i);
+    // 16 bytes, non-temporal when NT.
+    template <bool NT>
+    NQ_HD void load4(uint32_t i, uint32_t (&r)[4]) const {
+        u32x4a4 v;
+#if defined(__HIP_DEVICE_COMPILE__)
+        if constexpr (NT)
+            v = __builtin_nontemporal_load((const u32x4a4 *)(base + i));
+        else
 #endif
+            v = *(const u32x4a4 *)(base + i);
         r[0] = v.x;
         r[1] = v.y;
         r[2] = v.z;
         r[3] = v.w;
     }
+    // 16 bytes that are read once (non-temporal when NQ_NTL).
+    NQ_HD void load_stream4(uint32_t i, uint32_t (&r)[4]) const { load4<NQ_NTL != 0>(i, r); }
 };
 
 // Lookup tables (LDS in the kernels, host arrays in the emulator).
@@ -273,6 +285,22 @@ struct LdsSrc {
     }
 };
 
+// Cache policy of the staging loads, measured per format on MI355X
+// ([14336, 4096] tensors to bf16 over rotations whose payloads alone pass
+// 1 GiB, so every launch reads HBM): ordinary and non-temporal loads come
+// within about 1% of each other for most formats at their best tile size;
+// ordinary loads are ahead by up to 12% on the small tiles of the codebook
+// formats, non-temporal ones by about 1% on the three 8-bit formats (q8_0,
+// q8_1, q8_k), which read the most payload bytes per value.
+template <int F>
+constexpr bool staging_nt() {
+#if NQ_STAGE_NT >= 0
+    return NQ_STAGE_NT != 0;
+#else
+    return F == Q8_0 || F == Q8_1 || F == Q8_K;
+#endif
+}
+
 template <int F, int UPT>
 struct Stage {
     static constexpr uint32_t UPB = block_values(F) / 8;
@@ -321,7 +349,7 @@ NQ_HD void stage_load(const Src &src, const KArgs &a, uint32_t t, uint32_t tid, 
 #pragma unroll
     for (uint32_t k = 0; k < ST::NK; k++) {
         const uint32_t c0 = k * WG + tid;
-        src.load_stream4(a0 + 4u * (c0 < cmax ? c0 : cmax), r[k]);
+        src.template load4<staging_nt<F>()>(a0 + 4u * (c0 < cmax ? c0 : cmax), r[k]);
     }
 }
 
@@ -456,21 +484,15 @@ NQ_HD void fill_tables(uint64_t *t8, uint32_t *t4, float *nvq, float *nvd, const
     }
 }
 
-// One workgroup per tile: workgroup t stages tile t in LDS and decodes it
-// (or decodes it from global memory when it is not staged); the hardware
-// keeps as many workgroups in flight as LDS and registers allow.  The tile's
-// loads are issued before the lookup tables are filled, so the two
-// latencies overlap, and one barrier publishes both.
+// Tile t of the launch described by `a`: staged in LDS and decoded (or
+// decoded from global memory when it is not staged).  The tile's loads are
+// issued before the lookup tables are filled, so the two latencies overlap,
+// and one barrier publishes both.  The LDS arrays are the kernel's.
 template <int F, int OT, int UPT, bool VEC>
-__global__ __launch_bounds__(WG) void k_decode(KArgs a) {
+__device__ __forceinline__ void decode_tile(const KArgs &a, uint32_t t, uint32_t tid, uint64_t *t8, uint32_t *t4,
+                                            float *nvq, float *nvd, uint32_t *lds) {
     using TS = TabSpec<F>;
     using ST = Stage<F, UPT>;
-    __shared__ uint64_t t8[TS::n8 > 0 ? TS::n8 : 1];
-    __shared__ uint32_t t4[TS::n4 > 0 ? TS::n4 : 1];
-    __shared__ float nvq[TS::nf > 0 ? TS::nf : 1];
-    __shared__ float nvd[TS::nd > 0 ? TS::nd : 1];
-    __shared__ __attribute__((aligned(16))) uint32_t lds[ST::SLOT_DW];
-    const uint32_t tid = threadIdx.x, t = blockIdx.x;
     const DevSrc src{a.base, a.last};
     Tab tab{t8, t4, nvq, nvd, 0xFFFFFFFFu, 1u};
     uint32_t g0 = 0;
@@ -493,6 +515,93 @@ __global__ __launch_bounds__(WG) void k_decode(KArgs a) {
         }
         decode_direct<F, OT, UPT, VEC>(src, tab, a, t, tid);
     }
+}
+
+// The LDS of one decode workgroup: lookup tables and the staged tile.
+#define NQ_DECODE_LDS(F, UPT)                                                   \
+    __shared__ uint64_t t8[TabSpec<F>::n8 > 0 ? TabSpec<F>::n8 : 1];            \
+    __shared__ uint32_t t4[TabSpec<F>::n4 > 0 ? TabSpec<F>::n4 : 1];            \
+    __shared__ float nvq[TabSpec<F>::nf > 0 ? TabSpec<F>::nf : 1];              \
+    __shared__ float nvd[TabSpec<F>::nd > 0 ? TabSpec<F>::nd : 1];              \
+    __shared__ __attribute__((aligned(16))) uint32_t lds[Stage<F, UPT>::SLOT_DW]
+
+// One workgroup per tile: workgroup t decodes tile t; the hardware keeps as
+// many workgroups in flight as LDS and registers allow.  STACKED: an "nvfp4"
+// launch with more than one divisor; otherwise the divisor count is the
+// constant 1, and the code for units past the first divisor group compiles
+// away (that code cost the one-divisor decode 10-15%).
+template <int F, int OT, int UPT, bool VEC, bool STACKED>
+__global__ __launch_bounds__(WG) void k_decode(KArgs a) {
+    NQ_DECODE_LDS(F, UPT);
+    if constexpr (!STACKED) a.ndiv = 1;
+    decode_tile<F, OT, UPT, VEC>(a, blockIdx.x, threadIdx.x, t8, t4, nvq, nvd, lds);
+}
+
+// ---------------------------------------------------------------------------
+// Several tensors of one format and output type in one launch
+// (nq_dequantize_packed_many).  Each tensor (or launch chunk of one) keeps
+// its own tiles, numbered on from the previous tensor's; a workgroup finds
+// its tensor by a binary search over the first-tile numbers, which are
+// uniform, so the search runs on scalar registers.  Decoding a unit does not
+// depend on the tile it sits in, so every value is the one a single-tensor
+// launch gives.
+// ---------------------------------------------------------------------------
+constexpr int MANY_MAX = 64;  // tensors (or chunks of tensors) per launch
+
+struct MTensor {
+    const uint32_t *base;     // payload, aligned down to 4 bytes
+    const uint32_t *tr_base;  // "nvfp4": the divisor word, aligned down to 4 bytes
+    void *out;                // output element 0
+    uint32_t mis, last;       // as KArgs
+    uint32_t tr_mis, tr_last; // as KArgs
+    uint32_t nunits;          // units of this tensor (chunk)
+    uint32_t tile0;           // its first tile, counted over the launch
+};
+
+struct MArgs {
+    uint32_t n;  // entries used
+    uint32_t ntiles;
+    MTensor t[MANY_MAX];
+};
+static_assert(sizeof(MArgs) <= 4096, "kernel arguments stay within 4 KiB");
+
+NQ_HD KArgs many_entry_args(const MTensor &e) {
+    KArgs a;
+    a.base = e.base;
+    a.tr_base = e.tr_base;
+    a.out = e.out;
+    a.mis = e.mis;
+    a.last = e.last;
+    a.tr_mis = e.tr_mis;
+    a.tr_last = e.tr_last;
+    a.nunits = e.nunits;
+    a.ndiv = 1;  // one divisor per "nvfp4" tensor
+    a.u0 = 0;
+    a.gu = e.nunits ? e.nunits : 1u;
+    return a;
+}
+
+// Index of the entry holding tile b: the last entry whose first tile is at
+// or before b (entries have at least one tile each).
+NQ_HD uint32_t many_find(const MArgs &m, uint32_t b) {
+    uint32_t lo = 0, hi = m.n;
+    while (hi - lo > 1u) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (m.t[mid].tile0 <= b)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    return lo;
+}
+
+template <int F, int OT, int UPT, bool VEC>
+__global__ __launch_bounds__(WG) void k_decode_many(MArgs m) {
+    NQ_DECODE_LDS(F, UPT);
+    const uint32_t b = blockIdx.x;
+    const uint32_t j = many_find(m, b);
+    const KArgs a = many_entry_args(m.t[j]);
+    decode_tile<F, OT, UPT, VEC>(a, b - m.t[j].tile0, threadIdx.x, t8, t4, nvq, nvd, lds);
 }
 
 // Host launch description for one call.
@@ -540,20 +649,35 @@ NQ_HD KArgs chunk_args(const LaunchArgs &L, uint64_t b0, uint64_t nb, uint32_t *
 }
 
 // Units per thread per tile, from the launch's units per resident workgroup
-// q (the device holds `resident` workgroups at once; 2048 on MI355X).  Few
-// units per resident workgroup call for small tiles, so that every compute
-// unit gets work; large launches take larger tiles, which spend less on
-// per-workgroup setup.  Formats whose codebook fills 8 KiB or more of LDS
-// (IQ2_S, IQ1_S, IQ1_M) copy it once per workgroup and so take larger tiles
-// sooner.  The classes come from measurements on MI355X over 0.6-180 MB
-// tensors of nine formats:
+// q (the device holds `resident` workgroups at once; 2048 on MI355X), capped
+// per format.  Few units per resident workgroup call for small tiles, so
+// that every compute unit gets work:
 //   q < 128 -> 1,  < 1024 -> 2,  < 2048 -> 4,  else 8;
-//   large codebooks: q < 128 -> 1, < 256 -> 2, < 512 -> 4, < 1024 -> 8, else 16.
-// Outputs that are not 16-byte aligned, and f64 outputs, always take 8.
-// NQ_UPT, when defined, fixes the tile size of every launch.
+//   large codebooks (IQ2_S, IQ1_S, IQ1_M, which copy 8-16 KiB to LDS per
+//   workgroup): q < 128 -> 1, < 256 -> 2, < 512 -> 4, < 1024 -> 8, else 16.
+// The cap (upt_max) is the tile size that decoded a [14336, 4096] tensor to
+// bf16 fastest on MI355X (2, 4 or 8, two runs each over rotations whose
+// payloads alone pass 1 GiB): smaller tiles keep more workgroups, and so
+// more independent loads and stores, in flight; formats whose workgroups
+// copy a codebook or fill a quotient table, and those with few payload bytes
+// per value (q2_k, tq2_0), do better with larger tiles.  Outputs that are not 16-byte aligned, and
+// f64 outputs, always take 8.  NQ_UPT, when defined, fixes the tile size of
+// every launch; NQ_UPT_MAX replaces every format's cap.
 template <int F>
 constexpr bool big_codebook() {
     return TabSpec<F>::n8 >= 1024;
+}
+
+template <int F>
+constexpr int upt_max() {
+#ifdef NQ_UPT_MAX
+    return NQ_UPT_MAX;
+#else
+    return (F == Q2_K || F == Q3_K || F == IQ2_XXS || F == IQ2_XS || F == IQ3_XXS || F == IQ1_S || F == IQ3_S ||
+            F == IQ2_S || F == IQ1_M || F == TQ1_0 || F == TQ2_0 || F == NVFP4_DIV) ? 8
+         : (F == Q5_0 || F == Q1_0 || F == Q2_0) ? 4
+         : 2;
+#endif
 }
 
 template <int F>
@@ -564,10 +688,12 @@ NQ_HD int choose_upt(uint64_t nunits, uint32_t resident) {
     return NQ_UPT;
 #else
     const uint64_t q = nunits / (resident ? resident : 1u);
+    int u;
     if constexpr (big_codebook<F>())
-        return q < 128 ? 1 : q < 256 ? 2 : q < 512 ? 4 : q < 1024 ? 8 : 16;
+        u = q < 128 ? 1 : q < 256 ? 2 : q < 512 ? 4 : q < 1024 ? 8 : 16;
     else
-        return q < 128 ? 1 : q < 1024 ? 2 : q < 2048 ? 4 : 8;
+        u = q < 128 ? 1 : q < 1024 ? 2 : q < 2048 ? 4 : 8;
+    return u < upt_max<F>() ? u : upt_max<F>();
 #endif
 }
 
@@ -581,7 +707,10 @@ template <int F, int OT, int UPT, bool VEC>
 int launch_chunk(const LaunchArgs &L, uint64_t b0, uint64_t nb, hipStream_t stream) {
     uint32_t grid;
     const KArgs a = chunk_args<F, OT, UPT>(L, b0, nb, &grid);
-    hipLaunchKernelGGL((k_decode<F, OT, UPT, VEC>), dim3(grid), dim3(WG), 0, stream, a);
+    if (F == NVFP4_DIV && a.ndiv > 1)
+        hipLaunchKernelGGL((k_decode<F, OT, UPT, VEC, F == NVFP4_DIV>), dim3(grid), dim3(WG), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_decode<F, OT, UPT, VEC, false>), dim3(grid), dim3(WG), 0, stream, a);
     return hipGetLastError() == hipSuccess ? 0 : 9;  // NQ_ERR_HIP
 }
 
@@ -618,6 +747,120 @@ int launch(const LaunchArgs &L, hipStream_t stream) {
         if (st != 0) return st;
     }
     return 0;
+}
+
+// One tensor of a many-tensor call: its payload, block count and output.
+struct ManyItem {
+    const uint8_t *payload;  // device
+    uint64_t nbytes;
+    uint64_t nblocks;
+    void *out;               // device, 16-byte aligned when VEC
+};
+
+// Entries of the launch chunk of item `it` that starts at block b0 (nb blocks).
+template <int F, int OT>
+NQ_HD MTensor many_entry(const ManyItem &it, uint64_t b0, uint64_t nb) {
+    LaunchArgs L;
+    L.payload = it.payload;
+    L.nbytes = it.nbytes;
+    L.nblocks = it.nblocks;
+    L.out = it.out;
+    L.resident = 0;
+    L.ndiv = 1;
+    L.gu = 1;
+    uint32_t grid;
+    const KArgs a = chunk_args<F, OT, 1>(L, b0, nb, &grid);
+    MTensor e;
+    e.base = a.base;
+    e.tr_base = a.tr_base;
+    e.out = a.out;
+    e.mis = a.mis;
+    e.last = a.last;
+    e.tr_mis = a.tr_mis;
+    e.tr_last = a.tr_last;
+    e.nunits = a.nunits;
+    e.tile0 = 0;
+    return e;
+}
+
+// Tiles of each entry for UPT units per thread, numbered from 0; false if the
+// launch would pass 2^31 - 1 workgroups.
+template <int UPT>
+NQ_HD bool many_number_tiles(MArgs &m) {
+    uint64_t t = 0;
+    for (uint32_t j = 0; j < m.n; j++) {
+        m.t[j].tile0 = (uint32_t)t;
+        t += (m.t[j].nunits + (uint64_t)WG * UPT - 1) / ((uint64_t)WG * UPT);
+        if (t > 0x7FFFFFFFull) return false;
+    }
+    m.ntiles = (uint32_t)t;
+    return true;
+}
+
+template <int F, int OT, int UPT, bool VEC>
+int launch_many_chunk(MArgs &m, hipStream_t stream) {
+    if (!many_number_tiles<UPT>(m)) return 9;  // NQ_ERR_HIP: cannot be launched as one grid
+    hipLaunchKernelGGL((k_decode_many<F, OT, UPT, VEC>), dim3(m.ntiles), dim3(WG), 0, stream, m);
+    return hipGetLastError() == hipSuccess ? 0 : 9;
+}
+
+// Launches of `n` non-empty tensors of format F to output type OT: entries
+// are packed MANY_MAX to a launch (a tensor larger than one launch chunk
+// takes several entries), and go(m, upt) receives each launch's arguments
+// with its units per thread.  The tile size follows the units of each launch
+// as for one tensor (choose_upt), limited to 2, 4 and 8 units per thread
+// (1 becomes 2, 16 becomes 8).  VEC: every output
+// is 16-byte aligned (otherwise, and for f64 outputs, always 8).  CB: blocks
+// per launch chunk (chunk_blocks<F>(); smaller in the emulator).  Host code
+// shared by the launcher and the emulator.
+template <int F, int OT, bool VEC, class Go>
+int many_plan(const ManyItem *items, int n, uint32_t resident, uint64_t CB, Go &&go) {
+    MArgs m;
+    m.n = 0;
+    m.ntiles = 0;
+    uint64_t units = 0;
+    auto flush = [&]() -> int {
+        if (m.n == 0) return 0;
+        const int c = choose_upt<F>(units, resident);
+        const int upt = (VEC && OT != 3) ? (c <= 2 ? 2 : c == 4 ? 4 : 8) : 8;
+        const int st = go(m, upt);
+        m.n = 0;
+        units = 0;
+        return st;
+    };
+    for (int i = 0; i < n; i++) {
+        for (uint64_t b0 = 0; b0 < items[i].nblocks; b0 += CB) {
+            const uint64_t nb = items[i].nblocks - b0 < CB ? items[i].nblocks - b0 : CB;
+            if (m.n == (uint32_t)MANY_MAX) {
+                const int st = flush();
+                if (st != 0) return st;
+            }
+            m.t[m.n++] = many_entry<F, OT>(items[i], b0, nb);
+            units += nb * (block_values(F) / 8);
+        }
+    }
+    return flush();
+}
+
+template <int F, int OT, bool VEC>
+int launch_many(const ManyItem *items, int n, uint32_t resident, hipStream_t stream) {
+    return many_plan<F, OT, VEC>(items, n, resident, chunk_blocks<F>(), [&](MArgs &m, int upt) -> int {
+        if constexpr (VEC && OT != 3) {
+            if (upt == 2) return launch_many_chunk<F, OT, 2, VEC>(m, stream);
+            if (upt == 4) return launch_many_chunk<F, OT, 4, VEC>(m, stream);
+        }
+        return launch_many_chunk<F, OT, 8, VEC>(m, stream);
+    });
+}
+
+template <int F>
+int launch_many_any(int ot, bool vec, const ManyItem *items, int n, uint32_t resident, hipStream_t stream) {
+    switch (ot) {
+    case 0: return vec ? launch_many<F, 0, true>(items, n, resident, stream) : launch_many<F, 0, false>(items, n, resident, stream);
+    case 1: return vec ? launch_many<F, 1, true>(items, n, resident, stream) : launch_many<F, 1, false>(items, n, resident, stream);
+    case 2: return vec ? launch_many<F, 2, true>(items, n, resident, stream) : launch_many<F, 2, false>(items, n, resident, stream);
+    default: return vec ? launch_many<F, 3, true>(items, n, resident, stream) : launch_many<F, 3, false>(items, n, resident, stream);
+    }
 }
 
 template <int F>

@@ -27,19 +27,21 @@ extern "C" {
 #endif
 
 /* Status codes.  Every metadata error is detected on the host before any
- * launch, so a failed call has written nothing. */
+ * launch, so a call failing with any status but NQ_ERR_HIP has written
+ * nothing (NQ_ERR_HIP: see nq_dequantize_packed). */
 typedef enum {
     NQ_OK = 0,
     NQ_ERR_NULL_ARG = 1,          /* a required pointer is NULL */
     NQ_ERR_UNKNOWN_FORMAT = 2,    /* name or id outside the closed registry */
     NQ_ERR_BAD_RANK = 3,          /* rank < 1 */
-    NQ_ERR_BAD_DIM = 4,           /* a negative dimension */
+    NQ_ERR_BAD_DIM = 4,           /* a negative dimension (or a count outside its range) */
     NQ_ERR_NOT_BLOCK_ALIGNED = 5, /* shape[rank-1] % B != 0 (also for empty tensors) */
     NQ_ERR_LENGTH_MISMATCH = 6,   /* nbytes differs from the length rule */
     NQ_ERR_OVERFLOW = 7,          /* byte count, or element count * 8, beyond INT64_MAX */
     NQ_ERR_BAD_DTYPE = 8,         /* out_dtype not one of nq_dtype */
     NQ_ERR_HIP = 9,               /* the HIP runtime reported an error at launch */
-    NQ_ERR_BAD_DIVISORS = 10      /* stacked nvfp4: divisors < 1, above 2^30, or not dividing the rows */
+    NQ_ERR_BAD_DIVISORS = 10,     /* stacked nvfp4: divisors < 1, above 2^30, or not dividing the rows */
+    NQ_ERR_MISALIGNED = 11        /* a pointer lacks the alignment the call requires */
 } nq_status;
 
 /* Output types: the page's FLOAT, FLOAT16, BFLOAT16 and DOUBLE. */
@@ -63,11 +65,14 @@ typedef struct {
     int32_t family;        /* nq_family */
 } nq_format_info;
 
-/* Number of registered formats (28). */
+/* Number of registered formats (28): the 27 identifiers of the
+ * DequantizePacked page's "Format identifiers" table and "nvfp4". */
 int nq_format_count(void);
 
-/* Registry entry by id.  NQ_ERR_NULL_ARG if out is NULL,
- * NQ_ERR_UNKNOWN_FORMAT if id is out of range. */
+/* Registry entry by id: ids 0..26 follow the order of the DequantizePacked
+ * page's "Format identifiers" table, id 27 is "nvfp4"; B and S are the
+ * page's "Quantization formats" block values and bytes.  NQ_ERR_NULL_ARG if
+ * out is NULL, NQ_ERR_UNKNOWN_FORMAT if id is out of range. */
 int nq_format_by_id(int32_t id, nq_format_info *out);
 
 /* Registry entry by identifier: exact, case-sensitive match of one of the
@@ -96,21 +101,56 @@ int nq_validate(int32_t format, uint64_t nbytes, const int64_t *shape, int32_t r
  *             dimension contiguous)
  *   out_dtype nq_dtype
  *   out       device pointer to prod(shape) elements of out_dtype, aligned to
- *             the element size; 16-byte alignment takes the vector-store path.
- *             May be NULL only if prod(shape) == 0.  Must not overlap payload.
+ *             the element size (else NQ_ERR_MISALIGNED); 16-byte alignment
+ *             takes the vector-store path.  May be NULL only if prod(shape)
+ *             == 0.  Must not overlap payload.
  *   stream    HIP stream (0 for the null stream)
  *
  * Element j of block i is out[i*B + j]: y = DequantizePacked(x) in the flat
  * row-major order of `shape`.  Ownership stays with the caller; nothing is
  * retained after return.  The call validates as nq_validate, returns NQ_OK
  * without launching for an empty tensor, and otherwise enqueues the decode
- * and returns NQ_OK, or NQ_ERR_HIP if the launch failed.  Payload bytes are
+ * and returns NQ_OK, or NQ_ERR_HIP if the launch failed.  A tensor of more
+ * than 2^30 units (8 values) or 2^32 payload bytes is decoded by several
+ * launches on `stream`; NQ_ERR_HIP from a later one leaves the earlier ones'
+ * outputs enqueued (written once the stream reaches them).  Payload bytes are
  * never inspected on the host: every byte pattern of the "gguf:" formats
  * decodes; for "nvfp4" only sign-zero finite E4M3FN scales and a finite
  * positive divisor are valid words (NInfer page, section 3.3), and other
  * words decode deterministically by the same formula. */
 int nq_dequantize_packed(int32_t format, const void *payload, uint64_t nbytes, const int64_t *shape,
                          int32_t rank, int32_t out_dtype, void *out, hipStream_t stream);
+
+/* One tensor of a many-tensor decode. */
+typedef struct {
+    int32_t format;         /* registry id */
+    int32_t rank;           /* >= 1 */
+    const int64_t *shape;   /* host array of `rank` dimensions */
+    const void *payload;    /* device, nbytes packed bytes, any alignment */
+    uint64_t nbytes;
+    void *out;              /* device, prod(shape) elements of the call's out_dtype */
+} nq_tensor;
+
+/* Decode `count` tensors to out_dtype on `stream`: the same output, bit for
+ * bit, as nq_dequantize_packed on each tensor in turn (DequantizePacked
+ * page, "Signature and storage"; a model's weight set is many such
+ * tensors), in fewer launches: the tensors of one format (and one output
+ * alignment class) share launches of up to 64 tensors each, so that small
+ * tensors fill the device together instead of one launch at a time.
+ *
+ * Every tensor is validated first, as nq_validate with out_dtype plus the
+ * pointer rules of nq_dequantize_packed (NULL payload with nbytes > 0 or
+ * NULL out with elements: NQ_ERR_NULL_ARG; out not element-aligned:
+ * NQ_ERR_MISALIGNED); on the first failure the call returns its status,
+ * stores its index in *failed (when failed is not NULL; -1 otherwise and on
+ * success) and launches nothing.  count < 0 is NQ_ERR_BAD_DIM, tensors NULL
+ * with count > 0 NQ_ERR_NULL_ARG, a bad out_dtype NQ_ERR_BAD_DTYPE; count ==
+ * 0 and empty tensors launch nothing.  No output may overlap another output
+ * or any payload.  NQ_ERR_HIP reports a failed launch; the launches before
+ * it stay enqueued.  The caller owns every buffer and the tensor array,
+ * which is not retained after return; nothing is allocated on the device. */
+int nq_dequantize_packed_many(const nq_tensor *tensors, int32_t count, int32_t out_dtype, int32_t *failed,
+                              hipStream_t stream);
 
 /* "nvfp4" planes stacked from several source matrices (NInfer
  * "tensor-formats" page, section 3.3): such a plane carries one binary32
@@ -155,7 +195,7 @@ int nq_dequantize_nvfp4_stacked(const void *payload, uint64_t nbytes, const int6
  * INT64_MAX (NQ_ERR_OVERFLOW), then nbytes.  nq_dequantize_fp8_row validates
  * the same way and then follows nq_dequantize_packed: asynchronous on
  * `stream`, payload of any alignment (NULL refused), `out` element-aligned
- * (16-byte alignment takes the vector stores), caller-owned buffers neither
+ * (NQ_ERR_MISALIGNED otherwise; 16-byte alignment takes the vector stores), caller-owned buffers neither
  * retained nor freed.  Code words 0x7F/0xFF (NaN) and refused scale words
  * (negative, non-finite) decode by the same formula. */
 typedef enum { NQ_FP8_ROW_BF16 = 0, NQ_FP8_ROW_FP16 = 1 } nq_fp8_row_scale;
@@ -189,8 +229,9 @@ int nq_dequantize_fp8_row(int32_t scale_kind, const void *payload, uint64_t nbyt
  * K < 2^31 and the byte counts within INT64_MAX (NQ_ERR_OVERFLOW); it stores
  * the byte sizes of codes and scales (either pointer may be NULL).
  * nq_quantize_grouped_absmax validates the same way, then requires x,
- * codes, scales and status non-NULL, x aligned to its element size, scales
- * to 2 bytes and status to 4 (NQ_ERR_NULL_ARG), and enqueues the encoder;
+ * codes, scales and status non-NULL (NQ_ERR_NULL_ARG), x aligned to its
+ * element size, scales to 2 bytes and status to 4 (NQ_ERR_MISALIGNED), and
+ * enqueues the encoder;
  * the caller owns every buffer.  x must not overlap the outputs. */
 typedef enum { NQ_GQ_Q4_G64 = 0, NQ_GQ_Q5_G64 = 1, NQ_GQ_Q6_G64 = 2, NQ_GQ_Q8_G32 = 3 } nq_grouped_scheme;
 
@@ -220,8 +261,9 @@ int nq_quantize_grouped_absmax(int32_t scheme, const void *x, const int64_t *sha
  * (NQ_ERR_BAD_RANK), shape (NQ_ERR_NULL_ARG), both dimensions > 0
  * (NQ_ERR_BAD_DIM), K % 32 (NQ_ERR_NOT_BLOCK_ALIGNED) and the byte counts
  * (NQ_ERR_OVERFLOW), and stores the blocks' byte size.  nq_quantize_q8_1
- * also requires x, blocks and status non-NULL, x aligned to its element size
- * and blocks and status to 4 bytes (NQ_ERR_NULL_ARG).  The caller owns every
+ * also requires x, blocks and status non-NULL (NQ_ERR_NULL_ARG), x aligned
+ * to its element size and blocks and status to 4 bytes (NQ_ERR_MISALIGNED).
+ * The caller owns every
  * buffer; x must not overlap the outputs.
  *
  * nq_gemv_q8_1: y[m*N + n] = sum_k w[n][k] * x[m][k] (binary32 output,
@@ -238,7 +280,8 @@ int nq_quantize_grouped_absmax(int32_t scheme, const void *x, const int64_t *sha
  * "nvfp4"), N, K > 0 and 1 <= M <= 8 (NQ_ERR_BAD_DIM), K % B
  * (NQ_ERR_NOT_BLOCK_ALIGNED), N, K < 2^31 (NQ_ERR_OVERFLOW) and nbytes
  * (NQ_ERR_LENGTH_MISMATCH).  nq_gemv_q8_1 also requires weight, xq and y
- * non-NULL and xq and y aligned to 4 bytes (NQ_ERR_NULL_ARG), then enqueues
+ * non-NULL (NQ_ERR_NULL_ARG) and xq and y aligned to 4 bytes
+ * (NQ_ERR_MISALIGNED), then enqueues
  * the product on `stream`.  The caller owns every buffer; y must not overlap
  * the inputs. */
 int nq_validate_quantize_q8_1(const int64_t *shape, int32_t rank, int32_t in_dtype, uint64_t *blocks_bytes);
@@ -274,8 +317,9 @@ int nq_gemv_q8_1(int32_t format, const void *weight, uint64_t nbytes, int64_t N,
  * (NQ_ERR_OVERFLOW).  nq_gemm_q8_1_workspace runs the same checks (nbytes
  * taken as the format's length rule) and stores the workspace size for the
  * shape on the current device (0 when the product would neither split K nor
- * rewrite the weight once; `bytes` NULL: NQ_ERR_NULL_ARG).  nq_gemm_q8_1 requires weight, xq and y non-NULL
- * and xq and y aligned to 4 bytes and workspace to 16 (NQ_ERR_NULL_ARG), then
+ * rewrite the weight once; `bytes` NULL: NQ_ERR_NULL_ARG).  nq_gemm_q8_1
+ * requires weight, xq and y non-NULL (NQ_ERR_NULL_ARG) and xq and y aligned
+ * to 4 bytes and workspace to 16 (NQ_ERR_MISALIGNED), then
  * enqueues the product on `stream`.  The caller owns every buffer; y must not
  * overlap the inputs. */
 int nq_validate_gemm_q8_1(int32_t format, uint64_t nbytes, int64_t N, int64_t K, int64_t M);
@@ -283,7 +327,9 @@ int nq_gemm_q8_1_workspace(int32_t format, int64_t N, int64_t K, int64_t M, uint
 int nq_gemm_q8_1(int32_t format, const void *weight, uint64_t nbytes, int64_t N, int64_t K, const void *xq,
                  int64_t M, float *y, void *workspace, uint64_t workspace_bytes, hipStream_t stream);
 
-/* Static description of a status code. */
+/* Static description of a status code (the nq_status values above; other
+ * values give "unknown status").  The pages define no status codes: these
+ * are the library's names for the failures its checks detect. */
 const char *nq_status_string(int status);
 
 #ifdef __cplusplus

@@ -39,6 +39,8 @@ struct HostSrc {
         for (int k = 0; k < N; k++) r[k] = dw(i + (uint32_t)k);
     }
     void load_stream4(uint32_t i, uint32_t (&r)[4]) const { load<4>(i, r); }
+    template <bool NT>
+    void load4(uint32_t i, uint32_t (&r)[4]) const { load<4>(i, r); }
     uint32_t dwx(uint32_t i) const { return dw(i < last ? i : last); }
     uint32_t dw(uint32_t i) const {
         const uintptr_t a = (uintptr_t)(base + i);
@@ -51,31 +53,30 @@ struct HostSrc {
     }
 };
 
-// One launch chunk with UPT units per thread, as the kernel runs it: one
-// workgroup per tile; a staged tile is copied into the LDS slot by every
-// thread, then decoded by every thread (the barrier); other tiles are
-// decoded from the payload directly.
+// The kernel's work on one tile, run thread by thread: the prologue (the
+// divisor group of the tile's first unit and the tables; stale divisor slots
+// poisoned), then for a staged tile every thread's staging into the LDS slot
+// (with guard words past it) and every thread's decode (the barrier between),
+// for other tiles every thread's decode from the payload.
 template <int F, int OT, int UPT>
-long run_chunk(const nq::LaunchArgs &L, uint64_t b0, uint64_t nb, const uint8_t *payload, uint64_t nbytes,
-               char *err, int errlen) {
-    using namespace nq;
-    constexpr uint64_t S = block_bytes(F);
-    using TS = TabSpec<F>;
-    using ST = Stage<F, UPT>;
-    std::vector<uint64_t> t8(TS::n8 > 0 ? TS::n8 : 1);
-    std::vector<uint32_t> t4(TS::n4 > 0 ? TS::n4 : 1);
-    std::vector<float> nvq(TS::nf > 0 ? TS::nf : 1);
-    std::vector<float> nvd(TS::nd > 0 ? TS::nd : 1);
-    uint32_t grid;
-    const KArgs a = chunk_args<F, OT, UPT>(L, b0, nb, &grid);
-    Check chk{(uintptr_t)(payload + b0 * S), (uintptr_t)(payload + (b0 + nb) * S), 0, {0}};
-    Check chk_tr{(uintptr_t)(payload + nbytes - 4ull * L.ndiv), (uintptr_t)(payload + nbytes), 0, {0}};
-    const HostSrc tr{a.tr_base, a.tr_last, &chk_tr};
-    // per tile (the kernel's prologue): the divisor group of the tile's first
-    // unit, and the tables; stale divisor slots are poisoned
-    auto setup = [&](uint32_t t, Tab &tab) {
+struct EmuTiles {
+    using TS = nq::TabSpec<F>;
+    using ST = nq::Stage<F, UPT>;
+    static constexpr uint32_t GUARD = 64, GUARD_WORD = 0x5A5A5A5Au;
+    std::vector<uint64_t> t8 = std::vector<uint64_t>(TS::n8 > 0 ? TS::n8 : 1);
+    std::vector<uint32_t> t4 = std::vector<uint32_t>(TS::n4 > 0 ? TS::n4 : 1);
+    std::vector<float> nvq = std::vector<float>(TS::nf > 0 ? TS::nf : 1);
+    std::vector<float> nvd = std::vector<float>(TS::nd > 0 ? TS::nd : 1);
+    std::vector<uint32_t> slot = std::vector<uint32_t>(ST::SLOT_DW + GUARD);
+    long lds_errors = 0;
+
+    void tile(const nq::KArgs &a, uint32_t t, Check &chk, Check &chk_tr) {
+        using namespace nq;
+        const HostSrc tr{a.tr_base, a.tr_last, &chk_tr};
+        const HostSrc src{a.base, a.last, &chk};
+        const bool vec = ((uintptr_t)a.out & 15) == 0;
         uint32_t g0 = 0;
-        tab = Tab{t8.data(), t4.data(), nvq.data(), nvd.data(), 0xFFFFFFFFu, 1u};
+        Tab tab{t8.data(), t4.data(), nvq.data(), nvd.data(), 0xFFFFFFFFu, 1u};
         if constexpr (F == NVFP4_DIV) {
             g0 = nv_first_group<UPT>(a, t, &tab.nv_bound);
             tab.nv_gu = a.gu < 0x7FFFFFFFull ? (uint32_t)a.gu : 0x7FFFFFFFu;
@@ -84,22 +85,7 @@ long run_chunk(const nq::LaunchArgs &L, uint64_t b0, uint64_t nb, const uint8_t 
         if (TS::n8 + TS::n4 + TS::nf > 0)
             for (uint32_t tid = 0; tid < (uint32_t)WG; tid++)
                 fill_tables<F>(t8.data(), t4.data(), nvq.data(), nvd.data(), tr, a, g0, tid, WG);
-    };
-    Tab tab{};
-    const HostSrc src{a.base, a.last, &chk};
-    const bool vec = ((uintptr_t)a.out & 15) == 0;
-    // the LDS slot plus guard words that staging must leave alone
-    constexpr uint32_t GUARD = 64, GUARD_WORD = 0x5A5A5A5Au;
-    std::vector<uint32_t> slot(ST::SLOT_DW + GUARD);
-    long lds_errors = 0;
-    const uint32_t nst = staged_tiles<F, UPT>(a);
-    if (grid != (a.nunits + ST::PER - 1) / ST::PER) {
-        snprintf(err, errlen, "grid %u is not one workgroup per tile", grid);
-        return 1;
-    }
-    for (uint32_t t = 0; t < grid; t++) {
-        setup(t, tab);
-        if (t < nst) {
+        if (t < staged_tiles<F, UPT>(a)) {
             std::fill(slot.begin(), slot.begin() + ST::SLOT_DW, 0xA5A5A5A5u);  // stale words poison the result
             std::fill(slot.begin() + ST::SLOT_DW, slot.end(), GUARD_WORD);
             for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) {
@@ -125,6 +111,9 @@ long run_chunk(const nq::LaunchArgs &L, uint64_t b0, uint64_t nb, const uint8_t 
             }
         }
     }
+};
+
+long report(Check &chk, Check &chk_tr, long lds_errors, char *err, int errlen) {
     long errors = 0;
     chk.errors += lds_errors;
     for (Check *c : {&chk, &chk_tr})
@@ -133,6 +122,114 @@ long run_chunk(const nq::LaunchArgs &L, uint64_t b0, uint64_t nb, const uint8_t 
             errors += c->errors;
         }
     return errors;
+}
+
+// One launch chunk with UPT units per thread, as the kernel runs it: one
+// workgroup per tile.
+template <int F, int OT, int UPT>
+long run_chunk(const nq::LaunchArgs &L, uint64_t b0, uint64_t nb, const uint8_t *payload, uint64_t nbytes,
+               char *err, int errlen) {
+    using namespace nq;
+    constexpr uint64_t S = block_bytes(F);
+    using ST = Stage<F, UPT>;
+    uint32_t grid;
+    const KArgs a = chunk_args<F, OT, UPT>(L, b0, nb, &grid);
+    Check chk{(uintptr_t)(payload + b0 * S), (uintptr_t)(payload + (b0 + nb) * S), 0, {0}};
+    Check chk_tr{(uintptr_t)(payload + nbytes - 4ull * L.ndiv), (uintptr_t)(payload + nbytes), 0, {0}};
+    if (grid != (a.nunits + ST::PER - 1) / ST::PER) {
+        snprintf(err, errlen, "grid %u is not one workgroup per tile", grid);
+        return 1;
+    }
+    EmuTiles<F, OT, UPT> emu;
+    for (uint32_t t = 0; t < grid; t++) emu.tile(a, t, chk, chk_tr);
+    return report(chk, chk_tr, emu.lds_errors, err, errlen);
+}
+
+// A many-tensor launch as the kernel runs it: every workgroup b of the grid
+// finds its entry with the kernel's search and decodes that entry's tile
+// b - tile0, its reads checked against that entry's payload bytes (and
+// divisor).  Also checks that the search lands on the entry whose tiles hold
+// b, and that the grid is the sum of the entries' tiles.
+template <int F, int OT, int UPT>
+long run_many_launch(const nq::MArgs &m, char *err, int errlen) {
+    using namespace nq;
+    constexpr uint64_t S = block_bytes(F), UPB = block_values(F) / 8;
+    using ST = Stage<F, UPT>;
+    EmuTiles<F, OT, UPT> emu;
+    long errors = 0;
+    uint64_t tiles = 0;
+    for (uint32_t j = 0; j < m.n; j++) tiles += (m.t[j].nunits + ST::PER - 1) / ST::PER;
+    if (tiles != m.ntiles || m.n == 0 || m.t[0].tile0 != 0) {
+        snprintf(err, errlen, "grid %u for %llu tiles of %u entries", m.ntiles, (unsigned long long)tiles, m.n);
+        return 1;
+    }
+    for (uint32_t b = 0; b < m.ntiles; b++) {
+        const uint32_t j = many_find(m, b);
+        const uint32_t end = j + 1 < m.n ? m.t[j + 1].tile0 : m.ntiles;
+        if (b < m.t[j].tile0 || b >= end) {
+            snprintf(err, errlen, "tile %u found entry %u with tiles [%u, %u)", b, j, m.t[j].tile0, end);
+            return 1;
+        }
+        const KArgs a = many_entry_args(m.t[j]);
+        const uintptr_t lo = (uintptr_t)a.base + a.mis, trlo = (uintptr_t)a.tr_base + a.tr_mis;
+        Check chk{lo, lo + (uint64_t)a.nunits / UPB * S, 0, {0}};
+        Check chk_tr{trlo, trlo + (F == NVFP4_DIV ? 4u : 0u), 0, {0}};
+        const long lds_before = emu.lds_errors;
+        emu.tile(a, b - m.t[j].tile0, chk, chk_tr);
+        const long e = report(chk, chk_tr, emu.lds_errors - lds_before, err, errlen);
+        if (e && errors == 0) errors = e;
+        else errors += e;
+    }
+    return errors;
+}
+
+// The many-tensor launcher's packing (many_plan) and every launch it makes.
+// *launches_out: launches made; *upt_mask: bit u set when a launch took u
+// units per thread.
+template <int F, int OT>
+long run_many(const nq::ManyItem *items, int n, uint32_t resident, uint64_t chunk, int *launches_out, int *upt_mask,
+              char *err, int errlen) {
+    using namespace nq;
+    long errors = 0;
+    *launches_out = 0;
+    *upt_mask = 0;
+    auto go = [&](MArgs &m, int upt) -> int {
+        (*launches_out)++;
+        *upt_mask |= 1 << upt;
+        long e;
+        if (upt == 2) {
+            if (!many_number_tiles<2>(m)) return 9;
+            e = run_many_launch<F, OT, 2>(m, err, errlen);
+        } else if (upt == 4) {
+            if (!many_number_tiles<4>(m)) return 9;
+            e = run_many_launch<F, OT, 4>(m, err, errlen);
+        } else {
+            if (!many_number_tiles<8>(m)) return 9;
+            e = run_many_launch<F, OT, 8>(m, err, errlen);
+        }
+        errors += e;
+        return 0;
+    };
+    const bool vec = n > 0 && ((uintptr_t)items[0].out & 15) == 0;
+    const uint64_t cb = chunk ? chunk : chunk_blocks<F>();
+    const int st = vec ? many_plan<F, OT, true>(items, n, resident, cb, go)
+                       : many_plan<F, OT, false>(items, n, resident, cb, go);
+    if (st != 0) {
+        snprintf(err, errlen, "launch plan failed with status %d", st);
+        return 1;
+    }
+    return errors;
+}
+
+template <int F>
+long run_many_ot(int ot, const nq::ManyItem *items, int n, uint32_t resident, uint64_t chunk, int *launches,
+                 int *upt_mask, char *err, int errlen) {
+    switch (ot) {
+    case 0: return run_many<F, 0>(items, n, resident, chunk, launches, upt_mask, err, errlen);
+    case 1: return run_many<F, 1>(items, n, resident, chunk, launches, upt_mask, err, errlen);
+    case 2: return run_many<F, 2>(items, n, resident, chunk, launches, upt_mask, err, errlen);
+    default: return run_many<F, 3>(items, n, resident, chunk, launches, upt_mask, err, errlen);
+    }
 }
 
 // The launcher's chunk loop and per-chunk choice of units per thread
@@ -564,6 +661,9 @@ using EmuGemm = long (*)(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t
                          uint64_t max_rows, uint64_t max_mrows, uint32_t cus, uint32_t *nsplit, char *err,
                          int errlen);
 extern EmuGemm nq_emu_gemm_table[nq::NUM_FORMATS];
+using EmuMany = long (*)(int ot, const nq::ManyItem *items, int n, uint32_t resident, uint64_t chunk, int *launches,
+                         int *upt_mask, char *err, int errlen);
+extern EmuMany nq_emu_many_table[nq::NUM_FORMATS];
 
 #if defined(NQ_EMU_PART)
 namespace {
@@ -571,6 +671,7 @@ template <int F>
 void reg() {
     if constexpr (F % NQ_EMU_PARTS == NQ_EMU_PART) {
         nq_emu_table[F] = &run_ot<F>;
+        nq_emu_many_table[F] = &run_many_ot<F>;
         if constexpr (F != nq::NVFP4_DIV) nq_emu_gemv_table[F] = &run_gemv_m<F>;
         if constexpr (nq::GmFmt<F>::OK) nq_emu_gemm_table[F] = &run_gemm<F>;
     }
@@ -589,6 +690,25 @@ struct Register {
 EmuRun nq_emu_table[nq::NUM_FORMATS];
 EmuGemv nq_emu_gemv_table[nq::NUM_FORMATS];
 EmuGemm nq_emu_gemm_table[nq::NUM_FORMATS];
+EmuMany nq_emu_many_table[nq::NUM_FORMATS];
+
+// Many-tensor decode of n tensors of one format (payload, nbytes, blocks and
+// output of each; all outputs 16-byte aligned or none), through the
+// launcher's packing (chunk: blocks per launch chunk, 0 for the library's)
+// and the kernel's tile search; returns out-of-payload reads and mapping
+// errors (0 on success), or -1 for a bad format.
+extern "C" __attribute__((visibility("default"))) long nq_emu_decode_many(int fmt, int ot, int n,
+                                                                         const uint8_t *const *payloads,
+                                                                         const uint64_t *nbytes,
+                                                                         const uint64_t *nblocks, void *const *outs,
+                                                                         uint32_t resident, uint64_t chunk,
+                                                                         int *launches, int *upt_mask, char *err,
+                                                                         int errlen) {
+    if (fmt < 0 || fmt >= nq::NUM_FORMATS || !nq_emu_many_table[fmt] || n < 0) return -1;
+    std::vector<nq::ManyItem> items((size_t)n);
+    for (int i = 0; i < n; i++) items[(size_t)i] = nq::ManyItem{payloads[i], nbytes[i], nblocks[i], outs[i]};
+    return nq_emu_many_table[fmt](ot, items.data(), n, resident, chunk, launches, upt_mask, err, errlen);
+}
 
 // Batched product on the matrix cores through the kernel's lane code;
 // returns out-of-payload weight reads (0 on success), or -1 for a format

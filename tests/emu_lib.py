@@ -62,6 +62,11 @@ def lib():
                                     ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64,
                                     ctypes.c_int, ctypes.c_uint32, ctypes.c_char_p, ctypes.c_int]
         L.nq_emu_decode.restype = ctypes.c_long
+        L.nq_emu_decode_many.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64,
+                                         ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                                         ctypes.c_char_p, ctypes.c_int]
+        L.nq_emu_decode_many.restype = ctypes.c_long
         L.nq_emu_tile_blocks.argtypes = [ctypes.c_int, ctypes.c_int]
         L.nq_emu_fp8_row.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64,
                                      ctypes.c_void_p, ctypes.c_uint64, ctypes.c_char_p, ctypes.c_int]
@@ -119,6 +124,52 @@ def decode(fmt_id, payload, nblocks, B, dtype, mis=0, out_mis=0, max_wgs=2048, c
     guards = bool(np.all(obuf[:ooff] == 0xA5) and np.all(obuf[ooff + n * osz:] == 0xA5))
     vals = obuf[ooff:ooff + n * osz].copy().view(NPT[dtype])
     return vals, rc, err.value.decode(), guards
+
+
+def decode_many(fmt_id, payloads, B, dtype, vec=True, resident=2048, chunk=0, mis=0):
+    """Many-tensor decode of payloads (one format; each payload whole blocks plus
+    its trailer) through the emulator.  Outputs are 16-byte aligned (vec) or
+    shifted by one element.  Returns (values per tensor, errors, message,
+    guards_ok, launches, set of units-per-thread taken)."""
+    osz = OSIZE[dtype]
+    bufs, outs, pptr, nbytes, nblocks, optr = [], [], [], [], [], []
+    info = _format(fmt_id)
+    T = info.trailer_bytes
+    for k, p in enumerate(payloads):
+        p = np.ascontiguousarray(p, dtype=np.uint8)
+        pb, po = _placed(p.size, 4, (mis + k) % 4)
+        pb[:] = 0xEE
+        pb[po:po + p.size] = p
+        nb = (p.size - T) // info.block_bytes
+        n = nb * B
+        ob, oo = _placed(n * osz, 16, 0 if vec else osz)
+        ob[:] = 0xA5
+        bufs.append((pb, po))
+        outs.append((ob, oo, n))
+        pptr.append(pb.ctypes.data + po)
+        nbytes.append(p.size)
+        nblocks.append(nb)
+        optr.append(ob.ctypes.data + oo)
+    cnt = len(payloads)
+    arr_p = (ctypes.c_void_p * max(1, cnt))(*pptr)
+    arr_nb = (ctypes.c_uint64 * max(1, cnt))(*nbytes)
+    arr_bl = (ctypes.c_uint64 * max(1, cnt))(*nblocks)
+    arr_o = (ctypes.c_void_p * max(1, cnt))(*optr)
+    err = ctypes.create_string_buffer(256)
+    launches, mask = ctypes.c_int(0), ctypes.c_int(0)
+    rc = lib().nq_emu_decode_many(fmt_id, {"f32": 0, "f16": 1, "bf16": 2, "f64": 3}[dtype], cnt, arr_p, arr_nb,
+                                  arr_bl, arr_o, resident, chunk, ctypes.byref(launches), ctypes.byref(mask), err, 256)
+    vals, guards = [], True
+    for ob, oo, n in outs:
+        guards &= bool(np.all(ob[:oo] == 0xA5) and np.all(ob[oo + n * osz:] == 0xA5))
+        vals.append(ob[oo:oo + n * osz].copy().view(NPT[dtype]))
+    upts = {u for u in (1, 2, 4, 8, 16) if mask.value >> u & 1}
+    return vals, rc, err.value.decode(), guards, launches.value, upts
+
+
+def _format(fmt_id):
+    import block_quantized_weight_nq_amd as nq
+    return nq.format_by_id(fmt_id)
 
 
 def tile_blocks(fmt_id, upt):

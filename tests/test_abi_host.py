@@ -15,11 +15,12 @@ import block_quantized_weight_nq_amd as nq
 import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "nq.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 def _declared():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(nq_\w+)\s*\(", text, re.M)))
 
 
@@ -95,7 +96,7 @@ def test_dequantize_rejects_bad_metadata_without_device():
     assert nq.dequantize_packed_raw(fid, p, 34, [32], 0, 0, 0) == 1
     assert nq.dequantize_packed_raw(99, p, 34, [32], 0, p, 0) == 2
     # an element-misaligned output is refused before launch
-    assert nq.dequantize_packed_raw(fid, p, 34, [32], 0, p + 2, 0) == 1
+    assert nq.dequantize_packed_raw(fid, p, 34, [32], 0, p + 2, 0) == 11
     # empty tensors succeed without launching (null pointers allowed)
     assert nq.dequantize_packed_raw(fid, 0, 0, [0, 32], 0, 0, 0) == 0
     nv = nq.format_query("nvfp4").id
@@ -147,7 +148,7 @@ def test_nvfp4_stacked_rejects_before_device():
     assert nq.dequantize_nvfp4_stacked_raw(p, 12 * 2 * 36 + 8, [12, 128], 2, 7, p, 0) == 8
     assert nq.dequantize_nvfp4_stacked_raw(0, 12 * 2 * 36 + 8, [12, 128], 2, 2, p, 0) == 1
     assert nq.dequantize_nvfp4_stacked_raw(p, 12 * 2 * 36 + 8, [12, 128], 2, 2, 0, 0) == 1
-    assert nq.dequantize_nvfp4_stacked_raw(p, 12 * 2 * 36 + 8, [12, 128], 2, 2, p + 1, 0) == 1
+    assert nq.dequantize_nvfp4_stacked_raw(p, 12 * 2 * 36 + 8, [12, 128], 2, 2, p + 1, 0) == 11   # bf16 output misaligned
     # empty planes succeed without launching (null pointers allowed when nothing is read or written)
     assert nq.dequantize_nvfp4_stacked_raw(p, 12, [6, 0], 3, 2, 0, 0) == 0
     assert nq.dequantize_nvfp4_stacked_raw(0, 0, [6, 0], 3, 2, 0, 0) == 6
@@ -179,7 +180,7 @@ def test_fp8_row_rejects_before_device():
     assert nq.dequantize_fp8_row_raw(0, p, 20, [3, 5], 0, p, 0) == 6
     assert nq.dequantize_fp8_row_raw(0, 0, 21, [3, 5], 0, p, 0) == 1
     assert nq.dequantize_fp8_row_raw(0, p, 21, [3, 5], 0, 0, 0) == 1
-    assert nq.dequantize_fp8_row_raw(0, p, 21, [3, 5], 0, p + 2, 0) == 1   # f32 output not element-aligned
+    assert nq.dequantize_fp8_row_raw(0, p, 21, [3, 5], 0, p + 2, 0) == 11   # f32 output not element-aligned
     assert nq.dequantize_fp8_row_raw(1, p, 21, [15], 0, p, 0) == 3
     assert nq.dequantize_fp8_row_raw(1, p, 0, [0, 5], 0, p, 0) == 4
 
@@ -202,9 +203,9 @@ def test_grouped_absmax_rejects_before_device():
     p = buf.ctypes.data
     assert nq.quantize_grouped_absmax_raw(0, 0, [2, 8], 0, p, p, p, 0) == 1
     assert nq.quantize_grouped_absmax_raw(0, p, [2, 8], 0, p, p, 0, 0) == 1
-    assert nq.quantize_grouped_absmax_raw(0, p + 2, [2, 8], 0, p, p, p, 0) == 1   # f32 source misaligned
-    assert nq.quantize_grouped_absmax_raw(0, p, [2, 8], 0, p, p + 1, p, 0) == 1   # scales misaligned
-    assert nq.quantize_grouped_absmax_raw(0, p, [2, 8], 0, p, p, p + 2, 0) == 1   # status misaligned
+    assert nq.quantize_grouped_absmax_raw(0, p + 2, [2, 8], 0, p, p, p, 0) == 11   # f32 source misaligned
+    assert nq.quantize_grouped_absmax_raw(0, p, [2, 8], 0, p, p + 1, p, 0) == 11   # scales misaligned
+    assert nq.quantize_grouped_absmax_raw(0, p, [2, 8], 0, p, p, p + 2, 0) == 11   # status misaligned
     assert nq.quantize_grouped_absmax_raw(4, p, [2, 8], 0, p, p, p, 0) == 2
 
 
@@ -225,9 +226,9 @@ def test_quantize_q8_1_rejects_before_device():
     assert nq.quantize_q8_1_raw(0, [2, 32], 0, p, p, 0) == 1
     assert nq.quantize_q8_1_raw(p, [2, 32], 0, 0, p, 0) == 1
     assert nq.quantize_q8_1_raw(p, [2, 32], 0, p, 0, 0) == 1
-    assert nq.quantize_q8_1_raw(p + 2, [2, 32], 0, p, p, 0) == 1   # f32 source misaligned
-    assert nq.quantize_q8_1_raw(p, [2, 32], 0, p + 2, p, 0) == 1   # blocks misaligned
-    assert nq.quantize_q8_1_raw(p, [2, 32], 0, p, p + 1, 0) == 1   # status misaligned
+    assert nq.quantize_q8_1_raw(p + 2, [2, 32], 0, p, p, 0) == 11   # f32 source misaligned
+    assert nq.quantize_q8_1_raw(p, [2, 32], 0, p + 2, p, 0) == 11   # blocks misaligned
+    assert nq.quantize_q8_1_raw(p, [2, 32], 0, p, p + 1, 0) == 11   # status misaligned
     assert nq.quantize_q8_1_raw(p, [2, 33], 0, p, p, 0) == 5
     assert nq.quantize_q8_1_raw(p, [2, 32], 9, p, p, 0) == 8
 
@@ -256,8 +257,8 @@ def test_gemv_rejects_before_device():
     assert nq.gemv_q8_1_raw(q8, 0, 34, 1, 32, p, 1, p, 0) == 1
     assert nq.gemv_q8_1_raw(q8, p, 34, 1, 32, 0, 1, p, 0) == 1
     assert nq.gemv_q8_1_raw(q8, p, 34, 1, 32, p, 1, 0, 0) == 1
-    assert nq.gemv_q8_1_raw(q8, p, 34, 1, 32, p + 2, 1, p, 0) == 1   # activation blocks misaligned
-    assert nq.gemv_q8_1_raw(q8, p, 34, 1, 32, p, 1, p + 2, 0) == 1   # output misaligned
+    assert nq.gemv_q8_1_raw(q8, p, 34, 1, 32, p + 2, 1, p, 0) == 11   # activation blocks misaligned
+    assert nq.gemv_q8_1_raw(q8, p, 34, 1, 32, p, 1, p + 2, 0) == 11   # output misaligned
     assert nq.gemv_q8_1_raw(q8, p, 35, 1, 32, p, 1, p, 0) == 6
 
 
@@ -290,10 +291,10 @@ def test_gemm_rejects_before_device():
     assert nq.gemm_q8_1_raw(q8, 0, 34, 1, 32, p, 9, p, 0, 0, 0) == 1
     assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, 0, 9, p, 0, 0, 0) == 1
     assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, p, 9, 0, 0, 0, 0) == 1
-    assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, p + 2, 9, p, 0, 0, 0) == 1   # activation blocks misaligned
-    assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, p, 9, p + 2, 0, 0, 0) == 1   # output misaligned
+    assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, p + 2, 9, p, 0, 0, 0) == 11   # activation blocks misaligned
+    assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, p, 9, p + 2, 0, 0, 0) == 11   # output misaligned
     assert nq.gemm_q8_1_raw(q8, p, 35, 1, 32, p, 9, p, 0, 0, 0) == 6
-    assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, p, 9, p, p + 8, 64, 0) == 1   # workspace not 16-byte aligned
+    assert nq.gemm_q8_1_raw(q8, p, 34, 1, 32, p, 9, p, p + 8, 64, 0) == 11   # workspace not 16-byte aligned
 
 
 def test_gemm_workspace_sizes():
@@ -324,3 +325,59 @@ def test_gemm_workspace_sizes():
     assert nq.gemm_q8_1_workspace("gguf:q8_0", 32768, 1024, 257) == (0, 33554432 + 4194304)
     assert nq.gemm_q8_1_workspace("nvfp4", 1, 64, 9)[0] == 2
     assert nq.gemm_q8_1_workspace("gguf:q4_k", 1, 100, 9)[0] == 5
+
+
+def test_status_strings_name_every_status():
+    L = nq.library()
+    for st, name in nq.STATUS_NAMES.items():
+        text = L.nq_status_string(st).decode()
+        assert text and text != "unknown status", (st, name)
+    assert L.nq_status_string(12).decode() == "unknown status"
+    assert "NULL" in L.nq_status_string(1).decode() and "align" in L.nq_status_string(11).decode()
+
+
+def test_many_tensor_decode_rejects_before_device():
+    """nq_dequantize_packed_many validates every tensor first and names the
+    first failing one; none of these calls reaches a launch."""
+    buf = np.zeros(256, dtype=np.uint32)
+    p = buf.ctypes.data
+    q4k, q8, nv = (nq.format_query(f).id for f in ("gguf:q4_k", "gguf:q8_0", "nvfp4"))
+    L = nq.library()
+    failed = ctypes.c_int32(5)
+    assert L.nq_dequantize_packed_many(None, 0, 2, ctypes.byref(failed), None) == 0 and failed.value == -1
+    assert L.nq_dequantize_packed_many(None, -1, 2, ctypes.byref(failed), None) == 4
+    assert L.nq_dequantize_packed_many(None, 3, 2, ctypes.byref(failed), None) == 1
+    assert L.nq_dequantize_packed_many(None, 1, 2, None, None) == 1
+    assert nq.dequantize_packed_many_raw([], 2, 0) == (0, -1)
+    ok = (q4k, p, 144, [256], p)
+    assert nq.dequantize_packed_many_raw([ok], 4, 0) == (8, -1)                         # bad dtype
+    assert nq.dequantize_packed_many_raw([ok, (q4k, p, 145, [256], p)], 2, 0) == (6, 1)  # length rule
+    assert nq.dequantize_packed_many_raw([ok, ok, (99, p, 34, [32], p)], 2, 0) == (2, 2)
+    assert nq.dequantize_packed_many_raw([ok, (q8, p, 34, [31], p)], 2, 0) == (5, 1)
+    assert nq.dequantize_packed_many_raw([(q8, p, 34, [-1, 32], p)], 2, 0) == (4, 0)
+    assert nq.dequantize_packed_many_raw([(q8, 0, 34, [32], p)], 2, 0) == (1, 0)        # NULL payload
+    assert nq.dequantize_packed_many_raw([(q8, p, 34, [32], 0)], 2, 0) == (1, 0)        # NULL out
+    assert nq.dequantize_packed_many_raw([(q8, p, 34, [32], p + 1)], 2, 0) == (11, 0)   # bf16 out misaligned
+    assert nq.dequantize_packed_many_raw([(q8, p, 34, [32], p + 2)], 0, 0) == (11, 0)   # f32 out misaligned
+    assert nq.dequantize_packed_many_raw([(nv, p, 40, [64], p + 4)], 3, 0) == (11, 0)  # f64 out misaligned
+    # empty tensors need no pointers; a failure after them is still reported by index
+    empty = (q4k, 0, 0, [0, 256], 0)
+    assert nq.dequantize_packed_many_raw([empty, empty, (nv, p, 4, [0, 64], 0), (nv, p, 3, [0, 64], 0)], 2, 0) \
+        == (6, 3)
+    assert nq.dequantize_packed_many_raw([empty, (nv, 0, 4, [5, 0], 0)], 2, 0) == (1, 1)   # trailer: payload needed
+
+
+def test_measure_stream_rejects_before_device():
+    buf = np.zeros(256, dtype=np.uint32)
+    p = (buf.ctypes.data + 15) // 16 * 16
+    assert nq.measure_stream_raw(0, 32, p, 32, 1, 0, 0) == 1
+    assert nq.measure_stream_raw(p, 32, 0, 32, 1, 0, 0) == 1
+    assert nq.measure_stream_raw(p + 8, 32, p, 32, 1, 0, 0) == 11
+    assert nq.measure_stream_raw(p, 32, p + 4, 32, 1, 0, 0) == 11
+    assert nq.measure_stream_raw(p, 48, p, 32, 1, 0, 0) == 4       # reads more than it writes
+    assert nq.measure_stream_raw(p, 8, p, 32, 1, 0, 0) == 4        # not a multiple of 16
+    assert nq.measure_stream_raw(p, 0, p, 0, 1, 0, 0) == 4
+    for c in (0, 3, 16, -1):
+        assert nq.measure_stream_raw(p, 16, p, 32, c, 0, 0) == 4   # chunks per thread not 1, 2, 4, 8
+    assert nq.measure_stream_raw(p, 16, p, 32, 2, 4, 0) == 4       # unknown flag bit
+    assert nq.measure_stream_raw(p, 16, p, (1 << 40) + 16, 1, 0, 0) == 7

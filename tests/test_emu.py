@@ -109,11 +109,18 @@ def test_emulated_tile_sizes(fmt, upt):
         assert _same(got, _oracle(fmt, p, nblocks, B, dtype), dtype)
 
 
+# The launcher's per-format cap on units per thread (upt_max in nq_kernel.h).
+UPT_CAP = {f: 2 for f in FORMATS}
+UPT_CAP.update({f: 4 for f in ("gguf:q5_0", "gguf:q1_0", "gguf:q2_0")})
+UPT_CAP.update({f: 8 for f in ("gguf:q2_k", "gguf:q3_k", "gguf:iq2_xxs", "gguf:iq2_xs", "gguf:iq3_xxs", "gguf:iq1_s",
+                               "gguf:iq3_s", "gguf:iq2_s", "gguf:iq1_m", "gguf:tq1_0", "gguf:tq2_0", "nvfp4")})
+
+
 def test_tile_size_classes():
     """The launcher's size classes by units per resident workgroup q: below
     128, 1024 and 2048 take 1, 2 and 4 units per thread, larger launches 8;
     formats with codebooks of 8 KiB or more step up at 128, 256, 512 and 1024
-    to 2, 4, 8 and 16."""
+    to 2, 4, 8 and 16; every choice is capped per format."""
     g = 2048
     plain = [(0, 1), (1, 1), (127, 1), (128, 2), (1023, 2), (1024, 4), (2047, 4), (2048, 8), (1 << 20, 8)]
     big = [(0, 1), (127, 1), (128, 2), (255, 2), (256, 4), (511, 4), (512, 8), (1023, 8), (1024, 16), (1 << 20, 16)]
@@ -121,6 +128,7 @@ def test_tile_size_classes():
         fid = nq.format_query(fmt).id
         table = big if fmt in ("gguf:iq2_s", "gguf:iq1_s", "gguf:iq1_m") else plain
         for q, want in table:
+            want = min(want, UPT_CAP[fmt])
             assert emu_lib.choose_upt(fid, q * g, g) == want, (fmt, q)
             assert emu_lib.choose_upt(fid, q * g + g - 1, g) == want, (fmt, q)
         assert emu_lib.choose_upt(fid, 100, 0) == 1
@@ -527,3 +535,61 @@ def test_emu_gemm_tiny_shapes(fmt, N, K, M):
         assert guards
         ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
         linear_check(y, ref, env, K, f"{fmt} [{N}, {K}] x {M}")
+
+
+# ---------------------------------------------------------------------------
+# Many-tensor launches (nq_dequantize_packed_many): the launcher's packing
+# into launches of at most 64 entries and the kernel's tile search, per tile.
+# ---------------------------------------------------------------------------
+def _many_case(fmt, counts, seed, dtype="bf16", vec=True, resident=2048, chunk=0):
+    info = nq.format_query(fmt)
+    B = info.block_values
+    recipe = RECIPE if fmt == "nvfp4" else RAW
+    payloads = [synth.payload(fmt, nb, seed + k, recipe) for k, nb in enumerate(counts)]
+    vals, bad, msg, guards, launches, upts = emu_lib.decode_many(info.id, payloads, B, dtype, vec=vec,
+                                                                 resident=resident, chunk=chunk)
+    assert bad == 0, msg
+    assert guards
+    for k, (p, nb) in enumerate(zip(payloads, counts)):
+        assert _same(vals[k], _oracle(fmt, p, nb, B, dtype), dtype), (fmt, k, nb)
+    return launches, upts
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_emulated_many_every_format(fmt):
+    """Ragged tensors of one format, one launch; tiny device (resident 16)
+    so the larger tensors take several 2-unit tiles."""
+    launches, upts = _many_case(fmt, [1, 3, 37, 2, 64, 5], 90, resident=16)
+    assert launches == 1 and upts == {2}
+
+
+@pytest.mark.parametrize("fmt", ["gguf:q4_k", "nvfp4", "gguf:q8_0", "gguf:iq2_s", "gguf:tq2_0"])
+def test_emulated_many_launch_limits_and_tile_sizes(fmt):
+    """130 tensors: three launches (64, 64, 2 entries); on a one-workgroup
+    device the two full launches take the format's largest tiles and the last
+    (2 small tensors) 2-unit tiles; on a large device every launch takes
+    2-unit tiles."""
+    counts = [1 + (7 * k) % 13 for k in range(128)] + [1, 1]
+    launches, upts = _many_case(fmt, counts, 500, resident=1)
+    assert launches == 3 and upts == {2, min(8, UPT_CAP[fmt])}
+    launches, upts = _many_case(fmt, counts, 500, resident=1 << 20)
+    assert launches == 3 and upts == {2}
+
+
+@pytest.mark.parametrize("fmt", ["gguf:q4_0", "gguf:q6_k", "nvfp4", "gguf:tq1_0"])
+@pytest.mark.parametrize("chunk", [1, 3, 40])
+def test_emulated_many_tensors_split_into_chunks(fmt, chunk):
+    """A tensor larger than a launch chunk takes several entries (each with the
+    tensor's divisor for nvfp4); entries of one tensor can fall in two launches."""
+    counts = [100, 7, 1, 129] + [2] * 60 + [77]
+    launches, upts = _many_case(fmt, counts, 700, resident=1, chunk=chunk)
+    entries = sum((c + chunk - 1) // chunk for c in counts)
+    assert launches == (entries + 63) // 64
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "f64"])
+@pytest.mark.parametrize("fmt", ["gguf:q5_1", "gguf:iq3_xxs", "gguf:mxfp4", "nvfp4"])
+def test_emulated_many_output_types_and_alignment(fmt, dtype):
+    for vec in (True, False):
+        launches, upts = _many_case(fmt, [4, 1, 33], 40, dtype=dtype, vec=vec, resident=1 << 20)
+        assert upts == ({2} if vec and dtype != "f64" else {8})
