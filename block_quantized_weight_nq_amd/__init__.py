@@ -17,14 +17,14 @@ NQ_OK = 0
 STATUS_NAMES = {0: "NQ_OK", 1: "NQ_ERR_NULL_ARG", 2: "NQ_ERR_UNKNOWN_FORMAT", 3: "NQ_ERR_BAD_RANK",
                 4: "NQ_ERR_BAD_DIM", 5: "NQ_ERR_NOT_BLOCK_ALIGNED", 6: "NQ_ERR_LENGTH_MISMATCH",
                 7: "NQ_ERR_OVERFLOW", 8: "NQ_ERR_BAD_DTYPE", 9: "NQ_ERR_HIP", 10: "NQ_ERR_BAD_DIVISORS",
-                11: "NQ_ERR_MISALIGNED"}
+                11: "NQ_ERR_MISALIGNED", 12: "NQ_ERR_SCRATCH"}
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "f64": 3}
 FAMILIES = {0: "simple", 1: "kquant", 2: "iq", 3: "fp4", 4: "ternary"}
 EXPORTS = ["nq_format_count", "nq_format_by_id", "nq_format_query", "nq_validate",
            "nq_dequantize_packed", "nq_dequantize_packed_many", "nq_measure_stream", "nq_validate_nvfp4_stacked", "nq_dequantize_nvfp4_stacked",
            "nq_validate_fp8_row", "nq_dequantize_fp8_row", "nq_validate_grouped_absmax",
            "nq_quantize_grouped_absmax", "nq_validate_quantize_q8_1", "nq_quantize_q8_1",
-           "nq_validate_gemv_q8_1", "nq_gemv_q8_1", "nq_validate_gemm_q8_1", "nq_gemm_q8_1_workspace", "nq_gemm_q8_1",
+           "nq_validate_gemv_q8_1", "nq_gemv_q8_1", "nq_validate_gemm_q8_1", "nq_gemm_q8_1_workspace", "nq_gemm_q8_1", "nq_gemm_q8_1_noalloc",
            "nq_status_string"]
 GEMV_MAX_M = 8
 GQ_SCHEMES = {"q4_g64_fp16": (0, 64), "q5_g64_fp16": (1, 64), "q6_g64_fp16": (2, 64), "q8_g32_fp16": (3, 32)}
@@ -98,6 +98,8 @@ def _lib():
         L.nq_gemm_q8_1_workspace.argtypes = [c.c_int32, c.c_int64, c.c_int64, c.c_int64, c.POINTER(c.c_uint64)]
         L.nq_gemm_q8_1.argtypes = [c.c_int32, c.c_void_p, c.c_uint64, c.c_int64, c.c_int64, c.c_void_p,
                                    c.c_int64, c.c_void_p, c.c_void_p, c.c_uint64, c.c_void_p]
+        L.nq_gemm_q8_1_noalloc.argtypes = [c.c_int32, c.c_void_p, c.c_uint64, c.c_int64, c.c_int64, c.c_void_p,
+                                            c.c_int64, c.c_void_p, c.c_void_p]
         L.nq_status_string.argtypes = [c.c_int]
         L.nq_status_string.restype = c.c_char_p
         _LIB = L
@@ -441,6 +443,15 @@ def gemm_q8_1_raw(fmt_id, w_ptr, nbytes, N, K, xq_ptr, M, y_ptr, ws_ptr, ws_byte
     return _lib().nq_gemm_q8_1(int(fmt_id), ctypes.c_void_p(w_ptr), nbytes, N, K, ctypes.c_void_p(xq_ptr), M,
                                ctypes.c_void_p(y_ptr), ctypes.c_void_p(ws_ptr), ws_bytes,
                                ctypes.c_void_p(stream_handle))
+
+
+GEMM_SCRATCH_BYTES = 32 << 20
+
+
+def gemm_q8_1_noalloc_raw(fmt_id, w_ptr, nbytes, N, K, xq_ptr, M, y_ptr, stream_handle):
+    """nq_gemm_q8_1_noalloc (the library's static scratch as the workspace); returns the status."""
+    return _lib().nq_gemm_q8_1_noalloc(fmt_id, ctypes.c_void_p(w_ptr), nbytes, N, K, ctypes.c_void_p(xq_ptr), M,
+                                       ctypes.c_void_p(y_ptr), ctypes.c_void_p(stream_handle))
 
 
 def _product(raw, fmt, weight, N, K, xq, out, stream):

@@ -33,7 +33,7 @@ KERNEL_SOURCES = ["k_simple.hip", "k_kquant.hip", "k_iq.hip", "k_fp4.hip", "k_te
                   "k_gemv_fp4t.hip", "k_gemm_simple.hip", "k_gemm_kquant.hip", "k_gemm_iq.hip",
                   "k_gemm_fp4t.hip", "k_many_simple.hip", "k_many_kquant.hip", "k_many_iq.hip", "k_many_fp4.hip",
                   "k_many_ternary.hip", "k_measure.hip"]
-HOST_SOURCES = ["nq_abi.cpp"]
+HOST_SOURCES = ["nq_abi.cpp", "nq_noalloc.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-ffp-contract=off",
           "-fno-fast-math", "-Wall", "-Wno-unused-function"]

@@ -514,6 +514,7 @@ NQ_API const char *nq_status_string(int status) {
     case NQ_ERR_HIP: return "HIP launch failed";
     case NQ_ERR_BAD_DIVISORS: return "divisors must be in [1, 2^30] and divide the row count";
     case NQ_ERR_MISALIGNED: return "a pointer is not aligned as the call requires";
+    case NQ_ERR_SCRATCH: return "the shape needs more workspace than the static scratch holds; use nq_gemm_q8_1";
     default: return "unknown status";
     }
 }

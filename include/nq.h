@@ -41,7 +41,8 @@ typedef enum {
     NQ_ERR_BAD_DTYPE = 8,         /* out_dtype not one of nq_dtype */
     NQ_ERR_HIP = 9,               /* the HIP runtime reported an error at launch */
     NQ_ERR_BAD_DIVISORS = 10,     /* stacked nvfp4: divisors < 1, above 2^30, or not dividing the rows */
-    NQ_ERR_MISALIGNED = 11        /* a pointer lacks the alignment the call requires */
+    NQ_ERR_MISALIGNED = 11,       /* a pointer lacks the alignment the call requires */
+    NQ_ERR_SCRATCH = 12           /* nq_gemm_q8_1_noalloc: the shape needs more than NQ_GEMM_SCRATCH_BYTES */
 } nq_status;
 
 /* Output types: the page's FLOAT, FLOAT16, BFLOAT16 and DOUBLE. */
@@ -326,6 +327,26 @@ int nq_validate_gemm_q8_1(int32_t format, uint64_t nbytes, int64_t N, int64_t K,
 int nq_gemm_q8_1_workspace(int32_t format, int64_t N, int64_t K, int64_t M, uint64_t *bytes);
 int nq_gemm_q8_1(int32_t format, const void *weight, uint64_t nbytes, int64_t N, int64_t K, const void *xq,
                  int64_t M, float *y, void *workspace, uint64_t workspace_bytes, hipStream_t stream);
+
+/* nq_gemm_q8_1_noalloc: for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  The same product, argument meaning, checks and result as
+ * nq_gemm_q8_1 called with a workspace of the size nq_gemm_q8_1_workspace
+ * reports (the same bits), but the workspace is the library's own static
+ * device scratch of NQ_GEMM_SCRATCH_BYTES: every GPU the library is loaded
+ * on holds one from load until the process ends.  The call allocates
+ * nothing.  A shape whose workspace exceeds the scratch is refused with
+ * NQ_ERR_SCRATCH before anything is launched (at that size: every
+ * Llama-3-8B-shaped weight with up to 256 activation rows fits; larger
+ * batches, whose weight is rewritten once per call, need nq_gemm_q8_1 and a
+ * workspace); NQ_ERR_HIP if the scratch's device address cannot be found.
+ * All calls on one GPU share its scratch, which keeps the last call's
+ * contents (nothing in it has to start at zero): calls ordered on one stream
+ * are safe, calls that may overlap on one GPU (other streams, other host
+ * threads) race and their outputs are undefined. */
+#define NQ_GEMM_SCRATCH_BYTES (32u << 20)
+int nq_gemm_q8_1_noalloc(int32_t format, const void *weight, uint64_t nbytes, int64_t N, int64_t K, const void *xq,
+                         int64_t M, float *y, hipStream_t stream);
 
 /* Static description of a status code (the nq_status values above; other
  * values give "unknown status").  The pages define no status codes: these

@@ -332,7 +332,7 @@ def test_status_strings_name_every_status():
     for st, name in nq.STATUS_NAMES.items():
         text = L.nq_status_string(st).decode()
         assert text and text != "unknown status", (st, name)
-    assert L.nq_status_string(12).decode() == "unknown status"
+    assert L.nq_status_string(13).decode() == "unknown status"
     assert "NULL" in L.nq_status_string(1).decode() and "align" in L.nq_status_string(11).decode()
 
 
@@ -381,3 +381,21 @@ def test_measure_stream_rejects_before_device():
         assert nq.measure_stream_raw(p, 16, p, 32, c, 0, 0) == 4   # chunks per thread not 1, 2, 4, 8
     assert nq.measure_stream_raw(p, 16, p, 32, 2, 4, 0) == 4       # unknown flag bit
     assert nq.measure_stream_raw(p, 16, p, (1 << 40) + 16, 1, 0, 0) == 7
+
+
+def test_gemm_noalloc_refuses_shapes_past_its_scratch_before_device():
+    """The no-allocation product checks as nq_gemm_q8_1 and refuses a shape
+    whose workspace passes its 32 MiB scratch (NQ_ERR_SCRATCH) before any
+    device work."""
+    buf = np.zeros(64, dtype=np.uint32)
+    p = buf.ctypes.data
+    q4k = nq.format_query("gguf:q4_k").id
+    nb = 14336 * 4096 // 256 * 144
+    st, need = nq.gemm_q8_1_workspace("gguf:q4_k", 14336, 4096, 512)
+    assert st == 0 and need > nq.GEMM_SCRATCH_BYTES
+    assert nq.gemm_q8_1_noalloc_raw(q4k, p, nb, 14336, 4096, p, 512, p, 0) == 12
+    assert nq.gemm_q8_1_noalloc_raw(q4k, p, nb + 1, 14336, 4096, p, 512, p, 0) == 6
+    assert nq.gemm_q8_1_noalloc_raw(nq.format_query("nvfp4").id, p, 40, 1, 64, p, 9, p, 0) == 2
+    assert nq.gemm_q8_1_noalloc_raw(q4k, p, nb, 14336, 4096, p, 0, p, 0) == 4
+    assert nq.gemm_q8_1_noalloc_raw(q4k, 0, nb, 14336, 4096, p, 64, p, 0) == 1
+    assert nq.gemm_q8_1_noalloc_raw(q4k, p, nb, 14336, 4096, p + 2, 64, p, 0) == 11
