@@ -298,11 +298,12 @@ NQ_HD void unit_q3_k(const Src &src, uint32_t bo, uint32_t s, float (&y)[8]) {
     const uint32_t l = (lbyte >> (4u * (k >> 3))) & 15u;
     const uint32_t a = (bytek(sc[2], k & 3u) >> (2u * (k >> 2))) & 3u;
     const float ds = M(d, (float)((int)(l + 16u * a) - 32));
+    // v - 4(1 - h) = (v + 4h) - 4: each byte takes its mask bit as bit 2
+    // beside its 2-bit code (four values per operation)
+    c[0] = opaque(c[0] | (((mk[0] >> hbit) & 0x01010101u) << 2));
+    c[1] = opaque(c[1] | (((mk[1] >> hbit) & 0x01010101u) << 2));
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-        const uint32_t hb = (bytek(mk[j >> 2], (uint32_t)(j & 3)) >> hbit) & 1u;
-        y[j] = M(ds, (float)((int)code_at(c, j) - 4 * (int)(1u - hb)));
-    }
+    for (int j = 0; j < 8; j++) y[j] = M(ds, (float)code_at(c, j) - 4.0f);
 }
 
 // Q4_K / Q5_K: a[k], m[k] from the 12-byte scales; v = P(q,4,32) (+16 P(high,1,32));
@@ -462,9 +463,10 @@ NQ_HD void unit_nvfp4_gguf(const Src &src, uint32_t bo, uint32_t s, float (&y)[8
 // exact in binary32, so the value is one correctly rounded division.  IEEE
 // products and quotients take the XOR of their operands' signs (zeros
 // included) and round symmetrically, so y is the quotient of the magnitudes
-// with sign bit (c bit 3) ^ (s bit 7).  The kernels read that magnitude from
-// a per-workgroup table of all 128 x 8 (s & 0x7F, c & 7) quotients computed
-// with the same division (e2m1_e4m3_div).
+// with sign bit (c bit 3) ^ (s bit 7) ^ (d_w's sign).  The kernels read that
+// magnitude from a per-workgroup table of all 128 x 8 (s & 0x7F, c & 7)
+// quotients |e2m1_e4m3_div| and insert the sign bit (a NaN quotient stays a
+// NaN whatever its sign).
 NQ_HD float e4m3fn(uint32_t w) {
     const uint32_t sign = (w >> 7) & 1u, E = (w >> 3) & 15u, m = w & 7u;
     float mag;
@@ -483,8 +485,46 @@ NQ_HD float e2m1(uint32_t c) {
 }
 NQ_HD float e2m1_e4m3_div(uint32_t sw, uint32_t c, float dw) { return M(e2m1(c), e4m3fn(sw)) / dw; }
 
-// DIRECT: divide by `dw` here instead of reading the table built for the
-// tile's first divisor group (same correctly rounded quotient).
+// Table entry k = 8 * (s & 0x7F) + (c & 7): the quotient's magnitude bits.
+NQ_HD uint32_t nvfp4_table_entry(uint32_t k, float dw) {
+    return __builtin_bit_cast(uint32_t, e2m1_e4m3_div(k >> 3, k & 7u, dw)) & 0x7FFFFFFFu;
+}
+
+// Four table entries of scale magnitude sm (0..127) from one division:
+// class 0 fills codes 1, 2, 4, 6 (E2M1 0.5, 1, 2, 4 times the scale), class 1
+// codes 0, 3, 5, 7 (0, 1.5, 3, 6).  With q = RN32(m * s / d_w) for m = 1 or
+// 1.5, the entries are q/2, q, 2q, 4q (and 0 * s / d_w): scaling by a power
+// of two is exact and commutes with round-to-nearest while neither side is
+// subnormal, and an overflow of 2q or 4q to infinity happens on both sides
+// alike.  So when q is finite and at least 2^-125 (q/2 still normal) the
+// entries are scaled from q; otherwise (a q that overflowed, NaN, tiny or
+// zero: only divisors that section 3.3 refuses, or a zero scale) each is
+// divided directly.  Every entry equals nvfp4_table_entry.
+NQ_HD void nvfp4_table_quad(uint32_t sm, uint32_t cls, float dw, uint32_t (&e)[4], uint32_t (&code)[4]) {
+    code[0] = cls ? 0u : 1u;
+    code[1] = cls ? 3u : 2u;
+    code[2] = cls ? 5u : 4u;
+    code[3] = cls ? 7u : 6u;
+    const float q = e2m1_e4m3_div(sm, code[1], dw);  // E2M1 codes 2 (1.0) and 3 (1.5)
+    const uint32_t b = __builtin_bit_cast(uint32_t, q) & 0x7FFFFFFFu;
+    if (b >= 0x01000000u && b < 0x7F800000u) {
+        const float a = bits_f32(b);
+        // q finite: s is not the NaN word and d_w is neither NaN nor zero, so 0 * s / d_w is zero
+        e[0] = cls ? 0u : __builtin_bit_cast(uint32_t, M(a, 0.5f));
+        e[1] = b;
+        e[2] = __builtin_bit_cast(uint32_t, M(a, 2.0f));
+        e[3] = __builtin_bit_cast(uint32_t, M(a, 4.0f));
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++) e[i] = nvfp4_table_entry(8u * sm + code[i], dw);
+    }
+}
+
+// DIRECT: divide by `dw` here (the quotient carries d_w's sign; the codes'
+// and scale's signs are XORed in) instead of reading the table built for the
+// tile's first divisor group, whose magnitudes take the sign bit of all
+// three (tab.nv_dsign: d_w's sign in bit 7 of every byte).  The same
+// correctly rounded quotient either way.
 template <bool DIRECT, class Src, class Tab>
 NQ_HD void unit_nvfp4_div(const Src &src, uint32_t bo, uint32_t s, const Tab &tab, float dw, float (&y)[8]) {
     const uint32_t g = s >> 1;
@@ -493,13 +533,26 @@ NQ_HD void unit_nvfp4_div(const Src &src, uint32_t bo, uint32_t s, const Tab &ta
     window<2>(src, bo + 4 + 8u * g, q);
     uint32_t c[2];
     nibbles(q, s & 1u, c);
-    const uint32_t row = 8u * (sw & 0x7Fu);
+    if constexpr (DIRECT) {
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-        const uint32_t code = code_at(c, j);
-        const uint32_t neg = ((code >> 3) ^ (sw >> 7)) & 1u;
-        const float mag = DIRECT ? e2m1_e4m3_div(sw & 0x7Fu, code & 7u, dw) : tab.nv(row + (code & 7u));
-        y[j] = bits_f32(__builtin_bit_cast(uint32_t, mag) ^ (neg << 31));
+        for (int j = 0; j < 8; j++) {
+            const uint32_t code = code_at(c, j);
+            const uint32_t neg = ((code >> 3) ^ (sw >> 7)) & 1u;
+            const float v = e2m1_e4m3_div(sw & 0x7Fu, code & 7u, dw);
+            y[j] = bits_f32(__builtin_bit_cast(uint32_t, v) ^ (neg << 31));
+        }
+    } else {
+        // per byte: the sign (bit 7) and the table offset in bytes (4 * code magnitude)
+        const uint32_t sm = ((sw & 0x80u) ? 0x80808080u : 0u) ^ tab.nv_dsign;
+        const uint32_t sg[2] = {((c[0] << 4) & 0x80808080u) ^ sm, ((c[1] << 4) & 0x80808080u) ^ sm};
+        const uint32_t ix[2] = {opaque((c[0] & 0x07070707u) << 2), opaque((c[1] & 0x07070707u) << 2)};
+        const uint32_t row = 32u * (sw & 0x7Fu);
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const uint32_t mag = tab.nvb(row + code_at(ix, j));
+            const uint32_t sbit = sg[j >> 2] << (24 - 8 * (j & 3));
+            y[j] = bits_f32((mag & 0x7FFFFFFFu) | (sbit & 0x80000000u));
+        }
     }
 }
 

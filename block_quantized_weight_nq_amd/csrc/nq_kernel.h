@@ -103,6 +103,7 @@ struct Tab {
     const float *nvd;        // "nvfp4": divisors of the groups the tile reaches, from that one on
     uint32_t nv_bound;       // "nvfp4": first unit (chunk-relative) past that divisor's group
     uint32_t nv_gu;          // "nvfp4": units per divisor group, capped at 2^31 - 1
+    uint32_t nv_dsign;       // "nvfp4": sign bit of the table's divisor in bit 7 of every byte
     NQ_HD uint64_t iq2xxs(uint32_t r) const { return t8[r]; }
     NQ_HD uint64_t iq2xs(uint32_t r) const { return t8[r]; }
     NQ_HD uint64_t iq2s(uint32_t r) const { return t8[r]; }
@@ -110,6 +111,8 @@ struct Tab {
     NQ_HD uint32_t iq3xxs(uint32_t r) const { return t4[r]; }
     NQ_HD uint32_t iq3s(uint32_t r) const { return t4[r]; }
     NQ_HD float nv(uint32_t k) const { return nvq[k]; }
+    // "nvfp4": table word at byte offset b (b = 4 * entry)
+    NQ_HD uint32_t nvb(uint32_t b) const { return *(const uint32_t *)((const char *)nvq + b); }
 };
 
 // Table sizes per format.
@@ -448,6 +451,10 @@ NQ_HD float divisor_at(const TrSrc &tr, const KArgs &a, uint32_t g) {
     return bits_f32(w[0]);
 }
 
+// "nvfp4": d_w's sign bit in bit 7 of every byte (the sign the table's
+// magnitudes lose).
+NQ_HD uint32_t nv_sign_bytes(float dw) { return (__builtin_bit_cast(uint32_t, dw) >> 31) ? 0x80808080u : 0u; }
+
 // "nvfp4": the divisor group of tile t's first unit, and the chunk-relative
 // unit where that group ends (capped at 2^32 - 1).
 template <int UPT>
@@ -480,7 +487,12 @@ NQ_HD void fill_tables(uint64_t *t8, uint32_t *t4, float *nvq, float *nvd, const
         const uint32_t nd = a.ndiv - g0 < (uint32_t)TS::nd ? a.ndiv - g0 : (uint32_t)TS::nd;
         for (uint32_t k = tid; k < nd; k += nthreads) nvd[k] = divisor_at(tr, a, g0 + k);
         const float dw = divisor_at(tr, a, g0);
-        for (uint32_t k = tid; k < (uint32_t)TS::nf; k += nthreads) nvq[k] = e2m1_e4m3_div(k >> 3, k & 7u, dw);
+        for (uint32_t k = tid; k < (uint32_t)TS::nf / 4u; k += nthreads) {
+            uint32_t e[4], code[4];
+            nvfp4_table_quad(k >> 1, k & 1u, dw, e, code);
+#pragma unroll
+            for (int i = 0; i < 4; i++) nvq[8u * (k >> 1) + code[i]] = bits_f32(e[i]);
+        }
     }
 }
 
@@ -494,13 +506,14 @@ __device__ __forceinline__ void decode_tile(const KArgs &a, uint32_t t, uint32_t
     using TS = TabSpec<F>;
     using ST = Stage<F, UPT>;
     const DevSrc src{a.base, a.last};
-    Tab tab{t8, t4, nvq, nvd, 0xFFFFFFFFu, 1u};
+    Tab tab{t8, t4, nvq, nvd, 0xFFFFFFFFu, 1u, 0u};
     uint32_t g0 = 0;
+    const DevSrc tr{a.tr_base, a.tr_last};
     if constexpr (F == NVFP4_DIV) {
         g0 = nv_first_group<UPT>(a, t, &tab.nv_bound);
         tab.nv_gu = a.gu < 0x7FFFFFFFull ? (uint32_t)a.gu : 0x7FFFFFFFu;
+        tab.nv_dsign = nv_sign_bytes(divisor_at(tr, a, g0));
     }
-    const DevSrc tr{a.tr_base, a.tr_last};
     if (t < staged_tiles<F, UPT>(a)) {
         uint32_t r[ST::NK][4];
         stage_load<F, UPT>(src, a, t, tid, r);

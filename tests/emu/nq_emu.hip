@@ -76,10 +76,11 @@ struct EmuTiles {
         const HostSrc src{a.base, a.last, &chk};
         const bool vec = ((uintptr_t)a.out & 15) == 0;
         uint32_t g0 = 0;
-        Tab tab{t8.data(), t4.data(), nvq.data(), nvd.data(), 0xFFFFFFFFu, 1u};
+        Tab tab{t8.data(), t4.data(), nvq.data(), nvd.data(), 0xFFFFFFFFu, 1u, 0u};
         if constexpr (F == NVFP4_DIV) {
             g0 = nv_first_group<UPT>(a, t, &tab.nv_bound);
             tab.nv_gu = a.gu < 0x7FFFFFFFull ? (uint32_t)a.gu : 0x7FFFFFFFu;
+            tab.nv_dsign = nv_sign_bytes(divisor_at(tr, a, g0));
             std::fill(nvd.begin(), nvd.end(), bits_f32(0x7FA5A5A5u));
         }
         if (TS::n8 + TS::n4 + TS::nf > 0)
@@ -760,6 +761,24 @@ extern "C" __attribute__((visibility("default"))) long nq_emu_decode(int fmt, in
     if (fmt < 0 || fmt >= nq::NUM_FORMATS || !nq_emu_table[fmt]) return -1;
     return nq_emu_table[fmt](ot, payload, nbytes, nblocks, out, max_wgs, chunk_blocks, force_upt,
                              ndiv < 1 ? 1 : ndiv, err, errlen);
+}
+
+// The "nvfp4" quotient table for each of n divisor words, built as the
+// kernels build it (nvfp4_table_quad, four entries per thread) and entry by
+// entry (nvfp4_table_entry, one division each): 1024 words per divisor in
+// `quad` and `direct`.
+extern "C" __attribute__((visibility("default"))) void nq_emu_nvfp4_tables(const uint32_t *dw_bits, long n,
+                                                                          uint32_t *quad, uint32_t *direct) {
+    for (long i = 0; i < n; i++) {
+        const float dw = nq::bits_f32(dw_bits[i]);
+        uint32_t *q = quad + 1024 * i, *d = direct + 1024 * i;
+        for (uint32_t k = 0; k < 256; k++) {
+            uint32_t e[4], code[4];
+            nq::nvfp4_table_quad(k >> 1, k & 1u, dw, e, code);
+            for (int j = 0; j < 4; j++) q[8u * (k >> 1) + code[j]] = e[j];
+        }
+        for (uint32_t k = 0; k < 1024; k++) d[k] = nq::nvfp4_table_entry(k, dw);
+    }
 }
 
 // Whole blocks per staged tile of format fmt at `upt` units per thread, for

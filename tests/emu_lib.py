@@ -17,12 +17,20 @@ _lib = None
 PARTS = 6
 
 
+# NQ_EMU_DEFINES="NAME=VALUE ..." builds and loads an emulator with the
+# kernels' tuning knobs set (a separate library file), to check the code
+# paths a tuning choice selects.
+DEFINES = os.environ.get("NQ_EMU_DEFINES", "").split()
+if DEFINES:
+    LIB = os.path.join(HERE, "emu", "libnq_emu_" + "_".join(d.replace("=", "") for d in DEFINES) + ".so")
+
+
 def build():
     """Compile the emulator: PARTS instantiation parts and the dispatch part in parallel, then link."""
     import concurrent.futures
     import tempfile
     flags = ["hipcc", "-x", "hip", "--offload-host-only", "-O1", "-std=c++17", "-fPIC", "-ffp-contract=off",
-             "-fvisibility=hidden"]
+             "-fvisibility=hidden"] + [f"-D{d}" for d in DEFINES]
     with tempfile.TemporaryDirectory() as tmp:
         jobs = [[f"-DNQ_EMU_PART={p}", f"-DNQ_EMU_PARTS={PARTS}"] for p in range(PARTS)] + [[]]
         objs = [os.path.join(tmp, f"part{i}.o") for i in range(len(jobs))]
@@ -67,6 +75,8 @@ def lib():
                                          ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
                                          ctypes.c_char_p, ctypes.c_int]
         L.nq_emu_decode_many.restype = ctypes.c_long
+        L.nq_emu_nvfp4_tables.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_void_p]
+        L.nq_emu_nvfp4_tables.restype = None
         L.nq_emu_tile_blocks.argtypes = [ctypes.c_int, ctypes.c_int]
         L.nq_emu_fp8_row.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64,
                                      ctypes.c_void_p, ctypes.c_uint64, ctypes.c_char_p, ctypes.c_int]
@@ -170,6 +180,16 @@ def decode_many(fmt_id, payloads, B, dtype, vec=True, resident=2048, chunk=0, mi
 def _format(fmt_id):
     import block_quantized_weight_nq_amd as nq
     return nq.format_by_id(fmt_id)
+
+
+def nvfp4_tables(dw_bits):
+    """(quad-built, entry-built) nvfp4 quotient tables, [n, 1024] uint32 each."""
+    dw_bits = np.ascontiguousarray(dw_bits, dtype=np.uint32)
+    n = dw_bits.size
+    quad = np.zeros((n, 1024), dtype=np.uint32)
+    direct = np.zeros((n, 1024), dtype=np.uint32)
+    lib().nq_emu_nvfp4_tables(dw_bits.ctypes.data, n, quad.ctypes.data, direct.ctypes.data)
+    return quad, direct
 
 
 def tile_blocks(fmt_id, upt):

@@ -134,13 +134,60 @@ def test_tile_size_classes():
         assert emu_lib.choose_upt(fid, 100, 0) == 1
 
 
-@pytest.mark.parametrize("d_w", [1.0, 3.0, 448.0, 1e-30, 3e38])
+@pytest.mark.parametrize("d_w", [1.0, 3.0, 448.0, 1e-30, 3e38, -3.0, -0.0, 0.0, float("inf"), float("-inf"),
+                                 float("nan"), -1e-38])
 def test_emulated_nvfp4_divisor(d_w):
+    """Valid divisors and the words section 3.3 refuses (negative, zero,
+    infinite, NaN, subnormal): the table's magnitudes with the divisor's sign
+    inserted give the oracle's quotients (NaN by class)."""
     info = nq.format_query("nvfp4")
-    p = synth.payload("nvfp4", 40, 3, RECIPE, divisor=d_w)
-    got, bad, msg, guards = emu_lib.decode(info.id, p, 40, 64, "f32", mis=2)
+    p = synth.payload("nvfp4", 40, 3, RAW, divisor=d_w)
+    for upt in (0, 2, 8):
+        got, bad, msg, guards = emu_lib.decode(info.id, p, 40, 64, "f32", mis=2, upt=upt)
+        assert bad == 0 and guards, msg
+        assert _same(got, _oracle("nvfp4", p, 40, 64, "f32"), "f32"), (d_w, upt)
+
+
+def test_nvfp4_table_from_two_quotients_per_scale():
+    """The kernels build the 1024-entry quotient table from one division per
+    scale magnitude and E2M1 class, scaled by powers of two; every entry must
+    equal its own correctly rounded division, for every scale word and
+    divisors of every binade and class: random words over the whole binary32
+    range, the valid range [1, 448], subnormals, powers of two near the
+    overflow and underflow edges, zeros, infinities and NaNs."""
+    rng = np.random.default_rng(5)
+    words = [rng.integers(0, 2 ** 32, size=40000, dtype=np.uint64).astype(np.uint32),
+             rng.integers(0x3F800000, 0x43E00001, size=20000, dtype=np.uint64).astype(np.uint32),
+             rng.integers(1, 0x00800000, size=5000, dtype=np.uint64).astype(np.uint32)]
+    edges = []
+    for e in list(range(0, 12)) + list(range(100, 150)) + list(range(240, 255)):
+        for m in (0, 1, 0x400000, 0x7FFFFF):
+            edges.append((e << 23) | m)
+    edges += [0, 0x7F800000, 0x7FC00000, 0x7F800001, 0x00000001, 0x00800000, 0x3F800000, 0x43E00000]
+    words.append(np.array(edges, dtype=np.uint32))
+    words = np.concatenate(words)
+    words = np.concatenate([words, words ^ np.uint32(0x80000000)])
+    quad, direct = emu_lib.nvfp4_tables(words)
+    qn = ((quad & 0x7F800000) == 0x7F800000) & ((quad & 0x007FFFFF) != 0)
+    dn = ((direct & 0x7F800000) == 0x7F800000) & ((direct & 0x007FFFFF) != 0)
+    bad = (qn != dn) | (~dn & (quad != direct))
+    assert not bad.any(), f"{int(bad.sum())} entries differ, first divisor word {int(words[np.nonzero(bad.any(1))[0][0]]):#010x}"
+
+
+@pytest.mark.parametrize("upt", [0, 2, 8])
+def test_emulated_nvfp4_stacked_signed_divisors(upt):
+    """Stacked divisors of both signs, zeros, an infinity and a NaN: tiles
+    that start in a negative group read the table with the sign inserted,
+    units past it divide directly."""
+    d_ws = [3.0, -3.0, -0.0, 0.0, float("inf"), -448.0, float("nan"), 1.0]
+    rows, K = 64, 128
+    nb = rows * K // 64
+    p = synth.payload("nvfp4", nb, 77, RAW, divisor=d_ws, divisors=len(d_ws))
+    ref = oracle.decode_nvfp4_stacked(p, [rows, K], len(d_ws), "f32")
+    fid = nq.format_query("nvfp4").id
+    got, bad, msg, guards = emu_lib.decode(fid, p, nb, 64, "f32", mis=1, upt=upt, ndiv=len(d_ws))
     assert bad == 0 and guards, msg
-    assert _same(got, _oracle("nvfp4", p, 40, 64, "f32"), "f32")
+    assert _same(got, ref, "f32")
 
 
 @pytest.mark.parametrize("upt", [0, 1, 2, 8, 16])

@@ -126,7 +126,8 @@ def test_nvfp4_every_scale_byte_and_code():
     for dtype in ("f32", "bf16", "f16"):
         announce(f"gguf:nvfp4 exhaustive {dtype}")
         _check("gguf:nvfp4", p, [256 * 64], dtype)
-        for d_w in (1.0, 3.0, 7.1234567, 448.0, 1e-30, 3e38):
+        for d_w in (1.0, 3.0, 7.1234567, 448.0, 1e-30, 3e38, -3.0, -0.0, 0.0, float("inf"), float("-inf"),
+                    float("nan"), 1e-40):
             announce(f"nvfp4 exhaustive {dtype} d_w={d_w}")
             q = np.concatenate([p, np.array([d_w], "<f4").view(np.uint8)])
             _check("nvfp4", q, [256 * 64], dtype)
