@@ -1,4 +1,6 @@
 """Helpers for GPU tests: upload, decode through the C ABI, download."""
+import concurrent.futures
+import os
 import sys
 
 import numpy as np
@@ -54,3 +56,33 @@ def oracle_blocks(fmt, payload_np, block_ids, dtype):
     rows = payload_np[: (payload_np.size - T)].reshape(-1, S)[idx]
     f32 = oracle.decode_blocks_f32(fmt, rows.ravel(), d_w)
     return oracle.convert(f32, dtype) if dtype != "f32" else f32
+
+
+def oracle_threads():
+    """Host threads for fanned-out oracle decodes: the cores this process may use, at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_decode_parallel(fmt, payload_np, nblocks, dtype, threads=None):
+    """The oracle's decode of a whole payload, its blocks split over host threads
+    (blocks decode independently; each chunk carries the format's trailer).
+    The first block is decoded on this thread first, so the oracle's lazily
+    built codebooks exist before the threads start."""
+    _, B, S, T = oracle.info(fmt)
+    threads = threads or oracle_threads()
+    trailer = payload_np[nblocks * S:] if T else None
+
+    def part(b0, b1):
+        q = payload_np[b0 * S:b1 * S]
+        if T:
+            q = np.concatenate([q, trailer])
+        return oracle.decode(fmt, q, [(b1 - b0) * B], dtype)
+
+    if nblocks == 0:
+        return part(0, 0)
+    part(0, 1)
+    n = min(nblocks, threads * 4)
+    edges = [nblocks * k // n for k in range(n + 1)]
+    with concurrent.futures.ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(lambda k: part(edges[k], edges[k + 1]), range(n)))
+    return np.concatenate(parts)

@@ -2,15 +2,16 @@
 
 The page defines decoding twice: in its "Mathematical decoding rules" (which
 the oracle restates in C) and in its "Equivalent Python notation".  This
-helper extracts the second notation's code blocks from the mounted copy of
+helper extracts the second notation's code blocks from a local text copy of
 the page at run time -- nothing of it is stored in this repository -- and
 executes them in a private namespace, so tests can compare the oracle with an
-independent reading.  CPU tests only; returns None when the copy of the page
-is not mounted (the GPU machine has none).
+independent reading.  The copy's path comes from the NQ_PAGE_TEXT environment
+variable; without it (or without the file) load() returns None and the tests
+that use it are skipped.  CPU tests only.
 """
 import os
 
-PAGE = "/root/reference/PAPER.md"
+PAGE = os.environ.get("NQ_PAGE_TEXT", "")
 
 
 def _segment(lines, start_pred, end_pred, include_end):
@@ -23,7 +24,7 @@ def _segment(lines, start_pred, end_pred, include_end):
 
 
 def load():
-    if not os.path.exists(PAGE):
+    if not PAGE or not os.path.exists(PAGE):
         return None
     with open(PAGE, encoding="utf-8") as f:
         lines = f.read().split("\n")

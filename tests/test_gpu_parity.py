@@ -3,8 +3,8 @@
 Every comparison is exact except NaN payloads, which the DequantizePacked page
 leaves unspecified (compared by class).  Inputs come from the seeded
 generator; sizes span many workgroups with a ragged tail, and the full-size
-workloads are checked on sampled blocks in the same launch configuration the
-benchmark times.
+workloads are compared in full, the weight-set workload through the
+many-tensor call the benchmark times.
 """
 import numpy as np
 import pytest
@@ -15,7 +15,7 @@ import compare
 import oracle
 import synth
 from synth import workloads
-from gpu_util import TORCH_DT, announce, decode, oracle_blocks, to_numpy, upload
+from gpu_util import TORCH_DT, announce, decode, oracle_blocks, oracle_decode_parallel, oracle_threads, to_numpy, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -134,12 +134,16 @@ def test_nvfp4_every_scale_byte_and_code():
 
 
 def test_output_conversion_edges_through_q8_k():
-    """y = d * q with binary32 d covering every high half-word and the low
-    half-words around both rounding points: exercises the hardware bf16/f16
-    conversions on ties, subnormals, overflow and NaN."""
+    """y = d * q with binary32 d covering every high half-word with the low
+    half-words the oracle's conversion pin uses (at and around the bf16 and f16
+    rounding points, odd-LSB ties included) plus 2^18 random words:
+    exercises the hardware bf16/f16 conversions on ties, subnormals, overflow
+    and NaN (q = 1 converts d itself; the other codes scale it)."""
     hi = np.arange(65536, dtype=np.uint32) << 16
-    lows = np.array([0x0000, 0x0FFF, 0x1000, 0x1001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint32)
-    d = (hi[:, None] | lows[None, :]).ravel()
+    lows = np.array([0x0000, 0x0001, 0x0FFF, 0x1000, 0x1001, 0x1FFF, 0x2000, 0x2001, 0x3000,
+                     0x7FFF, 0x8000, 0x8001, 0xBFFF, 0xC000, 0xFFFF], dtype=np.uint32)
+    rand = np.random.default_rng(2025).integers(0, 2 ** 32, size=1 << 18, dtype=np.uint64).astype(np.uint32)
+    d = np.concatenate([(hi[:, None] | lows[None, :]).ravel(), rand])
     n = d.size
     blk = np.zeros((n, 292), dtype=np.uint8)
     blk[:, 0:4] = d.view(np.uint8).reshape(n, 4)
@@ -186,44 +190,61 @@ def test_every_tile_size_class(fmt):
 
 
 # ---------------------------------------------------------------------------
-# Full-size workloads, sampled blocks.
+# Full-size workloads, compared in full against the oracle, whose decode is
+# fanned out over host threads (gpu_util.oracle_threads: the cores this
+# process may use, at most 16).
 # ---------------------------------------------------------------------------
-def _full_size_sampled(name, fmt, shape, recipe, seed, dtype, nsample=2048):
+def _full_size(name, fmt, shape, recipe, seed, dtype):
     info = nq.format_query(fmt)
-    B = info.block_values
-    nel = int(np.prod(shape))
-    nb = nel // B
-    announce(f"full-size {name} {fmt} {shape} {dtype} seed={seed:#x}")
+    nb = int(np.prod(shape)) // info.block_values
+    announce(f"full-size {name} {fmt} {shape} {dtype} seed={seed:#x} threads={oracle_threads()}")
     p = synth.payload(fmt, nb, seed, recipe)
     payload, _ = upload(p)
     out = nq.dequantize_packed(fmt, payload, shape, TORCH_DT[dtype])
     torch.cuda.synchronize()
-    rng = np.random.default_rng(seed & 0xFFFFFFFF)
-    ids = np.unique(np.concatenate([[0, nb - 1], rng.integers(0, nb, size=nsample)]))
-    got = to_numpy(out.reshape(nb, B)[torch.from_numpy(ids).to("cuda:0")], dtype).ravel()
-    ref = oracle_blocks(fmt, p, ids, dtype)
-    assert compare.same(got, ref, dtype), f"{name}: {compare.describe(got, ref, dtype)}"
+    got = to_numpy(out.reshape(-1), dtype)
     del out, payload
+    ref = oracle_decode_parallel(fmt, p, nb, dtype)
+    assert compare.same(got, ref, dtype), f"{name}: {compare.describe(got, ref, dtype)}"
     torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("config", [1, 2, 3, 4])
-def test_full_size_configs_sampled(config):
+def test_full_size_configs_in_full(config):
     tensors, dtypes = workloads.CONFIGS[config]()
     for name, fmt, shape, recipe, seed in tensors:
         for dtype in dtypes:
-            _full_size_sampled(name, fmt, shape, recipe, seed, dtype)
+            _full_size(name, fmt, shape, recipe, seed, dtype)
 
 
-def test_full_size_llama3_8b_set_sampled():
-    tensors, dtypes = workloads.config5()
-    seen = set()
-    for t, (name, fmt, shape, recipe, seed) in enumerate(tensors):
-        key = (fmt, tuple(shape))
-        if key in seen and t != len(tensors) - 1:
-            continue
-        seen.add(key)
-        _full_size_sampled(name, fmt, shape, recipe, seed, "bf16", nsample=1024)
+def test_full_size_llama3_8b_set_in_full():
+    """The whole Llama-3-8B-shaped set (226 tensors, 8.03 G values) decoded to
+    bf16 by one nq_dequantize_packed_many call, the launch configuration the
+    benchmark times, and every output compared with the oracle."""
+    tensors, _ = workloads.config5()
+    items = []
+    for name, fmt, shape, recipe, seed in tensors:
+        info = nq.format_query(fmt)
+        nb = int(np.prod(shape)) // info.block_values
+        p = synth.payload(fmt, nb, seed, recipe)
+        payload = torch.from_numpy(p).to("cuda:0")
+        out = torch.empty(int(np.prod(shape)), dtype=torch.bfloat16, device="cuda:0")
+        items.append((name, fmt, shape, recipe, seed, nb, info.id, payload, out))
+        del p
+    announce(f"full-size llama3-8b set: one many-tensor call over {len(items)} tensors")
+    st, failed = nq.dequantize_packed_many_raw([(it[6], it[7].data_ptr(), it[7].numel(), it[2], it[8].data_ptr())
+                                                 for it in items], 2, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert (st, failed) == (0, -1)
+    threads = oracle_threads()
+    for k, (name, fmt, shape, recipe, seed, nb, fid, payload, out) in enumerate(items):
+        if k % 20 == 0:
+            announce(f"full-size llama3-8b set: comparing tensor {k} ({name}), oracle on {threads} threads")
+        got = to_numpy(out, "bf16")
+        ref = oracle_decode_parallel(fmt, synth.payload(fmt, nb, seed, recipe), nb, "bf16", threads)
+        assert compare.same(got, ref, "bf16"), f"{name}: {compare.describe(got, ref, 'bf16')}"
+    del items
+    torch.cuda.empty_cache()
 
 
 def test_graph_replays_match_eager():

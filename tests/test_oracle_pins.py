@@ -414,7 +414,7 @@ def test_golden_one_block(ex):
 NOTATION = page_notation.load()
 
 
-@pytest.mark.skipif(NOTATION is None, reason="page text not mounted")
+@pytest.mark.skipif(NOTATION is None, reason="NQ_PAGE_TEXT does not name a copy of the page text")
 @pytest.mark.parametrize("fmt", GGUF)
 @pytest.mark.parametrize("recipe", [synth.raw(), RECIPE], ids=repr)
 def test_oracle_matches_page_python_notation(fmt, recipe):
@@ -431,7 +431,7 @@ def test_oracle_matches_page_python_notation(fmt, recipe):
     assert np.array_equal(y[~nan].view(np.uint32), ref[~nan].view(np.uint32))
 
 
-@pytest.mark.skipif(NOTATION is None, reason="page text not mounted")
+@pytest.mark.skipif(NOTATION is None, reason="NQ_PAGE_TEXT does not name a copy of the page text")
 def test_oracle_codebooks_match_page_python_notation():
     for book in ROWS:
         g = oracle.grid(book)
