@@ -52,9 +52,18 @@ def _hipcc():
 MFMA_UNITS = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
-def _compile(src, is_kernel, build_dir=BUILD, defines=()):
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for the host
+# sources (the C ABI's validators and launchers); device code is built as
+# always.  Used by tests/run_sanitized.py for libnq_san.so.
+SAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
+
+
+def _compile(src, is_kernel, build_dir=BUILD, defines=(), sanitize=False):
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
     extra = MFMA_UNITS if src.startswith("k_gemm_") else []
+    if sanitize and src in HOST_SOURCES:
+        extra = extra + SAN_HOST
     cmd = [_hipcc(), *COMMON, *DEVICE, *extra, *[f"-D{d}" for d in defines], "-x", "hip", "-c",
            os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -63,21 +72,23 @@ def _compile(src, is_kernel, build_dir=BUILD, defines=()):
     return obj
 
 
-def build(jobs=None, verbose=False, out=LIB, defines=()):
+def build(jobs=None, verbose=False, out=LIB, defines=(), sanitize=False):
     """Compile every source and link the library (default: libnq.so in-tree).
 
     `defines` are extra -D macros (the tuning knobs NQ_UPT, NQ_RESIDENT_PER_CU,
     NQ_NT_STORE, NQ_NTL of csrc/nq_kernel.h, NQ_F8_NB of csrc/nq_fp8row.h and
     NQ_GM_REWRITE_M of csrc/nq_gemm.h);
-    a non-default `out` builds elsewhere.
+    a non-default `out` builds elsewhere; `sanitize` builds the host sources
+    with AddressSanitizer and UndefinedBehaviorSanitizer.
     """
     build_dir = BUILD if out == LIB else out + ".build"
     os.makedirs(build_dir, exist_ok=True)
     jobs = jobs or min(8, os.cpu_count() or 4)
-    work = [(s, True, build_dir, tuple(defines)) for s in KERNEL_SOURCES + HOST_SOURCES]
+    work = [(s, True, build_dir, tuple(defines), sanitize) for s in KERNEL_SOURCES + HOST_SOURCES]
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda a: _compile(*a), work))
     tmp = out + ".tmp"
+    # (sanitized objects resolve their runtime against the one the test run preloads)
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

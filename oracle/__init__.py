@@ -12,8 +12,13 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# NQ_SANITIZE=1: a separate build under AddressSanitizer and
+# UndefinedBehaviorSanitizer (clang, whose runtime the sanitized test run
+# preloads; see tests/run_sanitized.py)
+SANITIZE = os.environ.get("NQ_SANITIZE") == "1"
+_LIB_PATH = os.path.join(_HERE, "liboracle_san.so" if SANITIZE else "liboracle.so")
 _SRC = os.path.join(_HERE, "nq_oracle.c")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
 
 # -O1, no contraction, no fast-math: each float operation is one IEEE
 # binary32 operation (x86-64 SSE), as the decoding rules require.
@@ -28,8 +33,11 @@ _lib = None
 
 
 def build():
-    """Compile liboracle.so with gcc."""
-    subprocess.run(["gcc", *CFLAGS, "-o", _LIB_PATH, _SRC, "-lm"], check=True)
+    """Compile liboracle.so with gcc (NQ_SANITIZE=1: liboracle_san.so with clang and the sanitizers)."""
+    if SANITIZE:
+        subprocess.run(["/opt/rocm/llvm/bin/clang", *CFLAGS, *SAN_FLAGS, "-o", _LIB_PATH, _SRC, "-lm"], check=True)
+    else:
+        subprocess.run(["gcc", *CFLAGS, "-o", _LIB_PATH, _SRC, "-lm"], check=True)
 
 
 def lib():

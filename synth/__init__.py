@@ -19,15 +19,20 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libsynth.so")
+SANITIZE = os.environ.get("NQ_SANITIZE") == "1"  # separate sanitized build (tests/run_sanitized.py)
+_LIB_PATH = os.path.join(_HERE, "libsynth_san.so" if SANITIZE else "libsynth.so")
 _SRC = os.path.join(_HERE, "synth.c")
 _lib = None
 
 
 def build():
-    """Compile libsynth.so (gcc, OpenMP)."""
-    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
-           "-o", _LIB_PATH, _SRC]
+    """Compile libsynth.so (gcc, OpenMP; NQ_SANITIZE=1: libsynth_san.so, clang with the sanitizers)."""
+    if SANITIZE:
+        cmd = ["/opt/rocm/llvm/bin/clang", "-O1", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
+               "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g",
+               "-o", _LIB_PATH, _SRC]
+    else:
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-o", _LIB_PATH, _SRC]
     subprocess.run(cmd, check=True)
 
 

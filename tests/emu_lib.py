@@ -23,6 +23,13 @@ PARTS = 6
 DEFINES = os.environ.get("NQ_EMU_DEFINES", "").split()
 if DEFINES:
     LIB = os.path.join(HERE, "emu", "libnq_emu_" + "_".join(d.replace("=", "") for d in DEFINES) + ".so")
+# NQ_SANITIZE=1: host code under AddressSanitizer and UndefinedBehaviorSanitizer
+# (tests/run_sanitized.py preloads the runtime)
+SANITIZE = os.environ.get("NQ_SANITIZE") == "1"
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+if SANITIZE:
+    LIB = LIB[:-3] + "_san.so"
 
 
 def build():
@@ -30,7 +37,7 @@ def build():
     import concurrent.futures
     import tempfile
     flags = ["hipcc", "-x", "hip", "--offload-host-only", "-O1", "-std=c++17", "-fPIC", "-ffp-contract=off",
-             "-fvisibility=hidden"] + [f"-D{d}" for d in DEFINES]
+             "-fvisibility=hidden"] + [f"-D{d}" for d in DEFINES] + (SAN_FLAGS if SANITIZE else [])
     with tempfile.TemporaryDirectory() as tmp:
         jobs = [[f"-DNQ_EMU_PART={p}", f"-DNQ_EMU_PARTS={PARTS}"] for p in range(PARTS)] + [[]]
         objs = [os.path.join(tmp, f"part{i}.o") for i in range(len(jobs))]
