@@ -24,6 +24,7 @@ reports:
                  reads a payload out of a warm cache
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+       python bench.py --formats gguf:q6_k,nvfp4 --shapes 14336x4096,4096x4096   (profiling target)
 """
 import argparse
 import json
@@ -613,6 +614,34 @@ def gemv_only(torch, nq, synth, args):
     print(json.dumps(line), flush=True)
 
 
+def formats_only(torch, nq, synth, args):
+    """Single-tensor decodes of the named formats at the named shapes, each
+    over a cold rotation (rotating_measurement): one JSON line of its own.
+    A small, fixed target for counter and trace runs.  It calls only
+    nq_format_query and nq_dequantize_packed, so it also runs against earlier
+    builds of the library."""
+    from synth import workloads
+    names = [f for f in args.formats.split(",") if f]
+    shapes = [[int(d) for d in sh.split("x")] for sh in args.shapes.split(",") if sh]
+    need = 0
+    for f in names:
+        info = nq.format_query(f)
+        for sh in shapes:
+            need = max(need, math.prod(sh) // info.block_values * info.block_bytes + info.trailer_bytes)
+    staging = torch.empty(need, dtype=torch.uint8, pin_memory=True)
+    res = {}
+    for sh in shapes:
+        for f in names:
+            info = nq.format_query(f)
+            key = f"{f}{sh}->{args.dtype}"
+            res[key] = rotating_measurement(torch, nq, synth, key, f, sh, workloads.recipe_for(f), 0x6E718000 + info.id,
+                                            args.dtype, staging, launches=args.launches)
+            log(f"{key}: {res[key]['gbps']} GB/s ({100 * res[key]['frac_hbm_peak']:.1f}% of peak), "
+                f"{res[key]['replicas']} replicas")
+    print(json.dumps({"metric": METRIC, "unit": "GB/s", "n_gpus": 1, "data": "synthetic",
+                      "call": "nq_dequantize_packed, one tensor per launch", "workloads": res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -624,6 +653,11 @@ def main():
                     help="measure only the products with q8_1 activations (one JSON line of its own)")
     ap.add_argument("--gemm-only", action="store_true",
                     help="measure only the batched products on the matrix cores (one JSON line of its own)")
+    ap.add_argument("--formats", default="", metavar="F1,F2,...",
+                    help="measure only single-tensor decodes of these formats at --shapes (one JSON line of its own)")
+    ap.add_argument("--shapes", default="14336x4096", metavar="RxC,...", help="shapes for --formats")
+    ap.add_argument("--dtype", default="bf16", choices=sorted(OUT_CODES), help="output type for --formats")
+    ap.add_argument("--launches", type=int, default=60, help="launches per timed replay for --formats")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
                     help="first run a plain device copy of this many MiB (for counter calibration)")
     args = ap.parse_args()
@@ -654,6 +688,9 @@ def main():
         log(f"copy calibration: 3 x {args.calibrate_copy} MiB device copies done")
         del a, b
 
+    if args.formats:
+        formats_only(torch, nq, synth, args)
+        return
     if args.gemv_only:
         gemv_only(torch, nq, synth, args)
         return
@@ -710,10 +747,11 @@ def main():
     extra = {}
     ceilings = {}
     if not args.no_per_format:
-        # streaming ceilings at representative read:write mixes (bytes per value)
-        for key, (rb, wb) in {"1:1 copy": (1, 1), "q4_k -> bf16": (0.5625, 2), "q8_0 -> bf16": (1.0625, 2),
-                              "iq2_xxs -> f32": (0.2578, 4)}.items():
-            n = 58720256
+        # streaming ceilings at representative read:write mixes (bytes per value) and sizes (values)
+        for key, (rb, wb, n) in {"1:1 copy": (1, 1, 58720256), "q4_k -> bf16": (0.5625, 2, 58720256),
+                                 "q8_0 -> bf16": (1.0625, 2, 58720256), "iq2_xxs -> f32": (0.2578, 4, 58720256),
+                                 "q4_k [4096, 4096] -> bf16": (0.5625, 2, 16777216),
+                                 "q6_k [4096, 4096] -> bf16": (0.8203125, 2, 16777216)}.items():
             ceilings[key] = stream_ceiling(torch, nq, int(rb * n), int(wb * n))
             log(f"stream ceiling {key}: {ceilings[key]['gbps']} GB/s")
         # every format at the [14336, 4096] shape -> bf16

@@ -22,7 +22,8 @@
 //                 (staging_nt), 0 ordinary, 1 non-temporal for every format
 //   NQ_UPT        units (8 outputs) per thread per tile for every launch
 //                 (default: chosen per launch from its size, see choose_upt)
-//   NQ_UPT_MAX    cap on that choice for every format (default: per format, upt_max)
+//   NQ_UPT_LONG   tile size of long launches for every format (default: per
+//                 format, upt_long)
 //   NQ_RESIDENT_PER_CU  workgroups a compute unit holds at once, the scale of
 //                 the per-launch tile-size choice
 //   NQ_NT_STORE   non-temporal output stores: 0 never, 1 always, 2 16-bit outputs only
@@ -260,13 +261,16 @@ NQ_HD inline void div_magic(uint64_t d, uint32_t *m, uint32_t *s) {
 constexpr int WG = 256;  // threads per workgroup (4 wave64)
 
 // ---------------------------------------------------------------------------
-// LDS-staged decode.  A workgroup copies each full tile's payload bytes into
-// LDS with coalesced 16-byte loads (one to three per thread), loads of the
-// next tile in flight while the current one decodes from LDS; the unit
-// decoders are unchanged and read through LdsSrc.  Every global dword index
-// is clamped to the last payload dword, so staging never leaves the payload.
-// The phases (stage_load, stage_store, decode_staged) are host-compilable so
-// the emulator can run them in barrier order.
+// LDS-staged decode.  A workgroup decodes one tile.  It copies a full tile's
+// payload bytes into LDS with coalesced 16-byte loads, Stage::NK per thread
+// (1 to 5, by format and tile size), all issued before the lookup tables are
+// filled; after one barrier every thread decodes its units from LDS through
+// LdsSrc with the same unit decoders the direct path uses.  Latency is hidden
+// by the other workgroups resident on the compute unit, not by prefetching
+// inside one.  Every global dword index is clamped to the last payload dword,
+// so staging never leaves the payload.  The phases (stage_load, stage_store,
+// decode_staged) are host-compilable so the emulator can run them in barrier
+// order.
 // ---------------------------------------------------------------------------
 
 struct LdsSrc {
@@ -661,30 +665,41 @@ NQ_HD KArgs chunk_args(const LaunchArgs &L, uint64_t b0, uint64_t nb, uint32_t *
     return a;
 }
 
-// Units per thread per tile, from the launch's units per resident workgroup
-// q (the device holds `resident` workgroups at once; 2048 on MI355X), capped
-// per format.  Few units per resident workgroup call for small tiles, so
-// that every compute unit gets work:
-//   q < 128 -> 1,  < 1024 -> 2,  < 2048 -> 4,  else 8;
-//   large codebooks (IQ2_S, IQ1_S, IQ1_M, which copy 8-16 KiB to LDS per
-//   workgroup): q < 128 -> 1, < 256 -> 2, < 512 -> 4, < 1024 -> 8, else 16.
-// The cap (upt_max) is the tile size that decoded a [14336, 4096] tensor to
-// bf16 fastest on MI355X (2, 4 or 8, two runs each over rotations whose
-// payloads alone pass 1 GiB): smaller tiles keep more workgroups, and so
-// more independent loads and stores, in flight; formats whose workgroups
-// copy a codebook or fill a quotient table, and those with few payload bytes
-// per value (q2_k, tq2_0), do better with larger tiles.  Outputs that are not 16-byte aligned, and
-// f64 outputs, always take 8.  NQ_UPT, when defined, fixes the tile size of
-// every launch; NQ_UPT_MAX replaces every format's cap.
+// Units per thread per tile for a launch of `nunits` units.  With R the
+// workgroups the device holds at once (`resident`; 2048 on MI355X) and
+// tiles(u) = ceil(nunits / (256 u)) the launch's workgroups at u units per
+// thread, the choice counts rounds of R workgroups:
+//   - q = nunits / R below 128: 1 (under half a round even then);
+//   - tiles(L) >= 4R, L the format's long-launch size (upt_long): L.  Many
+//     rounds of small tiles: the workgroups drift apart, so loads and stores
+//     of several tiles are in flight on every compute unit throughout;
+//   - else the smallest of 2, 4, 8 whose tiles fit in one round, if one does:
+//     the whole launch starts at once, in as many workgroups as fit;
+//   - else L.
+// One to three rounds run nearly in step: each round starts only as the one
+// before drains, which left a launch of two rounds of 2-unit tiles 20% slower
+// than one round of 4-unit tiles ([4096, 4096] tensors to bf16, formats q4_0,
+// q4_k, q6_k, mxfp4, gguf:nvfp4, iq4_xs on MI355X; rows from 1024 to 14336 at
+// 4096 columns were measured for 12 formats and tile sizes 2, 4 and 8, over
+// rotations whose payloads alone pass 1 GiB).  L is the size that decoded a
+// [14336, 4096] tensor to bf16 fastest: smaller tiles keep more independent
+// loads and stores in flight; formats whose workgroups copy a codebook or
+// fill a quotient table, and those with few payload bytes per value (q2_k,
+// tq2_0), do better with larger tiles.
+// Large codebooks (IQ2_S, IQ1_S, IQ1_M, which copy 8-16 KiB to LDS per
+// workgroup) keep a rule by q alone: q < 128 -> 1, < 256 -> 2, < 512 -> 4,
+// else 8.  Outputs that are not 16-byte aligned, and f64 outputs, always take
+// 8.  NQ_UPT, when defined, fixes the tile size of every launch; NQ_UPT_LONG
+// replaces every format's L.
 template <int F>
 constexpr bool big_codebook() {
     return TabSpec<F>::n8 >= 1024;
 }
 
 template <int F>
-constexpr int upt_max() {
-#ifdef NQ_UPT_MAX
-    return NQ_UPT_MAX;
+constexpr int upt_long() {
+#ifdef NQ_UPT_LONG
+    return NQ_UPT_LONG;
 #else
     return (F == Q2_K || F == Q3_K || F == IQ2_XXS || F == IQ2_XS || F == IQ3_XXS || F == IQ1_S || F == IQ3_S ||
             F == IQ2_S || F == IQ1_M || F == TQ1_0 || F == TQ2_0 || F == NVFP4_DIV) ? 8
@@ -700,13 +715,20 @@ NQ_HD int choose_upt(uint64_t nunits, uint32_t resident) {
     (void)resident;
     return NQ_UPT;
 #else
-    const uint64_t q = nunits / (resident ? resident : 1u);
-    int u;
-    if constexpr (big_codebook<F>())
-        u = q < 128 ? 1 : q < 256 ? 2 : q < 512 ? 4 : q < 1024 ? 8 : 16;
-    else
-        u = q < 128 ? 1 : q < 1024 ? 2 : q < 2048 ? 4 : 8;
-    return u < upt_max<F>() ? u : upt_max<F>();
+    const uint64_t R = resident ? resident : 1u;
+    const uint64_t q = nunits / R;
+    if (q < 128) return 1;
+    if constexpr (big_codebook<F>()) {
+        const int u = q < 256 ? 2 : q < 512 ? 4 : 8;
+        return u < upt_long<F>() ? u : upt_long<F>();
+    } else {
+        constexpr int L = upt_long<F>();
+        auto tiles = [&](uint64_t u) { return (nunits + WG * u - 1) / (WG * u); };
+        if (tiles(L) >= 4 * R) return L;
+        for (int u = 2; u <= 8; u *= 2)
+            if (tiles(u) <= R) return u;
+        return L;
+    }
 #endif
 }
 
@@ -748,12 +770,7 @@ int launch(const LaunchArgs &L, hipStream_t stream) {
             case 2: st = launch_chunk<F, OT, 2, true>(L, b0, nb, stream); break;
             case 4: st = launch_chunk<F, OT, 4, true>(L, b0, nb, stream); break;
             case 8: st = launch_chunk<F, OT, 8, true>(L, b0, nb, stream); break;
-            default:
-                if constexpr (big_codebook<F>())
-                    st = launch_chunk<F, OT, 16, true>(L, b0, nb, stream);
-                else
-                    st = 9;  // unreachable: other formats top out at 8
-                break;
+            default: st = 9; break;  // unreachable: choose_upt returns 1, 2, 4 or 8
             }
 #endif
         }
@@ -822,7 +839,7 @@ int launch_many_chunk(MArgs &m, hipStream_t stream) {
 // takes several entries), and go(m, upt) receives each launch's arguments
 // with its units per thread.  The tile size follows the units of each launch
 // as for one tensor (choose_upt), limited to 2, 4 and 8 units per thread
-// (1 becomes 2, 16 becomes 8).  VEC: every output
+// (1 becomes 2).  VEC: every output
 // is 16-byte aligned (otherwise, and for f64 outputs, always 8).  CB: blocks
 // per launch chunk (chunk_blocks<F>(); smaller in the emulator).  Host code
 // shared by the launcher and the emulator.

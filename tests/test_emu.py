@@ -109,28 +109,45 @@ def test_emulated_tile_sizes(fmt, upt):
         assert _same(got, _oracle(fmt, p, nblocks, B, dtype), dtype)
 
 
-# The launcher's per-format cap on units per thread (upt_max in nq_kernel.h).
+# The launcher's tile size for long launches, per format (upt_long in nq_kernel.h).
 UPT_CAP = {f: 2 for f in FORMATS}
 UPT_CAP.update({f: 4 for f in ("gguf:q5_0", "gguf:q1_0", "gguf:q2_0")})
 UPT_CAP.update({f: 8 for f in ("gguf:q2_k", "gguf:q3_k", "gguf:iq2_xxs", "gguf:iq2_xs", "gguf:iq3_xxs", "gguf:iq1_s",
                                "gguf:iq3_s", "gguf:iq2_s", "gguf:iq1_m", "gguf:tq1_0", "gguf:tq2_0", "nvfp4")})
+BIG_CODEBOOK = ("gguf:iq2_s", "gguf:iq1_s", "gguf:iq1_m")
 
 
-def test_tile_size_classes():
-    """The launcher's size classes by units per resident workgroup q: below
-    128, 1024 and 2048 take 1, 2 and 4 units per thread, larger launches 8;
-    formats with codebooks of 8 KiB or more step up at 128, 256, 512 and 1024
-    to 2, 4, 8 and 16; every choice is capped per format."""
+def test_tile_size_by_rounds():
+    """The launcher's tile size for [rows, 4096] tensors with 2048 resident
+    workgroups (units = rows * 512; tiles = units / (256 * upt)): 1 below 128
+    units per resident workgroup; the long-launch size L when its tiles fill
+    the device four times over; otherwise the smallest of 2, 4, 8 whose tiles
+    fit in one round, else L.  Large codebooks step up by units per resident
+    workgroup alone, to at most 8."""
     g = 2048
-    plain = [(0, 1), (1, 1), (127, 1), (128, 2), (1023, 2), (1024, 4), (2047, 4), (2048, 8), (1 << 20, 8)]
-    big = [(0, 1), (127, 1), (128, 2), (255, 2), (256, 4), (511, 4), (512, 8), (1023, 8), (1024, 16), (1 << 20, 16)]
+    # rows -> choice, for L = 2, 4, 8
+    by_rows = {
+        256: (1, 1, 1),       # q = 64
+        512: (2, 2, 2),       # q = 128: tiles(2) = 512 fit
+        2048: (2, 2, 2),      # tiles(2) = 2048 = one round
+        2049: (4, 4, 4),      # tiles(2) = 2049 > 2048, tiles(4) fit
+        3072: (4, 4, 4),
+        4096: (4, 4, 4),      # tiles(4) = 2048
+        4097: (8, 8, 8),
+        6144: (8, 8, 8),
+        8192: (2, 8, 8),      # tiles(2) = 8192 = 4 rounds; L = 4: 4096 tiles, one fits at 8
+        8193: (2, 4, 8),      # no size fits in one round: L
+        14336: (2, 4, 8),
+        16384: (2, 4, 8),     # L = 4: tiles(4) = 8192, four rounds
+        1 << 20: (2, 4, 8),
+    }
+    big = {256: 1, 512: 2, 1023: 2, 1024: 4, 2047: 4, 2048: 8, 14336: 8, 1 << 20: 8}
     for fmt in FORMATS:
         fid = nq.format_query(fmt).id
-        table = big if fmt in ("gguf:iq2_s", "gguf:iq1_s", "gguf:iq1_m") else plain
-        for q, want in table:
-            want = min(want, UPT_CAP[fmt])
-            assert emu_lib.choose_upt(fid, q * g, g) == want, (fmt, q)
-            assert emu_lib.choose_upt(fid, q * g + g - 1, g) == want, (fmt, q)
+        col = {2: 0, 4: 1, 8: 2}[UPT_CAP[fmt]]
+        table = big if fmt in BIG_CODEBOOK else {r: w[col] for r, w in by_rows.items()}
+        for rows, want in table.items():
+            assert emu_lib.choose_upt(fid, rows * 512, g) == want, (fmt, rows)
         assert emu_lib.choose_upt(fid, 100, 0) == 1
 
 
