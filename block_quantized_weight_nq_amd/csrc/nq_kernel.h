@@ -673,8 +673,9 @@ NQ_HD KArgs chunk_args(const LaunchArgs &L, uint64_t b0, uint64_t nb, uint32_t *
 //   - tiles(L) >= 4R, L the format's long-launch size (upt_long): L.  Many
 //     rounds of small tiles: the workgroups drift apart, so loads and stores
 //     of several tiles are in flight on every compute unit throughout;
-//   - else the smallest of 2, 4, 8 whose tiles fit in one round, if one does:
-//     the whole launch starts at once, in as many workgroups as fit;
+//   - else the smallest of 2 (4 for "nvfp4", upt_first), 4, 8 whose tiles
+//     fit in one round, if one does: the whole launch starts at once, in as
+//     many workgroups as fit;
 //   - else L.
 // One to three rounds run nearly in step: each round starts only as the one
 // before drains, which left a launch of two rounds of 2-unit tiles 20% slower
@@ -702,10 +703,18 @@ constexpr int upt_long() {
     return NQ_UPT_LONG;
 #else
     return (F == Q2_K || F == Q3_K || F == IQ2_XXS || F == IQ2_XS || F == IQ3_XXS || F == IQ1_S || F == IQ3_S ||
-            F == IQ2_S || F == IQ1_M || F == TQ1_0 || F == TQ2_0 || F == NVFP4_DIV) ? 8
-         : (F == Q5_0 || F == Q1_0 || F == Q2_0) ? 4
+            F == IQ2_S || F == IQ1_M || F == TQ1_0 || F == TQ2_0) ? 8
+         : (F == Q5_0 || F == Q1_0 || F == Q2_0 || F == NVFP4_DIV) ? 4
          : 2;
 #endif
+}
+
+// The smallest tile size of the one-round choice: 4 for "nvfp4", whose
+// workgroups each fill a quotient table (two divisions per scale value) that
+// 2-unit tiles would fill once per 512 units, 2 otherwise.
+template <int F>
+constexpr int upt_first() {
+    return F == NVFP4_DIV ? 4 : 2;
 }
 
 template <int F>
@@ -725,7 +734,7 @@ NQ_HD int choose_upt(uint64_t nunits, uint32_t resident) {
         constexpr int L = upt_long<F>();
         auto tiles = [&](uint64_t u) { return (nunits + WG * u - 1) / (WG * u); };
         if (tiles(L) >= 4 * R) return L;
-        for (int u = 2; u <= 8; u *= 2)
+        for (int u = upt_first<F>(); u <= 8; u *= 2)
             if (tiles(u) <= R) return u;
         return L;
     }

@@ -82,6 +82,7 @@ struct EmuTiles {
             tab.nv_gu = a.gu < 0x7FFFFFFFull ? (uint32_t)a.gu : 0x7FFFFFFFu;
             tab.nv_dsign = nv_sign_bytes(divisor_at(tr, a, g0));
             std::fill(nvd.begin(), nvd.end(), bits_f32(0x7FA5A5A5u));
+            std::fill(nvq.begin(), nvq.end(), bits_f32(0x7FA5A5A5u));  // a table word the fill misses is NaN
         }
         if (TS::n8 + TS::n4 + TS::nf > 0)
             for (uint32_t tid = 0; tid < (uint32_t)WG; tid++)

@@ -111,9 +111,9 @@ def test_emulated_tile_sizes(fmt, upt):
 
 # The launcher's tile size for long launches, per format (upt_long in nq_kernel.h).
 UPT_CAP = {f: 2 for f in FORMATS}
-UPT_CAP.update({f: 4 for f in ("gguf:q5_0", "gguf:q1_0", "gguf:q2_0")})
+UPT_CAP.update({f: 4 for f in ("gguf:q5_0", "gguf:q1_0", "gguf:q2_0", "nvfp4")})
 UPT_CAP.update({f: 8 for f in ("gguf:q2_k", "gguf:q3_k", "gguf:iq2_xxs", "gguf:iq2_xs", "gguf:iq3_xxs", "gguf:iq1_s",
-                               "gguf:iq3_s", "gguf:iq2_s", "gguf:iq1_m", "gguf:tq1_0", "gguf:tq2_0", "nvfp4")})
+                               "gguf:iq3_s", "gguf:iq2_s", "gguf:iq1_m", "gguf:tq1_0", "gguf:tq2_0")})
 BIG_CODEBOOK = ("gguf:iq2_s", "gguf:iq1_s", "gguf:iq1_m")
 
 
@@ -122,8 +122,8 @@ def test_tile_size_by_rounds():
     workgroups (units = rows * 512; tiles = units / (256 * upt)): 1 below 128
     units per resident workgroup; the long-launch size L when its tiles fill
     the device four times over; otherwise the smallest of 2, 4, 8 whose tiles
-    fit in one round, else L.  Large codebooks step up by units per resident
-    workgroup alone, to at most 8."""
+    fit in one round (4, 8 for "nvfp4"), else L.  Large codebooks step up by
+    units per resident workgroup alone, to at most 8."""
     g = 2048
     # rows -> choice, for L = 2, 4, 8
     by_rows = {
@@ -146,6 +146,8 @@ def test_tile_size_by_rounds():
         fid = nq.format_query(fmt).id
         col = {2: 0, 4: 1, 8: 2}[UPT_CAP[fmt]]
         table = big if fmt in BIG_CODEBOOK else {r: w[col] for r, w in by_rows.items()}
+        if fmt == "nvfp4":  # one-round choices start at 4
+            table = {r: (4 if w == 2 else w) for r, w in table.items()}
         for rows, want in table.items():
             assert emu_lib.choose_upt(fid, rows * 512, g) == want, (fmt, rows)
         assert emu_lib.choose_upt(fid, 100, 0) == 1
