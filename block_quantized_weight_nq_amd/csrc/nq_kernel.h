@@ -18,8 +18,9 @@
 // Tuning knobs (compile-time; the defaults are the measured best on MI355X):
 //   NQ_NTL        1: load_stream4 (the row-scaled FP8 and product kernels'
 //                 streaming loads) is non-temporal
-//   NQ_STAGE_NT   the decode's staging loads: -1 (default) per format
-//                 (staging_nt), 0 ordinary, 1 non-temporal for every format
+//   NQ_STAGE_NT   the decode's staging loads: -1 (default) by launch size and
+//                 format (stage_nt), 0 ordinary, 1 non-temporal for every launch
+//   NQ_STAGE_NT_UNITS  launches below this many units stage non-temporally
 //   NQ_UPT        units (8 outputs) per thread per tile for every launch
 //                 (default: chosen per launch from its size, see choose_upt)
 //   NQ_UPT_LONG   tile size of long launches for every format (default: per
@@ -292,19 +293,36 @@ struct LdsSrc {
     }
 };
 
-// Cache policy of the staging loads, measured per format on MI355X
-// ([14336, 4096] tensors to bf16 over rotations whose payloads alone pass
-// 1 GiB, so every launch reads HBM): ordinary and non-temporal loads come
-// within about 1% of each other for most formats at their best tile size;
-// ordinary loads are ahead by up to 12% on the small tiles of the codebook
-// formats, non-temporal ones by about 1% on the three 8-bit formats (q8_0,
-// q8_1, q8_k), which read the most payload bytes per value.
+// Cache policy of the staging loads, by launch size, measured on MI355X
+// over rotations whose payloads alone pass 1 GiB (so every launch reads
+// HBM):
+//   - launches below NQ_STAGE_NT_UNITS units (6 * 2^20, 48 M values) load
+//     non-temporally: 7-15% faster than ordinary loads at [1024, 4096] to
+//     bf16, 0-6% at [4096, 4096] and [4096, 14336] (21 formats);
+//   - longer launches take the format's choice (staging_nt): non-temporal
+//     for the three 8-bit formats (q8_0, q8_1, q8_k), which read the most
+//     payload bytes per value, and "nvfp4" (1-4% ahead at [14336, 4096]);
+//     ordinary for the rest, which came within 2% either way at
+//     [14336, 4096] but lost up to 5% non-temporally (q6_k, tq2_0) in the
+//     long many-tensor launches of a weight set.
+// The policy is a template argument of the kernels (two instantiations):
+// under a run-time switch, two global loads that differ only in the
+// non-temporal hint are merged by the compiler and lose it.
+#ifndef NQ_STAGE_NT_UNITS
+#define NQ_STAGE_NT_UNITS (6u << 20)
+#endif
 template <int F>
 constexpr bool staging_nt() {
+    return F == Q8_0 || F == Q8_1 || F == Q8_K || F == NVFP4_DIV;
+}
+
+template <int F>
+NQ_HD bool stage_nt(uint64_t units) {
 #if NQ_STAGE_NT >= 0
+    (void)units;
     return NQ_STAGE_NT != 0;
 #else
-    return F == Q8_0 || F == Q8_1 || F == Q8_K;
+    return units < (uint64_t)NQ_STAGE_NT_UNITS || staging_nt<F>();
 #endif
 }
 
@@ -348,7 +366,7 @@ NQ_HD uint32_t staged_tiles(const KArgs &a) {
 
 // Global loads of tile t's chunks for this thread (into registers); t is a
 // staged tile, so every chunk lies inside the payload.
-template <int F, int UPT, class Src>
+template <int F, int UPT, bool NT, class Src>
 NQ_HD void stage_load(const Src &src, const KArgs &a, uint32_t t, uint32_t tid, uint32_t (&r)[Stage<F, UPT>::NK][4]) {
     using ST = Stage<F, UPT>;
     uint32_t cmax;
@@ -356,7 +374,7 @@ NQ_HD void stage_load(const Src &src, const KArgs &a, uint32_t t, uint32_t tid, 
 #pragma unroll
     for (uint32_t k = 0; k < ST::NK; k++) {
         const uint32_t c0 = k * WG + tid;
-        src.template load4<staging_nt<F>()>(a0 + 4u * (c0 < cmax ? c0 : cmax), r[k]);
+        src.template load4<NT>(a0 + 4u * (c0 < cmax ? c0 : cmax), r[k]);
     }
 }
 
@@ -504,7 +522,7 @@ NQ_HD void fill_tables(uint64_t *t8, uint32_t *t4, float *nvq, float *nvd, const
 // decoded from global memory when it is not staged).  The tile's loads are
 // issued before the lookup tables are filled, so the two latencies overlap,
 // and one barrier publishes both.  The LDS arrays are the kernel's.
-template <int F, int OT, int UPT, bool VEC>
+template <int F, int OT, int UPT, bool VEC, bool NT>
 __device__ __forceinline__ void decode_tile(const KArgs &a, uint32_t t, uint32_t tid, uint64_t *t8, uint32_t *t4,
                                             float *nvq, float *nvd, uint32_t *lds) {
     using TS = TabSpec<F>;
@@ -520,7 +538,7 @@ __device__ __forceinline__ void decode_tile(const KArgs &a, uint32_t t, uint32_t
     }
     if (t < staged_tiles<F, UPT>(a)) {
         uint32_t r[ST::NK][4];
-        stage_load<F, UPT>(src, a, t, tid, r);
+        stage_load<F, UPT, NT>(src, a, t, tid, r);
         if constexpr (TS::n8 + TS::n4 + TS::nf > 0) fill_tables<F>(t8, t4, nvq, nvd, tr, a, g0, tid, WG);
         stage_store<F, UPT>(lds, a, t, tid, r);
         __syncthreads();
@@ -546,12 +564,13 @@ __device__ __forceinline__ void decode_tile(const KArgs &a, uint32_t t, uint32_t
 // many workgroups in flight as LDS and registers allow.  STACKED: an "nvfp4"
 // launch with more than one divisor; otherwise the divisor count is the
 // constant 1, and the code for units past the first divisor group compiles
-// away (that code cost the one-divisor decode 10-15%).
-template <int F, int OT, int UPT, bool VEC, bool STACKED>
+// away (that code cost the one-divisor decode 10-15%).  NT: non-temporal
+// staging loads (stage_nt).
+template <int F, int OT, int UPT, bool VEC, bool STACKED, bool NT>
 __global__ __launch_bounds__(WG) void k_decode(KArgs a) {
     NQ_DECODE_LDS(F, UPT);
     if constexpr (!STACKED) a.ndiv = 1;
-    decode_tile<F, OT, UPT, VEC>(a, blockIdx.x, threadIdx.x, t8, t4, nvq, nvd, lds);
+    decode_tile<F, OT, UPT, VEC, NT>(a, blockIdx.x, threadIdx.x, t8, t4, nvq, nvd, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -612,13 +631,13 @@ NQ_HD uint32_t many_find(const MArgs &m, uint32_t b) {
     return lo;
 }
 
-template <int F, int OT, int UPT, bool VEC>
+template <int F, int OT, int UPT, bool VEC, bool NT>
 __global__ __launch_bounds__(WG) void k_decode_many(MArgs m) {
     NQ_DECODE_LDS(F, UPT);
     const uint32_t b = blockIdx.x;
     const uint32_t j = many_find(m, b);
     const KArgs a = many_entry_args(m.t[j]);
-    decode_tile<F, OT, UPT, VEC>(a, b - m.t[j].tile0, threadIdx.x, t8, t4, nvq, nvd, lds);
+    decode_tile<F, OT, UPT, VEC, NT>(a, b - m.t[j].tile0, threadIdx.x, t8, t4, nvq, nvd, lds);
 }
 
 // Host launch description for one call.
@@ -751,10 +770,18 @@ template <int F, int OT, int UPT, bool VEC>
 int launch_chunk(const LaunchArgs &L, uint64_t b0, uint64_t nb, hipStream_t stream) {
     uint32_t grid;
     const KArgs a = chunk_args<F, OT, UPT>(L, b0, nb, &grid);
-    if (F == NVFP4_DIV && a.ndiv > 1)
-        hipLaunchKernelGGL((k_decode<F, OT, UPT, VEC, F == NVFP4_DIV>), dim3(grid), dim3(WG), 0, stream, a);
-    else
-        hipLaunchKernelGGL((k_decode<F, OT, UPT, VEC, false>), dim3(grid), dim3(WG), 0, stream, a);
+    const bool nt = stage_nt<F>(L.nblocks * (block_values(F) / 8));  // by the whole tensor's units
+    if (F == NVFP4_DIV && a.ndiv > 1) {
+        if (nt)
+            hipLaunchKernelGGL((k_decode<F, OT, UPT, VEC, F == NVFP4_DIV, true>), dim3(grid), dim3(WG), 0, stream, a);
+        else
+            hipLaunchKernelGGL((k_decode<F, OT, UPT, VEC, F == NVFP4_DIV, false>), dim3(grid), dim3(WG), 0, stream, a);
+    } else {
+        if (nt)
+            hipLaunchKernelGGL((k_decode<F, OT, UPT, VEC, false, true>), dim3(grid), dim3(WG), 0, stream, a);
+        else
+            hipLaunchKernelGGL((k_decode<F, OT, UPT, VEC, false, false>), dim3(grid), dim3(WG), 0, stream, a);
+    }
     return hipGetLastError() == hipSuccess ? 0 : 9;  // NQ_ERR_HIP
 }
 
@@ -837,18 +864,21 @@ NQ_HD bool many_number_tiles(MArgs &m) {
 }
 
 template <int F, int OT, int UPT, bool VEC>
-int launch_many_chunk(MArgs &m, hipStream_t stream) {
+int launch_many_chunk(MArgs &m, bool nt, hipStream_t stream) {
     if (!many_number_tiles<UPT>(m)) return 9;  // NQ_ERR_HIP: cannot be launched as one grid
-    hipLaunchKernelGGL((k_decode_many<F, OT, UPT, VEC>), dim3(m.ntiles), dim3(WG), 0, stream, m);
+    if (nt)
+        hipLaunchKernelGGL((k_decode_many<F, OT, UPT, VEC, true>), dim3(m.ntiles), dim3(WG), 0, stream, m);
+    else
+        hipLaunchKernelGGL((k_decode_many<F, OT, UPT, VEC, false>), dim3(m.ntiles), dim3(WG), 0, stream, m);
     return hipGetLastError() == hipSuccess ? 0 : 9;
 }
 
 // Launches of `n` non-empty tensors of format F to output type OT: entries
 // are packed MANY_MAX to a launch (a tensor larger than one launch chunk
-// takes several entries), and go(m, upt) receives each launch's arguments
-// with its units per thread.  The tile size follows the units of each launch
-// as for one tensor (choose_upt), limited to 2, 4 and 8 units per thread
-// (1 becomes 2).  VEC: every output
+// takes several entries), and go(m, upt, nt) receives each launch's
+// arguments with its units per thread and staging cache policy.  Both follow
+// the units of each launch as for one tensor (choose_upt, stage_nt), the
+// tile size limited to 2, 4 and 8 units per thread (1 becomes 2).  VEC: every output
 // is 16-byte aligned (otherwise, and for f64 outputs, always 8).  CB: blocks
 // per launch chunk (chunk_blocks<F>(); smaller in the emulator).  Host code
 // shared by the launcher and the emulator.
@@ -862,7 +892,7 @@ int many_plan(const ManyItem *items, int n, uint32_t resident, uint64_t CB, Go &
         if (m.n == 0) return 0;
         const int c = choose_upt<F>(units, resident);
         const int upt = (VEC && OT != 3) ? (c <= 2 ? 2 : c == 4 ? 4 : 8) : 8;
-        const int st = go(m, upt);
+        const int st = go(m, upt, stage_nt<F>(units));
         m.n = 0;
         units = 0;
         return st;
@@ -883,12 +913,12 @@ int many_plan(const ManyItem *items, int n, uint32_t resident, uint64_t CB, Go &
 
 template <int F, int OT, bool VEC>
 int launch_many(const ManyItem *items, int n, uint32_t resident, hipStream_t stream) {
-    return many_plan<F, OT, VEC>(items, n, resident, chunk_blocks<F>(), [&](MArgs &m, int upt) -> int {
+    return many_plan<F, OT, VEC>(items, n, resident, chunk_blocks<F>(), [&](MArgs &m, int upt, bool nt) -> int {
         if constexpr (VEC && OT != 3) {
-            if (upt == 2) return launch_many_chunk<F, OT, 2, VEC>(m, stream);
-            if (upt == 4) return launch_many_chunk<F, OT, 4, VEC>(m, stream);
+            if (upt == 2) return launch_many_chunk<F, OT, 2, VEC>(m, nt, stream);
+            if (upt == 4) return launch_many_chunk<F, OT, 4, VEC>(m, nt, stream);
         }
-        return launch_many_chunk<F, OT, 8, VEC>(m, stream);
+        return launch_many_chunk<F, OT, 8, VEC>(m, nt, stream);
     });
 }
 

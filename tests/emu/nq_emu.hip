@@ -92,7 +92,7 @@ struct EmuTiles {
             std::fill(slot.begin() + ST::SLOT_DW, slot.end(), GUARD_WORD);
             for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) {
                 uint32_t r[ST::NK][4];
-                stage_load<F, UPT>(src, a, t, tid, r);
+                stage_load<F, UPT, false>(src, a, t, tid, r);  // the policy changes no value
                 stage_store<F, UPT>(slot.data(), a, t, tid, r);
             }
             for (uint32_t i = ST::SLOT_DW; i < ST::SLOT_DW + GUARD; i++)
@@ -195,7 +195,7 @@ long run_many(const nq::ManyItem *items, int n, uint32_t resident, uint64_t chun
     long errors = 0;
     *launches_out = 0;
     *upt_mask = 0;
-    auto go = [&](MArgs &m, int upt) -> int {
+    auto go = [&](MArgs &m, int upt, bool) -> int {
         (*launches_out)++;
         *upt_mask |= 1 << upt;
         long e;
