@@ -708,7 +708,8 @@ NQ_HD KArgs chunk_args(const LaunchArgs &L, uint64_t b0, uint64_t nb, uint32_t *
 // tq2_0), do better with larger tiles.
 // Large codebooks (IQ2_S, IQ1_S, IQ1_M, which copy 8-16 KiB to LDS per
 // workgroup) keep a rule by q alone: q < 128 -> 1, < 256 -> 2, < 512 -> 4,
-// else 8.  Outputs that are not 16-byte aligned, and f64 outputs, always take
+// else 8.  The upt_wide formats take 16 from q = 3072 on, ahead of both
+// rules.  Outputs that are not 16-byte aligned, and f64 outputs, always take
 // 8.  NQ_UPT, when defined, fixes the tile size of every launch; NQ_UPT_LONG
 // replaces every format's L.
 template <int F>
@@ -726,6 +727,17 @@ constexpr int upt_long() {
          : (F == Q5_0 || F == Q1_0 || F == Q2_0 || F == NVFP4_DIV) ? 4
          : 2;
 #endif
+}
+
+// Formats whose long launches take 16-unit tiles (q >= 3072: a [14336, 4096]
+// tensor in 1792 workgroups, one round): the ones that copy the largest
+// codebooks to LDS per workgroup (IQ1_M, IQ1_S 16 KiB, IQ2_S 8 KiB, IQ2_XS
+// 4 KiB) and IQ3_S.  To bf16 at [14336, 4096] they ran 6-9% faster than with
+// 8-unit tiles over cold rotations; IQ2_XXS, IQ3_XXS and the formats without
+// codebooks ran 3-13% slower.
+template <int F>
+constexpr bool upt_wide() {
+    return F == IQ1_M || F == IQ1_S || F == IQ2_S || F == IQ2_XS || F == IQ3_S;
 }
 
 // The smallest tile size of the one-round choice: 4 for "nvfp4", whose
@@ -746,6 +758,7 @@ NQ_HD int choose_upt(uint64_t nunits, uint32_t resident) {
     const uint64_t R = resident ? resident : 1u;
     const uint64_t q = nunits / R;
     if (q < 128) return 1;
+    if (upt_wide<F>() && q >= 3072) return 16;
     if constexpr (big_codebook<F>()) {
         const int u = q < 256 ? 2 : q < 512 ? 4 : 8;
         return u < upt_long<F>() ? u : upt_long<F>();
@@ -806,7 +819,13 @@ int launch(const LaunchArgs &L, hipStream_t stream) {
             case 2: st = launch_chunk<F, OT, 2, true>(L, b0, nb, stream); break;
             case 4: st = launch_chunk<F, OT, 4, true>(L, b0, nb, stream); break;
             case 8: st = launch_chunk<F, OT, 8, true>(L, b0, nb, stream); break;
-            default: st = 9; break;  // unreachable: choose_upt returns 1, 2, 4 or 8
+            case 16:
+                if constexpr (upt_wide<F>())
+                    st = launch_chunk<F, OT, 16, true>(L, b0, nb, stream);
+                else
+                    st = 9;  // unreachable: only upt_wide formats take 16
+                break;
+            default: st = 9; break;  // unreachable: choose_upt returns 1, 2, 4, 8 or 16
             }
 #endif
         }
@@ -878,7 +897,7 @@ int launch_many_chunk(MArgs &m, bool nt, hipStream_t stream) {
 // takes several entries), and go(m, upt, nt) receives each launch's
 // arguments with its units per thread and staging cache policy.  Both follow
 // the units of each launch as for one tensor (choose_upt, stage_nt), the
-// tile size limited to 2, 4 and 8 units per thread (1 becomes 2).  VEC: every output
+// tile size limited to 2, 4 and 8 units per thread (1 becomes 2, 16 becomes 8).  VEC: every output
 // is 16-byte aligned (otherwise, and for f64 outputs, always 8).  CB: blocks
 // per launch chunk (chunk_blocks<F>(); smaller in the emulator).  Host code
 // shared by the launcher and the emulator.

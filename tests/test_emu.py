@@ -115,6 +115,7 @@ UPT_CAP.update({f: 4 for f in ("gguf:q5_0", "gguf:q1_0", "gguf:q2_0", "nvfp4")})
 UPT_CAP.update({f: 8 for f in ("gguf:q2_k", "gguf:q3_k", "gguf:iq2_xxs", "gguf:iq2_xs", "gguf:iq3_xxs", "gguf:iq1_s",
                                "gguf:iq3_s", "gguf:iq2_s", "gguf:iq1_m", "gguf:tq1_0", "gguf:tq2_0")})
 BIG_CODEBOOK = ("gguf:iq2_s", "gguf:iq1_s", "gguf:iq1_m")
+UPT_WIDE = BIG_CODEBOOK + ("gguf:iq2_xs", "gguf:iq3_s")  # 16-unit tiles from 3072 units per resident workgroup
 
 
 def test_tile_size_by_rounds():
@@ -123,7 +124,8 @@ def test_tile_size_by_rounds():
     units per resident workgroup; the long-launch size L when its tiles fill
     the device four times over; otherwise the smallest of 2, 4, 8 whose tiles
     fit in one round (4, 8 for "nvfp4"), else L.  Large codebooks step up by
-    units per resident workgroup alone, to at most 8."""
+    units per resident workgroup alone, to at most 8; the widest-codebook
+    formats and IQ3_S take 16 from 3072 units per resident workgroup."""
     g = 2048
     # rows -> choice, for L = 2, 4, 8
     by_rows = {
@@ -141,13 +143,15 @@ def test_tile_size_by_rounds():
         16384: (2, 4, 8),     # L = 4: tiles(4) = 8192, four rounds
         1 << 20: (2, 4, 8),
     }
-    big = {256: 1, 512: 2, 1023: 2, 1024: 4, 2047: 4, 2048: 8, 14336: 8, 1 << 20: 8}
+    big = {256: 1, 512: 2, 1023: 2, 1024: 4, 2047: 4, 2048: 8, 12287: 8, 12288: 16, 14336: 16, 1 << 20: 16}
     for fmt in FORMATS:
         fid = nq.format_query(fmt).id
         col = {2: 0, 4: 1, 8: 2}[UPT_CAP[fmt]]
         table = big if fmt in BIG_CODEBOOK else {r: w[col] for r, w in by_rows.items()}
         if fmt == "nvfp4":  # one-round choices start at 4
             table = {r: (4 if w == 2 else w) for r, w in table.items()}
+        if fmt in UPT_WIDE:  # q = rows / 4 >= 3072
+            table = {r: (16 if r >= 4 * 3072 else w) for r, w in table.items()}
         for rows, want in table.items():
             assert emu_lib.choose_upt(fid, rows * 512, g) == want, (fmt, rows)
         assert emu_lib.choose_upt(fid, 100, 0) == 1

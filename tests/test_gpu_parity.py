@@ -175,12 +175,12 @@ def test_every_tile_size_class(fmt):
     """Launch sizes that take each of the launcher's tile sizes (units per
     resident workgroup q, 8 resident per compute unit: 100 -> 1, 200 -> 2,
     600 -> 4, 1500 -> 8, 2100 -> the format's long-launch size; the IQ
-    formats with large codebooks step up by q alone), each one block past a
+    formats with large codebooks step up by q alone, to 16 at 3100), each one block past a
     whole number of units per workgroup, to f32 and bf16, compared in full."""
     info = nq.format_query(fmt)
     B = info.block_values
     resident = 8 * torch.cuda.get_device_properties(0).multi_processor_count
-    qs = (100, 200, 400, 800, 1500, 2100) if fmt in ("gguf:iq1_m", "gguf:iq2_s") else (100, 200, 600, 1500, 2100)
+    qs = (100, 200, 400, 800, 1500, 2100, 3100) if fmt in ("gguf:iq1_m", "gguf:iq2_s") else (100, 200, 600, 1500, 2100)
     for q in qs:
         n = resident * q * 8 + B
         nb = n // B
