@@ -458,7 +458,7 @@ NQ_API int nq_gemm_q8_1_workspace(int32_t format, int64_t N, int64_t K, int64_t 
     const int st = nq_validate_gemm_q8_1(format, wbytes, N, K, M);
     if (st != NQ_OK) return st;
     if ((uint64_t)M >= nq::GM_MIN_M)
-        *bytes = nq::gm_ws_layout(format, nq::gm_plan((uint64_t)N, (uint64_t)K, (uint64_t)M, compute_units()),
+        *bytes = nq::gm_ws_layout(format, nq::gm_plan(format, (uint64_t)N, (uint64_t)K, (uint64_t)M, compute_units()),
                                   (uint64_t)N, (uint64_t)K, (uint64_t)M)
                      .total;
     return NQ_OK;

@@ -710,11 +710,20 @@ inline GmPlan gm_plan_plain(const GmPlan &p, uint64_t K) {
     return GmPlan{1u, (uint32_t)((K / 32 + sp - 1) / sp), false, sp};
 }
 
-inline GmPlan gm_plan(uint64_t N, uint64_t K, uint64_t M, uint32_t cus) {
+// Activation rows above which format f's weight is rewritten once per call
+// (into the workspace) instead of per tile.  At 320 and 384 rows
+// ([14336, 4096] and [4096, 14336]) the per-tile rewrite measured 6-13%
+// faster for q4_k, q2_k and tq2_0 (and 0-9% for q8_k), while q4_0, q4_1,
+// q5_0, q5_k, iq2_xxs and iq3_s lost 5-21% without the once-per-call copy.
+NQ_HD constexpr uint64_t gm_rewrite_m(int f) {
+    return (f == Q4_K || f == Q2_K || f == TQ2_0 || f == Q8_K) ? 384u : GM_REWRITE_ONCE_M;
+}
+
+inline GmPlan gm_plan(int f, uint64_t N, uint64_t K, uint64_t M, uint32_t cus) {
     const uint64_t bm = gm_bm(M), tiles = (N + GM_BN - 1) / GM_BN * ((M + bm - 1) / bm);
     const uint64_t c = cus ? cus : 1u;
     const uint32_t sp0 = bm == 64u && tiles > 2ull * c ? 4u : GM_SP;
-    const GmPlan p{1u, (uint32_t)((K / 32 + sp0 - 1) / sp0), M > GM_REWRITE_ONCE_M, sp0};
+    const GmPlan p{1u, (uint32_t)((K / 32 + sp0 - 1) / sp0), M > gm_rewrite_m(f), sp0};
     if (tiles >= 2ull * c) return p;
     // K split; with 64-row tiles, five eighths to two per compute unit, into
     // 4-span steps and enough ranges for three workgroups per compute unit
@@ -809,7 +818,7 @@ uint64_t gm_max_rows(const GvLaunch &L) {
 template <int F>
 int launch_gemm_mfma(const GvLaunch &L, void *ws, uint64_t ws_bytes, hipStream_t stream) {
     const uint64_t max_rows = gm_max_rows<F>(L);
-    GmPlan p = gm_plan(L.N, L.K, L.M, L.cus);
+    GmPlan p = gm_plan(F, L.N, L.K, L.M, L.cus);
     const bool use = ws != nullptr && ws_bytes >= gm_ws_layout(F, p, L.N, L.K, L.M).total &&
                      (p.nsplit > 1 || p.rewrite_once);
     if (!use) p = gm_plan_plain(p, L.K);

@@ -307,9 +307,10 @@ int nq_gemv_q8_1(int32_t format, const void *weight, uint64_t nbytes, int64_t N,
  * owns, at least the size nq_gemm_q8_1_workspace reports, 16-byte aligned,
  * not overlapping the other buffers, and not used by another call until
  * this call's work on `stream` is done), and the partials are summed in
- * split order by a second launch.  Above 256 activation rows the weight's
- * 8-bit codes, scales and offsets are also written there once per call
- * (same values, same bits).  With workspace NULL or smaller than that size
+ * split order by a second launch.  Above 256 activation rows (384 for
+ * gguf:q4_k, gguf:q2_k, gguf:tq2_0 and gguf:q8_k) the weight's 8-bit codes,
+ * scales and offsets are also written there once per call (same values, same
+ * bits).  With workspace NULL or smaller than that size
  * the product runs unsplit and without the once-per-call rewrite.  Repeated
  * calls with the same shape, device and workspace choice (given or not)
  * give identical bits.

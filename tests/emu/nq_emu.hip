@@ -641,7 +641,7 @@ template <int F>
 long run_gemm(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y, uint64_t max_rows,
               uint64_t max_mrows, uint32_t cus, uint32_t *plan_out, char *err, int errlen) {
     using namespace nq;
-    GmPlan p = gm_plan(N, K, M, cus);
+    GmPlan p = gm_plan(F, N, K, M, cus);
     if (cus == 0) p = gm_plan_plain(GmPlan{1u, 0u, false, GM_SP}, K);
     *plan_out = p.nsplit | (p.rewrite_once ? 1u << 16 : 0u) | (p.sp == 4u ? 1u << 17 : 0u);
     const uint32_t bm = gm_bm(M);
@@ -730,7 +730,7 @@ extern "C" __attribute__((visibility("default"))) long nq_emu_gemm_q8_1(int fmt,
 // a workspace: K splits, steps per split, spans per step}.
 extern "C" __attribute__((visibility("default"))) void nq_emu_gemm_plan(int fmt, uint64_t N, uint64_t K, uint64_t M,
                                                                        uint32_t cus, uint64_t *out) {
-    const nq::GmPlan p = nq::gm_plan(N, K, M, cus), q = nq::gm_plan_plain(p, K);
+    const nq::GmPlan p = nq::gm_plan(fmt, N, K, M, cus), q = nq::gm_plan_plain(p, K);
     out[0] = p.nsplit;
     out[1] = p.sps;
     out[2] = p.sp;

@@ -531,7 +531,7 @@ def test_emu_gemm_plan_invariants(fmt):
     4 steps each, partials at most 2 GiB, only below two tiles per compute
     unit; 64-row tiles in 8-span steps within 512 workgroups); 4-span steps
     only with 64-row tiles; the weight rewritten once
-    exactly above 256 rows; the workspace is the partials plus the rewritten
+    exactly above 384 rows for q4_k and 256 for the others; the workspace is the partials plus the rewritten
     codes, scales and (q4_k) offsets, each rounded up to 256 bytes; without
     a workspace the plan is unsplit, in 8-span steps where 4-span ones came
     with a split."""
@@ -553,7 +553,7 @@ def test_emu_gemm_plan_invariants(fmt):
             else:
                 assert p["sps"] == steps
                 assert (p["sp"] == 4) == (bm == 64 and tiles > 512)
-            assert p["once"] == (M > 256)
+            assert p["once"] == (M > (384 if fmt == "gguf:q4_k" else 256))
             ws = _up(p["nsplit"] * M * N * 4) if p["nsplit"] > 1 else 0
             if p["once"]:
                 ws += _up(N * K) + _up(K // 32 * nh * N * 4) * (2 if aff else 1)
