@@ -726,8 +726,18 @@ inline GmPlan gm_plan(int f, uint64_t N, uint64_t K, uint64_t M, uint32_t cus) {
     const GmPlan p{1u, (uint32_t)((K / 32 + sp0 - 1) / sp0), M > gm_rewrite_m(f), sp0};
     if (tiles >= 2ull * c) return p;
     // K split; with 64-row tiles, five eighths to two per compute unit, into
-    // 4-span steps and enough ranges for three workgroups per compute unit
-    const bool mid = bm == 64u && 8u * tiles >= 5u * c;
+    // 4-span steps and enough ranges for three workgroups per compute unit,
+    // unless 8-span steps (two workgroups per compute unit, the split count
+    // rounded down) fill at least nine tenths of their slots while the
+    // 4-span split would spill a tail past its three per compute unit: at
+    // 0.625 tiles per compute unit (3 splits: 480 of 512 slots against 800
+    // workgroups for 768) that measured 1-10% faster on five formats, while
+    // at 0.75 (2 splits: 384 of 512) it lost 14-24%.
+    bool mid = bm == 64u && 8u * tiles >= 5u * c;
+    if (mid) {
+        const uint64_t s8 = 2u * c / tiles, s4 = (3u * c + tiles - 1) / tiles;
+        if (s8 >= 2u && 10u * s8 * tiles >= 18u * c && s4 * tiles > 3u * c) mid = false;
+    }
     const uint32_t sp = mid ? 4u : GM_SP;
     const uint64_t steps = (K / 32 + sp - 1) / sp, target = (mid ? 3ull : 2ull) * c;
     if (steps < 8) return p;

@@ -565,6 +565,7 @@ def test_emu_gemm_plan_invariants(fmt):
     assert plan(14336, 4096, 512) == (1, 4, 64)     # 896 tiles
     assert plan(4096, 14336, 512) == (3, 4, 64)     # 256 tiles: three splits in 4-span steps
     assert plan(4096, 14336, 384) == (4, 4, 64)     # 192 tiles
+    assert plan(4096, 14336, 320) == (3, 8, 64)     # 160 tiles: 8-span steps fill 480 of 512 slots
     assert plan(4096, 14336, 64) == (14, 8, 64)     # 32 tiles, 56 steps
     assert plan(14336, 4096, 16) == (4, 8, 16)      # 112 tiles of 16 rows
     assert plan(1024, 4096, 1100) == (3, 8, 64)     # 144 tiles: 3 splits (432 workgroups), not 4 (576)
