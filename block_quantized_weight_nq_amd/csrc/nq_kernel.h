@@ -149,17 +149,31 @@ struct KArgs {
     uint64_t gu;              // "nvfp4": units per divisor group (rows per source * K / 8)
 };
 
+// Output type codes: 0 binary32, 1 binary16, 2 bfloat16, 3 binary64 (the
+// C ABI's), and 4: binary32 with non-temporal stores, the launcher's choice
+// for short binary32 launches (NQ_F32_NT_UNITS).
+NQ_HD constexpr bool ot_f32(int ot) { return ot == 0 || ot == 4; }
+NQ_HD constexpr uint64_t ot_size(int ot) { return ot_f32(ot) ? 4u : ot == 3 ? 8u : 2u; }
+
 // Non-temporal 16-byte stores (streamed past the caches) pay off when each
 // store instruction of a wave covers whole cache lines: the 16-bit outputs,
 // where 64 lanes write one contiguous 1 KiB run.  The 32/64-bit outputs write
-// each line from two instructions and keep ordinary stores.  NQ_NT_STORE
-// overrides: 0 never, 1 always, 2 (default) 16-bit outputs only.
+// each line from two instructions and keep ordinary stores, except binary32
+// launches below NQ_F32_NT_UNITS units (3 * 2^18, 6 M values; output type
+// 4): over rotations whose payloads alone pass 1 GiB, non-temporal stores
+// decoded [64, 4096] to [1024, 4096] tensors to binary32 13-24% faster and
+// [2048, 4096] ones 11-15% slower, [8192, 4096] and larger ones 30-55%
+// slower (q4_0, q4_k, q8_0, nvfp4, iq2_xxs on MI355X).  NQ_NT_STORE
+// overrides: 0 never, 1 always, 2 (default) as described.
 #ifndef NQ_NT_STORE
 #define NQ_NT_STORE 2
 #endif
+#ifndef NQ_F32_NT_UNITS
+#define NQ_F32_NT_UNITS (3u << 18)
+#endif
 template <int OT>
 NQ_HD void vstore(void *p, u32x4 v) {
-    constexpr bool nt = NQ_NT_STORE == 1 || (NQ_NT_STORE == 2 && (OT == 1 || OT == 2));
+    constexpr bool nt = NQ_NT_STORE == 1 || (NQ_NT_STORE == 2 && (OT == 1 || OT == 2 || OT == 4));
 #if defined(__HIP_DEVICE_COMPILE__)
     if constexpr (nt) {
         __builtin_nontemporal_store(v, (u32x4 *)p);
@@ -175,7 +189,7 @@ NQ_HD void vstore(void *p, u32x4 v) {
 template <int OT, bool VEC>
 NQ_HD void store8(void *out, uint32_t u, const float (&y)[8]) {
     const uint64_t e = 8ull * u;
-    if constexpr (OT == 0) {
+    if constexpr (ot_f32(OT)) {
         float *o = (float *)out + e;
         if constexpr (VEC) {
             u32x4 a, b;
@@ -230,7 +244,7 @@ NQ_HD void store8(void *out, uint32_t u, const float (&y)[8]) {
 // One value at element e, converted as store8 converts it.
 template <int OT>
 NQ_HD void store1(void *out, uint64_t e, float y) {
-    if constexpr (OT == 0) {
+    if constexpr (ot_f32(OT)) {
         ((float *)out)[e] = y;
     } else if constexpr (OT == 1 || OT == 2) {
         f32x2 v;
@@ -664,7 +678,7 @@ constexpr uint64_t chunk_blocks() {
 template <int F, int OT, int UPT>
 NQ_HD KArgs chunk_args(const LaunchArgs &L, uint64_t b0, uint64_t nb, uint32_t *grid) {
     constexpr uint64_t S = block_bytes(F);
-    constexpr uint64_t OSZ = OT == 0 ? 4 : OT == 3 ? 8 : 2;
+    constexpr uint64_t OSZ = ot_size(OT);
     const uint8_t *p = L.payload + b0 * S;
     const uint8_t *tr = L.payload + L.nbytes - (F == NVFP4_DIV ? 4ull * L.ndiv : 0);
     KArgs a;
@@ -800,8 +814,10 @@ int launch_chunk(const LaunchArgs &L, uint64_t b0, uint64_t nb, hipStream_t stre
 
 template <int F, int OT>
 int launch(const LaunchArgs &L, hipStream_t stream) {
+    if constexpr (OT == 0 && NQ_NT_STORE == 2)
+        if (L.nblocks * (block_values(F) / 8) < (uint64_t)NQ_F32_NT_UNITS) return launch<F, 4>(L, stream);
     constexpr uint64_t CB = chunk_blocks<F>();
-    constexpr uint64_t OSZ = OT == 0 ? 4 : OT == 3 ? 8 : 2;
+    constexpr uint64_t OSZ = ot_size(OT);
     for (uint64_t b0 = 0; b0 < L.nblocks; b0 += CB) {
         const uint64_t nb = (L.nblocks - b0 < CB) ? L.nblocks - b0 : CB;
         const uintptr_t out = (uintptr_t)L.out + b0 * (uint64_t)block_values(F) * OSZ;
