@@ -1115,6 +1115,111 @@ __global__ __launch_bounds__(WG) void k_gemv(GvArgs a) {
     }
 }
 
+// One activation row, single-round kernel: the lane's items i = lane,
+// lane + 64, ... of the chunk (n items per row), each item's activation
+// columns read once and used for every row of the chunk; the first item's
+// columns (x0) were requested with the weight bytes.  Each row's partial
+// takes the items in the same order as gv_chunk_items.
+template <int F, int RW, class Act>
+NQ_HD void gv1_items1(const LdsSrc &ls, const GvChunk &c, uint32_t lane, uint32_t row_bytes, uint32_t n,
+                      const Act &act, const Tab &tab, const GvA &x0, float (&acc)[RW][1]) {
+    constexpr uint32_t IPB = GvItem<F>::IPB, S = (uint32_t)block_bytes(F);
+    for (uint32_t i = lane; i < n; i += 64u) {
+        const uint32_t bl = i / IPB, pt = i - bl * IPB;
+        GvA xi;
+        if (i != lane) gv_a<F>(act, 0u, c.c0 + bl, pt, xi);
+        const GvA &x = i == lane ? x0 : xi;
+#pragma unroll
+        for (int rr = 0; rr < RW; rr++)
+            if ((uint32_t)rr < c.rw) {
+                GvW w;
+                gv_w<F>(ls, c.o0 + (uint32_t)rr * row_bytes + bl * S, pt, tab, w);
+                acc[rr][0] = gv_dot<F>(w, x, acc[rr][0]);
+            }
+    }
+}
+
+// Single-round variant: when every chunk of the launch can be resident at
+// once, each wave takes exactly one chunk of RW whole rows and the launch's
+// waves cover all of them.  A wave requests all of its chunk's bytes before
+// anything else and then computes: nothing is issued after the weight
+// bytes, so no wave starts a second round of loads late in the transfer,
+// and the compute of waves whose bytes arrived early overlaps the loads
+// still in flight.  The bytes go straight from global memory into the
+// wave's LDS region (16-byte loads to LDS, lane l of load k filling group
+// 64k + l), so no registers hold them.  The launch's weight bytes start
+// 16-byte aligned (the host checks), so every group is one aligned 16-byte
+// load; a final group that passes the last weight dword is loaded by its
+// lane as the 16 bytes ending there and shifted into place (gv_put's rule),
+// so no load leaves the payload's dwords.  The activation is read from
+// global memory (cached); with one activation row, the columns of the
+// lane's first item are requested right behind the weight bytes.
+template <int F, int MT, int RW>
+__global__ __launch_bounds__(WG) void k_gemv1(GvArgs a, uint32_t region_dw) {
+    using TS = TabSpec<F>;
+    __shared__ uint64_t t8[TS::n8 > 0 ? TS::n8 : 1];
+    __shared__ uint32_t t4[TS::n4 > 0 ? TS::n4 : 1];
+    extern __shared__ __attribute__((aligned(16))) uint32_t gv_lds[];
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const uint32_t r = (blockIdx.x * GV_WAVES + wave) * (uint32_t)RW;
+    uint32_t *lds = gv_lds + wave * region_dw;
+    const bool live = r < a.rows;
+    GvChunk c{};
+    if (live) {
+        c = gv_chunk(a, r, 0u);
+        const uint32_t ng = c.g1 - c.g0 + 1u;
+        const bool tail = 4u * c.g1 + 3u > a.wlast;  // only the launch's last group can pass wlast
+        const uint32_t nfull = tail ? ng - 1u : ng;
+        for (uint32_t k = 0; 64u * k < ng; k++) {
+            const uint32_t j = 64u * k + lane;
+            if (j < nfull)
+                __builtin_amdgcn_global_load_lds((const void *)(a.wbase + 4u * (c.g0 + j)),
+                                                 (__attribute__((address_space(3))) void *)(lds + 256u * k), 16u, 0,
+                                                 NQ_NTL ? 2 : 0);
+        }
+        if (tail && lane == ((ng - 1u) & 63u)) {
+            uint32_t v[1][4];
+            const DevSrc src{a.wbase, a.wlast};
+            src.load_stream4(a.wlast - 3u, v[0]);
+            GvChunk one = c;
+            one.g0 = c.g1;  // gv_put's view: the single group g1 at the region's group ng - 1
+            gv_put<1>(one, a.wlast, 0u, v, lds + 4u * (ng - 1u));
+        }
+    }
+    const GvAct<false> act{a.xq, nullptr, a.K, a.kb, a.xrow, a.M};
+    constexpr uint32_t IPB = GvItem<F>::IPB;
+    const uint32_t n = live ? c.nb * IPB : 0u;
+    GvA x0;
+    if constexpr (MT == 1)
+        if (lane < n) gv_a<F>(act, 0u, c.c0 + lane / IPB, lane % IPB, x0);
+    if constexpr (TS::n8 + TS::n4 > 0) {
+        gv_fill_tables<F>(t8, t4, threadIdx.x);
+        __syncthreads();
+    }
+    if (!live) return;  // no workgroup barrier follows
+    float acc[RW][MT];
+#pragma unroll
+    for (int rr = 0; rr < RW; rr++)
+#pragma unroll
+        for (int m = 0; m < MT; m++) acc[rr][m] = 0.0f;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the 16-byte loads to LDS have landed
+    wave_lds_sync();                     // and the shifted last group's stores
+    const Tab tab{t8, t4, nullptr, nullptr, 0xFFFFFFFFu, 1u};
+    const LdsSrc ls{lds, 4u * (c.g1 - c.g0) + 3u};
+    if constexpr (MT == 1)
+        gv1_items1<F, RW>(ls, c, lane, a.row_bytes, n, act, tab, x0, acc);
+    else
+        gv_chunk_items<F, MT, RW>(ls, c, lane, a.M, a.row_bytes, act, tab, acc);
+#pragma unroll
+    for (int rr = 0; rr < RW; rr++)
+#pragma unroll
+        for (int m = 0; m < MT; m++) {
+            const float v = wave_sum63(acc[rr][m]);
+            if (lane == 63u && (uint32_t)rr < c.rw && m < (int)a.M) a.y[(uint64_t)m * a.ldy + r + (uint32_t)rr] = v;
+        }
+}
+
 // Host description of one product call.
 struct GvLaunch {
     const uint8_t *w;   // device weight payload [N, K]
@@ -1223,12 +1328,105 @@ int launch_gemv_mt(const GvLaunch &L, hipStream_t stream) {
     return gv_act_in_lds(L.M, L.K) ? launch_gemv_lds<F, MT, true>(L, stream) : launch_gemv_lds<F, MT, false>(L, stream);
 }
 
+#ifndef NQ_GV1
+#define NQ_GV1 1
+#endif
+
+// LDS dwords of a single-round wave region for chunks of rw rows: the
+// 16-byte groups the chunk can span at any start offset, plus one group of
+// padding.
+inline uint32_t gv1_region_dw(uint64_t row_bytes, uint32_t rw) {
+    return 4u * (uint32_t)((15u + rw * row_bytes + 15u) / 16u + 1u);
+}
+
+// Rows per chunk of the single-round launch, candidate k (0..2) in order of
+// preference: the fewest rows that fit (more, smaller chunks: less compute
+// per wave once its bytes are in), except that more than one activation row
+// takes two or three rows first (each activation read then serves every row
+// of the chunk) when two-row chunks still give every SIMD two waves.
+inline uint32_t gv1_candidate(uint64_t N, uint64_t M, uint32_t cus, int k) {
+    static const uint32_t few[3] = {1u, 2u, 3u}, more[3] = {2u, 3u, 1u};
+    return M > 1 && N / 2 >= 8u * (uint64_t)cus ? more[k] : few[k];
+}
+
+// A single-round launch: rows per chunk (0: none), wave region, LDS bytes
+// per workgroup and workgroups.
+struct Gv1Plan {
+    uint32_t rw, region_dw, lds, grid;
+};
+
+// The single-round plan of a launch of N rows of row_bytes bytes starting
+// at address w, on `cus` compute units; per_cu(rw, lds) gives the
+// workgroups of the rw-row kernel a compute unit holds at once with that
+// much dynamic LDS.  None (rw = 0) when the bytes do not start 16-byte
+// aligned, the launch holds fewer than 16 bytes or more than 32-bit byte
+// offsets reach (max_rows), or no candidate's chunks all fit at once.
+template <class PerCu>
+Gv1Plan gv1_plan(uint64_t N, uint64_t row_bytes, uint64_t M, uint64_t max_rows, uintptr_t w, uint32_t cus,
+                 PerCu per_cu) {
+    Gv1Plan p{0u, 0u, 0u, 0u};
+    if (!NQ_GV1 || (w & 15u) != 0u || N > max_rows || N * row_bytes < 16u) return p;
+    for (int k = 0; k < 3; k++) {
+        const uint32_t rw = gv1_candidate(N, M, cus, k);
+        const uint32_t region = gv1_region_dw(row_bytes, rw), lds = 4u * GV_WAVES * region;
+        const uint64_t chunks = (N + rw - 1) / rw, grid = (chunks + GV_WAVES - 1) / GV_WAVES;
+        if (lds > 65536u) continue;
+        const uint64_t held = (uint64_t)per_cu(rw, lds) * cus;
+        if (held >= 1u && grid <= held) {
+            p.rw = rw;
+            p.region_dw = region;
+            p.lds = lds;
+            p.grid = (uint32_t)grid;
+            return p;
+        }
+    }
+    return p;
+}
+
+template <int F, int MT, int RW>
+int gv1_per_cu(uint32_t lds) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)k_gemv1<F, MT, RW>, WG, lds) !=
+        hipSuccess)
+        return 0;
+    return per_cu;
+}
+
+// The single-round launch when its plan exists; -1 (nothing launched) when not.
+template <int F, int MT>
+int launch_gemv1(const GvLaunch &L, hipStream_t stream) {
+    const uint64_t row_bytes = L.K / (uint64_t)block_values(F) * (uint64_t)block_bytes(F);
+    const Gv1Plan p = gv1_plan(L.N, row_bytes, L.M, gv_max_rows<F>(L), (uintptr_t)L.w, L.cus,
+                               [](uint32_t rw, uint32_t lds) {
+                                   return rw == 1u ? gv1_per_cu<F, MT, 1>(lds)
+                                          : rw == 2u ? gv1_per_cu<F, MT, 2>(lds)
+                                                     : gv1_per_cu<F, MT, 3>(lds);
+                               });
+    if (p.rw == 0u) return -1;
+    GvArgs a = gv_args<F>(L, 0, L.N);
+    a.rw = p.rw;
+    a.cb = a.nbr;
+    if (p.rw == 1u)
+        hipLaunchKernelGGL((k_gemv1<F, MT, 1>), dim3(p.grid), dim3(WG), p.lds, stream, a, p.region_dw);
+    else if (p.rw == 2u)
+        hipLaunchKernelGGL((k_gemv1<F, MT, 2>), dim3(p.grid), dim3(WG), p.lds, stream, a, p.region_dw);
+    else
+        hipLaunchKernelGGL((k_gemv1<F, MT, 3>), dim3(p.grid), dim3(WG), p.lds, stream, a, p.region_dw);
+    return hipGetLastError() != hipSuccess ? 9 : 0;  // NQ_ERR_HIP
+}
+
+template <int F, int MT>
+int launch_gemv_m(const GvLaunch &L, hipStream_t s) {
+    const int st = launch_gemv1<F, MT>(L, s);
+    return st >= 0 ? st : launch_gemv_mt<F, MT>(L, s);
+}
+
 template <int F>
 int launch_gemv_f(const GvLaunch &L, hipStream_t s) {
-    if (L.M <= 1) return launch_gemv_mt<F, 1>(L, s);
-    if (L.M <= 2) return launch_gemv_mt<F, 2>(L, s);
-    if (L.M <= 4) return launch_gemv_mt<F, 4>(L, s);
-    return launch_gemv_mt<F, 8>(L, s);
+    if (L.M <= 1) return launch_gemv_m<F, 1>(L, s);
+    if (L.M <= 2) return launch_gemv_m<F, 2>(L, s);
+    if (L.M <= 4) return launch_gemv_m<F, 4>(L, s);
+    return launch_gemv_m<F, 8>(L, s);
 }
 
 }  // namespace nq

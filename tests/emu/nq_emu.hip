@@ -405,6 +405,97 @@ long run_gemv_lds(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, u
     return errors;
 }
 
+// The single-round product kernel (k_gemv1) for a plan the launcher made:
+// every wave's one chunk of p.rw rows, staged as the kernel stages it (the
+// 16-byte loads to LDS of groups g0 .. g1, each at a 16-byte aligned address
+// and inside the payload, and the last group's shifted load), into a
+// poisoned region whose size the plan gives; the staged bytes are compared
+// with the payload, then the lanes' items and each row's butterfly sum.
+template <int F, int MT, int RW>
+long run_gemv1(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y,
+               const nq::Gv1Plan &p, char *err, int errlen) {
+    using namespace nq;
+    const GvLaunch L{w, N, K, M, xq, y, 0u};
+    std::vector<uint64_t> t8(TabSpec<F>::n8 > 0 ? TabSpec<F>::n8 : 1);
+    std::vector<uint32_t> t4(TabSpec<F>::n4 > 0 ? TabSpec<F>::n4 : 1);
+    for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) gv_fill_tables<F>(t8.data(), t4.data(), tid);
+    const Tab tab{t8.data(), t4.data(), nullptr, nullptr, 0xFFFFFFFFu, 1u};
+    GvArgs a = gv_args<F>(L, 0, N);
+    a.rw = (uint32_t)RW;
+    a.cb = a.nbr;
+    if (a.wmis != 0u || ((uintptr_t)a.wbase & 15u) != 0u) {
+        snprintf(err, errlen, "single-round launch on weight bytes not 16-byte aligned");
+        return 1;
+    }
+    if (p.lds != 4u * GV_WAVES * p.region_dw || (uint64_t)p.grid * GV_WAVES * RW < N) {
+        snprintf(err, errlen, "plan: lds %u region %u grid %u for %llu rows", p.lds, p.region_dw, p.grid,
+                 (unsigned long long)N);
+        return 1;
+    }
+    Check chk{(uintptr_t)w, (uintptr_t)(w + N * a.row_bytes), 0, {0}};
+    const HostSrc src{a.wbase, a.wlast, &chk};
+    const GvAct<false> act{a.xq, nullptr, a.K, a.kb, a.xrow, a.M};
+    constexpr uint32_t IPB = GvItem<F>::IPB;
+    std::vector<uint32_t> lds(p.region_dw);
+    for (uint32_t b = 0; b < p.grid; b++)
+        for (uint32_t wave = 0; wave < GV_WAVES; wave++) {
+            const uint32_t r = (b * GV_WAVES + wave) * (uint32_t)RW;
+            if (r >= a.rows) continue;
+            const GvChunk c = gv_chunk(a, r, 0u);
+            const uint32_t ng = c.g1 - c.g0 + 1u;
+            const bool tail = 4u * c.g1 + 3u > a.wlast;
+            const uint32_t nfull = tail ? ng - 1u : ng;
+            if (4u * ng + 4u > p.region_dw) {
+                snprintf(err, errlen, "chunk of %u groups past its region of %u dwords", ng, p.region_dw);
+                return 1;
+            }
+            std::fill(lds.begin(), lds.end(), 0xA5A5A5A5u);
+            for (uint32_t j = 0; j < nfull; j++) {  // lane j % 64 of load j / 64
+                const uint32_t *g = a.wbase + 4u * (c.g0 + j);
+                if (((uintptr_t)g & 15u) != 0u && chk.errors++ == 0)
+                    snprintf(chk.msg, sizeof chk.msg, "16-byte load to LDS at %#lx not aligned", (unsigned long)g);
+                uint32_t v[4];
+                src.load<4>(4u * (c.g0 + j), v);
+                for (int e = 0; e < 4; e++) lds[4u * j + (uint32_t)e] = v[e];
+            }
+            if (tail) {
+                uint32_t v[1][4];
+                src.load_stream4(a.wlast - 3u, v[0]);
+                GvChunk one = c;
+                one.g0 = c.g1;
+                gv_put<1>(one, a.wlast, 0u, v, lds.data() + 4u * (ng - 1u));
+            }
+            for (uint32_t rr = 0; rr < c.rw; rr++) {
+                const uint8_t *cb = (const uint8_t *)lds.data() + c.o0 + rr * a.row_bytes;
+                const uint8_t *pb = w + (uint64_t)(c.r + rr) * a.row_bytes;
+                if (memcmp(cb, pb, a.row_bytes) != 0 && chk.errors++ == 0)
+                    snprintf(chk.msg, sizeof chk.msg, "staged chunk of row %u differs from the payload", c.r + rr);
+            }
+            const LdsSrc ls{lds.data(), 4u * (c.g1 - c.g0) + 3u};
+            const uint32_t n = c.nb * IPB;
+            static float acc[64][RW][MT];
+            for (uint32_t lane = 0; lane < 64u; lane++) {
+                for (int rr = 0; rr < RW; rr++)
+                    for (int m = 0; m < MT; m++) acc[lane][rr][m] = 0.0f;
+                if constexpr (MT == 1) {
+                    GvA x0;
+                    if (lane < n) gv_a<F>(act, 0u, c.c0 + lane / IPB, lane % IPB, x0);
+                    gv1_items1<F, RW>(ls, c, lane, a.row_bytes, n, act, tab, x0, acc[lane]);
+                } else {
+                    gv_chunk_items<F, MT, RW>(ls, c, lane, a.M, a.row_bytes, act, tab, acc[lane]);
+                }
+            }
+            for (uint32_t rr = 0; rr < c.rw; rr++)
+                for (int m = 0; m < MT; m++) {
+                    float v[64];
+                    for (int l = 0; l < 64; l++) v[l] = acc[l][rr][m];
+                    if (m < (int)a.M) a.y[(uint64_t)m * a.ldy + c.r + rr] = dpp_sum63(v);
+                }
+        }
+    if (chk.errors) snprintf(err, errlen, "%s", chk.msg);
+    return chk.errors;
+}
+
 template <int F, int MT, bool ALDS>
 long run_gemv_alds(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y,
                    uint32_t resident, uint64_t max_rows, char *err, int errlen) {
@@ -416,20 +507,41 @@ long run_gemv_alds(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, 
     }
 }
 
+// The launcher's choice: with gv1_cus > 0, the single-round plan on a device
+// of that many compute units, each holding min(gv1_per_cu, 160 KiB / (the
+// workgroup's LDS)) workgroups (the tables' static LDS included); when it
+// makes none, or with gv1_cus = 0, the chunk-loop kernel.  *rw_out: rows per
+// chunk of the single-round launch, 0 for the chunk loop.
 template <int F, int MT>
 long run_gemv(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y, uint32_t resident,
-              uint64_t max_rows, char *err, int errlen) {
+              uint64_t max_rows, uint32_t gv1_cus, uint32_t gv1_per_cu, uint32_t *rw_out, char *err, int errlen) {
+    using namespace nq;
+    *rw_out = 0u;
+    if (gv1_cus > 0u) {
+        const GvLaunch L{w, N, K, M, xq, y, gv1_cus};
+        const uint64_t row_bytes = K / (uint64_t)block_values(F) * (uint64_t)block_bytes(F);
+        constexpr uint32_t stat = 8u * (uint32_t)TabSpec<F>::n8 + 4u * (uint32_t)TabSpec<F>::n4;
+        const Gv1Plan p = gv1_plan(N, row_bytes, M, max_rows ? max_rows : gv_max_rows<F>(L), (uintptr_t)w, gv1_cus,
+                                   [&](uint32_t, uint32_t lds) {
+                                       const uint32_t by_lds = 163840u / (lds + stat);
+                                       return (int)(by_lds < gv1_per_cu ? by_lds : gv1_per_cu);
+                                   });
+        *rw_out = p.rw;
+        if (p.rw == 1u) return run_gemv1<F, MT, 1>(w, N, K, xq, M, y, p, err, errlen);
+        if (p.rw == 2u) return run_gemv1<F, MT, 2>(w, N, K, xq, M, y, p, err, errlen);
+        if (p.rw == 3u) return run_gemv1<F, MT, 3>(w, N, K, xq, M, y, p, err, errlen);
+    }
     return nq::gv_act_in_lds(M, K) ? run_gemv_alds<F, MT, true>(w, N, K, xq, M, y, resident, max_rows, err, errlen)
                                    : run_gemv_alds<F, MT, false>(w, N, K, xq, M, y, resident, max_rows, err, errlen);
 }
 
 template <int F>
 long run_gemv_m(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y, uint32_t res,
-                uint64_t max_rows, char *err, int errlen) {
-    if (M <= 1) return run_gemv<F, 1>(w, N, K, xq, M, y, res, max_rows, err, errlen);
-    if (M <= 2) return run_gemv<F, 2>(w, N, K, xq, M, y, res, max_rows, err, errlen);
-    if (M <= 4) return run_gemv<F, 4>(w, N, K, xq, M, y, res, max_rows, err, errlen);
-    return run_gemv<F, 8>(w, N, K, xq, M, y, res, max_rows, err, errlen);
+                uint64_t max_rows, uint32_t gv1_cus, uint32_t gv1_per_cu, uint32_t *rw_out, char *err, int errlen) {
+    if (M <= 1) return run_gemv<F, 1>(w, N, K, xq, M, y, res, max_rows, gv1_cus, gv1_per_cu, rw_out, err, errlen);
+    if (M <= 2) return run_gemv<F, 2>(w, N, K, xq, M, y, res, max_rows, gv1_cus, gv1_per_cu, rw_out, err, errlen);
+    if (M <= 4) return run_gemv<F, 4>(w, N, K, xq, M, y, res, max_rows, gv1_cus, gv1_per_cu, rw_out, err, errlen);
+    return run_gemv<F, 8>(w, N, K, xq, M, y, res, max_rows, gv1_cus, gv1_per_cu, rw_out, err, errlen);
 }
 
 // The 16 x 16 x 32 8-bit matrix instruction of one wave: lane l supplies row
@@ -657,7 +769,8 @@ using EmuRun = long (*)(int ot, const uint8_t *payload, uint64_t nbytes, uint64_
                        uint32_t max_wgs, uint64_t chunk, int force_upt, uint32_t ndiv, char *err, int errlen);
 extern EmuRun nq_emu_table[nq::NUM_FORMATS];
 using EmuGemv = long (*)(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y,
-                         uint32_t resident, uint64_t max_rows, char *err, int errlen);
+                         uint32_t resident, uint64_t max_rows, uint32_t gv1_cus, uint32_t gv1_per_cu,
+                         uint32_t *rw_out, char *err, int errlen);
 extern EmuGemv nq_emu_gemv_table[nq::NUM_FORMATS];
 using EmuGemm = long (*)(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y,
                          uint64_t max_rows, uint64_t max_mrows, uint32_t cus, uint32_t *nsplit, char *err,
@@ -742,14 +855,56 @@ extern "C" __attribute__((visibility("default"))) void nq_emu_gemm_plan(int fmt,
     out[8] = q.sp;
 }
 
-// Product with q8_1 activations through the kernel's lane code; returns
-// out-of-payload weight reads (0 on success), or -1 for a format without one.
+// The single-round product plan, as run_gemv models the device (gv1_cus
+// compute units, at most gv1_per_cu workgroups each, 160 KiB of LDS), for
+// weight bytes starting `w_mis` bytes past a 16-byte boundary: out = {rows
+// per chunk (0: none), region dwords, LDS bytes, workgroups}.
+template <int F>
+void gv1_plan_of(uint64_t N, uint64_t K, uint64_t M, uint32_t w_mis, uint32_t cus, uint32_t per_cu, uint64_t *out) {
+    using namespace nq;
+    const uint64_t row_bytes = K / (uint64_t)block_values(F) * (uint64_t)block_bytes(F);
+    constexpr uint32_t stat = 8u * (uint32_t)TabSpec<F>::n8 + 4u * (uint32_t)TabSpec<F>::n4;
+    const GvLaunch L{nullptr, N, K, M, nullptr, nullptr, cus};
+    const Gv1Plan p = gv1_plan(N, row_bytes, M, gv_max_rows<F>(L), (uintptr_t)(4096u + w_mis), cus,
+                               [&](uint32_t, uint32_t lds) {
+                                   const uint32_t by_lds = 163840u / (lds + stat);
+                                   return (int)(by_lds < per_cu ? by_lds : per_cu);
+                               });
+    out[0] = p.rw;
+    out[1] = p.region_dw;
+    out[2] = p.lds;
+    out[3] = p.grid;
+}
+
+extern "C" __attribute__((visibility("default"))) int nq_emu_gemv1_plan(int fmt, uint64_t N, uint64_t K, uint64_t M,
+                                                                       uint32_t w_mis, uint32_t cus,
+                                                                       uint32_t per_cu, uint64_t *out) {
+    using namespace nq;
+    switch (fmt) {
+#define NQ_GV1_CASE(X) \
+    case X: gv1_plan_of<X>(N, K, M, w_mis, cus, per_cu, out); return 0;
+    NQ_GV1_CASE(Q4_0) NQ_GV1_CASE(Q4_1) NQ_GV1_CASE(Q5_0) NQ_GV1_CASE(Q5_1) NQ_GV1_CASE(Q8_0) NQ_GV1_CASE(Q8_1)
+    NQ_GV1_CASE(Q2_K) NQ_GV1_CASE(Q3_K) NQ_GV1_CASE(Q4_K) NQ_GV1_CASE(Q5_K) NQ_GV1_CASE(Q6_K) NQ_GV1_CASE(Q8_K)
+    NQ_GV1_CASE(IQ2_XXS) NQ_GV1_CASE(IQ2_XS) NQ_GV1_CASE(IQ3_XXS) NQ_GV1_CASE(IQ1_S) NQ_GV1_CASE(IQ4_NL)
+    NQ_GV1_CASE(IQ3_S) NQ_GV1_CASE(IQ2_S) NQ_GV1_CASE(IQ4_XS) NQ_GV1_CASE(IQ1_M) NQ_GV1_CASE(TQ1_0)
+    NQ_GV1_CASE(TQ2_0) NQ_GV1_CASE(MXFP4) NQ_GV1_CASE(NVFP4_GGUF) NQ_GV1_CASE(Q1_0) NQ_GV1_CASE(Q2_0)
+#undef NQ_GV1_CASE
+    default: return -1;
+    }
+}
+
+// Product with q8_1 activations through the kernel's lane code (the
+// single-round kernel when gv1_cus > 0 and its plan exists, see run_gemv);
+// returns out-of-payload weight reads (0 on success), or -1 for a format
+// without one.
 extern "C" __attribute__((visibility("default"))) long nq_emu_gemv_q8_1(int fmt, const uint8_t *w, uint64_t N,
                                                                        uint64_t K, const uint8_t *xq, uint64_t M,
                                                                        float *y, uint32_t resident,
-                                                                       uint64_t max_rows, char *err, int errlen) {
+                                                                       uint64_t max_rows, uint32_t gv1_cus,
+                                                                       uint32_t gv1_per_cu, uint32_t *rw_out,
+                                                                       char *err, int errlen) {
     if (fmt < 0 || fmt >= nq::NUM_FORMATS || !nq_emu_gemv_table[fmt]) return -1;
-    return nq_emu_gemv_table[fmt](w, N, K, xq, M, y, resident, max_rows, err, errlen);
+    return nq_emu_gemv_table[fmt](w, N, K, xq, M, y, resident, max_rows, gv1_cus, gv1_per_cu, rw_out, err, errlen);
 }
 
 // Returns the number of out-of-payload reads (0 on success), or -1 for a bad format.

@@ -99,8 +99,12 @@ def lib():
         L.nq_emu_tile_blocks.restype = ctypes.c_long
         L.nq_emu_gemv_q8_1.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64,
                                        ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint32,
-                                       ctypes.c_uint64, ctypes.c_char_p, ctypes.c_int]
+                                       ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p,
+                                       ctypes.c_char_p, ctypes.c_int]
         L.nq_emu_gemv_q8_1.restype = ctypes.c_long
+        L.nq_emu_gemv1_plan.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
+                                        ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p]
+        L.nq_emu_gemv1_plan.restype = ctypes.c_int
         L.nq_emu_gemm_q8_1.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64,
                                        ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint64,
                                        ctypes.c_uint64, ctypes.c_uint32, ctypes.POINTER(ctypes.c_uint32),
@@ -254,9 +258,14 @@ def grouped_absmax(scheme_id, G, x, in_code, x_mis=0, codes_mis=0):
     return int(status[0]), codes, scales, rc, err.value.decode(), guards
 
 
-def gemv_q8_1(fmt_id, w, N, K, xq, M, w_mis=0, resident=2048, max_rows=0):
+def gemv_q8_1(fmt_id, w, N, K, xq, M, w_mis=0, resident=2048, max_rows=0, gv1_cus=0, gv1_per_cu=8,
+              with_rw=False):
     """The product through the emulator.  w: payload bytes, xq: q8_1 blocks.
-    Returns (y float32 [M, N], bad reads, message, guards_ok)."""
+    gv1_cus > 0: the launcher's single-round plan on a device of that many
+    compute units holding at most gv1_per_cu workgroups each (else, or when
+    the plan makes none, the chunk-loop kernel with `resident` workgroups).
+    Returns (y float32 [M, N], bad reads, message, guards_ok[, rows per
+    single-round chunk or 0])."""
     w = np.ascontiguousarray(w, dtype=np.uint8)
     wbuf, woff = _placed(w.size, 16, w_mis)
     wbuf[woff:woff + w.size] = w
@@ -265,11 +274,24 @@ def gemv_q8_1(fmt_id, w, N, K, xq, M, w_mis=0, resident=2048, max_rows=0):
     xbuf[xoff:xoff + xq.size] = xq
     ybuf = np.full(M * N + 32, np.float32(np.nan), dtype=np.float32)
     err = ctypes.create_string_buffer(256)
+    rw = ctypes.c_uint32(0)
     rc = lib().nq_emu_gemv_q8_1(fmt_id, wbuf.ctypes.data + woff, N, K, xbuf.ctypes.data + xoff, M,
-                                ybuf.ctypes.data + 64, resident, max_rows, err, 256)
+                                ybuf.ctypes.data + 64, resident, max_rows, gv1_cus, gv1_per_cu, ctypes.byref(rw),
+                                err, 256)
     y = ybuf[16:16 + M * N].reshape(M, N).copy()
     guards = bool(np.all(np.isnan(ybuf[:16])) and np.all(np.isnan(ybuf[16 + M * N:])))
+    if with_rw:
+        return y, rc, err.value.decode(), guards, rw.value
     return y, rc, err.value.decode(), guards
+
+
+def gemv1_plan(fmt_id, N, K, M, w_mis=0, cus=256, per_cu=8):
+    """The launcher's single-round product plan on the emulator's device
+    model: (rows per chunk or 0, region dwords, LDS bytes, workgroups)."""
+    out = (ctypes.c_uint64 * 4)()
+    rc = lib().nq_emu_gemv1_plan(fmt_id, N, K, M, w_mis, cus, per_cu, out)
+    assert rc == 0
+    return tuple(int(v) for v in out)
 
 
 def gemm_q8_1(fmt_id, w, N, K, xq, M, w_mis=0, max_rows=0, max_mrows=0, cus=0, with_splits=False):

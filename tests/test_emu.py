@@ -359,6 +359,52 @@ def test_emu_gemv_matches_oracle(fmt):
         linear_check(y, ref, env, K, f"{fmt} N={N} M={M}")
 
 
+@pytest.mark.parametrize("fmt", GGUF)
+def test_emu_gemv_single_round_matches_oracle(fmt):
+    """The single-round kernel: one chunk of 1, 2 or 3 whole rows per wave,
+    staged by aligned 16-byte loads to LDS (the launch's last group shifted
+    into place when the payload ends inside it), as the plan picks it on a
+    device that holds few workgroups; misaligned weight bytes and launches
+    whose chunks do not all fit take the chunk loop."""
+    idx, B, S, _ = oracle.info(fmt)
+    K = 3 * B if B >= 64 else 7 * B
+    for N, M, per_cu, w_mis, rw in [(12, 1, 3, 0, 1), (13, 1, 2, 0, 2), (12, 1, 1, 0, 3), (13, 1, 1, 0, 0),
+                                    (12, 1, 3, 4, 0), (13, 3, 2, 0, 2), (12, 8, 1, 0, 3), (5, 2, 1, 0, 2),
+                                    (7, 4, 4, 0, 1), (17, 4, 8, 0, 2)]:
+        w = synth.payload(fmt, N * K // B, 17 + N + M, synth.binade(-6, -2, False))
+        _, xq = oracle.quantize_q8_1(_act(M, K, N + 3).astype(np.float32))
+        y, rc, msg, guards, got = emu_lib.gemv_q8_1(idx, w, N, K, xq, M, w_mis=w_mis, gv1_cus=1,
+                                                    gv1_per_cu=per_cu, with_rw=True)
+        assert rc == 0, msg
+        assert guards
+        assert got == rw, (N, M, per_cu, w_mis)
+        ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
+        linear_check(y, ref, env, K, f"{fmt} N={N} M={M} rows per chunk {rw}")
+
+
+@pytest.mark.parametrize("fmt,N,K,M,rw", [("gguf:q4_k", 14336, 4096, 1, 2), ("gguf:q4_k", 4096, 14336, 1, 1),
+                                          ("gguf:q4_k", 4096, 4096, 8, 2), ("gguf:q6_k", 1024, 4096, 8, 1),
+                                          ("gguf:q8_0", 14336, 4096, 1, 0),
+                                          ("gguf:q6_k", 4096, 14336, 1, 0), ("gguf:q4_0", 1024, 4096, 1, 1),
+                                          ("gguf:iq2_xxs", 14336, 4096, 1, 2)])
+def test_emu_gemv_single_round_plan(fmt, N, K, M, rw):
+    """On a device of 256 compute units holding up to 8 workgroups each, the
+    single-round plan takes the fewest rows per chunk whose chunks all fit at
+    once, within 160 KiB of LDS per unit, or, for several activation rows and
+    at least 4096 rows, two rows first; weights too large for one round (q8_0
+    at [14336, 4096]: 62 MB) take the chunk loop."""
+    idx = oracle.info(fmt)[0]
+    p = emu_lib.gemv1_plan(idx, N, K, M)
+    assert p[0] == rw, p
+    if rw:
+        row_bytes = K // oracle.info(fmt)[1] * oracle.info(fmt)[2]
+        assert p[1] == 4 * ((15 + rw * row_bytes + 15) // 16 + 1)
+        assert p[2] == 4 * 4 * p[1]
+        assert p[3] == -(-(-(-N // rw)) // 4)
+        assert p[3] <= 256 * min(8, 163840 // p[2])
+    assert emu_lib.gemv1_plan(idx, N, K, M, w_mis=8)[0] == 0
+
+
 def test_emu_gemv_rejects_nvfp4_with_divisor():
     y, rc, _, _ = emu_lib.gemv_q8_1(nq.format_query("nvfp4").id, np.zeros(40, np.uint8), 1, 64,
                                     np.zeros(72, np.uint8), 1)

@@ -153,14 +153,17 @@ FULL = [("gguf:q4_k", 14336, 4096), ("gguf:q6_k", 4096, 14336), ("gguf:q8_0", 40
         ("gguf:mxfp4", 14336, 4096), ("gguf:q5_k", 4096, 4096)]
 
 
-@pytest.mark.parametrize("fmt,N,K", FULL)
-def test_gemv_full_size_sampled_rows(fmt, N, K):
-    """Llama-3-8B-shaped weights, M = 1 (the benchmark's launch): every output
-    computed on the GPU, sampled rows against the oracle."""
-    M = 1
+@pytest.mark.parametrize("fmt,N,K,M", [f + (1,) for f in FULL] +
+                         [("gguf:q4_k", 14336, 4096, 8), ("gguf:q4_0", 14336, 4096, 4),
+                          ("gguf:iq2_xs", 4096, 14336, 2), ("gguf:q6_k", 1024, 14336, 8)])
+def test_gemv_full_size_sampled_rows(fmt, N, K, M):
+    """Llama-3-8B-shaped weights, M = 1 (the benchmark's launch) and a few
+    decode batches: every output computed on the GPU, sampled rows against
+    the oracle.  Single-round launches with one, two and three rows per
+    chunk and the chunk loop (q6_k at [4096, 14336]) are among them."""
     w = _weights(fmt, N, K, 77)
     _, xq = oracle.quantize_q8_1(_act(M, K, 1).astype(np.float32))
-    announce(f"gemv full {fmt} [{N}, {K}]")
+    announce(f"gemv full {fmt} [{N}, {K}] M={M}")
     y = _gemv(fmt, w, N, K, xq)
     rng = np.random.default_rng(N + K)
     rows = np.unique(np.r_[0, 1, N - 1, rng.integers(0, N, size=61)])
