@@ -497,12 +497,12 @@ def gemm_only(torch, nq, synth, args):
     """The batched-product measurements alone (one JSON line): every GEMM_CASES
     entry at both shapes, the headline case's roofline, and the oracle beside it."""
     res = {}
-    for fmt, M in GEMM_CASES:
-        for shape in ([14336, 4096], [4096, 14336]):
+    for fmt, M in product_cases(GEMM_CASES, args):
+        for shape in product_shapes(args):
             key = f"gemm_q8_1 {fmt}{shape} M={M}"
             res[key] = gemm_measurement(torch, nq, synth, fmt, shape, M)
             log(f"{key}: {res[key]['tops']} TOP/s ({100 * res[key]['frac_alu_peak']:.1f}% of the ALU bound)")
-    head = res["gemm_q8_1 gguf:q4_k[14336, 4096] M=512"]
+    head = res.get("gemm_q8_1 gguf:q4_k[14336, 4096] M=512", next(iter(res.values())))
     roofline = {"bound": "alu", "achieved": head["tops"], "peak": round(GEMM_ALU_PEAK_TOPS, 1), "unit": "TOP/s",
                 "frac": head["frac_alu_peak"], "traffic": None, "kernel": "k_gemm gguf:q4_k M=512",
                 "mfma_i8_peak": MFMA_I8_PEAK_TOPS, "frac_mfma_i8_peak": head["frac_mfma_i8_peak"],
@@ -592,16 +592,31 @@ def gemv_cpu_baseline(synth, fmt="gguf:q4_k", shape=(14336, 4096), rows=14336, s
             "weights_per_s": round(rows * K / secs, 1)}
 
 
+def product_cases(cases, args):
+    """The (format, M) product cases to measure: all, or those --cases names."""
+    if not args.cases:
+        return cases
+    want = [(c.rsplit(":", 1)[0], int(c.rsplit(":", 1)[1])) for c in args.cases.split(",")]
+    return want
+
+
+def product_shapes(args):
+    """Weight shapes of the product measurements: both Llama-3-8B shapes, or --product-shapes."""
+    if not args.product_shapes:
+        return [[14336, 4096], [4096, 14336]]
+    return [[int(v) for v in t.split("x")] for t in args.product_shapes.split(",")]
+
+
 def gemv_only(torch, nq, synth, args):
     """The product measurements alone (one JSON line): every GEMV_CASES entry
     at both shapes, the dominant one's roofline, and the oracle beside it."""
     res = {}
-    for fmt, M in GEMV_CASES:
-        for shape in ([14336, 4096], [4096, 14336]):
+    for fmt, M in product_cases(GEMV_CASES, args):
+        for shape in product_shapes(args):
             key = f"gemv_q8_1 {fmt}{shape} M={M}"
             res[key] = gemv_measurement(torch, nq, synth, fmt, shape, M)
             log(f"{key}: {res[key]['gbps']} GB/s ({100 * res[key]['frac_hbm_peak']:.1f}% of peak)")
-    head = res["gemv_q8_1 gguf:q4_k[14336, 4096] M=1"]
+    head = res.get("gemv_q8_1 gguf:q4_k[14336, 4096] M=1", next(iter(res.values())))
     roofline = {"bound": "hbm", "achieved": head["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": head["frac_hbm_peak"], "traffic": None, "kernel": "k_gemv gguf:q4_k M=1",
                 "bytes_per_launch": head["bytes_per_launch"], "mean_launch_us": head["mean_launch_us"]}
@@ -653,6 +668,10 @@ def main():
                     help="measure only the products with q8_1 activations (one JSON line of its own)")
     ap.add_argument("--gemm-only", action="store_true",
                     help="measure only the batched products on the matrix cores (one JSON line of its own)")
+    ap.add_argument("--cases", default="", metavar="FMT:M,...",
+                    help="with --gemv-only / --gemm-only: measure only these (format, activation rows) cases")
+    ap.add_argument("--product-shapes", default="", metavar="NxK,...",
+                    help="with --gemv-only / --gemm-only: weight shapes (default [14336, 4096] and [4096, 14336])")
     ap.add_argument("--formats", default="", metavar="F1,F2,...",
                     help="measure only single-tensor decodes of these formats at --shapes (one JSON line of its own)")
     ap.add_argument("--shapes", default="14336x4096", metavar="RxC,...", help="shapes for --formats")
