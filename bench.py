@@ -618,7 +618,7 @@ def gemv_only(torch, nq, synth, args):
             log(f"{key}: {res[key]['gbps']} GB/s ({100 * res[key]['frac_hbm_peak']:.1f}% of peak)")
     head = res.get("gemv_q8_1 gguf:q4_k[14336, 4096] M=1", next(iter(res.values())))
     roofline = {"bound": "hbm", "achieved": head["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": head["frac_hbm_peak"], "traffic": None, "kernel": "k_gemv gguf:q4_k M=1",
+                "frac": head["frac_hbm_peak"], "traffic": None, "kernel": "gemv_q8_1 gguf:q4_k M=1 (k_gemv1)",
                 "bytes_per_launch": head["bytes_per_launch"], "mean_launch_us": head["mean_launch_us"]}
     cpu = None if args.no_cpu_baseline else gemv_cpu_baseline(synth)
     line = {"metric": "gemv_q8_1 GB/s (weight + activation + output) per launch, 1\u00d7MI355X",
