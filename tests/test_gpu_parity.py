@@ -136,12 +136,14 @@ def test_nvfp4_every_scale_byte_and_code():
 def test_output_conversion_edges_through_q8_k():
     """y = d * q with binary32 d covering every high half-word with the low
     half-words the oracle's conversion pin uses (at and around the bf16 and f16
-    rounding points, odd-LSB ties included) plus 2^18 random words:
+    rounding points, odd-LSB ties and f16's subnormal tie points included) plus
+    2^18 random words:
     exercises the hardware bf16/f16 conversions on ties, subnormals, overflow
     and NaN (q = 1 converts d itself; the other codes scale it)."""
     hi = np.arange(65536, dtype=np.uint32) << 16
-    lows = np.array([0x0000, 0x0001, 0x0FFF, 0x1000, 0x1001, 0x1FFF, 0x2000, 0x2001, 0x3000,
-                     0x7FFF, 0x8000, 0x8001, 0xBFFF, 0xC000, 0xFFFF], dtype=np.uint32)
+    lows = np.array([0x0000, 0x0001, 0x0FFF, 0x1000, 0x1001, 0x1FFF, 0x2000, 0x2001, 0x2FFF, 0x3000,
+                     0x3001, 0x3FFF, 0x4000, 0x4001, 0x5FFF, 0x6000, 0x6001, 0x7FFF, 0x8000, 0x8001,
+                     0xBFFF, 0xC000, 0xC001, 0xFFFF], dtype=np.uint32)
     rand = np.random.default_rng(2025).integers(0, 2 ** 32, size=1 << 18, dtype=np.uint64).astype(np.uint32)
     d = np.concatenate([(hi[:, None] | lows[None, :]).ravel(), rand])
     n = d.size

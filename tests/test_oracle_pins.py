@@ -158,10 +158,13 @@ def test_binary16_all_words_match_numpy():
 
 def _structured_f32_sample():
     """Every high half (sign, exponent, top mantissa bits) with low halves at
-    and around the rounding points of both bf16 and f16, plus random words."""
+    and around the rounding points of both bf16 and f16 (f16's odd-LSB ties,
+    and the tie points one and two bits up that its subnormal range moves
+    them to), plus random words."""
     hi = np.arange(65536, dtype=np.uint32) << 16
-    lows = np.array([0x0000, 0x0001, 0x0FFF, 0x1000, 0x1001, 0x1FFF, 0x2000, 0x2001, 0x3000,
-                     0x7FFF, 0x8000, 0x8001, 0xBFFF, 0xC000, 0xFFFF], dtype=np.uint32)
+    lows = np.array([0x0000, 0x0001, 0x0FFF, 0x1000, 0x1001, 0x1FFF, 0x2000, 0x2001, 0x2FFF, 0x3000,
+                     0x3001, 0x3FFF, 0x4000, 0x4001, 0x5FFF, 0x6000, 0x6001, 0x7FFF, 0x8000, 0x8001,
+                     0xBFFF, 0xC000, 0xC001, 0xFFFF], dtype=np.uint32)
     words = (hi[:, None] | lows[None, :]).ravel()
     rng = np.random.default_rng(2024)
     rand = rng.integers(0, 2 ** 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)
