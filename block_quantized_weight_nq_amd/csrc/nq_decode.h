@@ -383,12 +383,19 @@ NQ_HD uint32_t pow3(uint32_t p) { return p == 0 ? 1u : p == 1 ? 3u : p == 2 ? 9u
 // Digit k of each byte of w (byte b of the result: floor(3 * ((byte * 3^k)
 // mod 256) / 256), 0..2), two bytes per multiply in 16-bit fields: byte *
 // 3^k <= 20655 and 3 * 255 stay inside a field.
-NQ_HD uint32_t digits4(uint32_t w, uint32_t k) {
-    const uint32_t m = pow3(k);
-    const uint32_t e = ((((w & 0x00FF00FFu) * m) & 0x00FF00FFu) * 3u >> 8) & 0x00030003u;
-    const uint32_t o = (((((w >> 8) & 0x00FF00FFu) * m) & 0x00FF00FFu) * 3u >> 8) & 0x00030003u;
-    return e | (o << 8);
+// With m = 3^k given: bytes 0 and 2, and bytes 1 and 3, are moved into the
+// low bytes of two 16-bit fields by byte selects; after the multiply and the
+// mod-256 mask, 3 * r leaves each digit in bits 8-9 of its field, and one
+// more byte select gathers the four digits in byte order.
+NQ_HD uint32_t digits4m(uint32_t w, uint32_t m) {
+    const uint32_t e = perm(0u, w, 0x04020400u);  // [b0, 0, b2, 0]
+    const uint32_t o = perm(0u, w, 0x04030401u);  // [b1, 0, b3, 0]
+    const uint32_t fe = ((e * m) & 0x00FF00FFu) * 3u & 0x03000300u;
+    const uint32_t fo = ((o * m) & 0x00FF00FFu) * 3u & 0x03000300u;
+    return perm(fo, fe, 0x07030501u);  // [fe byte 1, fo byte 1, fe byte 3, fo byte 3]
 }
+
+NQ_HD uint32_t digits4(uint32_t w, uint32_t k) { return digits4m(w, pow3(k)); }
 
 // Unit s of a tq1_0 block, without branches (a wave's lanes hold every s):
 // s < 20 takes digit s/4 of bytes 8(s mod 4) .. +7; 20 <= s < 30 digit

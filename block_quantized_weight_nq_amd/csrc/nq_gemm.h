@@ -218,10 +218,14 @@ NQ_HD void gm_span(const Src &s, uint32_t bo, uint32_t p, const Tab &tab, GmSpan
         // signed and its scales and offsets sorted into halves
         GvW w;
         gv_w<F>(s, bo, p, tab, w);
-        if constexpr (F == Q8_0 || F == Q8_1 || F == Q8_K || F == IQ4_NL || F == MXFP4 || F == IQ4_XS ||
-                      F == TQ1_0) {
+        if constexpr (F == Q8_0 || F == Q8_1 || F == Q8_K || F == IQ4_NL || F == MXFP4 || F == IQ4_XS) {
 #pragma unroll
             for (int j = 0; j < 8; j++) o.c[j] = w.q[j];
+            o.ws[0] = o.ws[1] = w.f[0];
+        } else if constexpr (F == TQ1_0) {
+            // codes digit - 1
+#pragma unroll
+            for (int j = 0; j < 8; j++) o.c[j] = bsub(w.q[j], 0x01010101u);
             o.ws[0] = o.ws[1] = w.f[0];
         } else if constexpr (F == Q4_0) {
             // codes v - 8 (the low nibbles first, then the high)

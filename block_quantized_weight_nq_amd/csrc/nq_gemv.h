@@ -321,28 +321,27 @@ NQ_HD uint32_t iq_signs8(uint32_t s7) { return s7 | (parity7(s7) << 7); }
 // byte, and the result bytes are the two's-complement differences.
 NQ_HD uint32_t bsub(uint32_t c, uint32_t o) { return ((c | 0x80808080u) - o) ^ 0x80808080u; }
 
-// Four base-3 digits as signed codes: byte b of the result is digit k of
-// byte b of w minus 1 (the decoder's digit rule, digits4).
-NQ_HD uint32_t trits4(uint32_t w, uint32_t k) { return bsub(digits4(w, k), 0x01010101u); }
 
-// The 32 codes (digit - 1, value order) of 32-value item p (< 8) of a tq1_0
-// block: values 32k + i (k < 5, i < 32) are digit k of byte i, values
-// 160 + 16k + i (k < 5, i < 16) digit k of byte 32 + i, values 240 + 4k + i
-// (k < 4, i < 4) digit k of byte 48 + i.  Branch-free over the item (a
-// wave's lanes take different items): each half reads one 16-byte window
-// and one digit.
+// The 32 base-3 digits (0..2, value order; the weight is digit - 1) of
+// 32-value item p (< 8) of a tq1_0 block: values 32k + i (k < 5, i < 32)
+// are digit k of byte i, values 160 + 16k + i (k < 5, i < 16) digit k of
+// byte 32 + i, values 240 + 4k + i (k < 4, i < 4) digit k of byte 48 + i.
+// Branch-free over the item (a wave's lanes take different items): each
+// half reads one 16-byte window and takes one digit per byte, with the
+// multiplier 3^k worked out once per half.
 template <class Src>
 NQ_HD void tq1_item(const Src &s, uint32_t bo, uint32_t p, uint32_t (&c)[8]) {
     const bool lo = p < 5u, tail = p == 7u;
     const uint32_t k1 = lo ? p : tail ? 4u : 2u * (p - 5u);
+    const uint32_t m1 = pow3(k1), m2 = pow3(lo ? p : k1 + 1u);
     uint32_t q1[4], q2[4], h[1];
     window<4>(s, bo + (lo ? 0u : 32u), q1);
     window<4>(s, bo + (lo ? 16u : 32u), q2);
     window<1>(s, bo + 48u, h);
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-        c[j] = trits4(q1[j], k1);
-        c[4 + j] = tail ? trits4(h[0], (uint32_t)j) : trits4(q2[j], lo ? p : k1 + 1u);
+        c[j] = digits4m(q1[j], m1);
+        c[4 + j] = digits4m(tail ? h[0] : q2[j], tail ? pow3((uint32_t)j) : m2);
     }
 }
 
@@ -481,7 +480,7 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
 #pragma unroll
         for (int j = 0; j < 8; j++) w.q[j] = (q[j] >> (2u * (part & 3u))) & 0x03030303u;
     } else if constexpr (F == TQ1_0) {
-        // part p: 32 base-3 digits (tq1_item); d at 52; w = d * (digit - 1)
+        // part p: 32 base-3 digits v (tq1_item); d at 52; w = d * (v - 1)
         uint32_t c[8];
         tq1_item(s, bo, part, c);
         w.f[0] = f16(u16_at(s, bo + 52u));
@@ -782,7 +781,7 @@ NQ_HD void gv_a(const Act &act, uint32_t m, uint32_t b, uint32_t part, GvA &x) {
 template <int F>
 NQ_HD float gv_dot(const GvW &w, const GvA &x, float acc) {
     constexpr uint32_t LO4 = 0x0F0F0F0Fu;
-    if constexpr (F == Q8_0 || F == Q8_1 || F == Q8_K || F == IQ4_NL || F == MXFP4 || F == IQ4_XS || F == TQ1_0) {
+    if constexpr (F == Q8_0 || F == Q8_1 || F == Q8_K || F == IQ4_NL || F == MXFP4 || F == IQ4_XS) {
         // w = scale * (8-bit integer): the scale times the exact dot product
         int I = 0;
 #pragma unroll
@@ -794,7 +793,7 @@ NQ_HD float gv_dot(const GvW &w, const GvA &x, float acc) {
 #pragma unroll
         for (int j = 0; j < 8; j++) I = dot4(w.q[j], x.c[j], I);
         return __builtin_fmaf(w.f[0] * (float)I + w.f[1] * (float)x.S[0], x.d[0], acc);
-    } else if constexpr (F == Q5_0 || F == TQ2_0) {
+    } else if constexpr (F == Q5_0 || F == TQ2_0 || F == TQ1_0) {
         // w = d * (v - o), o = 16 or 1: exact integer offset through the codes' sum
         constexpr int O = F == Q5_0 ? 16 : 1;
         int I = 0;

@@ -56,6 +56,33 @@ def test_emulated_misaligned_payload_and_output(fmt, mis, out_mis):
     assert _same(got, _oracle(fmt, p, nblocks, B, dtype), dtype)
 
 
+def test_emulated_tq1_0_every_byte_at_every_position():
+    """tq1_0's base-3 digits: 256 blocks whose byte j is (i + 7 j) mod 256 put
+    every byte value (values past 242 included) at every position of a block,
+    and so under every digit of the layout; the decode, the single-row product
+    and the matrix-core product's span rewrite all take the digits from the
+    same rule as the oracle."""
+    fmt = "gguf:tq1_0"
+    idx, B, S, _ = oracle.info(fmt)
+    i = np.arange(256)[:, None]
+    j = np.arange(S)[None, :]
+    blk = ((i + 7 * j) % 256).astype(np.uint8)
+    blk[:, 52:54] = np.array([0x00, 0x3C], np.uint8)  # d = 1.0 keeps every product exact
+    p = blk.ravel()
+    for dtype in ("f32", "bf16"):
+        got, bad, msg, guards = emu_lib.decode(idx, p, 256, B, dtype, mis=1)
+        assert bad == 0 and guards, msg
+        assert _same(got, _oracle(fmt, p, 256, B, dtype), dtype)
+    N, K = 16, 16 * B
+    _, xq = oracle.quantize_q8_1(_act(9, K, 3).astype(np.float32))
+    for M in (1, 9):
+        run = emu_lib.gemv_q8_1 if M <= 8 else emu_lib.gemm_q8_1
+        ref_m, env_m = oracle.gemv_q8_1(fmt, p, N, K, xq[:M * K // 32 * 36], M)
+        y, rc, msg, guards = run(idx, p, N, K, xq[:M * K // 32 * 36], M)
+        assert rc == 0 and guards, msg
+        linear_check(y, ref_m, env_m, K, f"{fmt} M={M}")
+
+
 @pytest.mark.parametrize("fmt", ["gguf:q4_k", "gguf:q8_0", "gguf:mxfp4", "nvfp4", "gguf:iq2_s", "gguf:tq1_0"])
 @pytest.mark.parametrize("chunk,max_wgs", [(5, 1), (3, 2), (64, 3), (700, 3), (2900, 2), (700, 16), (2900, 8)])
 def test_emulated_chunks(fmt, chunk, max_wgs):
