@@ -29,6 +29,16 @@ namespace nq {
 
 constexpr int GV_MAX_M = 8;
 
+// Signed 4 x 8-bit dot product with accumulation (v_dot4 on the GPU).
+NQ_HD int dot4(uint32_t a, uint32_t b, int c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+#else
+    for (int k = 0; k < 4; k++) c += (int)(int8_t)(a >> (8 * k)) * (int)(int8_t)(b >> (8 * k));
+    return c;
+#endif
+}
+
 // ---------------------------------------------------------------- quantizer
 
 // Blocks per quantizer launch: thread indices stay below 2^31.
@@ -49,36 +59,41 @@ constexpr uint32_t q81_lanes() {
     return 32u / (uint32_t)gq_vpl<IN>();
 }
 
-// Phase 2 of a lane (after amax and the failure flag are combined over the
-// block's lanes): the block's d word, the lane's codes (zero when the block
-// fails) and status bits 1 and 2.
+// Phase 2 of a lane (after the magnitude word is combined over the block's
+// lanes): the block's d word, the lane's codes (four to a word; zero when the
+// block fails) and status bits 0 and 1.
 template <int VPL>
-NQ_HD uint32_t q81_encode(float amax, bool bad, const float (&v)[VPL], uint32_t *d16, int8_t (&q)[VPL]) {
-    uint32_t st = bad ? 1u : gq_encode<3, VPL>(amax, v, d16, q);
+NQ_HD uint32_t q81_encode(uint32_t mag, const float (&v)[VPL], uint32_t *d16, uint32_t (&qw)[VPL / 4]) {
+    uint32_t st = 1u;
+    if (mag < GQ_NONFINITE) st = gq_encode<3, VPL>(bits_f32(mag), v, d16, qw);
     if (st) {
         *d16 = 0u;
 #pragma unroll
-        for (int k = 0; k < VPL; k++) q[k] = 0;
+        for (int d = 0; d < VPL / 4; d++) qw[d] = 0u;
     }
     return st;
+}
+
+// The lane's code sum (exact).
+template <int VPL>
+NQ_HD int q81_sum(const uint32_t (&qw)[VPL / 4]) {
+    int sum = 0;
+#pragma unroll
+    for (int d = 0; d < VPL / 4; d++) sum = dot4(qw[d], 0x01010101u, sum);
+    return sum;
 }
 
 // Phase 3 (after the code sums are combined): lane j of block b stores its
 // codes; lane 0 stores the d and sum words.  Returns the block's status bits
 // (lane 0 reports them).
 template <int VPL>
-NQ_HD uint32_t q81_store(const Q81Args &a, uint32_t b, uint32_t j, const int8_t (&q)[VPL], uint32_t d16, int sum,
-                     uint32_t st) {
+NQ_HD uint32_t q81_store(const Q81Args &a, uint32_t b, uint32_t j, const uint32_t (&qw)[VPL / 4], uint32_t d16,
+                         int sum, uint32_t st) {
     const uint32_t s16 = gq_f32_to_f16(f16(d16) * (float)sum);  // exact product, one rounding
     if ((s16 & 0x7C00u) == 0x7C00u) st |= 4u;
     uint32_t *blk = a.blocks + (uint64_t)b * 9u;
 #pragma unroll
-    for (int d = 0; d < VPL / 4; d++) {
-        uint32_t w = 0u;
-#pragma unroll
-        for (int k = 0; k < 4; k++) w |= (uint32_t)(uint8_t)q[4 * d + k] << (8 * k);
-        blk[1u + j * (uint32_t)(VPL / 4) + (uint32_t)d] = w;
-    }
+    for (int d = 0; d < VPL / 4; d++) blk[1u + j * (uint32_t)(VPL / 4) + (uint32_t)d] = qw[d];
     if (j == 0u) blk[0] = st & 3u ? 0u : d16 | s16 << 16;
     return st;
 }
@@ -91,27 +106,20 @@ __global__ __launch_bounds__(WG) void k_quantize_q8_1(Q81Args a) {
     const uint32_t b = t / LPB, j = t % LPB;
     const bool live = b < a.nblocks;
     float v[VPL];
-    float amax = 0.0f;
-    bool bad = false;
+    uint32_t mag = 0u;
     if (live) {
-        gq_load<IN, VECIN>(GqDevSrc{a.x}, (uint64_t)b * 32u + j * (uint32_t)VPL, (uint32_t)VPL, v, &amax, &bad);
+        mag = gq_load<IN, VECIN>(GqDevSrc{a.x}, (uint64_t)b * 32u + j * (uint32_t)VPL, (uint32_t)VPL, v);
     } else {
 #pragma unroll
         for (int k = 0; k < VPL; k++) v[k] = 0.0f;
     }
     // every lane of the wave takes part in the exchanges
 #pragma unroll
-    for (uint32_t off = LPB / 2; off >= 1; off >>= 1) {
-        const float o = __shfl_xor(amax, (int)off, 64);
-        amax = o > amax ? o : amax;
-        bad |= __shfl_xor((int)bad, (int)off, 64) != 0;
-    }
-    int8_t q[VPL];
+    for (uint32_t off = LPB / 2; off >= 1; off >>= 1) mag = gq_umax(mag, (uint32_t)__shfl_xor((int)mag, (int)off, 64));
+    uint32_t q[VPL / 4];
     uint32_t d16 = 0u;
-    const uint32_t st = q81_encode<VPL>(amax, bad, v, &d16, q);
-    int sum = 0;
-#pragma unroll
-    for (int k = 0; k < VPL; k++) sum += q[k];
+    const uint32_t st = q81_encode<VPL>(mag, v, &d16, q);
+    int sum = q81_sum<VPL>(q);
 #pragma unroll
     for (uint32_t off = LPB / 2; off >= 1; off >>= 1) sum += __shfl_xor(sum, (int)off, 64);
     if (live) {
@@ -198,15 +206,6 @@ __device__ inline void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Signed 4 x 8-bit dot product with accumulation (v_dot4 on the GPU).
-NQ_HD int dot4(uint32_t a, uint32_t b, int c) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
-#else
-    for (int k = 0; k < 4; k++) c += (int)(int8_t)(a >> (8 * k)) * (int)(int8_t)(b >> (8 * k));
-    return c;
-#endif
-}
 
 constexpr uint32_t ONES8 = 0x01010101u;
 

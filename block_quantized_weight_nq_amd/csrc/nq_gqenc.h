@@ -15,8 +15,8 @@
 //
 // Work split: a lane encodes VPL consecutive values of one group (32 source
 // bytes: 8 binary32, 16 binary16/bfloat16 or 4 binary64 values); the G/VPL
-// lanes of a group are consecutive lanes of a wave and reduce amax with
-// cross-lane exchanges.  A wave's source loads and code stores are
+// lanes of a group are consecutive lanes of a wave and reduce amax (with the
+// failure test folded in) with cross-lane exchanges.  A wave's source loads and code stores are
 // contiguous.  Failures set bits of a caller-owned status word with an
 // atomic OR.
 #pragma once
@@ -100,7 +100,27 @@ struct GqDevSrc {
     }
 };
 
-NQ_HD bool gq_finite(float v) { return (__builtin_bit_cast(uint32_t, v) & 0x7F800000u) != 0x7F800000u; }
+// |v| as a word: for values other than NaN these words order as the
+// magnitudes do, and a word of 0x7F800000 or more is an infinity or a NaN, so
+// one integer maximum gives both a group's amax and whether it fails.
+NQ_HD uint32_t gq_mag(float v) { return __builtin_bit_cast(uint32_t, v) & 0x7FFFFFFFu; }
+constexpr uint32_t GQ_NONFINITE = 0x7F800000u;  // smallest magnitude word that fails
+NQ_HD uint32_t gq_umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// clamp(x, lo, hi) for lo <= hi and x not NaN (v_med3_f32).
+NQ_HD float gq_clamp(float x, float lo, float hi) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_fmed3f(x, lo, hi);
+#else
+    return x < lo ? lo : x > hi ? hi : x;
+#endif
+}
+
+// Code byte of a clamped quotient c (|c| <= 127): adding 1.5 * 2^23 leaves a
+// sum in [2^23, 2^24), where binary32 spacing is 1, so the addition itself
+// rounds c half to even and the sum's low mantissa byte is that integer in
+// two's complement.
+NQ_HD uint32_t gq_code_word(float c) { return __builtin_bit_cast(uint32_t, A(c, 12582912.0f)); }
 
 // binary32 -> binary16 word, round-to-nearest-even (overflow gives infinity,
 // subnormals are kept): the hardware conversion under the default mode.
@@ -122,49 +142,47 @@ NQ_HD uint32_t gq_chunk(const GqArgs &a, int G, uint32_t g, uint32_t j, uint64_t
     return col >= a.K ? 0u : (a.K - col < (uint32_t)GQ_VPL ? a.K - col : (uint32_t)GQ_VPL);
 }
 
-// Phase 1: a lane's GQ_VPL source values (zeros past the group's end), their
-// amax and whether one is not finite.
+// Phase 1: a lane's GQ_VPL source values (zeros past the group's end) and
+// the largest of their magnitude words (gq_mag).
 template <int IN, bool VECIN, class Src, int GQ_VPL = gq_vpl<IN>()>
-NQ_HD void gq_load(const Src &src, uint64_t off, uint32_t cnt, float (&v)[GQ_VPL], float *amax, bool *bad) {
+NQ_HD uint32_t gq_load(const Src &src, uint64_t off, uint32_t cnt, float (&v)[GQ_VPL]) {
     if (VECIN && cnt == (uint32_t)GQ_VPL) {
         src.template span<IN>(off, v);
     } else {
         for (int k = 0; k < GQ_VPL; k++)
             v[k] = (uint32_t)k < cnt ? src.template one<IN>(off + (uint64_t)k) : 0.0f;
     }
-    float m = 0.0f;
-    bool b = false;
+    uint32_t m = 0u;
 #pragma unroll
-    for (int k = 0; k < GQ_VPL; k++) {
-        b |= !gq_finite(v[k]);
-        const float t = __builtin_fabsf(v[k]);
-        m = t > m ? t : m;
-    }
-    *amax = m;
-    *bad = b;
+    for (int k = 0; k < GQ_VPL; k++) m = gq_umax(m, gq_mag(v[k]));
+    return m;
 }
 
 // Phase 3: the group's scale word from its amax (every lane of the group
-// computes it), and the lane's codes.  Returns status bits.
+// computes it), and the lane's codes, four bytes to a word in value order.
+// Returns status bits.  rint-then-clamp equals clamp-then-rint here because
+// the bounds are integers and rounding is monotonic.
 template <int S, int GQ_VPL>
-NQ_HD uint32_t gq_encode(float amax, const float (&v)[GQ_VPL], uint32_t *s16_out, int8_t (&q)[GQ_VPL]) {
-    constexpr int qmin = GQ[S].qmin, qmax = GQ[S].qmax;
+NQ_HD uint32_t gq_encode(float amax, const float (&v)[GQ_VPL], uint32_t *s16_out, uint32_t (&qw)[GQ_VPL / 4]) {
+    constexpr float qmin = (float)GQ[S].qmin, qmax = (float)GQ[S].qmax;
+#pragma unroll
+    for (int d = 0; d < GQ_VPL / 4; d++) qw[d] = 0u;
     if (amax == 0.0f) {
         *s16_out = 0u;
-#pragma unroll
-        for (int k = 0; k < GQ_VPL; k++) q[k] = 0;
         return 0u;
     }
-    const float raw = amax / (float)qmax;  // correctly rounded binary32 division
+    const float raw = amax / qmax;  // correctly rounded binary32 division
     uint32_t s16 = gq_f32_to_f16(raw);
     if (s16 == 0u) s16 = 1u;  // 2^-24 underflow rescue
     *s16_out = s16;
     if ((s16 & 0x7C00u) == 0x7C00u) return 2u;
     const float inv = 1.0f / f16(s16);
 #pragma unroll
-    for (int k = 0; k < GQ_VPL; k++) {
-        const float r = __builtin_rintf(M(v[k], inv));  // round half to even
-        q[k] = (int8_t)(r < (float)qmin ? qmin : r > (float)qmax ? qmax : (int)r);
+    for (int d = 0; d < GQ_VPL / 4; d++) {
+        uint32_t c[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) c[k] = gq_code_word(gq_clamp(M(v[4 * d + k], inv), qmin, qmax));
+        qw[d] = perm(perm(c[3], c[2], 0x00000400u), perm(c[1], c[0], 0x00000400u), 0x05040100u);
     }
     return 0u;
 }
@@ -172,30 +190,23 @@ NQ_HD uint32_t gq_encode(float amax, const float (&v)[GQ_VPL], uint32_t *s16_out
 // Phase 3 stores: the lane's codes (GQ_VPL bytes, or the cnt that exist) and,
 // for the group's first lane, the scale word.
 template <bool VECOUT, int GQ_VPL>
-NQ_HD void gq_store(const GqArgs &a, uint64_t off, uint32_t cnt, const int8_t (&q)[GQ_VPL], uint32_t g,
+NQ_HD void gq_store(const GqArgs &a, uint64_t off, uint32_t cnt, const uint32_t (&qw)[GQ_VPL / 4], uint32_t g,
                     uint32_t j, uint32_t s16) {
     if (VECOUT && cnt == (uint32_t)GQ_VPL) {
-        uint32_t w[GQ_VPL / 4];
-#pragma unroll
-        for (int d = 0; d < GQ_VPL / 4; d++) {
-            w[d] = 0u;
-#pragma unroll
-            for (int k = 0; k < 4; k++) w[d] |= (uint32_t)(uint8_t)q[4 * d + k] << (8 * k);
-        }
         uint32_t *p = (uint32_t *)(a.codes + off);
         if constexpr (GQ_VPL == 4) {
-            p[0] = w[0];
+            p[0] = qw[0];
         } else {
 #pragma unroll
             for (int d = 0; d < GQ_VPL / 4; d += 2) {
                 u32x2a4 v;
-                v.x = w[d];
-                v.y = w[d + 1];
+                v.x = qw[d];
+                v.y = qw[d + 1];
                 *(u32x2a4 *)(p + d) = v;
             }
         }
     } else {
-        for (uint32_t k = 0; k < cnt; k++) a.codes[off + k] = q[k];
+        for (uint32_t k = 0; k < cnt; k++) a.codes[off + k] = (int8_t)bytek(qw[k / 4u], k % 4u);
     }
     if (j == 0u) a.scales[g] = (uint16_t)s16;
 }
@@ -211,21 +222,15 @@ __global__ __launch_bounds__(WG) void k_grouped_absmax(GqArgs a) {
     uint64_t off = 0;
     const uint32_t cnt = live ? gq_chunk<GQ_VPL>(a, G, g, j, &off) : 0u;
     float v[GQ_VPL];
-    float amax;
-    bool bad;
-    gq_load<IN, VECIN>(GqDevSrc{a.x}, off, cnt, v, &amax, &bad);
+    uint32_t mag = gq_load<IN, VECIN>(GqDevSrc{a.x}, off, cnt, v);
     // the group's lanes are consecutive: exchange within each run of LPG lanes
     // (max is exact, so the order of the exchange does not matter)
 #pragma unroll
-    for (uint32_t d = 1; d < LPG; d <<= 1) {
-        const float o = __shfl_xor(amax, (int)d, 64);
-        amax = o > amax ? o : amax;
-        bad = __shfl_xor((int)bad, (int)d, 64) != 0 || bad;
-    }
+    for (uint32_t d = 1; d < LPG; d <<= 1) mag = gq_umax(mag, (uint32_t)__shfl_xor((int)mag, (int)d, 64));
     if (!live) return;
     uint32_t s16 = 0;
-    int8_t q[GQ_VPL];
-    const uint32_t st = bad ? 1u : gq_encode<S>(amax, v, &s16, q);
+    uint32_t q[GQ_VPL / 4];
+    const uint32_t st = mag >= GQ_NONFINITE ? 1u : gq_encode<S>(bits_f32(mag), v, &s16, q);
     if (st != 0u) {
         if (j == 0u) atomicOr(a.status, st);
         return;

@@ -1112,25 +1112,20 @@ long run_gq(const void *x, uint64_t N, uint64_t K, int8_t *codes, uint16_t *scal
         Check chk{0, 0, 0, {0}};
         const GqHostSrc<(int)ESZ> src{a.x, rows * K, &chk};
         for (uint32_t g = 0; g < a.ngroups; g++) {
-            float v[LPG][GQ_VPL], am[LPG];
-            bool bad[LPG];
+            float v[LPG][GQ_VPL];
             uint64_t off[LPG];
             uint32_t cnt[LPG];
-            float amax = 0.0f;
-            bool anybad = false;
+            uint32_t mag = 0u;
             for (uint32_t j = 0; j < LPG; j++) {
                 cnt[j] = gq_chunk<GQ_VPL>(a, (int)G, g, j, &off[j]);
-                if (vin)
-                    gq_load<IN, true>(src, off[j], cnt[j], v[j], &am[j], &bad[j]);
-                else
-                    gq_load<IN, false>(src, off[j], cnt[j], v[j], &am[j], &bad[j]);
-                amax = am[j] > amax ? am[j] : amax;
-                anybad |= bad[j];
+                const uint32_t m = vin ? gq_load<IN, true>(src, off[j], cnt[j], v[j])
+                                       : gq_load<IN, false>(src, off[j], cnt[j], v[j]);
+                mag = gq_umax(mag, m);
             }
             for (uint32_t j = 0; j < LPG; j++) {
                 uint32_t s16 = 0;
-                int8_t q[GQ_VPL];
-                const uint32_t st = anybad ? 1u : gq_encode<S>(amax, v[j], &s16, q);
+                uint32_t q[GQ_VPL / 4];
+                const uint32_t st = mag >= GQ_NONFINITE ? 1u : gq_encode<S>(bits_f32(mag), v[j], &s16, q);
                 if (st) {
                     *status |= st;
                     continue;
@@ -1200,25 +1195,20 @@ long run_q81(const void *x, uint64_t nblocks, uint32_t *blocks, uint32_t *status
         Check chk{0, 0, 0, {0}};
         const GqHostSrc<(int)ESZ> src{a.x, (uint64_t)a.nblocks * 32u, &chk};
         for (uint32_t b = 0; b < a.nblocks; b++) {
-            float v[LPB][VPL], am[LPB];
-            bool bad[LPB];
-            float amax = 0.0f;
-            bool anybad = false;
+            float v[LPB][VPL];
+            uint32_t mag = 0u;
             for (uint32_t j = 0; j < LPB; j++) {
-                if (vin)
-                    gq_load<IN, true>(src, (uint64_t)b * 32u + j * (uint32_t)VPL, (uint32_t)VPL, v[j], &am[j], &bad[j]);
-                else
-                    gq_load<IN, false>(src, (uint64_t)b * 32u + j * (uint32_t)VPL, (uint32_t)VPL, v[j], &am[j],
-                                       &bad[j]);
-                amax = am[j] > amax ? am[j] : amax;
-                anybad |= bad[j];
+                const uint64_t o = (uint64_t)b * 32u + j * (uint32_t)VPL;
+                const uint32_t m = vin ? gq_load<IN, true>(src, o, (uint32_t)VPL, v[j])
+                                       : gq_load<IN, false>(src, o, (uint32_t)VPL, v[j]);
+                mag = gq_umax(mag, m);
             }
-            int8_t q[LPB][VPL];
+            uint32_t q[LPB][VPL / 4];
             uint32_t d16[LPB], st[LPB];
             int sum = 0;
             for (uint32_t j = 0; j < LPB; j++) {
-                st[j] = q81_encode<VPL>(amax, anybad, v[j], &d16[j], q[j]);
-                for (int k = 0; k < VPL; k++) sum += q[j][k];
+                st[j] = q81_encode<VPL>(mag, v[j], &d16[j], q[j]);
+                sum += q81_sum<VPL>(q[j]);
             }
             for (uint32_t j = 0; j < LPB; j++) {
                 const uint32_t bits = q81_store<VPL>(a, b, j, q[j], d16[j], sum, st[j]);
