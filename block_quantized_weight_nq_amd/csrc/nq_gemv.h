@@ -1115,18 +1115,16 @@ __global__ __launch_bounds__(WG) void k_gemv(GvArgs a) {
 
 // One activation row, single-round kernel: the lane's items i = lane,
 // lane + 64, ... of the chunk (n items per row), each item's activation
-// columns read once and used for every row of the chunk; the first item's
-// columns (x0) were requested with the weight bytes.  Each row's partial
-// takes the items in the same order as gv_chunk_items.
+// columns read once and used for every row of the chunk.  Each row's
+// partial takes the items in the same order as gv_chunk_items.
 template <int F, int RW, class Act>
 NQ_HD void gv1_items1(const LdsSrc &ls, const GvChunk &c, uint32_t lane, uint32_t row_bytes, uint32_t n,
-                      const Act &act, const Tab &tab, const GvA &x0, float (&acc)[RW][1]) {
+                      const Act &act, const Tab &tab, float (&acc)[RW][1]) {
     constexpr uint32_t IPB = GvItem<F>::IPB, S = (uint32_t)block_bytes(F);
     for (uint32_t i = lane; i < n; i += 64u) {
         const uint32_t bl = i / IPB, pt = i - bl * IPB;
-        GvA xi;
-        if (i != lane) gv_a<F>(act, 0u, c.c0 + bl, pt, xi);
-        const GvA &x = i == lane ? x0 : xi;
+        GvA x;
+        gv_a<F>(act, 0u, c.c0 + bl, pt, x);
 #pragma unroll
         for (int rr = 0; rr < RW; rr++)
             if ((uint32_t)rr < c.rw) {
@@ -1137,38 +1135,151 @@ NQ_HD void gv1_items1(const LdsSrc &ls, const GvChunk &c, uint32_t lane, uint32_
     }
 }
 
+// The activation as the single-round kernel holds it in LDS: the rows' q8_1
+// blocks exactly as in memory (9 dwords each: the scale and sum half-words,
+// then 32 codes), row m's block ab at dword 9 * (m * kb + ab); the exact
+// code sum is formed from the codes.
+struct GvActRaw {
+    const uint32_t *lds;
+    uint32_t kb;
+    NQ_HD float block(uint32_t m, uint32_t ab, uint32_t (&c)[8], int *S) const {
+        const uint32_t *p = lds + 9u * (m * kb + ab);
+        int s = 0;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            c[j] = p[1 + j];
+            s = dot4(ONES8, c[j], s);
+        }
+        *S = s;
+        return f16(p[0] & 0xFFFFu);
+    }
+};
+
+// Waves per single-round workgroup at most (the hardware's 1024 threads).
+constexpr uint32_t GV1_MAX_WAVES = 16u;
+
+// s_waitcnt immediate for "at most n memory loads of this wave outstanding"
+// (vmcnt in bits 3:0 and 15:14; the export and LDS counters left at their
+// maxima, so they are not waited for).
+constexpr uint32_t gv_vm_imm(uint32_t n) { return (n & 15u) | (7u << 4) | (15u << 8) | ((n >> 4) << 14); }
+
+// Waits until at most x of the wave's memory loads are outstanding, with x
+// rounded down to one of a few counts (waiting for fewer is always safe).
+// x is wave-uniform.
+__device__ inline void gv_wait_vm(uint32_t x) {
+    if (x >= 32u)
+        __builtin_amdgcn_s_waitcnt(gv_vm_imm(32u));
+    else if (x >= 16u)
+        __builtin_amdgcn_s_waitcnt(gv_vm_imm(16u));
+    else if (x >= 12u)
+        __builtin_amdgcn_s_waitcnt(gv_vm_imm(12u));
+    else if (x >= 8u)
+        __builtin_amdgcn_s_waitcnt(gv_vm_imm(8u));
+    else if (x >= 6u)
+        __builtin_amdgcn_s_waitcnt(gv_vm_imm(6u));
+    else if (x >= 4u)
+        __builtin_amdgcn_s_waitcnt(gv_vm_imm(4u));
+    else if (x >= 3u)
+        __builtin_amdgcn_s_waitcnt(gv_vm_imm(3u));
+    else if (x >= 2u)
+        __builtin_amdgcn_s_waitcnt(gv_vm_imm(2u));
+    else if (x >= 1u)
+        __builtin_amdgcn_s_waitcnt(gv_vm_imm(1u));
+    else
+        __builtin_amdgcn_s_waitcnt(gv_vm_imm(0u));
+}
+
+// LDS dwords the single-round kernel keeps for act_dw activation dwords
+// (the wave regions after them start 16-byte aligned).
+NQ_HD uint32_t gv1_act_region(uint32_t act_dw) { return (act_dw + 3u) & ~3u; }
+
+// Phase 1 of a single-round workgroup: the activation blocks (act_dw dwords
+// from a 16-byte aligned address: 16-byte loads to LDS, and the last
+// act_dw mod 4 dwords by dword loads of wave 0) and the codebook tables
+// (dword loads to LDS), spread over the workgroup's waves: load i of wave w
+// moves group (or dword) 64 * (i * nw + w) + lane.
+template <int F>
+__device__ void gv1_stage(uint64_t *t8, uint32_t *t4, const uint32_t *xq, uint32_t *act, uint32_t act_dw,
+                          uint32_t wave, uint32_t nw, uint32_t lane) {
+    using TS = TabSpec<F>;
+    const uint32_t ng = act_dw / 4u, rd = act_dw % 4u;
+    for (uint32_t b = 64u * wave; b < ng; b += 64u * nw)
+        if (b + lane < ng)
+            __builtin_amdgcn_global_load_lds((const void *)(xq + 4u * (b + lane)),
+                                             (__attribute__((address_space(3))) void *)(act + 4u * b), 16u, 0, 0);
+    if (rd != 0u && wave == 0u && lane < rd)
+        __builtin_amdgcn_global_load_lds((const void *)(xq + 4u * ng + lane),
+                                         (__attribute__((address_space(3))) void *)(act + 4u * ng), 4u, 0, 0);
+    if constexpr (TS::n8 > 0) {
+        const uint32_t *g = (const uint32_t *)TS::src8();
+        constexpr uint32_t nd = 2u * (uint32_t)TS::n8;
+        for (uint32_t b = 64u * wave; b < nd; b += 64u * nw)
+            if (b + lane < nd)
+                __builtin_amdgcn_global_load_lds((const void *)(g + b + lane),
+                                                 (__attribute__((address_space(3))) void *)((uint32_t *)t8 + b), 4u,
+                                                 0, 0);
+    }
+    if constexpr (TS::n4 > 0) {
+        const uint32_t *g = TS::src4();
+        constexpr uint32_t nd = (uint32_t)TS::n4;
+        for (uint32_t b = 64u * wave; b < nd; b += 64u * nw)
+            if (b + lane < nd)
+                __builtin_amdgcn_global_load_lds((const void *)(g + b + lane),
+                                                 (__attribute__((address_space(3))) void *)(t4 + b), 4u, 0, 0);
+    }
+}
+
 // Single-round variant: when every chunk of the launch can be resident at
-// once, each wave takes exactly one chunk of RW whole rows and the launch's
-// waves cover all of them.  A wave requests all of its chunk's bytes before
-// anything else and then computes: nothing is issued after the weight
-// bytes, so no wave starts a second round of loads late in the transfer,
-// and the compute of waves whose bytes arrived early overlaps the loads
-// still in flight.  The bytes go straight from global memory into the
-// wave's LDS region (16-byte loads to LDS, lane l of load k filling group
-// 64k + l), so no registers hold them.  The launch's weight bytes start
-// 16-byte aligned (the host checks), so every group is one aligned 16-byte
-// load; a final group that passes the last weight dword is loaded by its
-// lane as the 16 bytes ending there and shifted into place (gv_put's rule),
-// so no load leaves the payload's dwords.  The activation is read from
-// global memory (cached); with one activation row, the columns of the
-// lane's first item are requested right behind the weight bytes.
-template <int F, int MT, int RW>
-__global__ __launch_bounds__(WG) void k_gemv1(GvArgs a, uint32_t region_dw) {
+// once, each wave takes exactly one chunk and the launch's waves cover all
+// of them.  A chunk is RW whole rows (KS = 1) or, for long rows, one of KS
+// parts of one row (RW = 1: part h holds blocks h * cb .. h * cb + cb - 1);
+// the KS waves of a row sit in one workgroup and their row sums meet in
+// LDS, added in part order.  A workgroup has nw = blockDim.x / 64 waves
+// (up to 16), so that one LDS copy of the activation serves them all.
+//
+// Loads, all issued before any wait, in this order:
+//  1. the workgroup's shared bytes, spread over its waves (gv1_stage): the
+//     activation rows' q8_1 blocks as they are in memory (from LDS dword
+//     0), and the codebook tables;
+//  2. the wave's chunk, straight from global memory into the wave's LDS
+//     region (16-byte loads to LDS, lane l of load k filling group 64k + l;
+//     the launch's weight bytes start 16-byte aligned, as the host checks,
+//     so every group is one aligned 16-byte load; a final group that passes
+//     the last weight dword is loaded by its lane as the 16 bytes ending
+//     there and shifted into place, gv_put's rule, so no load leaves the
+//     payload's dwords).
+// The memory counter completes in issue order, so waiting until no more
+// loads are outstanding than the wave's chunk loads with an active lane
+// (each of those is issued) means its phase-1 loads have landed; after a
+// workgroup barrier every wave's have.  A wave then waits for its own chunk
+// only: the compute of waves whose bytes arrived early overlaps the loads
+// still in flight, and nothing is issued after the weight bytes.
+template <int F, int MT, int RW, int KS>
+__global__ __launch_bounds__(64 * GV1_MAX_WAVES) void k_gemv1(GvArgs a, uint32_t region_dw, uint32_t act_dw) {
+    static_assert(KS == 1 || RW == 1, "a split row is a single-row chunk");
     using TS = TabSpec<F>;
     __shared__ uint64_t t8[TS::n8 > 0 ? TS::n8 : 1];
     __shared__ uint32_t t4[TS::n4 > 0 ? TS::n4 : 1];
+    __shared__ float part[KS > 1 ? GV1_MAX_WAVES : 1][MT];
     extern __shared__ __attribute__((aligned(16))) uint32_t gv_lds[];
+    const uint32_t nw = blockDim.x >> 6;
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const uint32_t r = (blockIdx.x * GV_WAVES + wave) * (uint32_t)RW;
-    uint32_t *lds = gv_lds + wave * region_dw;
+    const uint32_t cw = blockIdx.x * nw + wave;  // the wave's chunk
+    const uint32_t r = KS == 1 ? cw * (uint32_t)RW : cw / (uint32_t)KS;
+    const uint32_t h = KS == 1 ? 0u : cw % (uint32_t)KS;
+    uint32_t *lds = gv_lds + gv1_act_region(act_dw) + wave * region_dw;
     const bool live = r < a.rows;
+    gv1_stage<F>(t8, t4, a.xq, gv_lds, MT == 1 ? act_dw : 0u, wave, nw, lane);
+    __builtin_amdgcn_sched_barrier(0);  // the shared bytes' loads stay ahead of the chunk's
     GvChunk c{};
+    uint32_t issued = 0u;  // chunk loads with an active lane
     if (live) {
-        c = gv_chunk(a, r, 0u);
+        c = gv_chunk(a, r, h * a.cb);
         const uint32_t ng = c.g1 - c.g0 + 1u;
         const bool tail = 4u * c.g1 + 3u > a.wlast;  // only the launch's last group can pass wlast
         const uint32_t nfull = tail ? ng - 1u : ng;
+        issued = (nfull + 63u) / 64u;
         for (uint32_t k = 0; 64u * k < ng; k++) {
             const uint32_t j = 64u * k + lane;
             if (j < nfull)
@@ -1185,37 +1296,57 @@ __global__ __launch_bounds__(WG) void k_gemv1(GvArgs a, uint32_t region_dw) {
             gv_put<1>(one, a.wlast, 0u, v, lds + 4u * (ng - 1u));
         }
     }
-    const GvAct<false> act{a.xq, nullptr, a.K, a.kb, a.xrow, a.M};
-    constexpr uint32_t IPB = GvItem<F>::IPB;
-    const uint32_t n = live ? c.nb * IPB : 0u;
-    GvA x0;
-    if constexpr (MT == 1)
-        if (lane < n) gv_a<F>(act, 0u, c.c0 + lane / IPB, lane % IPB, x0);
-    if constexpr (TS::n8 + TS::n4 > 0) {
-        gv_fill_tables<F>(t8, t4, threadIdx.x);
-        __syncthreads();
-    }
-    if (!live) return;  // no workgroup barrier follows
+    __builtin_amdgcn_sched_barrier(0);
+    gv_wait_vm(issued);  // this wave's phase-1 loads have landed
+    __builtin_amdgcn_s_barrier();  // and every wave's
+    __builtin_amdgcn_sched_barrier(0);
+    if (KS == 1 && !live) return;  // no workgroup barrier follows
     float acc[RW][MT];
 #pragma unroll
     for (int rr = 0; rr < RW; rr++)
 #pragma unroll
         for (int m = 0; m < MT; m++) acc[rr][m] = 0.0f;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the 16-byte loads to LDS have landed
-    wave_lds_sync();                     // and the shifted last group's stores
-    const Tab tab{t8, t4, nullptr, nullptr, 0xFFFFFFFFu, 1u};
-    const LdsSrc ls{lds, 4u * (c.g1 - c.g0) + 3u};
-    if constexpr (MT == 1)
-        gv1_items1<F, RW>(ls, c, lane, a.row_bytes, n, act, tab, x0, acc);
-    else
-        gv_chunk_items<F, MT, RW>(ls, c, lane, a.M, a.row_bytes, act, tab, acc);
+    if (live) {
+        __builtin_amdgcn_s_waitcnt(gv_vm_imm(0u));  // the chunk's loads to LDS have landed
+        wave_lds_sync();                             // and the shifted last group's stores
+        const Tab tab{t8, t4, nullptr, nullptr, 0xFFFFFFFFu, 1u};
+        const LdsSrc ls{lds, 4u * (c.g1 - c.g0) + 3u};
+        if constexpr (MT == 1)
+            gv1_items1<F, RW>(ls, c, lane, a.row_bytes, c.nb * GvItem<F>::IPB, GvActRaw{gv_lds, a.kb}, tab, acc);
+        else
+            gv_chunk_items<F, MT, RW>(ls, c, lane, a.M, a.row_bytes, GvAct<false>{a.xq, nullptr, a.K, a.kb, a.xrow, a.M},
+                                      tab, acc);
+    }
+    if constexpr (KS == 1) {
 #pragma unroll
-    for (int rr = 0; rr < RW; rr++)
+        for (int rr = 0; rr < RW; rr++)
 #pragma unroll
-        for (int m = 0; m < MT; m++) {
-            const float v = wave_sum63(acc[rr][m]);
-            if (lane == 63u && (uint32_t)rr < c.rw && m < (int)a.M) a.y[(uint64_t)m * a.ldy + r + (uint32_t)rr] = v;
+            for (int m = 0; m < MT; m++) {
+                const float v = wave_sum63(acc[rr][m]);
+                if (lane == 63u && (uint32_t)rr < c.rw && m < (int)a.M)
+                    a.y[(uint64_t)m * a.ldy + r + (uint32_t)rr] = v;
+            }
+    } else {
+        // every wave of the workgroup reaches the barrier; part 0's wave adds
+        // the other parts' sums in part order and stores the row
+        float v[MT];
+#pragma unroll
+        for (int m = 0; m < MT; m++) v[m] = wave_sum63(acc[0][m]);
+        if (h != 0u && lane == 63u) {
+#pragma unroll
+            for (int m = 0; m < MT; m++) part[wave][m] = v[m];
         }
+        __syncthreads();
+        if (h == 0u && live && lane == 63u) {
+#pragma unroll
+            for (int m = 0; m < MT; m++) {
+                float t = v[m];
+#pragma unroll
+                for (int j = 1; j < KS; j++) t += part[wave + (uint32_t)j][m];
+                if (m < (int)a.M) a.y[(uint64_t)m * a.ldy + r] = t;
+            }
+        }
+    }
 }
 
 // Host description of one product call.
@@ -1330,11 +1461,11 @@ int launch_gemv_mt(const GvLaunch &L, hipStream_t stream) {
 #define NQ_GV1 1
 #endif
 
-// LDS dwords of a single-round wave region for chunks of rw rows: the
-// 16-byte groups the chunk can span at any start offset, plus one group of
-// padding.
-inline uint32_t gv1_region_dw(uint64_t row_bytes, uint32_t rw) {
-    return 4u * (uint32_t)((15u + rw * row_bytes + 15u) / 16u + 1u);
+// LDS dwords of a single-round wave region for chunks of chunk_bytes bytes:
+// the 16-byte groups such a chunk can span at any start offset, plus one
+// group of padding.
+inline uint32_t gv1_region_dw(uint64_t chunk_bytes) {
+    return 4u * (uint32_t)((15u + chunk_bytes + 15u) / 16u + 1u);
 }
 
 // Rows per chunk of the single-round launch, candidate k (0..2) in order of
@@ -1347,45 +1478,90 @@ inline uint32_t gv1_candidate(uint64_t N, uint64_t M, uint32_t cus, int k) {
     return M > 1 && N / 2 >= 8u * (uint64_t)cus ? more[k] : few[k];
 }
 
-// A single-round launch: rows per chunk (0: none), wave region, LDS bytes
-// per workgroup and workgroups.
+// Parts per row tried first for single-row chunks of one activation row: 2
+// when a row holds more than 64 items (a lane would take several items of
+// the row in turn) and at least two blocks, and either the rows are long
+// (K >= 8192) or whole rows would give fewer than 16 waves per compute
+// unit; else 1.  Measured on eight formats: the split gains 3-9% at
+// [4096, 14336] for q4_k, q4_0, q2_k and iq2_xxs (loses up to 6% for
+// mxfp4) and 5-10% at [1024, 4096], but loses 7-17% at [4096, 4096].
+inline uint32_t gv1_parts(uint64_t N, uint64_t nbr, uint32_t ipb, uint64_t K, uint32_t cus) {
+    return nbr >= 2u && nbr * ipb > 64u && (K >= 8192u || N < 16u * (uint64_t)cus) ? 2u : 1u;
+}
+
+// A single-round launch: rows per chunk (0: none), parts per row, blocks per
+// chunk row, waves per workgroup, wave region and activation dwords, LDS
+// bytes per workgroup and workgroups.
 struct Gv1Plan {
-    uint32_t rw, region_dw, lds, grid;
+    uint32_t rw, ks, cb, nw, region_dw, act_dw, lds, grid;
 };
 
-// The single-round plan of a launch of N rows of row_bytes bytes starting
-// at address w, on `cus` compute units; per_cu(rw, lds) gives the
-// workgroups of the rw-row kernel a compute unit holds at once with that
-// much dynamic LDS.  None (rw = 0) when the bytes do not start 16-byte
+constexpr uint32_t GV1_LDS_MAX = 163840u;  // LDS bytes of a compute unit (and of one workgroup at most)
+
+// The single-round plan of a launch of N rows of nbr blocks of S bytes (ipb
+// items each) starting at address w, with M activation rows of K values at
+// address xq, on `cus` compute units; per_cu(rw, ks, nw, lds) gives the
+// workgroups of nw waves of that kernel a compute unit holds at once with
+// that much dynamic LDS.  With one activation row (staged in LDS, one copy
+// per workgroup), for each candidate (rows per chunk, and single-row chunks
+// split in parts first) it takes the most workgroups per compute unit,
+// g = 8 .. 1, whose waves per workgroup, ceil(chunks / (cus * g)) (even for
+// split rows), stay within 16 and whose workgroups all fit at once: the
+// smallest workgroups, whose barrier waits on the fewest waves (measured
+// 0-13% faster than the largest that fit, at no loss); with several
+// activation rows (read from global memory) workgroups have four waves and
+// rows are not split.
+// None (rw = 0) when the weight bytes or the activation do not start 16-byte
 // aligned, the launch holds fewer than 16 bytes or more than 32-bit byte
-// offsets reach (max_rows), or no candidate's chunks all fit at once.
+// offsets reach (max_rows), or nothing fits.
 template <class PerCu>
-Gv1Plan gv1_plan(uint64_t N, uint64_t row_bytes, uint64_t M, uint64_t max_rows, uintptr_t w, uint32_t cus,
-                 PerCu per_cu) {
-    Gv1Plan p{0u, 0u, 0u, 0u};
-    if (!NQ_GV1 || (w & 15u) != 0u || N > max_rows || N * row_bytes < 16u) return p;
+Gv1Plan gv1_plan(uint64_t N, uint64_t nbr, uint32_t S, uint32_t ipb, uint64_t M, uint64_t K, uint64_t max_rows,
+                 uintptr_t w, uintptr_t xq, uint32_t cus, PerCu per_cu) {
+    Gv1Plan p{0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    const uint64_t row_bytes = nbr * S, act_dw = M == 1u ? (K / 32u) * 9u : 0u;
+    const uint64_t act_bytes = 4u * (uint64_t)gv1_act_region((uint32_t)act_dw);
+    if (!NQ_GV1 || (w & 15u) != 0u || (xq & 15u) != 0u || N > max_rows || N * row_bytes < 16u || cus == 0u ||
+        act_bytes > GV1_LDS_MAX)
+        return p;
     for (int k = 0; k < 3; k++) {
         const uint32_t rw = gv1_candidate(N, M, cus, k);
-        const uint32_t region = gv1_region_dw(row_bytes, rw), lds = 4u * GV_WAVES * region;
-        const uint64_t chunks = (N + rw - 1) / rw, grid = (chunks + GV_WAVES - 1) / GV_WAVES;
-        if (lds > 65536u) continue;
-        const uint64_t held = (uint64_t)per_cu(rw, lds) * cus;
-        if (held >= 1u && grid <= held) {
-            p.rw = rw;
-            p.region_dw = region;
-            p.lds = lds;
-            p.grid = (uint32_t)grid;
-            return p;
+        for (uint32_t ks = rw == 1u && M == 1u ? gv1_parts(N, nbr, ipb, K, cus) : 1u; ks >= 1u; ks /= 2u) {
+            const uint64_t cb = (nbr + ks - 1u) / ks;
+            const uint32_t region = gv1_region_dw(ks == 1u ? rw * row_bytes : cb * S);
+            const uint64_t chunks = ks == 1u ? (N + rw - 1) / rw : N * ks;
+            for (uint32_t gi = 8u; gi >= 1u; gi--) {
+                uint64_t g = gi;
+                uint64_t nw = (chunks + (uint64_t)cus * g - 1u) / ((uint64_t)cus * g);
+                nw += nw % ks;
+                if (M > 1u) {  // activation read from global memory: four-wave workgroups
+                    if (gi < 8u) break;
+                    nw = GV_WAVES;
+                    g = (chunks + nw * cus - 1u) / (nw * cus);
+                }
+                if (nw > GV1_MAX_WAVES) continue;
+                const uint64_t lds = act_bytes + 4u * nw * region;
+                if (lds > GV1_LDS_MAX) continue;
+                if ((uint64_t)per_cu(rw, ks, (uint32_t)nw, (uint32_t)lds) < g) continue;
+                p.rw = rw;
+                p.ks = ks;
+                p.cb = (uint32_t)cb;
+                p.nw = (uint32_t)nw;
+                p.region_dw = region;
+                p.act_dw = (uint32_t)act_dw;
+                p.lds = (uint32_t)lds;
+                p.grid = (uint32_t)((chunks + nw - 1u) / nw);
+                return p;
+            }
         }
     }
     return p;
 }
 
-template <int F, int MT, int RW>
-int gv1_per_cu(uint32_t lds) {
+template <int F, int MT, int RW, int KS>
+int gv1_per_cu(uint32_t nw, uint32_t lds) {
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)k_gemv1<F, MT, RW>, WG, lds) !=
-        hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)k_gemv1<F, MT, RW, KS>, 64 * (int)nw,
+                                                     lds) != hipSuccess)
         return 0;
     return per_cu;
 }
@@ -1393,23 +1569,28 @@ int gv1_per_cu(uint32_t lds) {
 // The single-round launch when its plan exists; -1 (nothing launched) when not.
 template <int F, int MT>
 int launch_gemv1(const GvLaunch &L, hipStream_t stream) {
-    const uint64_t row_bytes = L.K / (uint64_t)block_values(F) * (uint64_t)block_bytes(F);
-    const Gv1Plan p = gv1_plan(L.N, row_bytes, L.M, gv_max_rows<F>(L), (uintptr_t)L.w, L.cus,
-                               [](uint32_t rw, uint32_t lds) {
-                                   return rw == 1u ? gv1_per_cu<F, MT, 1>(lds)
-                                          : rw == 2u ? gv1_per_cu<F, MT, 2>(lds)
-                                                     : gv1_per_cu<F, MT, 3>(lds);
+    const uint64_t nbr = L.K / (uint64_t)block_values(F);
+    const Gv1Plan p = gv1_plan(L.N, nbr, (uint32_t)block_bytes(F), GvItem<F>::IPB, L.M, L.K, gv_max_rows<F>(L),
+                               (uintptr_t)L.w, (uintptr_t)L.xq, L.cus,
+                               [](uint32_t rw, uint32_t ks, uint32_t nw, uint32_t lds) {
+                                   return ks == 2u   ? gv1_per_cu<F, MT, 1, 2>(nw, lds)
+                                          : rw == 1u ? gv1_per_cu<F, MT, 1, 1>(nw, lds)
+                                          : rw == 2u ? gv1_per_cu<F, MT, 2, 1>(nw, lds)
+                                                     : gv1_per_cu<F, MT, 3, 1>(nw, lds);
                                });
     if (p.rw == 0u) return -1;
     GvArgs a = gv_args<F>(L, 0, L.N);
     a.rw = p.rw;
-    a.cb = a.nbr;
-    if (p.rw == 1u)
-        hipLaunchKernelGGL((k_gemv1<F, MT, 1>), dim3(p.grid), dim3(WG), p.lds, stream, a, p.region_dw);
+    a.cb = p.cb;
+    const dim3 grid(p.grid), block(64u * p.nw);
+    if (p.ks == 2u)
+        hipLaunchKernelGGL((k_gemv1<F, MT, 1, 2>), grid, block, p.lds, stream, a, p.region_dw, p.act_dw);
+    else if (p.rw == 1u)
+        hipLaunchKernelGGL((k_gemv1<F, MT, 1, 1>), grid, block, p.lds, stream, a, p.region_dw, p.act_dw);
     else if (p.rw == 2u)
-        hipLaunchKernelGGL((k_gemv1<F, MT, 2>), dim3(p.grid), dim3(WG), p.lds, stream, a, p.region_dw);
+        hipLaunchKernelGGL((k_gemv1<F, MT, 2, 1>), grid, block, p.lds, stream, a, p.region_dw, p.act_dw);
     else
-        hipLaunchKernelGGL((k_gemv1<F, MT, 3>), dim3(p.grid), dim3(WG), p.lds, stream, a, p.region_dw);
+        hipLaunchKernelGGL((k_gemv1<F, MT, 3, 1>), grid, block, p.lds, stream, a, p.region_dw, p.act_dw);
     return hipGetLastError() != hipSuccess ? 9 : 0;  // NQ_ERR_HIP
 }
 

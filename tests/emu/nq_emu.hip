@@ -405,48 +405,111 @@ long run_gemv_lds(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, u
     return errors;
 }
 
-// The single-round product kernel (k_gemv1) for a plan the launcher made:
-// every wave's one chunk of p.rw rows, staged as the kernel stages it (the
-// 16-byte loads to LDS of groups g0 .. g1, each at a 16-byte aligned address
-// and inside the payload, and the last group's shifted load), into a
-// poisoned region whose size the plan gives; the staged bytes are compared
-// with the payload, then the lanes' items and each row's butterfly sum.
-template <int F, int MT, int RW>
+// The emulator's device model of a compute unit: at most `limit`
+// workgroups, 160 KiB of LDS and 32 waves (eight per SIMD).
+int gv1_emu_per_cu(uint32_t limit, uint32_t nw, uint32_t lds) {
+    const uint32_t by_lds = nq::GV1_LDS_MAX / lds, by_waves = 32u / nw;
+    uint32_t n = limit < by_lds ? limit : by_lds;
+    return (int)(n < by_waves ? n : by_waves);
+}
+
+// Phase-1 staging of a single-round workgroup as gv1_stage spreads it:
+// load i of wave w moves group 64 * (i * nw + w) + lane of ng; every group
+// must be moved exactly once.  Returns false (with a message) otherwise.
+bool gv1_stage_cover(uint32_t ng, uint32_t nw, std::vector<uint32_t> &hits) {
+    hits.assign(ng, 0u);
+    for (uint32_t w = 0; w < nw; w++)
+        for (uint32_t b = 64u * w; b < ng; b += 64u * nw)
+            for (uint32_t lane = 0; lane < 64u; lane++)
+                if (b + lane < ng) hits[b + lane]++;
+    for (uint32_t q = 0; q < ng; q++)
+        if (hits[q] != 1u) return false;
+    return true;
+}
+
+// The single-round product kernel (k_gemv1) for a plan the launcher made.
+// Per workgroup of p.nw waves: phase 1, the activation blocks (one
+// activation row; several are read from global memory) and codebook tables
+// moved into LDS as gv1_stage spreads them (coverage checked), then
+// every wave's one chunk (p.rw whole rows, or part h of a row split in KS
+// parts of p.cb blocks), staged as the kernel stages it (the 16-byte loads
+// to LDS of groups g0 .. g1, each at a 16-byte aligned address and inside
+// the payload, and the last group's shifted load) into a poisoned region
+// whose size the plan gives; the staged bytes are compared with the
+// payload; the count of chunk loads the wave waits on is checked against
+// the loads that have an active lane; then the lanes' items (activation
+// from the LDS copy) and each chunk row's butterfly sum, and for split rows
+// the parts' sums added in part order by part 0's wave.
+template <int F, int MT, int RW, int KS>
 long run_gemv1(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y,
                const nq::Gv1Plan &p, char *err, int errlen) {
     using namespace nq;
+    static_assert(KS == 1 || RW == 1, "a split row is a single-row chunk");
     const GvLaunch L{w, N, K, M, xq, y, 0u};
     std::vector<uint64_t> t8(TabSpec<F>::n8 > 0 ? TabSpec<F>::n8 : 1);
     std::vector<uint32_t> t4(TabSpec<F>::n4 > 0 ? TabSpec<F>::n4 : 1);
-    for (uint32_t tid = 0; tid < (uint32_t)WG; tid++) gv_fill_tables<F>(t8.data(), t4.data(), tid);
+    std::vector<uint32_t> hits;
+    if ((TabSpec<F>::n8 > 0 && !gv1_stage_cover(2u * (uint32_t)TabSpec<F>::n8, p.nw, hits)) ||
+        (TabSpec<F>::n4 > 0 && !gv1_stage_cover((uint32_t)TabSpec<F>::n4, p.nw, hits))) {
+        snprintf(err, errlen, "table staging does not cover every dword once");
+        return 1;
+    }
+    if constexpr (TabSpec<F>::n8 > 0)
+        memcpy(t8.data(), TabSpec<F>::src8(), sizeof(uint64_t) * (size_t)TabSpec<F>::n8);
+    if constexpr (TabSpec<F>::n4 > 0)
+        memcpy(t4.data(), TabSpec<F>::src4(), sizeof(uint32_t) * (size_t)TabSpec<F>::n4);
     const Tab tab{t8.data(), t4.data(), nullptr, nullptr, 0xFFFFFFFFu, 1u};
     GvArgs a = gv_args<F>(L, 0, N);
     a.rw = (uint32_t)RW;
-    a.cb = a.nbr;
-    if (a.wmis != 0u || ((uintptr_t)a.wbase & 15u) != 0u) {
-        snprintf(err, errlen, "single-round launch on weight bytes not 16-byte aligned");
+    a.cb = p.cb;
+    if (a.wmis != 0u || ((uintptr_t)a.wbase & 15u) != 0u || ((uintptr_t)xq & 15u) != 0u) {
+        snprintf(err, errlen, "single-round launch on weight or activation bytes not 16-byte aligned");
         return 1;
     }
-    if (p.lds != 4u * GV_WAVES * p.region_dw || (uint64_t)p.grid * GV_WAVES * RW < N) {
-        snprintf(err, errlen, "plan: lds %u region %u grid %u for %llu rows", p.lds, p.region_dw, p.grid,
-                 (unsigned long long)N);
+    const uint64_t chunks = KS == 1 ? (N + RW - 1) / RW : N * KS;
+    if (p.lds != 4u * (gv1_act_region(p.act_dw) + p.nw * p.region_dw) || p.lds > GV1_LDS_MAX || p.nw == 0u ||
+        p.nw > GV1_MAX_WAVES || p.nw % KS != 0u || (uint64_t)p.grid * p.nw < chunks ||
+        p.act_dw != (M == 1u ? a.kb * 9u : 0u) || p.ks != (uint32_t)KS ||
+        (KS == 1 ? p.cb != a.nbr : (uint64_t)p.cb * (KS - 1) >= a.nbr || (uint64_t)p.cb * KS < a.nbr)) {
+        snprintf(err, errlen, "plan: lds %u region %u act %u waves %u grid %u parts %u of %u blocks for %llu rows",
+                 p.lds, p.region_dw, p.act_dw, p.nw, p.grid, p.ks, p.cb, (unsigned long long)N);
         return 1;
     }
+    if (!gv1_stage_cover(p.act_dw / 4u, p.nw, hits)) {  // the act_dw mod 4 last dwords: wave 0's lanes
+        snprintf(err, errlen, "activation staging does not cover every group once");
+        return 1;
+    }
+    std::vector<uint32_t> act_lds(p.act_dw + 1u);
+    memcpy(act_lds.data(), xq, 4u * (size_t)p.act_dw);
+    const GvActRaw act{act_lds.data(), a.kb};                          // one activation row: from LDS
+    const GvAct<false> gact{a.xq, nullptr, a.K, a.kb, a.xrow, a.M};  // several: from global memory
     Check chk{(uintptr_t)w, (uintptr_t)(w + N * a.row_bytes), 0, {0}};
     const HostSrc src{a.wbase, a.wlast, &chk};
-    const GvAct<false> act{a.xq, nullptr, a.K, a.kb, a.xrow, a.M};
     constexpr uint32_t IPB = GvItem<F>::IPB;
+    const uint32_t S = (uint32_t)block_bytes(F);
     std::vector<uint32_t> lds(p.region_dw);
-    for (uint32_t b = 0; b < p.grid; b++)
-        for (uint32_t wave = 0; wave < GV_WAVES; wave++) {
-            const uint32_t r = (b * GV_WAVES + wave) * (uint32_t)RW;
+    std::vector<float> part((size_t)p.nw * MT);
+    for (uint32_t b = 0; b < p.grid; b++) {
+        std::fill(part.begin(), part.end(), 0.0f);
+        for (uint32_t wave = 0; wave < p.nw; wave++) {
+            const uint32_t cw = b * p.nw + wave;
+            const uint32_t r = KS == 1 ? cw * (uint32_t)RW : cw / (uint32_t)KS;
+            const uint32_t h = KS == 1 ? 0u : cw % (uint32_t)KS;
             if (r >= a.rows) continue;
-            const GvChunk c = gv_chunk(a, r, 0u);
+            const GvChunk c = gv_chunk(a, r, h * a.cb);
             const uint32_t ng = c.g1 - c.g0 + 1u;
             const bool tail = 4u * c.g1 + 3u > a.wlast;
             const uint32_t nfull = tail ? ng - 1u : ng;
-            if (4u * ng + 4u > p.region_dw) {
-                snprintf(err, errlen, "chunk of %u groups past its region of %u dwords", ng, p.region_dw);
+            if (4u * ng + 4u > p.region_dw || c.nb == 0u) {
+                snprintf(err, errlen, "chunk of %u groups (%u blocks) past its region of %u dwords", ng, c.nb,
+                         p.region_dw);
+                return 1;
+            }
+            uint32_t active = 0u;  // chunk loads with at least one active lane
+            for (uint32_t k = 0; 64u * k < ng; k++) active += 64u * k < nfull ? 1u : 0u;
+            if ((nfull + 63u) / 64u != active) {
+                snprintf(err, errlen, "wave waits on %u chunk loads, %u have an active lane", (nfull + 63u) / 64u,
+                         active);
                 return 1;
             }
             std::fill(lds.begin(), lds.end(), 0xA5A5A5A5u);
@@ -467,8 +530,8 @@ long run_gemv1(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint
             }
             for (uint32_t rr = 0; rr < c.rw; rr++) {
                 const uint8_t *cb = (const uint8_t *)lds.data() + c.o0 + rr * a.row_bytes;
-                const uint8_t *pb = w + (uint64_t)(c.r + rr) * a.row_bytes;
-                if (memcmp(cb, pb, a.row_bytes) != 0 && chk.errors++ == 0)
+                const uint8_t *pb = w + (uint64_t)(c.r + rr) * a.row_bytes + (uint64_t)c.c0 * S;
+                if (memcmp(cb, pb, (size_t)c.nb * S) != 0 && chk.errors++ == 0)
                     snprintf(chk.msg, sizeof chk.msg, "staged chunk of row %u differs from the payload", c.r + rr);
             }
             const LdsSrc ls{lds.data(), 4u * (c.g1 - c.g0) + 3u};
@@ -477,21 +540,34 @@ long run_gemv1(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint
             for (uint32_t lane = 0; lane < 64u; lane++) {
                 for (int rr = 0; rr < RW; rr++)
                     for (int m = 0; m < MT; m++) acc[lane][rr][m] = 0.0f;
-                if constexpr (MT == 1) {
-                    GvA x0;
-                    if (lane < n) gv_a<F>(act, 0u, c.c0 + lane / IPB, lane % IPB, x0);
-                    gv1_items1<F, RW>(ls, c, lane, a.row_bytes, n, act, tab, x0, acc[lane]);
-                } else {
-                    gv_chunk_items<F, MT, RW>(ls, c, lane, a.M, a.row_bytes, act, tab, acc[lane]);
-                }
+                if constexpr (MT == 1)
+                    gv1_items1<F, RW>(ls, c, lane, a.row_bytes, n, act, tab, acc[lane]);
+                else
+                    gv_chunk_items<F, MT, RW>(ls, c, lane, a.M, a.row_bytes, gact, tab, acc[lane]);
             }
             for (uint32_t rr = 0; rr < c.rw; rr++)
                 for (int m = 0; m < MT; m++) {
                     float v[64];
                     for (int l = 0; l < 64; l++) v[l] = acc[l][rr][m];
-                    if (m < (int)a.M) a.y[(uint64_t)m * a.ldy + c.r + rr] = dpp_sum63(v);
+                    const float sum = dpp_sum63(v);
+                    if (KS > 1)
+                        part[(size_t)wave * MT + (size_t)m] = sum;
+                    else if (m < (int)a.M)
+                        a.y[(uint64_t)m * a.ldy + c.r + rr] = sum;
                 }
         }
+        if constexpr (KS > 1) {
+            for (uint32_t wave = 0; wave < p.nw; wave += (uint32_t)KS) {
+                const uint32_t r = (b * p.nw + wave) / (uint32_t)KS;
+                if (r >= a.rows) continue;
+                for (int m = 0; m < (int)a.M; m++) {
+                    float t = part[(size_t)wave * MT + (size_t)m];
+                    for (int j = 1; j < KS; j++) t += part[(size_t)(wave + (uint32_t)j) * MT + (size_t)m];
+                    a.y[(uint64_t)m * a.ldy + r] = t;
+                }
+            }
+        }
+    }
     if (chk.errors) snprintf(err, errlen, "%s", chk.msg);
     return chk.errors;
 }
@@ -511,7 +587,8 @@ long run_gemv_alds(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, 
 // of that many compute units, each holding min(gv1_per_cu, 160 KiB / (the
 // workgroup's LDS)) workgroups (the tables' static LDS included); when it
 // makes none, or with gv1_cus = 0, the chunk-loop kernel.  *rw_out: rows per
-// chunk of the single-round launch, 0 for the chunk loop.
+// chunk of the single-round launch (0 for the chunk loop), plus 256 times its
+// parts per row.
 template <int F, int MT>
 long run_gemv(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint64_t M, float *y, uint32_t resident,
               uint64_t max_rows, uint32_t gv1_cus, uint32_t gv1_per_cu, uint32_t *rw_out, char *err, int errlen) {
@@ -519,17 +596,17 @@ long run_gemv(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint6
     *rw_out = 0u;
     if (gv1_cus > 0u) {
         const GvLaunch L{w, N, K, M, xq, y, gv1_cus};
-        const uint64_t row_bytes = K / (uint64_t)block_values(F) * (uint64_t)block_bytes(F);
         constexpr uint32_t stat = 8u * (uint32_t)TabSpec<F>::n8 + 4u * (uint32_t)TabSpec<F>::n4;
-        const Gv1Plan p = gv1_plan(N, row_bytes, M, max_rows ? max_rows : gv_max_rows<F>(L), (uintptr_t)w, gv1_cus,
-                                   [&](uint32_t, uint32_t lds) {
-                                       const uint32_t by_lds = 163840u / (lds + stat);
-                                       return (int)(by_lds < gv1_per_cu ? by_lds : gv1_per_cu);
+        const Gv1Plan p = gv1_plan(N, K / (uint64_t)block_values(F), (uint32_t)block_bytes(F), GvItem<F>::IPB, M,
+                                   K, max_rows ? max_rows : gv_max_rows<F>(L), (uintptr_t)w, (uintptr_t)xq, gv1_cus,
+                                   [&](uint32_t, uint32_t, uint32_t nw, uint32_t lds) {
+                                       return gv1_emu_per_cu(gv1_per_cu, nw, lds + stat);
                                    });
-        *rw_out = p.rw;
-        if (p.rw == 1u) return run_gemv1<F, MT, 1>(w, N, K, xq, M, y, p, err, errlen);
-        if (p.rw == 2u) return run_gemv1<F, MT, 2>(w, N, K, xq, M, y, p, err, errlen);
-        if (p.rw == 3u) return run_gemv1<F, MT, 3>(w, N, K, xq, M, y, p, err, errlen);
+        *rw_out = p.rw | p.ks << 8;
+        if (p.ks == 2u) return run_gemv1<F, MT, 1, 2>(w, N, K, xq, M, y, p, err, errlen);
+        if (p.rw == 1u) return run_gemv1<F, MT, 1, 1>(w, N, K, xq, M, y, p, err, errlen);
+        if (p.rw == 2u) return run_gemv1<F, MT, 2, 1>(w, N, K, xq, M, y, p, err, errlen);
+        if (p.rw == 3u) return run_gemv1<F, MT, 3, 1>(w, N, K, xq, M, y, p, err, errlen);
     }
     return nq::gv_act_in_lds(M, K) ? run_gemv_alds<F, MT, true>(w, N, K, xq, M, y, resident, max_rows, err, errlen)
                                    : run_gemv_alds<F, MT, false>(w, N, K, xq, M, y, resident, max_rows, err, errlen);
@@ -862,18 +939,21 @@ extern "C" __attribute__((visibility("default"))) void nq_emu_gemm_plan(int fmt,
 template <int F>
 void gv1_plan_of(uint64_t N, uint64_t K, uint64_t M, uint32_t w_mis, uint32_t cus, uint32_t per_cu, uint64_t *out) {
     using namespace nq;
-    const uint64_t row_bytes = K / (uint64_t)block_values(F) * (uint64_t)block_bytes(F);
     constexpr uint32_t stat = 8u * (uint32_t)TabSpec<F>::n8 + 4u * (uint32_t)TabSpec<F>::n4;
     const GvLaunch L{nullptr, N, K, M, nullptr, nullptr, cus};
-    const Gv1Plan p = gv1_plan(N, row_bytes, M, gv_max_rows<F>(L), (uintptr_t)(4096u + w_mis), cus,
-                               [&](uint32_t, uint32_t lds) {
-                                   const uint32_t by_lds = 163840u / (lds + stat);
-                                   return (int)(by_lds < per_cu ? by_lds : per_cu);
+    const Gv1Plan p = gv1_plan(N, K / (uint64_t)block_values(F), (uint32_t)block_bytes(F), GvItem<F>::IPB, M, K,
+                               gv_max_rows<F>(L), (uintptr_t)(4096u + w_mis), (uintptr_t)4096u, cus,
+                               [&](uint32_t, uint32_t, uint32_t nw, uint32_t lds) {
+                                   return gv1_emu_per_cu(per_cu, nw, lds + stat);
                                });
     out[0] = p.rw;
     out[1] = p.region_dw;
     out[2] = p.lds;
     out[3] = p.grid;
+    out[4] = p.ks;
+    out[5] = p.cb;
+    out[6] = p.nw;
+    out[7] = p.act_dw;
 }
 
 extern "C" __attribute__((visibility("default"))) int nq_emu_gemv1_plan(int fmt, uint64_t N, uint64_t K, uint64_t M,

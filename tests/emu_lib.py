@@ -259,13 +259,13 @@ def grouped_absmax(scheme_id, G, x, in_code, x_mis=0, codes_mis=0):
 
 
 def gemv_q8_1(fmt_id, w, N, K, xq, M, w_mis=0, resident=2048, max_rows=0, gv1_cus=0, gv1_per_cu=8,
-              with_rw=False):
+              with_rw=False, with_parts=False):
     """The product through the emulator.  w: payload bytes, xq: q8_1 blocks.
     gv1_cus > 0: the launcher's single-round plan on a device of that many
     compute units holding at most gv1_per_cu workgroups each (else, or when
     the plan makes none, the chunk-loop kernel with `resident` workgroups).
     Returns (y float32 [M, N], bad reads, message, guards_ok[, rows per
-    single-round chunk or 0])."""
+    single-round chunk or 0][, parts per row of a single-round launch])."""
     w = np.ascontiguousarray(w, dtype=np.uint8)
     wbuf, woff = _placed(w.size, 16, w_mis)
     wbuf[woff:woff + w.size] = w
@@ -280,15 +280,20 @@ def gemv_q8_1(fmt_id, w, N, K, xq, M, w_mis=0, resident=2048, max_rows=0, gv1_cu
                                 err, 256)
     y = ybuf[16:16 + M * N].reshape(M, N).copy()
     guards = bool(np.all(np.isnan(ybuf[:16])) and np.all(np.isnan(ybuf[16 + M * N:])))
+    out = (y, rc, err.value.decode(), guards)
     if with_rw:
-        return y, rc, err.value.decode(), guards, rw.value
-    return y, rc, err.value.decode(), guards
+        out += (rw.value & 0xFF,)
+    if with_parts:
+        out += (rw.value >> 8,)
+    return out
 
 
 def gemv1_plan(fmt_id, N, K, M, w_mis=0, cus=256, per_cu=8):
     """The launcher's single-round product plan on the emulator's device
-    model: (rows per chunk or 0, region dwords, LDS bytes, workgroups)."""
-    out = (ctypes.c_uint64 * 4)()
+    model (at most per_cu workgroups, 160 KiB of LDS and 32 waves per compute
+    unit): (rows per chunk or 0, region dwords, LDS bytes, workgroups, parts
+    per row, blocks per chunk row, waves per workgroup, activation dwords)."""
+    out = (ctypes.c_uint64 * 8)()
     rc = lib().nq_emu_gemv1_plan(fmt_id, N, K, M, w_mis, cus, per_cu, out)
     assert rc == 0
     return tuple(int(v) for v in out)

@@ -388,16 +388,22 @@ def test_emu_gemv_matches_oracle(fmt):
 
 @pytest.mark.parametrize("fmt", GGUF)
 def test_emu_gemv_single_round_matches_oracle(fmt):
-    """The single-round kernel: one chunk of 1, 2 or 3 whole rows per wave,
-    staged by aligned 16-byte loads to LDS (the launch's last group shifted
-    into place when the payload ends inside it), as the plan picks it on a
-    device that holds few workgroups; misaligned weight bytes and launches
-    whose chunks do not all fit take the chunk loop."""
+    """The single-round kernel on a device of one compute unit holding
+    per_cu workgroups of up to 16 waves: phase 1 moves the activation blocks
+    (the last act_dw mod 4 dwords by dword loads) and the codebook tables
+    into LDS, spread over the workgroup's waves; each wave's chunk of 1, 2 or
+    3 whole rows is staged by aligned 16-byte loads to LDS (the launch's last
+    group shifted into place when the payload ends inside it).  Whole rows
+    per chunk grow when more waves than one workgroup of 16 (or per_cu of
+    them) would be needed.  Several activation rows are read from global
+    memory by four-wave workgroups (two rows per chunk first once there are
+    16 or more rows); misaligned weight bytes and launches that do not fit
+    take the chunk loop."""
     idx, B, S, _ = oracle.info(fmt)
     K = 3 * B if B >= 64 else 7 * B
-    for N, M, per_cu, w_mis, rw in [(12, 1, 3, 0, 1), (13, 1, 2, 0, 2), (12, 1, 1, 0, 3), (13, 1, 1, 0, 0),
-                                    (12, 1, 3, 4, 0), (13, 3, 2, 0, 2), (12, 8, 1, 0, 3), (5, 2, 1, 0, 2),
-                                    (7, 4, 4, 0, 1), (17, 4, 8, 0, 2)]:
+    for N, M, per_cu, w_mis, rw in [(12, 1, 1, 0, 1), (20, 1, 1, 0, 2), (40, 1, 1, 0, 3), (60, 1, 1, 0, 0),
+                                    (39, 1, 2, 0, 2), (12, 1, 3, 4, 0), (13, 3, 2, 0, 2), (12, 8, 1, 0, 3),
+                                    (5, 2, 1, 0, 2), (17, 4, 8, 0, 2), (33, 4, 1, 0, 0), (7, 4, 4, 0, 1)]:
         w = synth.payload(fmt, N * K // B, 17 + N + M, synth.binade(-6, -2, False))
         _, xq = oracle.quantize_q8_1(_act(M, K, N + 3).astype(np.float32))
         y, rc, msg, guards, got = emu_lib.gemv_q8_1(idx, w, N, K, xq, M, w_mis=w_mis, gv1_cus=1,
@@ -409,26 +415,91 @@ def test_emu_gemv_single_round_matches_oracle(fmt):
         linear_check(y, ref, env, K, f"{fmt} N={N} M={M} rows per chunk {rw}")
 
 
-@pytest.mark.parametrize("fmt,N,K,M,rw", [("gguf:q4_k", 14336, 4096, 1, 2), ("gguf:q4_k", 4096, 14336, 1, 1),
-                                          ("gguf:q4_k", 4096, 4096, 8, 2), ("gguf:q6_k", 1024, 4096, 8, 1),
-                                          ("gguf:q8_0", 14336, 4096, 1, 0),
-                                          ("gguf:q6_k", 4096, 14336, 1, 0), ("gguf:q4_0", 1024, 4096, 1, 1),
-                                          ("gguf:iq2_xxs", 14336, 4096, 1, 2)])
-def test_emu_gemv_single_round_plan(fmt, N, K, M, rw):
-    """On a device of 256 compute units holding up to 8 workgroups each, the
-    single-round plan takes the fewest rows per chunk whose chunks all fit at
-    once, within 160 KiB of LDS per unit, or, for several activation rows and
-    at least 4096 rows, two rows first; weights too large for one round (q8_0
-    at [14336, 4096]: 62 MB) take the chunk loop."""
-    idx = oracle.info(fmt)[0]
+def _items_per_block(fmt):
+    """Items of the product's integer path per block: 64-value items for
+    q4_k, q5_k and q6_k, 32-value items otherwise."""
+    B = oracle.info(fmt)[1]
+    return B // 64 if fmt in ("gguf:q4_k", "gguf:q5_k", "gguf:q6_k") else B // 32
+
+
+@pytest.mark.parametrize("fmt", GGUF)
+def test_emu_gemv_row_split_matches_oracle(fmt):
+    """Single-round launches whose rows hold more than 64 items: each row is
+    split in two parts (blocks 0 .. cb - 1 and cb .. nbr - 1, cb =
+    ceil(nbr / 2)) taken by two waves of one workgroup, and part 0's wave
+    adds the two row sums.  Odd block counts give unequal parts; the longer
+    rows give each lane several items per part; 9 rows (18 parts) take two
+    workgroups of 10 waves, the second with one empty row.  (Several
+    activation rows keep whole rows.)"""
+    idx, B, S, _ = oracle.info(fmt)
+    ipb = _items_per_block(fmt)
+    for nbr, N, M in [(64 // ipb + 1, 5, 1), (64 // ipb + 1, 9, 1), (2 * (64 // ipb) + 3, 3, 1),
+                      (2 * (64 // ipb) + 3, 6, 1)]:
+        K = nbr * B
+        w = synth.payload(fmt, N * nbr, 23 + N + nbr, synth.binade(-6, -2, False))
+        _, xq = oracle.quantize_q8_1(_act(M, K, N + nbr).astype(np.float32))
+        y, rc, msg, guards, rw, ks = emu_lib.gemv_q8_1(idx, w, N, K, xq, M, gv1_cus=1, gv1_per_cu=8, with_rw=True,
+                                                       with_parts=True)
+        assert rc == 0, msg
+        assert guards
+        assert (rw, ks) == (1, 2), (nbr, N, M)
+        ref, env = oracle.gemv_q8_1(fmt, w, N, K, xq, M)
+        linear_check(y, ref, env, K, f"{fmt} N={N} K={K} M={M} split rows")
+
+
+@pytest.mark.parametrize("fmt,N,K,M,rw,ks", [("gguf:q4_k", 14336, 4096, 1, 2, 1), ("gguf:q4_k", 4096, 14336, 1, 1, 2),
+                                             ("gguf:q4_k", 4096, 4096, 8, 2, 1), ("gguf:q6_k", 1024, 4096, 8, 1, 1),
+                                             ("gguf:q8_0", 14336, 4096, 1, 0, 0),
+                                             ("gguf:q6_k", 4096, 14336, 1, 0, 0), ("gguf:q4_0", 1024, 4096, 1, 1, 2),
+                                             ("gguf:iq2_xxs", 14336, 4096, 1, 2, 1),
+                                             ("gguf:iq4_xs", 4096, 14336, 1, 1, 2),
+                                             ("gguf:q4_k", 1024, 4096, 1, 1, 1),
+                                             ("gguf:q4_0", 4096, 4096, 1, 1, 1),
+                                             ("gguf:mxfp4", 2048, 4096, 1, 1, 2)])
+def test_emu_gemv_single_round_plan(fmt, N, K, M, rw, ks):
+    """On a device of 256 compute units holding up to 8 workgroups, 160 KiB
+    of LDS and 32 waves each, the single-round plan takes the fewest rows per
+    chunk whose chunks all fit at once, or, for several activation rows and
+    at least 4096 rows, two rows first; single-row chunks of rows with more
+    than 64 items split each row in two parts first when K >= 8192 or whole
+    rows would give fewer than 16 waves per unit (q4_k and iq4_xs with 14336
+    columns, q4_0 and mxfp4 with 1024 or 2048 rows of 4096), not at [4096,
+    4096]; a q4_k row of 4096 columns (64 items) stays whole.  With one activation row, workgroups hold up to 16 waves
+    (the activation copy in LDS serves them all), as many workgroups per
+    unit as fit; several activation rows take four-wave workgroups.  Weights
+    too large for one round (q8_0 at [14336, 4096]: 62 MB) take the chunk
+    loop."""
+    idx, B, S, _ = oracle.info(fmt)
     p = emu_lib.gemv1_plan(idx, N, K, M)
-    assert p[0] == rw, p
+    assert (p[0], p[4]) == (rw, ks), p
     if rw:
-        row_bytes = K // oracle.info(fmt)[1] * oracle.info(fmt)[2]
-        assert p[1] == 4 * ((15 + rw * row_bytes + 15) // 16 + 1)
-        assert p[2] == 4 * 4 * p[1]
-        assert p[3] == -(-(-(-N // rw)) // 4)
-        assert p[3] <= 256 * min(8, 163840 // p[2])
+        nbr = K // B
+        cb = -(-nbr // ks)
+        assert p[5] == cb
+        chunk_bytes = rw * nbr * S if ks == 1 else cb * S
+        assert p[1] == 4 * ((15 + chunk_bytes + 15) // 16 + 1)
+        nw, act_dw = p[6], p[7]
+        assert act_dw == ((K // 32) * 9 if M == 1 else 0)
+        assert p[2] == 4 * (-(-act_dw // 4) * 4 + nw * p[1])
+        chunks = -(-N // rw) if ks == 1 else N * ks
+        assert 1 <= nw <= 16 and nw % ks == 0
+        assert p[3] == -(-chunks // nw)
+        g = -(-p[3] // 256)  # workgroups per compute unit
+        assert g <= min(8, 163840 // p[2], 32 // nw)
+        # the fewest workgroups per compute unit: with one fewer, a workgroup
+        # would need more than 16 waves or would not fit
+        if M > 1:
+            assert nw == 4
+        else:
+            # the most workgroups per compute unit (the smallest workgroups):
+            # with one more per unit, they would not all fit at once
+            g = max(gg for gg in range(1, 9) if -(-chunks // (256 * gg)) + (-(-chunks // (256 * gg))) % ks == nw)
+            assert nw == -(-chunks // (256 * g)) + (-(-chunks // (256 * g))) % ks
+            for g1 in range(g + 1, 9):
+                nw1 = -(-chunks // (256 * g1))
+                nw1 += nw1 % ks
+                lds1 = 4 * (-(-act_dw // 4) * 4 + nw1 * p[1])
+                assert nw1 > 16 or lds1 > 163840 or min(8, 163840 // lds1, 32 // nw1) < g1
     assert emu_lib.gemv1_plan(idx, N, K, M, w_mis=8)[0] == 0
 
 
