@@ -23,6 +23,8 @@
 // binary32 (the decoded-unit path below remains for formats without one).
 #pragma once
 
+#include <type_traits>
+
 #include "nq_gqenc.h"
 
 namespace nq {
@@ -370,6 +372,72 @@ NQ_HD void kq_scale_min(const uint32_t (&h)[3], uint32_t k, uint32_t *sc, uint32
     *mn = (((b3 >> 4) | ((b2 >> 6) << 4)) & hi) | ((b2 & 63u) & ~hi);
 }
 
+// A single-round wave region whose weight windows start at multiples of AL
+// bytes (4 or 16): the launch's weight bytes start 16-byte aligned and, for
+// the formats of gv_dword_windows, every block and every window the weight
+// reader takes in it sits at a multiple of 4 bytes (of 16 for q4_k and q5_k,
+// whose blocks are multiples of 16 bytes).  Windows are then plain dword
+// loads (16-byte loads for AL = 16) with no byte shifts.
+template <int AL>
+struct LdsSrcAl : LdsSrc {};
+
+template <int F>
+constexpr int gv_dword_windows() {
+    return (F == Q4_K || F == Q5_K) ? 16
+         : (F == Q8_1 || F == Q8_K || F == Q4_1 || F == Q5_1 || F == IQ4_XS || F == NVFP4_GGUF || F == Q2_K) ? 4
+                                                                                                         : 0;
+}
+
+template <class Src>
+struct GvSrcAl {
+    static constexpr int value = 0;
+};
+template <int AL>
+struct GvSrcAl<LdsSrcAl<AL>> {
+    static constexpr int value = AL;
+};
+
+// The single-round kernel's view of a wave region of format F.
+template <int F>
+using Gv1Src = std::conditional_t<(gv_dword_windows<F>() > 0), LdsSrcAl<gv_dword_windows<F>()>, LdsSrc>;
+
+template <class Src>
+NQ_HD Src gv_src(const uint32_t *base, uint32_t last) {
+    Src s;
+    s.base = base;
+    s.last = last;
+    return s;
+}
+
+// ND payload dwords from byte off of the source: window(), or plain loads
+// from an aligned region.
+template <int ND, class Src>
+NQ_HD void gw_window(const Src &s, uint32_t off, uint32_t (&w)[ND]) {
+    constexpr int AL = GvSrcAl<Src>::value;
+    if constexpr (AL > 0) {
+        const uint32_t *p = s.base + (off >> 2);
+#if !defined(__HIP_DEVICE_COMPILE__)
+        if (((uintptr_t)p & (uintptr_t)(AL - 1)) != 0u || (off & 3u) != 0u) __builtin_trap();
+#endif
+        if constexpr (AL == 16 && ND % 4 == 0) {
+            const u32x4 *q = (const u32x4 *)__builtin_assume_aligned(p, 16);
+#pragma unroll
+            for (int k = 0; k < ND / 4; k++) {
+                const u32x4 v = q[k];
+                w[4 * k] = v.x;
+                w[4 * k + 1] = v.y;
+                w[4 * k + 2] = v.z;
+                w[4 * k + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < ND; k++) w[k] = p[k];
+        }
+    } else {
+        window<ND>(s, off, w);
+    }
+}
+
 // Weights of item `part` of the block at LDS byte offset bo.
 template <int F, class Src>
 NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w) {
@@ -377,7 +445,7 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
         // d at 0, 32 signed codes at 2: w = d * q
         w.f[0] = f16(u16_at(s, bo));
         uint32_t q[8];
-        window<8>(s, bo + 2u, q);
+        gw_window<8>(s, bo + 2u, q);
 #pragma unroll
         for (int j = 0; j < 8; j++) w.q[j] = q[j];
     } else if constexpr (F == Q4_0) {
@@ -385,21 +453,21 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
         // the high nibble of byte j - 16; w = d * (v - 8)
         w.f[0] = f16(u16_at(s, bo));
         uint32_t q[4];
-        window<4>(s, bo + 2u, q);
+        gw_window<4>(s, bo + 2u, q);
 #pragma unroll
         for (int j = 0; j < 4; j++) w.q[j] = q[j];
     } else if constexpr (F == Q8_1) {
         // d at 0, the sum at 2 (not used), 32 signed codes at 4: w = d * q
         w.f[0] = f16(u16_at(s, bo));
         uint32_t q[8];
-        window<8>(s, bo + 4u, q);
+        gw_window<8>(s, bo + 4u, q);
 #pragma unroll
         for (int j = 0; j < 8; j++) w.q[j] = q[j];
     } else if constexpr (F == Q8_K) {
         // binary32 d at 0, 256 signed codes at 4 (part p: codes 32p .. 32p+31): w = RN32(d * q)
         uint32_t h[1], q[8];
-        window<1>(s, bo, h);
-        window<8>(s, bo + 4u + 32u * part, q);
+        gw_window<1>(s, bo, h);
+        gw_window<8>(s, bo + 4u + 32u * part, q);
         w.f[0] = bits_f32(h[0]);
 #pragma unroll
         for (int j = 0; j < 8; j++) w.q[j] = q[j];
@@ -414,14 +482,14 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
         if constexpr (F == Q4_1) {
             w.f[0] = f16(u16_at(s, bo));
             w.f[1] = f16(u16_at(s, bo + 2u));
-            window<4>(s, bo + 4u, q);
+            gw_window<4>(s, bo + 4u, q);
         } else if constexpr (F == IQ4_NL) {
             w.f[0] = f16(u16_at(s, bo));
-            window<4>(s, bo + 2u, q);
+            gw_window<4>(s, bo + 2u, q);
         } else {
             const uint32_t e = u8_at(s, bo);
             w.f[0] = bits_f32(e < 2u ? (0x00200000u << e) : ((e - 1u) << 23));
-            window<4>(s, bo + 1u, q);
+            gw_window<4>(s, bo + 1u, q);
         }
 #pragma unroll
         for (int j = 0; j < 4; j++) {
@@ -444,8 +512,8 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
         constexpr uint32_t LO4 = 0x0F0F0F0Fu;
         const uint32_t ho = F == Q5_0 ? 2u : 4u;
         uint32_t hw[1], q[4];
-        window<1>(s, bo + ho, hw);
-        window<4>(s, bo + ho + 4u, q);
+        gw_window<1>(s, bo + ho, hw);
+        gw_window<4>(s, bo + ho + 4u, q);
         w.f[0] = f16(u16_at(s, bo));
         if constexpr (F == Q5_1) w.f[1] = f16(u16_at(s, bo + 2u));
 #pragma unroll
@@ -458,8 +526,8 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
         // w = RN32(d * s_k) * IQ4[v], s_k = scale nibble k + 16 * high bits 2k,2k+1 - 32
         constexpr uint32_t LO4 = 0x0F0F0F0Fu;
         uint32_t hdr[2], q[4];
-        window<2>(s, bo, hdr);
-        window<4>(s, bo + 8u + 16u * part, q);
+        gw_window<2>(s, bo, hdr);
+        gw_window<4>(s, bo + 8u + 16u * part, q);
         const float d = f16(hdr[0] & 0xFFFFu);
         const uint32_t high = hdr[0] >> 16;
         const uint32_t lo = (bytek(hdr[1], part >> 1) >> (4u * (part & 1u))) & 15u;
@@ -474,7 +542,7 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
         // part c: values 32c + i, bits 2(c mod 4) of byte 32(c / 4) + i; d at
         // 64; w = d * (v - 1)
         uint32_t q[8];
-        window<8>(s, bo + 32u * (part >> 2), q);
+        gw_window<8>(s, bo + 32u * (part >> 2), q);
         w.f[0] = f16(u16_at(s, bo + 64u));
 #pragma unroll
         for (int j = 0; j < 8; j++) w.q[j] = (q[j] >> (2u * (part & 3u))) & 0x03030303u;
@@ -491,7 +559,7 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
         // 4 + 8g .. 4 + 8g + 7; w = half-scale(g) * V[v]
         constexpr uint32_t LO4 = 0x0F0F0F0Fu;
         uint32_t q[4];
-        window<4>(s, bo + 4u + 16u * part, q);
+        gw_window<4>(s, bo + 4u + 16u * part, q);
         const uint32_t sb = u16_at(s, bo + 2u * part);
         w.f[0] = nvfp4_half_scale(sb & 0xFFu);
         w.f[1] = nvfp4_half_scale(sb >> 8);
@@ -507,9 +575,9 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
         // half) or 2g+1 (high half) of bytes 16 .. 47
         constexpr uint32_t LO4 = 0x0F0F0F0Fu;
         uint32_t h[4], q[8], qh[8];
-        window<4>(s, bo, h);
-        window<8>(s, bo + 48u + 32u * part, q);
-        window<8>(s, bo + 16u, qh);
+        gw_window<4>(s, bo, h);
+        gw_window<8>(s, bo + 48u + 32u * part, q);
+        gw_window<8>(s, bo + 16u, qh);
         const float d = f16(h[0] & 0xFFFFu), dmin = f16(h[0] >> 16);
         const uint32_t hs[3] = {h[1], h[2], h[3]};
         uint32_t sc0, m0, sc1, m1;
@@ -529,8 +597,8 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
         // sub-block scale bytes 2c, 2c+1 (low nibble: scale, high: min);
         // d at 80, dmin at 82; w = RN32(d * (s mod 16)) * v - RN32(dmin * (s / 16))
         uint32_t q[8], h[1];
-        window<8>(s, bo + 16u + 32u * (part >> 2), q);
-        window<1>(s, bo + 80u, h);
+        gw_window<8>(s, bo + 16u + 32u * (part >> 2), q);
+        gw_window<1>(s, bo + 80u, h);
         const uint32_t sc = u16_at(s, bo + 2u * part);
         const float d = f16(h[0] & 0xFFFFu), dmin = f16(h[0] >> 16);
         w.f[0] = M(d, (float)(sc & 15u));
@@ -545,9 +613,9 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
         // nibble k / 8 of byte 96 + k mod 8, a: bits 2(k / 4) of byte 104 + k
         // mod 4); d at 108; w = RN32(d * s) * (v - 4 (1 - h))
         uint32_t q[8], mk[8], sc[3];
-        window<8>(s, bo + 32u + 32u * (part >> 2), q);
-        window<8>(s, bo, mk);
-        window<3>(s, bo + 96u, sc);
+        gw_window<8>(s, bo + 32u + 32u * (part >> 2), q);
+        gw_window<8>(s, bo, mk);
+        gw_window<3>(s, bo + 96u, sc);
         const float d = f16(u16_at(s, bo + 108u));
 #pragma unroll
         for (int e = 0; e < 2; e++) {
@@ -563,14 +631,14 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
         // part p: values 32p + i, bit i mod 8 of byte 2 + 4p + i / 8; w = +-d (d
         // for a set bit): code 2b - 1
         uint32_t q[1];
-        window<1>(s, bo + 2u + 4u * part, q);
+        gw_window<1>(s, bo + 2u + 4u * part, q);
         w.f[0] = f16(u16_at(s, bo));
 #pragma unroll
         for (int j = 0; j < 8; j++) w.q[j] = bits4(q[0] >> (4 * j));
     } else if constexpr (F == Q2_0) {
         // part p: values 32p + 4t + k, bits 2k of byte 2 + 8p + t; w = d * (v - 1)
         uint32_t q[2];
-        window<2>(s, bo + 2u + 8u * part, q);
+        gw_window<2>(s, bo + 2u + 8u * part, q);
         w.f[0] = f16(u16_at(s, bo));
 #pragma unroll
         for (int j = 0; j < 8; j++) w.q[j] = crumbs4(bytek(q[j >> 2], (uint32_t)(j & 3)));
@@ -585,11 +653,11 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
             // pairs at 2 + 8g, the aux word at 66 + 4g; seven sign bits per unit
             // (+ parity), scale nibble aux >> 28
             uint32_t ix[2], aux[1];
-            window<2>(s, bo + 2u + 8u * g, ix);
+            gw_window<2>(s, bo + 2u + 8u * g, ix);
             if constexpr (F == IQ2_XXS)
                 aux[0] = ix[1];
             else
-                window<1>(s, bo + 66u + 4u * g, aux);
+                gw_window<1>(s, bo + 66u + 4u * g, aux);
             w.f[0] = M(M(d, A(0.5f, (float)(aux[0] >> 28))), F == IQ2_XXS ? 0.25f : 0.5f);
 #pragma unroll
             for (int l = 0; l < 4; l++) {
@@ -618,10 +686,10 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
             uint32_t wd[2], lo[1], sgn[1];
             uint32_t hi = 0;
             if constexpr (F == IQ2_XS) {
-                window<2>(s, bo + 2u + 8u * g, wd);  // four 16-bit words: 9-bit index, 7 sign bits
+                gw_window<2>(s, bo + 2u + 8u * g, wd);  // four 16-bit words: 9-bit index, 7 sign bits
             } else {
-                window<1>(s, bo + 2u + 4u * g, lo);   // four index low bytes
-                window<1>(s, bo + 34u + 4u * g, sgn); // four sign bytes
+                gw_window<1>(s, bo + 2u + 4u * g, lo);   // four index low bytes
+                gw_window<1>(s, bo + 34u + 4u * g, sgn); // four sign bytes
                 hi = u8_at(s, bo + 66u + g);          // four 2-bit index high parts
             }
 #pragma unroll
@@ -647,8 +715,8 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
             // bytes at 74 + 4g, scale nibble g mod 2 of byte 106 + g / 2:
             // c = RN32(d * (1 + 2 t))
             uint32_t ix[2], sgn[1];
-            window<2>(s, bo + 2u + 8u * g, ix);
-            window<1>(s, bo + 74u + 4u * g, sgn);
+            gw_window<2>(s, bo + 2u + 8u * g, ix);
+            gw_window<1>(s, bo + 74u + 4u * g, sgn);
             const uint32_t h = u8_at(s, bo + 66u + g);
             const uint32_t sc = u8_at(s, bo + 106u + (g >> 1));
             w.f[0] = M(d, (float)(1u + 2u * ((sc >> (4u * (g & 1u))) & 15u)));
@@ -668,7 +736,7 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
             // bits per unit, scale bits 12-14, delta sign bit 15); grid bytes
             // hold value + 1; w = RN32(d * (2 t + 1)) * (v + delta)
             uint32_t ix[1];
-            window<1>(s, bo + 2u + 4u * g, ix);
+            gw_window<1>(s, bo + 2u + 4u * g, ix);
             const uint32_t a = u16_at(s, bo + 34u + 2u * g);
             w.f[0] = M(d, (float)(2u * ((a >> 12) & 7u) + 1u));
             w.f[1] = (a & 0x8000u) ? -0.125f : 0.125f;
@@ -683,9 +751,9 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
             // 3 index bits, delta sign bit 3), scale words at 48 (3 bits per
             // pair of units; the binary16 d in their top nibbles)
             uint32_t ix[1], hw[1], sw[2];
-            window<1>(s, bo + 4u * g, ix);
-            window<1>(s, bo + 32u + 2u * g, hw);  // the unit nibbles of this group (low 16 bits)
-            window<2>(s, bo + 48u, sw);
+            gw_window<1>(s, bo + 4u * g, ix);
+            gw_window<1>(s, bo + 32u + 2u * g, hw);  // the unit nibbles of this group (low 16 bits)
+            gw_window<2>(s, bo + 48u, sw);
             const uint32_t dbits = ((sw[0] & 0xFFFFu) >> 12) | ((sw[0] >> 28) << 4) | (((sw[1] & 0xFFFFu) >> 12) << 8) |
                                    ((sw[1] >> 28) << 12);
             const float dm = f16(dbits);
@@ -710,8 +778,8 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
         // (sub-block 2g+1) nibbles of bytes 16 + 32g .. 16 + 32g + 31;
         // w = RN32(d * sc) * v - RN32(dmin * m)
         uint32_t h[4], q[8];
-        window<4>(s, bo, h);
-        window<8>(s, bo + 16u + 32u * part, q);
+        gw_window<4>(s, bo, h);
+        gw_window<8>(s, bo + 16u + 32u * part, q);
         const float d = f16(h[0] & 0xFFFFu), dmin = f16(h[0] >> 16);
         const uint32_t hs[3] = {h[1], h[2], h[3]};
         uint32_t sc0, m0, sc1, m1;
@@ -731,9 +799,9 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
         constexpr uint32_t LO4 = 0x0F0F0F0Fu;
         const uint32_t hh = part >> 1, c0 = part & 1u;
         uint32_t ql[8], qh[8], sw[2];
-        window<8>(s, bo + 64u * hh + 32u * c0, ql);
-        window<8>(s, bo + 128u + 32u * hh, qh);
-        window<2>(s, bo + 192u + 8u * hh + 2u * c0, sw);
+        gw_window<8>(s, bo + 64u * hh + 32u * c0, ql);
+        gw_window<8>(s, bo + 128u + 32u * hh, qh);
+        gw_window<2>(s, bo + 192u + 8u * hh + 2u * c0, sw);
         const float d = f16(u16_at(s, bo + 208u));
 #pragma unroll
         for (int e = 0; e < 2; e++) {
@@ -999,8 +1067,8 @@ NQ_HD void gv_put(const GvChunk &c, uint32_t wlast, uint32_t lane, const uint32_
 // A lane's positions of a staged chunk (items lane, lane + 64, ... of one
 // row's blocks c0..c0+nb-1): per position the weights of each of the chunk's
 // rows, then per activation row its columns, used by every row.
-template <int F, int MT, int RW, class Act>
-NQ_HD void gv_chunk_items(const LdsSrc &s, const GvChunk &c, uint32_t lane, uint32_t nm, uint32_t row_bytes,
+template <int F, int MT, int RW, class Act, class Src>
+NQ_HD void gv_chunk_items(const Src &s, const GvChunk &c, uint32_t lane, uint32_t nm, uint32_t row_bytes,
                           const Act &act, const Tab &tab, float (&acc)[RW][MT]) {
     constexpr uint32_t IPB = GvItem<F>::IPB, S = (uint32_t)block_bytes(F);
     const uint32_t n = c.nb * IPB;
@@ -1117,8 +1185,8 @@ __global__ __launch_bounds__(WG) void k_gemv(GvArgs a) {
 // lane + 64, ... of the chunk (n items per row), each item's activation
 // columns read once and used for every row of the chunk.  Each row's
 // partial takes the items in the same order as gv_chunk_items.
-template <int F, int RW, class Act>
-NQ_HD void gv1_items1(const LdsSrc &ls, const GvChunk &c, uint32_t lane, uint32_t row_bytes, uint32_t n,
+template <int F, int RW, class Act, class Src>
+NQ_HD void gv1_items1(const Src &ls, const GvChunk &c, uint32_t lane, uint32_t row_bytes, uint32_t n,
                       const Act &act, const Tab &tab, float (&acc)[RW][1]) {
     constexpr uint32_t IPB = GvItem<F>::IPB, S = (uint32_t)block_bytes(F);
     for (uint32_t i = lane; i < n; i += 64u) {
@@ -1310,7 +1378,7 @@ __global__ __launch_bounds__(64 * GV1_MAX_WAVES) void k_gemv1(GvArgs a, uint32_t
         __builtin_amdgcn_s_waitcnt(gv_vm_imm(0u));  // the chunk's loads to LDS have landed
         wave_lds_sync();                             // and the shifted last group's stores
         const Tab tab{t8, t4, nullptr, nullptr, 0xFFFFFFFFu, 1u};
-        const LdsSrc ls{lds, 4u * (c.g1 - c.g0) + 3u};
+        const Gv1Src<F> ls = gv_src<Gv1Src<F>>(lds, 4u * (c.g1 - c.g0) + 3u);
         if constexpr (MT == 1)
             gv1_items1<F, RW>(ls, c, lane, a.row_bytes, c.nb * GvItem<F>::IPB, GvActRaw{gv_lds, a.kb}, tab, acc);
         else

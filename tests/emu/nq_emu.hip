@@ -534,7 +534,7 @@ long run_gemv1(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint
                 if (memcmp(cb, pb, (size_t)c.nb * S) != 0 && chk.errors++ == 0)
                     snprintf(chk.msg, sizeof chk.msg, "staged chunk of row %u differs from the payload", c.r + rr);
             }
-            const LdsSrc ls{lds.data(), 4u * (c.g1 - c.g0) + 3u};
+            const Gv1Src<F> ls = gv_src<Gv1Src<F>>(lds.data(), 4u * (c.g1 - c.g0) + 3u);
             const uint32_t n = c.nb * IPB;
             static float acc[64][RW][MT];
             for (uint32_t lane = 0; lane < 64u; lane++) {
