@@ -1203,25 +1203,41 @@ NQ_HD void gv1_items1(const Src &ls, const GvChunk &c, uint32_t lane, uint32_t r
     }
 }
 
-// The activation as the single-round kernel holds it in LDS: the rows' q8_1
-// blocks exactly as in memory (9 dwords each: the scale and sum half-words,
-// then 32 codes), row m's block ab at dword 9 * (m * kb + ab); the exact
-// code sum is formed from the codes.
+// The activation row as the single-round kernel holds it in LDS: its kb
+// q8_1 blocks as in memory (9 dwords each; block ab at dword 9 * ab), except
+// that the workgroup (gv1_act_prep) replaces each block's binary16 sum
+// half-word, which the product does not use, with the exact sum of its
+// codes (|sum| <= 32 * 127, a signed 16-bit value).
 struct GvActRaw {
     const uint32_t *lds;
-    uint32_t kb;
-    NQ_HD float block(uint32_t m, uint32_t ab, uint32_t (&c)[8], int *S) const {
-        const uint32_t *p = lds + 9u * (m * kb + ab);
-        int s = 0;
+    NQ_HD float block(uint32_t, uint32_t ab, uint32_t (&c)[8], int *S) const {
+        const uint32_t *p = lds + 9u * ab;
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            c[j] = p[1 + j];
-            s = dot4(ONES8, c[j], s);
-        }
-        *S = s;
+        for (int j = 0; j < 8; j++) c[j] = p[1 + j];
+        *S = (int)(int16_t)(uint16_t)(p[0] >> 16);
         return f16(p[0] & 0xFFFFu);
     }
 };
+
+// Formats whose product uses the activation blocks' code sums (gv_dot: a
+// min, offset or delta term); the others skip gv1_act_prep.
+template <int F>
+constexpr bool gv_uses_sum() {
+    return F == Q4_0 || F == Q4_1 || F == Q5_0 || F == Q5_1 || F == Q2_K || F == Q3_K || F == Q4_K ||
+           F == Q5_K || F == Q6_K || F == TQ1_0 || F == TQ2_0 || F == Q1_0 || F == Q2_0 || F == IQ1_S;
+}
+
+// The exact code sums of the staged activation blocks t, t + nt, ... (thread
+// t of nt), written over their sum half-words.
+NQ_HD void gv1_act_prep(uint32_t *lds, uint32_t kb, uint32_t t, uint32_t nt) {
+    for (uint32_t ab = t; ab < kb; ab += nt) {
+        uint32_t *p = lds + 9u * ab;
+        int s = 0;
+#pragma unroll
+        for (int j = 0; j < 8; j++) s = dot4(ONES8, p[1 + j], s);
+        p[0] = (p[0] & 0xFFFFu) | ((uint32_t)s << 16);
+    }
+}
 
 // Waves per single-round workgroup at most (the hardware's 1024 threads).
 constexpr uint32_t GV1_MAX_WAVES = 16u;
@@ -1230,6 +1246,9 @@ constexpr uint32_t GV1_MAX_WAVES = 16u;
 // (vmcnt in bits 3:0 and 15:14; the export and LDS counters left at their
 // maxima, so they are not waited for).
 constexpr uint32_t gv_vm_imm(uint32_t n) { return (n & 15u) | (7u << 4) | (15u << 8) | ((n >> 4) << 14); }
+// s_waitcnt immediate for "no LDS access of this wave outstanding" (the
+// memory and export counters at their maxima).
+constexpr uint32_t GV_LGKM0_IMM = 15u | (7u << 4) | (0u << 8) | (3u << 14);
 
 // Waits until at most x of the wave's memory loads are outstanding, with x
 // rounded down to one of a few counts (waiting for fewer is always safe).
@@ -1368,6 +1387,14 @@ __global__ __launch_bounds__(64 * GV1_MAX_WAVES) void k_gemv1(GvArgs a, uint32_t
     gv_wait_vm(issued);  // this wave's phase-1 loads have landed
     __builtin_amdgcn_s_barrier();  // and every wave's
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (MT == 1 && gv_uses_sum<F>()) {
+        // the activation blocks' code sums, once per workgroup, while the
+        // chunks are still in flight
+        gv1_act_prep(gv_lds, a.kb, threadIdx.x, blockDim.x);
+        __builtin_amdgcn_s_waitcnt(GV_LGKM0_IMM);  // the LDS stores are done
+        __builtin_amdgcn_s_barrier();              // every wave's
+        __builtin_amdgcn_sched_barrier(0);
+    }
     if (KS == 1 && !live) return;  // no workgroup barrier follows
     float acc[RW][MT];
 #pragma unroll
@@ -1380,7 +1407,7 @@ __global__ __launch_bounds__(64 * GV1_MAX_WAVES) void k_gemv1(GvArgs a, uint32_t
         const Tab tab{t8, t4, nullptr, nullptr, 0xFFFFFFFFu, 1u};
         const Gv1Src<F> ls = gv_src<Gv1Src<F>>(lds, 4u * (c.g1 - c.g0) + 3u);
         if constexpr (MT == 1)
-            gv1_items1<F, RW>(ls, c, lane, a.row_bytes, c.nb * GvItem<F>::IPB, GvActRaw{gv_lds, a.kb}, tab, acc);
+            gv1_items1<F, RW>(ls, c, lane, a.row_bytes, c.nb * GvItem<F>::IPB, GvActRaw{gv_lds}, tab, acc);
         else
             gv_chunk_items<F, MT, RW>(ls, c, lane, a.M, a.row_bytes, GvAct<false>{a.xq, nullptr, a.K, a.kb, a.xrow, a.M},
                                       tab, acc);

@@ -430,7 +430,8 @@ bool gv1_stage_cover(uint32_t ng, uint32_t nw, std::vector<uint32_t> &hits) {
 // The single-round product kernel (k_gemv1) for a plan the launcher made.
 // Per workgroup of p.nw waves: phase 1, the activation blocks (one
 // activation row; several are read from global memory) and codebook tables
-// moved into LDS as gv1_stage spreads them (coverage checked), then
+// moved into LDS as gv1_stage spreads them (coverage checked) and the
+// activation blocks' code sums formed by the threads, then
 // every wave's one chunk (p.rw whole rows, or part h of a row split in KS
 // parts of p.cb blocks), staged as the kernel stages it (the 16-byte loads
 // to LDS of groups g0 .. g1, each at a 16-byte aligned address and inside
@@ -479,9 +480,11 @@ long run_gemv1(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, uint
         snprintf(err, errlen, "activation staging does not cover every group once");
         return 1;
     }
-    std::vector<uint32_t> act_lds(p.act_dw + 1u);
+    std::vector<uint32_t> act_lds(gv1_act_region(p.act_dw) + 1u);
     memcpy(act_lds.data(), xq, 4u * (size_t)p.act_dw);
-    const GvActRaw act{act_lds.data(), a.kb};                          // one activation row: from LDS
+    if (p.act_dw > 0u && gv_uses_sum<F>())  // the workgroup's threads form the code sums
+        for (uint32_t t = 0; t < 64u * p.nw; t++) gv1_act_prep(act_lds.data(), a.kb, t, 64u * p.nw);
+    const GvActRaw act{act_lds.data()};                          // one activation row: from LDS
     const GvAct<false> gact{a.xq, nullptr, a.K, a.kb, a.xrow, a.M};  // several: from global memory
     Check chk{(uintptr_t)w, (uintptr_t)(w + N * a.row_bytes), 0, {0}};
     const HostSrc src{a.wbase, a.wlast, &chk};

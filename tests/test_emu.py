@@ -480,7 +480,8 @@ def test_emu_gemv_single_round_plan(fmt, N, K, M, rw, ks):
         assert p[1] == 4 * ((15 + chunk_bytes + 15) // 16 + 1)
         nw, act_dw = p[6], p[7]
         assert act_dw == ((K // 32) * 9 if M == 1 else 0)
-        assert p[2] == 4 * (-(-act_dw // 4) * 4 + nw * p[1])
+        act_region = -(-act_dw // 4) * 4
+        assert p[2] == 4 * (act_region + nw * p[1])
         chunks = -(-N // rw) if ks == 1 else N * ks
         assert 1 <= nw <= 16 and nw % ks == 0
         assert p[3] == -(-chunks // nw)
@@ -498,7 +499,7 @@ def test_emu_gemv_single_round_plan(fmt, N, K, M, rw, ks):
             for g1 in range(g + 1, 9):
                 nw1 = -(-chunks // (256 * g1))
                 nw1 += nw1 % ks
-                lds1 = 4 * (-(-act_dw // 4) * 4 + nw1 * p[1])
+                lds1 = 4 * (act_region + nw1 * p[1])
                 assert nw1 > 16 or lds1 > 163840 or min(8, 163840 // lds1, 32 // nw1) < g1
     assert emu_lib.gemv1_plan(idx, N, K, M, w_mis=8)[0] == 0
 
