@@ -372,6 +372,21 @@ NQ_HD void kq_scale_min(const uint32_t (&h)[3], uint32_t k, uint32_t *sc, uint32
     *mn = (((b3 >> 4) | ((b2 >> 6) << 4)) & hi) | ((b2 & 63u) & ~hi);
 }
 
+// The sub-scales and mins of the pair of sub-blocks 2g, 2g + 1 (g < 4), as
+// the bytes [sc(2g), sc(2g+1), m(2g), m(2g+1)] of one word, by byte selects:
+// with j = 2g mod 4, A = [b1[j], b1[j+1], b2[j], b2[j+1]] gives the pair for
+// g < 2 (6 low bits); for g >= 2 the low 4 bits come from b3[j], b3[j+1]
+// (low nibbles for the scales, high for the mins) and bits 4-5 are bits 6-7
+// of A's bytes.  Same values as kq_scale_min for k = 2g and 2g + 1.
+NQ_HD uint32_t kq_scale_min_pair(const uint32_t (&h)[3], uint32_t g) {
+    const uint32_t j = (2u * g) & 3u;
+    const uint32_t sa = 0x05040100u + j * 0x01010101u;
+    const uint32_t A = perm(h[1], h[0], sa);
+    const uint32_t B = perm(h[2], h[2], sa - 0x04040000u);
+    const uint32_t hi = (B & 0x00000F0Fu) | ((B >> 4) & 0x0F0F0000u) | ((A >> 2) & 0x30303030u);
+    return g < 2u ? A & 0x3F3F3F3Fu : hi;
+}
+
 // A single-round wave region whose weight windows start at multiples of AL
 // bytes (4 or 16): the launch's weight bytes start 16-byte aligned and, for
 // the formats of gv_dword_windows, every block and every window the weight
@@ -580,13 +595,11 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
         gw_window<8>(s, bo + 16u, qh);
         const float d = f16(h[0] & 0xFFFFu), dmin = f16(h[0] >> 16);
         const uint32_t hs[3] = {h[1], h[2], h[3]};
-        uint32_t sc0, m0, sc1, m1;
-        kq_scale_min(hs, 2u * part, &sc0, &m0);
-        kq_scale_min(hs, 2u * part + 1u, &sc1, &m1);
-        w.f[0] = M(d, (float)sc0);
-        w.f[1] = M(dmin, (float)m0);
-        w.f[2] = M(d, (float)sc1);
-        w.f[3] = M(dmin, (float)m1);
+        const uint32_t sm = kq_scale_min_pair(hs, part);
+        w.f[0] = M(d, (float)bytek(sm, 0u));
+        w.f[1] = M(dmin, (float)bytek(sm, 2u));
+        w.f[2] = M(d, (float)bytek(sm, 1u));
+        w.f[3] = M(dmin, (float)bytek(sm, 3u));
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             w.q[j] = (q[j] & LO4) | (((qh[j] >> (2u * part)) & 0x01010101u) << 4);
@@ -782,13 +795,11 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
         gw_window<8>(s, bo + 16u + 32u * part, q);
         const float d = f16(h[0] & 0xFFFFu), dmin = f16(h[0] >> 16);
         const uint32_t hs[3] = {h[1], h[2], h[3]};
-        uint32_t sc0, m0, sc1, m1;
-        kq_scale_min(hs, 2u * part, &sc0, &m0);
-        kq_scale_min(hs, 2u * part + 1u, &sc1, &m1);
-        w.f[0] = M(d, (float)sc0);
-        w.f[1] = M(dmin, (float)m0);
-        w.f[2] = M(d, (float)sc1);
-        w.f[3] = M(dmin, (float)m1);
+        const uint32_t sm = kq_scale_min_pair(hs, part);
+        w.f[0] = M(d, (float)bytek(sm, 0u));
+        w.f[1] = M(dmin, (float)bytek(sm, 2u));
+        w.f[2] = M(d, (float)bytek(sm, 1u));
+        w.f[3] = M(dmin, (float)bytek(sm, 3u));
 #pragma unroll
         for (int j = 0; j < 8; j++) w.q[j] = q[j];
     } else if constexpr (F == Q6_K) {
