@@ -1141,6 +1141,14 @@ extern "C" __attribute__((visibility("default"))) uint32_t nq_emu_f8_div(uint32_
     nq::div_magic(d, &m, &sh);
     return (uint32_t)(((uint64_t)n * m) >> sh);
 }
+// The K-quant sub-scale and min pair of a 64-value product item (g < 4)
+// from the 12 packed scale bytes h[0..2], as the word [sc(2g), sc(2g+1),
+// m(2g), m(2g+1)].
+extern "C" __attribute__((visibility("default"))) uint32_t nq_emu_kq_scale_min_pair(uint32_t h0, uint32_t h1,
+                                                                                   uint32_t h2, uint32_t g) {
+    const uint32_t h[3] = {h0, h1, h2};
+    return nq::kq_scale_min_pair(h, g);
+}
 namespace {
 
 // Source reader of the encoder emulation: element reads and 16-byte reads,

@@ -94,6 +94,8 @@ def lib():
                                             ctypes.c_char_p, ctypes.c_int]
         L.nq_emu_grouped_absmax.restype = ctypes.c_long
         L.nq_emu_f8_div.restype = ctypes.c_uint32
+        L.nq_emu_kq_scale_min_pair.argtypes = [ctypes.c_uint32] * 4
+        L.nq_emu_kq_scale_min_pair.restype = ctypes.c_uint32
         L.nq_emu_choose_upt.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint32]
         L.nq_emu_choose_upt.restype = ctypes.c_int
         L.nq_emu_tile_blocks.restype = ctypes.c_long
@@ -234,6 +236,15 @@ def decode_fp8_row(kind, payload, N, K, dtype, mis=0, out_mis=0, chunk=0):
 def f8_div(n, d):
     """The FP8 row kernels' multiply-shift division floor(n / d)."""
     return lib().nq_emu_f8_div(n, d)
+
+
+def kq_scale_min_pair(scales12, g):
+    """The product's sub-scale and min pair of 64-value item g (< 4) of a
+    K-quant block from its 12 packed scale bytes: (sc(2g), sc(2g+1), m(2g),
+    m(2g+1))."""
+    h = np.frombuffer(bytes(scales12), dtype="<u4")
+    w = lib().nq_emu_kq_scale_min_pair(int(h[0]), int(h[1]), int(h[2]), g)
+    return tuple((w >> (8 * k)) & 0xFF for k in range(4))
 
 
 def grouped_absmax(scheme_id, G, x, in_code, x_mis=0, codes_mis=0):

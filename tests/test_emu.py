@@ -504,6 +504,33 @@ def test_emu_gemv_single_round_plan(fmt, N, K, M, rw, ks):
     assert emu_lib.gemv1_plan(idx, N, K, M, w_mis=8)[0] == 0
 
 
+def _kquant_scale_min(q, j):
+    """Sub-block j's 6-bit scale and min from the 12 packed bytes of a q4_k /
+    q5_k block (DequantizePacked, "Mathematical decoding rules", Q4_K): for j
+    < 4 the low 6 bits of bytes j and j + 4; otherwise the low nibble (scale)
+    or high nibble (min) of byte j + 4 with the top two bits of byte j - 4
+    (scale) or j (min) above it."""
+    if j < 4:
+        return q[j] & 63, q[j + 4] & 63
+    return (q[j + 4] & 15) | ((q[j - 4] >> 6) << 4), (q[j + 4] >> 4) | ((q[j] >> 6) << 4)
+
+
+def test_emu_kq_scale_min_pair():
+    """The product's byte-select rule for the scale and min pair of a 64-value
+    item equals the per-sub-block rule, on random scale fields and on fields
+    with every bit set or clear (both halves of each byte, both item pairs
+    per half)."""
+    rng = np.random.default_rng(0x5C41E)
+    fields = [rng.integers(0, 256, 12, dtype=np.uint8) for _ in range(3000)]
+    fields += [np.full(12, v, np.uint8) for v in (0x00, 0xFF, 0xC0, 0x3F, 0x0F, 0xF0, 0x55, 0xAA)]
+    for q in fields:
+        q = [int(v) for v in q]
+        for g in range(4):
+            s0, m0 = _kquant_scale_min(q, 2 * g)
+            s1, m1 = _kquant_scale_min(q, 2 * g + 1)
+            assert emu_lib.kq_scale_min_pair(bytes(q), g) == (s0, s1, m0, m1), (q, g)
+
+
 def test_emu_gemv_rejects_nvfp4_with_divisor():
     y, rc, _, _ = emu_lib.gemv_q8_1(nq.format_query("nvfp4").id, np.zeros(40, np.uint8), 1, 64,
                                     np.zeros(72, np.uint8), 1)
