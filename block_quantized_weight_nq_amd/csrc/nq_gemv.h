@@ -968,13 +968,17 @@ NQ_HD float gv_dot(const GvW &w, const GvA &x, float acc) {
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             if constexpr (F == Q4_K) {
+                // high nibbles as the signed bytes (q & 0xF0) ^ 0x80 = 16 v - 128
+                // (one 3-input bitwise instruction): the dot product D with
+                // the second block's codes is 16 I1 - 128 S1, S1 their sum
                 I0 = dot4(w.q[j] & LO4, x.c[j], I0);
-                I1 = dot4((w.q[j] >> 4) & LO4, x.c[8 + j], I1);
+                I1 = dot4((w.q[j] & 0xF0F0F0F0u) ^ 0x80808080u, x.c[8 + j], I1);
             } else {
                 I0 = dot4(w.q[j], x.c[j], I0);
                 I1 = dot4(w.q[8 + j], x.c[8 + j], I1);
             }
         }
+        if constexpr (F == Q4_K) I1 = (I1 + x.S[1] * 128) >> 4;  // exact: D + 128 S1 = 16 I1
         acc = __builtin_fmaf(w.f[0] * (float)I0 - w.f[1] * (float)x.S[0], x.d[0], acc);
         return __builtin_fmaf(w.f[2] * (float)I1 - w.f[3] * (float)x.S[1], x.d[1], acc);
     } else if constexpr (F == Q6_K) {
