@@ -228,12 +228,9 @@ NQ_HD void gm_span(const Src &s, uint32_t bo, uint32_t p, const Tab &tab, GmSpan
             for (int j = 0; j < 8; j++) o.c[j] = bsub(w.q[j], 0x01010101u);
             o.ws[0] = o.ws[1] = w.f[0];
         } else if constexpr (F == Q4_0) {
-            // codes v - 8 (the low nibbles first, then the high)
+            // codes v - 8 (the item's words: the low nibbles, then the high)
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                o.c[j] = bsub(w.q[j] & LO4, 0x08080808u);
-                o.c[4 + j] = bsub((w.q[j] >> 4) & LO4, 0x08080808u);
-            }
+            for (int j = 0; j < 8; j++) o.c[j] = bsub(w.q[j], 0x08080808u);
             o.ws[0] = o.ws[1] = w.f[0];
         } else if constexpr (F == Q4_1 || F == Q5_1) {
             // w = d * v + m

@@ -465,12 +465,18 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
         for (int j = 0; j < 8; j++) w.q[j] = q[j];
     } else if constexpr (F == Q4_0) {
         // d at 0, 16 bytes at 2: value j < 16 the low nibble of byte j, j >= 16
-        // the high nibble of byte j - 16; w = d * (v - 8)
+        // the high nibble of byte j - 16; w = d * (v - 8).  The nibbles are
+        // split here, once per item (words 0-3 low, 4-7 high), not per
+        // activation row.
+        constexpr uint32_t LO4 = 0x0F0F0F0Fu;
         w.f[0] = f16(u16_at(s, bo));
         uint32_t q[4];
         gw_window<4>(s, bo + 2u, q);
 #pragma unroll
-        for (int j = 0; j < 4; j++) w.q[j] = q[j];
+        for (int j = 0; j < 4; j++) {
+            w.q[j] = q[j] & LO4;
+            w.q[4 + j] = (q[j] >> 4) & LO4;
+        }
     } else if constexpr (F == Q8_1) {
         // d at 0, the sum at 2 (not used), 32 signed codes at 4: w = d * q
         w.f[0] = f16(u16_at(s, bo));
@@ -800,6 +806,9 @@ NQ_HD void gv_w(const Src &s, uint32_t bo, uint32_t part, const Tab &tab, GvW &w
         w.f[1] = M(dmin, (float)bytek(sm, 2u));
         w.f[2] = M(d, (float)bytek(sm, 1u));
         w.f[3] = M(dmin, (float)bytek(sm, 3u));
+        // the code bytes as they are (gv_dot splits the nibbles: holding
+        // both halves here took the two-row kernels with several activation
+        // rows from 65 to 81 registers)
 #pragma unroll
         for (int j = 0; j < 8; j++) w.q[j] = q[j];
     } else if constexpr (F == Q6_K) {
@@ -959,8 +968,8 @@ NQ_HD float gv_dot(const GvW &w, const GvA &x, float acc) {
         int I = 0;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            I = dot4(w.q[j] & LO4, x.c[j], I);
-            I = dot4((w.q[j] >> 4) & LO4, x.c[4 + j], I);
+            I = dot4(w.q[j], x.c[j], I);
+            I = dot4(w.q[4 + j], x.c[4 + j], I);
         }
         return __builtin_fmaf(w.f[0] * (float)(I - 8 * x.S[0]), x.d[0], acc);
     } else if constexpr (F == Q4_K || F == Q5_K) {
