@@ -55,6 +55,14 @@ constexpr uint32_t GM_BN = 128;            // weight rows per tile
 constexpr uint32_t GM_BM = 64;             // activation rows per tile (32 for batches of at most 32 rows)
 constexpr uint32_t GM_SP = 8;              // spans per K step (256 values; 4 on large grids, gm_plan)
 constexpr uint64_t GM_MAX_MROWS = 1ull << 16;  // activation rows per launch
+
+// Activation rows per launch for K columns: at most GM_MAX_MROWS, and few
+// enough that byte offsets into the launch's q8_1 rows (K / 32 * 36 bytes
+// each) fit 32 bits.
+inline uint64_t gm_max_mrows(uint64_t K) {
+    const uint64_t by_bytes = (1ull << 32) / (K / 32u * 36u);
+    return by_bytes < GM_MAX_MROWS ? by_bytes : GM_MAX_MROWS;
+}
 constexpr uint64_t GM_MIN_M = 5;  // fewer activation rows take the single-row kernel (faster there)
 #ifndef NQ_GM_REWRITE_M
 #define NQ_GM_REWRITE_M 256
@@ -352,15 +360,17 @@ NQ_HD void gm_stage_wc(const GmArgs &a, uint32_t n0, uint32_t t0, uint32_t tid, 
         const uint32_t i = tid + (uint32_t)WG * r, n = i / G::SP, t = t0 + i % G::SP;
         ok[r] = n0 + n < a.rows && t < a.kspans;
         const uint32_t nn = ok[r] ? n0 + n : 0u, tt = ok[r] ? t : 0u;
-        const uint32_t *p = a.cw + (uint64_t)nn * a.kspans * 8u + (uint64_t)tt * 8u;
+        // 32-bit byte offsets: a launch's codes and scales each span fewer
+        // than 2^32 bytes (gm_max_rows, launch_gemm_mfma)
+        const uint32_t *p = (const uint32_t *)((const uint8_t *)a.cw + (nn * a.kspans + tt) * 32u);
         const u32x4 v0 = *(const u32x4 *)p, v1 = *(const u32x4 *)(p + 4);
         c[r][0] = v0.x; c[r][1] = v0.y; c[r][2] = v0.z; c[r][3] = v0.w;
         c[r][4] = v1.x; c[r][5] = v1.y; c[r][6] = v1.z; c[r][7] = v1.w;
 #pragma unroll
         for (uint32_t h = 0; h < G::NH; h++) {
-            const uint64_t k = ((uint64_t)tt * G::NH + h) * a.ldy + nn;
-            sw[r][h] = a.cs[k];
-            so[r][h] = G::AFF ? a.co[k] : 0.0f;
+            const uint32_t kb = ((tt * G::NH + h) * a.ldy + nn) * 4u;
+            sw[r][h] = *(const float *)((const uint8_t *)a.cs + kb);
+            so[r][h] = G::AFF ? *(const float *)((const uint8_t *)a.co + kb) : 0.0f;
         }
     }
     float *ws = (float *)(lds + G::WS), *ow = (float *)(lds + G::WO);
@@ -420,7 +430,10 @@ NQ_HD void gm_stage_x(const GmArgs &a, uint32_t m0, uint32_t t0, uint32_t tid, u
     for (uint32_t r = 0; r < R; r++) {
         const uint32_t i = tid + (uint32_t)WG * r, m = i / G::SP, t = t0 + i % G::SP;
         ok[r] = i < G::BM * G::SP && m0 + m < a.M && t < a.kspans;
-        const uint32_t *p = a.xq + (ok[r] ? (uint64_t)(m0 + m) * a.xrow + (uint64_t)t * 9u : 0ull);
+        // a 32-bit byte offset: a launch's activation rows span fewer than
+        // 2^32 bytes (gm_max_mrows)
+        const uint32_t *p = (const uint32_t *)((const uint8_t *)a.xq +
+                                               (ok[r] ? ((m0 + m) * a.xrow + t * 9u) * 4u : 0u));
         const u32x4a4 v0 = *(const u32x4a4 *)(p + 1), v1 = *(const u32x4a4 *)(p + 5);
         c[r][0] = v0.x; c[r][1] = v0.y; c[r][2] = v0.z; c[r][3] = v0.w;
         c[r][4] = v1.x; c[r][5] = v1.y; c[r][6] = v1.z; c[r][7] = v1.w;
@@ -814,11 +827,14 @@ GmArgs gm_args(const GvLaunch &L, uint64_t r0, uint64_t rows, uint64_t m0, uint6
 
 inline uint32_t gm_grid(const GmArgs &a) { return 8u * a.xq8 + a.xr8; }
 
-// Weight rows per launch: byte offsets fit 32 bits, whole tiles when more
-// than one, and at most 2^24 rows (the grid stays below 2^31).
+// Weight rows per launch: byte offsets fit 32 bits, and so do the byte
+// offsets of the rewritten codes (K per row), whole tiles when more than
+// one, and at most 2^24 rows (the grid stays below 2^31).
 template <int F>
 uint64_t gm_max_rows(const GvLaunch &L) {
     uint64_t r = gv_max_rows<F>(L);
+    const uint64_t by_codes = (1ull << 32) / L.K;
+    if (r > by_codes) r = by_codes;
     if (r > (1ull << 24)) r = 1ull << 24;
     return r >= GM_BN ? r / GM_BN * GM_BN : r;
 }
@@ -830,8 +846,9 @@ template <int F>
 int launch_gemm_mfma(const GvLaunch &L, void *ws, uint64_t ws_bytes, hipStream_t stream) {
     const uint64_t max_rows = gm_max_rows<F>(L);
     GmPlan p = gm_plan(F, L.N, L.K, L.M, L.cus);
+    // (the rewritten scales, K / 32 * NH * N words, take 32-bit byte offsets)
     const bool use = ws != nullptr && ws_bytes >= gm_ws_layout(F, p, L.N, L.K, L.M).total &&
-                     (p.nsplit > 1 || p.rewrite_once);
+                     (p.nsplit > 1 || p.rewrite_once) && (L.K / 32u) * 2u * L.N * 4u < (1ull << 32);
     if (!use) p = gm_plan_plain(p, L.K);
     const GmWsLayout wl = gm_ws_layout(F, p, L.N, L.K, L.M);
     const bool split = p.nsplit > 1;
@@ -849,8 +866,9 @@ int launch_gemm_mfma(const GvLaunch &L, void *ws, uint64_t ws_bytes, hipStream_t
             r0 += rows;
         }
     }
-    for (uint64_t m0 = 0; m0 < L.M; m0 += GM_MAX_MROWS) {
-        const uint64_t mrows = L.M - m0 < GM_MAX_MROWS ? L.M - m0 : GM_MAX_MROWS;
+    const uint64_t max_mrows = gm_max_mrows(L.K);
+    for (uint64_t m0 = 0; m0 < L.M; m0 += max_mrows) {
+        const uint64_t mrows = L.M - m0 < max_mrows ? L.M - m0 : max_mrows;
         for (uint64_t r0 = 0; r0 < L.N;) {
             const uint64_t rows = L.N - r0 < max_rows ? L.N - r0 : max_rows;
             const GmArgs a = gm_args<F>(L, r0, rows, m0, mrows, p, out, canon, &wl);

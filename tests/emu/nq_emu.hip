@@ -674,7 +674,7 @@ long run_gemm_sh(const uint8_t *w, uint64_t N, uint64_t K, const uint8_t *xq, ui
     using G = GmFmt<F, Sh::BM, SP>;
     const GvLaunch L{w, N, K, M, xq, y, 0u};
     const uint64_t lim = max_rows ? max_rows : gm_max_rows<F>(L);
-    const uint64_t mlim = max_mrows ? max_mrows : GM_MAX_MROWS;
+    const uint64_t mlim = max_mrows ? max_mrows : gm_max_mrows(K);
     const uint64_t row_bytes = K / (uint64_t)block_values(F) * (uint64_t)block_bytes(F);
     std::vector<uint64_t> t8(TabSpec<F>::n8 > 0 ? TabSpec<F>::n8 : 1);
     std::vector<uint32_t> t4(TabSpec<F>::n4 > 0 ? TabSpec<F>::n4 : 1);
