@@ -394,19 +394,32 @@ NQ_HD void gm_stage_wc(const GmArgs &a, uint32_t n0, uint32_t t0, uint32_t tid, 
 // + g mod 8); codes to cw (K bytes per row), scales and offsets to cs / co.
 NQ_HD uint64_t gm_rewrite_items(uint32_t rows, uint32_t kspans) { return (uint64_t)rows * ((kspans + 7u) / 8u) * 8u; }
 
+// Item g's span: its row n and span t (false past K), its codes stored to
+// cw, its scales and offsets in o.
 template <int F, class Src>
-NQ_HD void gm_rewrite_item(const GmArgs &a, const Src &src, const Tab &tab, uint64_t g, uint32_t *cw, float *cs,
-                           float *co) {
+NQ_HD bool gm_rewrite_span(const GmArgs &a, const Src &src, const Tab &tab, uint64_t g, uint32_t *cw, uint32_t *n_out,
+                           uint32_t *t_out, GmSpan &o) {
     using G = GmFmt<F>;
     const uint64_t g8 = g >> 3;
     const uint32_t n = (uint32_t)(g8 % a.rows), t = (uint32_t)(g8 / a.rows) * 8u + (uint32_t)(g & 7u);
-    if (t >= a.kspans) return;
+    if (t >= a.kspans) return false;
     const uint32_t b = t / G::SPB;
-    GmSpan o;
     gm_span<F>(src, a.wmis + n * a.row_bytes + b * (uint32_t)block_bytes(F), t - b * G::SPB, tab, o);
     u32x4 *d = (u32x4 *)(cw + (uint64_t)n * a.kspans * 8u + (uint64_t)t * 8u);
     d[0] = u32x4{o.c[0], o.c[1], o.c[2], o.c[3]};
     d[1] = u32x4{o.c[4], o.c[5], o.c[6], o.c[7]};
+    *n_out = n;
+    *t_out = t;
+    return true;
+}
+
+template <int F, class Src>
+NQ_HD void gm_rewrite_item(const GmArgs &a, const Src &src, const Tab &tab, uint64_t g, uint32_t *cw, float *cs,
+                           float *co) {
+    using G = GmFmt<F>;
+    GmSpan o;
+    uint32_t n, t;
+    if (!gm_rewrite_span<F>(a, src, tab, g, cw, &n, &t, o)) return;
 #pragma unroll
     for (uint32_t h = 0; h < G::NH; h++) {
         cs[((uint64_t)t * G::NH + h) * a.ldy + n] = o.ws[h];
@@ -678,7 +691,43 @@ __global__ __launch_bounds__(WG) void k_gemm_rewrite(GmArgs a, uint32_t *cw, flo
     }
     const Tab tab{t8, t4, nullptr, nullptr, 0xFFFFFFFFu, 1u};
     const GmSrc src{a.wbase, a.wlast};
-    gm_rewrite_item<F>(a, src, tab, (uint64_t)blockIdx.x * WG + threadIdx.x, cw, cs, co);
+    using G = GmFmt<F>;
+    constexpr uint32_t GR = (uint32_t)WG / 8u;  // groups (rows) per workgroup
+    GmSpan o;
+    uint32_t n = 0u, t = 0u;
+    const bool live =
+        gm_rewrite_span<F>(a, src, tab, (uint64_t)blockIdx.x * WG + threadIdx.x, cw, &n, &t, o);
+    // The workgroup's groups are rows n0 .. n0 + GR - 1 of one span octet q
+    // unless they pass the last row: then its scales and offsets go through
+    // LDS, so that consecutive threads store consecutive rows of one span
+    // (whole 128-byte runs instead of words N apart).
+    const uint64_t g80 = (uint64_t)blockIdx.x * GR;
+    const uint32_t n0 = (uint32_t)(g80 % a.rows), q = (uint32_t)(g80 / a.rows);
+    if (n0 + GR <= a.rows) {
+        __shared__ float tw[G::NH][8][GR + 1], to[G::AFF ? G::NH : 1][8][GR + 1];
+        const uint32_t j = threadIdx.x / 8u, sp = threadIdx.x % 8u;  // this thread's row and span in the tile
+#pragma unroll
+        for (uint32_t h = 0; h < G::NH; h++) {
+            tw[h][sp][j] = live ? o.ws[h] : 0.0f;
+            if constexpr (G::AFF) to[h][sp][j] = live ? o.ow[h] : 0.0f;
+        }
+        __syncthreads();
+        const uint32_t sj = threadIdx.x % GR, ss = threadIdx.x / GR;  // store: row sj of span ss
+        const uint32_t ts = 8u * q + ss;
+        if (ts < a.kspans) {
+#pragma unroll
+            for (uint32_t h = 0; h < G::NH; h++) {
+                cs[((uint64_t)ts * G::NH + h) * a.ldy + n0 + sj] = tw[h][ss][sj];
+                if constexpr (G::AFF) co[((uint64_t)ts * G::NH + h) * a.ldy + n0 + sj] = to[h][ss][sj];
+            }
+        }
+    } else if (live) {
+#pragma unroll
+        for (uint32_t h = 0; h < G::NH; h++) {
+            cs[((uint64_t)t * G::NH + h) * a.ldy + n] = o.ws[h];
+            if constexpr (G::AFF) co[((uint64_t)t * G::NH + h) * a.ldy + n] = o.ow[h];
+        }
+    }
 }
 
 // The K splits' partial outputs summed in split order: y[i] = ((p0 + p1) + p2) ...
